@@ -1,0 +1,140 @@
+"""CPU oracle for ternary quantize/pack/unpack and the packed-ternary matmul.
+
+TEST INFRASTRUCTURE ONLY.  Only the test suite, ``__graft_entry__.smoke()`` and
+the CPU-baseline leg of ``bench.py`` may import this package.  The product
+path (``ternary_weight_only_amd``) never imports it, and this package imports
+nothing from the product path.
+
+The arithmetic lives in ``tq_oracle.c`` (plain scalar C, fp64 for the matmul),
+compiled with the host C compiler into ``liboracle.so`` next to this file.
+Each function below only marshals numpy arrays to that library.
+
+Sources: precisit "pack-unpack-run" README (codec.py description: absmean
+scale rounded to fp16, nearest-even ternary codes, five base-3 digits per
+byte, byte-aligned groups with zero-trit padding, bytes 243..255 invalid;
+scale-rule and payload-rate paragraphs) and tiny-llm "Week 2 Day 3: Quantize
+the Model" ("Mathematical Formulation", "Computation Flow").
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+import subprocess
+
+import numpy as np
+
+_HERE = os.path.dirname(os.path.abspath(__file__))
+_SRC = os.path.join(_HERE, "tq_oracle.c")
+_LIB = os.path.join(_HERE, "liboracle.so")
+
+# Status bits (same values as the library's device status bits).
+NONFINITE = 1
+SCALE_OVERFLOW = 2
+INVALID_BYTE = 4
+BAD_PADDING = 8
+
+ERR_NULL = -1
+ERR_SHAPE = -2
+
+_lib = None
+
+
+def build(force: bool = False) -> str:
+    """Compile tq_oracle.c into liboracle.so with gcc; returns the path."""
+    if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
+        tmp = _LIB + ".tmp%d" % os.getpid()
+        subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC",
+                               "-shared", "-o", tmp, _SRC, "-lm"])
+        os.replace(tmp, _LIB)
+    return _LIB
+
+
+def _load():
+    global _lib
+    if _lib is None:
+        build()
+        lib = ctypes.CDLL(_LIB)
+        i64, p = ctypes.c_int64, ctypes.c_void_p
+        lib.oracle_packed_row_bytes.argtypes = [i64, i64]
+        lib.oracle_packed_row_bytes.restype = i64
+        lib.oracle_quantize_pack.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.oracle_quantize_pack.restype = ctypes.c_int
+        lib.oracle_unpack.argtypes = [p, i64, i64, i64, p, p]
+        lib.oracle_unpack.restype = ctypes.c_int
+        lib.oracle_matmul.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
+        lib.oracle_matmul.restype = ctypes.c_int
+        _lib = lib
+    return _lib
+
+
+def _ptr(a: np.ndarray) -> int:
+    return a.ctypes.data
+
+
+class OracleError(RuntimeError):
+    pass
+
+
+def packed_row_bytes(K: int, G: int) -> int:
+    """Packed bytes per row: (K/G) * ceil(G/5); 0 for invalid arguments."""
+    return int(_load().oracle_packed_row_bytes(K, G))
+
+
+def quantize_pack(w_bits: np.ndarray, G: int):
+    """w_bits: uint16 [N,K] bf16 bit patterns.
+
+    Returns (packed uint8 [N, (K/G)*ceil(G/5)], scales uint16 [N, K/G] fp16 bits,
+    status bits int).
+    """
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N,K]")
+    N, K = w.shape
+    rb = packed_row_bytes(K, G)
+    if rb == 0:
+        raise OracleError("invalid shape K=%d G=%d" % (K, G))
+    packed = np.empty((N, rb), np.uint8)
+    scales = np.empty((N, K // G), np.uint16)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_quantize_pack(_ptr(w), N, K, G, _ptr(packed), _ptr(scales), _ptr(st))
+    if rc:
+        raise OracleError("oracle_quantize_pack rc=%d" % rc)
+    return packed, scales, int(st[0])
+
+
+def unpack(packed: np.ndarray, N: int, K: int, G: int):
+    """Returns (codes int8 [N,K] in {-1,0,1}, status bits int)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    rb = packed_row_bytes(K, G)
+    if rb == 0 or p.size != N * rb:
+        raise OracleError("packed has %d bytes, expected %d" % (p.size, N * rb))
+    codes = np.empty((N, K), np.int8)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_unpack(_ptr(p), N, K, G, _ptr(codes), _ptr(st))
+    if rc:
+        raise OracleError("oracle_unpack rc=%d" % rc)
+    return codes, int(st[0])
+
+
+def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):
+    """y[m,n] = sum_k x[m,k] c[n,k] s[n,k/G] in fp64.
+
+    x_bits: uint16 [M,K] bf16 bits.  Returns (y float64 [M,N],
+    bound float64 [M,N] = sum_k |x c s|, status bits int).
+    """
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M,K]")
+    M = x.shape[0]
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    rb = packed_row_bytes(K, G)
+    if rb == 0 or p.size != N * rb or s.size != N * (K // G):
+        raise OracleError("bad packed/scales sizes")
+    y = np.empty((M, N), np.float64)
+    bound = np.empty((M, N), np.float64)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_matmul(_ptr(x), _ptr(p), _ptr(s), M, N, K, G, _ptr(y), _ptr(bound), _ptr(st))
+    if rc:
+        raise OracleError("oracle_matmul rc=%d" % rc)
+    return y, bound, int(st[0])

@@ -1,0 +1,423 @@
+/*
+ * tq_oracle.c -- plain, slow CPU reference for group-wise ternary weight
+ * quantization, packing, unpacking and the packed-ternary x bf16 matmul.
+ *
+ * TEST INFRASTRUCTURE ONLY.  Nothing in the product path may link, load or
+ * call this file: only the test suite, the smoke check and the benchmark's
+ * CPU-baseline leg use it.  It shares no code, header, table or helper with
+ * the HIP library; the two agree only through the data format below.
+ *
+ * Sources (web pages; cited by title and section):
+ *  [P4] precisit "pack-unpack-run" README, the paragraph describing codec.py
+ *       (absmean scale rounded to fp16, nearest-even ternary codes, five
+ *       base-three digits per byte, per-group byte alignment with zero-trit
+ *       padding, byte values 243..255 invalid), the scale-rule paragraph
+ *       (no calibration, zero stored scale -> zero group, columns divisible
+ *       by the group size) and the payload-rate paragraph.
+ *  [P2] tiny-llm "Week 2 Day 3: Quantize the Model", sections
+ *       "Mathematical Formulation" and "Computation Flow" (per-group
+ *       factoring of the scale out of the inner sum; fp32-or-wider
+ *       accumulator per output element).
+ *
+ * Readings where the pages leave a step open (all listed in the design doc):
+ *  - digit = code + 1 and the first weight of five is the least significant
+ *    base-3 digit:  byte = sum_i (c[5b+i] + 1) * 3^i.
+ *  - padding trits (positions >= G in a group's last byte) hold code 0.
+ *  - scale = one round-to-nearest-even to fp16 of the EXACT mean of |w|
+ *    (exact integer sum of the bf16 magnitudes, then one rounding).
+ *  - code = +1 if w > s/2, -1 if w < -s/2, else 0 (|w| == s/2 -> 0).
+ *  - non-finite weight in a group: status NONFINITE, scale 0x7E00, codes 0.
+ *  - mean that rounds to >= 65520: status SCALE_OVERFLOW, scale 0x7C00,
+ *    codes 0.
+ *  - unpack: byte >= 243 -> INVALID_BYTE and code 0 for that byte's
+ *    positions; a padding trit that is not code 0 -> BAD_PADDING.
+ *
+ * Everything here is scalar C.  Floating-point matmul is done in fp64:
+ * every product x*c*s is exact in fp64 (bf16 x fp16 significands need 19
+ * bits), so only the order of the fp64 sum rounds.
+ */
+#include <math.h>
+#include <stdint.h>
+#include <stddef.h>
+#include <stdlib.h>
+#include <string.h>
+
+/* Return codes (same numeric values as the library's host-side codes). */
+#define OR_OK          0
+#define OR_ERR_NULL   -1
+#define OR_ERR_SHAPE  -2
+
+/* Status bits OR-ed into *status (same values as the library's device bits). */
+#define OR_NONFINITE       1
+#define OR_SCALE_OVERFLOW  2
+#define OR_INVALID_BYTE    4
+#define OR_BAD_PADDING     8
+
+/* ------------------------------------------------------------------------ */
+/* Sizes                                                                      */
+/* ------------------------------------------------------------------------ */
+
+/* Bytes per group: ceil(G/5) base-3 bytes ([P4] codec.py description). */
+static int64_t bytes_per_group(int64_t G) { return (G + 4) / 5; }
+
+/* Packed bytes of one row of K weights; 0 if the arguments are invalid. */
+int64_t oracle_packed_row_bytes(int64_t K, int64_t G)
+{
+    if (K < 1 || G < 1 || K % G != 0) return 0;
+    return (K / G) * bytes_per_group(G);
+}
+
+static int check_shape(int64_t N, int64_t K, int64_t G)
+{
+    if (N < 1 || K < 1 || G < 1) return OR_ERR_SHAPE;
+    if (K % G != 0) return OR_ERR_SHAPE;  /* [P4] scale-rule paragraph */
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* A small unsigned big integer: 8 little-endian 64-bit limbs (512 bits).    */
+/* The exact sum of G bf16 magnitudes is below G * 2^261, so 512 bits hold   */
+/* it for any G below 2^250.                                                  */
+/* ------------------------------------------------------------------------ */
+
+#define NLIMB 8
+typedef struct { uint64_t w[NLIMB]; } big_t;
+
+static void big_zero(big_t *a) { memset(a, 0, sizeof *a); }
+
+static int big_is_zero(const big_t *a)
+{
+    for (int i = 0; i < NLIMB; ++i) if (a->w[i]) return 0;
+    return 1;
+}
+
+/* a += v * 2^sh, with v < 2^64. */
+static void big_add_shifted(big_t *a, uint64_t v, int sh)
+{
+    int limb = sh / 64, off = sh % 64;
+    uint64_t lo = v << off;
+    uint64_t hi = off ? (v >> (64 - off)) : 0;
+    uint64_t carry = 0;
+    for (int i = limb; i < NLIMB; ++i) {
+        uint64_t add = (i == limb) ? lo : (i == limb + 1) ? hi : 0;
+        uint64_t s = a->w[i] + add;
+        uint64_t c1 = s < add;
+        uint64_t s2 = s + carry;
+        uint64_t c2 = s2 < s;
+        a->w[i] = s2;
+        carry = c1 + c2;
+        if (i > limb + 1 && carry == 0) break;
+    }
+}
+
+/* Bit number i of a. */
+static int big_bit(const big_t *a, int i)
+{
+    if (i < 0 || i >= 64 * NLIMB) return 0;
+    return (int)((a->w[i / 64] >> (i % 64)) & 1u);
+}
+
+/* 1 if any bit below position n is set. */
+static int big_any_below(const big_t *a, int n)
+{
+    for (int i = 0; i < n && i < 64 * NLIMB; ++i) if (big_bit(a, i)) return 1;
+    return 0;
+}
+
+/* q = a >> n (floor). */
+static void big_shr(const big_t *a, int n, big_t *q)
+{
+    big_zero(q);
+    for (int i = n; i < 64 * NLIMB; ++i)
+        if (big_bit(a, i)) q->w[(i - n) / 64] |= (uint64_t)1 << ((i - n) % 64);
+}
+
+/* q = floor(a / d), returns a mod d; d >= 1 and d < 2^32. */
+static uint64_t big_divmod_small(const big_t *a, uint64_t d, big_t *q)
+{
+    big_zero(q);
+    uint64_t rem = 0;
+    for (int i = 64 * NLIMB - 1; i >= 0; --i) {
+        rem = (rem << 1) | (uint64_t)big_bit(a, i);
+        if (rem >= d) {
+            rem -= d;
+            q->w[i / 64] |= (uint64_t)1 << (i % 64);
+        }
+    }
+    return rem;
+}
+
+/* -1, 0, +1 as a <, ==, > (G * 2^n). */
+static int big_cmp_g_pow2(const big_t *a, uint64_t G, int n)
+{
+    big_t b;
+    big_zero(&b);
+    big_add_shifted(&b, G, n);
+    for (int i = NLIMB - 1; i >= 0; --i) {
+        if (a->w[i] > b.w[i]) return 1;
+        if (a->w[i] < b.w[i]) return -1;
+    }
+    return 0;
+}
+
+/*
+ * Round-half-even of the rational a / (G * 2^n) to an integer, for results
+ * that fit in 64 bits.  Written as: a / 2^n = A + f with integer A and
+ * fraction f in [0,1); A = G*q + r; the exact quotient is q + (r + f)/G and
+ * the decision compares (r + f)/G with 1/2.
+ */
+static uint64_t big_rne_div(const big_t *a, uint64_t G, int n)
+{
+    big_t A, Q;
+    big_shr(a, n, &A);
+    uint64_t r = big_divmod_small(&A, G, &Q);
+    uint64_t q = Q.w[0];
+    /* f compared with 1/2: sign of (f - 1/2) and whether f > 0. */
+    int f_pos = big_any_below(a, n);
+    int f_cmp_half;                       /* -1: f < 1/2, 0: f == 1/2, 1: f > 1/2 */
+    if (n == 0) f_cmp_half = -1;          /* f == 0 */
+    else if (!big_bit(a, n - 1)) f_cmp_half = -1;
+    else f_cmp_half = big_any_below(a, n - 1) ? 1 : 0;
+
+    /* 2(r + f) compared with G. */
+    int up;
+    if (2 * r + 2 <= G) up = 0;                         /* 2r + 2f < G     */
+    else if (2 * r > G) up = 1;                         /* 2r >= G + 1     */
+    else if (2 * r == G) up = f_pos ? 1 : (int)(q & 1); /* exact tie if f=0 */
+    else /* 2r == G - 1 */ up = (f_cmp_half > 0) ? 1 : (f_cmp_half == 0 ? (int)(q & 1) : 0);
+    return q + (uint64_t)up;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a1: group scale                                                            */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * bf16 magnitude bits u (sign cleared, finite) as sig * 2^(e - 133) with an
+ * integer significand sig <= 255 and e >= 0:
+ *   normal    (E = u>>7 in 1..254): value = (128 + m) * 2^(E - 134)
+ *   subnormal (E = 0):              value = m * 2^-133
+ */
+static void bf16_mag_parts(uint16_t u, uint64_t *sig, int *e)
+{
+    int E = (u >> 7) & 0xFF;
+    int m = u & 0x7F;
+    if (E == 0) { *sig = (uint64_t)m; *e = 0; }
+    else        { *sig = (uint64_t)(128 + m); *e = E - 1; }
+}
+
+/*
+ * Scale of one group ([P4] codec.py description and scale-rule paragraph):
+ * the mean of |w| over the G weights, rounded once to fp16 with ties to
+ * even.  The sum is exact: sum |w| = A * 2^-133 with A an integer.
+ *
+ * In units of the fp16 subnormal step 2^-24 the mean is V = A / (G * 2^109).
+ *   V < 1024:  subnormal (or the smallest normal if it rounds up to 1024);
+ *              fp16 bits = RNE(V).
+ *   else:      V in [2^(10+k), 2^(11+k)) for some k >= 0; the fp16 value is
+ *              Q * 2^k with Q = RNE(V / 2^k) in [1024, 2048], whose bits are
+ *              (k << 10) + Q (a carry to 2048 moves into the exponent).
+ * Returns the status bits of the group (0 or OR_SCALE_OVERFLOW).
+ */
+static int group_scale_bits(const uint16_t *w, int64_t G, uint16_t *out_bits)
+{
+    big_t A;
+    big_zero(&A);
+    for (int64_t j = 0; j < G; ++j) {
+        uint64_t sig; int e;
+        bf16_mag_parts((uint16_t)(w[j] & 0x7FFF), &sig, &e);
+        big_add_shifted(&A, sig, e);
+    }
+    if (big_is_zero(&A)) { *out_bits = 0; return 0; }
+
+    uint64_t bits;
+    if (big_cmp_g_pow2(&A, (uint64_t)G, 109 + 10) < 0) {
+        bits = big_rne_div(&A, (uint64_t)G, 109);          /* 0 .. 1024 */
+    } else {
+        int k = 0;
+        /* smallest k with V < 2^(11+k); past k = 29 the result overflows */
+        while (k < 40 && big_cmp_g_pow2(&A, (uint64_t)G, 109 + 11 + k) >= 0) ++k;
+        if (k >= 30) { *out_bits = 0x7C00; return OR_SCALE_OVERFLOW; }
+        uint64_t Q = big_rne_div(&A, (uint64_t)G, 109 + k);  /* 1024 .. 2048 */
+        bits = ((uint64_t)k << 10) + Q;
+    }
+    if (bits >= 0x7C00) { *out_bits = 0x7C00; return OR_SCALE_OVERFLOW; }
+    *out_bits = (uint16_t)bits;
+    return 0;
+}
+
+/* ------------------------------------------------------------------------ */
+/* Plain conversions to double (exact)                                        */
+/* ------------------------------------------------------------------------ */
+
+/* bf16 bits -> double, exact; non-finite inputs are not passed here. */
+static double bf16_to_double(uint16_t b)
+{
+    uint64_t sig; int e;
+    bf16_mag_parts((uint16_t)(b & 0x7FFF), &sig, &e);
+    double v = ldexp((double)sig, e - 133);
+    return (b & 0x8000) ? -v : v;
+}
+
+/* fp16 bits -> double, exact; finite inputs only. */
+static double f16_to_double(uint16_t h)
+{
+    int E = (h >> 10) & 0x1F;
+    int m = h & 0x3FF;
+    double v = (E == 0) ? ldexp((double)m, -24) : ldexp((double)(1024 + m), E - 25);
+    return (h & 0x8000) ? -v : v;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a1-a3: quantize + pack                                                     */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * w[N,K] bf16 bits, row-major; groups of G along K.
+ * packed[N][K/G][ceil(G/5)] bytes, scales[N][K/G] fp16 bits.
+ * *status receives the OR of all group status bits (may be NULL).
+ */
+int oracle_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int64_t G,
+                         uint8_t *packed, uint16_t *scales, int32_t *status)
+{
+    if (!w || !packed || !scales) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G, B = bytes_per_group(G);
+    int32_t st = 0;
+    int8_t *code = (int8_t *)__builtin_alloca((size_t)(5 * B));
+
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < nG; ++g) {
+            const uint16_t *wg = w + n * K + g * G;
+            uint8_t *pg = packed + (n * nG + g) * B;
+            int gst = 0;
+            uint16_t sbits = 0;
+
+            for (int64_t j = 0; j < G; ++j)
+                if (((wg[j] >> 7) & 0xFF) == 0xFF) gst |= OR_NONFINITE;
+            if (gst) sbits = 0x7E00;
+            else gst |= group_scale_bits(wg, G, &sbits);
+
+            /* a2: codes.  |w| == s/2 is a tie and goes to 0 (round half to
+             * even of +-0.5); beyond 1.5 s the code saturates at +-1. */
+            for (int64_t t = 0; t < 5 * B; ++t) code[t] = 0;  /* padding = 0 */
+            if (!gst) {
+                double half = 0.5 * f16_to_double(sbits);
+                for (int64_t j = 0; j < G; ++j) {
+                    double v = bf16_to_double(wg[j]);
+                    code[j] = (int8_t)(v > half ? 1 : (v < -half ? -1 : 0));
+                }
+            }
+
+            /* a3: five base-3 digits per byte, first weight lowest digit. */
+            for (int64_t b = 0; b < B; ++b) {
+                int byte = 0, p3 = 1;
+                for (int i = 0; i < 5; ++i) {
+                    byte += (code[5 * b + i] + 1) * p3;
+                    p3 *= 3;
+                }
+                pg[b] = (uint8_t)byte;
+            }
+            scales[n * nG + g] = sbits;
+            st |= gst;
+        }
+    }
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a4: unpack                                                                 */
+/* ------------------------------------------------------------------------ */
+
+/* packed -> codes[N,K] int8 in {-1,0,1}. */
+int oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int64_t G,
+                  int8_t *codes, int32_t *status)
+{
+    if (!packed || !codes) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G, B = bytes_per_group(G);
+    int32_t st = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < nG; ++g) {
+            const uint8_t *pg = packed + (n * nG + g) * B;
+            int8_t *cg = codes + n * K + g * G;
+            for (int64_t b = 0; b < B; ++b) {
+                int v = pg[b];
+                int valid = v < 243;
+                if (!valid) st |= OR_INVALID_BYTE;
+                for (int i = 0; i < 5; ++i) {
+                    int d = v % 3;
+                    v /= 3;
+                    int64_t pos = 5 * b + i;
+                    if (pos < G) cg[pos] = (int8_t)(valid ? d - 1 : 0);
+                    else if (valid && d != 1) st |= OR_BAD_PADDING;
+                }
+            }
+        }
+    }
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* a5/a6: matmul in fp64                                                      */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * y[m,n] = sum_k x[m,k] * c[n,k] * s[n, k/G], summed in fp64 in k order
+ * ([P2] "Mathematical Formulation": the group scale multiplies the group's
+ * inner sum; here every term is formed exactly instead).
+ * bound[m,n] = sum_k |x[m,k] * c[n,k] * s[n, k/G]| (may be NULL).
+ * x: [M,K] bf16 bits (finite).  Invalid bytes decode to code 0 and set
+ * INVALID_BYTE.  Non-finite scales (never produced by the packer for a
+ * valid group) are passed through as IEEE values.
+ */
+int oracle_matmul(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                  int64_t M, int64_t N, int64_t K, int64_t G,
+                  double *y, double *bound, int32_t *status)
+{
+    if (!x || !packed || !scales || !y) return OR_ERR_NULL;
+    if (M < 1) return OR_ERR_SHAPE;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G;
+    int8_t *crow = (int8_t *)malloc((size_t)K);
+    double *wrow = (double *)malloc((size_t)K * sizeof(double));
+    double *xd = (double *)malloc((size_t)(M * K) * sizeof(double));
+    if (!crow || !wrow || !xd) { free(crow); free(wrow); free(xd); return OR_ERR_NULL; }
+    for (int64_t i = 0; i < M * K; ++i) xd[i] = bf16_to_double(x[i]);
+    int32_t st = 0;
+
+    for (int64_t n = 0; n < N; ++n) {
+        /* decode row n: w_hat = c * s */
+        int32_t rst = 0;
+        oracle_unpack(packed + n * oracle_packed_row_bytes(K, G), 1, K, G, crow, &rst);
+        st |= rst & OR_INVALID_BYTE;
+        for (int64_t g = 0; g < nG; ++g) {
+            uint16_t h = scales[n * nG + g];
+            double s;
+            if (((h >> 10) & 0x1F) == 0x1F)  /* inf / NaN scale */
+                s = (h & 0x3FF) ? NAN : ((h & 0x8000) ? -INFINITY : INFINITY);
+            else
+                s = f16_to_double(h);
+            for (int64_t j = 0; j < G; ++j) wrow[g * G + j] = (double)crow[g * G + j] * s;
+        }
+        for (int64_t m = 0; m < M; ++m) {
+            const double *xm = xd + m * K;
+            double acc = 0.0, bacc = 0.0;
+            for (int64_t k = 0; k < K; ++k) {
+                double t = xm[k] * wrow[k];
+                acc += t;
+                bacc += fabs(t);
+            }
+            y[m * N + n] = acc;
+            if (bound) bound[m * N + n] = bacc;
+        }
+    }
+    free(crow); free(wrow); free(xd);
+    if (status) *status |= st;
+    return OR_OK;
+}

@@ -1,0 +1,100 @@
+"""Seeded synthetic inputs shared by the tests, the benchmark and the oracle checks.
+
+This module draws random numbers and rounds them to bf16; it contains none of
+the quantization or matmul arithmetic.  Both the HIP path and the CPU oracle
+consume the arrays it returns; neither side generates its own inputs.
+
+Generator: SplitMix64 (Steele, Lea and Flood, "Fast splittable pseudorandom
+number generators", OOPSLA 2014) counter stream -> two uniforms in (0, 1] from
+the top 53 bits -> Box-Muller transform in float64 -> times sigma -> float32
+(round to nearest even) -> bf16 (round to nearest even).  Element i of a
+stream with seed s uses counters 2*(i//2) and 2*(i//2)+1; even i takes the
+cosine branch, odd i the sine branch.
+"""
+from __future__ import annotations
+
+import numpy as np
+
+_GOLDEN = np.uint64(0x9E3779B97F4A7C15)
+_M1 = np.uint64(0xBF58476D1CE4E5B9)
+_M2 = np.uint64(0x94D049BB133111EB)
+
+
+def splitmix64(seed: int, counters: np.ndarray) -> np.ndarray:
+    """SplitMix64 output for the given counters (uint64 array)."""
+    with np.errstate(over="ignore"):
+        z = np.uint64(seed & 0xFFFFFFFFFFFFFFFF) + (counters.astype(np.uint64) + np.uint64(1)) * _GOLDEN
+        z = (z ^ (z >> np.uint64(30))) * _M1
+        z = (z ^ (z >> np.uint64(27))) * _M2
+        return z ^ (z >> np.uint64(31))
+
+
+def f32_to_bf16_bits(a: np.ndarray) -> np.ndarray:
+    """float32 -> bf16 bit patterns, round to nearest even (finite inputs)."""
+    u = np.ascontiguousarray(a, dtype=np.float32).view(np.uint32)
+    rounding = np.uint32(0x7FFF) + ((u >> np.uint32(16)) & np.uint32(1))
+    return ((u + rounding) >> np.uint32(16)).astype(np.uint16)
+
+
+def bf16_bits_to_f32(b: np.ndarray) -> np.ndarray:
+    """bf16 bit patterns -> float32 (exact)."""
+    return (np.asarray(b, dtype=np.uint16).astype(np.uint32) << np.uint32(16)).view(np.float32)
+
+
+def normal_f64(seed: int, n: int, start: int = 0) -> np.ndarray:
+    """n standard normals (float64) of stream `seed`, elements start..start+n-1."""
+    idx = np.arange(start, start + n, dtype=np.uint64)
+    pair = idx // np.uint64(2)
+    r1 = splitmix64(seed, pair * np.uint64(2))
+    r2 = splitmix64(seed, pair * np.uint64(2) + np.uint64(1))
+    u1 = ((r1 >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
+    u2 = ((r2 >> np.uint64(11)).astype(np.float64) + 1.0) * (2.0 ** -53)
+    rad = np.sqrt(-2.0 * np.log(u1))
+    ang = 2.0 * np.pi * u2
+    return np.where((idx & np.uint64(1)) == 0, rad * np.cos(ang), rad * np.sin(ang))
+
+
+def normal_bf16(seed: int, shape, sigma: float = 1.0, chunk: int = 1 << 22) -> np.ndarray:
+    """bf16 bit patterns (uint16 array of `shape`) of N(0, sigma^2) samples."""
+    n = int(np.prod(shape))
+    out = np.empty(n, np.uint16)
+    for s in range(0, n, chunk):
+        e = min(n, s + chunk)
+        v = (normal_f64(seed, e - s, start=s) * sigma).astype(np.float32)
+        out[s:e] = f32_to_bf16_bits(v)
+    return out.reshape(shape)
+
+
+# ---------------------------------------------------------------------------
+# The synthetic workloads (seeds fixed here; shapes follow the FFN matrices of
+# a Qwen-like decoder with hidden 1024 / intermediate 3584, and an 8B-class
+# dense decoder with hidden 4096 / intermediate 14336).
+# ---------------------------------------------------------------------------
+
+W_SIGMA = 0.02
+X_SIGMA = 1.0
+
+
+def small_matrix(K: int = 512, seed: int = 0) -> np.ndarray:
+    """W[256,K] ~ N(0, 0.02) with group 0 of row 0 and the last 64-group of
+    row 255 forced to zero (all-zero groups)."""
+    w = normal_bf16(seed, (256, K), W_SIGMA)
+    w[0, 0:64] = 0
+    w[255, K - 64:K] = 0
+    return w
+
+
+def ffn_shapes(hidden: int = 1024, inter: int = 3584):
+    """(name, N, K) of the gate, up and down projections of one FFN block."""
+    return [("gate", inter, hidden), ("up", inter, hidden), ("down", hidden, inter)]
+
+
+def ffn_weight(layer: int, proj: int, hidden: int = 1024, inter: int = 3584) -> np.ndarray:
+    """Weights of layer `layer`, projection proj (0 gate, 1 up, 2 down)."""
+    _, N, K = ffn_shapes(hidden, inter)[proj]
+    return normal_bf16(1000 + 3 * layer + proj, (N, K), W_SIGMA)
+
+
+def activation(seed: int, M: int, K: int) -> np.ndarray:
+    """x[M,K] ~ N(0,1) as bf16 bits."""
+    return normal_bf16(seed, (M, K), X_SIGMA)

@@ -1,0 +1,98 @@
+"""The pins must catch plausible mistakes in the oracle.
+
+Each case compiles a copy of oracle/tq_oracle.c with one planted mistake (on
+the CPU, into a temporary directory), points the oracle wrapper at it, and
+requires that at least one of the pin tests fails.  The real oracle is
+restored afterwards.
+"""
+import ctypes
+import os
+import shutil
+import subprocess
+import tempfile
+
+import pytest
+
+import oracle
+from tests import test_oracle_format as fmt
+from tests import test_oracle_matmul as mm
+from tests import test_oracle_scale as sc
+
+SRC = os.path.join(os.path.dirname(oracle.__file__), "tq_oracle.c")
+GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
+
+MUTATIONS = {
+    "digit_order_msd_first": ("byte += (code[5 * b + i] + 1) * p3;",
+                              "byte += (code[5 * b + (4 - i)] + 1) * p3;"),
+    "dropped_last_term_in_sum": ("    for (int64_t j = 0; j < G; ++j) {\n        uint64_t sig; int e;",
+                                 "    for (int64_t j = 0; j < G - 1; ++j) {\n        uint64_t sig; int e;"),
+    "tie_rounds_up": ("else if (2 * r == G) up = f_pos ? 1 : (int)(q & 1);",
+                      "else if (2 * r == G) up = 1;"),
+    "code_tie_away_from_zero": ("code[j] = (int8_t)(v > half ? 1 : (v < -half ? -1 : 0));",
+                                "code[j] = (int8_t)(v >= half ? 1 : (v <= -half ? -1 : 0));"),
+    "code_sign_flipped": ("code[j] = (int8_t)(v > half ? 1 : (v < -half ? -1 : 0));",
+                          "code[j] = (int8_t)(v > half ? -1 : (v < -half ? 1 : 0));"),
+    "padding_trit_minus_one": ("code[t] = 0;  /* padding = 0 */", "code[t] = -1;  /* padding */"),
+    "invalid_threshold_off_by_one": ("int valid = v < 243;", "int valid = v < 242;"),
+    "padding_not_checked": ("else if (valid && d != 1) st |= OR_BAD_PADDING;", "else {}"),
+    "scale_of_first_group_only": ("wrow[g * G + j] = (double)crow[g * G + j] * s;",
+                                  "wrow[g * G + j] = (double)crow[g * G + j] * f16_to_double(scales[n * nG]);"),
+    "x_transposed": ("const double *xm = xd + m * K;", "const double *xm = xd + m;"),
+    "bound_not_absolute": ("bacc += fabs(t);", "bacc += t;"),
+}
+
+PINS = [
+    fmt.test_all_243_codewords_decode,
+    fmt.test_all_243_codewords_encode_bijection,
+    lambda: fmt.test_invalid_bytes_rejected(GOLDEN),
+    fmt.test_group_alignment_and_padding_ranges,
+    fmt.test_bad_padding_flagged,
+    fmt.test_zero_group_and_zero_scale,
+    lambda: fmt.test_hand_worked_group(GOLDEN),
+    lambda: sc.test_scale_vs_fraction_normal(64),
+    lambda: sc.test_scale_vs_fraction_wide_exponents(64),
+    sc.test_scale_constructed_midpoints,
+    sc.test_codes_tie_fixture,
+    sc.test_codes_vs_numpy_rint,
+    lambda: mm.test_matmul_vs_exact_rationals(3, 320, 64, 2),
+    mm.test_matmul_vs_numpy_matmul,
+    mm.test_one_hot_rows_exact,
+]
+
+
+def _load_variant(path):
+    lib = ctypes.CDLL(path)
+    i64, p = ctypes.c_int64, ctypes.c_void_p
+    lib.oracle_packed_row_bytes.argtypes = [i64, i64]
+    lib.oracle_packed_row_bytes.restype = i64
+    lib.oracle_quantize_pack.argtypes = [p, i64, i64, i64, p, p, p]
+    lib.oracle_unpack.argtypes = [p, i64, i64, i64, p, p]
+    lib.oracle_matmul.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
+    return lib
+
+
+@pytest.mark.parametrize("name", sorted(MUTATIONS))
+def test_planted_mistake_is_caught(name):
+    old, new = MUTATIONS[name]
+    src = open(SRC).read()
+    assert src.count(old) == 1, "mutation anchor must match exactly once"
+    d = tempfile.mkdtemp(prefix="oracle_mut_")
+    try:
+        c = os.path.join(d, "m.c")
+        so = os.path.join(d, "libm.so")
+        open(c, "w").write(src.replace(old, new))
+        subprocess.check_call(["gcc", "-O1", "-std=c11", "-w", "-fPIC", "-shared", "-o", so, c, "-lm"])
+        saved = oracle._load()
+        oracle._lib = _load_variant(so)
+        failures = 0
+        try:
+            for pin in PINS:
+                try:
+                    pin()
+                except (AssertionError, oracle.OracleError):
+                    failures += 1
+        finally:
+            oracle._lib = saved
+        assert failures > 0, "no pin caught mutation %s" % name
+    finally:
+        shutil.rmtree(d)
