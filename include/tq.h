@@ -1,0 +1,147 @@
+/*
+ * tq.h -- C ABI of libtq.so: group-wise ternary weight quantization and the
+ * packed-ternary x bf16-activation matmul, hand-written HIP for gfx950
+ * (AMD Instinct MI355X).
+ *
+ * Format (precisit "pack-unpack-run" README, codec.py description, scale-rule
+ * and payload-rate paragraphs):
+ *   - W[N,K] is split along K into groups of G weights (K % G == 0).
+ *   - Each group stores one fp16 scale s = mean |w| over the group, rounded
+ *     once to fp16 (round half to even) from the exact sum.
+ *   - Each weight stores a code c in {-1,0,1}: c = sign(w) if |w| > s/2,
+ *     else 0 (|w| == s/2 is a tie and goes to 0).
+ *   - Codes are packed five per byte as base-3 digits d = c + 1, the first
+ *     weight of the five in the least significant digit:
+ *       byte = sum_{i<5} (c[5b+i] + 1) * 3^i,
+ *     each group separately byte-aligned in ceil(G/5) bytes, positions >= G
+ *     padded with code 0.  Byte values 243..255 are invalid.
+ *   - The reconstruction is w_hat = c * s; a zero scale makes a zero group.
+ *   - Payload: 8 * (ceil(G/5) + 2) / G bits per weight (1.875 at G=64,
+ *     1.750 at G=128).
+ *
+ * Layouts (all row-major, no padding between rows):
+ *   w       uint16 [N][K]                 bf16 bit patterns
+ *   packed  uint8  [N][K/G][ceil(G/5)]    group bytes, groups in K order
+ *   scales  uint16 [N][K/G]               fp16 bit patterns
+ *   codes   int8   [N][K]                 {-1, 0, 1}
+ *   x       uint16 [M][K]                 bf16 bit patterns (finite)
+ *   y       float  [M][N]                 fp32, y = x * W_hat^T
+ *
+ * Ownership: every pointer argument is a DEVICE pointer owned by the caller;
+ * the library never allocates, frees or retains caller memory, and keeps no
+ * per-call state.  Every call only enqueues work on `stream` (a hipStream_t,
+ * or NULL for the null stream) and returns without synchronizing.  Calls are
+ * thread-safe.
+ *
+ * Errors: argument errors detected on the host return a negative tq_status
+ * and enqueue nothing.  Data errors found on the device are OR-ed into
+ * *d_status (a device int32 the caller zeroes beforehand; d_status may be
+ * NULL to skip reporting); read it after synchronizing the stream.  When a
+ * bit is set, the outputs of the affected groups are as documented per call.
+ *
+ * Supported on the GPU: G in {64, 128}.
+ */
+#ifndef TQ_H
+#define TQ_H
+
+#include <stddef.h>
+#include <stdint.h>
+
+#ifdef __cplusplus
+extern "C" {
+#endif
+
+typedef enum {
+    TQ_OK = 0,
+    TQ_ERR_NULL = -1,    /* a required pointer is NULL                          */
+    TQ_ERR_SHAPE = -2,   /* M, N or K < 1; K % G != 0; M > 16 in tq_gemv;       */
+                         /* sizes whose byte counts overflow int64              */
+    TQ_ERR_GROUP = -3,   /* G not in {64, 128}                                  */
+    TQ_ERR_ALIGN = -4,   /* a pointer is not aligned as its call requires       */
+    TQ_ERR_LAUNCH = -5   /* the HIP runtime reported an error at launch         */
+} tq_status;
+
+/* Device status bits. */
+enum {
+    TQ_DEV_NONFINITE = 1,      /* a weight is Inf or NaN (tq_quantize_pack)        */
+    TQ_DEV_SCALE_OVERFLOW = 2, /* a group mean rounds to >= 65520 (tq_quantize_pack)*/
+    TQ_DEV_INVALID_BYTE = 4,   /* a packed byte is >= 243 (unpack, gemv, gemm)     */
+    TQ_DEV_BAD_PADDING = 8     /* a padding trit is not code 0 (tq_unpack)         */
+};
+
+/* Human-readable name of a tq_status value. */
+const char *tq_status_string(int status);
+
+/* Packed bytes of an [N,K] matrix: N * (K/G) * ceil(G/5); 0 on bad arguments
+ * (host-only helper, any G >= 1). */
+int64_t tq_packed_bytes(int64_t N, int64_t K, int G);
+
+/*
+ * Quantize and pack W (steps: group scale, ternary codes, base-3 packing).
+ * Source: precisit "pack-unpack-run" README, codec.py description and
+ * scale-rule paragraph.
+ *   w        [N,K] bf16, 16-byte aligned
+ *   packed   [N, K/G, ceil(G/5)] bytes (any alignment)
+ *   scales   [N, K/G] fp16 (2-byte aligned)
+ * Group outputs under device errors: a group holding an Inf/NaN weight gets
+ * scale 0x7E00 and all codes 0 (TQ_DEV_NONFINITE); a group whose mean rounds
+ * to >= 65520 gets scale 0x7C00 and all codes 0 (TQ_DEV_SCALE_OVERFLOW).
+ * Bit-exact and deterministic: results do not depend on launch shape.
+ */
+int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
+                     uint8_t *packed, uint16_t *scales,
+                     int32_t *d_status, void *stream);
+
+/*
+ * Decode packed bytes to codes and validate them.
+ * Source: precisit "pack-unpack-run" README, codec.py description
+ * (decoding; values 243..255 invalid; zero-trit padding).
+ *   packed   [N, K/G, ceil(G/5)] bytes (any alignment)
+ *   codes    [N,K] int8 {-1,0,1}, 8-byte aligned
+ * An invalid byte sets TQ_DEV_INVALID_BYTE and decodes to code 0 at its five
+ * positions; a padding trit other than code 0 sets TQ_DEV_BAD_PADDING.
+ */
+int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
+              int8_t *codes, int32_t *d_status, void *stream);
+
+/*
+ * Decode GEMV / skinny matmul, 1 <= M <= 16:
+ *   y[m,n] = sum_g s[n,g] * sum_{j<G} x[m, gG+j] * c[n, gG+j]
+ * with fp32 group partials scaled by the fp16 group scale and accumulated in
+ * fp32 (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical
+ * Formulation" and "Revisit the Decode Roofline": one-token decode streams
+ * every packed weight once).
+ *   x        [M,K] bf16, 16-byte aligned
+ *   packed   [N, K/G, ceil(G/5)] bytes, 16-byte aligned
+ *   scales   [N, K/G] fp16, 2-byte aligned
+ *   y        [M,N] fp32, 4-byte aligned, overwritten
+ * Invalid packed bytes set TQ_DEV_INVALID_BYTE; their contribution is then
+ * unspecified.  Accuracy: |y - y_exact| <= 1e-3 * sum_k |x[m,k] w_hat[n,k]|.
+ */
+int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+            int64_t M, int64_t N, int64_t K, int G,
+            float *y, int32_t *d_status, void *stream);
+
+/*
+ * Prefill matmul for any M >= 1 (tuned for M >= 512): the same result as
+ * tq_gemv, computed with bf16 MFMA on dequantized code tiles (codes are exact
+ * in bf16), fp32 group partials scaled by the fp16 group scale in fp32.
+ * Source: tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical
+ * Formulation" and the decode-roofline remark that prefill reuses each
+ * weight tile across many rows and needs a matrix schedule.
+ *   x        [M,K] bf16, 16-byte aligned
+ *   packed   [N, K/G, ceil(G/5)] bytes (any alignment)
+ *   scales   [N, K/G] fp16, 2-byte aligned
+ *   y        [M,N] fp32, 4-byte aligned, overwritten
+ * Invalid packed bytes set TQ_DEV_INVALID_BYTE; their contribution is then
+ * unspecified.  Accuracy as tq_gemv.
+ */
+int tq_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+            int64_t M, int64_t N, int64_t K, int G,
+            float *y, int32_t *d_status, void *stream);
+
+#ifdef __cplusplus
+}
+#endif
+
+#endif /* TQ_H */

@@ -1,0 +1,30 @@
+"""ternary_weight_only_amd -- group-wise ternary weight quantization and the
+packed-ternary x bf16 matmul on AMD MI355X (gfx950).
+
+The work happens in libtq.so (hand-written HIP; C ABI in include/tq.h).  This
+package only marshals torch tensors to that ABI:
+
+    packed, scales = quantize_pack(w_bf16, G)      # a1-a3
+    codes          = unpack(packed, N, K, G)       # a4
+    y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
+    y              = gemm(x_bf16, packed, scales, N, K, G)   # any M
+
+torch supplies device memory and the current stream; no arithmetic of the
+method runs in Python or torch.  The library is loaded on first use and a
+missing build raises immediately; there is no CPU fallback.
+"""
+from .binding import (  # noqa: F401
+    TQError,
+    DEV_BAD_PADDING,
+    DEV_INVALID_BYTE,
+    DEV_NONFINITE,
+    DEV_SCALE_OVERFLOW,
+    check,
+    gemm,
+    gemv,
+    lib,
+    new_status,
+    packed_bytes,
+    quantize_pack,
+    unpack,
+)

@@ -1,0 +1,141 @@
+"""ctypes binding of libtq.so (C ABI: include/tq.h).
+
+Argument marshalling only: shape/dtype/device/contiguity checks on torch
+tensors, output allocation, raw device pointers and the current HIP stream.
+Every step of the computation runs in the library's kernels.
+"""
+from __future__ import annotations
+
+import ctypes
+import os
+
+import torch
+
+_PKG = os.path.dirname(os.path.abspath(__file__))
+LIB_PATH = os.path.join(_PKG, "libtq.so")
+
+DEV_NONFINITE = 1
+DEV_SCALE_OVERFLOW = 2
+DEV_INVALID_BYTE = 4
+DEV_BAD_PADDING = 8
+
+# Every symbol include/tq.h declares.
+SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_unpack",
+           "tq_gemv", "tq_gemm")
+
+_lib = None
+
+
+class TQError(RuntimeError):
+    pass
+
+
+def lib() -> ctypes.CDLL:
+    """Load libtq.so (after torch, so both share one HIP runtime)."""
+    global _lib
+    if _lib is None:
+        if not os.path.exists(LIB_PATH):
+            raise TQError("libtq.so is not built (%s); run "
+                          "`python -m ternary_weight_only_amd.build`" % LIB_PATH)
+        l = ctypes.CDLL(LIB_PATH)
+        p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
+        l.tq_status_string.argtypes = [i32]
+        l.tq_status_string.restype = ctypes.c_char_p
+        l.tq_packed_bytes.argtypes = [i64, i64, i32]
+        l.tq_packed_bytes.restype = i64
+        l.tq_quantize_pack.argtypes = [p, i64, i64, i32, p, p, p, p]
+        l.tq_quantize_pack.restype = i32
+        l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
+        l.tq_unpack.restype = i32
+        for f in (l.tq_gemv, l.tq_gemm):
+            f.argtypes = [p, p, p, i64, i64, i64, i32, p, p, p]
+            f.restype = i32
+        _lib = l
+    return _lib
+
+
+def _rc(rc: int, what: str):
+    if rc != 0:
+        raise TQError("%s failed: %s" % (what, lib().tq_status_string(rc).decode()))
+
+
+def _stream() -> int:
+    return torch.cuda.current_stream().cuda_stream
+
+
+def _dev(t: torch.Tensor, name: str, dtypes, ndim: int):
+    if not isinstance(t, torch.Tensor) or not t.is_cuda:
+        raise TQError("%s must be a device tensor" % name)
+    if t.dtype not in dtypes:
+        raise TQError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
+    if t.dim() != ndim or not t.is_contiguous():
+        raise TQError("%s must be a contiguous %d-D tensor" % (name, ndim))
+
+
+def _st(status):
+    return 0 if status is None else status.data_ptr()
+
+
+def packed_bytes(N: int, K: int, G: int) -> int:
+    return int(lib().tq_packed_bytes(N, K, G))
+
+
+def new_status(device=None) -> torch.Tensor:
+    """A zeroed device int32 status word."""
+    return torch.zeros(1, dtype=torch.int32, device=device or "cuda")
+
+
+def check(status: torch.Tensor) -> int:
+    """Synchronize-free read of a status word (forces a device->host copy)."""
+    return int(status.item())
+
+
+def quantize_pack(w: torch.Tensor, G: int, status=None, out=None):
+    """w: [N,K] bf16 -> (packed uint8 [N, (K/G)*ceil(G/5)], scales fp16 [N, K/G])."""
+    _dev(w, "w", (torch.bfloat16, torch.int16), 2)
+    N, K = w.shape
+    rb = (K // G) * ((G + 4) // 5) if G > 0 and K % G == 0 else 0
+    if out is None:
+        packed = torch.empty((N, max(rb, 1)), dtype=torch.uint8, device=w.device)
+        scales = torch.empty((N, max(K // G, 1)), dtype=torch.float16, device=w.device)
+    else:
+        packed, scales = out
+    _rc(lib().tq_quantize_pack(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
+                               _st(status), _stream()), "tq_quantize_pack")
+    return packed, scales
+
+
+def unpack(packed: torch.Tensor, N: int, K: int, G: int, status=None, out=None):
+    """packed -> codes int8 [N,K]."""
+    _dev(packed, "packed", (torch.uint8,), packed.dim())
+    if packed.numel() != packed_bytes(N, K, G):
+        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), packed_bytes(N, K, G)))
+    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device) if out is None else out
+    _rc(lib().tq_unpack(packed.data_ptr(), N, K, G, codes.data_ptr(), _st(status), _stream()),
+        "tq_unpack")
+    return codes
+
+
+def _mm(fn, name, x, packed, scales, N, K, G, status, out):
+    _dev(x, "x", (torch.bfloat16, torch.int16), 2)
+    _dev(packed, "packed", (torch.uint8,), packed.dim())
+    _dev(scales, "scales", (torch.float16, torch.int16), scales.dim())
+    M = x.shape[0]
+    if x.shape[1] != K:
+        raise TQError("x has K=%d, expected %d" % (x.shape[1], K))
+    if packed.numel() != packed_bytes(N, K, G) or scales.numel() != N * (K // G):
+        raise TQError("packed/scales sizes do not match N=%d K=%d G=%d" % (N, K, G))
+    y = torch.empty((M, N), dtype=torch.float32, device=x.device) if out is None else out
+    _rc(fn(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), M, N, K, G, y.data_ptr(),
+           _st(status), _stream()), name)
+    return y
+
+
+def gemv(x, packed, scales, N: int, K: int, G: int, status=None, out=None):
+    """y[M,N] = x[M,K] * W_hat^T for 1 <= M <= 16 (decode path)."""
+    return _mm(lib().tq_gemv, "tq_gemv", x, packed, scales, N, K, G, status, out)
+
+
+def gemm(x, packed, scales, N: int, K: int, G: int, status=None, out=None):
+    """y[M,N] = x[M,K] * W_hat^T for any M (prefill path)."""
+    return _mm(lib().tq_gemm, "tq_gemm", x, packed, scales, N, K, G, status, out)

@@ -1,0 +1,103 @@
+// tq_api.hip -- the extern "C" entry points of libtq.so (declared in
+// include/tq.h): host-side argument validation, then one launch on the
+// caller's stream.  Nothing here allocates, synchronizes or falls back to
+// another implementation; bad arguments return an error with nothing
+// enqueued (tiny-llm "Week 2 Day 3: Quantize the Model", task 3: validate the
+// layout before encoding the kernel and reject explicitly instead of
+// falling back).
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "../../include/tq.h"
+#include "tq_internal.h"
+
+namespace {
+
+bool aligned(const void *p, uintptr_t a) { return (reinterpret_cast<uintptr_t>(p) % a) == 0; }
+
+// Shape rules shared by every call: N, K >= 1, G in {64,128}, K % G == 0
+// (precisit "pack-unpack-run" README, scale-rule paragraph), and every byte
+// count below 2^62.
+int check_nkg(int64_t N, int64_t K, int G) {
+  if (G != 64 && G != 128) return TQ_ERR_GROUP;
+  if (N < 1 || K < 1 || K % G != 0) return TQ_ERR_SHAPE;
+  if (N > (int64_t(1) << 40) / K) return TQ_ERR_SHAPE;  // N*K*4 stays far below 2^62
+  return TQ_OK;
+}
+
+int finish_launch() {
+  const hipError_t e = hipGetLastError();
+  return e == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+}  // namespace
+
+extern "C" {
+
+const char *tq_status_string(int status) {
+  switch (status) {
+    case TQ_OK: return "TQ_OK";
+    case TQ_ERR_NULL: return "TQ_ERR_NULL: a required pointer is NULL";
+    case TQ_ERR_SHAPE: return "TQ_ERR_SHAPE: bad M/N/K or K not divisible by G";
+    case TQ_ERR_GROUP: return "TQ_ERR_GROUP: G must be 64 or 128";
+    case TQ_ERR_ALIGN: return "TQ_ERR_ALIGN: pointer not aligned as required";
+    case TQ_ERR_LAUNCH: return "TQ_ERR_LAUNCH: HIP launch failed";
+    default: return "unknown tq status";
+  }
+}
+
+int64_t tq_packed_bytes(int64_t N, int64_t K, int G) {
+  if (N < 1 || K < 1 || G < 1 || K % G != 0) return 0;
+  return N * (K / G) * (int64_t)((G + 4) / 5);
+}
+
+int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,
+                     uint16_t *scales, int32_t *d_status, void *stream) {
+  if (!w || !packed || !scales) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  hipGetLastError();  // clear a stale error so the check below sees only ours
+  tq::launch_quantize_pack(w, N, K, G, packed, scales, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
+              int32_t *d_status, void *stream) {
+  if (!packed || !codes) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(codes, 8) || !aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  hipGetLastError();
+  tq::launch_unpack(packed, N, K, G, codes, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
+            int64_t N, int64_t K, int G, float *y, int32_t *d_status, void *stream) {
+  if (!x || !packed || !scales || !y) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (M < 1 || M > 16) return TQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(y, 4) ||
+      !aligned(d_status, 4))
+    return TQ_ERR_ALIGN;
+  hipGetLastError();
+  tq::launch_gemv(x, packed, scales, M, N, K, G, y, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
+            int64_t N, int64_t K, int G, float *y, int32_t *d_status, void *stream) {
+  if (!x || !packed || !scales || !y) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (M < 1 || M > (int64_t(1) << 40) / K) return TQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(scales, 2) || !aligned(y, 4) || !aligned(d_status, 4))
+    return TQ_ERR_ALIGN;
+  hipGetLastError();
+  tq::launch_gemm(x, packed, scales, M, N, K, G, y, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+}  // extern "C"

@@ -1,0 +1,33 @@
+// tq_internal.h -- launchers shared between the C-ABI file and the kernel
+// files of libtq.so.  Host code only sees these declarations.
+#pragma once
+
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+namespace tq {
+
+// Device status bits (numeric values fixed by include/tq.h).
+constexpr int kDevNonfinite = 1;
+constexpr int kDevScaleOverflow = 2;
+constexpr int kDevInvalidByte = 4;
+constexpr int kDevBadPadding = 8;
+
+constexpr int bytes_per_group(int G) { return (G + 4) / 5; }
+
+void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
+                          uint8_t *packed, uint16_t *scales, int32_t *d_status,
+                          hipStream_t stream);
+
+void launch_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
+                   int8_t *codes, int32_t *d_status, hipStream_t stream);
+
+void launch_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                 int64_t M, int64_t N, int64_t K, int G, float *y,
+                 int32_t *d_status, hipStream_t stream);
+
+void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                 int64_t M, int64_t N, int64_t K, int G, float *y,
+                 int32_t *d_status, hipStream_t stream);
+
+}  // namespace tq

@@ -1,0 +1,352 @@
+// tq_quant.hip -- quantize/pack and unpack kernels for gfx950.
+//
+// Format: precisit "pack-unpack-run" README, codec.py description and
+// scale-rule paragraph: per group of G weights an fp16 scale equal to the
+// mean of |w| (one round-half-even from the exact sum), codes c = sign(w)
+// where |w| > s/2 (ties to 0), five base-3 digits (c + 1) per byte with the
+// first weight least significant, ceil(G/5) bytes per group, padding trits of
+// code 0, byte values 243..255 invalid.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+constexpr int kWave = 64;
+constexpr int kBlock = 256;
+constexpr int kWavesPerBlock = kBlock / kWave;
+
+// ---------------------------------------------------------------------------
+// fp16 rounding of a fixed-point magnitude.
+//
+// A bf16 magnitude u (sign cleared) is sig * 2^(e - 133) with sig <= 255:
+// normal E = u >> 7 >= 1 gives sig = 128 + (u & 127), e = E - 1; subnormal
+// E = 0 gives sig = u & 127, e = 0.  A group's magnitudes are summed as
+// integers sig << (e - e_max + kWin), exact while every shift is >= 0.
+// ---------------------------------------------------------------------------
+constexpr int kWin = 48;  // 128 terms of 255 << 48 stay below 2^63
+
+// Round-half-even of T / 2^r to an integer (r >= 1; T < 2^63).
+__device__ __forceinline__ uint64_t rne_shift(uint64_t T, uint32_t r) {
+  if (r >= 64) return 0;
+  const uint64_t q = T >> r;
+  const uint64_t rem = T & ((1ull << r) - 1);
+  const uint64_t half = 1ull << (r - 1);
+  return q + ((rem > half) || (rem == half && (q & 1)) ? 1 : 0);
+}
+
+// fp16 bits of RNE(T * 2^sh * 2^-24), i.e. the value T * 2^sh in units of the
+// fp16 subnormal step.  Sets *ovf and returns 0x7C00 when it rounds to >= 65520.
+__device__ __forceinline__ uint32_t f16_bits_of_fixed(uint64_t T, int sh, bool *ovf) {
+  *ovf = false;
+  if (T == 0) return 0;
+  if (sh >= 0) { *ovf = true; return 0x7C00; }  // T >= 2^55 here: far beyond 65504
+  const int r = -sh;
+  const int L = 63 - __clzll((long long)T);
+  if (L < r + 10) return (uint32_t)rne_shift(T, (uint32_t)r);  // below 1024 steps
+  const int k = L - r - 10;                                    // value in [2^(10+k), 2^(11+k))
+  if (k >= 30) { *ovf = true; return 0x7C00; }
+  const uint32_t bits = ((uint32_t)k << 10) + (uint32_t)rne_shift(T, (uint32_t)(L - 10));
+  if (bits >= 0x7C00) { *ovf = true; return 0x7C00; }
+  return bits;
+}
+
+// Exact fallback for one group: 320-bit sum of sig << e, then one rounding of
+// sum * 2^-133 / 2^t to fp16.  Only runs for groups whose fixed-point window
+// dropped bits that could change the rounding.
+__device__ __noinline__ uint32_t f16_scale_exact(const uint16_t *grp, int G, int t, bool *ovf) {
+  uint64_t A[5] = {0, 0, 0, 0, 0};
+  for (int j = 0; j < G; ++j) {
+    const uint32_t u = grp[j] & 0x7FFFu;
+    const uint32_t E = u >> 7, m = u & 0x7Fu;
+    const uint64_t sig = E ? 128u + m : m;
+    const int e = E ? (int)E - 1 : 0;
+    const int limb = e >> 6, off = e & 63;
+    const uint64_t lo = sig << off;
+    const uint64_t hi = off ? (sig >> (64 - off)) : 0;
+    uint64_t carry = 0;
+    for (int i = limb; i < 5; ++i) {
+      const uint64_t add = (i == limb) ? lo : (i == limb + 1 ? hi : 0);
+      const uint64_t s1 = A[i] + add;
+      const uint64_t c1 = s1 < add;
+      const uint64_t s2 = s1 + carry;
+      carry = c1 + (s2 < s1);
+      A[i] = s2;
+    }
+  }
+  int L = -1;
+  for (int i = 4; i >= 0 && L < 0; --i)
+    if (A[i]) L = 64 * i + 63 - __clzll((long long)A[i]);
+  *ovf = false;
+  if (L < 0) return 0;
+  // value in units of 2^-24: A / 2^(109 + t)
+  const int r = 109 + t;
+  auto bits_at = [&](int pos, int n) -> uint64_t {  // bits [pos, pos+n), n <= 32
+    uint64_t v = 0;
+    for (int b = 0; b < n; ++b) {
+      const int p = pos + b;
+      if (p >= 0 && p < 320) v |= ((A[p >> 6] >> (p & 63)) & 1ull) << b;
+    }
+    return v;
+  };
+  auto any_below = [&](int pos) -> bool {
+    for (int p = 0; p < pos && p < 320; ++p)
+      if ((A[p >> 6] >> (p & 63)) & 1ull) return true;
+    return false;
+  };
+  auto rne_at = [&](int d) -> uint64_t {  // RNE(A / 2^d), result < 2^13
+    const uint64_t q = bits_at(d, 13);
+    const bool half = bits_at(d - 1, 1) != 0;
+    const bool sticky = any_below(d - 1);
+    return q + ((half && (sticky || (q & 1))) ? 1 : 0);
+  };
+  if (L < r + 10) return (uint32_t)rne_at(r);
+  const int k = L - r - 10;
+  if (k >= 30) { *ovf = true; return 0x7C00; }
+  const uint32_t bits = ((uint32_t)k << 10) + (uint32_t)rne_at(L - 10);
+  if (bits >= 0x7C00) { *ovf = true; return 0x7C00; }
+  return bits;
+}
+
+__device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
+  return (uint32_t)__shfl_xor((int)v, mask, kWave);
+}
+
+__device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
+  const uint32_t lo = shfl_xor_u32((uint32_t)v, mask);
+  const uint32_t hi = shfl_xor_u32((uint32_t)(v >> 32), mask);
+  return ((uint64_t)hi << 32) | lo;
+}
+
+// ---------------------------------------------------------------------------
+// quantize + pack.
+// A wave handles a chunk of 512 consecutive weights (= 512/G whole groups,
+// since the flat group index n*(K/G) + g addresses w at (n*(K/G) + g) * G).
+// Each lane loads 8 bf16 with one 128-bit load; G/8 lanes share a group and
+// combine their exponent maxima, fixed-point sums and flags with xor
+// shuffles.  Digits go through LDS to be regrouped five per byte.
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
+    const uint16_t *__restrict__ w, int64_t total_groups, uint8_t *__restrict__ packed,
+    uint16_t *__restrict__ scales, int32_t *__restrict__ d_status) {
+  constexpr int LPG = G / 8;               // lanes per group
+  constexpr int GPC = 512 / G;             // groups per chunk
+  constexpr int B = bytes_per_group(G);    // bytes per group
+  constexpr int CB = GPC * B;              // bytes per chunk (104)
+  constexpr int LOG2G = (G == 64) ? 6 : 7;
+  __shared__ __align__(16) uint8_t digits_s[kWavesPerBlock][512];
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int sub = lane % LPG;
+  const int qg = lane / LPG;
+  const int64_t nchunks = (total_groups + GPC - 1) / GPC;
+
+  for (int64_t base = (int64_t)blockIdx.x * kWavesPerBlock; base < nchunks;
+       base += (int64_t)gridDim.x * kWavesPerBlock) {
+    const int64_t chunk = base + wv;
+    const int64_t gi = chunk * GPC + qg;
+    const bool active = chunk < nchunks && gi < total_groups;
+
+    uint32_t raw[4] = {0, 0, 0, 0};
+    if (active) {
+      const uint4 v = *reinterpret_cast<const uint4 *>(w + gi * G + sub * 8);
+      raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
+    }
+    uint32_t h[8];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) { h[2 * i] = raw[i] & 0xFFFFu; h[2 * i + 1] = raw[i] >> 16; }
+
+    // exponent maximum and non-finite flag over the group
+    int emax = 0;
+    uint32_t nonfinite = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t E = (h[i] >> 7) & 0xFFu;
+      nonfinite |= (E == 0xFFu);
+      const int e = E ? (int)E - 1 : 0;
+      emax = e > emax ? e : emax;
+    }
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+      const int o = (int)shfl_xor_u32((uint32_t)emax, m);
+      emax = o > emax ? o : emax;
+      nonfinite |= shfl_xor_u32(nonfinite, m);
+    }
+
+    // fixed-point sum anchored at the group's largest exponent
+    uint64_t T = 0;
+    uint32_t inexact = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t u = h[i] & 0x7FFFu;
+      const uint32_t E = u >> 7;
+      const uint64_t sig = E ? 128u + (u & 0x7Fu) : (u & 0x7Fu);
+      const int e = E ? (int)E - 1 : 0;
+      const int sh = e - emax + kWin;
+      if (sh >= 0) {
+        T += sig << sh;
+      } else if (sh > -8) {
+        T += sig >> (-sh);
+        inexact |= (sig & ((1ull << (-sh)) - 1)) != 0;
+      } else {
+        inexact |= sig != 0;
+      }
+    }
+#pragma unroll
+    for (int m = 1; m < LPG; m <<= 1) {
+      T += shfl_xor_u64(T, m);
+      inexact |= shfl_xor_u32(inexact, m);
+    }
+
+    // one rounding of the mean to fp16; the true sum lies in [T, T + G) units
+    // of 2^(emax - 181) and the mean in units of 2^-24 is that times
+    // 2^(emax - 157 - log2 G)
+    uint32_t sbits;
+    int flags = 0;
+    bool need_exact = false;
+    if (nonfinite) {
+      sbits = 0x7E00;
+      flags = kDevNonfinite;
+    } else {
+      const int sh = emax - 157 - LOG2G;
+      bool ovf;
+      sbits = f16_bits_of_fixed(T, sh, &ovf);
+      if (inexact) {
+        bool ovf2;
+        const uint32_t hi = f16_bits_of_fixed(T + (uint64_t)G, sh, &ovf2);
+        need_exact = hi != sbits;
+      }
+      if (ovf && !need_exact) flags = kDevScaleOverflow;
+    }
+    if (need_exact && active && sub == 0) {
+      bool ovf;
+      sbits = f16_scale_exact(w + gi * G, G, LOG2G, &ovf);
+      flags = ovf ? kDevScaleOverflow : 0;
+    }
+    const int leader = qg * LPG;
+    sbits = (uint32_t)__shfl((int)sbits, leader, kWave);
+    flags = __shfl(flags, leader, kWave);
+
+    // codes: |w| > s/2, compared as ordered fp32 bit patterns (exact, no
+    // denormal flushing involved); flagged groups keep all codes at 0
+    const uint32_t half_bits =
+        __float_as_uint(__half2float(__ushort_as_half((unsigned short)sbits)) * 0.5f);
+    uint64_t dig = 0;
+#pragma unroll
+    for (int i = 0; i < 8; ++i) {
+      const uint32_t mag = (h[i] & 0x7FFFu) << 16;
+      uint32_t d = 1;
+      if (!flags && mag > half_bits) d = (h[i] & 0x8000u) ? 0u : 2u;
+      dig |= (uint64_t)d << (8 * i);
+    }
+
+    __syncthreads();  // previous iteration's readers are done with digits_s
+    *reinterpret_cast<uint64_t *>(&digits_s[wv][lane * 8]) = dig;
+    __syncthreads();
+
+    // five digits per byte, base 3, first weight least significant
+#pragma unroll
+    for (int pass = 0; pass < 2; ++pass) {
+      const int j = lane + pass * kWave;
+      if (j < CB) {
+        const int q = j / B, b = j % B;
+        const int64_t gq = chunk * GPC + q;
+        if (chunk < nchunks && gq < total_groups) {
+          uint32_t byte = 0, p3 = 1;
+#pragma unroll
+          for (int i = 0; i < 5; ++i) {
+            const int pos = 5 * b + i;
+            const uint32_t d = pos < G ? digits_s[wv][q * G + pos] : 1u;
+            byte += d * p3;
+            p3 *= 3;
+          }
+          packed[gq * B + b] = (uint8_t)byte;
+        }
+      }
+    }
+    if (active && sub == 0) {
+      scales[gi] = (uint16_t)sbits;
+      if (flags && d_status) atomicOr(d_status, flags);
+    }
+  }
+}
+
+// ---------------------------------------------------------------------------
+// unpack: one thread per 8 consecutive codes of a group (one 64-bit store).
+// ---------------------------------------------------------------------------
+template <int G>
+__global__ __launch_bounds__(kBlock) void unpack_kernel(const uint8_t *__restrict__ packed,
+                                                        int64_t total_groups,
+                                                        int8_t *__restrict__ codes,
+                                                        int32_t *__restrict__ d_status) {
+  constexpr int TPG = G / 8;
+  constexpr int B = bytes_per_group(G);
+  const int64_t total = total_groups * TPG;
+  int flags = 0;
+  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total;
+       t += (int64_t)gridDim.x * kBlock) {
+    const int64_t gi = t / TPG;
+    const int p0 = (int)(t % TPG) * 8;
+    const uint8_t *pg = packed + gi * B;
+    const int b0 = p0 / 5, b1 = (p0 + 7) / 5;
+    uint64_t out = 0;
+    for (int b = b0; b <= b1; ++b) {
+      uint32_t v = pg[b];
+      const bool valid = v < 243u;
+      if (!valid) flags |= kDevInvalidByte;
+#pragma unroll
+      for (int i = 0; i < 5; ++i) {
+        const uint32_t d = v % 3u;
+        v /= 3u;
+        const int pos = 5 * b + i;
+        if (pos >= p0 && pos < p0 + 8) {
+          const uint32_t c = valid ? (uint32_t)(int8_t)((int)d - 1) & 0xFFu : 0u;
+          out |= (uint64_t)c << (8 * (pos - p0));
+        }
+        if (pos >= G && valid && d != 1u) flags |= kDevBadPadding;
+      }
+    }
+    *reinterpret_cast<uint64_t *>(codes + gi * G + p0) = out;
+  }
+  if (flags && d_status) atomicOr(d_status, flags);
+}
+
+int grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
+  int64_t g = (work_items + per_block - 1) / per_block;
+  if (g < 1) g = 1;
+  return (int)(g < cap ? g : cap);
+}
+
+}  // namespace
+
+void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,
+                          uint16_t *scales, int32_t *d_status, hipStream_t stream) {
+  const int64_t total_groups = N * (K / G);
+  const int64_t nchunks = (total_groups * G + 511) / 512;
+  const int grid = grid_for(nchunks, kWavesPerBlock, 8192);
+  if (G == 64)
+    hipLaunchKernelGGL(quantize_pack_kernel<64>, dim3(grid), dim3(kBlock), 0, stream, w,
+                       total_groups, packed, scales, d_status);
+  else
+    hipLaunchKernelGGL(quantize_pack_kernel<128>, dim3(grid), dim3(kBlock), 0, stream, w,
+                       total_groups, packed, scales, d_status);
+}
+
+void launch_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
+                   int32_t *d_status, hipStream_t stream) {
+  const int64_t total_groups = N * (K / G);
+  const int grid = grid_for(total_groups * (G / 8), kBlock, 16384);
+  if (G == 64)
+    hipLaunchKernelGGL(unpack_kernel<64>, dim3(grid), dim3(kBlock), 0, stream, packed,
+                       total_groups, codes, d_status);
+  else
+    hipLaunchKernelGGL(unpack_kernel<128>, dim3(grid), dim3(kBlock), 0, stream, packed,
+                       total_groups, codes, d_status);
+}
+
+}  // namespace tq

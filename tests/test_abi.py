@@ -1,0 +1,97 @@
+"""The C-ABI library loads and exports what include/tq.h declares; host-side
+argument checks return their error codes before anything reaches the GPU.
+
+No test here launches a kernel: every call below is rejected by the host-side
+validation in tq_api.hip, which runs before any HIP call.
+"""
+import ctypes
+import os
+import re
+
+import pytest
+
+ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
+HEADER = os.path.join(ROOT, "include", "tq.h")
+
+
+def _lib():
+    import ternary_weight_only_amd as tq
+    if not os.path.exists(tq.binding.LIB_PATH):
+        from ternary_weight_only_amd import build
+        build.build_library()
+    return tq.lib()
+
+
+def declared_functions():
+    text = open(HEADER).read()
+    text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
+    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+
+
+def test_header_declares_the_four_entry_points():
+    names = declared_functions()
+    for f in ("tq_quantize_pack", "tq_unpack", "tq_gemv", "tq_gemm"):
+        assert f in names
+
+
+def test_library_exports_every_declared_symbol():
+    lib = _lib()
+    for name in declared_functions():
+        assert hasattr(lib, name), name
+    import ternary_weight_only_amd.binding as b
+    assert sorted(b.SYMBOLS) == declared_functions()
+
+
+def test_packed_bytes_helper():
+    lib = _lib()
+    assert lib.tq_packed_bytes(256, 512, 64) == 256 * 8 * 13
+    assert lib.tq_packed_bytes(256, 320, 64) == 256 * 65
+    assert lib.tq_packed_bytes(3584, 1024, 128) == 3584 * 8 * 26
+    assert lib.tq_packed_bytes(1, 100, 64) == 0
+    assert lib.tq_packed_bytes(0, 128, 64) == 0
+
+
+FAKE = 0x100000  # never dereferenced: every call below fails validation first
+
+
+@pytest.mark.parametrize("fn", ["tq_gemv", "tq_gemm"])
+def test_matmul_argument_errors(fn):
+    lib = _lib()
+    f = getattr(lib, fn)
+    assert f(None, FAKE, FAKE, 1, 8, 128, 64, FAKE, None, None) == -1      # NULL
+    assert f(FAKE, FAKE, FAKE, 1, 8, 100, 64, FAKE, None, None) == -2      # K % G
+    assert f(FAKE, FAKE, FAKE, 1, 0, 128, 64, FAKE, None, None) == -2      # N < 1
+    assert f(FAKE, FAKE, FAKE, 0, 8, 128, 64, FAKE, None, None) == -2      # M < 1
+    assert f(FAKE, FAKE, FAKE, 1, 8, 96, 32, FAKE, None, None) == -3       # G
+    assert f(FAKE + 2, FAKE, FAKE, 1, 8, 128, 64, FAKE, None, None) == -4  # x alignment
+    assert f(FAKE, FAKE, FAKE + 1, 1, 8, 128, 64, FAKE, None, None) == -4  # scales
+    assert f(FAKE, FAKE, FAKE, 1, 8, 128, 64, FAKE + 2, None, None) == -4  # y
+    if fn == "tq_gemv":
+        assert f(FAKE, FAKE, FAKE, 17, 8, 128, 64, FAKE, None, None) == -2  # M > 16
+        assert f(FAKE, FAKE + 8, FAKE, 1, 8, 128, 64, FAKE, None, None) == -4
+
+
+def test_quantize_unpack_argument_errors():
+    lib = _lib()
+    q, u = lib.tq_quantize_pack, lib.tq_unpack
+    assert q(None, 4, 128, 64, FAKE, FAKE, None, None) == -1
+    assert q(FAKE, 4, 130, 64, FAKE, FAKE, None, None) == -2
+    assert q(FAKE, 4, 128, 5, FAKE, FAKE, None, None) == -3
+    assert q(FAKE + 2, 4, 128, 64, FAKE, FAKE, None, None) == -4
+    assert q(FAKE, 4, 128, 64, FAKE, FAKE + 1, None, None) == -4
+    assert q(FAKE, 4, 128, 64, FAKE, FAKE, FAKE + 1, None) == -4
+    assert u(None, 4, 128, 64, FAKE, None, None) == -1
+    assert u(FAKE, 4, 128, 64, FAKE + 4, None, None) == -4
+    assert u(FAKE, 4, 128, 48, FAKE, None, None) == -3
+    for rc in (0, -1, -2, -3, -4, -5):
+        assert lib.tq_status_string(rc)
+
+
+def test_product_path_does_not_import_oracle():
+    pkg = os.path.join(ROOT, "ternary_weight_only_amd")
+    for dirpath, _, files in os.walk(pkg):
+        for fname in files:
+            if fname.endswith((".py", ".hip", ".h", ".cpp")):
+                text = open(os.path.join(dirpath, fname)).read()
+                assert "import oracle" not in text and "from oracle" not in text, fname
+                assert "tq_oracle" not in text and "liboracle" not in text, fname

@@ -1,0 +1,163 @@
+"""GPU parity: the HIP path through the C ABI against the CPU oracle.
+
+Bar: packed bytes, scales, codes and status bits bit-exact; matmul outputs
+within |y - y_ref| <= 1e-3 * sum_k |x_k w_hat_k| per element (y_ref fp64);
+one-hot activations bit-exact.
+"""
+import itertools
+
+import numpy as np
+import pytest
+
+import oracle
+from ternary_weight_only_amd import inputs
+from tests.gpu_helpers import (assert_within_bound, check_quantize_exact, gpu_matmul,
+                               gpu_quantize, gpu_unpack, say)
+
+pytestmark = pytest.mark.gpu
+
+
+@pytest.mark.parametrize("K,G", [(512, 64), (320, 64), (512, 128)])
+def test_small_matrix_quantize_unpack_exact(K, G):
+    w = inputs.small_matrix(K=K)
+    say("small matrix W[256,%d] G=%d seed 0: quantize_pack, unpack" % (K, G))
+    p, s = check_quantize_exact(w, G, "W[256,%d] G=%d" % (K, G))
+    codes_gpu, st = gpu_unpack(p, 256, K, G)
+    codes_ref, st_ref = oracle.unpack(p, 256, K, G)
+    assert st == st_ref == 0
+    assert np.array_equal(codes_gpu, codes_ref)
+
+
+@pytest.mark.parametrize("K,G", [(512, 64), (320, 64), (512, 128)])
+@pytest.mark.parametrize("kind,M", [("gemv", 1), ("gemv", 8), ("gemv", 3), ("gemv", 10),
+                                    ("gemv", 16), ("gemm", 1), ("gemm", 8), ("gemm", 128),
+                                    ("gemm", 513)])
+def test_small_matrix_matmul(K, G, kind, M):
+    w = inputs.small_matrix(K=K)
+    p, s, _ = oracle.quantize_pack(w, G)
+    x = inputs.activation(1 if M == 1 else 2, M, K)
+    say("%s M=%d W[256,%d] G=%d" % (kind, M, K, G))
+    y, st = gpu_matmul(kind, x, p, s, 256, K, G)
+    y_ref, bound, _ = oracle.matmul(x, p, s, 256, K, G)
+    assert st == 0
+    assert_within_bound(y, y_ref, bound, "%s M=%d K=%d G=%d" % (kind, M, K, G))
+
+
+@pytest.mark.parametrize("kind", ["gemv", "gemm"])
+@pytest.mark.parametrize("G", [64, 128])
+def test_one_hot_activations_exact(kind, G):
+    """x = e_k gives y[n] = c[n,k] * s[n,k/G] exactly: pins K indexing, digit
+    order within a byte and the group -> scale mapping bit for bit."""
+    N, K = 250, 1024
+    w = inputs.normal_bf16(31, (N, K), 0.02)
+    p, s, _ = oracle.quantize_pack(w, G)
+    codes, _ = oracle.unpack(p, N, K, G)
+    ks = [0, 1, 2, 3, 4, 5, 6, 63, 64, 65, 127, 128, 500, 1023, 640, 641, 642, 643, 644, 645]
+    ks = ks[:16]
+    x = np.zeros((len(ks), K), np.uint16)
+    for i, k in enumerate(ks):
+        x[i, k] = 0x3F80
+    say("one-hot %s G=%d N=%d K=%d" % (kind, G, N, K))
+    y, _ = gpu_matmul(kind, x, p, s, N, K, G)
+    sf = s.view(np.float16).astype(np.float32)
+    for i, k in enumerate(ks):
+        want = codes[:, k].astype(np.float32) * sf[:, k // G]
+        assert np.array_equal(y[i], want), (kind, k)
+
+
+def test_ones_times_single_group_exact():
+    """x = ones, W nonzero in one group: y = s * sum(c) exactly."""
+    N, K, G = 64, 512, 128
+    w = np.zeros((N, K), np.uint16)
+    w[:, 256:384] = inputs.normal_bf16(32, (N, 128), 0.02)
+    p, s, _ = oracle.quantize_pack(w, G)
+    codes, _ = oracle.unpack(p, N, K, G)
+    x = np.full((2, K), 0x3F80, np.uint16)
+    for kind in ("gemv", "gemm"):
+        y, _ = gpu_matmul(kind, x, p, s, N, K, G)
+        want = codes[:, 256:384].sum(1).astype(np.float32) * s[:, 2].view(np.float16).astype(np.float32)
+        assert np.array_equal(y[0], want) and np.array_equal(y[1], want)
+
+
+def _random_finite_bf16(rng, n, emin, emax):
+    sign = rng.integers(0, 2, n).astype(np.uint16) << 15
+    e = rng.integers(emin, emax + 1, n).astype(np.uint16) << 7
+    m = rng.integers(0, 128, n).astype(np.uint16)
+    return sign | e | m
+
+
+def _bf16(v):
+    return int(inputs.f32_to_bf16_bits(np.array([v], np.float32))[0])
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_quantize_stress_groups_exact(G):
+    """Groups built to break a windowed or floating-point sum: exponents over
+    ~140 binades, bf16 subnormals, fp16 midpoints with and without a 2^-100
+    excess, overflow and non-finite groups."""
+    rng = np.random.default_rng(33)
+    rows = [
+        _random_finite_bf16(rng, 64 * G, 0, 140).reshape(64, G),
+        _random_finite_bf16(rng, 64 * G, 90, 120).reshape(64, G),
+        _random_finite_bf16(rng, 64 * G, 0, 10).reshape(64, G),
+        _random_finite_bf16(rng, 64 * G, 126, 145).reshape(64, G),
+    ]
+    special = np.zeros((8, G), np.uint16)
+    # exact fp16 midpoint (ties to even) and the same plus 2^-100 (rounds up)
+    # sum = G * (1 + 2^-11): mean on the midpoint of 0x3C00 / 0x3C01
+    half = G // 2
+    special[0, :half] = _bf16(2.0)
+    special[0, half] = _bf16(G * 2.0 ** -11)
+    special[1] = special[0]
+    special[1, half + 1] = _bf16(2.0 ** -100)
+    special[2, :] = _bf16(7e4)               # overflow
+    special[3, :] = _bf16(2.0 ** -30)        # underflow to 0
+    special[4, :] = inputs.normal_bf16(34, (G,), 0.02)
+    special[4, 3] = 0x7FC1                   # NaN
+    special[5, :] = _bf16(1.0)
+    special[5, 7] = 0xFF80                   # -inf
+    special[6, :] = _bf16(2.0 ** -133 * 5)   # smallest subnormals
+    special[7, :] = _bf16(65504.0 / 2)
+    w = np.concatenate(rows + [special])
+    say("quantize stress G=%d rows=%d" % (G, w.shape[0]))
+    check_quantize_exact(w, G, "stress G=%d" % G)
+
+
+def test_unpack_flags_invalid_and_padding():
+    N, K, G = 16, 256, 64
+    w = inputs.normal_bf16(35, (N, K), 0.02)
+    p, s, _ = oracle.quantize_pack(w, G)
+    bad = p.copy()
+    bad[3, 5] = 250
+    codes, st = gpu_unpack(bad, N, K, G)
+    codes_ref, st_ref = oracle.unpack(bad, N, K, G)
+    assert st == st_ref == 4 and np.array_equal(codes, codes_ref)
+    pad = p.copy()
+    pad[7, 12] = pad[7, 12] + 81 if pad[7, 12] < 162 else pad[7, 12] - 81
+    codes, st = gpu_unpack(pad, N, K, G)
+    codes_ref, st_ref = oracle.unpack(pad, N, K, G)
+    assert st == st_ref == 8 and np.array_equal(codes, codes_ref)
+    for kind in ("gemv", "gemm"):
+        x = inputs.activation(36, 2, K)
+        _, st = gpu_matmul(kind, x, bad, s, N, K, G)
+        assert st & 4
+
+
+def test_quantize_deterministic_and_repeatable():
+    w = inputs.normal_bf16(37, (1000, 3584), 0.02)
+    a = gpu_quantize(w, 128)
+    b = gpu_quantize(w, 128)
+    assert all(np.array_equal(u, v) for u, v in zip(a[:2], b[:2])) and a[2] == b[2]
+
+
+@pytest.mark.parametrize("N,K,G", [(1, 64, 64), (1, 128, 128), (7, 192, 64), (3, 384, 128)])
+def test_degenerate_shapes(N, K, G):
+    w = inputs.normal_bf16(38, (N, K), 0.02)
+    p, s = check_quantize_exact(w, G, "N=%d K=%d G=%d" % (N, K, G))
+    codes, st = gpu_unpack(p, N, K, G)
+    assert np.array_equal(codes, oracle.unpack(p, N, K, G)[0])
+    for kind, M in itertools.product(("gemv", "gemm"), (1, 5)):
+        x = inputs.activation(39, M, K)
+        y, st = gpu_matmul(kind, x, p, s, N, K, G)
+        y_ref, bound, _ = oracle.matmul(x, p, s, N, K, G)
+        assert_within_bound(y, y_ref, bound, "%s N=%d K=%d G=%d M=%d" % (kind, N, K, G, M))
