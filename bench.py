@@ -1,0 +1,266 @@
+"""Benchmark of the ternary hot path on one MI355X.
+
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--G 128] [--prefill-m 512]
+
+Workload: the 24-layer Qwen-like FFN stack (hidden 1024, intermediate 3584:
+gate and up W[3584,1024], down W[1024,3584]; 72 matrices, 264,241,152 bf16
+weights ~ N(0, 0.02)), G = 128.  One step is one pass of every step of the
+hot path over that stack, in this order:
+  a5  decode GEMV, M = 1, through all 72 matrices          (tq_gemv)
+  a6  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm)
+  a1-a3 quantize + pack all 72 bf16 matrices                (tq_quantize_pack)
+  a4  unpack + validate all 72 packed matrices              (tq_unpack)
+The packed weights live in a ring of three slots; step t reads slot t%3 and
+packs into slot (t+2)%3, so the weights a GEMV reads were written two steps
+(over 2 GB of traffic) earlier and come from HBM, not from the caches.
+Each row's 72 launches are captured in a HIP graph; HIP events between the
+graph replays time each row on the stream the kernels run on.
+
+`value` is the decode GEMV's packed-weight bandwidth: (packed code bytes +
+fp16 scale bytes of the 72 matrices) / GEMV time per step.  The JSON line
+also carries every row's throughput, the roofline entry of the GEMV kernel
+and the CPU oracle's rate on a bounded sample of the same GEMV workload.
+"""
+from __future__ import annotations
+
+import argparse
+import json
+import os
+import sys
+import time
+
+ROOT = os.path.dirname(os.path.abspath(__file__))
+if ROOT not in sys.path:
+    sys.path.insert(0, ROOT)
+
+HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
+MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
+METRIC = "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
+
+
+def parse():
+    ap = argparse.ArgumentParser()
+    ap.add_argument("--gpus", type=int, default=1)
+    ap.add_argument("--steps", type=int, default=20)
+    ap.add_argument("--warmup", type=int, default=3)
+    ap.add_argument("--G", type=int, default=128)
+    ap.add_argument("--prefill-m", type=int, default=512)
+    ap.add_argument("--no-cpu-baseline", action="store_true")
+    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    return ap.parse_args()
+
+
+def gen_weights():
+    """The 72 bf16 weight matrices (seeded; generated in parallel processes)."""
+    from concurrent.futures import ProcessPoolExecutor
+    from ternary_weight_only_amd import inputs
+    jobs = [(l, p) for l in range(24) for p in range(3)]
+    workers = min(16, os.cpu_count() or 1)
+    with ProcessPoolExecutor(max_workers=workers) as ex:
+        return list(ex.map(_gen_one, jobs))
+
+
+def _gen_one(job):
+    from ternary_weight_only_amd import inputs
+    return inputs.ffn_weight(job[0], job[1])
+
+
+def cpu_baseline(mats, x_dec, G, seconds):
+    """The CPU oracle (unchanged) on a bounded sample of the GEMV workload:
+    whole passes of fp64 GEMV through the 72 packed matrices, on one core."""
+    import oracle
+    packed = [oracle.quantize_pack(w, G)[:2] for w in mats]
+    nbytes = sum(p.nbytes + s.nbytes for p, s in packed)
+    t0 = time.perf_counter()
+    passes = 0
+    while True:
+        for (p, s), w, x in zip(packed, mats, x_dec):
+            N, K = w.shape
+            oracle.matmul(x, p, s, N, K, G)
+        passes += 1
+        el = time.perf_counter() - t0
+        if el >= seconds:
+            break
+    return {"value": nbytes * passes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
+            "sample": "%d full passes of M=1 fp64 GEMV through the 72-matrix FFN stack (G=%d), "
+                      "single thread, %.1f s" % (passes, G, el)}
+
+
+def main():
+    args = parse()
+    if args.gpus != 1:
+        print("bench.py runs on one GPU only; --gpus %d is not supported (no multi-GPU path is "
+              "built)" % args.gpus, file=sys.stderr)
+        sys.exit(2)
+
+    import numpy as np
+    import torch
+
+    import ternary_weight_only_amd as tq
+    from ternary_weight_only_amd import inputs
+    from ternary_weight_only_amd.binding import lib
+
+    G, MP = args.G, args.prefill_m
+    dev = torch.device("cuda:0")
+    torch.cuda.set_device(dev)
+    L = lib()
+
+    mats = gen_weights()
+    shapes = [w.shape for w in mats]
+    x_dec_host = [inputs.activation(5000 + i, 1, K) for i, (N, K) in enumerate(shapes)]
+
+    def bf16(a):
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
+
+    w_dev = [bf16(w) for w in mats]
+    x_dec = [bf16(x) for x in x_dec_host]
+    x_pre = {K: bf16(inputs.activation(30 + K, MP, K)) for K in sorted({k for _, k in shapes})}
+    RING = 3
+    P = [[torch.empty(tq.packed_bytes(N, K, G), dtype=torch.uint8, device=dev) for N, K in shapes]
+         for _ in range(RING)]
+    S = [[torch.empty(N * (K // G), dtype=torch.float16, device=dev) for N, K in shapes]
+         for _ in range(RING)]
+    y_dec = [torch.empty(1, N, dtype=torch.float32, device=dev) for N, K in shapes]
+    y_pre = {N: torch.empty(MP, N, dtype=torch.float32, device=dev) for N, _ in shapes}
+    codes = [torch.empty(N, K, dtype=torch.int8, device=dev) for N, K in shapes]
+    status = tq.new_status(dev)
+    stp = status.data_ptr()
+
+    def run_quant(slot, stream):
+        for i, (N, K) in enumerate(shapes):
+            rc = L.tq_quantize_pack(w_dev[i].data_ptr(), N, K, G, P[slot][i].data_ptr(),
+                                    S[slot][i].data_ptr(), stp, stream)
+            assert rc == 0, rc
+
+    def run_unpack(slot, stream):
+        for i, (N, K) in enumerate(shapes):
+            rc = L.tq_unpack(P[slot][i].data_ptr(), N, K, G, codes[i].data_ptr(), stp, stream)
+            assert rc == 0, rc
+
+    def run_gemv(slot, stream):
+        for i, (N, K) in enumerate(shapes):
+            rc = L.tq_gemv(x_dec[i].data_ptr(), P[slot][i].data_ptr(), S[slot][i].data_ptr(), 1, N,
+                           K, G, y_dec[i].data_ptr(), stp, stream)
+            assert rc == 0, rc
+
+    def run_gemm(slot, stream):
+        for i, (N, K) in enumerate(shapes):
+            rc = L.tq_gemm(x_pre[K].data_ptr(), P[slot][i].data_ptr(), S[slot][i].data_ptr(), MP, N,
+                           K, G, y_pre[N].data_ptr(), stp, stream)
+            assert rc == 0, rc
+
+    # fill every ring slot, then check slot 0 against the oracle on sampled rows
+    s0 = torch.cuda.current_stream().cuda_stream
+    for slot in range(RING):
+        run_quant(slot, s0)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    import oracle
+    for i in (0, 2, 71):
+        N, K = shapes[i]
+        rows = np.array([0, 1, N // 2, N - 1])
+        p_ref, s_ref, _ = oracle.quantize_pack(mats[i][rows], G)
+        p = P[0][i].view(N, -1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
+        assert np.array_equal(p, p_ref), "bench inputs: packed bytes differ from the oracle"
+
+    # one graph per (row, slot); all rows run on one side stream
+    stream = torch.cuda.Stream()
+    graphs = {}
+    for name, fn in (("gemv", run_gemv), ("gemm", run_gemm), ("quant", run_quant),
+                     ("unpack", run_unpack)):
+        for slot in range(RING):
+            g = torch.cuda.CUDAGraph()
+            with torch.cuda.graph(g, stream=stream):
+                fn(slot, torch.cuda.current_stream().cuda_stream)
+            graphs[(name, slot)] = g
+    torch.cuda.synchronize()
+
+    order = ("gemv", "gemm", "quant", "unpack")
+
+    def step(t, evs=None):
+        rd, wr = t % RING, (t + 2) % RING
+        slots = {"gemv": rd, "gemm": rd, "quant": wr, "unpack": wr}
+        with torch.cuda.stream(stream):
+            if evs is not None:
+                evs[0].record(stream)
+            for j, name in enumerate(order):
+                graphs[(name, slots[name])].replay()
+                if evs is not None:
+                    evs[j + 1].record(stream)
+
+    for t in range(args.warmup):
+        step(t)
+    torch.cuda.synchronize()
+    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+           for _ in range(args.steps)]
+    t_start = time.perf_counter()
+    for t in range(args.steps):
+        step(args.warmup + t, evs[t])
+    torch.cuda.synchronize()
+    wall = time.perf_counter() - t_start
+    assert int(status.item()) == 0, "device status %d" % int(status.item())
+
+    per = {name: 0.0 for name in order}
+    total_ms = 0.0
+    for t in range(args.steps):
+        for j, name in enumerate(order):
+            per[name] += evs[t][j].elapsed_time(evs[t][j + 1])
+        total_ms += evs[t][0].elapsed_time(evs[t][-1])
+    per = {k: v / args.steps for k, v in per.items()}
+    ms_per_step = total_ms / args.steps
+
+    packed_bytes = sum(P[0][i].numel() + 2 * S[0][i].numel() for i in range(len(shapes)))
+    weights = sum(N * K for N, K in shapes)
+    gemm_flops = sum(2.0 * MP * N * K for N, K in shapes)
+    gemv_gbs = packed_bytes / (per["gemv"] * 1e-3) / 1e9
+    gemm_tflops = gemm_flops / (per["gemm"] * 1e-3) / 1e12
+    quant_bytes = weights * 2 + packed_bytes
+    unpack_bytes = packed_bytes + weights
+    launch_ms = per["gemv"] / len(shapes)
+    rows = {
+        "a5_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
+                    "launches": len(shapes), "bytes_per_step": packed_bytes},
+        "a6_gemm": {"ms": per["gemm"], "TFLOP/s": gemm_tflops,
+                    "frac_mfma": gemm_tflops / MFMA_BF16_PEAK_TFLOPS, "M": MP,
+                    "flop_per_step": gemm_flops},
+        "a1_a3_quantize_pack": {"ms": per["quant"],
+                                "GB/s": quant_bytes / (per["quant"] * 1e-3) / 1e9,
+                                "bytes_per_step": quant_bytes},
+        "a4_unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
+                      "bytes_per_step": unpack_bytes},
+    }
+    out = {
+        "metric": METRIC,
+        "value": round(gemv_gbs, 2),
+        "unit": "GB/s",
+        "n_gpus": 1,
+        "steps": args.steps,
+        "warmup": args.warmup,
+        "ms_per_step": round(ms_per_step, 4),
+        "higher_is_better": True,
+        "scaling": "weak",
+        "vs_baseline": None,
+        "dtype": "bf16",
+        "data": "synthetic",
+        "config": {"workload": "qwen-like FFN stack: 24 layers x {gate,up W[3584,1024], down "
+                               "W[1024,3584]}, G=%d; decode GEMV M=1 + prefill GEMM M=%d + "
+                               "quantize/pack + unpack per step" % (G, MP),
+                   "G": G, "matrices": len(shapes), "weights": weights, "decode_M": 1,
+                   "prefill_M": MP, "parallelism": "single GPU"},
+        "roofline": {"kernel": "tq_gemv", "bound": "hbm",
+                     "achieved": round(packed_bytes / len(shapes) / (launch_ms * 1e-3) / 1e9, 2),
+                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
+                     "frac": round(packed_bytes / len(shapes) / (launch_ms * 1e-3) / 1e9
+                                   / HBM_PEAK_GBS, 4),
+                     "traffic": None,
+                     "avg_launch_us": round(launch_ms * 1e3, 3)},
+        "rows": rows,
+        "wall_s_timed": round(wall, 4),
+    }
+    if not args.no_cpu_baseline:
+        out["cpu_baseline"] = cpu_baseline(mats, x_dec_host, G, args.cpu_seconds)
+    print(json.dumps(out), flush=True)
+
+
+if __name__ == "__main__":
+    main()
