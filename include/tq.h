@@ -123,6 +123,25 @@ int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
             float *y, int32_t *d_status, void *stream);
 
 /*
+ * Batched decode GEMV: `count` independent problems of the same shape, each
+ * exactly as tq_gemv(xs[i], packeds[i], scales[i], M, N, K, G, ys[i]), run in
+ * as few launches as possible (one per 64 problems) so that a stack of small
+ * matrices -- e.g. the same projection of every layer of a decoder -- streams
+ * its packed weights without a kernel launch per matrix.
+ *   xs, packeds, scales, ys   HOST arrays of `count` DEVICE pointers, with
+ *                             the layouts and alignments of tq_gemv; read
+ *                             during the call only
+ *   count >= 0                (0 enqueues nothing)
+ * The outputs ys[i] must not overlap each other or any input.  Errors and
+ * device status as tq_gemv; a NULL or misaligned pointer in any entry rejects
+ * the whole call with nothing enqueued.
+ */
+int tq_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys,
+                    int64_t M, int64_t N, int64_t K, int G,
+                    int32_t *d_status, void *stream);
+
+/*
  * Prefill matmul for any M >= 1 (tuned for M >= 512): the same result as
  * tq_gemv, computed with bf16 MFMA on dequantized code tiles (codes are exact
  * in bf16), fp32 group partials scaled by the fp16 group scale in fp32.

@@ -7,6 +7,7 @@ package only marshals torch tensors to that ABI:
     packed, scales = quantize_pack(w_bf16, G)      # a1-a3
     codes          = unpack(packed, N, K, G)       # a4
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
+    ys             = gemv_batched(xs, packeds, scales, N, K, G)  # many same-shaped
     y              = gemm(x_bf16, packed, scales, N, K, G)   # any M
 
 torch supplies device memory and the current stream; no arithmetic of the
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     check,
     gemm,
     gemv,
+    gemv_batched,
     lib,
     new_status,
     packed_bytes,

@@ -71,6 +71,23 @@ def test_matmul_argument_errors(fn):
         assert f(FAKE, FAKE + 8, FAKE, 1, 8, 128, 64, FAKE, None, None) == -4
 
 
+def test_gemv_batched_argument_errors():
+    lib = _lib()
+    arr = ctypes.c_void_p * 2
+    good = arr(FAKE, FAKE + 4096)
+    bad_al = arr(FAKE, FAKE + 4)
+    nul = arr(FAKE, None)
+    f = lib.tq_gemv_batched
+    assert f(0, None, None, None, None, 1, 8, 128, 64, None, None) == 0      # nothing to do
+    assert f(-1, good, good, good, good, 1, 8, 128, 64, None, None) == -2
+    assert f(2, None, good, good, good, 1, 8, 128, 64, None, None) == -1
+    assert f(2, nul, good, good, good, 1, 8, 128, 64, None, None) == -1
+    assert f(2, good, good, good, good, 1, 8, 100, 64, None, None) == -2
+    assert f(2, good, good, good, good, 17, 8, 128, 64, None, None) == -2
+    assert f(2, good, good, good, good, 1, 8, 96, 32, None, None) == -3
+    assert f(2, bad_al, good, good, good, 1, 8, 128, 64, None, None) == -4
+
+
 def test_quantize_unpack_argument_errors():
     lib = _lib()
     q, u = lib.tq_quantize_pack, lib.tq_unpack

@@ -122,3 +122,29 @@ def test_8b_class_ffn_batched_gemv(shape):
         x = inputs.activation((50 if N > K else 53) + i, M, K)
         _check_gemv_rows("gemv", x, packed, scales, p_ref, s_ref, N, K, G, rows,
                          "8B W[%d,%d] M=%d" % (N, K, M))
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_ffn_stack_batched_decode(G):
+    """The 72-matrix stack decoded with two batched calls (48 gate/up matrices
+    with K=1024, 24 down matrices with K=3584); sampled rows of every matrix
+    checked against the oracle."""
+    shapes = inputs.ffn_shapes()
+    for group in ((0, 1), (2,)):
+        _, N, K = shapes[group[0]]
+        mats = [(l, p) for l in range(24) for p in group]
+        ws = [inputs.ffn_weight(l, p) for l, p in mats]
+        xs = [inputs.activation(5000 + 3 * l + p, 1, K) for l, p in mats]
+        say("batched stack decode K=%d G=%d count=%d" % (K, G, len(mats)))
+        qs = [_quantize_dev(w, G) for w in ws]
+        st = tq.new_status()
+        ys = tq.gemv_batched([dev_bf16(x) for x in xs], [q[0] for q in qs], [q[1] for q in qs],
+                             N, K, G, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) == 0
+        for i, (l, p) in enumerate(mats):
+            rows = _sample_rows(N, 24, 7000 + i)
+            p_ref, s_ref, _ = oracle.quantize_pack(ws[i][rows], G)
+            y_ref, bound, _ = oracle.matmul(xs[i], p_ref, s_ref, len(rows), K, G)
+            assert_within_bound(ys[i].cpu().numpy()[:, rows], y_ref, bound,
+                                "batched stack layer %d proj %d" % (l, p))

@@ -161,3 +161,32 @@ def test_degenerate_shapes(N, K, G):
         y, st = gpu_matmul(kind, x, p, s, N, K, G)
         y_ref, bound, _ = oracle.matmul(x, p, s, N, K, G)
         assert_within_bound(y, y_ref, bound, "%s N=%d K=%d G=%d M=%d" % (kind, N, K, G, M))
+
+
+@pytest.mark.parametrize("N,K,G,count", [(256, 512, 64, 5), (250, 1024, 128, 3), (96, 320, 64, 70),
+                                         (100, 3584, 128, 2), (40, 14336, 128, 2), (33, 4096, 64, 4)])
+def test_gemv_batched_matches_oracle(N, K, G, count):
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
+    ws = [inputs.normal_bf16(300 + i, (N, K), 0.02) for i in range(count)]
+    xs = [inputs.activation(400 + i, 1, K) for i in range(count)]
+    refs = [oracle.quantize_pack(w, G) for w in ws]
+    say("gemv_batched N=%d K=%d G=%d count=%d" % (N, K, G, count))
+    st = tq.new_status()
+    ys = tq.gemv_batched([dev_bf16(x) for x in xs], [dev_u8(p) for p, _, _ in refs],
+                         [dev_f16bits(s) for _, s, _ in refs], N, K, G, status=st)
+    import torch
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for i in range(count):
+        p, s, _ = refs[i]
+        y_ref, bound, _ = oracle.matmul(xs[i], p, s, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "batched item %d" % i)
+    # an invalid byte in one problem is reported
+    bad = refs[count - 1][0].copy()
+    bad[0, 0] = 247
+    st = tq.new_status()
+    tq.gemv_batched([dev_bf16(xs[0])], [dev_u8(bad)], [dev_f16bits(refs[count - 1][1])], N, K, G,
+                    status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 4
