@@ -8,13 +8,14 @@ weights ~ N(0, 0.02)), G = 128.  One step is one pass of every step of the
 hot path over that stack, in this order:
   a5  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_batched:
       one launch for the 48 K=1024 matrices, one for the 24 K=3584 ones)
-  a6  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm)
+  a6  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
+      likewise two launches; each matrix has its own activations' output)
   a1-a3 quantize + pack all 72 bf16 matrices                (tq_quantize_pack)
   a4  unpack + validate all 72 packed matrices              (tq_unpack)
 The packed weights live in a ring of three slots; step t reads slot t%3 and
 packs into slot (t+2)%3, so the weights a GEMV reads were written two steps
 (over 2 GB of traffic) earlier and come from HBM, not from the caches.
-Each row's 72 launches are captured in a HIP graph; HIP events between the
+Each row's launches are captured in a HIP graph; HIP events between the
 graph replays time each row on the stream the kernels run on.
 
 `value` is the decode GEMV's packed-weight bandwidth: (packed code bytes +
@@ -123,7 +124,6 @@ def main():
     S = [[torch.empty(N * (K // G), dtype=torch.float16, device=dev) for N, K in shapes]
          for _ in range(RING)]
     y_dec = [torch.empty(1, N, dtype=torch.float32, device=dev) for N, K in shapes]
-    y_pre = {N: torch.empty(MP, N, dtype=torch.float32, device=dev) for N, _ in shapes}
     codes = [torch.empty(N, K, dtype=torch.int8, device=dev) for N, K in shapes]
     status = tq.new_status(dev)
     stp = status.data_ptr()
@@ -155,10 +155,17 @@ def main():
             rc = L.tq_gemv_batched(len(idx), ax, ap, asc, ay, 1, N, K, G, stp, stream)
             assert rc == 0, rc
 
+    # the prefill pass: likewise two batched calls, each problem with its own
+    # output (the activations of a K are shared)
+    y_pre = [torch.empty(MP, N, dtype=torch.float32, device=dev) for N, K in shapes]
+
     def run_gemm(slot, stream):
-        for i, (N, K) in enumerate(shapes):
-            rc = L.tq_gemm(x_pre[K].data_ptr(), P[slot][i].data_ptr(), S[slot][i].data_ptr(), MP, N,
-                           K, G, y_pre[N].data_ptr(), stp, stream)
+        for (N, K), idx in groups.items():
+            ax = (arr * len(idx))(*[x_pre[K].data_ptr() for i in idx])
+            ap = (arr * len(idx))(*[P[slot][i].data_ptr() for i in idx])
+            asc = (arr * len(idx))(*[S[slot][i].data_ptr() for i in idx])
+            ay = (arr * len(idx))(*[y_pre[i].data_ptr() for i in idx])
+            rc = L.tq_gemm_batched(len(idx), ax, ap, asc, ay, MP, N, K, G, stp, stream)
             assert rc == 0, rc
 
     # fill every ring slot, then check slot 0 against the oracle on sampled rows

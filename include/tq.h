@@ -152,12 +152,33 @@ int tq_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *
  *   packed   [N, K/G, ceil(G/5)] bytes (any alignment)
  *   scales   [N, K/G] fp16, 2-byte aligned
  *   y        [M,N] fp32, 4-byte aligned, overwritten
+ * K is at most 4194304 (2^22); larger K returns TQ_ERR_SHAPE.
  * Invalid packed bytes set TQ_DEV_INVALID_BYTE; their contribution is then
  * unspecified.  Accuracy as tq_gemv.
  */
 int tq_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
             int64_t M, int64_t N, int64_t K, int G,
             float *y, int32_t *d_status, void *stream);
+
+/*
+ * Batched prefill matmul: `count` independent problems of the same shape,
+ * each exactly as tq_gemm(xs[i], packeds[i], scales[i], M, N, K, G, ys[i]),
+ * in as few launches as possible (one per 64 problems) so that the tiles of
+ * all problems share the chip -- e.g. the same projection of every layer of
+ * a decoder, or the gate and up projections that read the same activations.
+ * Results are bit-identical to the single-problem calls.
+ *   xs, packeds, scales, ys   HOST arrays of `count` DEVICE pointers, with
+ *                             the layouts and alignments of tq_gemm; read
+ *                             during the call only
+ *   count >= 0                (0 enqueues nothing)
+ * The outputs ys[i] must not overlap each other or any input.  Errors and
+ * device status as tq_gemm; a NULL or misaligned pointer in any entry rejects
+ * the whole call with nothing enqueued.
+ */
+int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys,
+                    int64_t M, int64_t N, int64_t K, int G,
+                    int32_t *d_status, void *stream);
 
 #ifdef __cplusplus
 }

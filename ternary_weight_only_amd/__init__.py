@@ -9,6 +9,7 @@ package only marshals torch tensors to that ABI:
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
     ys             = gemv_batched(xs, packeds, scales, N, K, G)  # many same-shaped
     y              = gemm(x_bf16, packed, scales, N, K, G)   # any M
+    ys             = gemm_batched(xs, packeds, scales, N, K, G)  # many same-shaped
 
 torch supplies device memory and the current stream; no arithmetic of the
 method runs in Python or torch.  The library is loaded on first use and a
@@ -22,6 +23,7 @@ from .binding import (  # noqa: F401
     DEV_SCALE_OVERFLOW,
     check,
     gemm,
+    gemm_batched,
     gemv,
     gemv_batched,
     lib,

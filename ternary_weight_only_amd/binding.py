@@ -21,7 +21,7 @@ DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_unpack",
-           "tq_gemv", "tq_gemv_batched", "tq_gemm")
+           "tq_gemv", "tq_gemv_batched", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -50,8 +50,9 @@ def lib() -> ctypes.CDLL:
         for f in (l.tq_gemv, l.tq_gemm):
             f.argtypes = [p, p, p, i64, i64, i64, i32, p, p, p]
             f.restype = i32
-        l.tq_gemv_batched.argtypes = [i32, p, p, p, p, i64, i64, i64, i32, p, p]
-        l.tq_gemv_batched.restype = i32
+        for f in (l.tq_gemv_batched, l.tq_gemm_batched):
+            f.argtypes = [i32, p, p, p, p, i64, i64, i64, i32, p, p]
+            f.restype = i32
         _lib = l
     return _lib
 
@@ -138,20 +139,19 @@ def gemv(x, packed, scales, N: int, K: int, G: int, status=None, out=None):
     return _mm(lib().tq_gemv, "tq_gemv", x, packed, scales, N, K, G, status, out)
 
 
-def gemv_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
-    """[x_i] ([M,K] bf16 each), [packed_i], [scales_i] -> [y_i] ([M,N] fp32), one call."""
+def _batched(fn, name, xs, packeds, scales_list, N, K, G, status, outs):
     count = len(xs)
     if not (len(packeds) == len(scales_list) == count):
-        raise TQError("gemv_batched: lists of different lengths")
+        raise TQError("%s: lists of different lengths" % name)
     ys = []
     for i in range(count):
         _dev(xs[i], "x", (torch.bfloat16, torch.int16), 2)
         _dev(packeds[i], "packed", (torch.uint8,), packeds[i].dim())
         _dev(scales_list[i], "scales", (torch.float16, torch.int16), scales_list[i].dim())
         if xs[i].shape != xs[0].shape or xs[i].shape[1] != K:
-            raise TQError("gemv_batched: every x must be [M,%d]" % K)
+            raise TQError("%s: every x must be [M,%d]" % (name, K))
         if packeds[i].numel() != packed_bytes(N, K, G) or scales_list[i].numel() != N * (K // G):
-            raise TQError("gemv_batched: packed/scales sizes do not match N=%d K=%d G=%d" % (N, K, G))
+            raise TQError("%s: packed/scales sizes do not match N=%d K=%d G=%d" % (name, N, K, G))
         ys.append(torch.empty((xs[0].shape[0], N), dtype=torch.float32, device=xs[i].device)
                   if outs is None else outs[i])
     arr = ctypes.c_void_p * max(count, 1)
@@ -160,9 +160,20 @@ def gemv_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, 
     asc = arr(*[t.data_ptr() for t in scales_list])
     ay = arr(*[t.data_ptr() for t in ys])
     M = xs[0].shape[0] if count else 1
-    _rc(lib().tq_gemv_batched(count, ax, ap, asc, ay, M, N, K, G, _st(status), _stream()),
-        "tq_gemv_batched")
+    _rc(fn(count, ax, ap, asc, ay, M, N, K, G, _st(status), _stream()), name)
     return ys
+
+
+def gemv_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """[x_i] ([M,K] bf16 each, M <= 16), [packed_i], [scales_i] -> [y_i] ([M,N] fp32), one call."""
+    return _batched(lib().tq_gemv_batched, "tq_gemv_batched", xs, packeds, scales_list, N, K, G,
+                    status, outs)
+
+
+def gemm_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """[x_i] ([M,K] bf16 each), [packed_i], [scales_i] -> [y_i] ([M,N] fp32), one call."""
+    return _batched(lib().tq_gemm_batched, "tq_gemm_batched", xs, packeds, scales_list, N, K, G,
+                    status, outs)
 
 
 def gemm(x, packed, scales, N: int, K: int, G: int, status=None, out=None):

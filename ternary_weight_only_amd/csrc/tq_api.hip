@@ -115,10 +115,33 @@ int tq_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, in
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
   if (M < 1 || M > (int64_t(1) << 40) / K) return TQ_ERR_SHAPE;
+  if (K > (int64_t(1) << 22)) return TQ_ERR_SHAPE;  // a 128-row x slab stays under 1 GiB
   if (!aligned(x, 16) || !aligned(scales, 2) || !aligned(y, 4) || !aligned(d_status, 4))
     return TQ_ERR_ALIGN;
   hipGetLastError();
   tq::launch_gemm(x, packed, scales, M, N, K, G, y, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                    int64_t K, int G, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !ys) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (M < 1 || M > (int64_t(1) << 40) / K) return TQ_ERR_SHAPE;
+  if (K > (int64_t(1) << 22)) return TQ_ERR_SHAPE;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(scales[i], 2) || !aligned(ys[i], 4))
+      return TQ_ERR_ALIGN;
+  }
+  hipGetLastError();
+  tq::launch_gemm_batched(count, xs, packeds, scales, ys, M, N, K, G, d_status,
+                          (hipStream_t)stream);
   return finish_launch();
 }
 

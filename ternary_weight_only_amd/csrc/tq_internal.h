@@ -34,4 +34,11 @@ void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scale
                  int64_t M, int64_t N, int64_t K, int G, float *y,
                  int32_t *d_status, hipStream_t stream);
 
+// Problems per batched GEMM launch.
+constexpr int kGemmMaxBatch = 64;
+
+void launch_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                         const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                         int64_t K, int G, int32_t *d_status, hipStream_t stream);
+
 }  // namespace tq

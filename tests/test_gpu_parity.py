@@ -190,3 +190,67 @@ def test_gemv_batched_matches_oracle(N, K, G, count):
                     status=st)
     torch.cuda.synchronize()
     assert int(st.item()) & 4
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+def test_gemm_ragged_unaligned_packed_and_invalid_bytes(G, offset):
+    """tq_gemm over partial tiles (M=300, N=200 leave ragged 256-row and
+    128-row tiles), packed bytes at every alignment (the ABI allows any), and
+    an invalid byte at the first and at the very last byte of the buffer."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits
+    M, N, K = 300, 200, 640
+    w = inputs.normal_bf16(60 + G, (N, K), 0.02)
+    p, s, _ = oracle.quantize_pack(w, G)
+    x = inputs.activation(61, M, K)
+    y_ref, bound, _ = oracle.matmul(x, p, s, N, K, G)
+    flat = p.reshape(-1)
+    buf = torch.zeros(flat.size + 8, dtype=torch.uint8, device="cuda")
+    pd = buf[offset:offset + flat.size]
+    xd, sd = dev_bf16(x), dev_f16bits(s)
+    say("gemm ragged M=%d N=%d K=%d G=%d packed offset %d" % (M, N, K, G, offset))
+    pd.copy_(torch.from_numpy(flat))
+    st = tq.new_status()
+    y = tq.gemm(xd, pd, sd, N, K, G, status=st).cpu().numpy()
+    assert int(st.item()) == 0
+    assert_within_bound(y, y_ref, bound, "gemm ragged G=%d offset %d" % (G, offset))
+    for pos in (0, flat.size - 1):
+        bad = flat.copy()
+        bad[pos] = 243 + pos % 13
+        pd.copy_(torch.from_numpy(bad))
+        st = tq.new_status()
+        tq.gemm(xd, pd, sd, N, K, G, status=st)
+        torch.cuda.synchronize()
+        assert int(st.item()) & 4, "invalid byte at %d not flagged" % pos
+
+
+@pytest.mark.parametrize("M,N,K,G,count", [(512, 3584, 1024, 128, 3), (100, 200, 640, 64, 5),
+                                           (300, 96, 320, 64, 70)])
+def test_gemm_batched_matches_single_calls_and_oracle(M, N, K, G, count):
+    """tq_gemm_batched: bit-identical to one tq_gemm per problem (count=70
+    takes two launches), and within the bound of the oracle on sampled rows."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
+    ws = [inputs.normal_bf16(500 + i, (N, K), 0.02) for i in range(count)]
+    xs = [inputs.activation(600 + i, M, K) for i in range(count)]
+    refs = [oracle.quantize_pack(w, G) for w in ws]
+    xd = [dev_bf16(x) for x in xs]
+    pdv = [dev_u8(p) for p, _, _ in refs]
+    sdv = [dev_f16bits(s) for _, s, _ in refs]
+    say("gemm_batched M=%d N=%d K=%d G=%d count=%d" % (M, N, K, G, count))
+    st = tq.new_status()
+    ys = tq.gemm_batched(xd, pdv, sdv, N, K, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rng = np.random.default_rng(M + count)
+    for i in range(count):
+        y1 = tq.gemm(xd[i], pdv[i], sdv[i], N, K, G)
+        assert torch.equal(ys[i], y1), "batched item %d differs from the single call" % i
+        if i < 3 or i == count - 1:
+            rows = np.sort(rng.choice(M, size=min(M, 16), replace=False))
+            p, s, _ = refs[i]
+            y_ref, bound, _ = oracle.matmul(xs[i][rows], p, s, N, K, G)
+            assert_within_bound(ys[i].cpu().numpy()[rows], y_ref, bound, "batched item %d" % i)
