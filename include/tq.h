@@ -115,6 +115,10 @@ int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
  *   packed   [N, K/G, ceil(G/5)] bytes, 16-byte aligned
  *   scales   [N, K/G] fp16, 2-byte aligned
  *   y        [M,N] fp32, 4-byte aligned, overwritten
+ * K is at most 4194304 (2^22); larger K returns TQ_ERR_SHAPE.  Results are
+ * deterministic (a fixed summation order for given shapes).  M = 1 runs a
+ * table-decode kernel with dot2 accumulation; 2 <= M <= 16 (and M = 1 shapes
+ * that kernel does not take) run on the matrix cores.
  * Invalid packed bytes set TQ_DEV_INVALID_BYTE; their contribution is then
  * unspecified.  Accuracy: |y - y_exact| <= 1e-3 * sum_k |x[m,k] w_hat[n,k]|.
  */

@@ -79,6 +79,7 @@ int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, in
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
   if (M < 1 || M > 16) return TQ_ERR_SHAPE;
+  if (K > (int64_t(1) << 22)) return TQ_ERR_SHAPE;  // 32-bit offsets into x
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(y, 4) ||
       !aligned(d_status, 4))
     return TQ_ERR_ALIGN;
@@ -96,6 +97,7 @@ int tq_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
   if (M < 1 || M > 16) return TQ_ERR_SHAPE;
+  if (K > (int64_t(1) << 22)) return TQ_ERR_SHAPE;
   if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
   for (int i = 0; i < count; ++i) {
     if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;

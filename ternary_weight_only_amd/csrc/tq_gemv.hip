@@ -1,4 +1,5 @@
-// tq_gemv.hip -- decode GEMV / skinny matmul (1 <= M <= 16) for gfx950.
+// tq_gemv.hip -- skinny matmul (2 <= M <= 16, and M = 1 for shapes the M = 1
+// kernel in tq_gemv_m1.hip does not take) for gfx950.
 //
 // y[m,n] = sum_g s[n,g] * sum_{j<G} x[m, gG+j] * c[n, gG+j]
 // (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation":
@@ -6,26 +7,33 @@
 // "Revisit the Decode Roofline": one-token decode streams every packed weight
 // once, so the kernel is bound by HBM bandwidth).
 //
-// M = 1 kernel (gemv_m1_kernel):
-//   * A row's packed bytes are split into 13-byte chunks.  13 bytes hold 65
-//     trits: one G=64 group plus its padding trit, or one half of a G=128
-//     group (26 bytes), so every chunk belongs to exactly one group and one
-//     fp16 scale.  A row has L = K/64 chunks.
-//   * Each lane owns one chunk position for all the rows it visits, so its 65
-//     activations stay in registers as bf16 pairs (x0,x1)(x2,x3)(x4,0) per
-//     byte, with zeros at padding positions.
-//   * A byte is decoded by one LDS lookup: a 256-entry table maps it to three
-//     bf16 pairs of codes (c0,c1)(c2,c3)(c4,0); v_dot2_f32_bf16 multiplies
-//     them with the activation pairs into fp32.  Entries 243..255 hold NaN,
-//     so an invalid byte turns the chunk sum into NaN, which is checked once
-//     per chunk.  The table is replicated 16 times, copy j living in LDS bank
-//     group j, and lane l reads copy l%16: the 16 lanes served together hit
-//     16 different bank groups whatever the byte values are.
-//   * The lookup address (byte * 256 + copy * 16) is built by one v_perm_b32
-//     from the data dword and a per-lane constant.
-//   * Chunk sums are scaled by the group's fp16 scale, reduced over 16-lane
-//     segments with DPP, then across a row's segments through LDS in a fixed
-//     order (deterministic results).
+// The multiply-adds run on the matrix cores (v_mfma_f32_16x16x32_bf16) with
+// one packed byte per lane and MFMA:
+//   * The 32 k-slots of an MFMA are four bytes' worth of codes, 8 slots per
+//     byte: the byte's five codes and three zeros.  Lane l = j + 16 q feeds
+//     byte (T q + t) of the current group of weight row j of a 16-row tile
+//     (B operand) and the five matching activations of x row j (A operand;
+//     rows j >= M are zero), so after T MFMAs (T = 8 for G=128, 4 for G=64)
+//     lane (j, q) holds y[4q + r][row j] partial sums for r = 0..3.
+//   * A 256-entry LDS table maps a byte to exactly that B fragment: three
+//     bf16 code pairs (c0,c1)(c2,c3)(c4,0) and a zero dword.  One
+//     ds_read_b128 per byte, no decode arithmetic.  The table is replicated
+//     16 times, copy j in bank group j, and lane l reads copy l % 16; the
+//     address (byte * 256 + copy * 16) is one v_perm_b32.  Entries 243..255
+//     are NaN, so an invalid byte makes its output NaN, which is flagged.
+//   * Byte slots past the group's ceil(G/5) bytes (and code positions past G)
+//     meet zero activations, so the padding trits and the neighbouring
+//     group's bytes contribute nothing.
+//   * A group's partial tile is scaled by its fp16 scale in fp32 and added
+//     to the accumulator.
+// Work: persistent blocks of 8 waves each take a contiguous range of "slabs"
+// (16 * TL * 8 / S weight rows of one problem).  Within a slab, wave w covers
+// TL (1 or 2) 16-row tiles for one of S consecutive K ranges (S = 1, 2, 4 or 8
+// chosen from the shape).  A wave streams the groups of its slabs as one loop
+// whose body has no branch around a load, no global store and no barrier, so
+// its packed bytes stay four groups in flight across slab boundaries; each
+// slab's partial tiles wait in LDS, and every four slabs the S parts of a tile
+// are added in a fixed order and stored, so results are deterministic.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -36,53 +44,25 @@ namespace tq {
 namespace {
 
 constexpr int kWave = 64;
+constexpr int kWaves = 8;          // waves per block
+constexpr int kThreads = kWave * kWaves;
+constexpr int kCopies = 16;        // table replicas, one per 16-byte LDS bank group
+constexpr int kLutEntries = 256;   // byte values; 243..255 decode to NaN
+constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
+constexpr int kMaxBatch = 64;      // problems per batched launch
+constexpr int kRing = 4;           // groups of packed bytes in flight per wave
+constexpr int kXLead = 2;          // groups of activations in flight per wave
+constexpr int kXBuf = 4;           // activation buffers (a divisor of kRing, > kXLead)
+constexpr int kSlots = 4;          // slabs per batch whose partial sums wait in LDS
 
-typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
-typedef uint32_t u32x4_a4 __attribute__((ext_vector_type(4), aligned(4)));
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-typedef __attribute__((address_space(3))) const volatile u32x4 lds_u32x4_cv;
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x4 lds_u32x4_c;
 typedef __attribute__((address_space(3))) const unsigned char lds_bytes_c;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
-}
-
-__device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
-  return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
-                                         __builtin_bit_cast(bf16x2_t, b), c, false);
-}
-
-template <int CTRL>
-__device__ __forceinline__ float dpp_f32(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               0xF, 0xF, false));
-}
-
-// DPP move restricted to the rows in ROWMASK (other rows read 0).
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_f32_rows(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               ROWMASK, 0xF, false));
-}
-
-// Sum over each row of 16 lanes; every lane of the row receives the sum.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f32<0x141>(v);  // row_half_mirror
-  v += dpp_f32<0x140>(v);  // row_mirror
-  return v;
-}
-
-// ---------------------------------------------------------------------------
-// M = 1
-// ---------------------------------------------------------------------------
-constexpr int kCopies = 16;        // LUT replicas, one per 16-byte LDS bank group
-constexpr int kLutEntries = 256;   // byte values; 243..255 decode to NaN
-constexpr int kChunk = 13;         // bytes per lane chunk
-constexpr int kMaxWaves = 8;
-
-// LUT entry for byte value e: three bf16 pairs of the codes of its five
+// Table entry for byte value e: three bf16 pairs of the codes of its five
 // base-3 digits (first weight = least significant digit), fourth dword 0.
 __device__ __forceinline__ uint4 lut_entry(uint32_t e) {
   if (e >= 243u) return make_uint4(0x7FC07FC0u, 0x7FC07FC0u, 0x7FC07FC0u, 0u);
@@ -97,15 +77,11 @@ __device__ __forceinline__ uint4 lut_entry(uint32_t e) {
 }
 
 // Buffer resource over [p, p + bytes): the hardware range check returns 0 for
-// every dword at or past `bytes`, so loads need no branches at the edges.
+// a load past `bytes`, so loads need no branches at the edges.
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                            0x00020000);
 }
-
-constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
-constexpr int kRing = 4;  // row batches in flight per lane
-constexpr int kMaxBatch = 64;  // problems per batched launch
 
 // Up to kMaxBatch same-shaped problems per launch, passed by value.
 struct GemvBatch {
@@ -115,351 +91,386 @@ struct GemvBatch {
   float *y[kMaxBatch];
 };
 
-// The work of a launch is count * nb row batches (nb per problem); a batch
-// is one row per row slot (R = 64W / Lp rows).  A block owns a contiguous
-// range of batches, which may cross from one problem into the next.  Threads
-// t = 0..64W-1 map to (row slot rr = t/Lp, chunk c = t % Lp); lanes with
-// c >= L idle.  Each lane keeps the packed bytes of its next D batches in
-// flight in a register ring.
-template <int G, int D, bool WAVE_ROWS>
-__global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void gemv_m1_kernel(const GemvBatch args, int count, int N, int K, int L, int Lp,
-                    int32_t *__restrict__ d_status) {
+template <int G>
+struct Geo {
+  static constexpr int B = bytes_per_group(G);  // 13 or 26 bytes per group
+  static constexpr int T = G == 128 ? 8 : 4;    // bytes per k-lane per group (= MFMAs per tile)
+  static constexpr int XD = 5 * T / 2;          // activation dwords per lane per group: 20 or 10
+  static constexpr int PD = T == 8 ? 3 : 2;     // packed dwords a lane loads per tile and group
+};
+
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+
+// Grid: persistent blocks over "slabs" of 16 * kTiles * (kWaves / S) weight
+// rows of one problem.  S (1, 2, 4, 8) splits K between the waves of a slab;
+// a wave covers kTiles (1 or 2) 16-row tiles.
+template <int G, int kTiles>
+__global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, int64_t ldy,
+                 int32_t *__restrict__ d_status) {
+  using Gm = Geo<G>;
+  constexpr int T = Gm::T, XD = Gm::XD, PD = Gm::PD, B = Gm::B;
   __shared__ uint4 lut[kLutEntries * kCopies];
-  __shared__ float segsum[2][4 * kMaxWaves];  // R * (Lp/16) = 4W floats per batch
+  __shared__ f32x4 res[kSlots][kWaves][kTiles][kWave];
 
-  const int tid = threadIdx.x;
-  const int nthreads = blockDim.x;
-  const int R = nthreads / Lp;  // rows per batch
-  const int nseg = Lp / 16;     // 16-lane segments per row
-  const int rr = tid / Lp;
-  const int c = tid % Lp;
-  const bool lane_on = c < L;
+  const int tid = threadIdx.x, lane = tid & (kWave - 1);
+  const int wv = __builtin_amdgcn_readfirstlane(tid / kWave);
   const int nG = K / G;
-  const uint32_t rowbytes = (uint32_t)L * kChunk;
-  const uint32_t total = (uint32_t)N * rowbytes;  // < 2^31, checked by the launcher
-  const int gidx = G == 64 ? c : (c >> 1);
-  const int nb = (N + R - 1) / R;  // batches per problem
-  const int nbatches = nb * count;
-  const int q = nbatches / (int)gridDim.x, rmd = nbatches % (int)gridDim.x;
-  const int b_begin = (int)blockIdx.x * q + ((int)blockIdx.x < rmd ? (int)blockIdx.x : rmd);
-  const int b_end = b_begin + q + ((int)blockIdx.x < rmd ? 1 : 0);
+  const uint32_t rowbytes = (uint32_t)nG * B;
+  const int S = 1 << lgS;
+  const int part = wv & (S - 1), wtile = wv >> lgS;         // K range and tile pair of the wave
+  const int lg_rows = (kTiles == 2 ? 5 : 4) + 3 - lgS;      // slab rows: 16 * kTiles * (kWaves / S)
+  const int slab_rows = 1 << lg_rows;
+  const int spp = (N + slab_rows - 1) >> lg_rows;           // slabs per problem
+  const int nslabs = spp * count;
+  const int g_begin = (part * nG) >> lgS, g_end = ((part + 1) * nG) >> lgS;
 
-  // lane's byte address of local batch b is a0 + b * bstep; idle lanes get
-  // an offset past any range so their loads read zeros.  Rows past N lie
-  // past the end of the buffers and read zeros too (they are never stored).
-  const uint32_t a0 = lane_on ? (uint32_t)rr * rowbytes + (uint32_t)c * kChunk : kOutOfRange;
-  const uint32_t bstep = (uint32_t)R * rowbytes;
-  const uint32_t s0 = lane_on ? 2u * ((uint32_t)rr * (uint32_t)nG + (uint32_t)gidx) : kOutOfRange;
-  const uint32_t sstep = 2u * (uint32_t)R * (uint32_t)nG;
-  const uint32_t pbytes = (total + 3u) & ~3u, sbytes = (uint32_t)N * (uint32_t)nG * 2u;
-
-  u32x4 ring[D];
-  uint32_t rofs[D], rsc[D];
-  auto issue = [&](int slot, int g) {
-    const int pi = g / nb, b = g - pi * nb;  // problem and local batch (uniform)
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[pi], pbytes);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.scales[pi], sbytes);
-    const uint32_t a = a0 + (uint32_t)b * bstep;
-    ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, a & ~3u, 0, 0);
-    rofs[slot] = a & 3u;
-    rsc[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, s0 + (uint32_t)b * sstep, 0, 0);
-  };
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (b_begin + d < b_end) issue(d, b_begin + d);
-
-  // Activations of this lane's chunk as bf16 pairs (x0,x1)(x2,x3)(x4,0) per
-  // byte, from x[64c .. 64c+72) (zeros past K and for idle lanes).  The
-  // lane's trit p is x[64c + h + p] (h = 1 for the second half of a G=128
-  // group); Dn[i] holds the pair (x[64c+h+2i], x[64c+h+2i+1]).
-  uint32_t xa[kChunk][3];
-  auto load_x = [&](int pi) {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[pi], (uint32_t)K * 2u);
-    u32x4 xr[9];
-#pragma unroll
-    for (int i = 0; i < 9; ++i)
-      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, lane_on ? 128u * c + 16u * i : kOutOfRange,
-                                                    0, 0);
-    const int h = (G == 128) ? (c & 1) : 0;
-    uint32_t Dw[36];
-#pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      Dw[4 * i] = xr[i].x; Dw[4 * i + 1] = xr[i].y; Dw[4 * i + 2] = xr[i].z; Dw[4 * i + 3] = xr[i].w;
-    }
-    uint32_t Dn[34];
-#pragma unroll
-    for (int i = 0; i < 34; ++i) Dn[i] = __builtin_amdgcn_alignbyte(Dw[i + 1], Dw[i], 2u * h);
-    auto pair_at = [&](int p) -> uint32_t {  // (x_p, x_{p+1}) of the lane
-      return (p & 1) ? __builtin_amdgcn_alignbyte(Dn[(p + 1) / 2], Dn[(p - 1) / 2], 2u)
-                     : Dn[p / 2];
-    };
-#pragma unroll
-    for (int j = 0; j < kChunk; ++j) {
-      xa[j][0] = pair_at(5 * j);
-      xa[j][1] = pair_at(5 * j + 2);
-      xa[j][2] = pair_at(5 * j + 4) & 0xFFFFu;
-    }
-    // padding trits carry no activation: p = 64 for G=64 and for the second
-    // half of a G=128 group, p = 63 too for the latter
-    if (G == 64) {
-      xa[kChunk - 1][2] = 0u;
-    } else if (h) {
-      xa[kChunk - 1][1] &= 0xFFFFu;
-      xa[kChunk - 1][2] = 0u;
-    }
-  };
-  int p_cur = b_begin < b_end ? b_begin / nb : 0;
-  load_x(p_cur);
-
-  // table: each thread builds one entry and writes a share of its copies;
-  // the copy index is rotated by the lane so a wave's 16-byte writes spread
-  // over all 16 bank groups
+  // ---- decode table: each thread writes 8 of the 4096 (entry, copy) slots,
+  // the copy index rotated by the entry so a wave's writes spread the banks ----
   {
     const int ent = tid % kLutEntries;
     const uint4 e = lut_entry((uint32_t)ent);
-    const int per = nthreads >= 2 * kLutEntries ? 2 : 1;  // threads per entry (>= 256 threads)
-    const int share = kCopies / per;
-    const int first = (tid / kLutEntries) * share;
-    if (tid < per * kLutEntries) {
-      for (int k = 0; k < share; ++k) {
-        const int cp = (first + k + tid) % kCopies;
-        lut[ent * kCopies + cp] = e;
-      }
-    }
+    const int first = (tid / kLutEntries) * (kCopies / 2);
+#pragma unroll
+    for (int k = 0; k < kCopies / 2; ++k) lut[ent * kCopies + ((first + k + ent) & (kCopies - 1))] = e;
   }
-  // per-lane byte offset of its table copy, in byte 0 of a perm source
-  const uint32_t copyoff = (uint32_t)(tid % kCopies) * 16u;
   __syncthreads();
 
+  const int j = lane & 15, q = lane >> 4;
+  const uint32_t copyoff = (uint32_t)j * 16u;  // byte 0 of a perm source: the lane's table copy
+  // Lanes q = 3 run past the group's last byte (slots 26..31 of 32 for
+  // G=128, 13..15 of 16 for G=64): those slots are forced to byte 121, whose
+  // codes are all 0, so whatever follows the group cannot turn into NaN.
+  constexpr int kLive3 = B - 3 * T;  // live bytes of lane q = 3: 2 or 1
+  const uint32_t keep = q == 3 ? (kLive3 == 2 ? 0x0000FFFFu : 0x000000FFu) : 0xFFFFFFFFu;
+  const uint32_t wmask[2] = {keep, q == 3 ? 0u : 0xFFFFFFFFu};
+  const uint32_t wfill[2] = {0x79797979u & ~keep, q == 3 ? 0x79797979u : 0u};
   lds_bytes_c *lut_bytes = (lds_bytes_c *)(lut);
-  uint32_t bad = 0;
-  int buf = 0;
-  for (int g0 = b_begin; g0 < b_end; g0 += D) {
+
+  // Activations of lane (j, q) for a group: x[j][gG + 5Tq .. gG + 5Tq + 5T),
+  // as XD dwords.  Loads are 16 bytes (8 for G=64) at offsets aligned to
+  // their size, so with K a multiple of 64 none straddles the end of x; for
+  // q = 3 only the first load holds positions < G, the others are made
+  // out-of-range (zeros: code positions past G carry no activation).
+  constexpr int XL = G == 128 ? 5 : 5;                      // loads per group
+  constexpr int XW = G == 128 ? 4 : 2;                      // dwords per load
+  uint32_t xoff[XL];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
-      const int g = g0 + d;
-      if (g < b_end) {  // uniform over the block
-        const int pi = g / nb, b = g - pi * nb;
-        if (pi != p_cur) {  // the block's range crossed into the next problem
-          p_cur = pi;
-          load_x(pi);
-        }
-        // realign the lane's 13 bytes to byte 0
-        const uint32_t o = rofs[d];
-        const u32x4 A = ring[d];
-        const uint32_t aw[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, o),
-                                __builtin_amdgcn_alignbyte(A.z, A.y, o),
-                                __builtin_amdgcn_alignbyte(A.w, A.z, o),
-                                __builtin_amdgcn_alignbyte(0u, A.w, o)};
-        const float sc = __half2float(__ushort_as_half((unsigned short)rsc[d]));
-        if (g + D < b_end) issue(d, g + D);  // refill the slot with the batch D ahead
-        u32x4 e[kChunk];
+  for (int u = 0; u < XL; ++u) {
+    const bool on = j < M && !(q == 3 && u >= 1);
+    xoff[u] = on ? ((uint32_t)j * (uint32_t)K + (uint32_t)(5 * T * q) + (uint32_t)(XW * 2 * u)) * 2u
+                 : kOutOfRange;
+  }
+  (void)XD;
+
+  uint32_t flags = 0;
+  // The block's slabs are the contiguous range [first, first + nmy), taken in
+  // batches of up to kSlots.  Within a batch a wave streams its groups
+  // [g_begin, g_end) of every slab as one sequence of iterations
+  // u = k * ngw + (g - g_begin): the loop body has no branch around a load,
+  // no global store and no barrier, so packed bytes stay kRing iterations in
+  // flight across slab boundaries.  A slab's per-wave partial sums are parked
+  // in LDS; the batch ends with one reduction (fixed order over the S K
+  // ranges) and the stores.
+  const int ngw = g_end - g_begin;  // >= 1 since S <= nG
+  const int per = nslabs / (int)gridDim.x, rem = nslabs - per * (int)gridDim.x;
+  const int bid = (int)blockIdx.x;
+  const int nmy = per + (bid < rem ? 1 : 0);
+  const int first = bid * per + min(bid, rem);
+
+  // Slab cursor: problem pi, slab rs of that problem; stepped without division.
+  struct Slab {
+    int pi, rs;
+  };
+  auto step = [&](Slab &c) {
+    if (++c.rs == spp) {
+      c.rs = 0;
+      ++c.pi;
+    }
+  };
+  struct Where {
+    int pi, row0, nrows;
+  };
+  auto where = [&](const Slab &c, bool valid) -> Where {  // not valid: a real problem, no rows
+    const int row0 = c.rs << lg_rows;
+    return Where{min(c.pi, count - 1), row0, valid ? min(slab_rows, N - row0) : 0};
+  };
+
+  struct PkStage {
+    uint32_t pk[kTiles][PD];
+    uint32_t sc[kTiles];
+    uint32_t ofs[kTiles];
+  };
+  struct XStage {
+    uint32_t xd[XL * XW];
+  };
+  // packed bytes and scales of group g of slab w (rows past w.nrows read 0)
+  auto issue_pk = [&](const Where &w, int g, PkStage &st) {
+    const uintptr_t pabs =
+        reinterpret_cast<uintptr_t>(args.packed[w.pi]) + (uint64_t)w.row0 * rowbytes;
+    const uint32_t pbase = (uint32_t)(pabs & 3u);
+    // whole dwords: a dword load is fully in range or fully past it (reads 0)
+    const __amdgpu_buffer_rsrc_t rp =
+        make_rsrc(reinterpret_cast<const void *>(pabs - pbase),
+                  (pbase + (uint32_t)w.nrows * rowbytes + 3u) & ~3u);
+    const __amdgpu_buffer_rsrc_t rs =
+        make_rsrc(args.scales[w.pi] + (int64_t)w.row0 * nG, (uint32_t)w.nrows * (uint32_t)nG * 2u);
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          // address = byte * 256 + copyoff: byte (j%4) of aw[j/4] into byte 1
-          const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
-          const uint32_t addr = __builtin_amdgcn_perm(copyoff, aw[j >> 2], sel);
-          // one full 128-bit read (ds_read_b128 outruns ds_read_b96 on
-          // gfx950); volatile keeps the compiler from narrowing it
-          e[j] = *(lds_u32x4_cv *)(lut_bytes + addr);
-        }
-        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+    for (int t = 0; t < kTiles; ++t) {
+      const int r = 16 * kTiles * wtile + 16 * t + j;  // slab row of the lane
+      const bool on = r < w.nrows;
+      const uint32_t a = pbase + (uint32_t)r * rowbytes + (uint32_t)(g * B + T * q);
+      const uint32_t a4 = on ? (a & ~3u) : kOutOfRange;
+      st.ofs[t] = a & 3u;
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          float &acc = (j & 3) == 0 ? acc0 : (j & 3) == 1 ? acc1 : (j & 3) == 2 ? acc2 : acc3;
-          acc = dot2_bf16(e[j].x, xa[j][0], acc);
-          acc = dot2_bf16(e[j].y, xa[j][1], acc);
-          acc = dot2_bf16(e[j].z, xa[j][2], acc);
-        }
-        // The fourth dword of each read is unused; holding it to here stops
-        // the register allocator from reusing its register while the read is
-        // in flight (that reuse forces a wait right after the read).
+      for (int d = 0; d < PD; ++d)
+        st.pk[t][d] = __builtin_amdgcn_raw_buffer_load_b32(rp, a4 + 4u * d, 0, 0);
+      st.sc[t] = __builtin_amdgcn_raw_buffer_load_b16(
+          rs, on ? 2u * ((uint32_t)r * (uint32_t)nG + (uint32_t)g) : kOutOfRange, 0, 0);
+    }
+  };
+  // activations of group g of problem pi (all zeros if !valid)
+  auto issue_x = [&](bool valid, int pi, int g, XStage &st) {
+    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[pi], (uint32_t)M * (uint32_t)K * 2u);
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) asm volatile("" ::"v"(e[j].w));
-        const float pc = (acc0 + acc1) + (acc2 + acc3);
-        float part = row16_sum(sc * pc);
-        float *__restrict__ yp = args.y[pi];
-        if (WAVE_ROWS) {
-          // a row is Lp <= 64 consecutive lanes of one wave: add its 16-lane
-          // rows with row_bcast15/31; the row's last lane holds the sum (an
-          // invalid byte anywhere in the row makes it NaN)
-          if (Lp >= 32) part += dpp_f32_rows<0x142, 0xA>(part);  // row_bcast:15
-          if (Lp >= 64) part += dpp_f32_rows<0x143, 0xC>(part);  // row_bcast:31
-          const int n = b * R + rr;
-          if (c == Lp - 1 && n < N) {
-            bad |= (part != part);
-            yp[n] = part;
+    for (int v = 0; v < XL; ++v) {
+      const uint32_t o =
+          (xoff[v] == kOutOfRange || !valid) ? kOutOfRange : xoff[v] + (uint32_t)(g * G) * 2u;
+      if (XW == 4) {
+        const u32x4 d = __builtin_amdgcn_raw_buffer_load_b128(rx, o, 0, 0);
+        st.xd[4 * v] = d.x; st.xd[4 * v + 1] = d.y; st.xd[4 * v + 2] = d.z; st.xd[4 * v + 3] = d.w;
+      } else {
+        const u32x2 d = __builtin_amdgcn_raw_buffer_load_b64(rx, o, 0, 0);
+        st.xd[2 * v] = d.x; st.xd[2 * v + 1] = d.y;
+      }
+    }
+  };
+
+  f32x4 acc[kTiles];
+#pragma unroll
+  for (int t = 0; t < kTiles; ++t) acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
+
+  // the MFMAs of one iteration; all-zero loads add nothing (scale 0)
+  auto compute = [&](const PkStage &sp, const XStage &sx) {
+    // A fragments: byte t of the lane's run takes activations 5t .. 5t+4
+    u32x4 A[T];
+#pragma unroll
+    for (int t = 0; t < T; ++t) {
+      auto pair = [&](int e) -> uint32_t {  // (x_e, x_{e+1}) of the run
+        return (e & 1) ? __builtin_amdgcn_alignbyte(sx.xd[(e + 1) / 2], sx.xd[(e - 1) / 2], 2u)
+                       : sx.xd[e / 2];
+      };
+      const int e = 5 * t;
+      const uint32_t last =
+          ((e + 4) & 1) ? (sx.xd[(e + 3) / 2] >> 16) : (sx.xd[(e + 4) / 2] & 0xFFFFu);
+      A[t] = u32x4{pair(e), pair(e + 2), last, 0u};
+    }
+    // all table reads of the iteration first, then the MFMAs
+    u32x4 b[kTiles][T];
+#pragma unroll
+    for (int k = 0; k < kTiles; ++k) {
+      uint32_t w[2];
+      w[0] = (__builtin_amdgcn_alignbyte(sp.pk[k][1], sp.pk[k][0], sp.ofs[k]) & wmask[0]) | wfill[0];
+      w[1] = PD == 3 ? (__builtin_amdgcn_alignbyte(sp.pk[k][PD - 1], sp.pk[k][1], sp.ofs[k]) &
+                        wmask[1]) | wfill[1]
+                     : 0u;
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        // address = byte * 256 + copy * 16: byte (t % 4) of w[t / 4] into byte 1
+        const uint32_t sel = 0x0C0C0004u | ((uint32_t)(t & 3) << 8);
+        const uint32_t addr = __builtin_amdgcn_perm(copyoff, w[t >> 2], sel);
+        b[k][t] = *(lds_u32x4_c *)(lut_bytes + addr);
+      }
+    }
+#pragma unroll
+    for (int k = 0; k < kTiles; ++k) {
+      f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[t]),
+                                                        __builtin_bit_cast(bf16x8, b[k][t]), part, 0, 0, 0);
+      const float sc = __half2float(__ushort_as_half((unsigned short)sp.sc[k]));
+#pragma unroll
+      for (int r = 0; r < 4; ++r) acc[k][r] = fmaf(sc, part[r], acc[k][r]);
+    }
+    __builtin_amdgcn_sched_group_barrier(0x100, kTiles * T, 0);  // table reads
+    __builtin_amdgcn_sched_group_barrier(0x008, kTiles * T, 0);  // MFMAs
+  };
+
+  Slab batch = {first / spp, first - (first / spp) * spp};  // first slab of the batch
+  for (int k0 = 0; k0 < nmy; k0 += kSlots) {
+    const int nb = min(kSlots, nmy - k0);
+    const int U = nb * ngw;
+    // issue cursors (slab within the batch, group) for packed bytes and activations
+    int pk_k = 0, pk_g = g_begin, x_k = 0, x_g = g_begin;
+    Slab pk_c = batch, x_c = batch;
+    Where pk_w = where(batch, true), x_w = pk_w;
+    auto next_pk = [&]() {
+      if (++pk_g == g_end) {
+        pk_g = g_begin;
+        ++pk_k;
+        step(pk_c);
+        pk_w = where(pk_c, pk_k < nb);
+      }
+    };
+    auto next_x = [&]() {
+      if (++x_g == g_end) {
+        x_g = g_begin;
+        ++x_k;
+        step(x_c);
+        x_w = where(x_c, x_k < nb);
+      }
+    };
+
+    PkStage ring[kRing];
+    XStage xs[kXBuf];
+#pragma unroll
+    for (int d = 0; d < kRing; ++d) {
+      issue_pk(pk_w, pk_g, ring[d]);
+      next_pk();
+    }
+#pragma unroll
+    for (int d = 0; d < kXLead; ++d) {
+      issue_x(x_k < nb, x_w.pi, x_g, xs[d]);
+      next_x();
+    }
+    int gi = 0, ks = 0;  // group of the current slab, slab within the batch
+    auto round = [&](int u0) {
+#pragma unroll
+      for (int d = 0; d < kRing; ++d) {
+        const int u = u0 + d;
+        compute(ring[d], xs[d % kXBuf]);
+        issue_pk(pk_w, pk_g, ring[d]);
+        next_pk();
+        issue_x(x_k < nb, x_w.pi, x_g, xs[(d + kXLead) % kXBuf]);
+        next_x();
+        if (++gi == ngw && u < U) {  // park the slab's partial sums
+#pragma unroll
+          for (int t = 0; t < kTiles; ++t) {
+            res[ks][wv][t][lane] = acc[t];
+            acc[t] = f32x4{0.f, 0.f, 0.f, 0.f};
           }
-        } else {
-          if ((tid & 15) == 0) segsum[buf][rr * nseg + c / 16] = part;
-          __syncthreads();
-          if (tid < R) {
-            const int n = b * R + tid;
-            if (n < N) {
-              float sum = 0.f;
-              for (int k = 0; k < nseg; ++k) sum += segsum[buf][tid * nseg + k];
-              bad |= (sum != sum);
-              yp[n] = sum;
+          gi = 0;
+          ++ks;
+        }
+      }
+    };
+    // The first round is peeled so that the loop is entered with its loads
+    // in flight in the same order as on its back edge.
+    round(0);
+    for (int u0 = kRing; u0 < U; u0 += kRing) round(u0);
+    __syncthreads();
+    if (part == 0) {
+      Slab c = batch;
+      for (int k = 0; k < nb; ++k, step(c)) {
+        const Where w = where(c, true);
+        float *__restrict__ y = args.y[w.pi];
+#pragma unroll
+        for (int t = 0; t < kTiles; ++t) {
+          f32x4 v = res[k][wv][t][lane];
+          for (int p = 1; p < S; ++p) v += res[k][wv + p][t][lane];
+          const int r = 16 * kTiles * wtile + 16 * t + j;  // slab row of lane column j
+#pragma unroll
+          for (int e = 0; e < 4; ++e) {
+            const int m = 4 * q + e;
+            if (m < M && r < w.nrows) {
+              flags |= (v[e] != v[e]);
+              y[(int64_t)m * ldy + w.row0 + r] = v[e];
             }
           }
-          buf ^= 1;
         }
       }
     }
+    __syncthreads();  // res[] is reused by the next batch
+    for (int k = 0; k < nb; ++k) step(batch);
   }
-  if (bad && d_status) atomicOr(d_status, kDevInvalidByte);
+  if (flags && d_status) atomicOr(d_status, kDevInvalidByte);
 }
 
-// ---------------------------------------------------------------------------
-// General fallback: one wave per row, lanes stride over the row's groups.
-// Used for 2 <= M <= 16 and for K > 16384.
-// ---------------------------------------------------------------------------
-template <int G, int MT>
-__global__ __launch_bounds__(256) void gemv_rowwave_kernel(
-    const uint16_t *__restrict__ x, const uint8_t *__restrict__ packed,
-    const uint16_t *__restrict__ scales, int M, int64_t N, int64_t K, float *__restrict__ y,
-    int32_t *__restrict__ d_status) {
-  constexpr int B = bytes_per_group(G);
-  const int lane = threadIdx.x & (kWave - 1);
+// Slab shape: the K split S and tiles per wave TL.  Prefer two tiles per
+// wave (the activation fragments of a group serve both) and the smallest S
+// that gives about four slabs per CU; a wave keeps at least one group.
+struct Split {
+  int S, TL;
+};
+Split choose_split(int count, int64_t N, int64_t K, int G) {
   const int64_t nG = K / G;
-  int flags = 0;
-  for (int64_t row = (int64_t)blockIdx.x * 4 + threadIdx.x / kWave; row < N;
-       row += (int64_t)gridDim.x * 4) {
-    float acc[MT];
-#pragma unroll
-    for (int m = 0; m < MT; ++m) acc[m] = 0.f;
-    for (int64_t g = lane; g < nG; g += kWave) {
-      const float s = __half2float(__ushort_as_half(scales[row * nG + g]));
-      const uint8_t *pg = packed + (row * nG + g) * B;
-      const uint16_t *xg = x + g * G;
-      float part[MT];
-#pragma unroll
-      for (int m = 0; m < MT; ++m) part[m] = 0.f;
-      for (int b = 0; b < B; ++b) {
-        uint32_t v = pg[b];
-        if (v >= 243u) { flags |= kDevInvalidByte; continue; }
-#pragma unroll
-        for (int i = 0; i < 5; ++i) {
-          const uint32_t d = v % 3u;
-          v /= 3u;
-          const int pos = 5 * b + i;
-          if (pos < G && d != 1u) {
-#pragma unroll
-            for (int m = 0; m < MT; ++m) {
-              if (m < M) {
-                const float xv = bf16_to_f32(xg[(int64_t)m * K + pos]);
-                part[m] += (d == 2u) ? xv : -xv;
-              }
-            }
-          }
-        }
-      }
-#pragma unroll
-      for (int m = 0; m < MT; ++m) acc[m] = fmaf(s, part[m], acc[m]);
+  auto slabs = [&](int S, int TL) {
+    const int64_t rows = 16 * TL * (kWaves / S);
+    return count * ((N + rows - 1) / rows);
+  };
+  for (int TL = 2; TL >= 1; --TL)
+    for (int S = 1; S <= kWaves; S *= 2) {
+      if (S > nG) break;
+      if (slabs(S, TL) >= 4 * 256) return Split{S, TL};
     }
-#pragma unroll
-    for (int m = 0; m < MT; ++m) {
-      float v = acc[m];
-#pragma unroll
-      for (int o = kWave / 2; o > 0; o >>= 1) v += __shfl_xor(v, o, kWave);
-      acc[m] = v;
-    }
-    if (lane == 0) {
-#pragma unroll
-      for (int m = 0; m < MT; ++m)
-        if (m < M) y[(int64_t)m * N + row] = acc[m];
-    }
-  }
-  if (flags && d_status) atomicOr(d_status, flags);
+  int S = 1;
+  while (S * 2 <= kWaves && S * 2 <= nG) S *= 2;
+  return Split{S, slabs(S, 2) >= 2 * 256 ? 2 : 1};
 }
 
 template <int G>
-void launch_rowwave(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
-                    int64_t N, int64_t K, float *y, int32_t *d_status, hipStream_t stream) {
-  int64_t blocks = (N + 3) / 4;
-  const int grid = (int)(blocks < 16384 ? blocks : 16384);
-  const int m = (int)M;
-#define TQ_GEMV_CASE(MT)                                                                        \
-  hipLaunchKernelGGL((gemv_rowwave_kernel<G, MT>), dim3(grid), dim3(256), 0, stream, x, packed, \
-                     scales, m, N, K, y, d_status)
-  if (m <= 1) TQ_GEMV_CASE(1);
-  else if (m <= 2) TQ_GEMV_CASE(2);
-  else if (m <= 4) TQ_GEMV_CASE(4);
-  else if (m <= 8) TQ_GEMV_CASE(8);
-  else TQ_GEMV_CASE(16);
-#undef TQ_GEMV_CASE
-}
-
-// Blocks of W waves whose threads tile whole rows: Lp = 16*ceil(K/1024)
-// lanes per row must divide 64*W with W <= 8; 0 when no such W exists.
-int m1_waves(int64_t K) {
-  if (K % 64 != 0 || K / 64 > 256) return 0;
-  const int L = (int)(K / 64);
-  const int s = (L + 15) / 16;
-  int g4 = 1;
-  for (int d = 1; d <= 4; ++d)
-    if (s % d == 0 && 4 % d == 0) g4 = d;
-  const int w0 = s / g4;  // smallest W with 64W % Lp == 0
-  if (w0 > 8) return 0;
-  return w0 * (8 / w0);   // up to 8 waves per block
-}
-
-template <int G>
-void launch_m1(const GemvBatch &args, int count, int64_t N, int64_t K, int32_t *d_status,
-               hipStream_t stream) {
-  const int L = (int)(K / 64);
-  const int Lp = 16 * ((L + 15) / 16);
-  const int threads = 64 * m1_waves(K);
-  const int R = threads / Lp;
-  // persistent blocks: two per CU fit the 64 KB table
-  const int64_t nbatches = (N + R - 1) / R * count;
-  const int cap = 2 * 256;
-  const int grid = (int)(nbatches < cap ? nbatches : cap);
-  if (Lp <= 64)
-    hipLaunchKernelGGL((gemv_m1_kernel<G, kRing, true>), dim3(grid), dim3(threads), 0, stream,
-                       args, count, (int)N, (int)K, L, Lp, d_status);
+void launch(const GemvBatch &args, int count, int64_t M, int64_t N, int64_t K, int64_t ldy,
+            int32_t *d_status, hipStream_t stream) {
+  const Split sp = choose_split(count, N, K, G);
+  const int64_t slab_rows = 16 * sp.TL * (kWaves / sp.S);
+  const int64_t slabs = count * ((N + slab_rows - 1) / slab_rows);
+  const int grid = (int)(slabs < 256 ? slabs : 256);  // one 8-wave block per CU
+  if (sp.TL == 2)
+    hipLaunchKernelGGL((gemv_kernel<G, 2>), dim3(grid), dim3(kThreads), 0, stream, args, count,
+                       (int)M, (int)N, (int)K, __builtin_ctz((unsigned)sp.S), ldy, d_status);
   else
-    hipLaunchKernelGGL((gemv_m1_kernel<G, kRing, false>), dim3(grid), dim3(threads), 0, stream,
-                       args, count, (int)N, (int)K, L, Lp, d_status);
+    hipLaunchKernelGGL((gemv_kernel<G, 1>), dim3(grid), dim3(kThreads), 0, stream, args, count,
+                       (int)M, (int)N, (int)K, __builtin_ctz((unsigned)sp.S), ldy, d_status);
 }
 
-bool m1_supported(int64_t M, int64_t N, int64_t K) {
-  return M == 1 && m1_waves(K) > 0 && N * (K / 64) * 13 < (int64_t(1) << 31);
-}
+constexpr int64_t kChunkRows = int64_t(1) << 24;  // weight rows per launch
 
 }  // namespace
 
 void launch_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
                  int64_t N, int64_t K, int G, float *y, int32_t *d_status, hipStream_t stream) {
-  if (m1_supported(M, N, K)) {
+  if (gemv_m1_supported(M, N, K)) {
+    launch_gemv_m1(x, packed, scales, N, K, G, y, d_status, stream);
+    return;
+  }
+  const int64_t rowbytes = (K / G) * bytes_per_group(G);
+  for (int64_t n0 = 0; n0 < N; n0 += kChunkRows) {
+    const int64_t n = N - n0 < kChunkRows ? N - n0 : kChunkRows;
     GemvBatch args = {};
-    args.x[0] = x; args.packed[0] = packed; args.scales[0] = scales; args.y[0] = y;
-    if (G == 64) launch_m1<64>(args, 1, N, K, d_status, stream);
-    else launch_m1<128>(args, 1, N, K, d_status, stream);
-  } else {
-    if (G == 64) launch_rowwave<64>(x, packed, scales, M, N, K, y, d_status, stream);
-    else launch_rowwave<128>(x, packed, scales, M, N, K, y, d_status, stream);
+    args.x[0] = x;
+    args.packed[0] = packed + n0 * rowbytes;
+    args.scales[0] = scales + n0 * (K / G);
+    args.y[0] = y + n0;
+    if (G == 64) launch<64>(args, 1, M, n, K, N, d_status, stream);
+    else launch<128>(args, 1, M, n, K, N, d_status, stream);
   }
 }
 
 void launch_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                          const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                          int64_t K, int G, int32_t *d_status, hipStream_t stream) {
-  if (m1_supported(M, N, K)) {
-    for (int i0 = 0; i0 < count; i0 += kMaxBatch) {
-      const int cnt = count - i0 < kMaxBatch ? count - i0 : kMaxBatch;
-      GemvBatch args = {};
-      for (int i = 0; i < cnt; ++i) {
-        args.x[i] = xs[i0 + i]; args.packed[i] = packeds[i0 + i];
-        args.scales[i] = scales[i0 + i]; args.y[i] = ys[i0 + i];
-      }
-      if (G == 64) launch_m1<64>(args, cnt, N, K, d_status, stream);
-      else launch_m1<128>(args, cnt, N, K, d_status, stream);
-    }
-  } else {
+  if (gemv_m1_supported(M, N, K)) {
+    launch_gemv_m1_batched(count, xs, packeds, scales, ys, N, K, G, d_status, stream);
+    return;
+  }
+  if (N > kChunkRows) {
     for (int i = 0; i < count; ++i)
       launch_gemv(xs[i], packeds[i], scales[i], M, N, K, G, ys[i], d_status, stream);
+    return;
+  }
+  for (int i0 = 0; i0 < count; i0 += kMaxBatch) {
+    const int cnt = count - i0 < kMaxBatch ? count - i0 : kMaxBatch;
+    GemvBatch args = {};
+    for (int i = 0; i < cnt; ++i) {
+      args.x[i] = xs[i0 + i]; args.packed[i] = packeds[i0 + i];
+      args.scales[i] = scales[i0 + i]; args.y[i] = ys[i0 + i];
+    }
+    if (G == 64) launch<64>(args, cnt, M, N, K, N, d_status, stream);
+    else launch<128>(args, cnt, M, N, K, N, d_status, stream);
   }
 }
 

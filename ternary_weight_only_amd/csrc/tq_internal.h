@@ -30,6 +30,16 @@ void launch_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *co
                          const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                          int64_t K, int G, int32_t *d_status, hipStream_t stream);
 
+// M = 1 decode kernel (tq_gemv_m1.hip), for the shapes it supports.
+bool gemv_m1_supported(int64_t M, int64_t N, int64_t K);
+
+void launch_gemv_m1(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t N,
+                    int64_t K, int G, float *y, int32_t *d_status, hipStream_t stream);
+
+void launch_gemv_m1_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                            const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
+                            int G, int32_t *d_status, hipStream_t stream);
+
 void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
                  int64_t M, int64_t N, int64_t K, int G, float *y,
                  int32_t *d_status, hipStream_t stream);

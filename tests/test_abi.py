@@ -66,8 +66,7 @@ def test_matmul_argument_errors(fn):
     assert f(FAKE + 2, FAKE, FAKE, 1, 8, 128, 64, FAKE, None, None) == -4  # x alignment
     assert f(FAKE, FAKE, FAKE + 1, 1, 8, 128, 64, FAKE, None, None) == -4  # scales
     assert f(FAKE, FAKE, FAKE, 1, 8, 128, 64, FAKE + 2, None, None) == -4  # y
-    if fn == "tq_gemm":
-        assert f(FAKE, FAKE, FAKE, 1, 1, (1 << 22) + 64, 64, FAKE, None, None) == -2  # K cap
+    assert f(FAKE, FAKE, FAKE, 1, 1, (1 << 22) + 64, 64, FAKE, None, None) == -2  # K cap
     if fn == "tq_gemv":
         assert f(FAKE, FAKE, FAKE, 17, 8, 128, 64, FAKE, None, None) == -2  # M > 16
         assert f(FAKE, FAKE + 8, FAKE, 1, 8, 128, 64, FAKE, None, None) == -4
@@ -88,8 +87,7 @@ def test_batched_argument_errors(fn):
     assert f(2, good, good, good, good, 1, 8, 100, 64, None, None) == -2
     if fn == "tq_gemv_batched":
         assert f(2, good, good, good, good, 17, 8, 128, 64, None, None) == -2
-    else:
-        assert f(2, good, good, good, good, 1, 1, (1 << 22) + 64, 64, None, None) == -2
+    assert f(2, good, good, good, good, 1, 1, (1 << 22) + 64, 64, None, None) == -2
     assert f(2, good, good, good, good, 0, 8, 128, 64, None, None) == -2
     assert f(2, good, good, good, good, 1, 8, 96, 32, None, None) == -3
     assert f(2, bad_al, good, good, good, 1, 8, 128, 64, None, None) == -4

@@ -226,6 +226,39 @@ def test_gemm_ragged_unaligned_packed_and_invalid_bytes(G, offset):
         assert int(st.item()) & 4, "invalid byte at %d not flagged" % pos
 
 
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("N", [200, 201, 202, 203])
+def test_gemv_ragged_buffer_ends_and_invalid_bytes(G, N):
+    """tq_gemv at M = 1, 5 and 16 over ragged row tiles, with N chosen so the
+    packed buffer (N * 130 bytes) ends at every offset modulo 4: the last
+    dword loads of the last row run past the end of the buffer.  An invalid
+    byte at the first and at the very last byte of the buffer is flagged."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
+    K = 640
+    w = inputs.normal_bf16(70 + G + N, (N, K), 0.02)
+    p, s, _ = oracle.quantize_pack(w, G)
+    flat = p.reshape(-1)
+    sd = dev_f16bits(s)
+    for M in (1, 5, 16):
+        x = inputs.activation(71 + M, M, K)
+        y_ref, bound, _ = oracle.matmul(x, p, s, N, K, G)
+        xd = dev_bf16(x)
+        say("gemv ragged M=%d N=%d K=%d G=%d" % (M, N, K, G))
+        st = tq.new_status()
+        y = tq.gemv(xd, dev_u8(p), sd, N, K, G, status=st).cpu().numpy()
+        assert int(st.item()) == 0
+        assert_within_bound(y, y_ref, bound, "gemv ragged M=%d N=%d G=%d" % (M, N, G))
+        for pos in (0, flat.size - 1):
+            bad = flat.copy()
+            bad[pos] = 243 + pos % 13
+            st = tq.new_status()
+            tq.gemv(xd, dev_u8(bad.reshape(p.shape)), sd, N, K, G, status=st)
+            torch.cuda.synchronize()
+            assert int(st.item()) & 4, "invalid byte at %d not flagged (M=%d)" % (pos, M)
+
+
 @pytest.mark.parametrize("M,N,K,G,count", [(512, 3584, 1024, 128, 3), (100, 200, 640, 64, 5),
                                            (300, 96, 320, 64, 70)])
 def test_gemm_batched_matches_single_calls_and_oracle(M, N, K, G, count):
