@@ -43,9 +43,6 @@ typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __attribute__((address_space(3))) const volatile u32x4 lds_u32x4_cv;
 typedef __attribute__((address_space(3))) const unsigned char lds_bytes_c;
 
-__device__ __forceinline__ float bf16_to_f32(uint16_t b) {
-  return __uint_as_float((uint32_t)b << 16);
-}
 
 __device__ __forceinline__ float dot2_bf16(uint32_t a, uint32_t b, float c) {
   return __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2_t, a),
@@ -116,14 +113,16 @@ struct GemvBatch {
 };
 
 // The work of a launch is count * nb row batches (nb per problem); a batch
-// is one row per row slot (R = 64W / Lp rows).  A block owns a contiguous
-// range of batches, which may cross from one problem into the next.  Threads
-// t = 0..64W-1 map to (row slot rr = t/Lp, chunk c = t % Lp); lanes with
-// c >= L idle.  Each lane keeps the packed bytes of its next D batches in
-// flight in a register ring.
+// is one row per row slot (R = 64W / Lp rows).  Block b takes segment b % S
+// of problem b / S: batches [s*nb/S, (s+1)*nb/S), so its activations are
+// loaded once.  Threads t = 0..64W-1 map to (row slot rr = t/Lp, chunk
+// c = t % Lp); lanes with c >= L idle.  Each lane keeps the packed bytes of
+// its next D batches in flight in a register ring; the loop body loads
+// unconditionally (batches past the segment read out of range, as zeros) and
+// its only store is predicated, so the loads stay D batches ahead.
 template <int G, int D, bool WAVE_ROWS>
 __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void gemv_m1_kernel(const GemvBatch args, int count, int N, int K, int L, int Lp,
+void gemv_m1_kernel(const GemvBatch args, int S, int N, int K, int L, int Lp,
                     int32_t *__restrict__ d_status) {
   __shared__ uint4 lut[kLutEntries * kCopies];
   __shared__ float segsum[2][4 * kMaxWaves];  // R * (Lp/16) = 4W floats per batch
@@ -140,12 +139,10 @@ void gemv_m1_kernel(const GemvBatch args, int count, int N, int K, int L, int Lp
   const uint32_t total = (uint32_t)N * rowbytes;  // < 2^31, checked by the launcher
   const int gidx = G == 64 ? c : (c >> 1);
   const int nb = (N + R - 1) / R;  // batches per problem
-  const int nbatches = nb * count;
-  const int q = nbatches / (int)gridDim.x, rmd = nbatches % (int)gridDim.x;
-  const int b_begin = (int)blockIdx.x * q + ((int)blockIdx.x < rmd ? (int)blockIdx.x : rmd);
-  const int b_end = b_begin + q + ((int)blockIdx.x < rmd ? 1 : 0);
+  const int pi = (int)blockIdx.x / S, seg = (int)blockIdx.x - pi * S;
+  const int b_begin = (int)(((int64_t)seg * nb) / S), b_end = (int)(((int64_t)(seg + 1) * nb) / S);
 
-  // lane's byte address of local batch b is a0 + b * bstep; idle lanes get
+  // lane's byte address of batch b is a0 + b * bstep; idle lanes get
   // an offset past any range so their loads read zeros.  Rows past N lie
   // past the end of the buffers and read zeros too (they are never stored).
   const uint32_t a0 = lane_on ? (uint32_t)rr * rowbytes + (uint32_t)c * kChunk : kOutOfRange;
@@ -153,21 +150,20 @@ void gemv_m1_kernel(const GemvBatch args, int count, int N, int K, int L, int Lp
   const uint32_t s0 = lane_on ? 2u * ((uint32_t)rr * (uint32_t)nG + (uint32_t)gidx) : kOutOfRange;
   const uint32_t sstep = 2u * (uint32_t)R * (uint32_t)nG;
   const uint32_t pbytes = (total + 3u) & ~3u, sbytes = (uint32_t)N * (uint32_t)nG * 2u;
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[pi], pbytes);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.scales[pi], sbytes);
+  float *__restrict__ yp = args.y[pi];
 
   u32x4 ring[D];
   uint32_t rofs[D], rsc[D];
-  auto issue = [&](int slot, int g) {
-    const int pi = g / nb, b = g - pi * nb;  // problem and local batch (uniform)
-    const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[pi], pbytes);
-    const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.scales[pi], sbytes);
+  auto issue = [&](int slot, int b) {  // batches at or past b_end read zeros
+    const bool on = b < b_end;
     const uint32_t a = a0 + (uint32_t)b * bstep;
-    ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, a & ~3u, 0, 0);
+    ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, on ? (a & ~3u) : kOutOfRange, 0, 0);
     rofs[slot] = a & 3u;
-    rsc[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, s0 + (uint32_t)b * sstep, 0, 0);
+    rsc[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, on ? s0 + (uint32_t)b * sstep : kOutOfRange,
+                                                     0, 0);
   };
-#pragma unroll
-  for (int d = 0; d < D; ++d)
-    if (b_begin + d < b_end) issue(d, b_begin + d);
 
   // Activations of this lane's chunk as bf16 pairs (x0,x1)(x2,x3)(x4,0) per
   // byte, from x[64c .. 64c+72) (zeros past K and for idle lanes).  The
@@ -209,8 +205,9 @@ void gemv_m1_kernel(const GemvBatch args, int count, int N, int K, int L, int Lp
       xa[kChunk - 1][2] = 0u;
     }
   };
-  int p_cur = b_begin < b_end ? b_begin / nb : 0;
-  load_x(p_cur);
+  load_x(pi);
+#pragma unroll
+  for (int d = 0; d < D; ++d) issue(d, b_begin + d);
 
   // table: each thread builds one entry and writes a share of its copies;
   // the copy index is rotated by the lane so a wave's 16-byte writes spread
@@ -235,79 +232,76 @@ void gemv_m1_kernel(const GemvBatch args, int count, int N, int K, int L, int Lp
   lds_bytes_c *lut_bytes = (lds_bytes_c *)(lut);
   uint32_t bad = 0;
   int buf = 0;
-  for (int g0 = b_begin; g0 < b_end; g0 += D) {
+  auto round = [&](int g0) {
 #pragma unroll
     for (int d = 0; d < D; ++d) {
-      const int g = g0 + d;
-      if (g < b_end) {  // uniform over the block
-        const int pi = g / nb, b = g - pi * nb;
-        if (pi != p_cur) {  // the block's range crossed into the next problem
-          p_cur = pi;
-          load_x(pi);
-        }
-        // realign the lane's 13 bytes to byte 0
-        const uint32_t o = rofs[d];
-        const u32x4 A = ring[d];
-        const uint32_t aw[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, o),
-                                __builtin_amdgcn_alignbyte(A.z, A.y, o),
-                                __builtin_amdgcn_alignbyte(A.w, A.z, o),
-                                __builtin_amdgcn_alignbyte(0u, A.w, o)};
-        const float sc = __half2float(__ushort_as_half((unsigned short)rsc[d]));
-        if (g + D < b_end) issue(d, g + D);  // refill the slot with the batch D ahead
-        u32x4 e[kChunk];
+      const int b = g0 + d;
+      // realign the lane's 13 bytes to byte 0
+      const uint32_t o = rofs[d];
+      const u32x4 A = ring[d];
+      const uint32_t aw[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, o),
+                              __builtin_amdgcn_alignbyte(A.z, A.y, o),
+                              __builtin_amdgcn_alignbyte(A.w, A.z, o),
+                              __builtin_amdgcn_alignbyte(0u, A.w, o)};
+      const float sc = __half2float(__ushort_as_half((unsigned short)rsc[d]));
+      issue(d, b + D);  // refill the slot with the batch D ahead
+      u32x4 e[kChunk];
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          // address = byte * 256 + copyoff: byte (j%4) of aw[j/4] into byte 1
-          const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
-          const uint32_t addr = __builtin_amdgcn_perm(copyoff, aw[j >> 2], sel);
-          // one full 128-bit read (ds_read_b128 outruns ds_read_b96 on
-          // gfx950); volatile keeps the compiler from narrowing it
-          e[j] = *(lds_u32x4_cv *)(lut_bytes + addr);
-        }
-        float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
+      for (int j = 0; j < kChunk; ++j) {
+        // address = byte * 256 + copyoff: byte (j%4) of aw[j/4] into byte 1
+        const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
+        const uint32_t addr = __builtin_amdgcn_perm(copyoff, aw[j >> 2], sel);
+        // one full 128-bit read (ds_read_b128 outruns ds_read_b96 on
+        // gfx950); volatile keeps the compiler from narrowing it
+        e[j] = *(lds_u32x4_cv *)(lut_bytes + addr);
+      }
+      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) {
-          float &acc = (j & 3) == 0 ? acc0 : (j & 3) == 1 ? acc1 : (j & 3) == 2 ? acc2 : acc3;
-          acc = dot2_bf16(e[j].x, xa[j][0], acc);
-          acc = dot2_bf16(e[j].y, xa[j][1], acc);
-          acc = dot2_bf16(e[j].z, xa[j][2], acc);
-        }
-        // The fourth dword of each read is unused; holding it to here stops
-        // the register allocator from reusing its register while the read is
-        // in flight (that reuse forces a wait right after the read).
+      for (int j = 0; j < kChunk; ++j) {
+        float &acc = (j & 3) == 0 ? acc0 : (j & 3) == 1 ? acc1 : (j & 3) == 2 ? acc2 : acc3;
+        acc = dot2_bf16(e[j].x, xa[j][0], acc);
+        acc = dot2_bf16(e[j].y, xa[j][1], acc);
+        acc = dot2_bf16(e[j].z, xa[j][2], acc);
+      }
+      // The fourth dword of each read is unused; holding it to here stops
+      // the register allocator from reusing its register while the read is
+      // in flight (that reuse forces a wait right after the read).
 #pragma unroll
-        for (int j = 0; j < kChunk; ++j) asm volatile("" ::"v"(e[j].w));
-        const float pc = (acc0 + acc1) + (acc2 + acc3);
-        float part = row16_sum(sc * pc);
-        float *__restrict__ yp = args.y[pi];
-        if (WAVE_ROWS) {
-          // a row is Lp <= 64 consecutive lanes of one wave: add its 16-lane
-          // rows with row_bcast15/31; the row's last lane holds the sum (an
-          // invalid byte anywhere in the row makes it NaN)
-          if (Lp >= 32) part += dpp_f32_rows<0x142, 0xA>(part);  // row_bcast:15
-          if (Lp >= 64) part += dpp_f32_rows<0x143, 0xC>(part);  // row_bcast:31
-          const int n = b * R + rr;
-          if (c == Lp - 1 && n < N) {
-            bad |= (part != part);
-            yp[n] = part;
+      for (int j = 0; j < kChunk; ++j) asm volatile("" ::"v"(e[j].w));
+      const float pc = (acc0 + acc1) + (acc2 + acc3);
+      float part = row16_sum(sc * pc);
+      const bool live = b < b_end;
+      if (WAVE_ROWS) {
+        // a row is Lp <= 64 consecutive lanes of one wave: add its 16-lane
+        // rows with row_bcast15/31; the row's last lane holds the sum (an
+        // invalid byte anywhere in the row makes it NaN)
+        if (Lp >= 32) part += dpp_f32_rows<0x142, 0xA>(part);  // row_bcast:15
+        if (Lp >= 64) part += dpp_f32_rows<0x143, 0xC>(part);  // row_bcast:31
+        const int n = b * R + rr;
+        if (live && c == Lp - 1 && n < N) {
+          bad |= (part != part);
+          yp[n] = part;
+        }
+      } else {
+        if ((tid & 15) == 0) segsum[buf][rr * nseg + c / 16] = part;
+        __syncthreads();
+        if (tid < R) {
+          const int n = b * R + tid;
+          if (live && n < N) {
+            float sum = 0.f;
+            for (int k = 0; k < nseg; ++k) sum += segsum[buf][tid * nseg + k];
+            bad |= (sum != sum);
+            yp[n] = sum;
           }
-        } else {
-          if ((tid & 15) == 0) segsum[buf][rr * nseg + c / 16] = part;
-          __syncthreads();
-          if (tid < R) {
-            const int n = b * R + tid;
-            if (n < N) {
-              float sum = 0.f;
-              for (int k = 0; k < nseg; ++k) sum += segsum[buf][tid * nseg + k];
-              bad |= (sum != sum);
-              yp[n] = sum;
-            }
-          }
-          buf ^= 1;
         }
+        buf ^= 1;
       }
     }
-  }
+  };
+  // The first round is peeled so that the loop is entered with its loads in
+  // flight in the same order as on its back edge.
+  if (b_begin < b_end) round(b_begin);
+  for (int g0 = b_begin + D; g0 < b_end; g0 += D) round(g0);
   if (bad && d_status) atomicOr(d_status, kDevInvalidByte);
 }
 
@@ -336,16 +330,19 @@ void launch_m1(const GemvBatch &args, int count, int64_t N, int64_t K, int32_t *
   const int Lp = 16 * ((L + 15) / 16);
   const int threads = 64 * m1_waves(K);
   const int R = threads / Lp;
-  // persistent blocks: two per CU fit the 64 KB table
-  const int64_t nbatches = (N + R - 1) / R * count;
-  const int cap = 2 * 256;
-  const int grid = (int)(nbatches < cap ? nbatches : cap);
+  // segments per problem: at most two blocks per CU over the whole launch
+  // (two fit the 64 KB table), so every block is resident from the start,
+  // and at least one batch per segment
+  const int64_t nb = (N + R - 1) / R;
+  const int64_t want = count <= 2 * 256 ? (2 * 256) / count : 1;
+  const int S = (int)(want < nb ? want : nb);
+  const int grid = count * S;
   if (Lp <= 64)
     hipLaunchKernelGGL((gemv_m1_kernel<G, kRing, true>), dim3(grid), dim3(threads), 0, stream,
-                       args, count, (int)N, (int)K, L, Lp, d_status);
+                       args, S, (int)N, (int)K, L, Lp, d_status);
   else
     hipLaunchKernelGGL((gemv_m1_kernel<G, kRing, false>), dim3(grid), dim3(threads), 0, stream,
-                       args, count, (int)N, (int)K, L, Lp, d_status);
+                       args, S, (int)N, (int)K, L, Lp, d_status);
 }
 
 bool m1_supported(int64_t M, int64_t N, int64_t K) {
