@@ -30,6 +30,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -53,22 +55,6 @@ template <int CTRL>
 __device__ __forceinline__ float dpp_f32(float v) {
   return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
                                                                0xF, 0xF, false));
-}
-
-// DPP move restricted to the rows in ROWMASK (other rows read 0).
-template <int CTRL, int ROWMASK>
-__device__ __forceinline__ float dpp_f32_rows(float v) {
-  return __builtin_bit_cast(float, __builtin_amdgcn_update_dpp(0, __builtin_bit_cast(int, v), CTRL,
-                                                               ROWMASK, 0xF, false));
-}
-
-// Sum over each row of 16 lanes; every lane of the row receives the sum.
-__device__ __forceinline__ float row16_sum(float v) {
-  v += dpp_f32<0xB1>(v);   // quad_perm [1,0,3,2]
-  v += dpp_f32<0x4E>(v);   // quad_perm [2,3,0,1]
-  v += dpp_f32<0x141>(v);  // row_half_mirror
-  v += dpp_f32<0x140>(v);  // row_mirror
-  return v;
 }
 
 // ---------------------------------------------------------------------------
@@ -101,6 +87,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 }
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
+constexpr uint32_t kFar = 0x40000000u;  // buffer ranges here stay below this
 constexpr int kRing = 4;  // row batches in flight per lane
 constexpr int kMaxBatch = 64;  // problems per batched launch
 
@@ -113,34 +100,69 @@ struct GemvBatch {
 };
 
 // The work of a launch is count * nb row batches (nb per problem); a batch
-// is one row per row slot (R = 64W / Lp rows).  Block b takes segment b % S
-// of problem b / S: batches [s*nb/S, (s+1)*nb/S), so its activations are
-// loaded once.  Threads t = 0..64W-1 map to (row slot rr = t/Lp, chunk
+// is one row per row slot (R = 64W / Lp rows).  Block (s, p) of the 2-D grid
+// takes segment s of problem p: q or q+1 consecutive batches starting at
+// s*q + min(s, rem), so its activations are loaded once and no block
+// divides.  Threads t = 0..64W-1 map to (row slot rr = t/Lp, chunk
 // c = t % Lp); lanes with c >= L idle.  Each lane keeps the packed bytes of
 // its next D batches in flight in a register ring; the loop body loads
 // unconditionally (batches past the segment read out of range, as zeros) and
 // its only store is predicated, so the loads stay D batches ahead.
-template <int G, int D, bool WAVE_ROWS>
+//
+// Start-up order: the activations are requested first, then the first D
+// batches of packed bytes; the table is built while both are in flight.
+// Then the activations reach registers in one of two ways:
+//   * staged (XDIRECT false): the block loads x once (XL 16-byte pieces per
+//     thread at most) into LDS, padded by 16 bytes after every 128, and each
+//     lane reads its 144-byte window from there: lanes 16 apart in chunk
+//     index land in different bank groups, and the caches see one copy of x
+//     per block instead of one per row of a batch;
+//   * direct (XDIRECT true, long rows whose staged copy would not leave room
+//     for two blocks per CU): each lane loads its window itself; a batch
+//     then has few rows, so little is loaded twice.
+template <int G, bool WAVE_ROWS, int XL, bool XDIRECT, bool AL>
 __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void gemv_m1_kernel(const GemvBatch args, int S, int N, int K, int L, int Lp,
-                    int32_t *__restrict__ d_status) {
+void gemv_m1_kernel(const GemvBatch args, int N, int K, int L, int Lp, int R, float inv_lp,
+                    int q, int rem, int32_t *__restrict__ d_status) {
   __shared__ uint4 lut[kLutEntries * kCopies];
-  __shared__ float segsum[2][4 * kMaxWaves];  // R * (Lp/16) = 4W floats per batch
+  __shared__ float segsum[2][16 * kMaxWaves];  // 4 batches x R x (Lp/16) = 16W floats
+  typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+  extern __shared__ u32x4 xstage_[];  // staged activations (dynamic size)
+  lds_u32x4 *xstage = (lds_u32x4 *)xstage_;
 
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
-  const int R = nthreads / Lp;  // rows per batch
-  const int nseg = Lp / 16;     // 16-lane segments per row
-  const int rr = tid / Lp;
-  const int c = tid % Lp;
+  const int nseg = Lp >> 4;  // 16-lane segments per row
+  // tid / Lp through a rounded reciprocal: (tid + 1/2) / Lp lies at least
+  // 1/(2 Lp) away from an integer, far more than the float error here
+  const int rr = (int)(((float)tid + 0.5f) * inv_lp);
+  const int c = tid - rr * Lp;
   const bool lane_on = c < L;
   const int nG = K / G;
   const uint32_t rowbytes = (uint32_t)L * kChunk;
-  const uint32_t total = (uint32_t)N * rowbytes;  // < 2^31, checked by the launcher
+  const uint32_t total = (uint32_t)N * rowbytes;  // < 2^30, checked by the launcher
   const int gidx = G == 64 ? c : (c >> 1);
-  const int nb = (N + R - 1) / R;  // batches per problem
-  const int pi = (int)blockIdx.x / S, seg = (int)blockIdx.x - pi * S;
-  const int b_begin = (int)(((int64_t)seg * nb) / S), b_end = (int)(((int64_t)(seg + 1) * nb) / S);
+  const int pi = (int)blockIdx.y, seg = (int)blockIdx.x;
+  const int b_begin = seg * q + (seg < rem ? seg : rem);
+  const int b_end = b_begin + q + (seg < rem ? 1 : 0);
+
+  // activations x[0, K); reads past the end give zeros (the last lane's
+  // window reaches 16 bytes beyond x)
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[pi], (uint32_t)K * 2u);
+  const int nxc = (K >> 3) + 1;  // staged 16-byte pieces: x plus one of zeros
+  constexpr int kXLoads = XDIRECT ? 9 : XL;
+  u32x4 xv[kXLoads];
+#pragma unroll
+  for (int i = 0; i < kXLoads; ++i) {
+    uint32_t off;
+    if (XDIRECT) {
+      off = lane_on ? 128u * (uint32_t)c + 16u * (uint32_t)i : kOutOfRange;
+    } else {
+      const int j = tid + i * nthreads;
+      off = j < nxc ? 16u * (uint32_t)j : kOutOfRange;
+    }
+    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+  }
 
   // lane's byte address of batch b is a0 + b * bstep; idle lanes get
   // an offset past any range so their loads read zeros.  Rows past N lie
@@ -151,32 +173,83 @@ void gemv_m1_kernel(const GemvBatch args, int S, int N, int K, int L, int Lp,
   const uint32_t sstep = 2u * (uint32_t)R * (uint32_t)nG;
   const uint32_t pbytes = (total + 3u) & ~3u, sbytes = (uint32_t)N * (uint32_t)nG * 2u;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[pi], pbytes);
-  const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.scales[pi], sbytes);
+  // scales are read as the aligned dwords holding them (a 16-bit load's
+  // result would be copied between registers at the loop's back edge, which
+  // makes the loop wait for every load in flight); the range is widened to
+  // whole dwords, which never reaches past a page the buffer touches
+  const uintptr_t sp = (uintptr_t)args.scales[pi];
+  const uint32_t shead = (uint32_t)(sp & 3u);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc((const void *)(sp - shead), (sbytes + shead + 3u) & ~3u);
   float *__restrict__ yp = args.y[pi];
 
-  u32x4 ring[D];
-  uint32_t rofs[D], rsc[D];
+  // With AL (both batch steps multiples of 4 bytes) a lane's byte offset
+  // within its dword and the half holding its scale are the same for every
+  // batch, and a batch's load offsets are the lane's base plus a uniform
+  // step, or plus kFar past the segment (bases and ranges stay below kFar,
+  // so the sums stay past the range without wrapping).
+  const uint32_t o_lane = a0 & 3u, sh_lane = ((shead + s0) & 2u) << 3;
+  const uint32_t a0al = lane_on ? (a0 & ~3u) : kOutOfRange;
+  const uint32_t s0al = lane_on ? ((shead + s0) & ~3u) : kOutOfRange;
+  u32x4 ring[kRing];
+  uint32_t rsc[kRing];
   auto issue = [&](int slot, int b) {  // batches at or past b_end read zeros
     const bool on = b < b_end;
-    const uint32_t a = a0 + (uint32_t)b * bstep;
-    ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, on ? (a & ~3u) : kOutOfRange, 0, 0);
-    rofs[slot] = a & 3u;
-    rsc[slot] = __builtin_amdgcn_raw_buffer_load_b16(rs, on ? s0 + (uint32_t)b * sstep : kOutOfRange,
-                                                     0, 0);
+    if (AL) {
+      const uint32_t pb = on ? (uint32_t)b * bstep : kFar, sb = on ? (uint32_t)b * sstep : kFar;
+      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, a0al + pb, 0, 0);
+      rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, s0al + sb, 0, 0);
+    } else {
+      const uint32_t a = a0 + (uint32_t)b * bstep;
+      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, on ? (a & ~3u) : kOutOfRange, 0, 0);
+      rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(
+          rs, on ? ((shead + s0 + (uint32_t)b * sstep) & ~3u) : kOutOfRange, 0, 0);
+    }
   };
+#pragma unroll
+  for (int d = 0; d < kRing; ++d) issue(d, b_begin + d);
+
+  // table: each thread builds one entry and writes a share of its copies;
+  // the copy index is rotated by the lane so a wave's 16-byte writes spread
+  // over all 16 bank groups
+  {
+    const int ent = tid % kLutEntries;
+    const uint4 e = lut_entry((uint32_t)ent);
+    const int per = nthreads >= 2 * kLutEntries ? 2 : 1;  // threads per entry (>= 256 threads)
+    const int share = kCopies / per;
+    const int first = (tid / kLutEntries) * share;
+    if (tid < per * kLutEntries) {
+      for (int k = 0; k < share; ++k) {
+        const int cp = (first + k + tid) % kCopies;
+        lut[ent * kCopies + cp] = e;
+      }
+    }
+  }
+  if constexpr (!XDIRECT) {
+    // piece j goes to slot j + j/8
+#pragma unroll
+    for (int i = 0; i < XL; ++i) {
+      const int j = tid + i * nthreads;
+      if (j < nxc) xstage[j + (j >> 3)] = xv[i];
+    }
+  }
+  __syncthreads();
 
   // Activations of this lane's chunk as bf16 pairs (x0,x1)(x2,x3)(x4,0) per
-  // byte, from x[64c .. 64c+72) (zeros past K and for idle lanes).  The
-  // lane's trit p is x[64c + h + p] (h = 1 for the second half of a G=128
-  // group); Dn[i] holds the pair (x[64c+h+2i], x[64c+h+2i+1]).
+  // byte, from x[64c .. 64c+72) (pieces 8c .. 8c+8, at slots 9c .. 9c+9 of
+  // the staged copy; zeros for idle lanes).  The lane's trit p is
+  // x[64c + h + p] (h = 1 for the second half of a G=128 group); Dn[i] holds
+  // the pair (x[64c+h+2i], x[64c+h+2i+1]).
   uint32_t xa[kChunk][3];
-  auto load_x = [&](int pi) {
-    const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[pi], (uint32_t)K * 2u);
+  {
     u32x4 xr[9];
 #pragma unroll
-    for (int i = 0; i < 9; ++i)
-      xr[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, lane_on ? 128u * c + 16u * i : kOutOfRange,
-                                                    0, 0);
+    for (int i = 0; i < 9; ++i) {
+      if constexpr (XDIRECT)
+        xr[i] = xv[i];
+      else
+        xr[i] = lane_on ? xstage[9 * c + i + (i >> 3)] : u32x4{0u, 0u, 0u, 0u};
+    }
     const int h = (G == 128) ? (c & 1) : 0;
     uint32_t Dw[36];
 #pragma unroll
@@ -204,111 +277,113 @@ void gemv_m1_kernel(const GemvBatch args, int S, int N, int K, int L, int Lp,
       xa[kChunk - 1][1] &= 0xFFFFu;
       xa[kChunk - 1][2] = 0u;
     }
-  };
-  load_x(pi);
-#pragma unroll
-  for (int d = 0; d < D; ++d) issue(d, b_begin + d);
-
-  // table: each thread builds one entry and writes a share of its copies;
-  // the copy index is rotated by the lane so a wave's 16-byte writes spread
-  // over all 16 bank groups
-  {
-    const int ent = tid % kLutEntries;
-    const uint4 e = lut_entry((uint32_t)ent);
-    const int per = nthreads >= 2 * kLutEntries ? 2 : 1;  // threads per entry (>= 256 threads)
-    const int share = kCopies / per;
-    const int first = (tid / kLutEntries) * share;
-    if (tid < per * kLutEntries) {
-      for (int k = 0; k < share; ++k) {
-        const int cp = (first + k + tid) % kCopies;
-        lut[ent * kCopies + cp] = e;
-      }
-    }
   }
   // per-lane byte offset of its table copy, in byte 0 of a perm source
   const uint32_t copyoff = (uint32_t)(tid % kCopies) * 16u;
-  __syncthreads();
 
   lds_bytes_c *lut_bytes = (lds_bytes_c *)(lut);
   uint32_t bad = 0;
   int buf = 0;
+  const int l16 = tid & 15;  // lane within its 16-lane DPP row
+  const bool hi8 = (l16 & 8) != 0, hi4 = (l16 & 4) != 0;
   auto round = [&](int g0) {
+    float v[kRing];
 #pragma unroll
-    for (int d = 0; d < D; ++d) {
+    for (int d = 0; d < kRing; ++d) {
       const int b = g0 + d;
       // realign the lane's 13 bytes to byte 0
-      const uint32_t o = rofs[d];
+      const uint32_t o = AL ? o_lane : ((a0 + (uint32_t)b * bstep) & 3u);
       const u32x4 A = ring[d];
       const uint32_t aw[4] = {__builtin_amdgcn_alignbyte(A.y, A.x, o),
                               __builtin_amdgcn_alignbyte(A.z, A.y, o),
                               __builtin_amdgcn_alignbyte(A.w, A.z, o),
                               __builtin_amdgcn_alignbyte(0u, A.w, o)};
-      const float sc = __half2float(__ushort_as_half((unsigned short)rsc[d]));
-      issue(d, b + D);  // refill the slot with the batch D ahead
-      u32x4 e[kChunk];
+      // the scale is the low or high half of its dword
+      const uint32_t sh = AL ? sh_lane : (((shead + s0 + (uint32_t)b * sstep) & 2u) << 3);
+      const float sc = __half2float(__ushort_as_half((unsigned short)(rsc[d] >> sh)));
+      issue(d, b + kRing);  // refill the slot with the batch kRing ahead
+      // the lookups go in two halves (7 + 6 bytes), each read in full
+      // before its products, which keeps register use within four waves
+      // per SIMD; one accumulator chain per chunk
+      float acc = 0.f;
+      auto half = [&](auto J0, auto J1) {
+        constexpr int j0 = decltype(J0)::value, j1 = decltype(J1)::value;
+        u32x4 e[j1 - j0];
 #pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        // address = byte * 256 + copyoff: byte (j%4) of aw[j/4] into byte 1
-        const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
-        const uint32_t addr = __builtin_amdgcn_perm(copyoff, aw[j >> 2], sel);
-        // one full 128-bit read (ds_read_b128 outruns ds_read_b96 on
-        // gfx950); volatile keeps the compiler from narrowing it
-        e[j] = *(lds_u32x4_cv *)(lut_bytes + addr);
-      }
-      float acc0 = 0.f, acc1 = 0.f, acc2 = 0.f, acc3 = 0.f;
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) {
-        float &acc = (j & 3) == 0 ? acc0 : (j & 3) == 1 ? acc1 : (j & 3) == 2 ? acc2 : acc3;
-        acc = dot2_bf16(e[j].x, xa[j][0], acc);
-        acc = dot2_bf16(e[j].y, xa[j][1], acc);
-        acc = dot2_bf16(e[j].z, xa[j][2], acc);
-      }
-      // The fourth dword of each read is unused; holding it to here stops
-      // the register allocator from reusing its register while the read is
-      // in flight (that reuse forces a wait right after the read).
-#pragma unroll
-      for (int j = 0; j < kChunk; ++j) asm volatile("" ::"v"(e[j].w));
-      const float pc = (acc0 + acc1) + (acc2 + acc3);
-      float part = row16_sum(sc * pc);
-      const bool live = b < b_end;
-      if (WAVE_ROWS) {
-        // a row is Lp <= 64 consecutive lanes of one wave: add its 16-lane
-        // rows with row_bcast15/31; the row's last lane holds the sum (an
-        // invalid byte anywhere in the row makes it NaN)
-        if (Lp >= 32) part += dpp_f32_rows<0x142, 0xA>(part);  // row_bcast:15
-        if (Lp >= 64) part += dpp_f32_rows<0x143, 0xC>(part);  // row_bcast:31
-        const int n = b * R + rr;
-        if (live && c == Lp - 1 && n < N) {
-          bad |= (part != part);
-          yp[n] = part;
+        for (int j = j0; j < j1; ++j) {
+          // address = byte * 256 + copyoff: byte (j%4) of aw[j/4] into byte 1
+          const uint32_t sel = 0x0C0C0004u | ((uint32_t)(j & 3) << 8);
+          const uint32_t addr = __builtin_amdgcn_perm(copyoff, aw[j >> 2], sel);
+          // one full 128-bit read (ds_read_b128 outruns ds_read_b96 on
+          // gfx950); volatile keeps the compiler from narrowing it
+          e[j - j0] = *(lds_u32x4_cv *)(lut_bytes + addr);
         }
-      } else {
-        if ((tid & 15) == 0) segsum[buf][rr * nseg + c / 16] = part;
-        __syncthreads();
-        if (tid < R) {
-          const int n = b * R + tid;
-          if (live && n < N) {
-            float sum = 0.f;
-            for (int k = 0; k < nseg; ++k) sum += segsum[buf][tid * nseg + k];
-            bad |= (sum != sum);
-            yp[n] = sum;
-          }
+#pragma unroll
+        for (int j = j0; j < j1; ++j) {
+          acc = dot2_bf16(e[j - j0].x, xa[j][0], acc);
+          acc = dot2_bf16(e[j - j0].y, xa[j][1], acc);
+          acc = dot2_bf16(e[j - j0].z, xa[j][2], acc);
         }
-        buf ^= 1;
+        // The fourth dword of each read is unused; holding it to here stops
+        // the register allocator from reusing its register while the read
+        // is in flight (that reuse forces a wait right after the read).
+#pragma unroll
+        for (int j = j0; j < j1; ++j) asm volatile("" ::"v"(e[j - j0].w));
+      };
+      half(std::integral_constant<int, 0>{}, std::integral_constant<int, 7>{});
+      half(std::integral_constant<int, 7>{}, std::integral_constant<int, kChunk>{});
+      v[d] = sc * acc;
+    }
+    // Sum each batch's chunk values over the 16 lanes of a DPP row, four
+    // batches at once: exchange halves across lane bit 3 (row_ror:8), then
+    // across bit 2 (row_half_mirror), then add within quads.  Afterwards
+    // every lane of quad k (lanes 4k..4k+3 of the row) holds batch k's sum.
+    const float keep0 = hi8 ? v[2] : v[0], send0 = hi8 ? v[0] : v[2];
+    const float keep1 = hi8 ? v[3] : v[1], send1 = hi8 ? v[1] : v[3];
+    const float u0 = keep0 + dpp_f32<0x128>(send0);  // row_ror:8
+    const float u1 = keep1 + dpp_f32<0x128>(send1);
+    const float keep = hi4 ? u1 : u0, send = hi4 ? u0 : u1;
+    float s = keep + dpp_f32<0x141>(send);  // row_half_mirror
+    s += dpp_f32<0xB1>(s);                  // quad_perm [1,0,3,2]
+    s += dpp_f32<0x4E>(s);                  // quad_perm [2,3,0,1]
+    const int k = l16 >> 2;                 // this lane's batch
+    if (WAVE_ROWS) {
+      // a row is Lp = 16, 32 or 64 lanes of one wave: add its DPP rows
+      if (Lp >= 32) s += __shfl_xor(s, 16);
+      if (Lp >= 64) s += __shfl_xor(s, 32);
+      const int n = (g0 + k) * R + rr;
+      if (c < 16 && (l16 & 3) == 0 && g0 + k < b_end && n < N) {
+        bad |= (s != s);
+        yp[n] = s;
       }
+    } else {
+      // rows span waves: add the row's Lp/16 DPP-row sums through LDS
+      float *ss = segsum[buf];
+      if ((l16 & 3) == 0) ss[(k * R + rr) * nseg + (c >> 4)] = s;
+      __syncthreads();
+      if (tid < kRing * R) {
+        const int kk = tid & 3, r = tid >> 2;
+        const int n = (g0 + kk) * R + r;
+        if (g0 + kk < b_end && n < N) {
+          float sum = 0.f;
+          for (int j = 0; j < nseg; ++j) sum += ss[(kk * R + r) * nseg + j];
+          bad |= (sum != sum);
+          yp[n] = sum;
+        }
+      }
+      buf ^= 1;
     }
   };
   // The first round is peeled so that the loop is entered with its loads in
-  // flight in the same order as on its back edge.
-  if (b_begin < b_end) round(b_begin);
-  for (int g0 = b_begin + D; g0 < b_end; g0 += D) round(g0);
+  // flight in the same order as on its back edge.  Every segment holds at
+  // least one batch (the launcher makes at most nb segments), so the peeled
+  // round runs unconditionally: no path reaches the loop around it, with
+  // the start-up loads in another order.
+  round(b_begin);
+  for (int g0 = b_begin + kRing; g0 < b_end; g0 += kRing) round(g0);
   if (bad && d_status) atomicOr(d_status, kDevInvalidByte);
 }
 
-// ---------------------------------------------------------------------------
-// General fallback: one wave per row, lanes stride over the row's groups.
-// Used for 2 <= M <= 16 and for K > 16384.
-// ---------------------------------------------------------------------------
 // Blocks of W waves whose threads tile whole rows: Lp = 16*ceil(K/1024)
 // lanes per row must divide 64*W with W <= 8; 0 when no such W exists.
 int m1_waves(int64_t K) {
@@ -323,30 +398,84 @@ int m1_waves(int64_t K) {
   return w0 * (8 / w0);   // up to 8 waves per block
 }
 
+// LDS of one block: the table, the segment sums and the staged activations
+// (16-byte pieces of x plus a zero piece, one pad slot after every 8);
+// two blocks per CU need at most half of the CU's 160 KB
+constexpr int kStaticLds = kLutEntries * kCopies * 16 + 2 * 16 * kMaxWaves * 4;
+int m1_stage_bytes(int K) {
+  const int nxc = K / 8 + 1;
+  return 16 * (nxc + (nxc - 1) / 8 + 1);
+}
+bool m1_staged(int K) { return kStaticLds + m1_stage_bytes(K) <= 80 * 1024; }
+
+struct M1Shape {
+  dim3 grid;
+  int threads, N, K, L, Lp, R, q, rem;
+};
+
+template <int G, bool WR, int XL, bool XD, bool AL>
+void launch_m1_k(const GemvBatch &args, const M1Shape &s, int32_t *d_status, hipStream_t stream) {
+  const int lds = XD ? 0 : m1_stage_bytes(s.K);
+  hipLaunchKernelGGL((gemv_m1_kernel<G, WR, XL, XD, AL>), s.grid, dim3(s.threads), lds, stream,
+                     args, s.N, s.K, s.L, s.Lp, s.R, 1.0f / (float)s.Lp, s.q, s.rem, d_status);
+}
+
+template <int G, bool WR, int XL, bool XD>
+void launch_m1_al(const GemvBatch &args, const M1Shape &s, int32_t *d_status, hipStream_t stream) {
+  // both batch steps (R rows of packed bytes, R rows of scales) in whole dwords
+  const int64_t bstep = (int64_t)s.R * s.L * kChunk, sstep = 2 * (int64_t)s.R * (s.K / G);
+  if (bstep % 4 == 0 && sstep % 4 == 0)
+    launch_m1_k<G, WR, XL, XD, true>(args, s, d_status, stream);
+  else
+    launch_m1_k<G, WR, XL, XD, false>(args, s, d_status, stream);
+}
+
+template <int G, bool WR>
+void launch_m1_wr(const GemvBatch &args, const M1Shape &s, int32_t *d_status, hipStream_t stream) {
+  if (!m1_staged(s.K)) {
+    launch_m1_al<G, WR, 1, true>(args, s, d_status, stream);
+    return;
+  }
+  // staged 16-byte pieces of activations (plus a zero piece) per thread
+  const int xl = ((s.K >> 3) + 1 + s.threads - 1) / s.threads;
+  if (xl <= 1)
+    launch_m1_al<G, WR, 1, false>(args, s, d_status, stream);
+  else if (xl <= 2)
+    launch_m1_al<G, WR, 2, false>(args, s, d_status, stream);
+  else
+    launch_m1_al<G, WR, 3, false>(args, s, d_status, stream);
+}
+
 template <int G>
 void launch_m1(const GemvBatch &args, int count, int64_t N, int64_t K, int32_t *d_status,
                hipStream_t stream) {
-  const int L = (int)(K / 64);
-  const int Lp = 16 * ((L + 15) / 16);
-  const int threads = 64 * m1_waves(K);
-  const int R = threads / Lp;
+  M1Shape s;
+  s.N = (int)N;
+  s.K = (int)K;
+  s.L = (int)(K / 64);
+  s.Lp = 16 * ((s.L + 15) / 16);
+  s.threads = 64 * m1_waves(K);
+  s.R = s.threads / s.Lp;
   // segments per problem: at most two blocks per CU over the whole launch
   // (two fit the 64 KB table), so every block is resident from the start,
   // and at least one batch per segment
-  const int64_t nb = (N + R - 1) / R;
+  const int64_t nb = (N + s.R - 1) / s.R;
   const int64_t want = count <= 2 * 256 ? (2 * 256) / count : 1;
   const int S = (int)(want < nb ? want : nb);
-  const int grid = count * S;
-  if (Lp <= 64)
-    hipLaunchKernelGGL((gemv_m1_kernel<G, kRing, true>), dim3(grid), dim3(threads), 0, stream,
-                       args, S, (int)N, (int)K, L, Lp, d_status);
+  s.q = (int)(nb / S);
+  s.rem = (int)(nb % S);
+  s.grid = dim3(S, count);
+  // rows within one wave (16, 32 or 64 lanes) are summed with cross-lane
+  // moves; longer rows, or 48-lane rows that cross waves, through LDS
+  if (s.Lp == 16 || s.Lp == 32 || s.Lp == 64)
+    launch_m1_wr<G, true>(args, s, d_status, stream);
   else
-    hipLaunchKernelGGL((gemv_m1_kernel<G, kRing, false>), dim3(grid), dim3(threads), 0, stream,
-                       args, S, (int)N, (int)K, L, Lp, d_status);
+    launch_m1_wr<G, false>(args, s, d_status, stream);
 }
 
 bool m1_supported(int64_t M, int64_t N, int64_t K) {
-  return M == 1 && m1_waves(K) > 0 && N * (K / 64) * 13 < (int64_t(1) << 31);
+  // packed bytes below 1 GiB: offsets plus kFar never wrap
+  return M == 1 && m1_waves(K) > 0 && N * (K / 64) * 13 < (int64_t(1) << 30);
 }
 
 }  // namespace

@@ -259,6 +259,40 @@ def test_gemv_ragged_buffer_ends_and_invalid_bytes(G, N):
             assert int(st.item()) & 4, "invalid byte at %d not flagged (M=%d)" % (pos, M)
 
 
+# Row lengths K that take every block shape of the one-row kernel: 16-, 32-
+# and 64-lane rows summed inside a wave, 48-lane rows that cross waves, and
+# 80- to 256-lane rows summed through LDS; activations staged through LDS or
+# loaded per lane; batch steps in whole dwords or not (K = 9280 and 13376
+# give odd byte offsets from one batch to the next).
+@pytest.mark.parametrize("K,G", [(1088, 64), (2048, 128), (2560, 64), (3072, 128), (4160, 64),
+                                 (6144, 128), (7168, 64), (8192, 128), (9280, 64), (13376, 64),
+                                 (16384, 128)])
+def test_gemv_row_shapes(K, G):
+    """tq_gemv at M = 1 over K values covering each row shape, N = 37 (a
+    ragged last batch of rows); an invalid byte in the middle of the buffer
+    is flagged."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
+    N = 37
+    w = inputs.normal_bf16(90 + K // 64, (N, K), 0.02)
+    p, s, _ = oracle.quantize_pack(w, G)
+    x = inputs.activation(91, 1, K)
+    y_ref, bound, _ = oracle.matmul(x, p, s, N, K, G)
+    say("gemv row shape M=1 N=%d K=%d G=%d" % (N, K, G))
+    xd, sd = dev_bf16(x), dev_f16bits(s)
+    st = tq.new_status()
+    y = tq.gemv(xd, dev_u8(p), sd, N, K, G, status=st).cpu().numpy()
+    assert int(st.item()) == 0
+    assert_within_bound(y, y_ref, bound, "gemv M=1 N=%d K=%d G=%d" % (N, K, G))
+    bad = p.reshape(-1).copy()
+    bad[bad.size // 2 + 3] = 250
+    st = tq.new_status()
+    tq.gemv(xd, dev_u8(bad.reshape(p.shape)), sd, N, K, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 4
+
+
 @pytest.mark.parametrize("M,N,K,G,count", [(512, 3584, 1024, 128, 3), (100, 200, 640, 64, 5),
                                            (300, 96, 320, 64, 70)])
 def test_gemm_batched_matches_single_calls_and_oracle(M, N, K, G, count):
