@@ -12,11 +12,20 @@ hot path over that stack, in this order:
       likewise two launches; each matrix has its own activations' output)
   a1-a3 quantize + pack all 72 bf16 matrices                (tq_quantize_pack)
   a4  unpack + validate all 72 packed matrices              (tq_unpack)
-The packed weights live in a ring of three slots; step t reads slot t%3 and
-packs into slot (t+2)%3, so the weights a GEMV reads were written two steps
-(over 2 GB of traffic) earlier and come from HBM, not from the caches.
-Each row's launches are captured in a HIP graph; HIP events between the
-graph replays time each row on the stream the kernels run on.
+The packed weights live in a ring of eight slots (480 MB, more than the
+256 MB memory-side cache); step t reads slot t%8 and packs into slot
+(t+2)%8, so the weights a GEMV reads were written six steps (several GB of
+traffic) earlier and come from HBM, not from the caches.
+The GEMV and GEMM rows are direct launches (two batched calls each); the 72
+launches of each of the other two rows are captured in a HIP graph.  HIP
+events between the rows time each row on the stream the kernels run on, so
+a row's time includes its launches' dispatch.
+
+The roofline entry times the GEMV kernel itself: after the timed steps, the
+decode pass runs over all eight slots back to back (16 launches, so each
+launch's dispatch overlaps the previous kernel) between two HIP events, and
+the average launch is the elapsed time / 16; every slot is read once per
+chain, after 7 others (405 MB), so the weights again come from HBM.
 
 `value` is the decode GEMV's packed-weight bandwidth: (packed code bytes +
 fp16 scale bytes of the 72 matrices) / GEMV time per step.  The JSON line
@@ -118,7 +127,7 @@ def main():
     w_dev = [bf16(w) for w in mats]
     x_dec = [bf16(x) for x in x_dec_host]
     x_pre = {K: bf16(inputs.activation(30 + K, MP, K)) for K in sorted({k for _, k in shapes})}
-    RING = 3
+    RING = 8
     P = [[torch.empty(tq.packed_bytes(N, K, G), dtype=torch.uint8, device=dev) for N, K in shapes]
          for _ in range(RING)]
     S = [[torch.empty(N * (K // G), dtype=torch.float16, device=dev) for N, K in shapes]
@@ -140,32 +149,37 @@ def main():
             assert rc == 0, rc
 
     # the decode pass: two batched calls (gate+up of all layers share K=1024,
-    # the downs K=3584), one launch each
+    # the downs K=3584), one launch each; the pointer arrays of every slot
+    # are built once
     groups = {}
     for i, (N, K) in enumerate(shapes):
         groups.setdefault((N, K), []).append(i)
     arr = ctypes.c_void_p
 
+    def ptrs(ts):
+        return (arr * len(ts))(*[t.data_ptr() for t in ts])
+
+    y_pre = [torch.empty(MP, N, dtype=torch.float32, device=dev) for N, K in shapes]
+    calls = {}  # (slot, (N, K)) -> pointer arrays of the GEMV and GEMM calls
+    for slot in range(RING):
+        for key, idx in groups.items():
+            calls[(slot, key)] = (
+                len(idx), ptrs([x_dec[i] for i in idx]), ptrs([P[slot][i] for i in idx]),
+                ptrs([S[slot][i] for i in idx]), ptrs([y_dec[i] for i in idx]),
+                ptrs([x_pre[key[1]] for i in idx]), ptrs([y_pre[i] for i in idx]))
+
     def run_gemv(slot, stream):
-        for (N, K), idx in groups.items():
-            ax = (arr * len(idx))(*[x_dec[i].data_ptr() for i in idx])
-            ap = (arr * len(idx))(*[P[slot][i].data_ptr() for i in idx])
-            asc = (arr * len(idx))(*[S[slot][i].data_ptr() for i in idx])
-            ay = (arr * len(idx))(*[y_dec[i].data_ptr() for i in idx])
-            rc = L.tq_gemv_batched(len(idx), ax, ap, asc, ay, 1, N, K, G, stp, stream)
+        for (N, K) in groups:
+            n, ax, ap, asc, ay, _, _ = calls[(slot, (N, K))]
+            rc = L.tq_gemv_batched(n, ax, ap, asc, ay, 1, N, K, G, stp, stream)
             assert rc == 0, rc
 
     # the prefill pass: likewise two batched calls, each problem with its own
     # output (the activations of a K are shared)
-    y_pre = [torch.empty(MP, N, dtype=torch.float32, device=dev) for N, K in shapes]
-
     def run_gemm(slot, stream):
-        for (N, K), idx in groups.items():
-            ax = (arr * len(idx))(*[x_pre[K].data_ptr() for i in idx])
-            ap = (arr * len(idx))(*[P[slot][i].data_ptr() for i in idx])
-            asc = (arr * len(idx))(*[S[slot][i].data_ptr() for i in idx])
-            ay = (arr * len(idx))(*[y_pre[i].data_ptr() for i in idx])
-            rc = L.tq_gemm_batched(len(idx), ax, ap, asc, ay, MP, N, K, G, stp, stream)
+        for (N, K) in groups:
+            n, _, ap, asc, _, axp, ayp = calls[(slot, (N, K))]
+            rc = L.tq_gemm_batched(n, axp, ap, asc, ayp, MP, N, K, G, stp, stream)
             assert rc == 0, rc
 
     # fill every ring slot, then check slot 0 against the oracle on sampled rows
@@ -182,11 +196,12 @@ def main():
         p = P[0][i].view(N, -1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
         assert np.array_equal(p, p_ref), "bench inputs: packed bytes differ from the oracle"
 
-    # one graph per (row, slot); all rows run on one side stream
+    # one graph per (row, slot) for the rows of many launches; all rows run on
+    # one side stream
     stream = torch.cuda.Stream()
+    sp = stream.cuda_stream
     graphs = {}
-    for name, fn in (("gemv", run_gemv), ("gemm", run_gemm), ("quant", run_quant),
-                     ("unpack", run_unpack)):
+    for name, fn in (("quant", run_quant), ("unpack", run_unpack)):
         for slot in range(RING):
             g = torch.cuda.CUDAGraph()
             with torch.cuda.graph(g, stream=stream):
@@ -203,7 +218,12 @@ def main():
             if evs is not None:
                 evs[0].record(stream)
             for j, name in enumerate(order):
-                graphs[(name, slots[name])].replay()
+                if name == "gemv":
+                    run_gemv(slots[name], sp)
+                elif name == "gemm":
+                    run_gemm(slots[name], sp)
+                else:
+                    graphs[(name, slots[name])].replay()
                 if evs is not None:
                     evs[j + 1].record(stream)
 
@@ -218,6 +238,21 @@ def main():
     torch.cuda.synchronize()
     wall = time.perf_counter() - t_start
     assert int(status.item()) == 0, "device status %d" % int(status.item())
+
+    # the GEMV kernel on its own: the decode pass over all slots back to back
+    chain = []
+    with torch.cuda.stream(stream):
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for slot in range(RING):
+                run_gemv(slot, sp)
+            e1.record(stream)
+            chain.append((e0, e1))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status %d" % int(status.item())
+    chain_ms = sorted(a.elapsed_time(b) for a, b in chain[1:])
+    launch_ms = chain_ms[len(chain_ms) // 2] / (RING * len(groups))
 
     per = {name: 0.0 for name in order}
     total_ms = 0.0
@@ -236,7 +271,6 @@ def main():
     quant_bytes = weights * 2 + packed_bytes
     unpack_bytes = packed_bytes + weights
     gemv_launches = len(groups)
-    launch_ms = per["gemv"] / gemv_launches
     rows = {
         "a5_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
                     "launches": gemv_launches, "bytes_per_step": packed_bytes},
@@ -273,7 +307,10 @@ def main():
                      "frac": round(packed_bytes / gemv_launches / (launch_ms * 1e-3) / 1e9
                                    / HBM_PEAK_GBS, 4),
                      "traffic": None,
-                     "avg_launch_us": round(launch_ms * 1e3, 3)},
+                     "avg_launch_us": round(launch_ms * 1e3, 3),
+                     "timing": "median of 3 chains of the decode pass over all %d slots "
+                               "(%d back-to-back launches) between HIP events"
+                               % (RING, RING * len(groups))},
         "rows": rows,
         "wall_s_timed": round(wall, 4),
     }
