@@ -410,6 +410,10 @@ constexpr int64_t kChunkRows = int64_t(1) << 18;  // per launch: <= 2^22 blocks
 
 void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
                  int64_t N, int64_t K, int G, float *y, int32_t *d_status, hipStream_t stream) {
+  if (gemm_wide_supported(1, M, N, K, G)) {
+    launch_gemm_wide(1, &x, &packed, &scales, &y, M, N, K, N, d_status, stream);
+    return;
+  }
   const int64_t rowbytes = (K / G) * bytes_per_group(G);
   for (int64_t n_off = 0; n_off < N; n_off += kChunkRows) {
     const int64_t n_len = N - n_off < kChunkRows ? N - n_off : kChunkRows;
@@ -428,6 +432,10 @@ void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scale
 void launch_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                          const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                          int64_t K, int G, int32_t *d_status, hipStream_t stream) {
+  if (gemm_wide_supported(count, M, N, K, G)) {
+    launch_gemm_wide(count, xs, packeds, scales, ys, M, N, K, N, d_status, stream);
+    return;
+  }
   // Same-shaped problems share a launch, kGemmMaxBatch at a time, while the
   // launch stays under 2^23 blocks; larger problems go one by one.
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);

@@ -1,0 +1,442 @@
+// tq_gemm_wide.hip -- prefill matmul for gfx950 with 256-row activation
+// tiles and 64-wide K stages (G = 128, M >= 256).
+//
+// y[m,n] = sum_g s[n,g] * sum_{j<G} x[m, gG+j] * c[n, gG+j]
+// (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation";
+// prefill reuses each weight tile across many rows, "Revisit the Decode
+// Roofline").
+//
+// Compared with gemm_kernel (128 x 128 tiles, 32-wide stages, two blocks per
+// CU), a block here computes a 256 x 128 tile of y with 8 waves and owns the
+// whole 160 KB of a CU's LDS:
+//   * each decoded code is used by 256 activation rows instead of 128, so the
+//     decode costs half as much per MFMA;
+//   * a stage holds 32 MFMAs per wave between barriers instead of 16.
+// Per 64-wide stage s:
+//   - the activations of stage s+2 go from memory straight into their slot
+//     of a 3-slot LDS ring (32 KB a slot; buffer loads with the lds modifier);
+//   - the packed bytes of stage s+1, loaded two stages earlier into a
+//     register ring, are looked up in the decode table, and the bytes of
+//     stage s+3 are requested;
+//   - the stage's 32 MFMAs per wave run (two 32-wide steps over 4 x 4 tiles
+//     of v_mfma_f32_16x16x32_bf16 per wave), and the 16 codes each thread
+//     decodes for stage s+1 are written to the other of two code slots;
+//   - at the end of a group (every second stage) the group's fp32 partial is
+//     scaled by s/2 and added to the accumulator;
+//   - one barrier, after a wait that leaves the younger loads in flight.
+// Codes enter the MFMA as the bf16 value 2c (exact, low byte zero: a pair of
+// codes is one v_perm of table bytes), as in gemm_kernel.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) unsigned char lds_bytes;
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2_c;
+typedef __attribute__((address_space(3))) u32x2 lds_u32x2;
+typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
+typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_c;
+
+constexpr int kWave = 64;
+constexpr int G = 128;                  // this kernel's group size
+constexpr int B = 26;                   // bytes per group
+constexpr int BM = 256;                 // activation rows per block
+constexpr int BN = 128;                 // weight rows per block
+constexpr int NT = 512;                 // threads per block (8 waves)
+constexpr int KS = 64;                  // K values per stage
+constexpr int SPG = G / KS;             // stages per group: 2
+constexpr int XRING = 3;                // activation slots
+constexpr int XSLOT = BM * KS * 2;      // 32 KiB
+constexpr int CSLOT = BN * KS * 2;      // 16 KiB
+constexpr int kCopies = 16;
+constexpr int kEntryBytes = 8;
+constexpr int LUTB = 256 * kCopies * kEntryBytes;  // 32 KiB
+constexpr uint32_t kCsOff = XRING * XSLOT;
+constexpr uint32_t kLutOff = kCsOff + 2 * CSLOT;
+constexpr int SMEM = kLutOff + LUTB;    // 160 KiB: the whole LDS of a CU
+constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr uint32_t kBadFlag = 0xFF00u;  // in the high dword of entries 243..255
+constexpr int TM = 4, TN = 4;           // 16 x 16 tiles per wave: 64 x 64
+
+struct GemmBatch {
+  const uint16_t *x[kGemmMaxBatch];
+  const uint8_t *packed[kGemmMaxBatch];
+  const uint16_t *scales[kGemmMaxBatch];
+  float *y[kGemmMaxBatch];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// Byte offset of 16-byte chunk kc (0..7) of row r in a swizzled tile of
+// 128-byte rows.  16 consecutive rows reading one chunk, and 16 consecutive
+// rows writing one chunk, land in 16 different 16-byte bank groups.
+__device__ __forceinline__ uint32_t swz(uint32_t r, uint32_t kc) {
+  return 16u * (8u * r + (kc ^ ((r >> 1) & 7u)));
+}
+
+// Table entry for byte e: high bytes of 2*c_i (0xC0 for -2, 0x00, 0x40 for
+// +2), i = 0..3 in the low dword, i = 4 in byte 0 of the high dword.
+__device__ __forceinline__ u32x2 code_entry(uint32_t e) {
+  if (e >= 243u) return u32x2{0u, kBadFlag};
+  uint32_t h[5];
+#pragma unroll
+  for (int i = 0; i < 5; ++i) {
+    const uint32_t d = e % 3u;
+    e /= 3u;
+    h[i] = d == 0u ? 0xC0u : (d == 2u ? 0x40u : 0u);
+  }
+  return u32x2{h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24), h[4]};
+}
+
+// A run of 16 codes starts at digit D0 of its first byte; lo/hi are the table
+// entries of the run's four bytes.  Output dword w is the bf16 pair
+// (2c_{2w}, 2c_{2w+1}) of the run.
+template <int D0>
+__device__ __forceinline__ void stitch(const uint32_t (&lo)[4], const uint32_t (&hi)[4],
+                                       uint32_t (&out)[8]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const int h1 = D0 + 2 * w, j1 = h1 / 5, o1 = h1 % 5;
+    const int h2 = h1 + 1, j2 = h2 / 5, o2 = h2 % 5;
+    // v_perm byte pool: src1 = bytes 0..3, src0 = bytes 4..7; selector 0x0C
+    // gives a zero byte
+    uint32_t s0, s1;
+    int b1, b2;
+    if (j1 == j2 && o2 <= 3) {
+      s0 = lo[j1]; s1 = lo[j1]; b1 = o1; b2 = o2;
+    } else if (j1 == j2) {  // digits 3 and 4 of one byte
+      s0 = hi[j1]; s1 = lo[j1]; b1 = 3; b2 = 4;
+    } else {                // digit 4 of byte j1, digit 0 of byte j2
+      s0 = hi[j1]; s1 = lo[j2]; b1 = 4; b2 = 0;
+    }
+    out[w] = __builtin_amdgcn_perm(s0, s1, 0x000C000Cu | ((uint32_t)b1 << 8) | ((uint32_t)b2 << 24));
+  }
+}
+
+template <int V>
+struct Int {
+  static constexpr int value = V;
+};
+
+__global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
+void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
+                      int32_t *__restrict__ d_status) {
+  __shared__ __align__(16) unsigned char smem_raw[SMEM];
+  lds_bytes *smem = (lds_bytes *)smem_raw;
+
+  const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
+  const int wm = wv >> 1, wn = wv & 1;
+  const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
+  const int pi = (int)blockIdx.y;
+  const int t = (int)blockIdx.x;
+  const int m0 = (t % tilesM) * BM, n0 = (t / tilesM) * BN;
+  const int nG = K / G, nS = K / KS;
+  const uint32_t rowbytes = (uint32_t)nG * B;
+  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
+
+  // Buffer descriptors based at this block's tiles: 32-bit offsets suffice.
+  const __amdgpu_buffer_rsrc_t rx =
+      make_rsrc(args.x[pi] + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
+  const uintptr_t pabs = reinterpret_cast<uintptr_t>(args.packed[pi]) + (uint64_t)n0 * rowbytes;
+  const uint32_t pbase = (uint32_t)(pabs & 3u);  // packed has any alignment
+  // The range is a whole number of dwords, so a dword load is either fully
+  // in range or fully past it (then it reads 0).
+  const __amdgpu_buffer_rsrc_t rp =
+      make_rsrc(reinterpret_cast<const void *>(pabs - pbase),
+                (pbase + (uint32_t)nrows * rowbytes + 3u) & ~3u);
+  const __amdgpu_buffer_rsrc_t rs =
+      make_rsrc(args.scales[pi] + (int64_t)n0 * nG, (uint32_t)nrows * (uint32_t)nG * 2u);
+
+  // ---- decode table: two threads per entry, eight copies each, the copy
+  // index rotated by the entry to spread the banks ----
+  {
+    const uint32_t e = (uint32_t)tid & 255u, half = (uint32_t)tid >> 8;
+    const u32x2 v = code_entry(e);
+#pragma unroll
+    for (int k = 0; k < kCopies / 2; ++k) {
+      const uint32_t j = (8u * half + (uint32_t)k + e) & (kCopies - 1);
+      *(lds_u32x2 *)(smem + kLutOff + (e * kCopies + j) * kEntryBytes) = v;
+    }
+  }
+
+  // Every stage issues the same loads -- past the end they read junk or
+  // zeros into slots that are never consumed -- so the wait counts are fixed.
+  const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);  // wave index, scalar
+  // ---- activations: op i of thread t fills chunk 512 i + t of the slot
+  // (row r = chunk / 8).  Offsets stay in the per-lane offset, the only part
+  // of a raw buffer address that is range-checked. ----
+  uint32_t xoff[4];
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t U = 512u * i + (uint32_t)tid;
+    const uint32_t r = U >> 3, kc = (U & 7u) ^ ((r >> 1) & 7u);  // inverse of swz
+    xoff[i] = (int)r < mrows ? ((uint32_t)r * (uint32_t)K + kc * 8u) * 2u : kOutOfRange;
+  }
+  auto dma_x = [&](int s) {
+    const uint32_t slot = (uint32_t)(s % XRING) * XSLOT;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      lds_bytes *dst = smem + slot + 16u * (512u * i + 64u * wvs);
+      __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst,
+                                               16, xoff[i] + (uint32_t)s * (KS * 2), 0, 0, 0);
+    }
+  };
+
+  // ---- scales: lanes hold column n = wn*64 + tn*16 + (lane & 15) ----
+  uint32_t soff[TN];
+#pragma unroll
+  for (int tn = 0; tn < TN; ++tn) {
+    const int n = wn * 64 + tn * 16 + (lane & 15);
+    soff[tn] = n < nrows ? 2u * (uint32_t)n * (uint32_t)nG : kOutOfRange;
+  }
+  uint32_t sc_cur[TN], sc_next[TN];
+  auto load_scales = [&](int g, uint32_t (&dst)[TN]) {
+#pragma unroll
+    for (int tn = 0; tn < TN; ++tn)
+      dst[tn] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[tn] + 2u * (uint32_t)g, 0, 0);
+  };
+
+  // ---- packed bytes: thread (row dr, quarter dq) decodes codes 16 dq .. 16
+  // dq + 15 of each stage; two dwords hold the run's four bytes ----
+  const int dr = tid & (BN - 1);
+  const uint32_t dqs = __builtin_amdgcn_readfirstlane(tid >> 7);  // uniform over a wave
+  const bool drow_on = dr < nrows;
+  const uint32_t prow = drow_on ? pbase + (uint32_t)dr * rowbytes : kOutOfRange;
+  const uint32_t lut_lane = kLutOff + (uint32_t)(tid & (kCopies - 1)) * kEntryBytes;
+  uint32_t flags = 0;
+  auto lookup = [&](const uint32_t (&raw)[2], uint32_t ofs, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
+    const uint32_t w = __builtin_amdgcn_alignbyte(raw[1], raw[0], ofs);
+#pragma unroll
+    for (int k = 0; k < 4; ++k) {
+      const uint32_t b = (w >> (8 * k)) & 0xFFu;
+      const u32x2 e = *(lds_u32x2_c *)(smem + ((b << 7) + lut_lane));
+      lo[k] = e.x;
+      hi[k] = e.y;
+    }
+  };
+
+  // ---- MFMA operands: lane reads rows r0 + 16 a, chunk 4 ks + (lane >> 4) ----
+  const uint32_t kq = (uint32_t)(lane >> 4);
+  uint32_t aoff[2], boff[2];
+#pragma unroll
+  for (int ks = 0; ks < 2; ++ks) {
+    aoff[ks] = swz((uint32_t)(wm * 64 + (lane & 15)), 4u * ks + kq);
+    boff[ks] = kCsOff + swz((uint32_t)(wn * 64 + (lane & 15)), 4u * ks + kq);
+  }
+
+  f32x4 acc[TM][TN], part[TM][TN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int b = 0; b < TN; ++b) {
+      acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+      part[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+    }
+
+  // The rest is instantiated per decode quarter DQ (uniform over a wave), so
+  // that each stage is one branch-free block the scheduler can interleave.
+  auto body = [&](auto dqc) {
+    constexpr int DQ = decltype(dqc)::value;
+    // one 8-byte load (one count of vmcnt) from the dword holding the run's
+    // first byte
+    auto load_packed = [&](int s, uint32_t (&dst)[2], uint32_t &ofs) {
+      const int g = s / SPG, st = s % SPG;
+      const uint32_t a = prow + (uint32_t)(g * B + (st * KS + 16 * DQ) / 5);
+      ofs = a & 3u;
+      const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rp, a & ~3u, 0, 0);
+      dst[0] = v.x;
+      dst[1] = v.y;
+    };
+    // codes of a run that is stage ST of its group -> two chunks of slot cs
+    auto emit = [&](auto stc, const uint32_t (&lo)[4], const uint32_t (&hi)[4], uint32_t cs) {
+      constexpr int ST = decltype(stc)::value;
+      flags |= (hi[0] | hi[1]) | (hi[2] | hi[3]);
+      uint32_t out[8];
+      stitch<(ST * KS + 16 * DQ) % 5>(lo, hi, out);
+#pragma unroll
+      for (int i = 0; i < 2; ++i)
+        *(lds_u32x4 *)(smem + cs + swz((uint32_t)dr, (uint32_t)(2 * DQ + i))) =
+            u32x4{out[4 * i], out[4 * i + 1], out[4 * i + 2], out[4 * i + 3]};
+    };
+
+    // ---- prologue: all of it completes before the loop, so the compiler's
+    // wait counts inside the loop need not cover it ----
+    uint32_t ring[2][2], rofs[2], first[2], first_ofs;
+    load_scales(0, sc_cur);
+    dma_x(0);
+    dma_x(1);
+    load_packed(0, first, first_ofs);
+    load_packed(1, ring[1], rofs[1]);
+    load_packed(2, ring[0], rofs[0]);
+    __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
+    __syncthreads();                // table and stage 0 activations ready
+    {
+      uint32_t lo[4], hi[4];
+      lookup(first, first_ofs, lo, hi);
+      emit(Int<0>{}, lo, hi, kCsOff);
+    }
+    __syncthreads();
+
+    // stage s is stage ST (= s & 1) of its group; it reads code slot ST and
+    // activation slot s % 3
+    auto stage = [&](auto stc, int s) {
+      constexpr int ST = decltype(stc)::value;
+      constexpr int P = ST, Q = 1 - ST;
+      constexpr int ST1 = (ST + 1) % SPG;  // place of stage s+1 in its group
+      // table lookups for stage s+1: its bytes were requested two stages ago
+      // (past the last stage they decode junk into the free code slot)
+      uint32_t lo[4], hi[4];
+      lookup(ring[Q], rofs[Q], lo, hi);
+      const uint32_t xs = (uint32_t)(s % XRING) * XSLOT;
+      // operands of one 32-wide step: 4 activation and 4 code fragments
+      auto read_ops = [&](int ks, bf16x8 (&av)[TM], bf16x8 (&bv)[TN]) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+          av[a] = *(lds_bf16x8_c *)(smem + xs + aoff[ks] + 2048u * a);
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          bv[b] = *(lds_bf16x8_c *)(smem + P * CSLOT + boff[ks] + 2048u * b);
+      };
+      auto mfmas = [&](int ks, const bf16x8 (&av)[TM], const bf16x8 (&bv)[TN]) {
+#pragma unroll
+        for (int a = 0; a < TM; ++a)
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+            part[a][b] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(
+                av[a], bv[b], (ST == 0 && ks == 0) ? f32x4{0.f, 0.f, 0.f, 0.f} : part[a][b], 0,
+                0, 0);
+      };
+      bf16x8 av0[TM], bv0[TN], av1[TM], bv1[TN];
+      read_ops(0, av0, bv0);
+      if (ST == 0) load_scales(s / SPG + 1, sc_next);
+      dma_x(s + 2);
+      load_packed(s + 3, ring[Q], rofs[Q]);
+      mfmas(0, av0, bv0);
+      read_ops(1, av1, bv1);
+      mfmas(1, av1, bv1);
+      emit(Int<ST1>{}, lo, hi, kCsOff + (uint32_t)Q * CSLOT);
+      if (ST == SPG - 1) {
+        // end of a group: acc += (s/2) * part (codes entered as 2c)
+#pragma unroll
+        for (int b = 0; b < TN; ++b) {
+          const float sh = 0.5f * __half2float(__ushort_as_half((unsigned short)sc_cur[b]));
+#pragma unroll
+          for (int a = 0; a < TM; ++a)
+#pragma unroll
+            for (int r = 0; r < 4; ++r) acc[a][b][r] = fmaf(sh, part[a][b][r], acc[a][b][r]);
+        }
+#pragma unroll
+        for (int b = 0; b < TN; ++b) sc_cur[b] = sc_next[b];
+      }
+      // Instruction order for the scheduler: the table and operand reads and
+      // the loads first, then each MFMA followed by vector-ALU work, so that
+      // the decode and the scaling run in the MFMA shadow.
+      constexpr int kValu = ST == SPG - 1 ? 3 : 1;
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU: table addresses
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: table, step 0
+      __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);  // VMEM reads
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+        if (i == 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads: step 1
+      }
+#pragma unroll
+      for (int i = 0; i < 16; ++i) {
+        __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
+        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+      }
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // DS writes
+      // The activations of stage s+1 (requested during stage s-1) must have
+      // landed before the barrier.  Only this stage's loads may stay in
+      // flight -- its scales (4, first stage of a group only), activations
+      // (4) and bytes (1) -- whatever order the compiler gave the previous
+      // stage's loads.
+      if (ST == 0)
+        asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+      else
+        asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+    };
+
+    for (int s = 0; s < nS; s += SPG) {  // nS is a multiple of SPG
+      stage(Int<0>{}, s);
+      stage(Int<1>{}, s + 1);
+    }
+  };
+  switch (dqs) {
+    case 0: body(Int<0>{}); break;
+    case 1: body(Int<1>{}); break;
+    case 2: body(Int<2>{}); break;
+    default: body(Int<3>{}); break;
+  }
+  // no load may still be writing this block's LDS when it exits
+  asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
+
+  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane>>4) + r ----
+  const int mb = wm * 64 + 4 * (lane >> 4), nb = wn * 64 + (lane & 15);
+  float *__restrict__ yl = args.y[pi] + (int64_t)(m0 + mb) * ldy + (n0 + nb);
+  if (mrows == BM && nrows == BN) {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
+#pragma unroll
+        for (int b = 0; b < TN; ++b) yr[16 * b] = acc[a][b][r];
+      }
+  } else {
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        if (mb + 16 * a + r >= mrows) continue;
+        float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
+#pragma unroll
+        for (int b = 0; b < TN; ++b)
+          if (nb + 16 * b < nrows) yr[16 * b] = acc[a][b][r];
+      }
+  }
+  if ((flags & kBadFlag) && drow_on && d_status) atomicOr(d_status, kDevInvalidByte);
+}
+
+}  // namespace
+
+bool gemm_wide_supported(int count, int64_t M, int64_t N, int64_t K, int G_) {
+  // G = 128 and at least one whole 256-row tile; 32-bit offsets (a 256-row
+  // slab of x); and enough tiles to give at least 3/4 of the 256 CUs one
+  // block each -- smaller grids run faster as 128 x 128 tiles, two per CU
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  return G_ == G && M >= BM && K % G == 0 && tiles < (int64_t(1) << 30) &&
+         (int64_t)BM * K * 2 < (int64_t(1) << 31) && tiles * count >= 192;
+}
+
+void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                      const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                      int64_t K, int64_t ldy, int32_t *d_status, hipStream_t stream) {
+  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
+  for (int base = 0; base < count; base += kGemmMaxBatch) {
+    const int n = count - base < kGemmMaxBatch ? count - base : kGemmMaxBatch;
+    GemmBatch a;
+    for (int i = 0; i < n; ++i) {
+      a.x[i] = xs[base + i];
+      a.packed[i] = packeds[base + i];
+      a.scales[i] = scales[base + i];
+      a.y[i] = ys[base + i];
+    }
+    hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)tiles, (unsigned)n), dim3(NT), 0, stream,
+                       a, (int)M, (int)N, (int)K, ldy, d_status);
+  }
+}
+
+}  // namespace tq

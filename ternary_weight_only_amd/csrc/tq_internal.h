@@ -47,6 +47,14 @@ void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scale
 // Problems per batched GEMM launch.
 constexpr int kGemmMaxBatch = 64;
 
+// G = 128, M >= 256: 256 x 128 tiles, 64-wide stages (tq_gemm_wide.hip),
+// for launches of count same-shaped problems with enough tiles.
+bool gemm_wide_supported(int count, int64_t M, int64_t N, int64_t K, int G);
+
+void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                      const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                      int64_t K, int64_t ldy, int32_t *d_status, hipStream_t stream);
+
 void launch_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                          const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                          int64_t K, int G, int32_t *d_status, hipStream_t stream);

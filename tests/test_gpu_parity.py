@@ -293,6 +293,47 @@ def test_gemv_row_shapes(K, G):
     assert int(st.item()) & 4
 
 
+def test_gemm_wide_tiles_ragged_unaligned_and_invalid_bytes():
+    """tq_gemm_batched at G = 128 with enough 256 x 128 tiles to take the
+    wide-tile kernel (48 problems of M=300, N=200: ragged tiles in both M and
+    N), the packed bytes of each problem at offset i % 4 (any alignment is
+    allowed), every output within the bound of the oracle; then an invalid
+    byte at the last byte of one problem's buffer is flagged."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits
+    M, N, K, G, count = 300, 200, 640, 128, 48
+    ws = [inputs.normal_bf16(700 + i, (N, K), 0.02) for i in range(count)]
+    xs = [inputs.activation(800 + i % 4, M, K) for i in range(count)]
+    refs = [oracle.quantize_pack(w, G) for w in ws]
+    flat_size = refs[0][0].size
+    bufs = [torch.zeros(flat_size + 8, dtype=torch.uint8, device="cuda") for _ in range(count)]
+    pdv = []
+    for i, (p, _, _) in enumerate(refs):
+        pd = bufs[i][i % 4:i % 4 + flat_size]
+        pd.copy_(torch.from_numpy(p.reshape(-1)))
+        pdv.append(pd)
+    xd = [dev_bf16(x) for x in xs]
+    sdv = [dev_f16bits(s) for _, s, _ in refs]
+    say("gemm wide tiles M=%d N=%d K=%d G=%d count=%d" % (M, N, K, G, count))
+    st = tq.new_status()
+    ys = tq.gemm_batched(xd, pdv, sdv, N, K, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    rows = np.array(list(range(8)) + list(range(248, 264)) + list(range(M - 8, M)))
+    for i in range(count):
+        p, s, _ = refs[i]
+        y_ref, bound, _ = oracle.matmul(xs[i][rows], p, s, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy()[rows], y_ref, bound, "wide item %d" % i)
+    bad = refs[5][0].reshape(-1).copy()
+    bad[-1] = 249
+    pdv[5].copy_(torch.from_numpy(bad))
+    st = tq.new_status()
+    tq.gemm_batched(xd, pdv, sdv, N, K, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 4
+
+
 @pytest.mark.parametrize("M,N,K,G,count", [(512, 3584, 1024, 128, 3), (100, 200, 640, 64, 5),
                                            (300, 96, 320, 64, 70)])
 def test_gemm_batched_matches_single_calls_and_oracle(M, N, K, G, count):
