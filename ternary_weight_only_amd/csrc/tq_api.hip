@@ -57,7 +57,7 @@ int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *pa
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
   if (!aligned(w, 16) || !aligned(scales, 2) || !aligned(d_status, 4)) return TQ_ERR_ALIGN;
-  hipGetLastError();  // clear a stale error so the check below sees only ours
+  (void)hipGetLastError();  // clear a stale error so the check below sees only ours
   tq::launch_quantize_pack(w, N, K, G, packed, scales, d_status, (hipStream_t)stream);
   return finish_launch();
 }
@@ -68,7 +68,7 @@ int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
   if (!aligned(codes, 8) || !aligned(d_status, 4)) return TQ_ERR_ALIGN;
-  hipGetLastError();
+  (void)hipGetLastError();
   tq::launch_unpack(packed, N, K, G, codes, d_status, (hipStream_t)stream);
   return finish_launch();
 }
@@ -83,7 +83,7 @@ int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, in
   if (!aligned(x, 16) || !aligned(packed, 16) || !aligned(scales, 2) || !aligned(y, 4) ||
       !aligned(d_status, 4))
     return TQ_ERR_ALIGN;
-  hipGetLastError();
+  (void)hipGetLastError();
   tq::launch_gemv(x, packed, scales, M, N, K, G, y, d_status, (hipStream_t)stream);
   return finish_launch();
 }
@@ -105,7 +105,7 @@ int tq_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *
         !aligned(ys[i], 4))
       return TQ_ERR_ALIGN;
   }
-  hipGetLastError();
+  (void)hipGetLastError();
   tq::launch_gemv_batched(count, xs, packeds, scales, ys, M, N, K, G, d_status,
                           (hipStream_t)stream);
   return finish_launch();
@@ -120,7 +120,7 @@ int tq_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, in
   if (K > (int64_t(1) << 22)) return TQ_ERR_SHAPE;  // a 128-row x slab stays under 1 GiB
   if (!aligned(x, 16) || !aligned(scales, 2) || !aligned(y, 4) || !aligned(d_status, 4))
     return TQ_ERR_ALIGN;
-  hipGetLastError();
+  (void)hipGetLastError();
   tq::launch_gemm(x, packed, scales, M, N, K, G, y, d_status, (hipStream_t)stream);
   return finish_launch();
 }
@@ -141,7 +141,7 @@ int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *
     if (!aligned(xs[i], 16) || !aligned(scales[i], 2) || !aligned(ys[i], 4))
       return TQ_ERR_ALIGN;
   }
-  hipGetLastError();
+  (void)hipGetLastError();
   tq::launch_gemm_batched(count, xs, packeds, scales, ys, M, N, K, G, d_status,
                           (hipStream_t)stream);
   return finish_launch();

@@ -129,8 +129,38 @@ struct Int {
   static constexpr int value = V;
 };
 
+// A tile of one problem: rows [m0, m0 + mrows) of x, rows [n0, n0 + nrows)
+// of W.  Tile j of a block is tile blockIdx.x + j * gridDim.x of the launch
+// (problem-major); past the launch's tiles it is empty (no rows: every load
+// of it reads zeros).
+struct Tile {
+  int pi, m0, n0, mrows, nrows;
+};
+
+__device__ __forceinline__ Tile block_tile(int j, int M, int N, int tilesM, int tpp, int total) {
+  const int t = (int)blockIdx.x + j * (int)gridDim.x;
+  Tile r;
+  if (t >= total) {
+    r.pi = 0; r.m0 = 0; r.n0 = 0; r.mrows = 0; r.nrows = 0;
+    return r;
+  }
+  r.pi = t / tpp;
+  const int tt = t - r.pi * tpp;
+  r.m0 = (tt % tilesM) * BM;
+  r.n0 = (tt / tilesM) * BN;
+  r.mrows = min(BM, M - r.m0);
+  r.nrows = min(BN, N - r.n0);
+  return r;
+}
+
+// Persistent blocks, one per CU: block b computes tiles b, b + grid, ... one
+// after another.  The stage pipeline (activations two stages ahead, packed
+// bytes three, scales one group) runs on across tile boundaries: each of the
+// three load streams keeps its own tile and moves to the next tile when its
+// stage count wraps, so a tile's first stages are loaded while the previous
+// tile computes, and the table is built once per block.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
+void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, int total,
                       int32_t *__restrict__ d_status) {
   __shared__ __align__(16) unsigned char smem_raw[SMEM];
   lds_bytes *smem = (lds_bytes *)smem_raw;
@@ -138,25 +168,11 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int wm = wv >> 1, wn = wv & 1;
   const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-  const int pi = (int)blockIdx.y;
-  const int t = (int)blockIdx.x;
-  const int m0 = (t % tilesM) * BM, n0 = (t / tilesM) * BN;
+  const int tpp = tilesM * tilesN;
   const int nG = K / G, nS = K / KS;
   const uint32_t rowbytes = (uint32_t)nG * B;
-  const int mrows = min(BM, M - m0), nrows = min(BN, N - n0);
-
-  // Buffer descriptors based at this block's tiles: 32-bit offsets suffice.
-  const __amdgpu_buffer_rsrc_t rx =
-      make_rsrc(args.x[pi] + (int64_t)m0 * K, (uint32_t)mrows * (uint32_t)K * 2u);
-  const uintptr_t pabs = reinterpret_cast<uintptr_t>(args.packed[pi]) + (uint64_t)n0 * rowbytes;
-  const uint32_t pbase = (uint32_t)(pabs & 3u);  // packed has any alignment
-  // The range is a whole number of dwords, so a dword load is either fully
-  // in range or fully past it (then it reads 0).
-  const __amdgpu_buffer_rsrc_t rp =
-      make_rsrc(reinterpret_cast<const void *>(pabs - pbase),
-                (pbase + (uint32_t)nrows * rowbytes + 3u) & ~3u);
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc(args.scales[pi] + (int64_t)n0 * nG, (uint32_t)nrows * (uint32_t)nG * 2u);
+  const int ntiles = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  auto tile = [&](int j) { return block_tile(j, M, N, tilesM, tpp, total); };
 
   // ---- decode table: two threads per entry, eight copies each, the copy
   // index rotated by the entry to spread the banks ----
@@ -173,46 +189,84 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
   // Every stage issues the same loads -- past the end they read junk or
   // zeros into slots that are never consumed -- so the wait counts are fixed.
   const uint32_t wvs = __builtin_amdgcn_readfirstlane(wv);  // wave index, scalar
-  // ---- activations: op i of thread t fills chunk 512 i + t of the slot
+
+  // ---- activation stream: op i of thread t fills chunk 512 i + t of a slot
   // (row r = chunk / 8).  Offsets stay in the per-lane offset, the only part
   // of a raw buffer address that is range-checked. ----
-  uint32_t xoff[4];
-#pragma unroll
-  for (int i = 0; i < 4; ++i) {
-    const uint32_t U = 512u * i + (uint32_t)tid;
-    const uint32_t r = U >> 3, kc = (U & 7u) ^ ((r >> 1) & 7u);  // inverse of swz
-    xoff[i] = (int)r < mrows ? ((uint32_t)r * (uint32_t)K + kc * 8u) * 2u : kOutOfRange;
-  }
-  auto dma_x = [&](int s) {
-    const uint32_t slot = (uint32_t)(s % XRING) * XSLOT;
+  // The row of op i is r0 + 64 i, with the same swizzled chunk for every i.
+  const uint32_t xr0 = (uint32_t)tid >> 3;
+  const uint32_t xbase = (xr0 * (uint32_t)K + (((uint32_t)tid & 7u) ^ ((xr0 >> 1) & 7u)) * 8u) * 2u;
+  int jx = 0, sx = 0, ux = 0;  // tile, its stage, ring slot of the next request
+  int xrows = 0;               // rows of the stream's tile
+  __amdgpu_buffer_rsrc_t rx;
+  auto set_x = [&](int j) {
+    const Tile T = tile(j);
+    rx = make_rsrc(args.x[T.pi] + (int64_t)T.m0 * K, (uint32_t)T.mrows * (uint32_t)K * 2u);
+    xrows = T.mrows;
+  };
+  set_x(0);
+  auto dma_x = [&]() {
+    const uint32_t slot = (uint32_t)ux * XSLOT;
 #pragma unroll
     for (int i = 0; i < 4; ++i) {
       lds_bytes *dst = smem + slot + 16u * (512u * i + 64u * wvs);
+      const uint32_t off = (int)(xr0 + 64u * i) < xrows
+                               ? xbase + (uint32_t)i * (64u * 2u) * (uint32_t)K + (uint32_t)sx * (KS * 2)
+                               : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst,
-                                               16, xoff[i] + (uint32_t)s * (KS * 2), 0, 0, 0);
+                                               16, off, 0, 0, 0);
+    }
+    ux = ux == XRING - 1 ? 0 : ux + 1;
+    if (++sx == nS) {
+      sx = 0;
+      set_x(++jx);
     }
   };
 
-  // ---- scales: lanes hold column n = wn*64 + tn*16 + (lane & 15) ----
-  uint32_t soff[TN];
-#pragma unroll
-  for (int tn = 0; tn < TN; ++tn) {
-    const int n = wn * 64 + tn * 16 + (lane & 15);
-    soff[tn] = n < nrows ? 2u * (uint32_t)n * (uint32_t)nG : kOutOfRange;
-  }
+  // ---- scale stream: lanes hold column n = wn*64 + tn*16 + (lane & 15) ----
+  const int sn0 = wn * 64 + (lane & 15);  // column of op tn: sn0 + 16 tn
+  int js = 0, gs = 0;  // tile, its group
+  int srows = 0;       // rows of the stream's tile
+  __amdgpu_buffer_rsrc_t rs;
+  auto set_s = [&](int j) {
+    const Tile T = tile(j);
+    rs = make_rsrc(args.scales[T.pi] + (int64_t)T.n0 * nG, (uint32_t)T.nrows * (uint32_t)nG * 2u);
+    srows = T.nrows;
+  };
+  set_s(0);
   uint32_t sc_cur[TN], sc_next[TN];
-  auto load_scales = [&](int g, uint32_t (&dst)[TN]) {
+  auto load_scales = [&](uint32_t (&dst)[TN]) {
 #pragma unroll
-    for (int tn = 0; tn < TN; ++tn)
-      dst[tn] = __builtin_amdgcn_raw_buffer_load_b16(rs, soff[tn] + 2u * (uint32_t)g, 0, 0);
+    for (int tn = 0; tn < TN; ++tn) {
+      const int n = sn0 + 16 * tn;
+      const uint32_t off = n < srows ? 2u * ((uint32_t)n * (uint32_t)nG + (uint32_t)gs) : kOutOfRange;
+      dst[tn] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
+    }
+    if (++gs == nG) {
+      gs = 0;
+      set_s(++js);
+    }
   };
 
-  // ---- packed bytes: thread (row dr, quarter dq) decodes codes 16 dq .. 16
-  // dq + 15 of each stage; two dwords hold the run's four bytes ----
+  // ---- packed-byte stream: thread (row dr, quarter dq) decodes codes 16 dq
+  // .. 16 dq + 15 of each stage; two dwords hold the run's four bytes ----
   const int dr = tid & (BN - 1);
   const uint32_t dqs = __builtin_amdgcn_readfirstlane(tid >> 7);  // uniform over a wave
-  const bool drow_on = dr < nrows;
-  const uint32_t prow = drow_on ? pbase + (uint32_t)dr * rowbytes : kOutOfRange;
+  int jp = 0, sp = 0;  // tile, its stage
+  __amdgpu_buffer_rsrc_t rp;
+  uint32_t prow;
+  auto set_p = [&](int j) {
+    const Tile T = tile(j);
+    const uintptr_t pabs =
+        reinterpret_cast<uintptr_t>(args.packed[T.pi]) + (uint64_t)T.n0 * rowbytes;
+    const uint32_t pbase = (uint32_t)(pabs & 3u);  // packed has any alignment
+    // The range is a whole number of dwords, so a dword load is either fully
+    // in range or fully past it (then it reads 0).
+    rp = make_rsrc(reinterpret_cast<const void *>(pabs - pbase),
+                   (pbase + (uint32_t)T.nrows * rowbytes + 3u) & ~3u);
+    prow = dr < T.nrows ? pbase + (uint32_t)dr * rowbytes : kOutOfRange;
+  };
+  set_p(0);
   const uint32_t lut_lane = kLutOff + (uint32_t)(tid & (kCopies - 1)) * kEntryBytes;
   uint32_t flags = 0;
   auto lookup = [&](const uint32_t (&raw)[2], uint32_t ofs, uint32_t (&lo)[4], uint32_t (&hi)[4]) {
@@ -244,19 +298,56 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
       part[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
     }
 
+  // ---- epilogue of tile j: lane holds column (lane & 15), rows
+  // 4*(lane>>4) + r of each 16 x 16 tile ----
+  auto store_tile = [&](int j) {
+    const Tile T = tile(j);
+    const int mb = wm * 64 + 4 * (lane >> 4), nb = wn * 64 + (lane & 15);
+    float *__restrict__ yl = args.y[T.pi] + (int64_t)(T.m0 + mb) * ldy + (T.n0 + nb);
+    if (T.mrows == BM && T.nrows == BN) {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
+#pragma unroll
+          for (int b = 0; b < TN; ++b) yr[16 * b] = acc[a][b][r];
+        }
+    } else {
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) {
+          if (mb + 16 * a + r >= T.mrows) continue;
+          float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
+#pragma unroll
+          for (int b = 0; b < TN; ++b)
+            if (nb + 16 * b < T.nrows) yr[16 * b] = acc[a][b][r];
+        }
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int b = 0; b < TN; ++b) acc[a][b] = f32x4{0.f, 0.f, 0.f, 0.f};
+  };
+
   // The rest is instantiated per decode quarter DQ (uniform over a wave), so
-  // that each stage is one branch-free block the scheduler can interleave.
+  // that each stage is one block the scheduler can interleave.
   auto body = [&](auto dqc) {
     constexpr int DQ = decltype(dqc)::value;
     // one 8-byte load (one count of vmcnt) from the dword holding the run's
     // first byte
-    auto load_packed = [&](int s, uint32_t (&dst)[2], uint32_t &ofs) {
-      const int g = s / SPG, st = s % SPG;
-      const uint32_t a = prow + (uint32_t)(g * B + (st * KS + 16 * DQ) / 5);
+    auto load_packed = [&](uint32_t (&dst)[2], uint32_t &ofs) {
+      const uint32_t a = prow + (uint32_t)((sp >> 1) * B) +
+                         ((sp & 1) ? (uint32_t)((KS + 16 * DQ) / 5) : (uint32_t)(16 * DQ / 5));
       ofs = a & 3u;
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rp, a & ~3u, 0, 0);
       dst[0] = v.x;
       dst[1] = v.y;
+      if (++sp == nS) {
+        sp = 0;
+        set_p(++jp);
+      }
     };
     // codes of a run that is stage ST of its group -> two chunks of slot cs
     auto emit = [&](auto stc, const uint32_t (&lo)[4], const uint32_t (&hi)[4], uint32_t cs) {
@@ -273,12 +364,12 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
     // ---- prologue: all of it completes before the loop, so the compiler's
     // wait counts inside the loop need not cover it ----
     uint32_t ring[2][2], rofs[2], first[2], first_ofs;
-    load_scales(0, sc_cur);
-    dma_x(0);
-    dma_x(1);
-    load_packed(0, first, first_ofs);
-    load_packed(1, ring[1], rofs[1]);
-    load_packed(2, ring[0], rofs[0]);
+    load_scales(sc_cur);
+    dma_x();
+    dma_x();
+    load_packed(first, first_ofs);
+    load_packed(ring[1], rofs[1]);
+    load_packed(ring[0], rofs[0]);
     __builtin_amdgcn_s_waitcnt(0);  // vmcnt(0) expcnt(0) lgkmcnt(0)
     __syncthreads();                // table and stage 0 activations ready
     {
@@ -288,17 +379,20 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
     }
     __syncthreads();
 
-    // stage s is stage ST (= s & 1) of its group; it reads code slot ST and
-    // activation slot s % 3
-    auto stage = [&](auto stc, int s) {
+    int uc = 0;  // ring slot of the stage being computed
+    int sc = 0;  // its stage within its tile
+    int jc = 0;  // its tile
+    // a stage is stage ST (= its index & 1) of its group; it reads code slot
+    // ST and the activation slot uc
+    auto stage = [&](auto stc) {
       constexpr int ST = decltype(stc)::value;
       constexpr int P = ST, Q = 1 - ST;
-      constexpr int ST1 = (ST + 1) % SPG;  // place of stage s+1 in its group
-      // table lookups for stage s+1: its bytes were requested two stages ago
-      // (past the last stage they decode junk into the free code slot)
+      constexpr int ST1 = (ST + 1) % SPG;  // place of the next stage in its group
+      // table lookups for the next stage: its bytes were requested two stages
+      // ago (past the last stage they decode junk into the free code slot)
       uint32_t lo[4], hi[4];
       lookup(ring[Q], rofs[Q], lo, hi);
-      const uint32_t xs = (uint32_t)(s % XRING) * XSLOT;
+      const uint32_t xs = (uint32_t)uc * XSLOT;
       // operands of one 32-wide step: 4 activation and 4 code fragments
       auto read_ops = [&](int ks, bf16x8 (&av)[TM], bf16x8 (&bv)[TN]) {
 #pragma unroll
@@ -319,13 +413,15 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
       };
       bf16x8 av0[TM], bv0[TN], av1[TM], bv1[TN];
       read_ops(0, av0, bv0);
-      if (ST == 0) load_scales(s / SPG + 1, sc_next);
-      dma_x(s + 2);
-      load_packed(s + 3, ring[Q], rofs[Q]);
+      if (ST == 0) load_scales(sc_next);
+      dma_x();
+      load_packed(ring[Q], rofs[Q]);
+      // the next stage's codes are assembled and written before the MFMAs,
+      // so that the table entries are not live across them
+      emit(Int<ST1>{}, lo, hi, kCsOff + (uint32_t)Q * CSLOT);
       mfmas(0, av0, bv0);
       read_ops(1, av1, bv1);
       mfmas(1, av1, bv1);
-      emit(Int<ST1>{}, lo, hi, kCsOff + (uint32_t)Q * CSLOT);
       if (ST == SPG - 1) {
         // end of a group: acc += (s/2) * part (codes entered as 2c)
 #pragma unroll
@@ -346,6 +442,8 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
       __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU: table addresses
       __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: table, step 0
       __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);  // VMEM reads
+      __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU: code assembly
+      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // DS writes
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
@@ -357,21 +455,32 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
         __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
       }
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // DS writes
-      // The activations of stage s+1 (requested during stage s-1) must have
-      // landed before the barrier.  Only this stage's loads may stay in
-      // flight -- its scales (4, first stage of a group only), activations
-      // (4) and bytes (1) -- whatever order the compiler gave the previous
-      // stage's loads.
+      uc = uc == XRING - 1 ? 0 : uc + 1;
+      if (ST == SPG - 1 && sc == nS - 1) {
+        // last stage of a tile: store it, then a full wait (the stores count
+        // in vmcnt too) before the barrier
+        store_tile(jc);
+        ++jc;
+        sc = 0;
+        asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
+        return;
+      }
+      ++sc;
+      // The activations of the next stage (requested during the previous
+      // stage) must have landed before the barrier.  Only this stage's loads
+      // may stay in flight -- its scales (4, first stage of a group only),
+      // activations (4) and bytes (1) -- whatever order the compiler gave the
+      // previous stage's loads.
       if (ST == 0)
         asm volatile("s_waitcnt vmcnt(9) lgkmcnt(0)\n\ts_barrier" ::: "memory");
       else
         asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
-    for (int s = 0; s < nS; s += SPG) {  // nS is a multiple of SPG
-      stage(Int<0>{}, s);
-      stage(Int<1>{}, s + 1);
+    const int nstages = ntiles * nS;  // a multiple of SPG
+    for (int u = 0; u < nstages; u += SPG) {
+      stage(Int<0>{});
+      stage(Int<1>{});
     }
   };
   switch (dqs) {
@@ -382,32 +491,7 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
   }
   // no load may still be writing this block's LDS when it exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
-
-  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane>>4) + r ----
-  const int mb = wm * 64 + 4 * (lane >> 4), nb = wn * 64 + (lane & 15);
-  float *__restrict__ yl = args.y[pi] + (int64_t)(m0 + mb) * ldy + (n0 + nb);
-  if (mrows == BM && nrows == BN) {
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
-#pragma unroll
-        for (int b = 0; b < TN; ++b) yr[16 * b] = acc[a][b][r];
-      }
-  } else {
-#pragma unroll
-    for (int a = 0; a < TM; ++a)
-#pragma unroll
-      for (int r = 0; r < 4; ++r) {
-        if (mb + 16 * a + r >= mrows) continue;
-        float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
-#pragma unroll
-        for (int b = 0; b < TN; ++b)
-          if (nb + 16 * b < nrows) yr[16 * b] = acc[a][b][r];
-      }
-  }
-  if ((flags & kBadFlag) && drow_on && d_status) atomicOr(d_status, kDevInvalidByte);
+  if ((flags & kBadFlag) && d_status) atomicOr(d_status, kDevInvalidByte);
 }
 
 }  // namespace
@@ -417,13 +501,24 @@ bool gemm_wide_supported(int count, int64_t M, int64_t N, int64_t K, int G_) {
   // slab of x); and enough tiles to give at least 3/4 of the 256 CUs one
   // block each -- smaller grids run faster as 128 x 128 tiles, two per CU
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return G_ == G && M >= BM && K % G == 0 && tiles < (int64_t(1) << 30) &&
+  return G_ == G && M >= BM && K % G == 0 && tiles * kGemmMaxBatch < (int64_t(1) << 31) &&
          (int64_t)BM * K * 2 < (int64_t(1) << 31) && tiles * count >= 192;
 }
 
 void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                       const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                       int64_t K, int64_t ldy, int32_t *d_status, hipStream_t stream) {
+  // one persistent block per CU
+  static int cus[64] = {};
+  int dev = 0;
+  hipGetDevice(&dev);
+  if (dev < 0 || dev >= 64) dev = 0;
+  if (cus[dev] <= 0) {
+    int n = 0;
+    if (hipDeviceGetAttribute(&n, hipDeviceAttributeMultiprocessorCount, dev) != hipSuccess || n <= 0)
+      n = 256;
+    cus[dev] = n;
+  }
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
   for (int base = 0; base < count; base += kGemmMaxBatch) {
     const int n = count - base < kGemmMaxBatch ? count - base : kGemmMaxBatch;
@@ -434,8 +529,10 @@ void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const
       a.scales[i] = scales[base + i];
       a.y[i] = ys[base + i];
     }
-    hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)tiles, (unsigned)n), dim3(NT), 0, stream,
-                       a, (int)M, (int)N, (int)K, ldy, d_status);
+    const int total = (int)(tiles * n);
+    const int grid = total < cus[dev] ? total : cus[dev];
+    hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a, (int)M,
+                       (int)N, (int)K, ldy, total, d_status);
   }
 }
 
