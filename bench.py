@@ -48,6 +48,10 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
+# HBM bytes per GEMV launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this bench, each
+# scaled by the same counter on a 256 MiB copy (profiles/gemv_m1_hbm_traffic.md); valid only
+# for the kernel source they were taken on (sha256 prefix of csrc/tq_gemv_m1.hip).
+GEMV_TRAFFIC = {"a0757d8a5806cc71": 30535168}
 
 
 def parse():
@@ -59,6 +63,9 @@ def parse():
     ap.add_argument("--prefill-m", type=int, default=512)
     ap.add_argument("--no-cpu-baseline", action="store_true")
     ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--calibrate-copy", action="store_true",
+                    help="after the timed steps, copy 256 MiB device to device three times "
+                         "(a kernel of known traffic for scaling hardware byte counters)")
     return ap.parse_args()
 
 
@@ -96,6 +103,17 @@ def cpu_baseline(mats, x_dec, G, seconds):
     return {"value": nbytes * passes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
             "sample": "%d full passes of M=1 fp64 GEMV through the 72-matrix FFN stack (G=%d), "
                       "single thread, %.1f s" % (passes, G, el)}
+
+
+def gemv_traffic():
+    import hashlib
+    path = os.path.join(ROOT, "ternary_weight_only_amd", "csrc", "tq_gemv_m1.hip")
+    try:
+        with open(path, "rb") as f:
+            h = hashlib.sha256(f.read()).hexdigest()[:16]
+    except OSError:
+        return None
+    return GEMV_TRAFFIC.get(h)
 
 
 def main():
@@ -254,6 +272,14 @@ def main():
     chain_ms = sorted(a.elapsed_time(b) for a, b in chain[1:])
     launch_ms = chain_ms[len(chain_ms) // 2] / (RING * len(groups))
 
+    if args.calibrate_copy:
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        dst = torch.empty_like(src)
+        for _ in range(3):
+            dst.copy_(src)
+        torch.cuda.synchronize()
+        del src, dst
+
     per = {name: 0.0 for name in order}
     total_ms = 0.0
     for t in range(args.steps):
@@ -306,7 +332,7 @@ def main():
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(packed_bytes / gemv_launches / (launch_ms * 1e-3) / 1e9
                                    / HBM_PEAK_GBS, 4),
-                     "traffic": None,
+                     "traffic": gemv_traffic(),
                      "avg_launch_us": round(launch_ms * 1e3, 3),
                      "timing": "median of 3 chains of the decode pass over all %d slots "
                                "(%d back-to-back launches) between HIP events"
