@@ -6,8 +6,8 @@ Workload: the 24-layer Qwen-like FFN stack (hidden 1024, intermediate 3584:
 gate and up W[3584,1024], down W[1024,3584]; 72 matrices, 264,241,152 bf16
 weights ~ N(0, 0.02)), G = 128.  One step is one pass of every step of the
 hot path over that stack, in this order:
-  a5  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_batched:
-      one launch for the 48 K=1024 matrices, one for the 24 K=3584 ones)
+  a5  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
+      one launch for the 48 K=1024 and the 24 K=3584 matrices together)
   a6  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
       likewise two launches; each matrix has its own activations' output)
   a1-a3 quantize + pack all 72 bf16 matrices                (tq_quantize_pack)
@@ -16,15 +16,16 @@ The packed weights live in a ring of eight slots (480 MB, more than the
 256 MB memory-side cache); step t reads slot t%8 and packs into slot
 (t+2)%8, so the weights a GEMV reads were written six steps (several GB of
 traffic) earlier and come from HBM, not from the caches.
-The GEMV and GEMM rows are direct launches (two batched calls each); the 72
-launches of each of the other two rows are captured in a HIP graph.  HIP
+The GEMV and GEMM rows are direct launches (one grouped call, and two batched
+calls); the 72 launches of each of the other two rows are captured in a HIP
+graph.  HIP
 events between the rows time each row on the stream the kernels run on, so
 a row's time includes its launches' dispatch.
 
 The roofline entry times the GEMV kernel itself: after the timed steps, the
-decode pass runs over all eight slots back to back (16 launches, so each
+decode pass runs over all eight slots back to back (8 launches, so each
 launch's dispatch overlaps the previous kernel) between two HIP events, and
-the average launch is the elapsed time / 16; every slot is read once per
+the average launch is the elapsed time / 8; every slot is read once per
 chain, after 7 others (405 MB), so the weights again come from HBM.
 
 `value` is the decode GEMV's packed-weight bandwidth: (packed code bytes +
@@ -166,9 +167,10 @@ def main():
             rc = L.tq_unpack(P[slot][i].data_ptr(), N, K, G, codes[i].data_ptr(), stp, stream)
             assert rc == 0, rc
 
-    # the decode pass: two batched calls (gate+up of all layers share K=1024,
-    # the downs K=3584), one launch each; the pointer arrays of every slot
-    # are built once
+    # the decode pass: one grouped call over all 72 matrices (one launch);
+    # the prefill pass: two batched calls (gate+up of all layers share
+    # K=1024, the downs K=3584); the pointer arrays of every slot are built
+    # once
     groups = {}
     for i, (N, K) in enumerate(shapes):
         groups.setdefault((N, K), []).append(i)
@@ -186,11 +188,16 @@ def main():
                 ptrs([S[slot][i] for i in idx]), ptrs([y_dec[i] for i in idx]),
                 ptrs([x_pre[key[1]] for i in idx]), ptrs([y_pre[i] for i in idx]))
 
+    i64s = ctypes.c_int64 * len(shapes)
+    g_ns = i64s(*[N for N, K in shapes])
+    g_ks = i64s(*[K for N, K in shapes])
+    grouped = {slot: (ptrs(x_dec), ptrs(P[slot]), ptrs(S[slot]), ptrs(y_dec))
+               for slot in range(RING)}
+
     def run_gemv(slot, stream):
-        for (N, K) in groups:
-            n, ax, ap, asc, ay, _, _ = calls[(slot, (N, K))]
-            rc = L.tq_gemv_batched(n, ax, ap, asc, ay, 1, N, K, G, stp, stream)
-            assert rc == 0, rc
+        ax, ap, asc, ay = grouped[slot]
+        rc = L.tq_gemv_grouped(len(shapes), ax, ap, asc, ay, g_ns, g_ks, G, stp, stream)
+        assert rc == 0, rc
 
     # the prefill pass: likewise two batched calls, each problem with its own
     # output (the activations of a K are shared)
@@ -270,7 +277,8 @@ def main():
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status %d" % int(status.item())
     chain_ms = sorted(a.elapsed_time(b) for a, b in chain[1:])
-    launch_ms = chain_ms[len(chain_ms) // 2] / (RING * len(groups))
+    gemv_launches = 1
+    launch_ms = chain_ms[len(chain_ms) // 2] / (RING * gemv_launches)
 
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
@@ -296,7 +304,6 @@ def main():
     gemm_tflops = gemm_flops / (per["gemm"] * 1e-3) / 1e12
     quant_bytes = weights * 2 + packed_bytes
     unpack_bytes = packed_bytes + weights
-    gemv_launches = len(groups)
     rows = {
         "a5_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
                     "launches": gemv_launches, "bytes_per_step": packed_bytes},
@@ -327,7 +334,7 @@ def main():
                                "quantize/pack + unpack per step" % (G, MP),
                    "G": G, "matrices": len(shapes), "weights": weights, "decode_M": 1,
                    "prefill_M": MP, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gemv_m1_kernel (tq_gemv_batched)", "bound": "hbm",
+        "roofline": {"kernel": "gemv_m1_kernel (tq_gemv_grouped)", "bound": "hbm",
                      "achieved": round(packed_bytes / gemv_launches / (launch_ms * 1e-3) / 1e9, 2),
                      "peak": HBM_PEAK_GBS, "unit": "GB/s",
                      "frac": round(packed_bytes / gemv_launches / (launch_ms * 1e-3) / 1e9
@@ -336,7 +343,7 @@ def main():
                      "avg_launch_us": round(launch_ms * 1e3, 3),
                      "timing": "median of 3 chains of the decode pass over all %d slots "
                                "(%d back-to-back launches) between HIP events"
-                               % (RING, RING * len(groups))},
+                               % (RING, RING * gemv_launches)},
         "rows": rows,
         "wall_s_timed": round(wall, 4),
     }

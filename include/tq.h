@@ -129,8 +129,8 @@ int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
 /*
  * Batched decode GEMV: `count` independent problems of the same shape, each
  * exactly as tq_gemv(xs[i], packeds[i], scales[i], M, N, K, G, ys[i]), run in
- * as few launches as possible (one per 64 problems) so that a stack of small
- * matrices -- e.g. the same projection of every layer of a decoder -- streams
+ * as few launches as possible (one per 128 problems at M = 1, per 64 above)
+ * so that a stack of small matrices -- e.g. the same projection of every layer of a decoder -- streams
  * its packed weights without a kernel launch per matrix.
  *   xs, packeds, scales, ys   HOST arrays of `count` DEVICE pointers, with
  *                             the layouts and alignments of tq_gemv; read
@@ -143,6 +143,28 @@ int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
 int tq_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                     const uint16_t *const *scales, float *const *ys,
                     int64_t M, int64_t N, int64_t K, int G,
+                    int32_t *d_status, void *stream);
+
+/*
+ * Grouped decode GEMV: `count` independent M = 1 problems of any shapes,
+ * problem i being tq_gemv(xs[i], packeds[i], scales[i], 1, Ns[i], Ks[i], G,
+ * ys[i]), in as few launches as possible: problems whose shapes run the same
+ * kernel configuration share a launch (up to 128 per launch), which shares
+ * the chip among them in proportion to their sizes -- e.g. every projection
+ * of a stack of decoder layers, whatever its shape, in one pass.  Results
+ * are bit-identical to the single-problem calls.
+ *   xs, packeds, scales, ys   HOST arrays of `count` DEVICE pointers, with
+ *                             the layouts and alignments of tq_gemv
+ *   Ns, Ks                    HOST arrays of `count` shapes
+ *                             (all HOST arrays are read during the call only)
+ *   count >= 0                (0 enqueues nothing)
+ * The outputs ys[i] must not overlap each other or any input.  Errors and
+ * device status as tq_gemv; a NULL or misaligned pointer or a bad shape in
+ * any entry rejects the whole call with nothing enqueued.
+ */
+int tq_gemv_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys,
+                    const int64_t *Ns, const int64_t *Ks, int G,
                     int32_t *d_status, void *stream);
 
 /*

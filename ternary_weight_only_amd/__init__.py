@@ -8,6 +8,7 @@ package only marshals torch tensors to that ABI:
     codes          = unpack(packed, N, K, G)       # a4
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
     ys             = gemv_batched(xs, packeds, scales, N, K, G)  # many same-shaped
+    ys             = gemv_grouped(xs, packeds, scales, Ns, Ks, G)  # M = 1, mixed shapes
     y              = gemm(x_bf16, packed, scales, N, K, G)   # any M
     ys             = gemm_batched(xs, packeds, scales, N, K, G)  # many same-shaped
 
@@ -26,6 +27,7 @@ from .binding import (  # noqa: F401
     gemm_batched,
     gemv,
     gemv_batched,
+    gemv_grouped,
     lib,
     new_status,
     packed_bytes,

@@ -21,7 +21,7 @@ DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_unpack",
-           "tq_gemv", "tq_gemv_batched", "tq_gemm", "tq_gemm_batched")
+           "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -53,6 +53,8 @@ def lib() -> ctypes.CDLL:
         for f in (l.tq_gemv_batched, l.tq_gemm_batched):
             f.argtypes = [i32, p, p, p, p, i64, i64, i64, i32, p, p]
             f.restype = i32
+        l.tq_gemv_grouped.argtypes = [i32, p, p, p, p, p, p, i32, p, p]
+        l.tq_gemv_grouped.restype = i32
         _lib = l
     return _lib
 
@@ -168,6 +170,36 @@ def gemv_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, 
     """[x_i] ([M,K] bf16 each, M <= 16), [packed_i], [scales_i] -> [y_i] ([M,N] fp32), one call."""
     return _batched(lib().tq_gemv_batched, "tq_gemv_batched", xs, packeds, scales_list, N, K, G,
                     status, outs)
+
+
+def gemv_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
+    """[x_i] ([1,K_i] bf16), [packed_i], [scales_i] of shapes (N_i, K_i) -> [y_i] ([1,N_i]
+    fp32): M = 1 GEMVs of mixed shapes in as few launches as possible."""
+    count = len(xs)
+    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == count):
+        raise TQError("tq_gemv_grouped: lists of different lengths")
+    ys = []
+    for i in range(count):
+        _dev(xs[i], "x", (torch.bfloat16, torch.int16), 2)
+        _dev(packeds[i], "packed", (torch.uint8,), packeds[i].dim())
+        _dev(scales_list[i], "scales", (torch.float16, torch.int16), scales_list[i].dim())
+        N, K = int(Ns[i]), int(Ks[i])
+        if tuple(xs[i].shape) != (1, K):
+            raise TQError("tq_gemv_grouped: x %d must be [1,%d]" % (i, K))
+        if packeds[i].numel() != packed_bytes(N, K, G) or scales_list[i].numel() != N * (K // G):
+            raise TQError("tq_gemv_grouped: packed/scales %d do not match N=%d K=%d G=%d"
+                          % (i, N, K, G))
+        ys.append(torch.empty((1, N), dtype=torch.float32, device=xs[i].device)
+                  if outs is None else outs[i])
+    arr = ctypes.c_void_p * max(count, 1)
+    i64s = ctypes.c_int64 * max(count, 1)
+    _rc(lib().tq_gemv_grouped(count, arr(*[t.data_ptr() for t in xs]),
+                              arr(*[t.data_ptr() for t in packeds]),
+                              arr(*[t.data_ptr() for t in scales_list]),
+                              arr(*[t.data_ptr() for t in ys]),
+                              i64s(*[int(n) for n in Ns]), i64s(*[int(k) for k in Ks]), G,
+                              _st(status), _stream()), "tq_gemv_grouped")
+    return ys
 
 
 def gemm_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):

@@ -8,6 +8,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "../../include/tq.h"
 #include "tq_internal.h"
 
@@ -108,6 +110,43 @@ int tq_gemv_batched(int count, const uint16_t *const *xs, const uint8_t *const *
   (void)hipGetLastError();
   tq::launch_gemv_batched(count, xs, packeds, scales, ys, M, N, K, G, d_status,
                           (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemv_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                    const int64_t *Ks, int G, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !ys || !Ns || !Ks) return TQ_ERR_NULL;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
+    const int rc = check_nkg(Ns[i], Ks[i], G);
+    if (rc) return rc;
+    if (Ks[i] > (int64_t(1) << 22)) return TQ_ERR_SHAPE;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
+        !aligned(ys[i], 4))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  // the shapes the M = 1 kernel takes share launches; any other goes alone
+  std::vector<const uint16_t *> gx, gs;
+  std::vector<const uint8_t *> gp;
+  std::vector<float *> gy;
+  std::vector<int64_t> gn, gk;
+  for (int i = 0; i < count; ++i) {
+    if (tq::gemv_m1_supported(1, Ns[i], Ks[i])) {
+      gx.push_back(xs[i]); gp.push_back(packeds[i]); gs.push_back(scales[i]); gy.push_back(ys[i]);
+      gn.push_back(Ns[i]); gk.push_back(Ks[i]);
+    } else {
+      tq::launch_gemv(xs[i], packeds[i], scales[i], 1, Ns[i], Ks[i], G, ys[i], d_status,
+                      (hipStream_t)stream);
+    }
+  }
+  if (!gx.empty())
+    tq::launch_gemv_m1_grouped((int)gx.size(), gx.data(), gp.data(), gs.data(), gy.data(),
+                               gn.data(), gk.data(), G, d_status, (hipStream_t)stream);
   return finish_launch();
 }
 

@@ -31,6 +31,7 @@
 #include <stdint.h>
 
 #include <type_traits>
+#include <vector>
 
 #include "tq_internal.h"
 
@@ -89,7 +90,7 @@ __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint3
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
 constexpr uint32_t kFar = 0x40000000u;  // buffer ranges here stay below this
 constexpr int kRing = 4;  // row batches in flight per lane
-constexpr int kMaxBatch = 64;  // problems per batched launch
+constexpr int kMaxBatch = 128;  // problems per launch (6.5 KB of kernel arguments)
 
 // Up to kMaxBatch same-shaped problems per launch, passed by value.
 struct GemvBatch {
@@ -99,11 +100,19 @@ struct GemvBatch {
   float *y[kMaxBatch];
 };
 
-// The work of a launch is count * nb row batches (nb per problem); a batch
-// is one row per row slot (R = 64W / Lp rows).  Block (s, p) of the 2-D grid
-// takes segment s of problem p: q or q+1 consecutive batches starting at
-// s*q + min(s, rem), so its activations are loaded once and no block
-// divides.  Threads t = 0..64W-1 map to (row slot rr = t/Lp, chunk
+// Shape of each problem of a launch (problems of one launch may differ in N
+// and K): S segments (blocks), the first `rem` of them with q + 1 row
+// batches, the others with q.
+struct GemvShapes {
+  int N[kMaxBatch], K[kMaxBatch], S[kMaxBatch], q[kMaxBatch], rem[kMaxBatch];
+};
+
+// The work of a launch is the row batches of its problems (nb per problem);
+// a batch is one row per row slot (R = 64W / Lp rows).  Block (s, p) of the
+// 2-D grid takes segment s of problem p: q or q+1 consecutive batches
+// starting at s*q + min(s, rem), so its activations are loaded once and no
+// block divides.  Problems of one launch may differ in N and K, as long as
+// they share the block size and the template configuration.  Threads t = 0..64W-1 map to (row slot rr = t/Lp, chunk
 // c = t % Lp); lanes with c >= L idle.  Each lane keeps the packed bytes of
 // its next D batches in flight in a register ring; the loop body loads
 // unconditionally (batches past the segment read out of range, as zeros) and
@@ -122,16 +131,21 @@ struct GemvBatch {
 //     then has few rows, so little is loaded twice.
 template <int G, bool WAVE_ROWS, int XL, bool XDIRECT, bool AL>
 __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
-void gemv_m1_kernel(const GemvBatch args, int N, int K, int L, int Lp, int R, float inv_lp,
-                    int q, int rem, int32_t *__restrict__ d_status) {
+void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restrict__ d_status) {
   __shared__ uint4 lut[kLutEntries * kCopies];
   __shared__ float segsum[2][16 * kMaxWaves];  // 4 batches x R x (Lp/16) = 16W floats
   typedef __attribute__((address_space(3))) u32x4 lds_u32x4;
   extern __shared__ u32x4 xstage_[];  // staged activations (dynamic size)
   lds_u32x4 *xstage = (lds_u32x4 *)xstage_;
 
+  const int pi = (int)blockIdx.y, seg = (int)blockIdx.x;
+  if (seg >= shp.S[pi]) return;  // the grid is as wide as the widest problem
+  const int N = shp.N[pi], K = shp.K[pi], q = shp.q[pi], rem = shp.rem[pi];
+  const int L = K >> 6, Lp = (L + 15) & ~15;
+  const float inv_lp = 1.0f / (float)Lp;
   const int tid = threadIdx.x;
   const int nthreads = blockDim.x;
+  const int R = (int)(((float)nthreads + 0.5f) * inv_lp);  // rows per batch: nthreads / Lp
   const int nseg = Lp >> 4;  // 16-lane segments per row
   // tid / Lp through a rounded reciprocal: (tid + 1/2) / Lp lies at least
   // 1/(2 Lp) away from an integer, far more than the float error here
@@ -142,7 +156,6 @@ void gemv_m1_kernel(const GemvBatch args, int N, int K, int L, int Lp, int R, fl
   const uint32_t rowbytes = (uint32_t)L * kChunk;
   const uint32_t total = (uint32_t)N * rowbytes;  // < 2^30, checked by the launcher
   const int gidx = G == 64 ? c : (c >> 1);
-  const int pi = (int)blockIdx.y, seg = (int)blockIdx.x;
   const int b_begin = seg * q + (seg < rem ? seg : rem);
   const int b_end = b_begin + q + (seg < rem ? 1 : 0);
 
@@ -408,69 +421,125 @@ int m1_stage_bytes(int K) {
 }
 bool m1_staged(int K) { return kStaticLds + m1_stage_bytes(K) <= 80 * 1024; }
 
-struct M1Shape {
-  dim3 grid;
-  int threads, N, K, L, Lp, R, q, rem;
+// Segments of a problem with nb row batches whose share of a launch is
+// `share` blocks out of 512 (at most two blocks per CU -- two fit the 64 KB
+// table -- so every block is resident from the start).  A block runs whole
+// rounds of kRing batches (a round's batches past its segment are computed
+// on zeros), so a CU's work is about ceil(blocks / 256) blocks times the
+// rounds of the longest segment, the launch counting 512 / share problems
+// like this one.  Among the segment counts up to the share that give each
+// segment a batch, take the one with the least work on the busiest CU, then
+// the least work in all, then the most blocks (more loads in flight).
+int m1_segments(int64_t share, int64_t nb) {
+  const int64_t count = share >= 512 ? 1 : 512 / share;
+  int64_t smax = share < nb ? share : nb;
+  int best = 1;
+  int64_t best_cu = -1, best_all = -1;
+  for (int64_t S = 1; S <= smax; ++S) {
+    const int64_t q = nb / S, rem = nb % S;
+    const int64_t rounds_long = (q + (rem ? 1 : 0) + kRing - 1) / kRing;
+    const int64_t rounds_short = (q + kRing - 1) / kRing;
+    const int64_t blocks = (int64_t)count * S;
+    const int64_t cu = ((blocks + 255) / 256) * rounds_long;
+    const int64_t all = (int64_t)count * (rem * rounds_long + (S - rem) * rounds_short);
+    if (best_cu < 0 || cu < best_cu || (cu == best_cu && all <= best_all)) {
+      best = (int)S;
+      best_cu = cu;
+      best_all = all;
+    }
+  }
+  return best;
+}
+
+// Launch configuration of one problem: the block size and the kernel's
+// template parameters.  Problems with equal configurations share launches.
+struct M1Config {
+  int threads;
+  bool wave_rows;  // rows of 16, 32 or 64 lanes, inside one wave
+  bool direct;     // activations loaded per lane (rows too long to stage)
+  int xl;          // staged pieces per thread: 1, 2 or 3
+  bool aligned;    // both batch steps in whole dwords
+  bool operator==(const M1Config &o) const {
+    return threads == o.threads && wave_rows == o.wave_rows && direct == o.direct &&
+           xl == o.xl && aligned == o.aligned;
+  }
 };
 
+M1Config m1_config(int64_t K, int G) {
+  M1Config c;
+  const int L = (int)(K / 64), Lp = 16 * ((L + 15) / 16);
+  c.threads = 64 * m1_waves(K);
+  const int R = c.threads / Lp;
+  c.wave_rows = Lp == 16 || Lp == 32 || Lp == 64;
+  c.direct = !m1_staged((int)K);
+  const int xl = ((int)(K >> 3) + 1 + c.threads - 1) / c.threads;
+  c.xl = c.direct ? 1 : (xl <= 1 ? 1 : (xl <= 2 ? 2 : 3));
+  const int64_t bstep = (int64_t)R * L * kChunk, sstep = 2 * (int64_t)R * (K / G);
+  c.aligned = bstep % 4 == 0 && sstep % 4 == 0;
+  return c;
+}
+
 template <int G, bool WR, int XL, bool XD, bool AL>
-void launch_m1_k(const GemvBatch &args, const M1Shape &s, int32_t *d_status, hipStream_t stream) {
-  const int lds = XD ? 0 : m1_stage_bytes(s.K);
-  hipLaunchKernelGGL((gemv_m1_kernel<G, WR, XL, XD, AL>), s.grid, dim3(s.threads), lds, stream,
-                     args, s.N, s.K, s.L, s.Lp, s.R, 1.0f / (float)s.Lp, s.q, s.rem, d_status);
+void launch_m1_k(const GemvBatch &args, const GemvShapes &shp, dim3 grid, int threads, int lds,
+                 int32_t *d_status, hipStream_t stream) {
+  hipLaunchKernelGGL((gemv_m1_kernel<G, WR, XL, XD, AL>), grid, dim3(threads), lds, stream, args,
+                     shp, d_status);
 }
 
 template <int G, bool WR, int XL, bool XD>
-void launch_m1_al(const GemvBatch &args, const M1Shape &s, int32_t *d_status, hipStream_t stream) {
-  // both batch steps (R rows of packed bytes, R rows of scales) in whole dwords
-  const int64_t bstep = (int64_t)s.R * s.L * kChunk, sstep = 2 * (int64_t)s.R * (s.K / G);
-  if (bstep % 4 == 0 && sstep % 4 == 0)
-    launch_m1_k<G, WR, XL, XD, true>(args, s, d_status, stream);
+void launch_m1_al(const M1Config &c, const GemvBatch &args, const GemvShapes &shp, dim3 grid,
+                  int lds, int32_t *d_status, hipStream_t stream) {
+  if (c.aligned)
+    launch_m1_k<G, WR, XL, XD, true>(args, shp, grid, c.threads, lds, d_status, stream);
   else
-    launch_m1_k<G, WR, XL, XD, false>(args, s, d_status, stream);
+    launch_m1_k<G, WR, XL, XD, false>(args, shp, grid, c.threads, lds, d_status, stream);
 }
 
 template <int G, bool WR>
-void launch_m1_wr(const GemvBatch &args, const M1Shape &s, int32_t *d_status, hipStream_t stream) {
-  if (!m1_staged(s.K)) {
-    launch_m1_al<G, WR, 1, true>(args, s, d_status, stream);
-    return;
-  }
-  // staged 16-byte pieces of activations (plus a zero piece) per thread
-  const int xl = ((s.K >> 3) + 1 + s.threads - 1) / s.threads;
-  if (xl <= 1)
-    launch_m1_al<G, WR, 1, false>(args, s, d_status, stream);
-  else if (xl <= 2)
-    launch_m1_al<G, WR, 2, false>(args, s, d_status, stream);
+void launch_m1_wr(const M1Config &c, const GemvBatch &args, const GemvShapes &shp, dim3 grid,
+                  int lds, int32_t *d_status, hipStream_t stream) {
+  if (c.direct)
+    launch_m1_al<G, WR, 1, true>(c, args, shp, grid, lds, d_status, stream);
+  else if (c.xl == 1)
+    launch_m1_al<G, WR, 1, false>(c, args, shp, grid, lds, d_status, stream);
+  else if (c.xl == 2)
+    launch_m1_al<G, WR, 2, false>(c, args, shp, grid, lds, d_status, stream);
   else
-    launch_m1_al<G, WR, 3, false>(args, s, d_status, stream);
+    launch_m1_al<G, WR, 3, false>(c, args, shp, grid, lds, d_status, stream);
 }
 
+// One launch over up to kMaxBatch problems that share configuration c.
 template <int G>
-void launch_m1(const GemvBatch &args, int count, int64_t N, int64_t K, int32_t *d_status,
-               hipStream_t stream) {
-  M1Shape s;
-  s.N = (int)N;
-  s.K = (int)K;
-  s.L = (int)(K / 64);
-  s.Lp = 16 * ((s.L + 15) / 16);
-  s.threads = 64 * m1_waves(K);
-  s.R = s.threads / s.Lp;
-  // segments per problem: at most two blocks per CU over the whole launch
-  // (two fit the 64 KB table), so every block is resident from the start,
-  // and at least one batch per segment
-  const int64_t nb = (N + s.R - 1) / s.R;
-  const int64_t want = count <= 2 * 256 ? (2 * 256) / count : 1;
-  const int S = (int)(want < nb ? want : nb);
-  s.q = (int)(nb / S);
-  s.rem = (int)(nb % S);
-  s.grid = dim3(S, count);
-  // rows within one wave (16, 32 or 64 lanes) are summed with cross-lane
-  // moves; longer rows, or 48-lane rows that cross waves, through LDS
-  if (s.Lp == 16 || s.Lp == 32 || s.Lp == 64)
-    launch_m1_wr<G, true>(args, s, d_status, stream);
+void launch_m1(const M1Config &c, int count, const uint16_t *const *xs,
+               const uint8_t *const *packeds, const uint16_t *const *scales, float *const *ys,
+               const int64_t *Ns, const int64_t *Ks, int32_t *d_status, hipStream_t stream) {
+  GemvBatch args = {};
+  GemvShapes shp = {};
+  int smax = 1, lds = 0;
+  // the 512 blocks of a launch are shared out in proportion to the problems'
+  // sizes (weights, i.e. packed bytes)
+  double total = 0.0;
+  for (int i = 0; i < count; ++i) total += (double)Ns[i] * (double)Ks[i];
+  for (int i = 0; i < count; ++i) {
+    args.x[i] = xs[i]; args.packed[i] = packeds[i]; args.scales[i] = scales[i]; args.y[i] = ys[i];
+    const int L = (int)(Ks[i] / 64), Lp = 16 * ((L + 15) / 16), R = c.threads / Lp;
+    const int64_t nb = (Ns[i] + R - 1) / R;
+    int64_t share = (int64_t)(512.0 * ((double)Ns[i] * (double)Ks[i]) / total);
+    if (share < 1) share = 1;
+    const int S = m1_segments(share, nb);
+    shp.N[i] = (int)Ns[i];
+    shp.K[i] = (int)Ks[i];
+    shp.S[i] = S;
+    shp.q[i] = (int)(nb / S);
+    shp.rem[i] = (int)(nb % S);
+    if (S > smax) smax = S;
+    if (!c.direct && m1_stage_bytes((int)Ks[i]) > lds) lds = m1_stage_bytes((int)Ks[i]);
+  }
+  const dim3 grid(smax, count);
+  if (c.wave_rows)
+    launch_m1_wr<G, true>(c, args, shp, grid, lds, d_status, stream);
   else
-    launch_m1_wr<G, false>(args, s, d_status, stream);
+    launch_m1_wr<G, false>(c, args, shp, grid, lds, d_status, stream);
 }
 
 bool m1_supported(int64_t M, int64_t N, int64_t K) {
@@ -482,12 +551,41 @@ bool m1_supported(int64_t M, int64_t N, int64_t K) {
 
 bool gemv_m1_supported(int64_t M, int64_t N, int64_t K) { return m1_supported(M, N, K); }
 
+void launch_gemv_m1_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                            const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                            const int64_t *Ks, int G, int32_t *d_status, hipStream_t stream) {
+  // problems in order, grouped by configuration, up to kMaxBatch per launch
+  const uint16_t *gx[kMaxBatch];
+  const uint8_t *gp[kMaxBatch];
+  const uint16_t *gs[kMaxBatch];
+  float *gy[kMaxBatch];
+  int64_t gn[kMaxBatch], gk[kMaxBatch];
+  std::vector<unsigned char> done((size_t)(count > 0 ? count : 0), 0);
+  for (int i0 = 0; i0 < count; ++i0) {
+    if (done[i0]) continue;
+    const M1Config c = m1_config(Ks[i0], G);
+    int n = 0;
+    for (int i = i0; i < count; ++i) {
+      if (done[i] || !(m1_config(Ks[i], G) == c)) continue;
+      done[i] = true;
+      gx[n] = xs[i]; gp[n] = packeds[i]; gs[n] = scales[i]; gy[n] = ys[i];
+      gn[n] = Ns[i]; gk[n] = Ks[i];
+      if (++n == kMaxBatch) {
+        if (G == 64) launch_m1<64>(c, n, gx, gp, gs, gy, gn, gk, d_status, stream);
+        else launch_m1<128>(c, n, gx, gp, gs, gy, gn, gk, d_status, stream);
+        n = 0;
+      }
+    }
+    if (n > 0) {
+      if (G == 64) launch_m1<64>(c, n, gx, gp, gs, gy, gn, gk, d_status, stream);
+      else launch_m1<128>(c, n, gx, gp, gs, gy, gn, gk, d_status, stream);
+    }
+  }
+}
+
 void launch_gemv_m1(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t N,
                     int64_t K, int G, float *y, int32_t *d_status, hipStream_t stream) {
-  GemvBatch args = {};
-  args.x[0] = x; args.packed[0] = packed; args.scales[0] = scales; args.y[0] = y;
-  if (G == 64) launch_m1<64>(args, 1, N, K, d_status, stream);
-  else launch_m1<128>(args, 1, N, K, d_status, stream);
+  launch_gemv_m1_grouped(1, &x, &packed, &scales, &y, &N, &K, G, d_status, stream);
 }
 
 void launch_gemv_m1_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
@@ -495,13 +593,10 @@ void launch_gemv_m1_batched(int count, const uint16_t *const *xs, const uint8_t 
                             int G, int32_t *d_status, hipStream_t stream) {
   for (int i0 = 0; i0 < count; i0 += kMaxBatch) {
     const int cnt = count - i0 < kMaxBatch ? count - i0 : kMaxBatch;
-    GemvBatch args = {};
-    for (int i = 0; i < cnt; ++i) {
-      args.x[i] = xs[i0 + i]; args.packed[i] = packeds[i0 + i];
-      args.scales[i] = scales[i0 + i]; args.y[i] = ys[i0 + i];
-    }
-    if (G == 64) launch_m1<64>(args, cnt, N, K, d_status, stream);
-    else launch_m1<128>(args, cnt, N, K, d_status, stream);
+    int64_t ns[kMaxBatch], ks[kMaxBatch];
+    for (int i = 0; i < cnt; ++i) { ns[i] = N; ks[i] = K; }
+    launch_gemv_m1_grouped(cnt, xs + i0, packeds + i0, scales + i0, ys + i0, ns, ks, G, d_status,
+                           stream);
   }
 }
 

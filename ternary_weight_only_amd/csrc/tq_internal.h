@@ -36,6 +36,12 @@ bool gemv_m1_supported(int64_t M, int64_t N, int64_t K);
 void launch_gemv_m1(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t N,
                     int64_t K, int G, float *y, int32_t *d_status, hipStream_t stream);
 
+// Problems of any shapes the M = 1 kernel takes, grouped into launches by
+// kernel configuration (problems in order within a group).
+void launch_gemv_m1_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                            const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                            const int64_t *Ks, int G, int32_t *d_status, hipStream_t stream);
+
 void launch_gemv_m1_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                             const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
                             int G, int32_t *d_status, hipStream_t stream);

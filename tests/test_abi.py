@@ -93,6 +93,27 @@ def test_batched_argument_errors(fn):
     assert f(2, bad_al, good, good, good, 1, 8, 128, 64, None, None) == -4
 
 
+def test_grouped_argument_errors():
+    lib = _lib()
+    f = lib.tq_gemv_grouped
+    arr = ctypes.c_void_p * 2
+    i64 = ctypes.c_int64 * 2
+    good = arr(FAKE, FAKE + 4096)
+    bad_al = arr(FAKE, FAKE + 4)
+    nul = arr(FAKE, None)
+    ns, ks = i64(8, 16), i64(128, 256)
+    assert f(0, None, None, None, None, None, None, 64, None, None) == 0     # nothing to do
+    assert f(-1, good, good, good, good, ns, ks, 64, None, None) == -2
+    assert f(2, good, good, good, good, None, ks, 64, None, None) == -1
+    assert f(2, nul, good, good, good, ns, ks, 64, None, None) == -1
+    assert f(2, good, good, good, good, ns, i64(128, 100), 64, None, None) == -2   # K % G
+    assert f(2, good, good, good, good, i64(8, 0), ks, 64, None, None) == -2       # N < 1
+    assert f(2, good, good, good, good, ns, i64(128, (1 << 22) + 64), 64, None, None) == -2
+    assert f(2, good, good, good, good, ns, ks, 32, None, None) == -3
+    assert f(2, bad_al, good, good, good, ns, ks, 64, None, None) == -4
+    assert f(2, good, good, good, good, ns, ks, 64, FAKE + 2, None) == -4        # status
+
+
 def test_quantize_unpack_argument_errors():
     lib = _lib()
     q, u = lib.tq_quantize_pack, lib.tq_unpack

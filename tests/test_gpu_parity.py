@@ -293,6 +293,48 @@ def test_gemv_row_shapes(K, G):
     assert int(st.item()) & 4
 
 
+@pytest.mark.parametrize("G", [64, 128])
+def test_gemv_grouped_mixed_shapes(G):
+    """tq_gemv_grouped over mixed shapes -- two kernel configurations, one
+    shape the M = 1 kernel does not take (K = 8320: 130 chunks), ragged N --
+    and more problems than one launch holds for the commonest configuration:
+    bit-identical to one tq_gemv per problem, within the oracle's bound on
+    sampled problems; an invalid byte in one problem is flagged."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
+    base = [(96, 1024), (40, 3584), (37, 640), (5, 8320), (64, 2048)]
+    shapes = [base[i % len(base)] if i < 10 else (32 + i % 7, 1024) for i in range(140)]
+    shapes = [(n, k) for n, k in shapes if k % G == 0]
+    ws = [inputs.normal_bf16(900 + i, (n, k), 0.02) for i, (n, k) in enumerate(shapes)]
+    xs = [inputs.activation(1000 + i, 1, k) for i, (n, k) in enumerate(shapes)]
+    refs = [oracle.quantize_pack(w, G) for w in ws]
+    xd = [dev_bf16(x) for x in xs]
+    pdv = [dev_u8(p) for p, _, _ in refs]
+    sdv = [dev_f16bits(s) for _, s, _ in refs]
+    Ns = [n for n, _ in shapes]
+    Ks = [k for _, k in shapes]
+    say("gemv_grouped G=%d count=%d" % (G, len(shapes)))
+    st = tq.new_status()
+    ys = tq.gemv_grouped(xd, pdv, sdv, Ns, Ks, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for i, (n, k) in enumerate(shapes):
+        y1 = tq.gemv(xd[i], pdv[i], sdv[i], n, k, G)
+        assert torch.equal(ys[i], y1), "grouped item %d (N=%d K=%d) differs" % (i, n, k)
+        if i < 10 or i == len(shapes) - 1:
+            p, s, _ = refs[i]
+            y_ref, bound, _ = oracle.matmul(xs[i], p, s, n, k, G)
+            assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "grouped item %d" % i)
+    bad = refs[1][0].reshape(-1).copy()
+    bad[bad.size // 3] = 247
+    pdv[1] = dev_u8(bad.reshape(refs[1][0].shape))
+    st = tq.new_status()
+    tq.gemv_grouped(xd, pdv, sdv, Ns, Ks, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) & 4
+
+
 def test_gemm_wide_tiles_ragged_unaligned_and_invalid_bytes():
     """tq_gemm_batched at G = 128 with enough 256 x 128 tiles to take the
     wide-tile kernel (48 problems of M=300, N=200: ragged tiles in both M and
