@@ -52,7 +52,7 @@ METRIC = "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% 
 # HBM bytes per GEMV launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this bench, each
 # scaled by the same counter on a 256 MiB copy (profiles/gemv_m1_hbm_traffic.md); valid only
 # for the kernel source they were taken on (sha256 prefix of csrc/tq_gemv_m1.hip).
-GEMV_TRAFFIC = {"a0757d8a5806cc71": 30535168}
+GEMV_TRAFFIC = {"1cfc50b97901eb3f": 60691548}
 
 
 def parse():
