@@ -6,12 +6,12 @@ Workload: the 24-layer Qwen-like FFN stack (hidden 1024, intermediate 3584:
 gate and up W[3584,1024], down W[1024,3584]; 72 matrices, 264,241,152 bf16
 weights ~ N(0, 0.02)), G = 128.  One step is one pass of every step of the
 hot path over that stack, in this order:
-  a5  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
+  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
       one launch for the 48 K=1024 and the 24 K=3584 matrices together)
-  a6  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
-      likewise two launches; each matrix has its own activations' output)
-  a1-a3 quantize + pack all 72 bf16 matrices                (tq_quantize_pack)
-  a4  unpack + validate all 72 packed matrices              (tq_unpack)
+  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
+      two launches, one per shape; each matrix has its own activations and output)
+  quantize + pack all 72 bf16 matrices                 (tq_quantize_pack)
+  unpack + validate all 72 packed matrices             (tq_unpack)
 The packed weights live in a ring of eight slots (480 MB, more than the
 256 MB memory-side cache); step t reads slot t%8 and packs into slot
 (t+2)%8, so the weights a GEMV reads were written six steps (several GB of
@@ -305,15 +305,15 @@ def main():
     quant_bytes = weights * 2 + packed_bytes
     unpack_bytes = packed_bytes + weights
     rows = {
-        "a5_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
+        "decode_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
                     "launches": gemv_launches, "bytes_per_step": packed_bytes},
-        "a6_gemm": {"ms": per["gemm"], "TFLOP/s": gemm_tflops,
+        "prefill_gemm": {"ms": per["gemm"], "TFLOP/s": gemm_tflops,
                     "frac_mfma": gemm_tflops / MFMA_BF16_PEAK_TFLOPS, "M": MP,
                     "flop_per_step": gemm_flops},
-        "a1_a3_quantize_pack": {"ms": per["quant"],
+        "quantize_pack": {"ms": per["quant"],
                                 "GB/s": quant_bytes / (per["quant"] * 1e-3) / 1e9,
                                 "bytes_per_step": quant_bytes},
-        "a4_unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
+        "unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
                       "bytes_per_step": unpack_bytes},
     }
     out = {

@@ -63,6 +63,8 @@ def _load():
         lib.oracle_unpack.restype = ctypes.c_int
         lib.oracle_matmul.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
         lib.oracle_matmul.restype = ctypes.c_int
+        lib.oracle_dequantize.argtypes = [p, p, i64, i64, i64, p, p]
+        lib.oracle_dequantize.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -114,6 +116,23 @@ def unpack(packed: np.ndarray, N: int, K: int, G: int):
     if rc:
         raise OracleError("oracle_unpack rc=%d" % rc)
     return codes, int(st[0])
+
+
+def dequantize(packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):
+    """Decode to bf16: w_hat[n,k] = bf16_RNE(c[n,k] * s[n,k/G]).
+
+    Returns (w_hat uint16 [N,K] bf16 bits, status bits int)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    rb = packed_row_bytes(K, G)
+    if rb == 0 or p.size != N * rb or s.size != N * (K // G):
+        raise OracleError("bad packed/scales sizes")
+    out = np.empty((N, K), np.uint16)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_dequantize(_ptr(p), _ptr(s), N, K, G, _ptr(out), _ptr(st))
+    if rc:
+        raise OracleError("oracle_dequantize rc=%d" % rc)
+    return out, int(st[0])
 
 
 def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):

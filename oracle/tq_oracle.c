@@ -189,7 +189,7 @@ static uint64_t big_rne_div(const big_t *a, uint64_t G, int n)
 }
 
 /* ------------------------------------------------------------------------ */
-/* a1: group scale                                                            */
+/* group scale                                                                */
 /* ------------------------------------------------------------------------ */
 
 /*
@@ -269,7 +269,7 @@ static double f16_to_double(uint16_t h)
 }
 
 /* ------------------------------------------------------------------------ */
-/* a1-a3: quantize + pack                                                     */
+/* quantize + pack                                                           */
 /* ------------------------------------------------------------------------ */
 
 /*
@@ -299,7 +299,7 @@ int oracle_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int64_t G,
             if (gst) sbits = 0x7E00;
             else gst |= group_scale_bits(wg, G, &sbits);
 
-            /* a2: codes.  |w| == s/2 is a tie and goes to 0 (round half to
+            /* Codes.  |w| == s/2 is a tie and goes to 0 (round half to
              * even of +-0.5); beyond 1.5 s the code saturates at +-1. */
             for (int64_t t = 0; t < 5 * B; ++t) code[t] = 0;  /* padding = 0 */
             if (!gst) {
@@ -310,7 +310,7 @@ int oracle_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int64_t G,
                 }
             }
 
-            /* a3: five base-3 digits per byte, first weight lowest digit. */
+            /* Five base-3 digits per byte, first weight lowest digit. */
             for (int64_t b = 0; b < B; ++b) {
                 int byte = 0, p3 = 1;
                 for (int i = 0; i < 5; ++i) {
@@ -328,7 +328,7 @@ int oracle_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int64_t G,
 }
 
 /* ------------------------------------------------------------------------ */
-/* a4: unpack                                                                 */
+/* unpack                                                                     */
 /* ------------------------------------------------------------------------ */
 
 /* packed -> codes[N,K] int8 in {-1,0,1}. */
@@ -363,7 +363,70 @@ int oracle_unpack(const uint8_t *packed, int64_t N, int64_t K, int64_t G,
 }
 
 /* ------------------------------------------------------------------------ */
-/* a5/a6: matmul in fp64                                                      */
+/* decode to bf16                                                             */
+/* ------------------------------------------------------------------------ */
+
+/* Nearest bf16 to a finite double, ties to even (sign kept, zero kept as
+ * +-0).  Only reached with |v| in the fp16 range, which lies inside bf16's
+ * normal range, so there is no subnormal or overflow case. */
+static uint16_t double_to_bf16_rne(double v)
+{
+    uint16_t sign = signbit(v) ? 0x8000 : 0;
+    double a = fabs(v);
+    if (a == 0.0) return sign;
+    int e;
+    double m = frexp(a, &e);          /* a = m * 2^e, 0.5 <= m < 1 */
+    double q = ldexp(m, 8);           /* 128 <= q < 256: 8 significant bits */
+    double r = floor(q);
+    double frac = q - r;
+    if (frac > 0.5 || (frac == 0.5 && fmod(r, 2.0) != 0.0)) r += 1.0;
+    if (r == 256.0) { r = 128.0; e += 1; }
+    int E = e - 1 + 127;              /* a = (r / 128) * 2^(e - 1) */
+    return (uint16_t)(sign | (uint16_t)(E << 7) | (uint16_t)((int)r - 128));
+}
+
+/*
+ * out[n,k] = bf16_RNE(c[n,k] * s[n,k/G]) as bf16 bits ([P4] codec.py
+ * description: decoding gives back c * s; screen.py description: the decoder
+ * hands the selected weights back as bf16).  c comes from the bytes exactly as in
+ * oracle_unpack (an invalid byte gives code 0 at its five positions and sets
+ * INVALID_BYTE; a padding trit other than code 0 sets BAD_PADDING).  The
+ * product is the IEEE one: c = 0 gives a zero with the sign of s, c = -1
+ * negates.  A non-finite scale sets NONFINITE; its group's outputs are then
+ * not defined here (they are written as 0).
+ */
+int oracle_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, int64_t K,
+                      int64_t G, uint16_t *out, int32_t *status)
+{
+    if (!packed || !scales || !out) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G;
+    int8_t *codes = (int8_t *)malloc((size_t)(N * K));
+    if (!codes) return OR_ERR_NULL;
+    int32_t st = 0;
+    rc = oracle_unpack(packed, N, K, G, codes, &st);
+    if (rc) { free(codes); return rc; }
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < nG; ++g) {
+            uint16_t sb = scales[n * nG + g];
+            int finite = ((sb >> 10) & 0x1F) != 0x1F;
+            if (!finite) st |= OR_NONFINITE;
+            double s = finite ? f16_to_double(sb) : 0.0;
+            for (int64_t j = 0; j < G; ++j) {
+                int64_t k = g * G + j;
+                double v = (double)codes[n * K + k] * s;  /* exact */
+                out[n * K + k] = finite ? double_to_bf16_rne(v) : 0;
+            }
+        }
+    }
+    free(codes);
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* matmul in fp64                                                             */
 /* ------------------------------------------------------------------------ */
 
 /*
