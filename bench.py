@@ -22,6 +22,11 @@ graph.  HIP
 events between the rows time each row on the stream the kernels run on, so
 a row's time includes its launches' dispatch.
 
+Outside the step, the decode to bf16 of every matrix of a slot (two
+tq_dequantize_batched calls, one per shape) runs over four slots back to back
+between two HIP events (median of three such chains, per pass); its row
+counts packed + scale bytes read and bf16 bytes written.
+
 The roofline entry times the GEMV kernel itself: after the timed steps, the
 decode pass runs over all eight slots back to back (8 launches, so each
 launch's dispatch overlaps the previous kernel) between two HIP events, and
@@ -280,6 +285,32 @@ def main():
     gemv_launches = 1
     launch_ms = chain_ms[len(chain_ms) // 2] / (RING * gemv_launches)
 
+    # decode to bf16, outside the step: every matrix of a slot into its own
+    # bf16 output, one batched call per shape (2 launches), median of 3 passes
+    w_hat = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for N, K in shapes]
+    dq_calls = {slot: [(N, K, len(idx), ptrs([P[slot][i] for i in idx]),
+                        ptrs([S[slot][i] for i in idx]), ptrs([w_hat[i] for i in idx]))
+                       for (N, K), idx in groups.items()] for slot in range(RING)}
+
+    def run_dequant(slot, stream):
+        for N, K, n, ap, asc, aw in dq_calls[slot]:
+            rc = L.tq_dequantize_batched(n, ap, asc, aw, N, K, G, stp, stream)
+            assert rc == 0, rc
+
+    dq = []
+    with torch.cuda.stream(stream):
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for slot in range(4):
+                run_dequant((4 * rep + slot) % RING, sp)
+            e1.record(stream)
+            dq.append((e0, e1))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status %d" % int(status.item())
+    dq_ms = sorted(a.elapsed_time(b) for a, b in dq[1:])[1] / 4
+    del w_hat
+
     if args.calibrate_copy:
         src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
         dst = torch.empty_like(src)
@@ -304,6 +335,7 @@ def main():
     gemm_tflops = gemm_flops / (per["gemm"] * 1e-3) / 1e12
     quant_bytes = weights * 2 + packed_bytes
     unpack_bytes = packed_bytes + weights
+    dequant_bytes = packed_bytes + 2 * weights
     rows = {
         "decode_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
                     "launches": gemv_launches, "bytes_per_step": packed_bytes},
@@ -313,6 +345,10 @@ def main():
         "quantize_pack": {"ms": per["quant"],
                                 "GB/s": quant_bytes / (per["quant"] * 1e-3) / 1e9,
                                 "bytes_per_step": quant_bytes},
+        "decode_bf16": {"ms": dq_ms, "GB/s": dequant_bytes / (dq_ms * 1e-3) / 1e9,
+                        "frac_hbm": dequant_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "bytes_per_pass": dequant_bytes, "launches": len(groups),
+                        "in_step": False},
         "unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
                       "bytes_per_step": unpack_bytes},
     }

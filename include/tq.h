@@ -63,10 +63,12 @@ typedef enum {
 
 /* Device status bits. */
 enum {
-    TQ_DEV_NONFINITE = 1,      /* a weight is Inf or NaN (tq_quantize_pack)        */
+    TQ_DEV_NONFINITE = 1,      /* a weight (tq_quantize_pack) or a scale           */
+                               /* (tq_dequantize) is Inf or NaN                    */
     TQ_DEV_SCALE_OVERFLOW = 2, /* a group mean rounds to >= 65520 (tq_quantize_pack)*/
     TQ_DEV_INVALID_BYTE = 4,   /* a packed byte is >= 243 (unpack, gemv, gemm)     */
-    TQ_DEV_BAD_PADDING = 8     /* a padding trit is not code 0 (tq_unpack)         */
+    TQ_DEV_BAD_PADDING = 8     /* a padding trit is not code 0 (tq_unpack,         */
+                               /* tq_dequantize)                                   */
 };
 
 /* Human-readable name of a tq_status value. */
@@ -103,6 +105,42 @@ int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
  */
 int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
               int8_t *codes, int32_t *d_status, void *stream);
+
+/*
+ * Decode packed codes and group scales to a bf16 weight matrix:
+ *   w_hat[n,k] = bf16_rne(c[n,k] * s[n, k/G])
+ * Source: precisit "pack-unpack-run" README, codec.py description (decoding
+ * gives back c * s) and screen.py description (the decoder hands the
+ * selected weights back as bf16).  The product is exact; its one rounding,
+ * to nearest with ties to even, is the fp16 -> bf16 rounding of s.  Zeros
+ * carry the IEEE sign of c * s (code 0 takes the sign of s).
+ *   packed   [N, K/G, ceil(G/5)] bytes (any alignment)
+ *   scales   [N, K/G] fp16, 2-byte aligned
+ *   w_hat    [N,K] bf16 bit patterns, 16-byte aligned, overwritten
+ * An invalid byte sets TQ_DEV_INVALID_BYTE and its five weights decode as
+ * code 0; a padding trit other than code 0 sets TQ_DEV_BAD_PADDING; an Inf
+ * or NaN scale sets TQ_DEV_NONFINITE and its group decodes to +0.
+ * Bit-exact and deterministic.
+ */
+int tq_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, int64_t K,
+                  int G, uint16_t *w_hat, int32_t *d_status, void *stream);
+
+/*
+ * Batched decode to bf16: `count` matrices of the same shape, each exactly
+ * as tq_dequantize(packeds[i], scales[i], N, K, G, w_hats[i]), in one
+ * launch per 64 matrices -- e.g. every tensor of one shape in a package,
+ * which one launch per tensor would leave mostly to launch ramp-up.
+ *   packeds, scales, w_hats   HOST arrays of `count` DEVICE pointers, with
+ *                             the layouts and alignments of tq_dequantize;
+ *                             read during the call only
+ *   count >= 0                (0 enqueues nothing)
+ * The outputs must not overlap each other or any input.  Errors and device
+ * status as tq_dequantize; a NULL or misaligned pointer in any entry
+ * rejects the whole call with nothing enqueued.
+ */
+int tq_dequantize_batched(int count, const uint8_t *const *packeds,
+                          const uint16_t *const *scales, uint16_t *const *w_hats,
+                          int64_t N, int64_t K, int G, int32_t *d_status, void *stream);
 
 /*
  * Decode GEMV / skinny matmul, 1 <= M <= 16:

@@ -4,8 +4,10 @@ packed-ternary x bf16 matmul on AMD MI355X (gfx950).
 The work happens in libtq.so (hand-written HIP; C ABI in include/tq.h).  This
 package only marshals torch tensors to that ABI:
 
-    packed, scales = quantize_pack(w_bf16, G)      # a1-a3
-    codes          = unpack(packed, N, K, G)       # a4
+    packed, scales = quantize_pack(w_bf16, G)      # scale, codes, base-3 bytes
+    codes          = unpack(packed, N, K, G)       # codes + validation
+    w_hat          = dequantize(packed, scales, N, K, G)  # bf16 c * s
+    w_hats         = dequantize_batched(packeds, scales, N, K, G)  # many same-shaped
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
     ys             = gemv_batched(xs, packeds, scales, N, K, G)  # many same-shaped
     ys             = gemv_grouped(xs, packeds, scales, Ns, Ks, G)  # M = 1, mixed shapes
@@ -23,6 +25,8 @@ from .binding import (  # noqa: F401
     DEV_NONFINITE,
     DEV_SCALE_OVERFLOW,
     check,
+    dequantize,
+    dequantize_batched,
     gemm,
     gemm_batched,
     gemv,

@@ -21,7 +21,7 @@ DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_unpack",
-           "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_dequantize", "tq_dequantize_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -47,6 +47,10 @@ def lib() -> ctypes.CDLL:
         l.tq_quantize_pack.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
         l.tq_unpack.restype = i32
+        l.tq_dequantize.argtypes = [p, p, i64, i64, i32, p, p, p]
+        l.tq_dequantize.restype = i32
+        l.tq_dequantize_batched.argtypes = [i32, p, p, p, i64, i64, i32, p, p]
+        l.tq_dequantize_batched.restype = i32
         for f in (l.tq_gemv, l.tq_gemm):
             f.argtypes = [p, p, p, i64, i64, i64, i32, p, p, p]
             f.restype = i32
@@ -119,6 +123,41 @@ def unpack(packed: torch.Tensor, N: int, K: int, G: int, status=None, out=None):
     _rc(lib().tq_unpack(packed.data_ptr(), N, K, G, codes.data_ptr(), _st(status), _stream()),
         "tq_unpack")
     return codes
+
+
+def dequantize(packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int, status=None,
+               out=None):
+    """(packed, fp16 scales) -> w_hat bf16 [N,K] = bf16(c * s)."""
+    _dev(packed, "packed", (torch.uint8,), packed.dim())
+    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16), scales.dim())
+    if packed.numel() != packed_bytes(N, K, G):
+        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), packed_bytes(N, K, G)))
+    if G <= 0 or scales.numel() != N * (K // G):
+        raise TQError("scales has %d entries, expected %d" % (scales.numel(), N * (K // max(G, 1))))
+    w_hat = torch.empty((N, K), dtype=torch.bfloat16, device=packed.device) if out is None else out
+    _rc(lib().tq_dequantize(packed.data_ptr(), scales.data_ptr(), N, K, G, w_hat.data_ptr(),
+                            _st(status), _stream()), "tq_dequantize")
+    return w_hat
+
+
+def dequantize_batched(packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """Same-shaped (packed, scales) pairs -> list of bf16 [N,K], one launch per 64."""
+    n = len(packeds)
+    if len(scales_list) != n:
+        raise TQError("packeds and scales differ in length")
+    for pk, sc in zip(packeds, scales_list):
+        _dev(pk, "packed", (torch.uint8,), pk.dim())
+        _dev(sc, "scales", (torch.float16, torch.int16, torch.uint16), sc.dim())
+        if pk.numel() != packed_bytes(N, K, G) or G <= 0 or sc.numel() != N * (K // G):
+            raise TQError("a packed/scales pair does not match N=%d K=%d G=%d" % (N, K, G))
+    if outs is None:
+        outs = [torch.empty((N, K), dtype=torch.bfloat16, device=pk.device) for pk in packeds]
+    arr = ctypes.c_void_p * max(n, 1)
+    _rc(lib().tq_dequantize_batched(n, arr(*[t.data_ptr() for t in packeds]),
+                                    arr(*[t.data_ptr() for t in scales_list]),
+                                    arr(*[t.data_ptr() for t in outs]), N, K, G, _st(status),
+                                    _stream()), "tq_dequantize_batched")
+    return outs
 
 
 def _mm(fn, name, x, packed, scales, N, K, G, status, out):

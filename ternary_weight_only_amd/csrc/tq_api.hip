@@ -75,6 +75,36 @@ int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
   return finish_launch();
 }
 
+int tq_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, int64_t K, int G,
+                  uint16_t *w_hat, int32_t *d_status, void *stream) {
+  if (!packed || !scales || !w_hat) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(w_hat, 16) || !aligned(scales, 2) || !aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  tq::launch_dequantize(packed, scales, N, K, G, w_hat, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_dequantize_batched(int count, const uint8_t *const *packeds,
+                          const uint16_t *const *scales, uint16_t *const *w_hats, int64_t N,
+                          int64_t K, int G, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!packeds || !scales || !w_hats) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!packeds[i] || !scales[i] || !w_hats[i]) return TQ_ERR_NULL;
+    if (!aligned(scales[i], 2) || !aligned(w_hats[i], 16)) return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_dequantize_batched(count, packeds, scales, w_hats, N, K, G, d_status,
+                                (hipStream_t)stream);
+  return finish_launch();
+}
+
 int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
             int64_t N, int64_t K, int G, float *y, int32_t *d_status, void *stream) {
   if (!x || !packed || !scales || !y) return TQ_ERR_NULL;

@@ -22,6 +22,17 @@ void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
 void launch_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
                    int8_t *codes, int32_t *d_status, hipStream_t stream);
 
+// Decode to bf16 (tq_dequant.hip): w_hat[n,k] = bf16(c[n,k] * s[n,k/G]).
+void launch_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, int64_t K, int G,
+                       uint16_t *w_hat, int32_t *d_status, hipStream_t stream);
+
+// Problems per batched decode launch.
+constexpr int kDequantMaxBatch = 64;
+
+void launch_dequantize_batched(int count, const uint8_t *const *packeds,
+                               const uint16_t *const *scales, uint16_t *const *w_hats, int64_t N,
+                               int64_t K, int G, int32_t *d_status, hipStream_t stream);
+
 void launch_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
                  int64_t M, int64_t N, int64_t K, int G, float *y,
                  int32_t *d_status, hipStream_t stream);

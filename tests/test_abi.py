@@ -130,6 +130,38 @@ def test_quantize_unpack_argument_errors():
         assert lib.tq_status_string(rc)
 
 
+def test_dequantize_argument_errors():
+    d = _lib().tq_dequantize
+    assert d(None, FAKE, 4, 128, 64, FAKE, None, None) == -1
+    assert d(FAKE, None, 4, 128, 64, FAKE, None, None) == -1
+    assert d(FAKE, FAKE, 4, 128, 64, None, None, None) == -1
+    assert d(FAKE, FAKE, 0, 128, 64, FAKE, None, None) == -2
+    assert d(FAKE, FAKE, 4, 160, 64, FAKE, None, None) == -2
+    assert d(FAKE, FAKE, 4, 128, 32, FAKE, None, None) == -3
+    assert d(FAKE, FAKE, 4, 128, 64, FAKE + 8, None, None) == -4    # w_hat 16-byte
+    assert d(FAKE, FAKE + 1, 4, 128, 64, FAKE, None, None) == -4    # scales 2-byte
+    assert d(FAKE, FAKE, 4, 128, 64, FAKE, FAKE + 2, None) == -4    # status 4-byte
+
+
+def test_dequantize_batched_argument_errors():
+    import ctypes
+    d = _lib().tq_dequantize_batched
+    arr = ctypes.c_void_p * 2
+
+    def ps(*v):
+        return arr(*v)
+    good = ps(FAKE, FAKE + 64)
+    assert d(0, None, None, None, 4, 128, 64, None, None) == 0          # nothing to do
+    assert d(-1, good, good, good, 4, 128, 64, None, None) == -2
+    assert d(2, None, good, good, 4, 128, 64, None, None) == -1
+    assert d(2, good, ps(FAKE, None), good, 4, 128, 64, None, None) == -1
+    assert d(2, good, good, good, 4, 100, 64, None, None) == -2
+    assert d(2, good, good, good, 4, 128, 96, None, None) == -3
+    assert d(2, good, good, ps(FAKE, FAKE + 8), 4, 128, 64, None, None) == -4
+    assert d(2, good, ps(FAKE + 1, FAKE), good, 4, 128, 64, None, None) == -4
+    assert d(2, good, good, good, 4, 128, 64, FAKE + 1, None) == -4
+
+
 def test_product_path_does_not_import_oracle():
     pkg = os.path.join(ROOT, "ternary_weight_only_amd")
     for dirpath, _, files in os.walk(pkg):
