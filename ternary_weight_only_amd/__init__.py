@@ -14,6 +14,9 @@ package only marshals torch tensors to that ABI:
     y              = gemm(x_bf16, packed, scales, N, K, G)   # any M
     ys             = gemm_batched(xs, packeds, scales, N, K, G)  # many same-shaped
 
+`ternary_weight_only_amd.package` writes and reads the per-tensor package
+(codes + fp16 scales + sha256 hashes) and decodes it to bf16 on the device.
+
 torch supplies device memory and the current stream; no arithmetic of the
 method runs in Python or torch.  The library is loaded on first use and a
 missing build raises immediately; there is no CPU fallback.
