@@ -65,6 +65,8 @@ def _load():
         lib.oracle_matmul.restype = ctypes.c_int
         lib.oracle_dequantize.argtypes = [p, p, i64, i64, i64, p, p]
         lib.oracle_dequantize.restype = ctypes.c_int
+        lib.oracle_fake_quantize.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.oracle_fake_quantize.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -133,6 +135,26 @@ def dequantize(packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):
     if rc:
         raise OracleError("oracle_dequantize rc=%d" % rc)
     return out, int(st[0])
+
+
+def fake_quantize(w_bits: np.ndarray, G: int):
+    """QAT forward: w_hat = bf16_RNE(c * s) from bf16 weights.
+
+    Returns (w_hat uint16 [N,K] bf16 bits, scales uint16 [N,K/G] fp16 bits,
+    status bits int)."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    if w.ndim != 2:
+        raise OracleError("w must be 2-D")
+    N, K = w.shape
+    if G < 1 or K % G:
+        raise OracleError("K % G != 0")
+    out = np.empty((N, K), np.uint16)
+    sc = np.empty((N, K // G), np.uint16)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_fake_quantize(_ptr(w), N, K, G, _ptr(out), _ptr(sc), _ptr(st))
+    if rc:
+        raise OracleError("oracle_fake_quantize rc=%d" % rc)
+    return out, sc, int(st[0])
 
 
 def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):

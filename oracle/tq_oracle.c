@@ -273,6 +273,35 @@ static double f16_to_double(uint16_t h)
 /* ------------------------------------------------------------------------ */
 
 /*
+ * Scale and codes of one group of G weights: sets *sbits and code[0, npad)
+ * (code[j] = 0 for j >= G), returns the group's status bits.  A group with
+ * an Inf/NaN weight gets scale 0x7E00, one whose mean overflows fp16 gets
+ * 0x7C00; both keep every code at 0.
+ */
+static int group_scale_and_codes(const uint16_t *wg, int64_t G, int64_t npad, uint16_t *sbits,
+                                 int8_t *code)
+{
+    int gst = 0;
+    *sbits = 0;
+    for (int64_t j = 0; j < G; ++j)
+        if (((wg[j] >> 7) & 0xFF) == 0xFF) gst |= OR_NONFINITE;
+    if (gst) *sbits = 0x7E00;
+    else gst |= group_scale_bits(wg, G, sbits);
+
+    /* Codes.  |w| == s/2 is a tie and goes to 0 (round half to even of
+     * +-0.5); beyond 1.5 s the code saturates at +-1. */
+    for (int64_t t = 0; t < npad; ++t) code[t] = 0;  /* padding = 0 */
+    if (!gst) {
+        double half = 0.5 * f16_to_double(*sbits);
+        for (int64_t j = 0; j < G; ++j) {
+            double v = bf16_to_double(wg[j]);
+            code[j] = (int8_t)(v > half ? 1 : (v < -half ? -1 : 0));
+        }
+    }
+    return gst;
+}
+
+/*
  * w[N,K] bf16 bits, row-major; groups of G along K.
  * packed[N][K/G][ceil(G/5)] bytes, scales[N][K/G] fp16 bits.
  * *status receives the OR of all group status bits (may be NULL).
@@ -291,24 +320,8 @@ int oracle_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int64_t G,
         for (int64_t g = 0; g < nG; ++g) {
             const uint16_t *wg = w + n * K + g * G;
             uint8_t *pg = packed + (n * nG + g) * B;
-            int gst = 0;
-            uint16_t sbits = 0;
-
-            for (int64_t j = 0; j < G; ++j)
-                if (((wg[j] >> 7) & 0xFF) == 0xFF) gst |= OR_NONFINITE;
-            if (gst) sbits = 0x7E00;
-            else gst |= group_scale_bits(wg, G, &sbits);
-
-            /* Codes.  |w| == s/2 is a tie and goes to 0 (round half to
-             * even of +-0.5); beyond 1.5 s the code saturates at +-1. */
-            for (int64_t t = 0; t < 5 * B; ++t) code[t] = 0;  /* padding = 0 */
-            if (!gst) {
-                double half = 0.5 * f16_to_double(sbits);
-                for (int64_t j = 0; j < G; ++j) {
-                    double v = bf16_to_double(wg[j]);
-                    code[j] = (int8_t)(v > half ? 1 : (v < -half ? -1 : 0));
-                }
-            }
+            uint16_t sbits;
+            int gst = group_scale_and_codes(wg, G, 5 * B, &sbits, code);
 
             /* Five base-3 digits per byte, first weight lowest digit. */
             for (int64_t b = 0; b < B; ++b) {
@@ -421,6 +434,47 @@ int oracle_dequantize(const uint8_t *packed, const uint16_t *scales, int64_t N, 
         }
     }
     free(codes);
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+/* ------------------------------------------------------------------------ */
+/* fake quantization (QAT forward)                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * w_hat[n,k] = bf16_RNE(c[n,k] * s[n,k/G]) straight from bf16 weights, with
+ * s and c the group scale and codes above.  Avenue README, introduction and
+ * closing remarks: BitNet-style quantization-aware training keeps latent
+ * weights.  Reading taken here: the forward pass uses w_hat, and the
+ * backward pass is straight-through (the gradient of w_hat is the gradient
+ * of w), so the backward needs no arithmetic.  A
+ * flagged group (non-finite weight, scale overflow) gives w_hat = +0 and
+ * its status bits; scales[N][K/G] receives the scales as quantize_pack
+ * would store them (may be NULL).
+ */
+int oracle_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t G, uint16_t *w_hat,
+                         uint16_t *scales, int32_t *status)
+{
+    if (!w || !w_hat) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G;
+    int32_t st = 0;
+    int8_t *code = (int8_t *)malloc((size_t)G);
+    if (!code) return OR_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < nG; ++g) {
+            uint16_t sbits;
+            int gst = group_scale_and_codes(w + n * K + g * G, G, G, &sbits, code);
+            double s = gst ? 0.0 : f16_to_double(sbits);
+            for (int64_t j = 0; j < G; ++j)
+                w_hat[n * K + g * G + j] = gst ? 0 : double_to_bf16_rne((double)code[j] * s);
+            if (scales) scales[n * nG + g] = sbits;
+            st |= gst;
+        }
+    }
+    free(code);
     if (status) *status |= st;
     return OR_OK;
 }
