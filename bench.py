@@ -29,6 +29,11 @@ chain writes 4.2 GB, so the 256 MB memory-side cache holds at most 6% of the
 writes back.  The row counts packed + scale bytes read and bf16 bytes
 written.
 
+Also outside the step, the QAT forward (tq_fake_quantize: bf16 weights to
+their bf16 ternarized values, 72 direct launches a pass) runs eight passes
+back to back between two HIP events (median of three chains); its row counts
+2 bytes read and 2 written per weight.
+
 The roofline entry times the GEMV kernel itself: after the timed steps, the
 decode pass runs over all eight slots back to back (8 launches, so each
 launch's dispatch overlaps the previous kernel) between two HIP events, and
@@ -311,6 +316,27 @@ def main():
     torch.cuda.synchronize()
     assert int(status.item()) == 0, "device status %d" % int(status.item())
     dq_ms = sorted(a.elapsed_time(b) for a, b in dq[1:])[1] / RING
+
+    # QAT forward (fake quantization), outside the step: every bf16 matrix to
+    # its bf16 w_hat (72 direct launches a pass), eight passes per chain
+    def run_fake(stream):
+        for i, (N, K) in enumerate(shapes):
+            rc = L.tq_fake_quantize(w_dev[i].data_ptr(), N, K, G, w_hat[i].data_ptr(), None,
+                                    stp, stream)
+            assert rc == 0, rc
+
+    fq = []
+    with torch.cuda.stream(stream):
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for _ in range(RING):
+                run_fake(sp)
+            e1.record(stream)
+            fq.append((e0, e1))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status %d" % int(status.item())
+    fq_ms = sorted(a.elapsed_time(b) for a, b in fq[1:])[1] / RING
     del w_hat
 
     if args.calibrate_copy:
@@ -350,6 +376,10 @@ def main():
         "decode_bf16": {"ms": dq_ms, "GB/s": dequant_bytes / (dq_ms * 1e-3) / 1e9,
                         "frac_hbm": dequant_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "bytes_per_pass": dequant_bytes, "launches": len(groups),
+                        "in_step": False},
+        "qat_forward": {"ms": fq_ms, "GB/s": 4 * weights / (fq_ms * 1e-3) / 1e9,
+                        "frac_hbm": 4 * weights / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                        "bytes_per_pass": 4 * weights, "launches": len(shapes),
                         "in_step": False},
         "unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
                       "bytes_per_step": unpack_bytes},

@@ -95,6 +95,28 @@ int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
                      int32_t *d_status, void *stream);
 
 /*
+ * QAT forward ("fake quantization"): the ternarized weights in bf16,
+ *   w_hat[n,k] = bf16_rne(c[n,k] * s[n, k/G])
+ * with s and c exactly as tq_quantize_pack computes them, in one pass that
+ * reads w and writes w_hat (no packed bytes).  Equal, bit for bit, to
+ * tq_quantize_pack followed by tq_dequantize on unflagged groups.
+ * Source: Avenue README (introduction and closing remarks: BitNet-style
+ * quantization-aware training keeps latent weights and ternarizes them in
+ * the forward pass; a kernel could remove the training overhead), with the
+ * scale and code rule of the precisit "pack-unpack-run" README.  The
+ * backward pass is straight-through (the gradient of w_hat is passed to w
+ * unchanged) and needs no kernel.
+ *   w        [N,K] bf16, 16-byte aligned
+ *   w_hat    [N,K] bf16 bit patterns, 16-byte aligned, overwritten
+ *   scales   [N, K/G] fp16, 2-byte aligned, or NULL (not written)
+ * A group with an Inf/NaN weight (TQ_DEV_NONFINITE) or a mean that rounds
+ * to >= 65520 (TQ_DEV_SCALE_OVERFLOW) gets w_hat = +0, and its scale as
+ * tq_quantize_pack stores it.  Bit-exact and deterministic.
+ */
+int tq_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,
+                     uint16_t *scales, int32_t *d_status, void *stream);
+
+/*
  * Decode packed bytes to codes and validate them.
  * Source: precisit "pack-unpack-run" README, codec.py description
  * (decoding; values 243..255 invalid; zero-trit padding).

@@ -5,6 +5,8 @@ The work happens in libtq.so (hand-written HIP; C ABI in include/tq.h).  This
 package only marshals torch tensors to that ABI:
 
     packed, scales = quantize_pack(w_bf16, G)      # scale, codes, base-3 bytes
+    w_hat          = fake_quantize(w_bf16, G)      # QAT forward, bf16 c * s
+    w_hat          = FakeQuantize.apply(w, G)      # same, straight-through gradient
     codes          = unpack(packed, N, K, G)       # codes + validation
     w_hat          = dequantize(packed, scales, N, K, G)  # bf16 c * s
     w_hats         = dequantize_batched(packeds, scales, N, K, G)  # many same-shaped
@@ -22,6 +24,7 @@ method runs in Python or torch.  The library is loaded on first use and a
 missing build raises immediately; there is no CPU fallback.
 """
 from .binding import (  # noqa: F401
+    FakeQuantize,
     TQError,
     DEV_BAD_PADDING,
     DEV_INVALID_BYTE,
@@ -30,6 +33,7 @@ from .binding import (  # noqa: F401
     check,
     dequantize,
     dequantize_batched,
+    fake_quantize,
     gemm,
     gemm_batched,
     gemv,

@@ -20,7 +20,8 @@ DEV_INVALID_BYTE = 4
 DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
-SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_unpack",
+SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_fake_quantize",
+           "tq_unpack",
            "tq_dequantize", "tq_dequantize_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
@@ -45,6 +46,8 @@ def lib() -> ctypes.CDLL:
         l.tq_packed_bytes.restype = i64
         l.tq_quantize_pack.argtypes = [p, i64, i64, i32, p, p, p, p]
         l.tq_quantize_pack.restype = i32
+        l.tq_fake_quantize.argtypes = [p, i64, i64, i32, p, p, p, p]
+        l.tq_fake_quantize.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
         l.tq_unpack.restype = i32
         l.tq_dequantize.argtypes = [p, p, i64, i64, i32, p, p, p]
@@ -112,6 +115,40 @@ def quantize_pack(w: torch.Tensor, G: int, status=None, out=None):
     _rc(lib().tq_quantize_pack(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
                                _st(status), _stream()), "tq_quantize_pack")
     return packed, scales
+
+
+def fake_quantize(w: torch.Tensor, G: int, status=None, out=None, scales_out=None):
+    """QAT forward: w [N,K] bf16 -> w_hat bf16 [N,K] = bf16(c * s).
+
+    scales_out, if given, is an fp16 [N, K/G] tensor that receives the
+    scales.  Use FakeQuantize.apply for the straight-through gradient."""
+    _dev(w, "w", (torch.bfloat16, torch.int16), 2)
+    N, K = w.shape
+    w_hat = torch.empty((N, K), dtype=torch.bfloat16, device=w.device) if out is None else out
+    sp = 0
+    if scales_out is not None:
+        _dev(scales_out, "scales_out", (torch.float16, torch.int16), scales_out.dim())
+        if G <= 0 or scales_out.numel() != N * (K // G):
+            raise TQError("scales_out has %d entries, expected %d" % (scales_out.numel(),
+                                                                    N * (K // max(G, 1))))
+        sp = scales_out.data_ptr()
+    _rc(lib().tq_fake_quantize(w.data_ptr(), N, K, G, w_hat.data_ptr(), sp, _st(status),
+                               _stream()), "tq_fake_quantize")
+    return w_hat
+
+
+class FakeQuantize(torch.autograd.Function):
+    """w_hat = fake_quantize(w, G) in the forward pass; the backward pass is
+    straight-through: the gradient of w_hat is returned as the gradient of w
+    unchanged (no kernel runs)."""
+
+    @staticmethod
+    def forward(ctx, w, G):
+        return fake_quantize(w, G)
+
+    @staticmethod
+    def backward(ctx, grad):
+        return grad, None
 
 
 def unpack(packed: torch.Tensor, N: int, K: int, G: int, status=None, out=None):

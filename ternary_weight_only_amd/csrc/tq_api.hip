@@ -64,6 +64,18 @@ int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *pa
   return finish_launch();
 }
 
+int tq_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,
+                     uint16_t *scales, int32_t *d_status, void *stream) {
+  if (!w || !w_hat) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(w, 16) || !aligned(w_hat, 16) || !aligned(scales, 2) || !aligned(d_status, 4))
+    return TQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  tq::launch_fake_quantize(w, N, K, G, w_hat, scales, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
 int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
               int32_t *d_status, void *stream) {
   if (!packed || !codes) return TQ_ERR_NULL;

@@ -19,6 +19,11 @@ void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
                           uint8_t *packed, uint16_t *scales, int32_t *d_status,
                           hipStream_t stream);
 
+// QAT forward (tq_quant.hip): w_hat = bf16(c * s) straight from w; scales
+// written only if not null.
+void launch_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,
+                          uint16_t *scales, int32_t *d_status, hipStream_t stream);
+
 void launch_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
                    int8_t *codes, int32_t *d_status, hipStream_t stream);
 

@@ -111,6 +111,13 @@ __device__ __noinline__ uint32_t f16_scale_exact(const uint16_t *grp, int G, int
   return bits;
 }
 
+// bf16 bits of the fp16 value h (finite, non-negative here): fp16 -> fp32 is
+// exact, then one round to nearest, ties to even, to 8 significant bits.
+__device__ __forceinline__ uint32_t bf16_of_f16(uint32_t h) {
+  const uint32_t u = __float_as_uint(__half2float(__ushort_as_half((unsigned short)h)));
+  return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
+}
+
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
   return (uint32_t)__shfl_xor((int)v, mask, kWave);
 }
@@ -128,11 +135,15 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 // Each lane loads 8 bf16 with one 128-bit load; G/8 lanes share a group and
 // combine their exponent maxima, fixed-point sums and flags with xor
 // shuffles.  Digits go through LDS to be regrouped five per byte.
+//
+// FAKE: the QAT forward instead.  Each lane writes its own 8 weights'
+// w_hat = bf16(c * s) where it read them (no LDS, no barrier), and the
+// scales are written only if `scales` is not null.
 // ---------------------------------------------------------------------------
-template <int G>
+template <int G, bool FAKE>
 __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
     const uint16_t *__restrict__ w, int64_t total_groups, uint8_t *__restrict__ packed,
-    uint16_t *__restrict__ scales, int32_t *__restrict__ d_status) {
+    uint16_t *__restrict__ scales, uint16_t *__restrict__ w_hat, int32_t *__restrict__ d_status) {
   constexpr int LPG = G / 8;               // lanes per group
   constexpr int GPC = 512 / G;             // groups per chunk
   constexpr int B = bytes_per_group(G);    // bytes per group
@@ -245,6 +256,30 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
       dig |= (uint64_t)d << (8 * i);
     }
 
+    if constexpr (FAKE) {
+      // w_hat of the 8 weights: a pair takes bytes 2d, 2d+1 of {hi, lo}
+      // per digit d (0..1 is -s, 2..3 +0, 4..5 +s); a flagged group is +0
+      const uint32_t sb = flags ? 0u : bf16_of_f16(sbits);
+      const uint32_t lo = flags ? 0u : (sb ^ 0x8000u);  // s >= 0: -s | +0
+      const uint32_t hi = sb | (sb << 16);
+      uint32_t out[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t pair = (uint32_t)((dig >> (16 * k)) & 0xFFu) |
+                              ((uint32_t)((dig >> (16 * k + 8)) & 0xFFu) << 16);
+        out[k] = __builtin_amdgcn_perm(hi, lo, pair * 0x0202u + 0x01000100u);
+      }
+      if (active) {
+        *reinterpret_cast<uint4 *>(w_hat + gi * G + sub * 8) =
+            make_uint4(out[0], out[1], out[2], out[3]);
+        if (sub == 0) {
+          if (scales) scales[gi] = (uint16_t)sbits;
+          if (flags && d_status) atomicOr(d_status, flags);
+        }
+      }
+      continue;
+    }
+
     __syncthreads();  // previous iteration's readers are done with digits_s
     *reinterpret_cast<uint64_t *>(&digits_s[wv][lane * 8]) = dig;
     __syncthreads();
@@ -330,11 +365,24 @@ void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_
   const int64_t nchunks = (total_groups * G + 511) / 512;
   const int grid = grid_for(nchunks, kWavesPerBlock, 8192);
   if (G == 64)
-    hipLaunchKernelGGL(quantize_pack_kernel<64>, dim3(grid), dim3(kBlock), 0, stream, w,
-                       total_groups, packed, scales, d_status);
+    hipLaunchKernelGGL((quantize_pack_kernel<64, false>), dim3(grid), dim3(kBlock), 0, stream, w,
+                       total_groups, packed, scales, nullptr, d_status);
   else
-    hipLaunchKernelGGL(quantize_pack_kernel<128>, dim3(grid), dim3(kBlock), 0, stream, w,
-                       total_groups, packed, scales, d_status);
+    hipLaunchKernelGGL((quantize_pack_kernel<128, false>), dim3(grid), dim3(kBlock), 0, stream,
+                       w, total_groups, packed, scales, nullptr, d_status);
+}
+
+void launch_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,
+                          uint16_t *scales, int32_t *d_status, hipStream_t stream) {
+  const int64_t total_groups = N * (K / G);
+  const int64_t nchunks = (total_groups * G + 511) / 512;
+  const int grid = grid_for(nchunks, kWavesPerBlock, 8192);
+  if (G == 64)
+    hipLaunchKernelGGL((quantize_pack_kernel<64, true>), dim3(grid), dim3(kBlock), 0, stream, w,
+                       total_groups, nullptr, scales, w_hat, d_status);
+  else
+    hipLaunchKernelGGL((quantize_pack_kernel<128, true>), dim3(grid), dim3(kBlock), 0, stream,
+                       w, total_groups, nullptr, scales, w_hat, d_status);
 }
 
 void launch_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,

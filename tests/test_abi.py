@@ -130,6 +130,18 @@ def test_quantize_unpack_argument_errors():
         assert lib.tq_status_string(rc)
 
 
+def test_fake_quantize_argument_errors():
+    f = _lib().tq_fake_quantize
+    assert f(None, 4, 128, 64, FAKE, None, None, None) == -1
+    assert f(FAKE, 4, 128, 64, None, None, None, None) == -1
+    assert f(FAKE, 4, 130, 64, FAKE, None, None, None) == -2
+    assert f(FAKE, 4, 128, 48, FAKE, None, None, None) == -3
+    assert f(FAKE + 2, 4, 128, 64, FAKE, None, None, None) == -4
+    assert f(FAKE, 4, 128, 64, FAKE + 8, None, None, None) == -4
+    assert f(FAKE, 4, 128, 64, FAKE, FAKE + 1, None, None) == -4
+    assert f(FAKE, 4, 128, 64, FAKE, None, FAKE + 2, None) == -4
+
+
 def test_dequantize_argument_errors():
     d = _lib().tq_dequantize
     assert d(None, FAKE, 4, 128, 64, FAKE, None, None) == -1
