@@ -10,15 +10,14 @@ hot path over that stack, in this order:
       one launch for the 48 K=1024 and the 24 K=3584 matrices together)
   prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
       two launches, one per shape; each matrix has its own activations and output)
-  quantize + pack all 72 bf16 matrices                 (tq_quantize_pack)
-  unpack + validate all 72 packed matrices             (tq_unpack)
+  quantize + pack all 72 bf16 matrices                 (tq_quantize_pack_batched:
+      two launches, one per shape)
+  unpack + validate all 72 packed matrices             (tq_unpack_batched: two)
 The packed weights live in a ring of eight slots (480 MB, more than the
 256 MB memory-side cache); step t reads slot t%8 and packs into slot
 (t+2)%8, so the weights a GEMV reads were written six steps (several GB of
 traffic) earlier and come from HBM, not from the caches.
-The GEMV and GEMM rows are direct launches (one grouped call, and two batched
-calls); the 72 launches of each of the other two rows are captured in a HIP
-graph.  HIP
+Every row is direct launches (pointer arrays built once per ring slot).  HIP
 events between the rows time each row on the stream the kernels run on, so
 a row's time includes its launches' dispatch.
 
@@ -29,8 +28,8 @@ chain writes 4.2 GB, so the 256 MB memory-side cache holds at most 6% of the
 writes back.  The row counts packed + scale bytes read and bf16 bytes
 written.
 
-Also outside the step, the QAT forward (tq_fake_quantize: bf16 weights to
-their bf16 ternarized values, 72 direct launches a pass) runs eight passes
+Also outside the step, the QAT forward (tq_fake_quantize_batched: bf16
+weights to their bf16 ternarized values, two launches a pass) runs eight passes
 back to back between two HIP events (median of three chains); its row counts
 2 bytes read and 2 written per weight.
 
@@ -168,16 +167,6 @@ def main():
     status = tq.new_status(dev)
     stp = status.data_ptr()
 
-    def run_quant(slot, stream):
-        for i, (N, K) in enumerate(shapes):
-            rc = L.tq_quantize_pack(w_dev[i].data_ptr(), N, K, G, P[slot][i].data_ptr(),
-                                    S[slot][i].data_ptr(), stp, stream)
-            assert rc == 0, rc
-
-    def run_unpack(slot, stream):
-        for i, (N, K) in enumerate(shapes):
-            rc = L.tq_unpack(P[slot][i].data_ptr(), N, K, G, codes[i].data_ptr(), stp, stream)
-            assert rc == 0, rc
 
     # the decode pass: one grouped call over all 72 matrices (one launch);
     # the prefill pass: two batched calls (gate+up of all layers share
@@ -199,6 +188,21 @@ def main():
                 len(idx), ptrs([x_dec[i] for i in idx]), ptrs([P[slot][i] for i in idx]),
                 ptrs([S[slot][i] for i in idx]), ptrs([y_dec[i] for i in idx]),
                 ptrs([x_pre[key[1]] for i in idx]), ptrs([y_pre[i] for i in idx]))
+
+    # quantize/pack and unpack: one batched call per shape (48 and 24 matrices)
+    qcalls = {slot: [(N, K, len(idx), ptrs([w_dev[i] for i in idx]), ptrs([P[slot][i] for i in idx]),
+                      ptrs([S[slot][i] for i in idx]), ptrs([codes[i] for i in idx]))
+                     for (N, K), idx in groups.items()] for slot in range(RING)}
+
+    def run_quant(slot, stream):
+        for N, K, n, aw, ap, asc, _ in qcalls[slot]:
+            rc = L.tq_quantize_pack_batched(n, aw, N, K, G, ap, asc, stp, stream)
+            assert rc == 0, rc
+
+    def run_unpack(slot, stream):
+        for N, K, n, _, ap, _, ac in qcalls[slot]:
+            rc = L.tq_unpack_batched(n, ap, N, K, G, ac, stp, stream)
+            assert rc == 0, rc
 
     i64s = ctypes.c_int64 * len(shapes)
     g_ns = i64s(*[N for N, K in shapes])
@@ -233,18 +237,10 @@ def main():
         p = P[0][i].view(N, -1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
         assert np.array_equal(p, p_ref), "bench inputs: packed bytes differ from the oracle"
 
-    # one graph per (row, slot) for the rows of many launches; all rows run on
-    # one side stream
+    # all rows run on one side stream, every launch a direct one
     stream = torch.cuda.Stream()
     sp = stream.cuda_stream
-    graphs = {}
-    for name, fn in (("quant", run_quant), ("unpack", run_unpack)):
-        for slot in range(RING):
-            g = torch.cuda.CUDAGraph()
-            with torch.cuda.graph(g, stream=stream):
-                fn(slot, torch.cuda.current_stream().cuda_stream)
-            graphs[(name, slot)] = g
-    torch.cuda.synchronize()
+    run = {"gemv": run_gemv, "gemm": run_gemm, "quant": run_quant, "unpack": run_unpack}
 
     order = ("gemv", "gemm", "quant", "unpack")
 
@@ -255,12 +251,7 @@ def main():
             if evs is not None:
                 evs[0].record(stream)
             for j, name in enumerate(order):
-                if name == "gemv":
-                    run_gemv(slots[name], sp)
-                elif name == "gemm":
-                    run_gemm(slots[name], sp)
-                else:
-                    graphs[(name, slots[name])].replay()
+                run[name](slots[name], sp)
                 if evs is not None:
                     evs[j + 1].record(stream)
 
@@ -319,10 +310,12 @@ def main():
 
     # QAT forward (fake quantization), outside the step: every bf16 matrix to
     # its bf16 w_hat (72 direct launches a pass), eight passes per chain
+    fq_calls = [(N, K, len(idx), ptrs([w_dev[i] for i in idx]), ptrs([w_hat[i] for i in idx]))
+                for (N, K), idx in groups.items()]
+
     def run_fake(stream):
-        for i, (N, K) in enumerate(shapes):
-            rc = L.tq_fake_quantize(w_dev[i].data_ptr(), N, K, G, w_hat[i].data_ptr(), None,
-                                    stp, stream)
+        for N, K, n, aw, awh in fq_calls:
+            rc = L.tq_fake_quantize_batched(n, aw, N, K, G, awh, None, stp, stream)
             assert rc == 0, rc
 
     fq = []
@@ -379,7 +372,7 @@ def main():
                         "in_step": False},
         "qat_forward": {"ms": fq_ms, "GB/s": 4 * weights / (fq_ms * 1e-3) / 1e9,
                         "frac_hbm": 4 * weights / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "bytes_per_pass": 4 * weights, "launches": len(shapes),
+                        "bytes_per_pass": 4 * weights, "launches": len(groups),
                         "in_step": False},
         "unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
                       "bytes_per_step": unpack_bytes},

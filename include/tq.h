@@ -95,6 +95,23 @@ int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
                      int32_t *d_status, void *stream);
 
 /*
+ * Batched quantize + pack: `count` matrices of the same shape, each exactly
+ * as tq_quantize_pack(ws[i], N, K, G, packeds[i], scales[i]), in one launch
+ * per 64 matrices -- e.g. every weight of one shape in a checkpoint, which
+ * one launch per matrix would leave to launch latency.
+ *   ws, packeds, scales   HOST arrays of `count` DEVICE pointers, with the
+ *                         layouts and alignments of tq_quantize_pack; read
+ *                         during the call only
+ *   count >= 0            (0 enqueues nothing)
+ * Outputs must not overlap each other or any input.  Device status as
+ * tq_quantize_pack; a NULL or misaligned pointer in any entry rejects the
+ * whole call with nothing enqueued.
+ */
+int tq_quantize_pack_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                             uint8_t *const *packeds, uint16_t *const *scales,
+                             int32_t *d_status, void *stream);
+
+/*
  * QAT forward ("fake quantization"): the ternarized weights in bf16,
  *   w_hat[n,k] = bf16_rne(c[n,k] * s[n, k/G])
  * with s and c exactly as tq_quantize_pack computes them, in one pass that
@@ -117,6 +134,21 @@ int tq_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w
                      uint16_t *scales, int32_t *d_status, void *stream);
 
 /*
+ * Batched QAT forward: `count` matrices of the same shape, each exactly as
+ * tq_fake_quantize(ws[i], N, K, G, w_hats[i], scales ? scales[i] : NULL),
+ * in one launch per 64 matrices -- e.g. every projection of one shape in a
+ * model, once per training step.
+ *   ws, w_hats   HOST arrays of `count` DEVICE pointers (16-byte aligned)
+ *   scales       NULL, or a HOST array of `count` DEVICE pointers (each
+ *                2-byte aligned, or NULL to skip that matrix's scales)
+ * Errors and device status as tq_fake_quantize; a NULL or misaligned
+ * pointer in any entry rejects the whole call with nothing enqueued.
+ */
+int tq_fake_quantize_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                             uint16_t *const *w_hats, uint16_t *const *scales,
+                             int32_t *d_status, void *stream);
+
+/*
  * Decode packed bytes to codes and validate them.
  * Source: precisit "pack-unpack-run" README, codec.py description
  * (decoding; values 243..255 invalid; zero-trit padding).
@@ -127,6 +159,17 @@ int tq_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w
  */
 int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G,
               int8_t *codes, int32_t *d_status, void *stream);
+
+/*
+ * Batched unpack: `count` same-shaped matrices, each exactly as
+ * tq_unpack(packeds[i], N, K, G, codes[i]), one launch per 64.
+ *   packeds, codes   HOST arrays of `count` DEVICE pointers (codes 8-byte
+ *                    aligned); read during the call only
+ * Errors and device status as tq_unpack; a NULL or misaligned pointer in any
+ * entry rejects the whole call with nothing enqueued.
+ */
+int tq_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
+                      int8_t *const *codes, int32_t *d_status, void *stream);
 
 /*
  * Decode packed codes and group scales to a bf16 weight matrix:

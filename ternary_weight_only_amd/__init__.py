@@ -8,6 +8,7 @@ package only marshals torch tensors to that ABI:
     w_hat          = fake_quantize(w_bf16, G)      # QAT forward, bf16 c * s
     w_hat          = FakeQuantize.apply(w, G)      # same, straight-through gradient
     codes          = unpack(packed, N, K, G)       # codes + validation
+    (the *_batched forms take lists of same-shaped matrices, one launch per 64)
     w_hat          = dequantize(packed, scales, N, K, G)  # bf16 c * s
     w_hats         = dequantize_batched(packeds, scales, N, K, G)  # many same-shaped
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
@@ -34,6 +35,7 @@ from .binding import (  # noqa: F401
     dequantize,
     dequantize_batched,
     fake_quantize,
+    fake_quantize_batched,
     gemm,
     gemm_batched,
     gemv,
@@ -43,5 +45,7 @@ from .binding import (  # noqa: F401
     new_status,
     packed_bytes,
     quantize_pack,
+    quantize_pack_batched,
     unpack,
+    unpack_batched,
 )

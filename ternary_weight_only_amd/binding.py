@@ -20,8 +20,8 @@ DEV_INVALID_BYTE = 4
 DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
-SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_fake_quantize",
-           "tq_unpack",
+SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
+           "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
            "tq_dequantize", "tq_dequantize_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
@@ -48,6 +48,11 @@ def lib() -> ctypes.CDLL:
         l.tq_quantize_pack.restype = i32
         l.tq_fake_quantize.argtypes = [p, i64, i64, i32, p, p, p, p]
         l.tq_fake_quantize.restype = i32
+        for f in (l.tq_quantize_pack_batched, l.tq_fake_quantize_batched):
+            f.argtypes = [i32, p, i64, i64, i32, p, p, p, p]
+            f.restype = i32
+        l.tq_unpack_batched.argtypes = [i32, p, i64, i64, i32, p, p, p]
+        l.tq_unpack_batched.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
         l.tq_unpack.restype = i32
         l.tq_dequantize.argtypes = [p, p, i64, i64, i32, p, p, p]
@@ -135,6 +140,63 @@ def fake_quantize(w: torch.Tensor, G: int, status=None, out=None, scales_out=Non
     _rc(lib().tq_fake_quantize(w.data_ptr(), N, K, G, w_hat.data_ptr(), sp, _st(status),
                                _stream()), "tq_fake_quantize")
     return w_hat
+
+
+def _ptrs(ts):
+    return (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+
+
+def _same_shape(ws, name):
+    for w in ws:
+        _dev(w, name, (torch.bfloat16, torch.int16), 2)
+    shapes = {tuple(w.shape) for w in ws}
+    if len(shapes) > 1:
+        raise TQError("%s: matrices of different shapes %s" % (name, sorted(shapes)))
+    return shapes.pop() if shapes else (0, 0)
+
+
+def quantize_pack_batched(ws, G: int, status=None):
+    """Same-shaped bf16 matrices -> list of (packed, scales), one launch per 64."""
+    N, K = _same_shape(ws, "w")
+    if not ws:
+        return []
+    rb = (K // G) * ((G + 4) // 5) if G > 0 and K % G == 0 else 0
+    dev = ws[0].device
+    pk = [torch.empty((N, max(rb, 1)), dtype=torch.uint8, device=dev) for _ in ws]
+    sc = [torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=dev) for _ in ws]
+    _rc(lib().tq_quantize_pack_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(pk), _ptrs(sc),
+                                       _st(status), _stream()), "tq_quantize_pack_batched")
+    return list(zip(pk, sc))
+
+
+def fake_quantize_batched(ws, G: int, status=None, with_scales: bool = False):
+    """Same-shaped bf16 matrices -> list of bf16 w_hat (and, with_scales, of
+    (w_hat, scales)), one launch per 64."""
+    N, K = _same_shape(ws, "w")
+    if not ws:
+        return []
+    dev = ws[0].device
+    wh = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in ws]
+    sc = [torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=dev)
+          for _ in ws] if with_scales else None
+    _rc(lib().tq_fake_quantize_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(wh),
+                                       _ptrs(sc) if with_scales else None, _st(status),
+                                       _stream()), "tq_fake_quantize_batched")
+    return list(zip(wh, sc)) if with_scales else wh
+
+
+def unpack_batched(packeds, N: int, K: int, G: int, status=None):
+    """Same-shaped packed matrices -> list of int8 codes [N,K], one launch per 64."""
+    for p in packeds:
+        _dev(p, "packed", (torch.uint8,), p.dim())
+        if p.numel() != packed_bytes(N, K, G):
+            raise TQError("packed has %d bytes, expected %d" % (p.numel(), packed_bytes(N, K, G)))
+    if not packeds:
+        return []
+    codes = [torch.empty((N, K), dtype=torch.int8, device=p.device) for p in packeds]
+    _rc(lib().tq_unpack_batched(len(packeds), _ptrs(packeds), N, K, G, _ptrs(codes), _st(status),
+                                _stream()), "tq_unpack_batched")
+    return codes
 
 
 class FakeQuantize(torch.autograd.Function):

@@ -76,6 +76,62 @@ int tq_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w
   return finish_launch();
 }
 
+int tq_quantize_pack_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                             uint8_t *const *packeds, uint16_t *const *scales,
+                             int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!ws || !packeds || !scales) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!ws[i] || !packeds[i] || !scales[i]) return TQ_ERR_NULL;
+    if (!aligned(ws[i], 16) || !aligned(scales[i], 2)) return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_quant_batched(count, ws, N, K, G, packeds, scales, nullptr, d_status,
+                           (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_fake_quantize_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                             uint16_t *const *w_hats, uint16_t *const *scales,
+                             int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!ws || !w_hats) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!ws[i] || !w_hats[i]) return TQ_ERR_NULL;
+    if (!aligned(ws[i], 16) || !aligned(w_hats[i], 16)) return TQ_ERR_ALIGN;
+    if (scales && !aligned(scales[i], 2)) return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_quant_batched(count, ws, N, K, G, nullptr, scales, w_hats, d_status,
+                           (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
+                      int8_t *const *codes, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!packeds || !codes) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!packeds[i] || !codes[i]) return TQ_ERR_NULL;
+    if (!aligned(codes[i], 8)) return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_unpack_batched(count, packeds, N, K, G, codes, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
 int tq_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
               int32_t *d_status, void *stream) {
   if (!packed || !codes) return TQ_ERR_NULL;

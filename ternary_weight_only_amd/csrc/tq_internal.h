@@ -19,6 +19,19 @@ void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G,
                           uint8_t *packed, uint16_t *scales, int32_t *d_status,
                           hipStream_t stream);
 
+// Problems per batched quantize / QAT-forward / unpack launch.
+constexpr int kQuantMaxBatch = 64;
+
+// count same-shaped problems: quantize + pack (w_hats == nullptr) or the QAT
+// forward (w_hats given; packeds unused; scales may be nullptr, or hold
+// nullptr entries, to skip them).
+void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                          uint8_t *const *packeds, uint16_t *const *scales,
+                          uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream);
+
+void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
+                           int8_t *const *codes, int32_t *d_status, hipStream_t stream);
+
 // QAT forward (tq_quant.hip): w_hat = bf16(c * s) straight from w; scales
 // written only if not null.
 void launch_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,

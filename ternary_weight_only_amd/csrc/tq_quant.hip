@@ -10,6 +10,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <type_traits>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -18,6 +20,7 @@ namespace {
 constexpr int kWave = 64;
 constexpr int kBlock = 256;
 constexpr int kWavesPerBlock = kBlock / kWave;
+constexpr int kMaxBlocks = 16384;  // blocks of one launch, over all its problems
 
 // ---------------------------------------------------------------------------
 // fp16 rounding of a fixed-point magnitude.
@@ -118,6 +121,16 @@ __device__ __forceinline__ uint32_t bf16_of_f16(uint32_t h) {
   return (u + 0x7FFFu + ((u >> 16) & 1u)) >> 16;
 }
 
+// Lane i's partner in butterfly step k of a 16-lane group, as a DPP move:
+// i^1, i^2 (quad permutes), then 7-i within each 8 lanes (row_half_mirror)
+// and 15-i within 16 (row_mirror).  Every step pairs lanes symmetrically, so
+// a commutative reduction leaves the same value in all lanes of the group.
+template <int STEP>
+__device__ __forceinline__ uint32_t dpp_partner(uint32_t v) {
+  constexpr int ctrl = STEP == 0 ? 0xB1 : STEP == 1 ? 0x4E : STEP == 2 ? 0x141 : 0x140;
+  return (uint32_t)__builtin_amdgcn_mov_dpp((int)v, ctrl, 0xF, 0xF, false);
+}
+
 __device__ __forceinline__ uint32_t shfl_xor_u32(uint32_t v, int mask) {
   return (uint32_t)__shfl_xor((int)v, mask, kWave);
 }
@@ -140,10 +153,22 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 // w_hat = bf16(c * s) where it read them (no LDS, no barrier), and the
 // scales are written only if `scales` is not null.
 // ---------------------------------------------------------------------------
+// Problems of one launch (blockIdx.y picks one), all of one shape.
+struct QuantBatch {
+  const uint16_t *w[kQuantMaxBatch];
+  uint8_t *packed[kQuantMaxBatch];
+  uint16_t *scales[kQuantMaxBatch];
+  uint16_t *w_hat[kQuantMaxBatch];
+};
+
 template <int G, bool FAKE>
-__global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
-    const uint16_t *__restrict__ w, int64_t total_groups, uint8_t *__restrict__ packed,
-    uint16_t *__restrict__ scales, uint16_t *__restrict__ w_hat, int32_t *__restrict__ d_status) {
+__global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch args,
+                                                               int64_t total_groups,
+                                                               int32_t *__restrict__ d_status) {
+  const uint16_t *__restrict__ w = args.w[blockIdx.y];
+  uint8_t *__restrict__ packed = args.packed[blockIdx.y];
+  uint16_t *__restrict__ scales = args.scales[blockIdx.y];
+  uint16_t *__restrict__ w_hat = args.w_hat[blockIdx.y];
   constexpr int LPG = G / 8;               // lanes per group
   constexpr int GPC = 512 / G;             // groups per chunk
   constexpr int B = bytes_per_group(G);    // bytes per group
@@ -172,76 +197,136 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
 #pragma unroll
     for (int i = 0; i < 4; ++i) { h[2 * i] = raw[i] & 0xFFFFu; h[2 * i + 1] = raw[i] >> 16; }
 
-    // exponent maximum and non-finite flag over the group
-    int emax = 0;
-    uint32_t nonfinite = 0;
+    // Fast path.  The sum of |w| in fp32: each lane adds its 8 magnitudes in
+    // order, then an xor butterfly over the group's LPG lanes (fp32 addition
+    // commutes, so every lane ends with the same sum S_hat).  Along any path
+    // there are at most 7 + log2(LPG) <= 11 rounded additions of non-negative
+    // terms, so |S_hat - S| <= 11 * 2^-24 * S, plus at most G * 2^-126 should
+    // subnormals be flushed.  With E = 2^-19 S_hat + 2^-118 the exact sum lies
+    // in [S_hat - E, S_hat + E] even after the rounding of those two
+    // operations; when both ends, divided by G, round to the same fp16 value,
+    // so does the exact mean (rounding is monotonic).  Otherwise the group
+    // takes the exact path below.
+    float acc = 0.f;
+    uint32_t maxmag = 0;
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
-      const uint32_t E = (h[i] >> 7) & 0xFFu;
-      nonfinite |= (E == 0xFFu);
-      const int e = E ? (int)E - 1 : 0;
-      emax = e > emax ? e : emax;
+      const uint32_t mag = h[i] & 0x7FFFu;
+      maxmag = mag > maxmag ? mag : maxmag;
+      acc += __uint_as_float(mag << 16);
     }
-#pragma unroll
-    for (int m = 1; m < LPG; m <<= 1) {
-      const int o = (int)shfl_xor_u32((uint32_t)emax, m);
-      emax = o > emax ? o : emax;
-      nonfinite |= shfl_xor_u32(nonfinite, m);
-    }
-
-    // fixed-point sum anchored at the group's largest exponent
-    uint64_t T = 0;
-    uint32_t inexact = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) {
-      const uint32_t u = h[i] & 0x7FFFu;
-      const uint32_t E = u >> 7;
-      const uint64_t sig = E ? 128u + (u & 0x7Fu) : (u & 0x7Fu);
-      const int e = E ? (int)E - 1 : 0;
-      const int sh = e - emax + kWin;
-      if (sh >= 0) {
-        T += sig << sh;
-      } else if (sh > -8) {
-        T += sig >> (-sh);
-        inexact |= (sig & ((1ull << (-sh)) - 1)) != 0;
-      } else {
-        inexact |= sig != 0;
-      }
-    }
-#pragma unroll
-    for (int m = 1; m < LPG; m <<= 1) {
-      T += shfl_xor_u64(T, m);
-      inexact |= shfl_xor_u32(inexact, m);
-    }
-
-    // one rounding of the mean to fp16; the true sum lies in [T, T + G) units
-    // of 2^(emax - 181) and the mean in units of 2^-24 is that times
-    // 2^(emax - 157 - log2 G)
-    uint32_t sbits;
+    auto step = [&](auto k) {
+      acc += __uint_as_float(dpp_partner<decltype(k)::value>(__float_as_uint(acc)));
+      const uint32_t o = dpp_partner<decltype(k)::value>(maxmag);
+      maxmag = o > maxmag ? o : maxmag;
+    };
+    step(std::integral_constant<int, 0>{});
+    step(std::integral_constant<int, 1>{});
+    step(std::integral_constant<int, 2>{});
+    if constexpr (LPG == 16) step(std::integral_constant<int, 3>{});
+    uint32_t sbits = 0;
     int flags = 0;
-    bool need_exact = false;
-    if (nonfinite) {
+    bool slow = false;
+    if (maxmag >= 0x7F80u) {  // an Inf or NaN weight
       sbits = 0x7E00;
       flags = kDevNonfinite;
     } else {
-      const int sh = emax - 157 - LOG2G;
-      bool ovf;
-      sbits = f16_bits_of_fixed(T, sh, &ovf);
-      if (inexact) {
-        bool ovf2;
-        const uint32_t hi = f16_bits_of_fixed(T + (uint64_t)G, sh, &ovf2);
-        need_exact = hi != sbits;
+      const float E = fmaf(acc, 0x1p-19f, 0x1p-118f);
+      constexpr float kInvG = 1.0f / G;
+      const uint32_t qlo = __half_as_ushort(__float2half_rn(fmaxf(acc - E, 0.f) * kInvG));
+      const uint32_t qhi = __half_as_ushort(__float2half_rn((acc + E) * kInvG));
+      if (qlo == qhi) {
+        sbits = qlo;
+        if (sbits >= 0x7C00u) {
+          sbits = 0x7C00;
+          flags = kDevScaleOverflow;
+        }
+      } else {
+        slow = true;
       }
-      if (ovf && !need_exact) flags = kDevScaleOverflow;
     }
-    if (need_exact && active && sub == 0) {
-      bool ovf;
-      sbits = f16_scale_exact(w + gi * G, G, LOG2G, &ovf);
-      flags = ovf ? kDevScaleOverflow : 0;
+
+    // Exact path, taken by the whole wave when one of its groups needs it
+    // (its shuffles need every lane): exponent maximum, a fixed-point sum
+    // anchored at it, and the 320-bit sum when that window is not enough.
+    if (__any(slow)) {
+      const uint32_t sbits_fast = sbits;
+      const int flags_fast = flags;
+      // exponent maximum and non-finite flag over the group
+      int emax = 0;
+      uint32_t nonfinite = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t E = (h[i] >> 7) & 0xFFu;
+        nonfinite |= (E == 0xFFu);
+        const int e = E ? (int)E - 1 : 0;
+        emax = e > emax ? e : emax;
+      }
+#pragma unroll
+      for (int m = 1; m < LPG; m <<= 1) {
+        const int o = (int)shfl_xor_u32((uint32_t)emax, m);
+        emax = o > emax ? o : emax;
+        nonfinite |= shfl_xor_u32(nonfinite, m);
+      }
+
+      // fixed-point sum anchored at the group's largest exponent
+      uint64_t T = 0;
+      uint32_t inexact = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        const uint32_t u = h[i] & 0x7FFFu;
+        const uint32_t E = u >> 7;
+        const uint64_t sig = E ? 128u + (u & 0x7Fu) : (u & 0x7Fu);
+        const int e = E ? (int)E - 1 : 0;
+        const int sh = e - emax + kWin;
+        if (sh >= 0) {
+          T += sig << sh;
+        } else if (sh > -8) {
+          T += sig >> (-sh);
+          inexact |= (sig & ((1ull << (-sh)) - 1)) != 0;
+        } else {
+          inexact |= sig != 0;
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < LPG; m <<= 1) {
+        T += shfl_xor_u64(T, m);
+        inexact |= shfl_xor_u32(inexact, m);
+      }
+
+      // one rounding of the mean to fp16; the true sum lies in [T, T + G) units
+      // of 2^(emax - 181) and the mean in units of 2^-24 is that times
+      // 2^(emax - 157 - log2 G)
+      sbits = 0;
+      flags = 0;
+      bool need_exact = false;
+      if (nonfinite) {
+        sbits = 0x7E00;
+        flags = kDevNonfinite;
+      } else {
+        const int sh = emax - 157 - LOG2G;
+        bool ovf;
+        sbits = f16_bits_of_fixed(T, sh, &ovf);
+        if (inexact) {
+          bool ovf2;
+          const uint32_t hi = f16_bits_of_fixed(T + (uint64_t)G, sh, &ovf2);
+          need_exact = hi != sbits;
+        }
+        if (ovf && !need_exact) flags = kDevScaleOverflow;
+      }
+      if (need_exact && active && sub == 0) {
+        bool ovf;
+        sbits = f16_scale_exact(w + gi * G, G, LOG2G, &ovf);
+        flags = ovf ? kDevScaleOverflow : 0;
+      }
+      const int leader = qg * LPG;
+      sbits = (uint32_t)__shfl((int)sbits, leader, kWave);
+      flags = __shfl(flags, leader, kWave);
+      if (!slow) {
+        sbits = sbits_fast;
+        flags = flags_fast;
+      }
     }
-    const int leader = qg * LPG;
-    sbits = (uint32_t)__shfl((int)sbits, leader, kWave);
-    flags = __shfl(flags, leader, kWave);
 
     // codes: |w| > s/2, compared as ordered fp32 bit patterns (exact, no
     // denormal flushing involved); flagged groups keep all codes at 0
@@ -314,11 +399,17 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(
 // ---------------------------------------------------------------------------
 // unpack: one thread per 8 consecutive codes of a group (one 64-bit store).
 // ---------------------------------------------------------------------------
+struct UnpackBatch {
+  const uint8_t *packed[kQuantMaxBatch];
+  int8_t *codes[kQuantMaxBatch];
+};
+
 template <int G>
-__global__ __launch_bounds__(kBlock) void unpack_kernel(const uint8_t *__restrict__ packed,
+__global__ __launch_bounds__(kBlock) void unpack_kernel(const UnpackBatch args,
                                                         int64_t total_groups,
-                                                        int8_t *__restrict__ codes,
                                                         int32_t *__restrict__ d_status) {
+  const uint8_t *__restrict__ packed = args.packed[blockIdx.y];
+  int8_t *__restrict__ codes = args.codes[blockIdx.y];
   constexpr int TPG = G / 8;
   constexpr int B = bytes_per_group(G);
   const int64_t total = total_groups * TPG;
@@ -359,42 +450,75 @@ int grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
 
 }  // namespace
 
-void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,
-                          uint16_t *scales, int32_t *d_status, hipStream_t stream) {
+// count problems of one shape, up to kQuantMaxBatch per launch; each
+// problem gets the same number of blocks (at most kMaxBlocks in a launch).
+void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                          uint8_t *const *packeds, uint16_t *const *scales,
+                          uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream) {
   const int64_t total_groups = N * (K / G);
   const int64_t nchunks = (total_groups * G + 511) / 512;
-  const int grid = grid_for(nchunks, kWavesPerBlock, 8192);
-  if (G == 64)
-    hipLaunchKernelGGL((quantize_pack_kernel<64, false>), dim3(grid), dim3(kBlock), 0, stream, w,
-                       total_groups, packed, scales, nullptr, d_status);
-  else
-    hipLaunchKernelGGL((quantize_pack_kernel<128, false>), dim3(grid), dim3(kBlock), 0, stream,
-                       w, total_groups, packed, scales, nullptr, d_status);
+  const bool fake = w_hats != nullptr;
+  for (int c0 = 0; c0 < count; c0 += kQuantMaxBatch) {
+    const int n = count - c0 < kQuantMaxBatch ? count - c0 : kQuantMaxBatch;
+    QuantBatch a{};
+    for (int i = 0; i < n; ++i) {
+      a.w[i] = ws[c0 + i];
+      a.packed[i] = packeds ? packeds[c0 + i] : nullptr;
+      a.scales[i] = scales ? scales[c0 + i] : nullptr;
+      a.w_hat[i] = fake ? w_hats[c0 + i] : nullptr;
+    }
+    const dim3 grid(grid_for(nchunks, kWavesPerBlock, kMaxBlocks / n), n);
+    if (G == 64) {
+      if (fake)
+        hipLaunchKernelGGL((quantize_pack_kernel<64, true>), grid, dim3(kBlock), 0, stream, a,
+                           total_groups, d_status);
+      else
+        hipLaunchKernelGGL((quantize_pack_kernel<64, false>), grid, dim3(kBlock), 0, stream, a,
+                           total_groups, d_status);
+    } else {
+      if (fake)
+        hipLaunchKernelGGL((quantize_pack_kernel<128, true>), grid, dim3(kBlock), 0, stream, a,
+                           total_groups, d_status);
+      else
+        hipLaunchKernelGGL((quantize_pack_kernel<128, false>), grid, dim3(kBlock), 0, stream, a,
+                           total_groups, d_status);
+    }
+  }
+}
+
+void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,
+                          uint16_t *scales, int32_t *d_status, hipStream_t stream) {
+  launch_quant_batched(1, &w, N, K, G, &packed, &scales, nullptr, d_status, stream);
 }
 
 void launch_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,
                           uint16_t *scales, int32_t *d_status, hipStream_t stream) {
+  launch_quant_batched(1, &w, N, K, G, nullptr, &scales, &w_hat, d_status, stream);
+}
+
+void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
+                           int8_t *const *codes, int32_t *d_status, hipStream_t stream) {
   const int64_t total_groups = N * (K / G);
-  const int64_t nchunks = (total_groups * G + 511) / 512;
-  const int grid = grid_for(nchunks, kWavesPerBlock, 8192);
-  if (G == 64)
-    hipLaunchKernelGGL((quantize_pack_kernel<64, true>), dim3(grid), dim3(kBlock), 0, stream, w,
-                       total_groups, nullptr, scales, w_hat, d_status);
-  else
-    hipLaunchKernelGGL((quantize_pack_kernel<128, true>), dim3(grid), dim3(kBlock), 0, stream,
-                       w, total_groups, nullptr, scales, w_hat, d_status);
+  for (int c0 = 0; c0 < count; c0 += kQuantMaxBatch) {
+    const int n = count - c0 < kQuantMaxBatch ? count - c0 : kQuantMaxBatch;
+    UnpackBatch a{};
+    for (int i = 0; i < n; ++i) {
+      a.packed[i] = packeds[c0 + i];
+      a.codes[i] = codes[c0 + i];
+    }
+    const dim3 grid(grid_for(total_groups * (G / 8), kBlock, kMaxBlocks / n), n);
+    if (G == 64)
+      hipLaunchKernelGGL(unpack_kernel<64>, grid, dim3(kBlock), 0, stream, a, total_groups,
+                         d_status);
+    else
+      hipLaunchKernelGGL(unpack_kernel<128>, grid, dim3(kBlock), 0, stream, a, total_groups,
+                         d_status);
+  }
 }
 
 void launch_unpack(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
                    int32_t *d_status, hipStream_t stream) {
-  const int64_t total_groups = N * (K / G);
-  const int grid = grid_for(total_groups * (G / 8), kBlock, 16384);
-  if (G == 64)
-    hipLaunchKernelGGL(unpack_kernel<64>, dim3(grid), dim3(kBlock), 0, stream, packed,
-                       total_groups, codes, d_status);
-  else
-    hipLaunchKernelGGL(unpack_kernel<128>, dim3(grid), dim3(kBlock), 0, stream, packed,
-                       total_groups, codes, d_status);
+  launch_unpack_batched(1, &packed, N, K, G, &codes, d_status, stream);
 }
 
 }  // namespace tq

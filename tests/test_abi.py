@@ -142,6 +142,36 @@ def test_fake_quantize_argument_errors():
     assert f(FAKE, 4, 128, 64, FAKE, None, FAKE + 2, None) == -4
 
 
+def test_quantize_unpack_batched_argument_errors():
+    import ctypes
+    lib = _lib()
+    arr = ctypes.c_void_p * 2
+
+    def ps(*v):
+        return arr(*v)
+    good = ps(FAKE, FAKE + 4096)
+    for f in (lib.tq_quantize_pack_batched, lib.tq_fake_quantize_batched):
+        assert f(0, None, 4, 128, 64, None, None, None, None) == 0
+        assert f(-1, good, 4, 128, 64, good, good, None, None) == -2
+        assert f(2, None, 4, 128, 64, good, good, None, None) == -1
+        assert f(2, ps(FAKE, None), 4, 128, 64, good, good, None, None) == -1
+        assert f(2, good, 4, 130, 64, good, good, None, None) == -2
+        assert f(2, good, 4, 128, 32, good, good, None, None) == -3
+        assert f(2, ps(FAKE, FAKE + 8), 4, 128, 64, good, good, None, None) == -4
+        assert f(2, good, 4, 128, 64, good, ps(FAKE, FAKE + 1), None, None) == -4
+        assert f(2, good, 4, 128, 64, good, good, FAKE + 2, None) == -4
+    q, fq = lib.tq_quantize_pack_batched, lib.tq_fake_quantize_batched
+    assert q(2, good, 4, 128, 64, good, None, None, None) == -1        # scales required
+    assert fq(2, good, 4, 128, 64, None, None, None, None) == -1       # w_hats required
+    assert fq(2, good, 4, 128, 64, ps(FAKE, FAKE + 8), None, None, None) == -4
+    u = lib.tq_unpack_batched
+    assert u(0, None, 4, 128, 64, None, None, None) == 0
+    assert u(2, None, 4, 128, 64, good, None, None) == -1
+    assert u(2, good, 4, 128, 64, ps(FAKE, None), None, None) == -1
+    assert u(2, good, 4, 128, 64, ps(FAKE, FAKE + 4), None, None) == -4
+    assert u(2, good, 4, 128, 48, good, None, None) == -3
+
+
 def test_dequantize_argument_errors():
     d = _lib().tq_dequantize
     assert d(None, FAKE, 4, 128, 64, FAKE, None, None) == -1
