@@ -16,31 +16,17 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include "tq_digits.h"
 #include "tq_internal.h"
 
 namespace tq {
 namespace {
 
 constexpr int kBlock = 256;
-constexpr uint32_t kLutInvalid = 1u << 31;
 constexpr int kMaxBlocks = 65536;  // blocks of one launch, over all its problems
 constexpr int kMinBlocks = 2048;   // 8 per CU: below this, fewer items per thread
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
-
-// Table entry of byte v: its five base-3 digits d_i = c_i + 1 as 2-bit
-// fields (d_i at bits 2i, so the first weight is lowest).  An invalid byte
-// reads as five digits 1 (code 0) and carries kLutInvalid.
-__device__ __forceinline__ uint32_t digit_entry(uint32_t v) {
-  if (v >= 243u) return 0x155u | kLutInvalid;
-  uint32_t e = 0;
-#pragma unroll
-  for (int i = 0; i < 5; ++i) {
-    e |= (v % 3u) << (2 * i);
-    v /= 3u;
-  }
-  return e;
-}
 
 // bf16 bits of the fp16 value h (finite): fp16 -> fp32 is exact, then one
 // round to nearest, ties to even, to 8 significant bits.  Every finite fp16

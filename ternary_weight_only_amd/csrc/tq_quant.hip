@@ -12,6 +12,7 @@
 
 #include <type_traits>
 
+#include "tq_digits.h"
 #include "tq_internal.h"
 
 namespace tq {
@@ -397,47 +398,85 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
 }
 
 // ---------------------------------------------------------------------------
-// unpack: one thread per 8 consecutive codes of a group (one 64-bit store).
+// unpack: one thread per 16 consecutive codes of a group (G % 16 == 0), one
+// 16-byte store, so a wave writes 1 KB contiguously.  The 16 codes lie in
+// four bytes of the group, read from the one or two aligned dwords holding
+// them (both hold bytes of the group, so no read leaves the buffer's
+// pages).  A 256-entry LDS table gives each byte's digits as 2-bit fields;
+// each 4 digits are spread into the 4 selector bytes of one v_perm_b32 that
+// picks 0xFF, 0x00 or 0x01 (codes -1, 0, 1).  U items per thread and pass,
+// their loads issued before any is decoded.
 // ---------------------------------------------------------------------------
 struct UnpackBatch {
   const uint8_t *packed[kQuantMaxBatch];
   int8_t *codes[kQuantMaxBatch];
 };
 
-template <int G>
-__global__ __launch_bounds__(kBlock) void unpack_kernel(const UnpackBatch args,
-                                                        int64_t total_groups,
+template <int G, int U>
+__global__ __launch_bounds__(kBlock) void unpack_kernel(const UnpackBatch args, uint64_t total,
                                                         int32_t *__restrict__ d_status) {
   const uint8_t *__restrict__ packed = args.packed[blockIdx.y];
   int8_t *__restrict__ codes = args.codes[blockIdx.y];
-  constexpr int TPG = G / 8;
+  constexpr int TPG = G / 16;                 // threads per group
   constexpr int B = bytes_per_group(G);
-  const int64_t total = total_groups * TPG;
+  constexpr int NPAD = 5 * B - G;             // padding trits, in the group's last byte
+  constexpr uint32_t kPadMask = (1u << (2 * NPAD)) - 1u;
+  constexpr uint32_t kPadZero = 0x5555u & kPadMask;
+
+  __shared__ uint32_t lut[256];
+  lut[threadIdx.x] = digit_entry(threadIdx.x);
+  __syncthreads();
+
+  const uint32_t pmis = (uint32_t)(reinterpret_cast<uintptr_t>(packed) & 3u);
+  const uint32_t *__restrict__ pw = reinterpret_cast<const uint32_t *>(packed - pmis);
+  const bool a16 = (reinterpret_cast<uintptr_t>(codes) & 15u) == 0;
   int flags = 0;
-  for (int64_t t = (int64_t)blockIdx.x * kBlock + threadIdx.x; t < total;
-       t += (int64_t)gridDim.x * kBlock) {
-    const int64_t gi = t / TPG;
-    const int p0 = (int)(t % TPG) * 8;
-    const uint8_t *pg = packed + gi * B;
-    const int b0 = p0 / 5, b1 = (p0 + 7) / 5;
-    uint64_t out = 0;
-    for (int b = b0; b <= b1; ++b) {
-      uint32_t v = pg[b];
-      const bool valid = v < 243u;
-      if (!valid) flags |= kDevInvalidByte;
+  const uint64_t stride = (uint64_t)gridDim.x * kBlock;
+  for (uint64_t t0 = (uint64_t)blockIdx.x * kBlock + threadIdx.x; t0 < total; t0 += U * stride) {
+    uint32_t w0[U], w1[U], sh[U];
 #pragma unroll
-      for (int i = 0; i < 5; ++i) {
-        const uint32_t d = v % 3u;
-        v /= 3u;
-        const int pos = 5 * b + i;
-        if (pos >= p0 && pos < p0 + 8) {
-          const uint32_t c = valid ? (uint32_t)(int8_t)((int)d - 1) & 0xFFu : 0u;
-          out |= (uint64_t)c << (8 * (pos - p0));
-        }
-        if (pos >= G && valid && d != 1u) flags |= kDevBadPadding;
+    for (int u = 0; u < U; ++u) {
+      uint64_t t = t0 + u * stride;
+      t = t < total ? t : total - 1;          // past the end: reload the last item, store nothing
+      const uint64_t gi = t / TPG;
+      const int p0 = (int)(t % TPG) * 16;
+      const uint64_t r = gi * B + p0 / 5 + pmis;
+      w0[u] = pw[r >> 2];
+      w1[u] = pw[(r + 3) >> 2];
+      sh[u] = 8u * (uint32_t)(r & 3u);
+    }
+#pragma unroll
+    for (int u = 0; u < U; ++u) {
+      const uint64_t t = t0 + u * stride;
+      if (t >= total) break;
+      const uint64_t gi = t / TPG;
+      const int p0 = (int)(t % TPG) * 16;
+      const int o = p0 - 5 * (p0 / 5);
+      const uint32_t bytes = (uint32_t)((((uint64_t)w1[u] << 32) | w0[u]) >> sh[u]);
+      const uint32_t e0 = lut[bytes & 0xFFu], e1 = lut[(bytes >> 8) & 0xFFu];
+      const uint32_t e2 = lut[(bytes >> 16) & 0xFFu], e3 = lut[bytes >> 24];
+      if ((e0 | e1 | e2 | e3) & kLutInvalid) flags |= kDevInvalidByte;
+      const uint64_t D = (uint64_t)((e0 & 0x3FFu) | ((e1 & 0x3FFu) << 10) | ((e2 & 0x3FFu) << 20)) |
+                         ((uint64_t)(e3 & 0x3FFu) << 30);
+      const uint64_t d = D >> (2 * o);        // digits of codes p0 .., then the next ones
+      if (p0 + 16 == G && (((uint32_t)(d >> 32)) & kPadMask) != kPadZero)
+        flags |= kDevBadPadding;
+      uint32_t out[4];
+#pragma unroll
+      for (int k = 0; k < 4; ++k) {
+        const uint32_t x = ((uint32_t)d >> (8 * k)) & 0xFFu;       // 4 digits
+        uint32_t y = (x | (x << 12)) & 0x000F000Fu;                 // d0 d1 | d2 d3
+        y = (y | (y << 6)) & 0x03030303u;                          // one digit per byte
+        out[k] = __builtin_amdgcn_perm(0u, 0x000100FFu, y);         // -1, 0, +1
+      }
+      int8_t *dst = codes + gi * G + p0;
+      if (a16) {
+        *reinterpret_cast<uint4 *>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
+      } else {  // codes only 8-byte aligned (the ABI's minimum)
+        reinterpret_cast<uint2 *>(dst)[0] = make_uint2(out[0], out[1]);
+        reinterpret_cast<uint2 *>(dst)[1] = make_uint2(out[2], out[3]);
       }
     }
-    *reinterpret_cast<uint64_t *>(codes + gi * G + p0) = out;
   }
   if (flags && d_status) atomicOr(d_status, flags);
 }
@@ -496,9 +535,32 @@ void launch_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16
   launch_quant_batched(1, &w, N, K, G, nullptr, &scales, &w_hat, d_status, stream);
 }
 
+template <int G, int U>
+void launch_unpack_u(const UnpackBatch &a, int n, uint64_t total, int32_t *d_status,
+                     hipStream_t stream) {
+  uint64_t blocks = (total + kBlock * U - 1) / (kBlock * U);
+  const uint64_t cap = (uint64_t)(kMaxBlocks / n);
+  if (blocks > cap) blocks = cap;
+  hipLaunchKernelGGL((unpack_kernel<G, U>), dim3((unsigned)blocks, (unsigned)n), dim3(kBlock), 0,
+                     stream, a, total, d_status);
+}
+
+template <int G>
+void launch_unpack_g(const UnpackBatch &a, int n, uint64_t total, int32_t *d_status,
+                     hipStream_t stream) {
+  // the most items per thread that still leaves 2048 blocks (8 per CU)
+  const uint64_t b4 = (total + kBlock * 4 - 1) / (kBlock * 4) * (uint64_t)n;
+  if (b4 >= 2048)
+    launch_unpack_u<G, 4>(a, n, total, d_status, stream);
+  else if (2 * b4 >= 2048)
+    launch_unpack_u<G, 2>(a, n, total, d_status, stream);
+  else
+    launch_unpack_u<G, 1>(a, n, total, d_status, stream);
+}
+
 void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
                            int8_t *const *codes, int32_t *d_status, hipStream_t stream) {
-  const int64_t total_groups = N * (K / G);
+  const uint64_t total = (uint64_t)N * (uint64_t)K / 16;  // items of 16 codes per problem
   for (int c0 = 0; c0 < count; c0 += kQuantMaxBatch) {
     const int n = count - c0 < kQuantMaxBatch ? count - c0 : kQuantMaxBatch;
     UnpackBatch a{};
@@ -506,13 +568,10 @@ void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, 
       a.packed[i] = packeds[c0 + i];
       a.codes[i] = codes[c0 + i];
     }
-    const dim3 grid(grid_for(total_groups * (G / 8), kBlock, kMaxBlocks / n), n);
     if (G == 64)
-      hipLaunchKernelGGL(unpack_kernel<64>, grid, dim3(kBlock), 0, stream, a, total_groups,
-                         d_status);
+      launch_unpack_g<64>(a, n, total, d_status, stream);
     else
-      hipLaunchKernelGGL(unpack_kernel<128>, grid, dim3(kBlock), 0, stream, a, total_groups,
-                         d_status);
+      launch_unpack_g<128>(a, n, total, d_status, stream);
   }
 }
 

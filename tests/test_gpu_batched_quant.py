@@ -48,3 +48,35 @@ def test_batched_match_single_calls_and_oracle(N, K, G, count):
             assert torch.equal(tq.fake_quantize(wd[i], G).view(torch.int16),
                                fb[i][0].view(torch.int16))
             assert torch.equal(tq.unpack(p, N, K, G), ub[i])
+
+
+@pytest.mark.parametrize("G", [64, 128])
+@pytest.mark.parametrize("offset", [0, 1, 2, 3])
+def test_unpack_random_bytes_any_alignment(G, offset):
+    """Random bytes over 0..255 (invalid ones and every padding pattern),
+    packed data at each alignment, codes 16-byte and only 8-byte aligned;
+    a small matrix (one item per thread) and 4096 x 1024."""
+    import torch
+    import ternary_weight_only_amd as tq
+    rng = np.random.default_rng(700 + G + offset)
+    for N, K in ((37, 5 * G), (4096, 1024)):
+        B = (G + 4) // 5
+        p = rng.integers(0, 256, size=(N, (K // G) * B)).astype(np.uint8)
+        if N > 100:  # valid bytes (random padding trits), one invalid byte at the end
+            p = rng.integers(0, 243, size=p.shape).astype(np.uint8)
+            p[-1, -1] = 250
+        flat = p.reshape(-1)
+        buf = torch.zeros(flat.size + 8, dtype=torch.uint8, device="cuda")
+        pd = buf[offset:offset + flat.size]
+        pd.copy_(torch.from_numpy(flat))
+        ref, st_ref = oracle.unpack(p, N, K, G)
+        for c_off in (0, 8):
+            cb = torch.empty(N * K + 16, dtype=torch.int8, device="cuda")
+            cd = cb[c_off:c_off + N * K].view(N, K)
+            st = tq.new_status()
+            say("unpack random bytes N=%d K=%d G=%d packed offset %d codes offset %d"
+                % (N, K, G, offset, c_off))
+            tq.unpack(pd, N, K, G, status=st, out=cd)
+            torch.cuda.synchronize()
+            assert np.array_equal(cd.cpu().numpy(), ref), (N, K, c_off)
+            assert int(st.item()) == st_ref
