@@ -67,6 +67,12 @@ def _load():
         lib.oracle_dequantize.restype = ctypes.c_int
         lib.oracle_fake_quantize.argtypes = [p, i64, i64, i64, p, p, p]
         lib.oracle_fake_quantize.restype = ctypes.c_int
+        lib.oracle_quantize_pack2.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.oracle_quantize_pack2.restype = ctypes.c_int
+        lib.oracle_unpack2.argtypes = [p, i64, i64, i64, p, p]
+        lib.oracle_unpack2.restype = ctypes.c_int
+        lib.oracle_matmul2.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
+        lib.oracle_matmul2.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -155,6 +161,57 @@ def fake_quantize(w_bits: np.ndarray, G: int):
     if rc:
         raise OracleError("oracle_fake_quantize rc=%d" % rc)
     return out, sc, int(st[0])
+
+
+def quantize_pack2(w_bits: np.ndarray, G: int):
+    """2-bit format: w_bits uint16 [N,K] bf16 -> (packed uint8 [N, K/4], scales
+    uint16 [N, K/G] fp16 bits, status bits int)."""
+    w = np.ascontiguousarray(w_bits, dtype=np.uint16)
+    if w.ndim != 2:
+        raise ValueError("w must be 2-D [N,K]")
+    N, K = w.shape
+    if G < 4 or G % 4 or K % G:
+        raise OracleError("invalid shape K=%d G=%d" % (K, G))
+    packed = np.empty((N, K // 4), np.uint8)
+    scales = np.empty((N, K // G), np.uint16)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_quantize_pack2(_ptr(w), N, K, G, _ptr(packed), _ptr(scales), _ptr(st))
+    if rc:
+        raise OracleError("oracle_quantize_pack2 rc=%d" % rc)
+    return packed, scales, int(st[0])
+
+
+def unpack2(packed: np.ndarray, N: int, K: int, G: int):
+    """2-bit packed [N, K/4] -> (codes int8 [N,K], status bits int)."""
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    if p.size != N * K // 4:
+        raise OracleError("bad packed size")
+    codes = np.empty((N, K), np.int8)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_unpack2(_ptr(p), N, K, G, _ptr(codes), _ptr(st))
+    if rc:
+        raise OracleError("oracle_unpack2 rc=%d" % rc)
+    return codes, int(st[0])
+
+
+def matmul2(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):
+    """As matmul, over the 2-bit format."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M,K]")
+    M = x.shape[0]
+    p = np.ascontiguousarray(packed, dtype=np.uint8)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    if p.size != N * K // 4 or s.size != N * (K // G):
+        raise OracleError("bad packed/scales sizes")
+    y = np.empty((M, N), np.float64)
+    bound = np.empty((M, N), np.float64)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_matmul2(_ptr(x), _ptr(p), _ptr(s), M, N, K, G, _ptr(y), _ptr(bound),
+                                _ptr(st))
+    if rc:
+        raise OracleError("oracle_matmul2 rc=%d" % rc)
+    return y, bound, int(st[0])
 
 
 def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):

@@ -492,14 +492,20 @@ int oracle_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t G, uin
  * INVALID_BYTE.  Non-finite scales (never produced by the packer for a
  * valid group) are passed through as IEEE values.
  */
-int oracle_matmul(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
-                  int64_t M, int64_t N, int64_t K, int64_t G,
-                  double *y, double *bound, int32_t *status)
+int oracle_unpack2(const uint8_t *packed, int64_t N, int64_t K, int64_t G, int8_t *codes,
+                   int32_t *status);
+
+/* y = x * W_hat^T over rows decoded from the base-3 format (two_bit = 0) or
+ * the 2-bit format (two_bit = 1). */
+static int matmul_rows(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                       int64_t M, int64_t N, int64_t K, int64_t G, int two_bit,
+                       double *y, double *bound, int32_t *status)
 {
     if (!x || !packed || !scales || !y) return OR_ERR_NULL;
     if (M < 1) return OR_ERR_SHAPE;
     int rc = check_shape(N, K, G);
     if (rc) return rc;
+    if (two_bit && G % 4) return OR_ERR_SHAPE;
     const int64_t nG = K / G;
     int8_t *crow = (int8_t *)malloc((size_t)K);
     double *wrow = (double *)malloc((size_t)K * sizeof(double));
@@ -511,7 +517,8 @@ int oracle_matmul(const uint16_t *x, const uint8_t *packed, const uint16_t *scal
     for (int64_t n = 0; n < N; ++n) {
         /* decode row n: w_hat = c * s */
         int32_t rst = 0;
-        oracle_unpack(packed + n * oracle_packed_row_bytes(K, G), 1, K, G, crow, &rst);
+        if (two_bit) oracle_unpack2(packed + n * (K / 4), 1, K, G, crow, &rst);
+        else oracle_unpack(packed + n * oracle_packed_row_bytes(K, G), 1, K, G, crow, &rst);
         st |= rst & OR_INVALID_BYTE;
         for (int64_t g = 0; g < nG; ++g) {
             uint16_t h = scales[n * nG + g];
@@ -537,4 +544,80 @@ int oracle_matmul(const uint16_t *x, const uint8_t *packed, const uint16_t *scal
     free(crow); free(wrow); free(xd);
     if (status) *status |= st;
     return OR_OK;
+}
+
+int oracle_matmul(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                  int64_t M, int64_t N, int64_t K, int64_t G,
+                  double *y, double *bound, int32_t *status)
+{
+    return matmul_rows(x, packed, scales, M, N, K, G, 0, y, bound, status);
+}
+
+/* ------------------------------------------------------------------------ */
+/* 2-bit format: four codes a byte                                           */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * Ternary codes in two bits each, four a byte (Avenue README, size note:
+ * model sizes counted for 2-bit packing; "Autoregressive Language Model on
+ * the 6502 Processor": ternary parameters packed four a byte).  Reading
+ * taken here: field f = c + 1 in {0, 1, 2}, the first weight in the lowest
+ * two bits, G/4 bytes a group, the same fp16 group scales and code rule as
+ * the base-3 format; field value 3 is invalid.
+ *   packed[N][K/G][G/4] bytes, scales[N][K/G] fp16 bits.
+ */
+int oracle_quantize_pack2(const uint16_t *w, int64_t N, int64_t K, int64_t G,
+                          uint8_t *packed, uint16_t *scales, int32_t *status)
+{
+    if (!w || !packed || !scales) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    if (G % 4) return OR_ERR_SHAPE;
+    const int64_t nG = K / G;
+    int32_t st = 0;
+    int8_t *code = (int8_t *)malloc((size_t)G);
+    if (!code) return OR_ERR_NULL;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < nG; ++g) {
+            uint16_t sbits;
+            int gst = group_scale_and_codes(w + n * K + g * G, G, G, &sbits, code);
+            uint8_t *pg = packed + n * (K / 4) + g * (G / 4);
+            for (int64_t b = 0; b < G / 4; ++b) {
+                int byte = 0;
+                for (int i = 0; i < 4; ++i) byte |= (code[4 * b + i] + 1) << (2 * i);
+                pg[b] = (uint8_t)byte;
+            }
+            scales[n * nG + g] = sbits;
+            st |= gst;
+        }
+    }
+    free(code);
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+/* 2-bit packed -> codes[N,K] in {-1,0,1}; a field of 3 reads as code 0 and
+ * sets INVALID_BYTE. */
+int oracle_unpack2(const uint8_t *packed, int64_t N, int64_t K, int64_t G, int8_t *codes,
+                   int32_t *status)
+{
+    if (!packed || !codes) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    if (G % 4) return OR_ERR_SHAPE;
+    int32_t st = 0;
+    for (int64_t i = 0; i < N * K; ++i) {
+        int f = (packed[i / 4] >> (2 * (i % 4))) & 3;
+        if (f == 3) { st |= OR_INVALID_BYTE; f = 1; }
+        codes[i] = (int8_t)(f - 1);
+    }
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+int oracle_matmul2(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                   int64_t M, int64_t N, int64_t K, int64_t G,
+                   double *y, double *bound, int32_t *status)
+{
+    return matmul_rows(x, packed, scales, M, N, K, G, 1, y, bound, status);
 }
