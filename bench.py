@@ -308,6 +308,53 @@ def main():
     assert int(status.item()) == 0, "device status %d" % int(status.item())
     dq_ms = sorted(a.elapsed_time(b) for a, b in dq[1:])[1] / RING
 
+    # decode GEMV over the 2-bit format, outside the step: the same matrices
+    # packed four codes a byte (same scales and codes), one batched call per
+    # shape over each ring slot, all slots back to back
+    P2 = {}
+    for i, (N, K) in enumerate(shapes):
+        p2 = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
+        s2 = torch.empty(N, K // G, dtype=torch.float16, device=dev)
+        rc = L.tq_quantize_pack2(w_dev[i].data_ptr(), N, K, G, p2.data_ptr(), s2.data_ptr(), stp,
+                                 s0)
+        assert rc == 0, rc
+        P2[i] = (p2, s2)
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0
+    for i in (0, 71):
+        N, K = shapes[i]
+        rows = np.array([0, N // 2, N - 1])
+        p_ref, _, _ = oracle.quantize_pack2(mats[i][rows], G)
+        p = P2[i][0][torch.from_numpy(rows).to(dev)].cpu().numpy()
+        assert np.array_equal(p, p_ref), "bench inputs: 2-bit packed bytes differ from the oracle"
+    P2s = {slot: {i: (P2[i][0].clone(), P2[i][1].clone()) for i in P2} for slot in range(RING)}
+    del P2
+    y2 = [torch.empty(1, N, dtype=torch.float32, device=dev) for N, K in shapes]
+    g2_calls = {slot: [(N, K, len(idx), ptrs([x_dec[i] for i in idx]),
+                        ptrs([P2s[slot][i][0] for i in idx]), ptrs([P2s[slot][i][1] for i in idx]),
+                        ptrs([y2[i] for i in idx]))
+                       for (N, K), idx in groups.items()] for slot in range(RING)}
+
+    def run_gemv2(slot, stream):
+        for N, K, n, ax, ap, asc, ay in g2_calls[slot]:
+            rc = L.tq_gemv2_batched(n, ax, ap, asc, ay, N, K, G, stp, stream)
+            assert rc == 0, rc
+
+    g2 = []
+    with torch.cuda.stream(stream):
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for slot in range(RING):
+                run_gemv2(slot, sp)
+            e1.record(stream)
+            g2.append((e0, e1))
+    torch.cuda.synchronize()
+    assert int(status.item()) == 0, "device status %d" % int(status.item())
+    g2_ms = sorted(a.elapsed_time(b) for a, b in g2[1:])[1] / RING
+    packed2_bytes = sum(N * K // 4 + 2 * N * (K // G) for N, K in shapes)
+    del P2s, g2_calls
+
     # QAT forward (fake quantization), outside the step: every bf16 matrix to
     # its bf16 w_hat (72 direct launches a pass), eight passes per chain
     fq_calls = [(N, K, len(idx), ptrs([w_dev[i] for i in idx]), ptrs([w_hat[i] for i in idx]))
@@ -370,6 +417,11 @@ def main():
                         "frac_hbm": dequant_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "bytes_per_pass": dequant_bytes, "launches": len(groups),
                         "in_step": False},
+        "decode_gemv_2bit": {"ms": g2_ms, "GB/s": packed2_bytes / (g2_ms * 1e-3) / 1e9,
+                             "frac_hbm": packed2_bytes / (g2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                             "Tweights/s": weights / (g2_ms * 1e-3) / 1e12,
+                             "bytes_per_pass": packed2_bytes, "launches": len(groups),
+                             "in_step": False},
         "qat_forward": {"ms": fq_ms, "GB/s": 4 * weights / (fq_ms * 1e-3) / 1e9,
                         "frac_hbm": 4 * weights / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "bytes_per_pass": 4 * weights, "launches": len(groups),

@@ -309,6 +309,51 @@ int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *
                     int64_t M, int64_t N, int64_t K, int G,
                     int32_t *d_status, void *stream);
 
+/*
+ * The 2-bit ternary format: codes in two bits each, four a byte.
+ * Source: Avenue README (size note: model sizes counted for 2-bit packing)
+ * and "Autoregressive Language Model on the 6502 Processor" (ternary
+ * parameters packed four a byte).  Layout taken here:
+ *   packed2  uint8 [N][K/G][G/4]   field f = c + 1 in bits 2i..2i+1 of byte
+ *                                   b for weight 4b + i (first weight lowest);
+ *                                   f = 3 is invalid
+ *   scales   [N, K/G] fp16, as for the base-3 format (same scale, same codes)
+ * 8 * (G/4 + 2) / G bits per weight: 2.25 at G = 64, 2.125 at G = 128.
+ */
+
+/* Quantize and pack to the 2-bit format (scale and codes exactly as
+ * tq_quantize_pack).  w [N,K] bf16 16-byte aligned; packed2 [N, K/4] bytes,
+ * 2-byte aligned; scales [N, K/G] fp16, 2-byte aligned.  Device status and
+ * flagged-group outputs as tq_quantize_pack (flagged groups: codes 0). */
+int tq_quantize_pack2(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed2,
+                      uint16_t *scales, int32_t *d_status, void *stream);
+
+/* 2-bit packed -> codes int8 [N,K] {-1,0,1}.  packed2 4-byte aligned, codes
+ * 16-byte aligned.  A field of 3 sets TQ_DEV_INVALID_BYTE and reads as 0. */
+int tq_unpack2(const uint8_t *packed2, int64_t N, int64_t K, int G, int8_t *codes,
+               int32_t *d_status, void *stream);
+
+/*
+ * Decode GEMV over the 2-bit format, M = 1:
+ *   y[n] = sum_g s[n,g] * sum_{j<G} x[gG+j] * c[n, gG+j]
+ * (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation").
+ *   x [1,K] bf16 16-byte aligned; packed2 [N, K/4] 16-byte aligned; scales
+ *   [N, K/G] fp16 2-byte aligned; y [N] fp32 4-byte aligned, overwritten
+ * K <= 4096 (K/64 <= 64) and N < 2^28, else TQ_ERR_SHAPE.  A field of 3 sets
+ * TQ_DEV_INVALID_BYTE and counts as code 0.  Deterministic; accuracy as
+ * tq_gemv.
+ */
+int tq_gemv2(const uint16_t *x, const uint8_t *packed2, const uint16_t *scales, int64_t N,
+             int64_t K, int G, float *y, int32_t *d_status, void *stream);
+
+/* Batched form: `count` same-shaped problems, each as tq_gemv2 on xs[i],
+ * packed2s[i], scales[i], ys[i] (HOST arrays of DEVICE pointers, read during
+ * the call only), one launch per 64.  Errors as tq_gemv2; a NULL or
+ * misaligned pointer in any entry rejects the whole call. */
+int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packed2s,
+                     const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
+                     int G, int32_t *d_status, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -10,6 +10,8 @@ package only marshals torch tensors to that ABI:
     codes          = unpack(packed, N, K, G)       # codes + validation
     (the *_batched forms take lists of same-shaped matrices, one launch per 64)
     w_hat          = dequantize(packed, scales, N, K, G)  # bf16 c * s
+    packed2, scales = quantize_pack2(w_bf16, G)     # 2-bit format, four codes a byte
+    y              = gemv2(x_bf16, packed2, scales, N, K, G)  # its M = 1 GEMV
     w_hats         = dequantize_batched(packeds, scales, N, K, G)  # many same-shaped
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
     ys             = gemv_batched(xs, packeds, scales, N, K, G)  # many same-shaped
@@ -41,11 +43,15 @@ from .binding import (  # noqa: F401
     gemv,
     gemv_batched,
     gemv_grouped,
+    gemv2,
+    gemv2_batched,
     lib,
     new_status,
     packed_bytes,
     quantize_pack,
     quantize_pack_batched,
+    quantize_pack2,
     unpack,
     unpack_batched,
+    unpack2,
 )

@@ -22,7 +22,8 @@ DEV_BAD_PADDING = 8
 # Every symbol include/tq.h declares.
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
            "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
-           "tq_dequantize", "tq_dequantize_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_unpack2",
+           "tq_gemv2", "tq_gemv2_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -51,6 +52,14 @@ def lib() -> ctypes.CDLL:
         for f in (l.tq_quantize_pack_batched, l.tq_fake_quantize_batched):
             f.argtypes = [i32, p, i64, i64, i32, p, p, p, p]
             f.restype = i32
+        l.tq_quantize_pack2.argtypes = [p, i64, i64, i32, p, p, p, p]
+        l.tq_quantize_pack2.restype = i32
+        l.tq_unpack2.argtypes = [p, i64, i64, i32, p, p, p]
+        l.tq_unpack2.restype = i32
+        l.tq_gemv2.argtypes = [p, p, p, i64, i64, i32, p, p, p]
+        l.tq_gemv2.restype = i32
+        l.tq_gemv2_batched.argtypes = [i32, p, p, p, p, i64, i64, i32, p, p]
+        l.tq_gemv2_batched.restype = i32
         l.tq_unpack_batched.argtypes = [i32, p, i64, i64, i32, p, p, p]
         l.tq_unpack_batched.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
@@ -197,6 +206,61 @@ def unpack_batched(packeds, N: int, K: int, G: int, status=None):
     _rc(lib().tq_unpack_batched(len(packeds), _ptrs(packeds), N, K, G, _ptrs(codes), _st(status),
                                 _stream()), "tq_unpack_batched")
     return codes
+
+
+def quantize_pack2(w: torch.Tensor, G: int, status=None):
+    """2-bit format: w [N,K] bf16 -> (packed2 uint8 [N, K/4], scales fp16 [N, K/G])."""
+    _dev(w, "w", (torch.bfloat16, torch.int16), 2)
+    N, K = w.shape
+    packed = torch.empty((N, max(K // 4, 1)), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=w.device)
+    _rc(lib().tq_quantize_pack2(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
+                                _st(status), _stream()), "tq_quantize_pack2")
+    return packed, scales
+
+
+def unpack2(packed: torch.Tensor, N: int, K: int, G: int, status=None):
+    """2-bit packed [N, K/4] -> codes int8 [N,K]."""
+    _dev(packed, "packed", (torch.uint8,), packed.dim())
+    if packed.numel() * 4 != N * K:
+        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), N * K // 4))
+    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _rc(lib().tq_unpack2(packed.data_ptr(), N, K, G, codes.data_ptr(), _st(status), _stream()),
+        "tq_unpack2")
+    return codes
+
+
+def gemv2(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int,
+          status=None, out=None):
+    """2-bit format, M = 1: x [1,K] bf16 -> y fp32 [1,N]."""
+    _dev(x, "x", (torch.bfloat16, torch.int16), 2)
+    _dev(packed, "packed", (torch.uint8,), packed.dim())
+    _dev(scales, "scales", (torch.float16, torch.int16), scales.dim())
+    if tuple(x.shape) != (1, K) or packed.numel() * 4 != N * K or scales.numel() != N * (K // G):
+        raise TQError("gemv2: shapes do not match N=%d K=%d G=%d" % (N, K, G))
+    y = torch.empty((1, N), dtype=torch.float32, device=x.device) if out is None else out
+    _rc(lib().tq_gemv2(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K, G, y.data_ptr(),
+                       _st(status), _stream()), "tq_gemv2")
+    return y
+
+
+def gemv2_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """2-bit format, M = 1, same-shaped problems: list of y fp32 [1,N], one launch per 64."""
+    n = len(xs)
+    if len(packeds) != n or len(scales_list) != n:
+        raise TQError("xs, packeds and scales differ in length")
+    for x, pk, sc in zip(xs, packeds, scales_list):
+        _dev(x, "x", (torch.bfloat16, torch.int16), 2)
+        _dev(pk, "packed", (torch.uint8,), pk.dim())
+        _dev(sc, "scales", (torch.float16, torch.int16), sc.dim())
+        if (tuple(x.shape) != (1, K) or pk.numel() * 4 != N * K or G <= 0
+                or sc.numel() != N * (K // G)):
+            raise TQError("gemv2_batched: shapes do not match N=%d K=%d G=%d" % (N, K, G))
+    if outs is None:
+        outs = [torch.empty((1, N), dtype=torch.float32, device=x.device) for x in xs]
+    _rc(lib().tq_gemv2_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
+                               N, K, G, _st(status), _stream()), "tq_gemv2_batched")
+    return outs
 
 
 class FakeQuantize(torch.autograd.Function):

@@ -91,7 +91,7 @@ int tq_quantize_pack_batched(int count, const uint16_t *const *ws, int64_t N, in
   }
   (void)hipGetLastError();
   tq::launch_quant_batched(count, ws, N, K, G, packeds, scales, nullptr, d_status,
-                           (hipStream_t)stream);
+                           (hipStream_t)stream, false);
   return finish_launch();
 }
 
@@ -111,7 +111,7 @@ int tq_fake_quantize_batched(int count, const uint16_t *const *ws, int64_t N, in
   }
   (void)hipGetLastError();
   tq::launch_quant_batched(count, ws, N, K, G, nullptr, scales, w_hats, d_status,
-                           (hipStream_t)stream);
+                           (hipStream_t)stream, false);
   return finish_launch();
 }
 
@@ -171,6 +171,57 @@ int tq_dequantize_batched(int count, const uint8_t *const *packeds,
   tq::launch_dequantize_batched(count, packeds, scales, w_hats, N, K, G, d_status,
                                 (hipStream_t)stream);
   return finish_launch();
+}
+
+int tq_quantize_pack2(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,
+                      uint16_t *scales, int32_t *d_status, void *stream) {
+  if (!w || !packed || !scales) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(w, 16) || !aligned(packed, 2) || !aligned(scales, 2) || !aligned(d_status, 4))
+    return TQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  tq::launch_quant_batched(1, &w, N, K, G, &packed, &scales, nullptr, d_status,
+                           (hipStream_t)stream, true);
+  return finish_launch();
+}
+
+int tq_unpack2(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
+               int32_t *d_status, void *stream) {
+  if (!packed || !codes) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(packed, 4) || !aligned(codes, 16) || !aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  tq::launch_unpack2(packed, N, K, G, codes, d_status, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                     const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
+                     int G, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !ys) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!tq::gemv2_supported(N, K, G)) return TQ_ERR_SHAPE;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
+        !aligned(ys[i], 4))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_gemv2_batched(count, xs, packeds, scales, ys, N, K, G, d_status,
+                           (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemv2(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t N,
+             int64_t K, int G, float *y, int32_t *d_status, void *stream) {
+  return tq_gemv2_batched(1, &x, &packed, &scales, &y, N, K, G, d_status, stream);
 }
 
 int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,

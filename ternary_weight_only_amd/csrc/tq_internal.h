@@ -25,9 +25,21 @@ constexpr int kQuantMaxBatch = 64;
 // count same-shaped problems: quantize + pack (w_hats == nullptr) or the QAT
 // forward (w_hats given; packeds unused; scales may be nullptr, or hold
 // nullptr entries, to skip them).
+// two_bit: pack 2-bit fields (four codes a byte, G/4 bytes a group) instead
+// of base-3 bytes.
 void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
                           uint8_t *const *packeds, uint16_t *const *scales,
-                          uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream);
+                          uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream,
+                          bool two_bit);
+
+// 2-bit format (tq_twobit.hip): codes, and the M = 1 decode GEMV of up to
+// kQuantMaxBatch same-shaped problems a launch (K/64 <= 64).
+void launch_unpack2(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
+                    int32_t *d_status, hipStream_t stream);
+bool gemv2_supported(int64_t N, int64_t K, int G);
+void launch_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                          const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
+                          int G, int32_t *d_status, hipStream_t stream);
 
 void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
                            int8_t *const *codes, int32_t *d_status, hipStream_t stream);

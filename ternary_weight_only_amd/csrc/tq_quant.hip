@@ -162,7 +162,10 @@ struct QuantBatch {
   uint16_t *w_hat[kQuantMaxBatch];
 };
 
-template <int G, bool FAKE>
+// MODE: kPack3 (base-3 bytes), kFake (QAT forward), kPack2 (2-bit fields).
+constexpr int kPack3 = 0, kFake = 1, kPack2 = 2;
+
+template <int G, int MODE>
 __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch args,
                                                                int64_t total_groups,
                                                                int32_t *__restrict__ d_status) {
@@ -342,7 +345,22 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
       dig |= (uint64_t)d << (8 * i);
     }
 
-    if constexpr (FAKE) {
+    if constexpr (MODE == kPack2) {
+      // four 2-bit fields d = c + 1 a byte, first weight lowest: this lane's
+      // 8 weights are 2 bytes of the group's G/4
+      uint32_t v = 0;
+#pragma unroll
+      for (int i = 0; i < 8; ++i) v |= (uint32_t)((dig >> (8 * i)) & 3u) << (2 * i);
+      if (active) {
+        *reinterpret_cast<uint16_t *>(packed + gi * (G / 4) + sub * 2) = (uint16_t)v;
+        if (sub == 0) {
+          scales[gi] = (uint16_t)sbits;
+          if (flags && d_status) atomicOr(d_status, flags);
+        }
+      }
+      continue;
+    }
+    if constexpr (MODE == kFake) {
       // w_hat of the 8 weights: a pair takes bytes 2d, 2d+1 of {hi, lo}
       // per digit d (0..1 is -s, 2..3 +0, 4..5 +s); a flagged group is +0
       const uint32_t sb = flags ? 0u : bf16_of_f16(sbits);
@@ -493,7 +511,8 @@ int grid_for(int64_t work_items, int64_t per_block, int64_t cap) {
 // problem gets the same number of blocks (at most kMaxBlocks in a launch).
 void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
                           uint8_t *const *packeds, uint16_t *const *scales,
-                          uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream) {
+                          uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream,
+                          bool two_bit) {
   const int64_t total_groups = N * (K / G);
   const int64_t nchunks = (total_groups * G + 511) / 512;
   const bool fake = w_hats != nullptr;
@@ -507,32 +526,39 @@ void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64
       a.w_hat[i] = fake ? w_hats[c0 + i] : nullptr;
     }
     const dim3 grid(grid_for(nchunks, kWavesPerBlock, kMaxBlocks / n), n);
+    const int mode = fake ? kFake : (two_bit ? kPack2 : kPack3);
     if (G == 64) {
-      if (fake)
-        hipLaunchKernelGGL((quantize_pack_kernel<64, true>), grid, dim3(kBlock), 0, stream, a,
+      if (mode == kFake)
+        hipLaunchKernelGGL((quantize_pack_kernel<64, kFake>), grid, dim3(kBlock), 0, stream, a,
+                           total_groups, d_status);
+      else if (mode == kPack2)
+        hipLaunchKernelGGL((quantize_pack_kernel<64, kPack2>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
       else
-        hipLaunchKernelGGL((quantize_pack_kernel<64, false>), grid, dim3(kBlock), 0, stream, a,
+        hipLaunchKernelGGL((quantize_pack_kernel<64, kPack3>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
     } else {
-      if (fake)
-        hipLaunchKernelGGL((quantize_pack_kernel<128, true>), grid, dim3(kBlock), 0, stream, a,
+      if (mode == kFake)
+        hipLaunchKernelGGL((quantize_pack_kernel<128, kFake>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
+      else if (mode == kPack2)
+        hipLaunchKernelGGL((quantize_pack_kernel<128, kPack2>), grid, dim3(kBlock), 0, stream,
+                           a, total_groups, d_status);
       else
-        hipLaunchKernelGGL((quantize_pack_kernel<128, false>), grid, dim3(kBlock), 0, stream, a,
-                           total_groups, d_status);
+        hipLaunchKernelGGL((quantize_pack_kernel<128, kPack3>), grid, dim3(kBlock), 0, stream,
+                           a, total_groups, d_status);
     }
   }
 }
 
 void launch_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,
                           uint16_t *scales, int32_t *d_status, hipStream_t stream) {
-  launch_quant_batched(1, &w, N, K, G, &packed, &scales, nullptr, d_status, stream);
+  launch_quant_batched(1, &w, N, K, G, &packed, &scales, nullptr, d_status, stream, false);
 }
 
 void launch_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w_hat,
                           uint16_t *scales, int32_t *d_status, hipStream_t stream) {
-  launch_quant_batched(1, &w, N, K, G, nullptr, &scales, &w_hat, d_status, stream);
+  launch_quant_batched(1, &w, N, K, G, nullptr, &scales, &w_hat, d_status, stream, false);
 }
 
 template <int G, int U>

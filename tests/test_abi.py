@@ -25,7 +25,7 @@ def _lib():
 def declared_functions():
     text = open(HEADER).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
-    return sorted(set(re.findall(r"\b(tq_[a-z_]+)\s*\(", text)))
+    return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
 
 
 def test_header_declares_the_four_entry_points():
@@ -202,6 +202,38 @@ def test_dequantize_batched_argument_errors():
     assert d(2, good, good, ps(FAKE, FAKE + 8), 4, 128, 64, None, None) == -4
     assert d(2, good, ps(FAKE + 1, FAKE), good, 4, 128, 64, None, None) == -4
     assert d(2, good, good, good, 4, 128, 64, FAKE + 1, None) == -4
+
+
+def test_two_bit_argument_errors():
+    import ctypes
+    lib = _lib()
+    q, u, g = lib.tq_quantize_pack2, lib.tq_unpack2, lib.tq_gemv2
+    assert q(None, 4, 128, 64, FAKE, FAKE, None, None) == -1
+    assert q(FAKE, 4, 128, 64, None, FAKE, None, None) == -1
+    assert q(FAKE, 4, 128, 64, FAKE, None, None, None) == -1
+    assert q(FAKE, 4, 130, 64, FAKE, FAKE, None, None) == -2
+    assert q(FAKE, 4, 128, 32, FAKE, FAKE, None, None) == -3
+    assert q(FAKE + 8, 4, 128, 64, FAKE, FAKE, None, None) == -4
+    assert q(FAKE, 4, 128, 64, FAKE + 1, FAKE, None, None) == -4
+    assert u(None, 4, 128, 64, FAKE, None, None) == -1
+    assert u(FAKE, 0, 128, 64, FAKE, None, None) == -2
+    assert u(FAKE + 2, 4, 128, 64, FAKE, None, None) == -4
+    assert u(FAKE, 4, 128, 64, FAKE + 8, None, None) == -4
+    assert g(None, FAKE, FAKE, 4, 128, 64, FAKE, None, None) == -1
+    assert g(FAKE, FAKE, FAKE, 4, 8192, 64, FAKE, None, None) == -2   # K/64 > 64
+    assert g(FAKE, FAKE, FAKE, 4, 128, 96, FAKE, None, None) == -3
+    assert g(FAKE, FAKE + 4, FAKE, 4, 128, 64, FAKE, None, None) == -4
+    assert g(FAKE + 8, FAKE, FAKE, 4, 128, 64, FAKE, None, None) == -4
+    assert g(FAKE, FAKE, FAKE, 4, 128, 64, FAKE + 2, None, None) == -4
+    arr = ctypes.c_void_p * 2
+    good = arr(FAKE, FAKE + 4096)
+    b = lib.tq_gemv2_batched
+    assert b(0, None, None, None, None, 4, 128, 64, None, None) == 0
+    assert b(-1, good, good, good, good, 4, 128, 64, None, None) == -2
+    assert b(2, good, None, good, good, 4, 128, 64, None, None) == -1
+    assert b(2, good, good, arr(FAKE, None), good, 4, 128, 64, None, None) == -1
+    assert b(2, good, arr(FAKE, FAKE + 8), good, good, 4, 128, 64, None, None) == -4
+    assert b(2, good, good, good, good, 4, 128, 64, FAKE + 1, None) == -4
 
 
 def test_product_path_does_not_import_oracle():
