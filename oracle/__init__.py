@@ -73,6 +73,12 @@ def _load():
         lib.oracle_unpack2.restype = ctypes.c_int
         lib.oracle_matmul2.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
         lib.oracle_matmul2.restype = ctypes.c_int
+        lib.oracle_w4_unpack.argtypes = [p, i64, i64, p]
+        lib.oracle_w4_unpack.restype = ctypes.c_int
+        lib.oracle_w4a16_dequantize.argtypes = [p, p, p, i64, i64, i64, p]
+        lib.oracle_w4a16_dequantize.restype = ctypes.c_int
+        lib.oracle_w4a16_matmul.argtypes = [p, p, p, p, i64, i64, i64, i64, p, p]
+        lib.oracle_w4a16_matmul.restype = ctypes.c_int
         _lib = lib
     return _lib
 
@@ -236,3 +242,55 @@ def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K
     if rc:
         raise OracleError("oracle_matmul rc=%d" % rc)
     return y, bound, int(st[0])
+
+
+# W4A16 (tiny-llm "Week 2 Day 3: Quantize the Model": "Group-Wise Affine
+# Quantization", "Reconstruct a Stored Group", "Packed Storage Layout",
+# "Computation Flow").  packed: uint32 [N, K/8], weight 8p + i in bits
+# 4i..4i+3 of word p; scales, biases: bf16 bits [N, K/G]; w_hat = q*s + b.
+
+def w4_unpack(packed: np.ndarray, N: int, K: int) -> np.ndarray:
+    """uint32 [N, K/8] -> unsigned codes uint8 [N, K]."""
+    p = np.ascontiguousarray(packed, dtype=np.uint32)
+    if p.size * 8 != N * K:
+        raise OracleError("bad packed size")
+    codes = np.empty((N, K), np.uint8)
+    rc = _load().oracle_w4_unpack(_ptr(p), N, K, _ptr(codes))
+    if rc:
+        raise OracleError("oracle_w4_unpack rc=%d" % rc)
+    return codes
+
+
+def w4a16_dequantize(packed, scales, biases, N: int, K: int, G: int) -> np.ndarray:
+    """-> w_hat float64 [N, K] = q*s + b."""
+    p = np.ascontiguousarray(packed, dtype=np.uint32)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    b = np.ascontiguousarray(biases, dtype=np.uint16)
+    if p.size * 8 != N * K or G <= 0 or s.size != N * (K // G) or b.size != s.size:
+        raise OracleError("bad packed/scales/biases sizes")
+    w = np.empty((N, K), np.float64)
+    rc = _load().oracle_w4a16_dequantize(_ptr(p), _ptr(s), _ptr(b), N, K, G, _ptr(w))
+    if rc:
+        raise OracleError("oracle_w4a16_dequantize rc=%d" % rc)
+    return w
+
+
+def w4a16_matmul(x_bits, packed, scales, biases, N: int, K: int, G: int):
+    """x bf16 bits [M,K] -> (y float64 [M,N], bound float64 [M,N] =
+    sum_k |x| (|q s| + |b|))."""
+    x = np.ascontiguousarray(x_bits, dtype=np.uint16)
+    if x.ndim != 2 or x.shape[1] != K:
+        raise ValueError("x must be [M,K]")
+    M = x.shape[0]
+    p = np.ascontiguousarray(packed, dtype=np.uint32)
+    s = np.ascontiguousarray(scales, dtype=np.uint16)
+    b = np.ascontiguousarray(biases, dtype=np.uint16)
+    if p.size * 8 != N * K or G <= 0 or s.size != N * (K // G) or b.size != s.size:
+        raise OracleError("bad packed/scales/biases sizes")
+    y = np.empty((M, N), np.float64)
+    bound = np.empty((M, N), np.float64)
+    rc = _load().oracle_w4a16_matmul(_ptr(x), _ptr(p), _ptr(s), _ptr(b), M, N, K, G, _ptr(y),
+                                     _ptr(bound))
+    if rc:
+        raise OracleError("oracle_w4a16_matmul rc=%d" % rc)
+    return y, bound

@@ -17,7 +17,9 @@
  *  [P2] tiny-llm "Week 2 Day 3: Quantize the Model", sections
  *       "Mathematical Formulation" and "Computation Flow" (per-group
  *       factoring of the scale out of the inner sum; fp32-or-wider
- *       accumulator per output element).
+ *       accumulator per output element); for the W4A16 functions at the
+ *       end also "Group-Wise Affine Quantization", "Reconstruct a Stored
+ *       Group" and "Packed Storage Layout".
  *
  * Readings where the pages leave a step open (all listed in the design doc):
  *  - digit = code + 1 and the first weight of five is the least significant
@@ -620,4 +622,107 @@ int oracle_matmul2(const uint16_t *x, const uint8_t *packed, const uint16_t *sca
                    double *y, double *bound, int32_t *status)
 {
     return matmul_rows(x, packed, scales, M, N, K, G, 1, y, bound, status);
+}
+
+
+/* ------------------------------------------------------------------------ */
+/* W4A16: group-wise affine int4 weights ([P2] "Group-Wise Affine          */
+/* Quantization", "Reconstruct a Stored Group", "Packed Storage Layout",   */
+/* "Computation Flow").  Layout:                                            */
+/*   packed [N][K/8] uint32, weight 8p + i in bits 4i..4i+3 of word p        */
+/*   scales, biases [N][K/G] bf16 bits; w_hat = q * s + b, q in [0, 15]      */
+/* The page defines no quantizer (the stored codes and parameters are used  */
+/* as they are), so there is none here.                                     */
+/* ------------------------------------------------------------------------ */
+
+static int check_w4(int64_t N, int64_t K, int64_t G)
+{
+    if (N < 1 || K < 1 || G < 8 || G % 8 || K % G) return OR_ERR_SHAPE;
+    return OR_OK;
+}
+
+/* The unsigned 4-bit code of weight k of a row (eight codes a word, the
+ * first in the lowest four bits). */
+static int w4_code(const uint32_t *row, int64_t k)
+{
+    return (int)((row[k / 8] >> (4 * (k % 8))) & 0xFu);
+}
+
+/* codes[N][K] = the unpacked unsigned codes. */
+int oracle_w4_unpack(const uint32_t *packed, int64_t N, int64_t K, uint8_t *codes)
+{
+    if (!packed || !codes) return OR_ERR_NULL;
+    if (N < 1 || K < 1 || K % 8) return OR_ERR_SHAPE;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) codes[n * K + k] = (uint8_t)w4_code(packed + n * (K / 8), k);
+    return OR_OK;
+}
+
+/* bf16 bits -> double, non-finite values included (exact). */
+static double bf16_any_to_double(uint16_t b)
+{
+    uint32_t u = (uint32_t)b << 16;
+    float f;
+    memcpy(&f, &u, sizeof f);
+    return (double)f;
+}
+
+/* w_hat[N][K] = q * s + b in fp64.  q * s is exact (4 x 8 significant bits);
+ * the sum with b is exact unless the exponents of q*s and b lie more than
+ * about 40 binades apart. */
+int oracle_w4a16_dequantize(const uint32_t *packed, const uint16_t *scales,
+                            const uint16_t *biases, int64_t N, int64_t K, int64_t G,
+                            double *w_hat)
+{
+    if (!packed || !scales || !biases || !w_hat) return OR_ERR_NULL;
+    int rc = check_w4(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G;
+    for (int64_t n = 0; n < N; ++n)
+        for (int64_t k = 0; k < K; ++k) {
+            const double s = bf16_any_to_double(scales[n * nG + k / G]);
+            const double b = bf16_any_to_double(biases[n * nG + k / G]);
+            w_hat[n * K + k] = (double)w4_code(packed + n * (K / 8), k) * s + b;
+        }
+    return OR_OK;
+}
+
+/*
+ * y[m][n] = sum_k x[m][k] * (q[n][k] * s[n][k/G] + b[n][k/G]), taken in the
+ * page's order: group by group, word by word, code by code, one
+ * reconstructed weight times one activation added to one accumulator
+ * (fp64 here, where the page asks for a float accumulator).
+ * bound[m][n] = sum_k |x[m][k]| * (|q s| + |b|): the size of the terms of
+ * the factored form s * sum(x q) + b * sum(x) that a kernel may evaluate.
+ */
+int oracle_w4a16_matmul(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                        const uint16_t *biases, int64_t M, int64_t N, int64_t K, int64_t G,
+                        double *y, double *bound)
+{
+    if (!x || !packed || !scales || !biases || !y || !bound) return OR_ERR_NULL;
+    int rc = check_w4(N, K, G);
+    if (rc) return rc;
+    if (M < 1) return OR_ERR_SHAPE;
+    const int64_t nG = K / G;
+    for (int64_t m = 0; m < M; ++m)
+        for (int64_t n = 0; n < N; ++n) {
+            const uint32_t *row = packed + n * (K / 8);
+            double acc = 0.0, bacc = 0.0;
+            for (int64_t g = 0; g < nG; ++g) {
+                const double s = bf16_any_to_double(scales[n * nG + g]);
+                const double b = bf16_any_to_double(biases[n * nG + g]);
+                for (int64_t p = 0; p < G / 8; ++p) {
+                    const uint32_t word = row[g * (G / 8) + p];
+                    for (int i = 0; i < 8; ++i) {
+                        const double q = (double)((word >> (4 * i)) & 0xFu);
+                        const double a = bf16_any_to_double(x[m * K + g * G + 8 * p + i]);
+                        acc += a * (q * s + b);
+                        bacc += fabs(a) * (fabs(q * s) + fabs(b));
+                    }
+                }
+            }
+            y[m * N + n] = acc;
+            bound[m * N + n] = bacc;
+        }
+    return OR_OK;
 }

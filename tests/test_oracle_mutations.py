@@ -17,6 +17,7 @@ import oracle
 from tests import test_oracle_format as fmt
 from tests import test_oracle_matmul as mm
 from tests import test_oracle_scale as sc
+from tests import test_oracle_w4a16 as w4
 
 SRC = os.path.join(os.path.dirname(oracle.__file__), "tq_oracle.c")
 GOLDEN = os.path.join(os.path.dirname(os.path.abspath(__file__)), "golden")
@@ -39,6 +40,17 @@ MUTATIONS = {
                                   "wrow[g * G + j] = (double)crow[g * G + j] * f16_to_double(scales[n * nG]);"),
     "x_transposed": ("const double *xm = xd + m * K;", "const double *xm = xd + m;"),
     "bound_not_absolute": ("bacc += fabs(t);", "bacc += t;"),
+    "w4_nibbles_high_first": ("return (int)((row[k / 8] >> (4 * (k % 8))) & 0xFu);",
+                              "return (int)((row[k / 8] >> (4 * (7 - k % 8))) & 0xFu);"),
+    "w4_matmul_nibbles_high_first": ("const double q = (double)((word >> (4 * i)) & 0xFu);",
+                                     "const double q = (double)((word >> (4 * (7 - i))) & 0xFu);"),
+    "w4_bias_dropped": ("acc += a * (q * s + b);", "acc += a * (q * s);"),
+    "w4_first_group_parameters_only": (
+        "const double s = bf16_any_to_double(scales[n * nG + g]);",
+        "const double s = bf16_any_to_double(scales[n * nG]);"),
+    "w4_bound_without_bias": ("bacc += fabs(a) * (fabs(q * s) + fabs(b));",
+                              "bacc += fabs(a) * fabs(q * s);"),
+    "w4_activation_off_by_one_word": ("x[m * K + g * G + 8 * p + i]", "x[m * K + g * G + 8 * (p ^ 1) + i]"),
 }
 
 PINS = [
@@ -57,17 +69,26 @@ PINS = [
     lambda: mm.test_matmul_vs_exact_rationals(3, 320, 64, 2),
     mm.test_matmul_vs_numpy_matmul,
     mm.test_one_hot_rows_exact,
+    lambda: w4.test_packing_layout_fixture(GOLDEN),
+    lambda: w4.test_orientation_example(GOLDEN),
+    lambda: w4.test_matmul_vs_factored_form(17, 1024, 128, 2),
+    w4.test_nonnegative_terms_bound_equals_y,
 ]
 
 
-def _load_variant(path):
+FUNCTIONS = ("oracle_packed_row_bytes", "oracle_quantize_pack", "oracle_unpack", "oracle_matmul",
+             "oracle_dequantize", "oracle_fake_quantize", "oracle_quantize_pack2",
+             "oracle_unpack2", "oracle_matmul2", "oracle_w4_unpack", "oracle_w4a16_dequantize",
+             "oracle_w4a16_matmul")
+
+
+def _load_variant(path, real):
+    """The mutated library, with every function's signature copied from the
+    real oracle's."""
     lib = ctypes.CDLL(path)
-    i64, p = ctypes.c_int64, ctypes.c_void_p
-    lib.oracle_packed_row_bytes.argtypes = [i64, i64]
-    lib.oracle_packed_row_bytes.restype = i64
-    lib.oracle_quantize_pack.argtypes = [p, i64, i64, i64, p, p, p]
-    lib.oracle_unpack.argtypes = [p, i64, i64, i64, p, p]
-    lib.oracle_matmul.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p]
+    for f in FUNCTIONS:
+        getattr(lib, f).argtypes = getattr(real, f).argtypes
+        getattr(lib, f).restype = getattr(real, f).restype
     return lib
 
 
@@ -83,7 +104,7 @@ def test_planted_mistake_is_caught(name):
         open(c, "w").write(src.replace(old, new))
         subprocess.check_call(["gcc", "-O1", "-std=c11", "-w", "-fPIC", "-shared", "-o", so, c, "-lm"])
         saved = oracle._load()
-        oracle._lib = _load_variant(so)
+        oracle._lib = _load_variant(so, saved)
         failures = 0
         try:
             for pin in PINS:
