@@ -33,6 +33,14 @@ weights to their bf16 ternarized values, two launches a pass) runs eight passes
 back to back between two HIP events (median of three chains); its row counts
 2 bytes read and 2 written per weight.
 
+Also outside the step, two other weight formats run the decode GEMV through
+the same 72 shapes, each over eight ring-slot copies back to back between two
+HIP events (median of three chains): the 2-bit ternary format (the same
+scales and codes, four codes a byte; tq_gemv2_batched, two launches a pass)
+and W4A16 (seeded stored 4-bit affine codes with bf16 scales and biases;
+tq_w4a16_gemv_batched, two launches a pass).  Their rows count code plus
+scale (and bias) bytes.
+
 The roofline entry times the GEMV kernel itself: after the timed steps, the
 decode pass runs over all eight slots back to back (8 launches, so each
 launch's dispatch overlaps the previous kernel) between two HIP events, and
@@ -355,6 +363,54 @@ def main():
     packed2_bytes = sum(N * K // 4 + 2 * N * (K // G) for N, K in shapes)
     del P2s, g2_calls
 
+    # W4A16 decode GEMV, outside the step: stored 4-bit affine parameters of
+    # the same 72 shapes (seeded, both scale orientations), each ring slot a
+    # copy, one batched call per shape and slot, all slots back to back
+    W4 = {}
+    for i, (N, K) in enumerate(shapes):
+        pk, sc, bi = inputs.w4a16_problem(5000 + i, N, K, G)
+        W4[i] = tuple(torch.from_numpy(a.view(np.int32 if a.dtype == np.uint32 else np.int16))
+                      .to(dev) for a in (pk, sc, bi))
+    y4 = [torch.empty(1, N, dtype=torch.bfloat16, device=dev) for N, K in shapes]
+    W4s = {slot: {i: tuple(t.clone() for t in W4[i]) for i in W4} for slot in range(RING)}
+    w4_calls = {slot: [(N, K, len(idx), ptrs([x_dec[i] for i in idx]),
+                        ptrs([W4s[slot][i][0] for i in idx]), ptrs([W4s[slot][i][1] for i in idx]),
+                        ptrs([W4s[slot][i][2] for i in idx]), ptrs([y4[i] for i in idx]))
+                       for (N, K), idx in groups.items()] for slot in range(RING)}
+
+    def run_w4(slot, stream):
+        for N, K, n, ax, ap, asc, abi, ay in w4_calls[slot]:
+            rc = L.tq_w4a16_gemv_batched(n, ax, ap, asc, abi, ay, N, K, G, stream)
+            assert rc == 0, rc
+
+    with torch.cuda.stream(stream):
+        run_w4(0, sp)
+    torch.cuda.synchronize()
+    # sampled rows of two matrices against the oracle, to the W4A16 bar
+    for i in (0, 71):
+        N, K = shapes[i]
+        rows = np.array([0, N // 2, N - 1])
+        pk, sc, bi = (t.cpu().numpy() for t in W4[i])
+        xb = x_dec[i].cpu().view(torch.int16).numpy().view(np.uint16)
+        y_ref, bd = oracle.w4a16_matmul(xb, pk.view(np.uint32)[rows], sc.view(np.uint16)[rows],
+                                        bi.view(np.uint16)[rows], len(rows), K, G)
+        yg = y4[i].float().cpu().numpy()[0, rows].astype(np.float64)
+        tol = 1e-3 * bd[0] * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref[0])
+        assert (np.abs(yg - y_ref[0]) <= tol).all(), "W4A16 GEMV differs from the oracle"
+    w4 = []
+    with torch.cuda.stream(stream):
+        for rep in range(4):
+            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
+            e0.record(stream)
+            for slot in range(RING):
+                run_w4(slot, sp)
+            e1.record(stream)
+            w4.append((e0, e1))
+    torch.cuda.synchronize()
+    w4_ms = sorted(a.elapsed_time(b) for a, b in w4[1:])[1] / RING
+    w4_bytes = sum(N * K // 2 + 4 * N * (K // G) for N, K in shapes)
+    del W4, W4s, w4_calls
+
     # QAT forward (fake quantization), outside the step: every bf16 matrix to
     # its bf16 w_hat (72 direct launches a pass), eight passes per chain
     fq_calls = [(N, K, len(idx), ptrs([w_dev[i] for i in idx]), ptrs([w_hat[i] for i in idx]))
@@ -422,6 +478,11 @@ def main():
                              "Tweights/s": weights / (g2_ms * 1e-3) / 1e12,
                              "bytes_per_pass": packed2_bytes, "launches": len(groups),
                              "in_step": False},
+        "decode_gemv_w4a16": {"ms": w4_ms, "GB/s": w4_bytes / (w4_ms * 1e-3) / 1e9,
+                              "frac_hbm": w4_bytes / (w4_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                              "Tweights/s": weights / (w4_ms * 1e-3) / 1e12,
+                              "bytes_per_pass": w4_bytes, "launches": len(groups),
+                              "in_step": False},
         "qat_forward": {"ms": fq_ms, "GB/s": 4 * weights / (fq_ms * 1e-3) / 1e9,
                         "frac_hbm": 4 * weights / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                         "bytes_per_pass": 4 * weights, "launches": len(groups),

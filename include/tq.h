@@ -354,6 +354,37 @@ int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const 
                      const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
                      int G, int32_t *d_status, void *stream);
 
+/*
+ * W4A16: group-wise affine 4-bit weights, bf16 activations and output
+ * (tiny-llm "Week 2 Day 3: Quantize the Model": "Group-Wise Affine
+ * Quantization", "Reconstruct a Stored Group", "Packed Storage Layout",
+ * "Mathematical Formulation", "Computation Flow").
+ *   x       [1,K] bf16, 16-byte aligned
+ *   packed  [N, K/8] uint32, 16-byte aligned: weight 8p + i of a row in bits
+ *           4i..4i+3 of its word p; codes q in [0, 15]
+ *   scales, biases  [N, K/G] bf16, 2-byte aligned; either sign of scale
+ *   y       [1,N] bf16, 2-byte aligned, overwritten
+ *   y[n] = bf16_RNE( sum_k x[k] * (q[n,k] * s[n,k/G] + b[n,k/G]) ), the sum
+ *   taken in fp32 as s * sum(x q) + b * sum(x) per group.
+ * G is 64 or 128 (TQ_ERR_GROUP otherwise); K <= 4096 (K/64 <= 64) and
+ * N < 2^28, else TQ_ERR_SHAPE.  No data errors exist in this format: every
+ * code is valid, and Inf/NaN parameters or activations propagate to y.
+ * Deterministic.  Accuracy: |y - y_exact| <= 1e-3 * sum_k |x| (|q s| + |b|)
+ * before the final bf16 rounding.
+ */
+int tq_w4a16_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                  const uint16_t *biases, int64_t N, int64_t K, int G, uint16_t *y,
+                  void *stream);
+
+/* Batched form: `count` same-shaped problems, each as tq_w4a16_gemv on
+ * xs[i], packeds[i], scales[i], biases[i], ys[i] (HOST arrays of DEVICE
+ * pointers, read during the call only), one launch per 64.  Errors as
+ * tq_w4a16_gemv; a NULL or misaligned pointer in any entry rejects the
+ * whole call. */
+int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
+                          const uint16_t *const *scales, const uint16_t *const *biases,
+                          uint16_t *const *ys, int64_t N, int64_t K, int G, void *stream);
+
 #ifdef __cplusplus
 }
 #endif

@@ -45,6 +45,8 @@ from .binding import (  # noqa: F401
     gemv_grouped,
     gemv2,
     gemv2_batched,
+    w4a16_gemv,
+    w4a16_gemv_batched,
     lib,
     new_status,
     packed_bytes,

@@ -23,7 +23,7 @@ DEV_BAD_PADDING = 8
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
            "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
            "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_unpack2",
-           "tq_gemv2", "tq_gemv2_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_gemv2", "tq_gemv2_batched", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -60,6 +60,10 @@ def lib() -> ctypes.CDLL:
         l.tq_gemv2.restype = i32
         l.tq_gemv2_batched.argtypes = [i32, p, p, p, p, i64, i64, i32, p, p]
         l.tq_gemv2_batched.restype = i32
+        l.tq_w4a16_gemv.argtypes = [p, p, p, p, i64, i64, i32, p, p]
+        l.tq_w4a16_gemv.restype = i32
+        l.tq_w4a16_gemv_batched.argtypes = [i32, p, p, p, p, p, i64, i64, i32, p]
+        l.tq_w4a16_gemv_batched.restype = i32
         l.tq_unpack_batched.argtypes = [i32, p, i64, i64, i32, p, p, p]
         l.tq_unpack_batched.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
@@ -260,6 +264,44 @@ def gemv2_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None,
         outs = [torch.empty((1, N), dtype=torch.float32, device=x.device) for x in xs]
     _rc(lib().tq_gemv2_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
                                N, K, G, _st(status), _stream()), "tq_gemv2_batched")
+    return outs
+
+
+def _w4_check(x, packed, scales, biases, N, K, G):
+    _dev(x, "x", (torch.bfloat16, torch.int16), 2)
+    _dev(packed, "packed", (torch.int32, torch.uint32), packed.dim())
+    _dev(scales, "scales", (torch.bfloat16, torch.int16), scales.dim())
+    _dev(biases, "biases", (torch.bfloat16, torch.int16), biases.dim())
+    if (tuple(x.shape) != (1, K) or packed.numel() * 8 != N * K or G <= 0
+            or scales.numel() != N * (K // G) or biases.numel() != scales.numel()):
+        raise TQError("w4a16: shapes do not match N=%d K=%d G=%d" % (N, K, G))
+
+
+def w4a16_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+               biases: torch.Tensor, N: int, K: int, G: int, out=None):
+    """W4A16, M = 1: x [1,K] bf16, packed int32/uint32 [N, K/8], scales and
+    biases bf16 [N, K/G] -> y bf16 [1,N]."""
+    _w4_check(x, packed, scales, biases, N, K, G)
+    y = torch.empty((1, N), dtype=torch.bfloat16, device=x.device) if out is None else out
+    _rc(lib().tq_w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                            biases.data_ptr(), N, K, G, y.data_ptr(), _stream()),
+        "tq_w4a16_gemv")
+    return y
+
+
+def w4a16_gemv_batched(xs, packeds, scales_list, biases_list, N: int, K: int, G: int,
+                       outs=None):
+    """Same-shaped W4A16 problems -> list of y bf16 [1,N], one launch per 64."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(biases_list) == n):
+        raise TQError("xs, packeds, scales and biases differ in length")
+    for x, pk, sc, bi in zip(xs, packeds, scales_list, biases_list):
+        _w4_check(x, pk, sc, bi, N, K, G)
+    if outs is None:
+        outs = [torch.empty((1, N), dtype=torch.bfloat16, device=x.device) for x in xs]
+    _rc(lib().tq_w4a16_gemv_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
+                                    _ptrs(biases_list), _ptrs(outs), N, K, G, _stream()),
+        "tq_w4a16_gemv_batched")
     return outs
 
 

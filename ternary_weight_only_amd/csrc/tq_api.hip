@@ -224,6 +224,33 @@ int tq_gemv2(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, i
   return tq_gemv2_batched(1, &x, &packed, &scales, &y, N, K, G, d_status, stream);
 }
 
+int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
+                          const uint16_t *const *scales, const uint16_t *const *biases,
+                          uint16_t *const *ys, int64_t N, int64_t K, int G, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !biases || !ys) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!tq::w4a16_gemv_supported(N, K, G)) return TQ_ERR_SHAPE;
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !biases[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
+        !aligned(biases[i], 2) || !aligned(ys[i], 2))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_w4a16_gemv_batched(count, xs, packeds, scales, biases, ys, N, K, G,
+                                (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_w4a16_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                  const uint16_t *biases, int64_t N, int64_t K, int G, uint16_t *y,
+                  void *stream) {
+  return tq_w4a16_gemv_batched(1, &x, &packed, &scales, &biases, &y, N, K, G, stream);
+}
+
 int tq_gemv(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
             int64_t N, int64_t K, int G, float *y, int32_t *d_status, void *stream) {
   if (!x || !packed || !scales || !y) return TQ_ERR_NULL;

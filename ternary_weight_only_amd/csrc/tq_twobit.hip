@@ -285,10 +285,11 @@ void launch_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *c
       a.scales[i] = scales[c0 + i];
       a.y[i] = ys[c0 + i];
     }
-    // about eight row steps a wave, and at most 512 blocks in the launch
-    // (two resident a CU, so the whole grid runs in one wave of blocks)
-    int64_t blocks = (N + 8 * rows_per_block - 1) / (8 * rows_per_block);
-    if (blocks * n > 512) blocks = 512 / n;
+    // each problem its share of 512 blocks (two resident a CU, so the whole
+    // grid runs in one wave of blocks), but no fewer than two row steps a wave
+    int64_t blocks = 512 / n;
+    const int64_t most = (N + 2 * rows_per_block - 1) / (2 * rows_per_block);
+    if (blocks > most) blocks = most;
     if (blocks < 1) blocks = 1;
     const dim3 grid((unsigned)blocks, (unsigned)n);
     if (G == 64)

@@ -98,3 +98,21 @@ def ffn_weight(layer: int, proj: int, hidden: int = 1024, inter: int = 3584) -> 
 def activation(seed: int, M: int, K: int) -> np.ndarray:
     """x[M,K] ~ N(0,1) as bf16 bits."""
     return normal_bf16(seed, (M, K), X_SIGMA)
+
+
+def w4a16_problem(seed: int, N: int, K: int, G: int):
+    """Stored W4A16 parameters of one [N,K] matrix: uniform 4-bit codes in
+    uint32 words [N, K/8], and per group a bf16 scale of random sign with
+    magnitude 0.01|z| + 1e-4 and a bf16 bias near -7.5 s, so that the
+    reconstructed weights are centred near zero in either orientation (as
+    stored checkpoints hold them).  Codes and signs come from numpy's PCG64
+    seeded with `seed`; magnitudes from the SplitMix64 normal stream."""
+    rng = np.random.default_rng(seed)
+    packed = rng.integers(0, 1 << 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
+    nG = K // G
+    mag = np.abs(normal_f64(seed, N * nG)).reshape(N, nG) * 0.01 + 1e-4
+    sign = np.where(rng.integers(0, 2, size=mag.shape) == 1, -1.0, 1.0)
+    s = f32_to_bf16_bits((sign * mag).astype(np.float32))
+    b = f32_to_bf16_bits((-sign * mag * 7.5 + 0.001 * normal_f64(seed + 1, N * nG).reshape(N, nG))
+                         .astype(np.float32))
+    return packed, s, b

@@ -236,6 +236,28 @@ def test_two_bit_argument_errors():
     assert b(2, good, good, good, good, 4, 128, 64, FAKE + 1, None) == -4
 
 
+def test_w4a16_argument_errors():
+    import ctypes
+    lib = _lib()
+    g = lib.tq_w4a16_gemv
+    assert g(None, FAKE, FAKE, FAKE, 4, 128, 128, FAKE, None) == -1
+    assert g(FAKE, FAKE, FAKE, None, 4, 128, 128, FAKE, None) == -1
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 8192, 128, FAKE, None) == -2   # K/64 > 64
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 200, 100, FAKE, None) == -3
+    assert g(FAKE + 8, FAKE, FAKE, FAKE, 4, 128, 128, FAKE, None) == -4
+    assert g(FAKE, FAKE + 4, FAKE, FAKE, 4, 128, 128, FAKE, None) == -4
+    assert g(FAKE, FAKE, FAKE, FAKE + 1, 4, 128, 128, FAKE, None) == -4
+    assert g(FAKE, FAKE, FAKE, FAKE, 4, 128, 128, FAKE + 1, None) == -4
+    arr = ctypes.c_void_p * 2
+    good = arr(FAKE, FAKE + 4096)
+    b = lib.tq_w4a16_gemv_batched
+    assert b(0, None, None, None, None, None, 4, 128, 128, None) == 0
+    assert b(-1, good, good, good, good, good, 4, 128, 128, None) == -2
+    assert b(2, good, good, good, None, good, 4, 128, 128, None) == -1
+    assert b(2, good, good, good, arr(FAKE, None), good, 4, 128, 128, None) == -1
+    assert b(2, good, arr(FAKE, FAKE + 8), good, good, good, 4, 128, 128, None) == -4
+
+
 def test_product_path_does_not_import_oracle():
     pkg = os.path.join(ROOT, "ternary_weight_only_amd")
     for dirpath, _, files in os.walk(pkg):

@@ -47,13 +47,7 @@ def numpy_unpack(packed, N, K):
 
 
 def random_problem(seed, N, K, G):
-    rng = np.random.default_rng(seed)
-    packed = rng.integers(0, 1 << 32, size=(N, K // 8), dtype=np.uint64).astype(np.uint32)
-    mag = np.abs(inputs.normal_f64(seed, N * (K // G))).reshape(N, K // G) * 0.01 + 1e-4
-    sign = np.where(rng.integers(0, 2, size=mag.shape) == 1, -1.0, 1.0)
-    s = bf16(sign * mag)
-    b = bf16(-sign * mag * 7.5 + 0.001 * inputs.normal_f64(seed + 1, mag.size).reshape(mag.shape))
-    return packed, s, b
+    return inputs.w4a16_problem(seed, N, K, G)
 
 
 def test_packing_layout_fixture(golden=GOLDEN):
