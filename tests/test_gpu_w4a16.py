@@ -113,3 +113,22 @@ def test_w4a16_repeatable():
     packed, s, b = random_problem(450, N, K, G)
     x = inputs.activation(451, 1, K)
     assert np.array_equal(gpu_w4(x, packed, s, b, N, K, G), gpu_w4(x, packed, s, b, N, K, G))
+
+
+def test_w4a16_nonfinite_scale_propagates_to_its_row_only():
+    """A NaN or Inf group scale reaches y of its own row only (q * NaN is
+    NaN; q * Inf is Inf, or NaN where q = 0); every other row stays within
+    the bar."""
+    N, K, G = 64, 512, 128
+    packed, s, b = random_problem(460, N, K, G)
+    x = inputs.activation(461, 1, K)
+    s = s.copy()
+    s[5, 1] = 0x7FC0                              # NaN
+    s[40, 3] = 0x7F80                             # +Inf
+    y = bf16_val(gpu_w4(x, packed, s, b, N, K, G))
+    assert np.isnan(y[5]) and not np.isfinite(y[40])
+    keep = np.ones(N, bool)
+    keep[[5, 40]] = False
+    y_ref, bound = oracle.w4a16_matmul(x, packed[keep], s[keep], b[keep], int(keep.sum()), K, G)
+    tol = 1e-3 * bound[0] * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref[0])
+    assert (np.abs(y[keep] - y_ref[0]) <= tol).all()
