@@ -36,7 +36,7 @@ back to back between two HIP events (median of three chains); its row counts
 Also outside the step, two other weight formats run the decode GEMV through
 the same 72 shapes, each over eight ring-slot copies back to back between two
 HIP events (median of three chains): the 2-bit ternary format (the same
-scales and codes, four codes a byte; tq_gemv2_batched, two launches a pass)
+scales and codes, four codes a byte; tq_gemv2_grouped, one launch a pass)
 and W4A16 (seeded stored 4-bit affine codes with bf16 scales and biases;
 tq_w4a16_gemv_batched, two launches a pass).  Their rows count code plus
 scale (and bias) bytes.
@@ -338,15 +338,14 @@ def main():
     P2s = {slot: {i: (P2[i][0].clone(), P2[i][1].clone()) for i in P2} for slot in range(RING)}
     del P2
     y2 = [torch.empty(1, N, dtype=torch.float32, device=dev) for N, K in shapes]
-    g2_calls = {slot: [(N, K, len(idx), ptrs([x_dec[i] for i in idx]),
-                        ptrs([P2s[slot][i][0] for i in idx]), ptrs([P2s[slot][i][1] for i in idx]),
-                        ptrs([y2[i] for i in idx]))
-                       for (N, K), idx in groups.items()] for slot in range(RING)}
+    g2_calls = {slot: (ptrs(x_dec), ptrs([P2s[slot][i][0] for i in range(len(shapes))]),
+                       ptrs([P2s[slot][i][1] for i in range(len(shapes))]), ptrs(y2))
+                for slot in range(RING)}
 
     def run_gemv2(slot, stream):
-        for N, K, n, ax, ap, asc, ay in g2_calls[slot]:
-            rc = L.tq_gemv2_batched(n, ax, ap, asc, ay, N, K, G, stp, stream)
-            assert rc == 0, rc
+        ax, ap, asc, ay = g2_calls[slot]
+        rc = L.tq_gemv2_grouped(len(shapes), ax, ap, asc, ay, g_ns, g_ks, G, stp, stream)
+        assert rc == 0, rc
 
     g2 = []
     with torch.cuda.stream(stream):
@@ -476,7 +475,7 @@ def main():
         "decode_gemv_2bit": {"ms": g2_ms, "GB/s": packed2_bytes / (g2_ms * 1e-3) / 1e9,
                              "frac_hbm": packed2_bytes / (g2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                              "Tweights/s": weights / (g2_ms * 1e-3) / 1e12,
-                             "bytes_per_pass": packed2_bytes, "launches": len(groups),
+                             "bytes_per_pass": packed2_bytes, "launches": 1,
                              "in_step": False},
         "decode_gemv_w4a16": {"ms": w4_ms, "GB/s": w4_bytes / (w4_ms * 1e-3) / 1e9,
                               "frac_hbm": w4_bytes / (w4_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

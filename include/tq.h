@@ -348,11 +348,20 @@ int tq_gemv2(const uint16_t *x, const uint8_t *packed2, const uint16_t *scales, 
 
 /* Batched form: `count` same-shaped problems, each as tq_gemv2 on xs[i],
  * packed2s[i], scales[i], ys[i] (HOST arrays of DEVICE pointers, read during
- * the call only), one launch per 64.  Errors as tq_gemv2; a NULL or
+ * the call only), one launch per 128.  Errors as tq_gemv2; a NULL or
  * misaligned pointer in any entry rejects the whole call. */
 int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packed2s,
                      const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
                      int G, int32_t *d_status, void *stream);
+
+/* Grouped form: `count` problems of their own shapes Ns[i] x Ks[i] (HOST
+ * arrays, as the pointer arrays), each as tq_gemv2, in one launch per 128
+ * problems.  Every problem must meet tq_gemv2's limits; the first that does
+ * not, or a NULL or misaligned pointer in any entry, rejects the whole call
+ * with that error.  Each row's result is bit-identical to tq_gemv2's. */
+int tq_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packed2s,
+                     const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                     const int64_t *Ks, int G, int32_t *d_status, void *stream);
 
 /*
  * W4A16: group-wise affine 4-bit weights, bf16 activations and output

@@ -45,6 +45,7 @@ from .binding import (  # noqa: F401
     gemv_grouped,
     gemv2,
     gemv2_batched,
+    gemv2_grouped,
     w4a16_gemv,
     w4a16_gemv_batched,
     lib,

@@ -23,7 +23,7 @@ DEV_BAD_PADDING = 8
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
            "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
            "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_unpack2",
-           "tq_gemv2", "tq_gemv2_batched", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_gemv2", "tq_gemv2_batched", "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -60,6 +60,8 @@ def lib() -> ctypes.CDLL:
         l.tq_gemv2.restype = i32
         l.tq_gemv2_batched.argtypes = [i32, p, p, p, p, i64, i64, i32, p, p]
         l.tq_gemv2_batched.restype = i32
+        l.tq_gemv2_grouped.argtypes = [i32, p, p, p, p, p, p, i32, p, p]
+        l.tq_gemv2_grouped.restype = i32
         l.tq_w4a16_gemv.argtypes = [p, p, p, p, i64, i64, i32, p, p]
         l.tq_w4a16_gemv.restype = i32
         l.tq_w4a16_gemv_batched.argtypes = [i32, p, p, p, p, p, i64, i64, i32, p]
@@ -302,6 +304,28 @@ def w4a16_gemv_batched(xs, packeds, scales_list, biases_list, N: int, K: int, G:
     _rc(lib().tq_w4a16_gemv_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
                                     _ptrs(biases_list), _ptrs(outs), N, K, G, _stream()),
         "tq_w4a16_gemv_batched")
+    return outs
+
+
+def gemv2_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
+    """2-bit format, M = 1, problems of mixed shapes in one launch:
+    list of y fp32 [1, Ns[i]]."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == n):
+        raise TQError("xs, packeds, scales, Ns and Ks differ in length")
+    for x, pk, sc, N, K in zip(xs, packeds, scales_list, Ns, Ks):
+        _dev(x, "x", (torch.bfloat16, torch.int16), 2)
+        _dev(pk, "packed", (torch.uint8,), pk.dim())
+        _dev(sc, "scales", (torch.float16, torch.int16), sc.dim())
+        if (tuple(x.shape) != (1, K) or pk.numel() * 4 != N * K or G <= 0
+                or sc.numel() != N * (K // G)):
+            raise TQError("gemv2_grouped: shapes do not match N=%d K=%d G=%d" % (N, K, G))
+    if outs is None:
+        outs = [torch.empty((1, N), dtype=torch.float32, device=x.device) for x, N in zip(xs, Ns)]
+    i64s = ctypes.c_int64 * max(n, 1)
+    _rc(lib().tq_gemv2_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
+                               i64s(*Ns), i64s(*Ks), G, _st(status), _stream()),
+        "tq_gemv2_grouped")
     return outs
 
 

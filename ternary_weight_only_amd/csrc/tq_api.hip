@@ -219,6 +219,28 @@ int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const 
   return finish_launch();
 }
 
+int tq_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                     const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                     const int64_t *Ks, int G, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !ys || !Ns || !Ks) return TQ_ERR_NULL;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_nkg(Ns[i], Ks[i], G);
+    if (rc) return rc;
+    if (!tq::gemv2_supported(Ns[i], Ks[i], G)) return TQ_ERR_SHAPE;
+    if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
+        !aligned(ys[i], 4))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_gemv2_grouped(count, xs, packeds, scales, ys, Ns, Ks, G, d_status,
+                           (hipStream_t)stream);
+  return finish_launch();
+}
+
 int tq_gemv2(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t N,
              int64_t K, int G, float *y, int32_t *d_status, void *stream) {
   return tq_gemv2_batched(1, &x, &packed, &scales, &y, N, K, G, d_status, stream);

@@ -40,6 +40,9 @@ bool gemv2_supported(int64_t N, int64_t K, int G);
 void launch_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                           const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
                           int G, int32_t *d_status, hipStream_t stream);
+void launch_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                          const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                          const int64_t *Ks, int G, int32_t *d_status, hipStream_t stream);
 
 // W4A16 decode GEMV (tq_w4a16.hip)
 bool w4a16_gemv_supported(int64_t N, int64_t K, int G);

@@ -57,11 +57,16 @@ __device__ __forceinline__ float dpp_f32(float v) {
                                                            0xF, 0xF, false));
 }
 
+constexpr int kGemv2MaxBatch = 128;  // problems a launch (5.5 KB of kernel arguments)
+
+// Problems of one launch: pointers, shapes, and the blocks each one takes
+// (blockIdx.x past a problem's count exits at once).
 struct Gemv2Batch {
-  const uint16_t *x[kQuantMaxBatch];
-  const uint8_t *packed[kQuantMaxBatch];
-  const uint16_t *scales[kQuantMaxBatch];
-  float *y[kQuantMaxBatch];
+  const uint16_t *x[kGemv2MaxBatch];
+  const uint8_t *packed[kGemv2MaxBatch];
+  const uint16_t *scales[kGemv2MaxBatch];
+  float *y[kGemv2MaxBatch];
+  int n[kGemv2MaxBatch], k[kGemv2MaxBatch], nblk[kGemv2MaxBatch];
 };
 
 // bf16 bits of field f's code (f = 3, invalid: 0)
@@ -70,11 +75,15 @@ __device__ __forceinline__ uint32_t code_bf16(uint32_t f) {
 }
 
 template <int G>
-__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv2_kernel(const Gemv2Batch args, int N, int K,
+__global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void gemv2_kernel(const Gemv2Batch args,
                                                        int32_t *__restrict__ d_status) {
   constexpr int CPG = G / 64;  // chunks per group
   __shared__ __align__(16) uint32_t lut[256 * kCopies * 2];
   __shared__ float res[kWaves][kResCap];
+  const int p = blockIdx.y;
+  const int nblk = args.nblk[p];
+  if ((int)blockIdx.x >= nblk) return;  // the grid is as wide as the widest problem
+  const int N = args.n[p], K = args.k[p];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // table: entry of byte b, copy c at dwords (b * kCopies + c) * 2; a thread
@@ -88,7 +97,6 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
         u32x4{lo, hi, lo, hi};
   }
 
-  const int p = blockIdx.y;
   const int L = K >> 6, nG = K / G;
   const int Lp = L <= 16 ? 16 : (L <= 32 ? 32 : 64);   // lanes a row
   const int R = 64 / Lp;                               // rows a wave step
@@ -121,7 +129,7 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
   // rows of this wave: first = (block * kWaves + wave) * R + rs, step RS.
   // Lanes run whole rounds of kRing steps; a step past the wave's rows loads
   // row N - 1 (kept in range) and its result is not stored.
-  const int RS = gridDim.x * kWaves * R;
+  const int RS = nblk * kWaves * R;
   const int first = (blockIdx.x * kWaves + wv) * R;
   const int nsteps = first < N ? (N - first + RS - 1) / RS : 0;
   const int nround = (nsteps + kRing - 1) / kRing;
@@ -270,34 +278,62 @@ bool gemv2_supported(int64_t N, int64_t K, int G) {
          N * (K / 4) < (int64_t(1) << 31) && N < (int64_t(1) << 28);
 }
 
-void launch_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
-                          const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
-                          int G, int32_t *d_status, hipStream_t stream) {
+namespace {
+
+// Blocks of one problem when it holds `share` of the launch's 512 (two
+// resident a CU, so the whole grid runs in one wave of blocks), but no fewer
+// than two row steps a wave.
+int gemv2_blocks(int64_t N, int64_t K, int share) {
   const int L = (int)(K / 64);
   const int Lp = L <= 16 ? 16 : (L <= 32 ? 32 : 64);
-  const int rows_per_block = kWaves * (64 / Lp);
-  for (int c0 = 0; c0 < count; c0 += kQuantMaxBatch) {
-    const int n = count - c0 < kQuantMaxBatch ? count - c0 : kQuantMaxBatch;
+  const int64_t rows_per_block = kWaves * (64 / Lp);
+  int64_t blocks = share;
+  const int64_t most = (N + 2 * rows_per_block - 1) / (2 * rows_per_block);
+  if (blocks > most) blocks = most;
+  return blocks < 1 ? 1 : (int)blocks;
+}
+
+void launch_gemv2_chunk(const Gemv2Batch &a, int n, int G, int32_t *d_status,
+                        hipStream_t stream) {
+  int width = 1;
+  for (int i = 0; i < n; ++i) width = a.nblk[i] > width ? a.nblk[i] : width;
+  const dim3 grid((unsigned)width, (unsigned)n);
+  if (G == 64)
+    hipLaunchKernelGGL(gemv2_kernel<64>, grid, dim3(kBlock), 0, stream, a, d_status);
+  else
+    hipLaunchKernelGGL(gemv2_kernel<128>, grid, dim3(kBlock), 0, stream, a, d_status);
+}
+
+}  // namespace
+
+void launch_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                          const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
+                          const int64_t *Ks, int G, int32_t *d_status, hipStream_t stream) {
+  for (int c0 = 0; c0 < count; c0 += kGemv2MaxBatch) {
+    const int n = count - c0 < kGemv2MaxBatch ? count - c0 : kGemv2MaxBatch;
     Gemv2Batch a{};
     for (int i = 0; i < n; ++i) {
       a.x[i] = xs[c0 + i];
       a.packed[i] = packeds[c0 + i];
       a.scales[i] = scales[c0 + i];
       a.y[i] = ys[c0 + i];
+      a.n[i] = (int)Ns[c0 + i];
+      a.k[i] = (int)Ks[c0 + i];
+      a.nblk[i] = gemv2_blocks(Ns[c0 + i], Ks[c0 + i], 512 / n > 0 ? 512 / n : 1);
     }
-    // each problem its share of 512 blocks (two resident a CU, so the whole
-    // grid runs in one wave of blocks), but no fewer than two row steps a wave
-    int64_t blocks = 512 / n;
-    const int64_t most = (N + 2 * rows_per_block - 1) / (2 * rows_per_block);
-    if (blocks > most) blocks = most;
-    if (blocks < 1) blocks = 1;
-    const dim3 grid((unsigned)blocks, (unsigned)n);
-    if (G == 64)
-      hipLaunchKernelGGL(gemv2_kernel<64>, grid, dim3(kBlock), 0, stream, a, (int)N, (int)K,
-                         d_status);
-    else
-      hipLaunchKernelGGL(gemv2_kernel<128>, grid, dim3(kBlock), 0, stream, a, (int)N, (int)K,
-                         d_status);
+    launch_gemv2_chunk(a, n, G, d_status, stream);
+  }
+}
+
+void launch_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                          const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
+                          int G, int32_t *d_status, hipStream_t stream) {
+  int64_t Ns[kGemv2MaxBatch], Ks[kGemv2MaxBatch];
+  for (int i = 0; i < kGemv2MaxBatch; ++i) { Ns[i] = N; Ks[i] = K; }
+  for (int c0 = 0; c0 < count; c0 += kGemv2MaxBatch) {
+    const int n = count - c0 < kGemv2MaxBatch ? count - c0 : kGemv2MaxBatch;
+    launch_gemv2_grouped(n, xs + c0, packeds + c0, scales + c0, ys + c0, Ns, Ks, G, d_status,
+                         stream);
   }
 }
 

@@ -234,6 +234,17 @@ def test_two_bit_argument_errors():
     assert b(2, good, good, arr(FAKE, None), good, 4, 128, 64, None, None) == -1
     assert b(2, good, arr(FAKE, FAKE + 8), good, good, 4, 128, 64, None, None) == -4
     assert b(2, good, good, good, good, 4, 128, 64, FAKE + 1, None) == -4
+    gr = lib.tq_gemv2_grouped
+    i64s = ctypes.c_int64 * 2
+    ns, ks = i64s(4, 8), i64s(128, 256)
+    assert gr(0, None, None, None, None, None, None, 64, None, None) == 0
+    assert gr(-1, good, good, good, good, ns, ks, 64, None, None) == -2
+    assert gr(2, good, good, good, good, None, ks, 64, None, None) == -1
+    assert gr(2, good, good, good, good, ns, i64s(128, 8192), 64, None, None) == -2
+    assert gr(2, good, good, good, good, ns, i64s(128, 200), 64, None, None) == -2
+    assert gr(2, good, good, good, good, ns, ks, 96, None, None) == -3
+    assert gr(2, good, arr(FAKE, FAKE + 8), good, good, ns, ks, 64, None, None) == -4
+    assert gr(2, good, good, good, arr(FAKE, None), ns, ks, 64, None, None) == -1
 
 
 def test_w4a16_argument_errors():

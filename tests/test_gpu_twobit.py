@@ -230,3 +230,34 @@ def test_gemv2_agrees_with_base3_gemv_on_same_weights():
     y3, _ = gpu_matmul("gemv", x, p3, s3, N, K, G)
     _, bound, _ = oracle.matmul2(x, p2, s2, N, K, G)
     assert (np.abs(y2.astype(np.float64) - y3.astype(np.float64)) <= 2e-3 * bound).all()
+
+
+def test_gemv2_grouped_mixed_shapes_bitwise_equal_to_single():
+    """One grouped launch over problems of different shapes (the decode
+    stack's two, a ragged one, every lanes-per-row width, a single row): each
+    result bit-identical to tq_gemv2 on its own and within the oracle's
+    bound."""
+    import torch
+    import ternary_weight_only_amd as tq
+    G = 128
+    shapes = [(3584, 1024)] * 5 + [(1024, 3584)] * 3 + [(1, 128), (777, 2048), (64, 4096),
+                                                        (300, 1152)]
+    probs = []
+    for i, (N, K) in enumerate(shapes):
+        w = inputs.normal_bf16(500 + i, (N, K), 0.02)
+        p, s, _ = oracle.quantize_pack2(w, G)
+        probs.append((inputs.activation(520 + i, 1, K), p, s))
+    say("gemv2_grouped %d problems" % len(shapes))
+    st = tq.new_status()
+    ys = tq.gemv2_grouped([dev_bf16(x) for x, _, _ in probs], [dev_u8(p) for _, p, _ in probs],
+                          [dev_f16bits(s) for _, _, s in probs], [N for N, _ in shapes],
+                          [K for _, K in shapes], G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for i, ((N, K), (x, p, s)) in enumerate(zip(shapes, probs)):
+        yg = ys[i].cpu().numpy()
+        y1, _ = gpu_gemv2(x, p, s, N, K, G)
+        assert np.array_equal(yg.view(np.uint32), y1.view(np.uint32)), i
+        if i in (0, 5, 8, 9, 10, 11):
+            y_ref, bound, _ = oracle.matmul2(x, p, s, N, K, G)
+            assert_within_bound(yg, y_ref, bound, "grouped %d" % i)
