@@ -38,7 +38,7 @@ the same 72 shapes, each over eight ring-slot copies back to back between two
 HIP events (median of three chains): the 2-bit ternary format (the same
 scales and codes, four codes a byte; tq_gemv2_grouped, one launch a pass)
 and W4A16 (seeded stored 4-bit affine codes with bf16 scales and biases;
-tq_w4a16_gemv_batched, two launches a pass).  Their rows count code plus
+tq_w4a16_gemv_grouped, one launch a pass).  Their rows count code plus
 scale (and bias) bytes.
 
 The roofline entry times the GEMV kernel itself: after the timed steps, the
@@ -372,15 +372,16 @@ def main():
                       .to(dev) for a in (pk, sc, bi))
     y4 = [torch.empty(1, N, dtype=torch.bfloat16, device=dev) for N, K in shapes]
     W4s = {slot: {i: tuple(t.clone() for t in W4[i]) for i in W4} for slot in range(RING)}
-    w4_calls = {slot: [(N, K, len(idx), ptrs([x_dec[i] for i in idx]),
-                        ptrs([W4s[slot][i][0] for i in idx]), ptrs([W4s[slot][i][1] for i in idx]),
-                        ptrs([W4s[slot][i][2] for i in idx]), ptrs([y4[i] for i in idx]))
-                       for (N, K), idx in groups.items()] for slot in range(RING)}
+    nm = range(len(shapes))
+    w4_calls = {slot: (ptrs(x_dec), ptrs([W4s[slot][i][0] for i in nm]),
+                       ptrs([W4s[slot][i][1] for i in nm]), ptrs([W4s[slot][i][2] for i in nm]),
+                       ptrs(y4))
+                for slot in range(RING)}
 
     def run_w4(slot, stream):
-        for N, K, n, ax, ap, asc, abi, ay in w4_calls[slot]:
-            rc = L.tq_w4a16_gemv_batched(n, ax, ap, asc, abi, ay, N, K, G, stream)
-            assert rc == 0, rc
+        ax, ap, asc, abi, ay = w4_calls[slot]
+        rc = L.tq_w4a16_gemv_grouped(len(shapes), ax, ap, asc, abi, ay, g_ns, g_ks, G, stream)
+        assert rc == 0, rc
 
     with torch.cuda.stream(stream):
         run_w4(0, sp)
@@ -480,7 +481,7 @@ def main():
         "decode_gemv_w4a16": {"ms": w4_ms, "GB/s": w4_bytes / (w4_ms * 1e-3) / 1e9,
                               "frac_hbm": w4_bytes / (w4_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
                               "Tweights/s": weights / (w4_ms * 1e-3) / 1e12,
-                              "bytes_per_pass": w4_bytes, "launches": len(groups),
+                              "bytes_per_pass": w4_bytes, "launches": 1,
                               "in_step": False},
         "qat_forward": {"ms": fq_ms, "GB/s": 4 * weights / (fq_ms * 1e-3) / 1e9,
                         "frac_hbm": 4 * weights / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,

@@ -387,12 +387,23 @@ int tq_w4a16_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *sca
 
 /* Batched form: `count` same-shaped problems, each as tq_w4a16_gemv on
  * xs[i], packeds[i], scales[i], biases[i], ys[i] (HOST arrays of DEVICE
- * pointers, read during the call only), one launch per 64.  Errors as
+ * pointers, read during the call only), one launch per 128.  Errors as
  * tq_w4a16_gemv; a NULL or misaligned pointer in any entry rejects the
  * whole call. */
 int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
                           const uint16_t *const *scales, const uint16_t *const *biases,
                           uint16_t *const *ys, int64_t N, int64_t K, int G, void *stream);
+
+/* Grouped form: `count` problems of their own shapes Ns[i] x Ks[i] (HOST
+ * arrays, as the pointer arrays), each as tq_w4a16_gemv, in one launch per
+ * 128 problems.  Every problem must meet tq_w4a16_gemv's limits; the first
+ * that does not, or a NULL or misaligned pointer in any entry, rejects the
+ * whole call with that error.  Each row's result is bit-identical to
+ * tq_w4a16_gemv's. */
+int tq_w4a16_gemv_grouped(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
+                          const uint16_t *const *scales, const uint16_t *const *biases,
+                          uint16_t *const *ys, const int64_t *Ns, const int64_t *Ks, int G,
+                          void *stream);
 
 #ifdef __cplusplus
 }

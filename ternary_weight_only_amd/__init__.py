@@ -48,6 +48,7 @@ from .binding import (  # noqa: F401
     gemv2_grouped,
     w4a16_gemv,
     w4a16_gemv_batched,
+    w4a16_gemv_grouped,
     lib,
     new_status,
     packed_bytes,

@@ -23,7 +23,8 @@ DEV_BAD_PADDING = 8
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
            "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
            "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_unpack2",
-           "tq_gemv2", "tq_gemv2_batched", "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_gemv2", "tq_gemv2_batched", "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched",
+           "tq_w4a16_gemv_grouped", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
 
@@ -66,6 +67,8 @@ def lib() -> ctypes.CDLL:
         l.tq_w4a16_gemv.restype = i32
         l.tq_w4a16_gemv_batched.argtypes = [i32, p, p, p, p, p, i64, i64, i32, p]
         l.tq_w4a16_gemv_batched.restype = i32
+        l.tq_w4a16_gemv_grouped.argtypes = [i32, p, p, p, p, p, p, p, i32, p]
+        l.tq_w4a16_gemv_grouped.restype = i32
         l.tq_unpack_batched.argtypes = [i32, p, i64, i64, i32, p, p, p]
         l.tq_unpack_batched.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
@@ -326,6 +329,22 @@ def gemv2_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=No
     _rc(lib().tq_gemv2_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
                                i64s(*Ns), i64s(*Ks), G, _st(status), _stream()),
         "tq_gemv2_grouped")
+    return outs
+
+
+def w4a16_gemv_grouped(xs, packeds, scales_list, biases_list, Ns, Ks, G: int, outs=None):
+    """W4A16 problems of mixed shapes in one launch -> list of y bf16 [1, Ns[i]]."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(biases_list) == len(Ns) == len(Ks) == n):
+        raise TQError("xs, packeds, scales, biases, Ns and Ks differ in length")
+    for x, pk, sc, bi, N, K in zip(xs, packeds, scales_list, biases_list, Ns, Ks):
+        _w4_check(x, pk, sc, bi, N, K, G)
+    if outs is None:
+        outs = [torch.empty((1, N), dtype=torch.bfloat16, device=x.device) for x, N in zip(xs, Ns)]
+    i64s = ctypes.c_int64 * max(n, 1)
+    _rc(lib().tq_w4a16_gemv_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
+                                    _ptrs(biases_list), _ptrs(outs), i64s(*Ns), i64s(*Ks), G,
+                                    _stream()), "tq_w4a16_gemv_grouped")
     return outs
 
 

@@ -267,6 +267,28 @@ int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *
   return finish_launch();
 }
 
+int tq_w4a16_gemv_grouped(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
+                          const uint16_t *const *scales, const uint16_t *const *biases,
+                          uint16_t *const *ys, const int64_t *Ns, const int64_t *Ks, int G,
+                          void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !biases || !ys || !Ns || !Ks) return TQ_ERR_NULL;
+  for (int i = 0; i < count; ++i) {
+    const int rc = check_nkg(Ns[i], Ks[i], G);
+    if (rc) return rc;
+    if (!tq::w4a16_gemv_supported(Ns[i], Ks[i], G)) return TQ_ERR_SHAPE;
+    if (!xs[i] || !packeds[i] || !scales[i] || !biases[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
+        !aligned(biases[i], 2) || !aligned(ys[i], 2))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_w4a16_gemv_grouped(count, xs, packeds, scales, biases, ys, Ns, Ks, G,
+                                (hipStream_t)stream);
+  return finish_launch();
+}
+
 int tq_w4a16_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
                   const uint16_t *biases, int64_t N, int64_t K, int G, uint16_t *y,
                   void *stream) {

@@ -50,6 +50,10 @@ void launch_w4a16_gemv_batched(int count, const uint16_t *const *xs,
                                const uint32_t *const *packeds, const uint16_t *const *scales,
                                const uint16_t *const *biases, uint16_t *const *ys, int64_t N,
                                int64_t K, int G, hipStream_t stream);
+void launch_w4a16_gemv_grouped(int count, const uint16_t *const *xs,
+                               const uint32_t *const *packeds, const uint16_t *const *scales,
+                               const uint16_t *const *biases, uint16_t *const *ys,
+                               const int64_t *Ns, const int64_t *Ks, int G, hipStream_t stream);
 
 void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
                            int8_t *const *codes, int32_t *d_status, hipStream_t stream);

@@ -65,20 +65,29 @@ __device__ __forceinline__ uint16_t f32_to_bf16_rne(float f) {
   return (uint16_t)((u + 0x7FFFu + ((u >> 16) & 1u)) >> 16);
 }
 
+constexpr int kW4MaxBatch = 128;  // problems a launch (6.5 KB of kernel arguments)
+
+// Problems of one launch: pointers, shapes, and the blocks each one takes
+// (blockIdx.x past a problem's count exits at once).
 struct W4Batch {
-  const uint16_t *x[kQuantMaxBatch];
-  const uint32_t *packed[kQuantMaxBatch];
-  const uint16_t *scales[kQuantMaxBatch];
-  const uint16_t *biases[kQuantMaxBatch];
-  uint16_t *y[kQuantMaxBatch];
+  const uint16_t *x[kW4MaxBatch];
+  const uint32_t *packed[kW4MaxBatch];
+  const uint16_t *scales[kW4MaxBatch];
+  const uint16_t *biases[kW4MaxBatch];
+  uint16_t *y[kW4MaxBatch];
+  int n[kW4MaxBatch], k[kW4MaxBatch], nblk[kW4MaxBatch];
 };
 
 template <int G>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void
-w4a16_gemv_kernel(const W4Batch args, int N, int K) {
+w4a16_gemv_kernel(const W4Batch args) {
   constexpr int CPG = G / 64;  // lanes a group
   __shared__ __align__(16) uint32_t lut[256 * kCopies];
   __shared__ float res[kWaves][kResCap];
+  const int p = blockIdx.y;
+  const int nblk = args.nblk[p];
+  if ((int)blockIdx.x >= nblk) return;  // the grid is as wide as the widest problem
+  const int N = args.n[p], K = args.k[p];
   const int tid = threadIdx.x, lane = tid & 63;
   const int wv = __builtin_amdgcn_readfirstlane(tid >> 6);
   // table: entry of byte b, copy c at dword b * kCopies + c holds the bf16
@@ -91,7 +100,6 @@ w4a16_gemv_kernel(const W4Batch args, int N, int K) {
     *reinterpret_cast<u32x4 *>(&lut[4 * i]) = u32x4{e, e, e, e};
   }
 
-  const int p = blockIdx.y;
   const int L = K >> 6, nG = K / G;
   const int Lp = L <= 16 ? 16 : (L <= 32 ? 32 : 64);  // lanes a row
   const int R = 64 / Lp;                              // rows a wave step
@@ -129,7 +137,7 @@ w4a16_gemv_kernel(const W4Batch args, int N, int K) {
   // rows of this wave: first = (block * kWaves + wave) * R + rs, step RS.
   // Lanes run whole rounds of kRing steps; a step past the wave's rows loads
   // row N - 1 (kept in range) and its result is not stored.
-  const int RS = gridDim.x * kWaves * R;
+  const int RS = nblk * kWaves * R;
   const int first = (blockIdx.x * kWaves + wv) * R;
   const int nsteps = first < N ? (N - first + RS - 1) / RS : 0;
   const int nround = (nsteps + kRing - 1) / kRing;
@@ -257,36 +265,60 @@ bool w4a16_gemv_supported(int64_t N, int64_t K, int G) {
          N * (K / 2) < (int64_t(1) << 31) && N < (int64_t(1) << 28);
 }
 
-void launch_w4a16_gemv_batched(int count, const uint16_t *const *xs,
-                               const uint32_t *const *packeds, const uint16_t *const *scales,
-                               const uint16_t *const *biases, uint16_t *const *ys, int64_t N,
-                               int64_t K, int G, hipStream_t stream) {
+namespace {
+
+// Blocks of one problem when it holds `share` of the launch's 512 (two
+// resident a CU, so the whole grid runs in one wave of blocks), but no fewer
+// than two row steps a wave.
+int w4_blocks(int64_t N, int64_t K, int share) {
   const int L = (int)(K / 64);
   const int Lp = L <= 16 ? 16 : (L <= 32 ? 32 : 64);
-  const int rows_per_block = kWaves * (64 / Lp);
-  for (int c0 = 0; c0 < count; c0 += kQuantMaxBatch) {
-    const int n = count - c0 < kQuantMaxBatch ? count - c0 : kQuantMaxBatch;
+  const int64_t rows_per_block = kWaves * (64 / Lp);
+  int64_t blocks = share;
+  const int64_t most = (N + 2 * rows_per_block - 1) / (2 * rows_per_block);
+  if (blocks > most) blocks = most;
+  return blocks < 1 ? 1 : (int)blocks;
+}
+
+}  // namespace
+
+void launch_w4a16_gemv_grouped(int count, const uint16_t *const *xs,
+                               const uint32_t *const *packeds, const uint16_t *const *scales,
+                               const uint16_t *const *biases, uint16_t *const *ys,
+                               const int64_t *Ns, const int64_t *Ks, int G, hipStream_t stream) {
+  for (int c0 = 0; c0 < count; c0 += kW4MaxBatch) {
+    const int n = count - c0 < kW4MaxBatch ? count - c0 : kW4MaxBatch;
     W4Batch a{};
+    int width = 1;
     for (int i = 0; i < n; ++i) {
       a.x[i] = xs[c0 + i];
       a.packed[i] = packeds[c0 + i];
       a.scales[i] = scales[c0 + i];
       a.biases[i] = biases[c0 + i];
       a.y[i] = ys[c0 + i];
+      a.n[i] = (int)Ns[c0 + i];
+      a.k[i] = (int)Ks[c0 + i];
+      a.nblk[i] = w4_blocks(Ns[c0 + i], Ks[c0 + i], 512 / n > 0 ? 512 / n : 1);
+      width = a.nblk[i] > width ? a.nblk[i] : width;
     }
-    // each problem its share of 512 blocks (two resident a CU, so the whole
-    // grid runs in one wave of blocks), but no fewer than two row steps a wave
-    int64_t blocks = 512 / n;
-    const int64_t most = (N + 2 * rows_per_block - 1) / (2 * rows_per_block);
-    if (blocks > most) blocks = most;
-    if (blocks < 1) blocks = 1;
-    const dim3 grid((unsigned)blocks, (unsigned)n);
+    const dim3 grid((unsigned)width, (unsigned)n);
     if (G == 64)
-      hipLaunchKernelGGL(w4a16_gemv_kernel<64>, grid, dim3(kBlock), 0, stream, a, (int)N,
-                         (int)K);
+      hipLaunchKernelGGL(w4a16_gemv_kernel<64>, grid, dim3(kBlock), 0, stream, a);
     else
-      hipLaunchKernelGGL(w4a16_gemv_kernel<128>, grid, dim3(kBlock), 0, stream, a, (int)N,
-                         (int)K);
+      hipLaunchKernelGGL(w4a16_gemv_kernel<128>, grid, dim3(kBlock), 0, stream, a);
+  }
+}
+
+void launch_w4a16_gemv_batched(int count, const uint16_t *const *xs,
+                               const uint32_t *const *packeds, const uint16_t *const *scales,
+                               const uint16_t *const *biases, uint16_t *const *ys, int64_t N,
+                               int64_t K, int G, hipStream_t stream) {
+  int64_t Ns[kW4MaxBatch], Ks[kW4MaxBatch];
+  for (int i = 0; i < kW4MaxBatch; ++i) { Ns[i] = N; Ks[i] = K; }
+  for (int c0 = 0; c0 < count; c0 += kW4MaxBatch) {
+    const int n = count - c0 < kW4MaxBatch ? count - c0 : kW4MaxBatch;
+    launch_w4a16_gemv_grouped(n, xs + c0, packeds + c0, scales + c0, biases + c0, ys + c0, Ns,
+                              Ks, G, stream);
   }
 }
 

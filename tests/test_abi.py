@@ -267,6 +267,16 @@ def test_w4a16_argument_errors():
     assert b(2, good, good, good, None, good, 4, 128, 128, None) == -1
     assert b(2, good, good, good, arr(FAKE, None), good, 4, 128, 128, None) == -1
     assert b(2, good, arr(FAKE, FAKE + 8), good, good, good, 4, 128, 128, None) == -4
+    gr = lib.tq_w4a16_gemv_grouped
+    i64s = ctypes.c_int64 * 2
+    ns, ks = i64s(4, 8), i64s(128, 256)
+    assert gr(0, None, None, None, None, None, None, None, 128, None) == 0
+    assert gr(-1, good, good, good, good, good, ns, ks, 128, None) == -2
+    assert gr(2, good, good, good, good, good, ns, None, 128, None) == -1
+    assert gr(2, good, good, good, good, good, ns, i64s(128, 8192), 128, None) == -2
+    assert gr(2, good, good, good, good, good, ns, ks, 100, None) == -3
+    assert gr(2, good, arr(FAKE, FAKE + 8), good, good, good, ns, ks, 128, None) == -4
+    assert gr(2, good, good, good, arr(FAKE, None), good, ns, ks, 128, None) == -1
 
 
 def test_product_path_does_not_import_oracle():

@@ -132,3 +132,26 @@ def test_w4a16_nonfinite_scale_propagates_to_its_row_only():
     y_ref, bound = oracle.w4a16_matmul(x, packed[keep], s[keep], b[keep], int(keep.sum()), K, G)
     tol = 1e-3 * bound[0] * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref[0])
     assert (np.abs(y[keep] - y_ref[0]) <= tol).all()
+
+
+def test_w4a16_grouped_mixed_shapes_bitwise_equal_to_single():
+    """One grouped launch over problems of different shapes (the stack's two,
+    a single row, ragged and long rows, both G's lane widths): each result
+    bit-identical to tq_w4a16_gemv alone and within the bar."""
+    import torch
+    import ternary_weight_only_amd as tq
+    G = 128
+    shapes = [(3584, 1024)] * 4 + [(1024, 3584)] * 3 + [(1, 128), (777, 2048), (64, 4096),
+                                                        (300, 1152)]
+    probs = [random_problem(600 + i, N, K, G) for i, (N, K) in enumerate(shapes)]
+    xs = [inputs.activation(620 + i, 1, K) for i, (N, K) in enumerate(shapes)]
+    say("w4a16 grouped %d problems" % len(shapes))
+    ys = tq.w4a16_gemv_grouped([dev_bf16(x) for x in xs], [dev_u32(p) for p, _, _ in probs],
+                               [dev_bf16(s) for _, s, _ in probs], [dev_bf16(b) for _, _, b in probs],
+                               [N for N, _ in shapes], [K for _, K in shapes], G)
+    torch.cuda.synchronize()
+    for i, ((N, K), (p, s, b)) in enumerate(zip(shapes, probs)):
+        yg = host_u16(ys[i])[0]
+        assert np.array_equal(yg, gpu_w4(xs[i], p, s, b, N, K, G)), i
+        y_ref, bound = oracle.w4a16_matmul(xs[i], p, s, b, N, K, G)
+        check(yg, y_ref[0], bound[0], "grouped %d" % i)
