@@ -320,13 +320,14 @@ def main():
     # packed four codes a byte (same scales and codes), one batched call per
     # shape over each ring slot, all slots back to back
     P2 = {}
-    for i, (N, K) in enumerate(shapes):
-        p2 = torch.empty(N, K // 4, dtype=torch.uint8, device=dev)
-        s2 = torch.empty(N, K // G, dtype=torch.float16, device=dev)
-        rc = L.tq_quantize_pack2(w_dev[i].data_ptr(), N, K, G, p2.data_ptr(), s2.data_ptr(), stp,
-                                 s0)
+    for (N, K), idx in groups.items():
+        out2 = [(torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
+                 torch.empty(N, K // G, dtype=torch.float16, device=dev)) for _ in idx]
+        rc = L.tq_quantize_pack2_batched(len(idx), ptrs([w_dev[i] for i in idx]), N, K, G,
+                                         ptrs([p for p, _ in out2]), ptrs([s for _, s in out2]),
+                                         stp, s0)
         assert rc == 0, rc
-        P2[i] = (p2, s2)
+        P2.update(zip(idx, out2))
     torch.cuda.synchronize()
     assert int(status.item()) == 0
     for i in (0, 71):

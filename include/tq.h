@@ -328,6 +328,14 @@ int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *
 int tq_quantize_pack2(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed2,
                       uint16_t *scales, int32_t *d_status, void *stream);
 
+/* Batched form: `count` same-shaped matrices, each as tq_quantize_pack2 on
+ * ws[i], packed2s[i], scales[i] (HOST arrays of DEVICE pointers, read during
+ * the call only), one launch per 64.  Errors as tq_quantize_pack2; a NULL or
+ * misaligned pointer in any entry rejects the whole call. */
+int tq_quantize_pack2_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                              uint8_t *const *packed2s, uint16_t *const *scales,
+                              int32_t *d_status, void *stream);
+
 /* 2-bit packed -> codes int8 [N,K] {-1,0,1}.  packed2 4-byte aligned, codes
  * 16-byte aligned.  A field of 3 sets TQ_DEV_INVALID_BYTE and reads as 0. */
 int tq_unpack2(const uint8_t *packed2, int64_t N, int64_t K, int G, int8_t *codes,

@@ -55,6 +55,7 @@ from .binding import (  # noqa: F401
     quantize_pack,
     quantize_pack_batched,
     quantize_pack2,
+    quantize_pack2_batched,
     unpack,
     unpack_batched,
     unpack2,

@@ -22,7 +22,7 @@ DEV_BAD_PADDING = 8
 # Every symbol include/tq.h declares.
 SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
            "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
-           "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_unpack2",
+           "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_quantize_pack2_batched", "tq_unpack2",
            "tq_gemv2", "tq_gemv2_batched", "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched",
            "tq_w4a16_gemv_grouped", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
@@ -55,6 +55,8 @@ def lib() -> ctypes.CDLL:
             f.restype = i32
         l.tq_quantize_pack2.argtypes = [p, i64, i64, i32, p, p, p, p]
         l.tq_quantize_pack2.restype = i32
+        l.tq_quantize_pack2_batched.argtypes = [i32, p, i64, i64, i32, p, p, p, p]
+        l.tq_quantize_pack2_batched.restype = i32
         l.tq_unpack2.argtypes = [p, i64, i64, i32, p, p, p]
         l.tq_unpack2.restype = i32
         l.tq_gemv2.argtypes = [p, p, p, i64, i64, i32, p, p, p]
@@ -226,6 +228,20 @@ def quantize_pack2(w: torch.Tensor, G: int, status=None):
     _rc(lib().tq_quantize_pack2(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
                                 _st(status), _stream()), "tq_quantize_pack2")
     return packed, scales
+
+
+def quantize_pack2_batched(ws, G: int, status=None):
+    """2-bit format, same-shaped bf16 matrices -> list of (packed2, scales),
+    one launch per 64."""
+    N, K = _same_shape(ws, "w")
+    if not ws:
+        return []
+    dev = ws[0].device
+    pk = [torch.empty((N, max(K // 4, 1)), dtype=torch.uint8, device=dev) for _ in ws]
+    sc = [torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=dev) for _ in ws]
+    _rc(lib().tq_quantize_pack2_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(pk), _ptrs(sc),
+                                        _st(status), _stream()), "tq_quantize_pack2_batched")
+    return list(zip(pk, sc))
 
 
 def unpack2(packed: torch.Tensor, N: int, K: int, G: int, status=None):

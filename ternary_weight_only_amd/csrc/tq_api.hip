@@ -186,6 +186,26 @@ int tq_quantize_pack2(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *p
   return finish_launch();
 }
 
+int tq_quantize_pack2_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
+                              uint8_t *const *packeds, uint16_t *const *scales,
+                              int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!ws || !packeds || !scales) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!ws[i] || !packeds[i] || !scales[i]) return TQ_ERR_NULL;
+    if (!aligned(ws[i], 16) || !aligned(packeds[i], 2) || !aligned(scales[i], 2))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_quant_batched(count, ws, N, K, G, packeds, scales, nullptr, d_status,
+                           (hipStream_t)stream, true);
+  return finish_launch();
+}
+
 int tq_unpack2(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
                int32_t *d_status, void *stream) {
   if (!packed || !codes) return TQ_ERR_NULL;

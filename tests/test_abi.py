@@ -234,6 +234,14 @@ def test_two_bit_argument_errors():
     assert b(2, good, good, arr(FAKE, None), good, 4, 128, 64, None, None) == -1
     assert b(2, good, arr(FAKE, FAKE + 8), good, good, 4, 128, 64, None, None) == -4
     assert b(2, good, good, good, good, 4, 128, 64, FAKE + 1, None) == -4
+    qb = lib.tq_quantize_pack2_batched
+    assert qb(0, None, 4, 128, 64, None, None, None, None) == 0
+    assert qb(-1, good, 4, 128, 64, good, good, None, None) == -2
+    assert qb(2, good, 4, 128, 64, None, good, None, None) == -1
+    assert qb(2, good, 4, 130, 64, good, good, None, None) == -2
+    assert qb(2, good, 4, 128, 32, good, good, None, None) == -3
+    assert qb(2, arr(FAKE, FAKE + 8), 4, 128, 64, good, good, None, None) == -4
+    assert qb(2, good, 4, 128, 64, arr(FAKE, FAKE + 1), good, None, None) == -4
     gr = lib.tq_gemv2_grouped
     i64s = ctypes.c_int64 * 2
     ns, ks = i64s(4, 8), i64s(128, 256)

@@ -261,3 +261,26 @@ def test_gemv2_grouped_mixed_shapes_bitwise_equal_to_single():
         if i in (0, 5, 8, 9, 10, 11):
             y_ref, bound, _ = oracle.matmul2(x, p, s, N, K, G)
             assert_within_bound(yg, y_ref, bound, "grouped %d" % i)
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_quantize_pack2_batched_exact(G):
+    """Batched 2-bit packing: every matrix bit-exact with the oracle (scales,
+    fields, flags), including a matrix with a non-finite group."""
+    import torch
+    import ternary_weight_only_amd as tq
+    N, K, count = 97, 1024, 5
+    ws = [inputs.normal_bf16(700 + i + G, (N, K), 0.02) for i in range(count)]
+    ws[3] = ws[3].copy()
+    ws[3][10, 5] = 0x7FC1                          # NaN: its group is flagged
+    say("quantize_pack2_batched %d x W[%d,%d] G=%d" % (count, N, K, G))
+    st = tq.new_status()
+    out = tq.quantize_pack2_batched([dev_bf16(w) for w in ws], G, status=st)
+    torch.cuda.synchronize()
+    flags = 0
+    for i, (p, s) in enumerate(out):
+        p_ref, s_ref, st_ref = oracle.quantize_pack2(ws[i], G)
+        assert np.array_equal(p.cpu().numpy(), p_ref), i
+        assert np.array_equal(host_u16(s), s_ref), i
+        flags |= st_ref
+    assert int(st.item()) == flags == 1
