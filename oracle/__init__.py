@@ -44,7 +44,7 @@ def build(force: bool = False) -> str:
     if force or not os.path.exists(_LIB) or os.path.getmtime(_LIB) < os.path.getmtime(_SRC):
         tmp = _LIB + ".tmp%d" % os.getpid()
         subprocess.check_call(["gcc", "-O2", "-std=c11", "-Wall", "-Wextra", "-fPIC",
-                               "-shared", "-o", tmp, _SRC, "-lm"])
+                               "-pthread", "-shared", "-o", tmp, _SRC, "-lm"])
         os.replace(tmp, _LIB)
     return _LIB
 
@@ -79,12 +79,34 @@ def _load():
         lib.oracle_w4a16_dequantize.restype = ctypes.c_int
         lib.oracle_w4a16_matmul.argtypes = [p, p, p, p, i64, i64, i64, i64, p, p]
         lib.oracle_w4a16_matmul.restype = ctypes.c_int
+        i32 = ctypes.c_int
+        lib.oracle_quantize_pack_mt.argtypes = [p, i64, i64, i64, p, p, p, i32]
+        lib.oracle_quantize_pack_mt.restype = i32
+        for f in (lib.oracle_matmul_mt, lib.oracle_matmul2_mt):
+            f.argtypes = [p, p, p, i64, i64, i64, i64, p, p, p, i32]
+            f.restype = i32
+        lib.oracle_w4a16_matmul_mt.argtypes = [p, p, p, p, i64, i64, i64, i64, p, p, i32]
+        lib.oracle_w4a16_matmul_mt.restype = i32
         _lib = lib
     return _lib
 
 
 def _ptr(a: np.ndarray) -> int:
     return a.ctypes.data
+
+
+def default_threads() -> int:
+    """Threads the row-partitioned entry points use when none is given: the
+    host's cores, at most 16.  Results do not depend on the count."""
+    try:
+        n = len(os.sched_getaffinity(0))
+    except (AttributeError, OSError):
+        n = os.cpu_count() or 1
+    return max(1, min(16, n))
+
+
+def _threads(threads) -> int:
+    return default_threads() if threads is None else max(1, int(threads))
 
 
 class OracleError(RuntimeError):
@@ -96,11 +118,12 @@ def packed_row_bytes(K: int, G: int) -> int:
     return int(_load().oracle_packed_row_bytes(K, G))
 
 
-def quantize_pack(w_bits: np.ndarray, G: int):
+def quantize_pack(w_bits: np.ndarray, G: int, threads=None):
     """w_bits: uint16 [N,K] bf16 bit patterns.
 
     Returns (packed uint8 [N, (K/G)*ceil(G/5)], scales uint16 [N, K/G] fp16 bits,
-    status bits int).
+    status bits int).  The rows are split over `threads` host threads (default:
+    the host's cores, at most 16); the result does not depend on the split.
     """
     w = np.ascontiguousarray(w_bits, dtype=np.uint16)
     if w.ndim != 2:
@@ -112,7 +135,8 @@ def quantize_pack(w_bits: np.ndarray, G: int):
     packed = np.empty((N, rb), np.uint8)
     scales = np.empty((N, K // G), np.uint16)
     st = np.zeros(1, np.int32)
-    rc = _load().oracle_quantize_pack(_ptr(w), N, K, G, _ptr(packed), _ptr(scales), _ptr(st))
+    rc = _load().oracle_quantize_pack_mt(_ptr(w), N, K, G, _ptr(packed), _ptr(scales), _ptr(st),
+                                         _threads(threads))
     if rc:
         raise OracleError("oracle_quantize_pack rc=%d" % rc)
     return packed, scales, int(st[0])
@@ -200,7 +224,8 @@ def unpack2(packed: np.ndarray, N: int, K: int, G: int):
     return codes, int(st[0])
 
 
-def matmul2(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):
+def matmul2(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int,
+            threads=None):
     """As matmul, over the 2-bit format."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if x.ndim != 2 or x.shape[1] != K:
@@ -213,18 +238,21 @@ def matmul2(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, 
     y = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64)
     st = np.zeros(1, np.int32)
-    rc = _load().oracle_matmul2(_ptr(x), _ptr(p), _ptr(s), M, N, K, G, _ptr(y), _ptr(bound),
-                                _ptr(st))
+    rc = _load().oracle_matmul2_mt(_ptr(x), _ptr(p), _ptr(s), M, N, K, G, _ptr(y), _ptr(bound),
+                                   _ptr(st), _threads(threads))
     if rc:
         raise OracleError("oracle_matmul2 rc=%d" % rc)
     return y, bound, int(st[0])
 
 
-def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int):
+def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K: int, G: int,
+           threads=None):
     """y[m,n] = sum_k x[m,k] c[n,k] s[n,k/G] in fp64.
 
     x_bits: uint16 [M,K] bf16 bits.  Returns (y float64 [M,N],
-    bound float64 [M,N] = sum_k |x c s|, status bits int).
+    bound float64 [M,N] = sum_k |x c s|, status bits int).  Weight rows are
+    split over `threads` host threads; each output's sum runs in k order
+    whatever the split.
     """
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
     if x.ndim != 2 or x.shape[1] != K:
@@ -238,7 +266,8 @@ def matmul(x_bits: np.ndarray, packed: np.ndarray, scales: np.ndarray, N: int, K
     y = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64)
     st = np.zeros(1, np.int32)
-    rc = _load().oracle_matmul(_ptr(x), _ptr(p), _ptr(s), M, N, K, G, _ptr(y), _ptr(bound), _ptr(st))
+    rc = _load().oracle_matmul_mt(_ptr(x), _ptr(p), _ptr(s), M, N, K, G, _ptr(y), _ptr(bound),
+                                  _ptr(st), _threads(threads))
     if rc:
         raise OracleError("oracle_matmul rc=%d" % rc)
     return y, bound, int(st[0])
@@ -275,7 +304,7 @@ def w4a16_dequantize(packed, scales, biases, N: int, K: int, G: int) -> np.ndarr
     return w
 
 
-def w4a16_matmul(x_bits, packed, scales, biases, N: int, K: int, G: int):
+def w4a16_matmul(x_bits, packed, scales, biases, N: int, K: int, G: int, threads=None):
     """x bf16 bits [M,K] -> (y float64 [M,N], bound float64 [M,N] =
     sum_k |x| (|q s| + |b|))."""
     x = np.ascontiguousarray(x_bits, dtype=np.uint16)
@@ -289,8 +318,8 @@ def w4a16_matmul(x_bits, packed, scales, biases, N: int, K: int, G: int):
         raise OracleError("bad packed/scales/biases sizes")
     y = np.empty((M, N), np.float64)
     bound = np.empty((M, N), np.float64)
-    rc = _load().oracle_w4a16_matmul(_ptr(x), _ptr(p), _ptr(s), _ptr(b), M, N, K, G, _ptr(y),
-                                     _ptr(bound))
+    rc = _load().oracle_w4a16_matmul_mt(_ptr(x), _ptr(p), _ptr(s), _ptr(b), M, N, K, G, _ptr(y),
+                                        _ptr(bound), _threads(threads))
     if rc:
         raise OracleError("oracle_w4a16_matmul rc=%d" % rc)
     return y, bound

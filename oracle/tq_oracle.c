@@ -39,6 +39,7 @@
  * bits), so only the order of the fp64 sum rounds.
  */
 #include <math.h>
+#include <pthread.h>
 #include <stdint.h>
 #include <stddef.h>
 #include <stdlib.h>
@@ -498,10 +499,12 @@ int oracle_unpack2(const uint8_t *packed, int64_t N, int64_t K, int64_t G, int8_
                    int32_t *status);
 
 /* y = x * W_hat^T over rows decoded from the base-3 format (two_bit = 0) or
- * the 2-bit format (two_bit = 1). */
+ * the 2-bit format (two_bit = 1), for the weight rows n0 <= n < n1 (every
+ * output y[m][n] is computed on its own, so any split of the rows gives the
+ * same values). */
 static int matmul_rows(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
                        int64_t M, int64_t N, int64_t K, int64_t G, int two_bit,
-                       double *y, double *bound, int32_t *status)
+                       int64_t n0, int64_t n1, double *y, double *bound, int32_t *status)
 {
     if (!x || !packed || !scales || !y) return OR_ERR_NULL;
     if (M < 1) return OR_ERR_SHAPE;
@@ -516,7 +519,7 @@ static int matmul_rows(const uint16_t *x, const uint8_t *packed, const uint16_t 
     for (int64_t i = 0; i < M * K; ++i) xd[i] = bf16_to_double(x[i]);
     int32_t st = 0;
 
-    for (int64_t n = 0; n < N; ++n) {
+    for (int64_t n = n0; n < n1; ++n) {
         /* decode row n: w_hat = c * s */
         int32_t rst = 0;
         if (two_bit) oracle_unpack2(packed + n * (K / 4), 1, K, G, crow, &rst);
@@ -552,7 +555,7 @@ int oracle_matmul(const uint16_t *x, const uint8_t *packed, const uint16_t *scal
                   int64_t M, int64_t N, int64_t K, int64_t G,
                   double *y, double *bound, int32_t *status)
 {
-    return matmul_rows(x, packed, scales, M, N, K, G, 0, y, bound, status);
+    return matmul_rows(x, packed, scales, M, N, K, G, 0, 0, N, y, bound, status);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -621,7 +624,7 @@ int oracle_matmul2(const uint16_t *x, const uint8_t *packed, const uint16_t *sca
                    int64_t M, int64_t N, int64_t K, int64_t G,
                    double *y, double *bound, int32_t *status)
 {
-    return matmul_rows(x, packed, scales, M, N, K, G, 1, y, bound, status);
+    return matmul_rows(x, packed, scales, M, N, K, G, 1, 0, N, y, bound, status);
 }
 
 
@@ -695,9 +698,9 @@ int oracle_w4a16_dequantize(const uint32_t *packed, const uint16_t *scales,
  * bound[m][n] = sum_k |x[m][k]| * (|q s| + |b|): the size of the terms of
  * the factored form s * sum(x q) + b * sum(x) that a kernel may evaluate.
  */
-int oracle_w4a16_matmul(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
-                        const uint16_t *biases, int64_t M, int64_t N, int64_t K, int64_t G,
-                        double *y, double *bound)
+static int w4a16_matmul_rows(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                             const uint16_t *biases, int64_t M, int64_t N, int64_t K, int64_t G,
+                             int64_t n0, int64_t n1, double *y, double *bound)
 {
     if (!x || !packed || !scales || !biases || !y || !bound) return OR_ERR_NULL;
     int rc = check_w4(N, K, G);
@@ -705,7 +708,7 @@ int oracle_w4a16_matmul(const uint16_t *x, const uint32_t *packed, const uint16_
     if (M < 1) return OR_ERR_SHAPE;
     const int64_t nG = K / G;
     for (int64_t m = 0; m < M; ++m)
-        for (int64_t n = 0; n < N; ++n) {
+        for (int64_t n = n0; n < n1; ++n) {
             const uint32_t *row = packed + n * (K / 8);
             double acc = 0.0, bacc = 0.0;
             for (int64_t g = 0; g < nG; ++g) {
@@ -725,4 +728,145 @@ int oracle_w4a16_matmul(const uint16_t *x, const uint32_t *packed, const uint16_
             bound[m * N + n] = bacc;
         }
     return OR_OK;
+}
+
+int oracle_w4a16_matmul(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                        const uint16_t *biases, int64_t M, int64_t N, int64_t K, int64_t G,
+                        double *y, double *bound)
+{
+    return w4a16_matmul_rows(x, packed, scales, biases, M, N, K, G, 0, N, y, bound);
+}
+
+/* ------------------------------------------------------------------------ */
+/* Row-partitioned threading (for test and baseline throughput only)        */
+/* ------------------------------------------------------------------------ */
+
+/*
+ * The _mt entry points split the weight rows into `threads` contiguous
+ * ranges and run the single-thread code above on each range in its own
+ * POSIX thread.  No output depends on another row, and each output is
+ * computed by the same loop in the same order as in the single-thread call,
+ * so the results are identical for every thread count.
+ */
+enum { MT_QUANT, MT_MATMUL, MT_MATMUL2, MT_W4A16 };
+
+typedef struct {
+    int kind;
+    const uint16_t *x, *w, *scales_in, *biases;
+    const void *packed_in;
+    uint8_t *packed_out;
+    uint16_t *scales_out;
+    int64_t M, N, K, G, n0, n1;
+    double *y, *bound;
+    int32_t status;
+    int rc;
+} mt_job;
+
+static void *mt_run(void *arg)
+{
+    mt_job *j = (mt_job *)arg;
+    j->status = 0;
+    switch (j->kind) {
+    case MT_QUANT: {
+        const int64_t rb = oracle_packed_row_bytes(j->K, j->G), nG = j->K / j->G;
+        j->rc = j->n1 > j->n0
+                    ? oracle_quantize_pack(j->w + j->n0 * j->K, j->n1 - j->n0, j->K, j->G,
+                                           j->packed_out + j->n0 * rb,
+                                           j->scales_out + j->n0 * nG, &j->status)
+                    : OR_OK;
+        break;
+    }
+    case MT_MATMUL:
+    case MT_MATMUL2:
+        j->rc = matmul_rows(j->x, (const uint8_t *)j->packed_in, j->scales_in, j->M, j->N, j->K,
+                            j->G, j->kind == MT_MATMUL2, j->n0, j->n1, j->y, j->bound,
+                            &j->status);
+        break;
+    default:
+        j->rc = w4a16_matmul_rows(j->x, (const uint32_t *)j->packed_in, j->scales_in, j->biases,
+                                  j->M, j->N, j->K, j->G, j->n0, j->n1, j->y, j->bound);
+        break;
+    }
+    return NULL;
+}
+
+static int mt_split(mt_job proto, int threads, int32_t *status)
+{
+    if (threads < 1) threads = 1;
+    if (threads > 256) threads = 256;
+    if (threads > proto.N) threads = (int)(proto.N > 0 ? proto.N : 1);
+    mt_job jobs[256];
+    pthread_t tids[256];
+    int started[256];
+    for (int t = 0; t < threads; ++t) {
+        jobs[t] = proto;
+        jobs[t].n0 = proto.N * t / threads;
+        jobs[t].n1 = proto.N * (t + 1) / threads;
+        started[t] = t > 0 && pthread_create(&tids[t], NULL, mt_run, &jobs[t]) == 0;
+        if (t > 0 && !started[t]) mt_run(&jobs[t]);  /* no thread: run it here */
+    }
+    mt_run(&jobs[0]);
+    int rc = OR_OK;
+    int32_t st = 0;
+    for (int t = 0; t < threads; ++t) {
+        if (started[t]) pthread_join(tids[t], NULL);
+        if (jobs[t].rc && !rc) rc = jobs[t].rc;
+        st |= jobs[t].status;
+    }
+    if (!rc && status) *status |= st;
+    return rc;
+}
+
+int oracle_quantize_pack_mt(const uint16_t *w, int64_t N, int64_t K, int64_t G,
+                            uint8_t *packed, uint16_t *scales, int32_t *status, int threads)
+{
+    if (!w || !packed || !scales) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    mt_job p = {0};
+    p.kind = MT_QUANT; p.w = w; p.packed_out = packed; p.scales_out = scales;
+    p.N = N; p.K = K; p.G = G;
+    return mt_split(p, threads, status);
+}
+
+int oracle_matmul_mt(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                     int64_t M, int64_t N, int64_t K, int64_t G, double *y, double *bound,
+                     int32_t *status, int threads)
+{
+    if (!x || !packed || !scales || !y) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    if (M < 1) return OR_ERR_SHAPE;
+    mt_job p = {0};
+    p.kind = MT_MATMUL; p.x = x; p.packed_in = packed; p.scales_in = scales;
+    p.M = M; p.N = N; p.K = K; p.G = G; p.y = y; p.bound = bound;
+    return mt_split(p, threads, status);
+}
+
+int oracle_matmul2_mt(const uint16_t *x, const uint8_t *packed, const uint16_t *scales,
+                      int64_t M, int64_t N, int64_t K, int64_t G, double *y, double *bound,
+                      int32_t *status, int threads)
+{
+    if (!x || !packed || !scales || !y) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    if (M < 1 || G % 4) return OR_ERR_SHAPE;
+    mt_job p = {0};
+    p.kind = MT_MATMUL2; p.x = x; p.packed_in = packed; p.scales_in = scales;
+    p.M = M; p.N = N; p.K = K; p.G = G; p.y = y; p.bound = bound;
+    return mt_split(p, threads, status);
+}
+
+int oracle_w4a16_matmul_mt(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                           const uint16_t *biases, int64_t M, int64_t N, int64_t K, int64_t G,
+                           double *y, double *bound, int threads)
+{
+    if (!x || !packed || !scales || !biases || !y || !bound) return OR_ERR_NULL;
+    int rc = check_w4(N, K, G);
+    if (rc) return rc;
+    if (M < 1) return OR_ERR_SHAPE;
+    mt_job p = {0};
+    p.kind = MT_W4A16; p.x = x; p.packed_in = packed; p.scales_in = scales; p.biases = biases;
+    p.M = M; p.N = N; p.K = K; p.G = G; p.y = y; p.bound = bound;
+    return mt_split(p, threads, NULL);
 }

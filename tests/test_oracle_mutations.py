@@ -79,7 +79,8 @@ PINS = [
 FUNCTIONS = ("oracle_packed_row_bytes", "oracle_quantize_pack", "oracle_unpack", "oracle_matmul",
              "oracle_dequantize", "oracle_fake_quantize", "oracle_quantize_pack2",
              "oracle_unpack2", "oracle_matmul2", "oracle_w4_unpack", "oracle_w4a16_dequantize",
-             "oracle_w4a16_matmul")
+             "oracle_w4a16_matmul", "oracle_quantize_pack_mt", "oracle_matmul_mt",
+             "oracle_matmul2_mt", "oracle_w4a16_matmul_mt")
 
 
 def _load_variant(path, real):
@@ -102,7 +103,8 @@ def test_planted_mistake_is_caught(name):
         c = os.path.join(d, "m.c")
         so = os.path.join(d, "libm.so")
         open(c, "w").write(src.replace(old, new))
-        subprocess.check_call(["gcc", "-O1", "-std=c11", "-w", "-fPIC", "-shared", "-o", so, c, "-lm"])
+        subprocess.check_call(["gcc", "-O1", "-std=c11", "-w", "-fPIC", "-pthread", "-shared", "-o",
+                               so, c, "-lm"])
         saved = oracle._load()
         oracle._lib = _load_variant(so, saved)
         failures = 0
