@@ -74,8 +74,14 @@ enum {
 /* Human-readable name of a tq_status value. */
 const char *tq_status_string(int status);
 
-/* Packed bytes of an [N,K] matrix: N * (K/G) * ceil(G/5); 0 on bad arguments
- * (host-only helper, any G >= 1). */
+/* Packed bytes of one row of K weights: (K/G) * ceil(G/5), each group
+ * byte-aligned in ceil(G/5) bytes (precisit "pack-unpack-run" README,
+ * codec.py description); 0 on bad arguments (K < 1, G < 1, K % G != 0).
+ * Host-only helper, any G >= 1. */
+int64_t tq_packed_row_bytes(int64_t K, int G);
+
+/* Packed bytes of an [N,K] matrix: N * tq_packed_row_bytes(K, G); 0 on bad
+ * arguments or when the count overflows int64 (host-only helper). */
 int64_t tq_packed_bytes(int64_t N, int64_t K, int G);
 
 /*

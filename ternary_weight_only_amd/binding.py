@@ -1,8 +1,9 @@
 """ctypes binding of libtq.so (C ABI: include/tq.h).
 
 Argument marshalling only: shape/dtype/device/contiguity checks on torch
-tensors, output allocation, raw device pointers and the current HIP stream.
-Every step of the computation runs in the library's kernels.
+tensors -- inputs, caller-supplied outputs and status words alike -- output
+allocation, raw device pointers and the current HIP stream.  Every step of
+the computation runs in the library's kernels.
 """
 from __future__ import annotations
 
@@ -20,13 +21,21 @@ DEV_INVALID_BYTE = 4
 DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
-SYMBOLS = ("tq_status_string", "tq_packed_bytes", "tq_quantize_pack", "tq_quantize_pack_batched",
-           "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack", "tq_unpack_batched",
-           "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2", "tq_quantize_pack2_batched", "tq_unpack2",
-           "tq_gemv2", "tq_gemv2_batched", "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched",
-           "tq_w4a16_gemv_grouped", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_quantize_pack",
+           "tq_quantize_pack_batched", "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack",
+           "tq_unpack_batched", "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2",
+           "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
+           "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
+           "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 
 _lib = None
+
+BF16 = (torch.bfloat16, torch.int16)
+F16 = (torch.float16, torch.int16)
+U8 = (torch.uint8,)
+I8 = (torch.int8,)
+F32 = (torch.float32,)
+W4 = (torch.int32, torch.uint32)
 
 
 class TQError(RuntimeError):
@@ -44,6 +53,8 @@ def lib() -> ctypes.CDLL:
         p, i64, i32 = ctypes.c_void_p, ctypes.c_int64, ctypes.c_int
         l.tq_status_string.argtypes = [i32]
         l.tq_status_string.restype = ctypes.c_char_p
+        l.tq_packed_row_bytes.argtypes = [i64, i32]
+        l.tq_packed_row_bytes.restype = i64
         l.tq_packed_bytes.argtypes = [i64, i64, i32]
         l.tq_packed_bytes.restype = i64
         l.tq_quantize_pack.argtypes = [p, i64, i64, i32, p, p, p, p]
@@ -100,21 +111,94 @@ def _stream() -> int:
     return torch.cuda.current_stream().cuda_stream
 
 
-def _dev(t: torch.Tensor, name: str, dtypes, ndim: int):
+# ---------------------------------------------------------------------------
+# validation: nothing reaches the library unless every tensor it will read
+# or write is a contiguous device tensor of the expected dtype and size on
+# the device of the call's first input
+# ---------------------------------------------------------------------------
+
+def _dev(t, name: str, dtypes, ndim=None, device=None):
+    """An input: a contiguous device tensor of one of `dtypes` (and `ndim`
+    dimensions, and on `device`, when given)."""
     if not isinstance(t, torch.Tensor) or not t.is_cuda:
         raise TQError("%s must be a device tensor" % name)
+    if device is not None and t.device != device:
+        raise TQError("%s is on %s, expected %s" % (name, t.device, device))
     if t.dtype not in dtypes:
         raise TQError("%s has dtype %s, expected one of %s" % (name, t.dtype, dtypes))
-    if t.dim() != ndim or not t.is_contiguous():
-        raise TQError("%s must be a contiguous %d-D tensor" % (name, ndim))
+    if not t.is_contiguous():
+        raise TQError("%s must be contiguous" % name)
+    if ndim is not None and t.dim() != ndim:
+        raise TQError("%s must be a %d-D tensor" % (name, ndim))
+    return t
 
 
-def _st(status):
-    return 0 if status is None else status.data_ptr()
+def _out(t, name: str, shape, dtype, dtypes, device):
+    """A call's output: allocated here as `shape` of `dtype` when `t` is
+    None; otherwise it must be a contiguous tensor of one of `dtypes` on
+    `device` holding exactly as many elements as `shape`."""
+    if t is None:
+        return torch.empty(shape, dtype=dtype, device=device)
+    _dev(t, name, dtypes, None, device)
+    n = 1
+    for d in shape:
+        n *= int(d)
+    if t.numel() != n:
+        raise TQError("%s has %d elements, expected %d (%s)" % (name, t.numel(), n, tuple(shape)))
+    return t
+
+
+def _outs(ts, name: str, shapes, dtype, dtypes, device):
+    """Outputs of a batched call: one per problem, as _out."""
+    if ts is None:
+        return [torch.empty(s, dtype=dtype, device=device) for s in shapes]
+    ts = list(ts)
+    if len(ts) != len(shapes):
+        raise TQError("%s: %d outputs for %d problems" % (name, len(ts), len(shapes)))
+    return [_out(t, "%s[%d]" % (name, i), s, dtype, dtypes, device)
+            for i, (t, s) in enumerate(zip(ts, shapes))]
+
+
+def _st(status, device) -> int:
+    """The device address of a status word: an int32 tensor of at least one
+    element on `device`, or None (no reporting)."""
+    if status is None:
+        return 0
+    if not isinstance(status, torch.Tensor) or not status.is_cuda or status.device != device:
+        raise TQError("status must be an int32 tensor on %s" % device)
+    if status.dtype != torch.int32 or status.numel() < 1 or not status.is_contiguous():
+        raise TQError("status must be a contiguous int32 tensor of at least one element")
+    return status.data_ptr()
+
+
+def packed_row_bytes(K: int, G: int) -> int:
+    """Packed bytes of one row: (K/G) * ceil(G/5); 0 for invalid arguments."""
+    return int(lib().tq_packed_row_bytes(K, G))
 
 
 def packed_bytes(N: int, K: int, G: int) -> int:
     return int(lib().tq_packed_bytes(N, K, G))
+
+
+def _groups(K: int, G: int) -> int:
+    return K // G if G > 0 and K % G == 0 else 0
+
+
+def _check_packed(packed, scales, N, K, G, device, what):
+    _dev(packed, "packed", U8, None, device)
+    _dev(scales, "scales", F16 + (torch.uint16,), None, device)
+    if packed.numel() != packed_bytes(N, K, G) or scales.numel() != N * _groups(K, G) \
+            or packed.numel() == 0:
+        raise TQError("%s: packed/scales sizes (%d, %d) do not match N=%d K=%d G=%d"
+                      % (what, packed.numel(), scales.numel(), N, K, G))
+
+
+def _ptrs(ts):
+    return (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
+
+
+def _i64s(vals):
+    return (ctypes.c_int64 * max(len(vals), 1))(*[int(v) for v in vals])
 
 
 def new_status(device=None) -> torch.Tensor:
@@ -127,18 +211,23 @@ def check(status: torch.Tensor) -> int:
     return int(status.item())
 
 
+# ---------------------------------------------------------------------------
+# quantize / QAT forward / unpack / decode
+# ---------------------------------------------------------------------------
+
 def quantize_pack(w: torch.Tensor, G: int, status=None, out=None):
-    """w: [N,K] bf16 -> (packed uint8 [N, (K/G)*ceil(G/5)], scales fp16 [N, K/G])."""
-    _dev(w, "w", (torch.bfloat16, torch.int16), 2)
+    """w: [N,K] bf16 -> (packed uint8 [N, (K/G)*ceil(G/5)], scales fp16 [N, K/G]).
+    `out`, if given, is a (packed, scales) pair of that size."""
+    _dev(w, "w", BF16, 2)
     N, K = w.shape
-    rb = (K // G) * ((G + 4) // 5) if G > 0 and K % G == 0 else 0
-    if out is None:
-        packed = torch.empty((N, max(rb, 1)), dtype=torch.uint8, device=w.device)
-        scales = torch.empty((N, max(K // G, 1)), dtype=torch.float16, device=w.device)
-    else:
-        packed, scales = out
+    rb, ng = packed_row_bytes(K, G), _groups(K, G)
+    if rb == 0:
+        raise TQError("quantize_pack: K=%d is not a multiple of G=%d" % (K, G))
+    packed, scales = (None, None) if out is None else out
+    packed = _out(packed, "packed", (N, rb), torch.uint8, U8, w.device)
+    scales = _out(scales, "scales", (N, ng), torch.float16, F16, w.device)
     _rc(lib().tq_quantize_pack(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
-                               _st(status), _stream()), "tq_quantize_pack")
+                               _st(status, w.device), _stream()), "tq_quantize_pack")
     return packed, scales
 
 
@@ -147,28 +236,23 @@ def fake_quantize(w: torch.Tensor, G: int, status=None, out=None, scales_out=Non
 
     scales_out, if given, is an fp16 [N, K/G] tensor that receives the
     scales.  Use FakeQuantize.apply for the straight-through gradient."""
-    _dev(w, "w", (torch.bfloat16, torch.int16), 2)
+    _dev(w, "w", BF16, 2)
     N, K = w.shape
-    w_hat = torch.empty((N, K), dtype=torch.bfloat16, device=w.device) if out is None else out
+    w_hat = _out(out, "w_hat", (N, K), torch.bfloat16, BF16, w.device)
     sp = 0
     if scales_out is not None:
-        _dev(scales_out, "scales_out", (torch.float16, torch.int16), scales_out.dim())
-        if G <= 0 or scales_out.numel() != N * (K // G):
-            raise TQError("scales_out has %d entries, expected %d" % (scales_out.numel(),
-                                                                    N * (K // max(G, 1))))
-        sp = scales_out.data_ptr()
-    _rc(lib().tq_fake_quantize(w.data_ptr(), N, K, G, w_hat.data_ptr(), sp, _st(status),
-                               _stream()), "tq_fake_quantize")
+        if _groups(K, G) == 0:
+            raise TQError("fake_quantize: K=%d is not a multiple of G=%d" % (K, G))
+        sp = _out(scales_out, "scales_out", (N, _groups(K, G)), torch.float16, F16,
+                  w.device).data_ptr()
+    _rc(lib().tq_fake_quantize(w.data_ptr(), N, K, G, w_hat.data_ptr(), sp,
+                               _st(status, w.device), _stream()), "tq_fake_quantize")
     return w_hat
-
-
-def _ptrs(ts):
-    return (ctypes.c_void_p * max(len(ts), 1))(*[t.data_ptr() for t in ts])
 
 
 def _same_shape(ws, name):
     for w in ws:
-        _dev(w, name, (torch.bfloat16, torch.int16), 2)
+        _dev(w, name, BF16, 2, ws[0].device)
     shapes = {tuple(w.shape) for w in ws}
     if len(shapes) > 1:
         raise TQError("%s: matrices of different shapes %s" % (name, sorted(shapes)))
@@ -180,12 +264,14 @@ def quantize_pack_batched(ws, G: int, status=None):
     N, K = _same_shape(ws, "w")
     if not ws:
         return []
-    rb = (K // G) * ((G + 4) // 5) if G > 0 and K % G == 0 else 0
+    rb, ng = packed_row_bytes(K, G), _groups(K, G)
+    if rb == 0:
+        raise TQError("quantize_pack_batched: K=%d is not a multiple of G=%d" % (K, G))
     dev = ws[0].device
-    pk = [torch.empty((N, max(rb, 1)), dtype=torch.uint8, device=dev) for _ in ws]
-    sc = [torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=dev) for _ in ws]
+    pk = [torch.empty((N, rb), dtype=torch.uint8, device=dev) for _ in ws]
+    sc = [torch.empty((N, ng), dtype=torch.float16, device=dev) for _ in ws]
     _rc(lib().tq_quantize_pack_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(pk), _ptrs(sc),
-                                       _st(status), _stream()), "tq_quantize_pack_batched")
+                                       _st(status, dev), _stream()), "tq_quantize_pack_batched")
     return list(zip(pk, sc))
 
 
@@ -197,170 +283,67 @@ def fake_quantize_batched(ws, G: int, status=None, with_scales: bool = False):
         return []
     dev = ws[0].device
     wh = [torch.empty((N, K), dtype=torch.bfloat16, device=dev) for _ in ws]
-    sc = [torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=dev)
+    if with_scales and _groups(K, G) == 0:
+        raise TQError("fake_quantize_batched: K=%d is not a multiple of G=%d" % (K, G))
+    sc = [torch.empty((N, _groups(K, G)), dtype=torch.float16, device=dev)
           for _ in ws] if with_scales else None
     _rc(lib().tq_fake_quantize_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(wh),
-                                       _ptrs(sc) if with_scales else None, _st(status),
+                                       _ptrs(sc) if with_scales else None, _st(status, dev),
                                        _stream()), "tq_fake_quantize_batched")
     return list(zip(wh, sc)) if with_scales else wh
 
 
+def unpack(packed: torch.Tensor, N: int, K: int, G: int, status=None, out=None):
+    """packed -> codes int8 [N,K]."""
+    _dev(packed, "packed", U8)
+    if packed.numel() != packed_bytes(N, K, G) or packed.numel() == 0:
+        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), packed_bytes(N, K, G)))
+    codes = _out(out, "codes", (N, K), torch.int8, I8, packed.device)
+    _rc(lib().tq_unpack(packed.data_ptr(), N, K, G, codes.data_ptr(), _st(status, packed.device),
+                        _stream()), "tq_unpack")
+    return codes
+
+
 def unpack_batched(packeds, N: int, K: int, G: int, status=None):
     """Same-shaped packed matrices -> list of int8 codes [N,K], one launch per 64."""
-    for p in packeds:
-        _dev(p, "packed", (torch.uint8,), p.dim())
-        if p.numel() != packed_bytes(N, K, G):
-            raise TQError("packed has %d bytes, expected %d" % (p.numel(), packed_bytes(N, K, G)))
     if not packeds:
         return []
-    codes = [torch.empty((N, K), dtype=torch.int8, device=p.device) for p in packeds]
-    _rc(lib().tq_unpack_batched(len(packeds), _ptrs(packeds), N, K, G, _ptrs(codes), _st(status),
-                                _stream()), "tq_unpack_batched")
+    dev = packeds[0].device if isinstance(packeds[0], torch.Tensor) else None
+    for p in packeds:
+        _dev(p, "packed", U8, None, dev)
+        if p.numel() != packed_bytes(N, K, G) or p.numel() == 0:
+            raise TQError("packed has %d bytes, expected %d" % (p.numel(), packed_bytes(N, K, G)))
+    codes = [torch.empty((N, K), dtype=torch.int8, device=dev) for _ in packeds]
+    _rc(lib().tq_unpack_batched(len(packeds), _ptrs(packeds), N, K, G, _ptrs(codes),
+                                _st(status, dev), _stream()), "tq_unpack_batched")
     return codes
 
 
-def quantize_pack2(w: torch.Tensor, G: int, status=None):
-    """2-bit format: w [N,K] bf16 -> (packed2 uint8 [N, K/4], scales fp16 [N, K/G])."""
-    _dev(w, "w", (torch.bfloat16, torch.int16), 2)
-    N, K = w.shape
-    packed = torch.empty((N, max(K // 4, 1)), dtype=torch.uint8, device=w.device)
-    scales = torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=w.device)
-    _rc(lib().tq_quantize_pack2(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
-                                _st(status), _stream()), "tq_quantize_pack2")
-    return packed, scales
+def dequantize(packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int, status=None,
+               out=None):
+    """(packed, fp16 scales) -> w_hat bf16 [N,K] = bf16(c * s)."""
+    _dev(packed, "packed", U8)
+    _check_packed(packed, scales, N, K, G, packed.device, "dequantize")
+    w_hat = _out(out, "w_hat", (N, K), torch.bfloat16, BF16, packed.device)
+    _rc(lib().tq_dequantize(packed.data_ptr(), scales.data_ptr(), N, K, G, w_hat.data_ptr(),
+                            _st(status, packed.device), _stream()), "tq_dequantize")
+    return w_hat
 
 
-def quantize_pack2_batched(ws, G: int, status=None):
-    """2-bit format, same-shaped bf16 matrices -> list of (packed2, scales),
-    one launch per 64."""
-    N, K = _same_shape(ws, "w")
-    if not ws:
+def dequantize_batched(packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """Same-shaped (packed, scales) pairs -> list of bf16 [N,K], one launch per 64."""
+    n = len(packeds)
+    if len(scales_list) != n:
+        raise TQError("packeds and scales differ in length")
+    if n == 0:
         return []
-    dev = ws[0].device
-    pk = [torch.empty((N, max(K // 4, 1)), dtype=torch.uint8, device=dev) for _ in ws]
-    sc = [torch.empty((N, max(K // max(G, 1), 1)), dtype=torch.float16, device=dev) for _ in ws]
-    _rc(lib().tq_quantize_pack2_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(pk), _ptrs(sc),
-                                        _st(status), _stream()), "tq_quantize_pack2_batched")
-    return list(zip(pk, sc))
-
-
-def unpack2(packed: torch.Tensor, N: int, K: int, G: int, status=None):
-    """2-bit packed [N, K/4] -> codes int8 [N,K]."""
-    _dev(packed, "packed", (torch.uint8,), packed.dim())
-    if packed.numel() * 4 != N * K:
-        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), N * K // 4))
-    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
-    _rc(lib().tq_unpack2(packed.data_ptr(), N, K, G, codes.data_ptr(), _st(status), _stream()),
-        "tq_unpack2")
-    return codes
-
-
-def gemv2(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int,
-          status=None, out=None):
-    """2-bit format, M = 1: x [1,K] bf16 -> y fp32 [1,N]."""
-    _dev(x, "x", (torch.bfloat16, torch.int16), 2)
-    _dev(packed, "packed", (torch.uint8,), packed.dim())
-    _dev(scales, "scales", (torch.float16, torch.int16), scales.dim())
-    if tuple(x.shape) != (1, K) or packed.numel() * 4 != N * K or scales.numel() != N * (K // G):
-        raise TQError("gemv2: shapes do not match N=%d K=%d G=%d" % (N, K, G))
-    y = torch.empty((1, N), dtype=torch.float32, device=x.device) if out is None else out
-    _rc(lib().tq_gemv2(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K, G, y.data_ptr(),
-                       _st(status), _stream()), "tq_gemv2")
-    return y
-
-
-def gemv2_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
-    """2-bit format, M = 1, same-shaped problems: list of y fp32 [1,N], one launch per 64."""
-    n = len(xs)
-    if len(packeds) != n or len(scales_list) != n:
-        raise TQError("xs, packeds and scales differ in length")
-    for x, pk, sc in zip(xs, packeds, scales_list):
-        _dev(x, "x", (torch.bfloat16, torch.int16), 2)
-        _dev(pk, "packed", (torch.uint8,), pk.dim())
-        _dev(sc, "scales", (torch.float16, torch.int16), sc.dim())
-        if (tuple(x.shape) != (1, K) or pk.numel() * 4 != N * K or G <= 0
-                or sc.numel() != N * (K // G)):
-            raise TQError("gemv2_batched: shapes do not match N=%d K=%d G=%d" % (N, K, G))
-    if outs is None:
-        outs = [torch.empty((1, N), dtype=torch.float32, device=x.device) for x in xs]
-    _rc(lib().tq_gemv2_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
-                               N, K, G, _st(status), _stream()), "tq_gemv2_batched")
-    return outs
-
-
-def _w4_check(x, packed, scales, biases, N, K, G):
-    _dev(x, "x", (torch.bfloat16, torch.int16), 2)
-    _dev(packed, "packed", (torch.int32, torch.uint32), packed.dim())
-    _dev(scales, "scales", (torch.bfloat16, torch.int16), scales.dim())
-    _dev(biases, "biases", (torch.bfloat16, torch.int16), biases.dim())
-    if (tuple(x.shape) != (1, K) or packed.numel() * 8 != N * K or G <= 0
-            or scales.numel() != N * (K // G) or biases.numel() != scales.numel()):
-        raise TQError("w4a16: shapes do not match N=%d K=%d G=%d" % (N, K, G))
-
-
-def w4a16_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
-               biases: torch.Tensor, N: int, K: int, G: int, out=None):
-    """W4A16, M = 1: x [1,K] bf16, packed int32/uint32 [N, K/8], scales and
-    biases bf16 [N, K/G] -> y bf16 [1,N]."""
-    _w4_check(x, packed, scales, biases, N, K, G)
-    y = torch.empty((1, N), dtype=torch.bfloat16, device=x.device) if out is None else out
-    _rc(lib().tq_w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(),
-                            biases.data_ptr(), N, K, G, y.data_ptr(), _stream()),
-        "tq_w4a16_gemv")
-    return y
-
-
-def w4a16_gemv_batched(xs, packeds, scales_list, biases_list, N: int, K: int, G: int,
-                       outs=None):
-    """Same-shaped W4A16 problems -> list of y bf16 [1,N], one launch per 64."""
-    n = len(xs)
-    if not (len(packeds) == len(scales_list) == len(biases_list) == n):
-        raise TQError("xs, packeds, scales and biases differ in length")
-    for x, pk, sc, bi in zip(xs, packeds, scales_list, biases_list):
-        _w4_check(x, pk, sc, bi, N, K, G)
-    if outs is None:
-        outs = [torch.empty((1, N), dtype=torch.bfloat16, device=x.device) for x in xs]
-    _rc(lib().tq_w4a16_gemv_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
-                                    _ptrs(biases_list), _ptrs(outs), N, K, G, _stream()),
-        "tq_w4a16_gemv_batched")
-    return outs
-
-
-def gemv2_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
-    """2-bit format, M = 1, problems of mixed shapes in one launch:
-    list of y fp32 [1, Ns[i]]."""
-    n = len(xs)
-    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == n):
-        raise TQError("xs, packeds, scales, Ns and Ks differ in length")
-    for x, pk, sc, N, K in zip(xs, packeds, scales_list, Ns, Ks):
-        _dev(x, "x", (torch.bfloat16, torch.int16), 2)
-        _dev(pk, "packed", (torch.uint8,), pk.dim())
-        _dev(sc, "scales", (torch.float16, torch.int16), sc.dim())
-        if (tuple(x.shape) != (1, K) or pk.numel() * 4 != N * K or G <= 0
-                or sc.numel() != N * (K // G)):
-            raise TQError("gemv2_grouped: shapes do not match N=%d K=%d G=%d" % (N, K, G))
-    if outs is None:
-        outs = [torch.empty((1, N), dtype=torch.float32, device=x.device) for x, N in zip(xs, Ns)]
-    i64s = ctypes.c_int64 * max(n, 1)
-    _rc(lib().tq_gemv2_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
-                               i64s(*Ns), i64s(*Ks), G, _st(status), _stream()),
-        "tq_gemv2_grouped")
-    return outs
-
-
-def w4a16_gemv_grouped(xs, packeds, scales_list, biases_list, Ns, Ks, G: int, outs=None):
-    """W4A16 problems of mixed shapes in one launch -> list of y bf16 [1, Ns[i]]."""
-    n = len(xs)
-    if not (len(packeds) == len(scales_list) == len(biases_list) == len(Ns) == len(Ks) == n):
-        raise TQError("xs, packeds, scales, biases, Ns and Ks differ in length")
-    for x, pk, sc, bi, N, K in zip(xs, packeds, scales_list, biases_list, Ns, Ks):
-        _w4_check(x, pk, sc, bi, N, K, G)
-    if outs is None:
-        outs = [torch.empty((1, N), dtype=torch.bfloat16, device=x.device) for x, N in zip(xs, Ns)]
-    i64s = ctypes.c_int64 * max(n, 1)
-    _rc(lib().tq_w4a16_gemv_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
-                                    _ptrs(biases_list), _ptrs(outs), i64s(*Ns), i64s(*Ks), G,
-                                    _stream()), "tq_w4a16_gemv_grouped")
+    _dev(packeds[0], "packed", U8)
+    dev = packeds[0].device
+    for pk, sc in zip(packeds, scales_list):
+        _check_packed(pk, sc, N, K, G, dev, "dequantize_batched")
+    outs = _outs(outs, "outs", [(N, K)] * n, torch.bfloat16, BF16, dev)
+    _rc(lib().tq_dequantize_batched(n, _ptrs(packeds), _ptrs(scales_list), _ptrs(outs), N, K, G,
+                                    _st(status, dev), _stream()), "tq_dequantize_batched")
     return outs
 
 
@@ -378,64 +361,20 @@ class FakeQuantize(torch.autograd.Function):
         return grad, None
 
 
-def unpack(packed: torch.Tensor, N: int, K: int, G: int, status=None, out=None):
-    """packed -> codes int8 [N,K]."""
-    _dev(packed, "packed", (torch.uint8,), packed.dim())
-    if packed.numel() != packed_bytes(N, K, G):
-        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), packed_bytes(N, K, G)))
-    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device) if out is None else out
-    _rc(lib().tq_unpack(packed.data_ptr(), N, K, G, codes.data_ptr(), _st(status), _stream()),
-        "tq_unpack")
-    return codes
-
-
-def dequantize(packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int, status=None,
-               out=None):
-    """(packed, fp16 scales) -> w_hat bf16 [N,K] = bf16(c * s)."""
-    _dev(packed, "packed", (torch.uint8,), packed.dim())
-    _dev(scales, "scales", (torch.float16, torch.int16, torch.uint16), scales.dim())
-    if packed.numel() != packed_bytes(N, K, G):
-        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), packed_bytes(N, K, G)))
-    if G <= 0 or scales.numel() != N * (K // G):
-        raise TQError("scales has %d entries, expected %d" % (scales.numel(), N * (K // max(G, 1))))
-    w_hat = torch.empty((N, K), dtype=torch.bfloat16, device=packed.device) if out is None else out
-    _rc(lib().tq_dequantize(packed.data_ptr(), scales.data_ptr(), N, K, G, w_hat.data_ptr(),
-                            _st(status), _stream()), "tq_dequantize")
-    return w_hat
-
-
-def dequantize_batched(packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
-    """Same-shaped (packed, scales) pairs -> list of bf16 [N,K], one launch per 64."""
-    n = len(packeds)
-    if len(scales_list) != n:
-        raise TQError("packeds and scales differ in length")
-    for pk, sc in zip(packeds, scales_list):
-        _dev(pk, "packed", (torch.uint8,), pk.dim())
-        _dev(sc, "scales", (torch.float16, torch.int16, torch.uint16), sc.dim())
-        if pk.numel() != packed_bytes(N, K, G) or G <= 0 or sc.numel() != N * (K // G):
-            raise TQError("a packed/scales pair does not match N=%d K=%d G=%d" % (N, K, G))
-    if outs is None:
-        outs = [torch.empty((N, K), dtype=torch.bfloat16, device=pk.device) for pk in packeds]
-    arr = ctypes.c_void_p * max(n, 1)
-    _rc(lib().tq_dequantize_batched(n, arr(*[t.data_ptr() for t in packeds]),
-                                    arr(*[t.data_ptr() for t in scales_list]),
-                                    arr(*[t.data_ptr() for t in outs]), N, K, G, _st(status),
-                                    _stream()), "tq_dequantize_batched")
-    return outs
-
+# ---------------------------------------------------------------------------
+# base-3 matmuls
+# ---------------------------------------------------------------------------
 
 def _mm(fn, name, x, packed, scales, N, K, G, status, out):
-    _dev(x, "x", (torch.bfloat16, torch.int16), 2)
-    _dev(packed, "packed", (torch.uint8,), packed.dim())
-    _dev(scales, "scales", (torch.float16, torch.int16), scales.dim())
+    _dev(x, "x", BF16, 2)
+    dev = x.device
     M = x.shape[0]
     if x.shape[1] != K:
         raise TQError("x has K=%d, expected %d" % (x.shape[1], K))
-    if packed.numel() != packed_bytes(N, K, G) or scales.numel() != N * (K // G):
-        raise TQError("packed/scales sizes do not match N=%d K=%d G=%d" % (N, K, G))
-    y = torch.empty((M, N), dtype=torch.float32, device=x.device) if out is None else out
+    _check_packed(packed, scales, N, K, G, dev, name)
+    y = _out(out, "y", (M, N), torch.float32, F32, dev)
     _rc(fn(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), M, N, K, G, y.data_ptr(),
-           _st(status), _stream()), name)
+           _st(status, dev), _stream()), name)
     return y
 
 
@@ -444,28 +383,28 @@ def gemv(x, packed, scales, N: int, K: int, G: int, status=None, out=None):
     return _mm(lib().tq_gemv, "tq_gemv", x, packed, scales, N, K, G, status, out)
 
 
+def gemm(x, packed, scales, N: int, K: int, G: int, status=None, out=None):
+    """y[M,N] = x[M,K] * W_hat^T for any M (prefill path)."""
+    return _mm(lib().tq_gemm, "tq_gemm", x, packed, scales, N, K, G, status, out)
+
+
 def _batched(fn, name, xs, packeds, scales_list, N, K, G, status, outs):
     count = len(xs)
     if not (len(packeds) == len(scales_list) == count):
         raise TQError("%s: lists of different lengths" % name)
-    ys = []
+    if count == 0:
+        return []
+    _dev(xs[0], "x", BF16, 2)
+    dev = xs[0].device
+    M = xs[0].shape[0]
     for i in range(count):
-        _dev(xs[i], "x", (torch.bfloat16, torch.int16), 2)
-        _dev(packeds[i], "packed", (torch.uint8,), packeds[i].dim())
-        _dev(scales_list[i], "scales", (torch.float16, torch.int16), scales_list[i].dim())
-        if xs[i].shape != xs[0].shape or xs[i].shape[1] != K:
-            raise TQError("%s: every x must be [M,%d]" % (name, K))
-        if packeds[i].numel() != packed_bytes(N, K, G) or scales_list[i].numel() != N * (K // G):
-            raise TQError("%s: packed/scales sizes do not match N=%d K=%d G=%d" % (name, N, K, G))
-        ys.append(torch.empty((xs[0].shape[0], N), dtype=torch.float32, device=xs[i].device)
-                  if outs is None else outs[i])
-    arr = ctypes.c_void_p * max(count, 1)
-    ax = arr(*[t.data_ptr() for t in xs])
-    ap = arr(*[t.data_ptr() for t in packeds])
-    asc = arr(*[t.data_ptr() for t in scales_list])
-    ay = arr(*[t.data_ptr() for t in ys])
-    M = xs[0].shape[0] if count else 1
-    _rc(fn(count, ax, ap, asc, ay, M, N, K, G, _st(status), _stream()), name)
+        _dev(xs[i], "x", BF16, 2, dev)
+        if tuple(xs[i].shape) != (M, K):
+            raise TQError("%s: every x must be [%d,%d]" % (name, M, K))
+        _check_packed(packeds[i], scales_list[i], N, K, G, dev, name)
+    ys = _outs(outs, "outs", [(M, N)] * count, torch.float32, F32, dev)
+    _rc(fn(count, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(ys), M, N, K, G,
+           _st(status, dev), _stream()), name)
     return ys
 
 
@@ -475,42 +414,202 @@ def gemv_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, 
                     status, outs)
 
 
-def gemv_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
-    """[x_i] ([1,K_i] bf16), [packed_i], [scales_i] of shapes (N_i, K_i) -> [y_i] ([1,N_i]
-    fp32): M = 1 GEMVs of mixed shapes in as few launches as possible."""
-    count = len(xs)
-    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == count):
-        raise TQError("tq_gemv_grouped: lists of different lengths")
-    ys = []
-    for i in range(count):
-        _dev(xs[i], "x", (torch.bfloat16, torch.int16), 2)
-        _dev(packeds[i], "packed", (torch.uint8,), packeds[i].dim())
-        _dev(scales_list[i], "scales", (torch.float16, torch.int16), scales_list[i].dim())
-        N, K = int(Ns[i]), int(Ks[i])
-        if tuple(xs[i].shape) != (1, K):
-            raise TQError("tq_gemv_grouped: x %d must be [1,%d]" % (i, K))
-        if packeds[i].numel() != packed_bytes(N, K, G) or scales_list[i].numel() != N * (K // G):
-            raise TQError("tq_gemv_grouped: packed/scales %d do not match N=%d K=%d G=%d"
-                          % (i, N, K, G))
-        ys.append(torch.empty((1, N), dtype=torch.float32, device=xs[i].device)
-                  if outs is None else outs[i])
-    arr = ctypes.c_void_p * max(count, 1)
-    i64s = ctypes.c_int64 * max(count, 1)
-    _rc(lib().tq_gemv_grouped(count, arr(*[t.data_ptr() for t in xs]),
-                              arr(*[t.data_ptr() for t in packeds]),
-                              arr(*[t.data_ptr() for t in scales_list]),
-                              arr(*[t.data_ptr() for t in ys]),
-                              i64s(*[int(n) for n in Ns]), i64s(*[int(k) for k in Ks]), G,
-                              _st(status), _stream()), "tq_gemv_grouped")
-    return ys
-
-
 def gemm_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
     """[x_i] ([M,K] bf16 each), [packed_i], [scales_i] -> [y_i] ([M,N] fp32), one call."""
     return _batched(lib().tq_gemm_batched, "tq_gemm_batched", xs, packeds, scales_list, N, K, G,
                     status, outs)
 
 
-def gemm(x, packed, scales, N: int, K: int, G: int, status=None, out=None):
-    """y[M,N] = x[M,K] * W_hat^T for any M (prefill path)."""
-    return _mm(lib().tq_gemm, "tq_gemm", x, packed, scales, N, K, G, status, out)
+def gemv_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
+    """[x_i] ([1,K_i] bf16), [packed_i], [scales_i] of shapes (N_i, K_i) -> [y_i] ([1,N_i]
+    fp32): M = 1 GEMVs of mixed shapes in as few launches as possible."""
+    count = len(xs)
+    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == count):
+        raise TQError("tq_gemv_grouped: lists of different lengths")
+    if count == 0:
+        return []
+    _dev(xs[0], "x", BF16, 2)
+    dev = xs[0].device
+    for i in range(count):
+        N, K = int(Ns[i]), int(Ks[i])
+        _dev(xs[i], "x", BF16, 2, dev)
+        if tuple(xs[i].shape) != (1, K):
+            raise TQError("tq_gemv_grouped: x %d must be [1,%d]" % (i, K))
+        _check_packed(packeds[i], scales_list[i], N, K, G, dev, "tq_gemv_grouped")
+    ys = _outs(outs, "outs", [(1, int(N)) for N in Ns], torch.float32, F32, dev)
+    _rc(lib().tq_gemv_grouped(count, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(ys),
+                              _i64s(Ns), _i64s(Ks), G, _st(status, dev), _stream()),
+        "tq_gemv_grouped")
+    return ys
+
+
+# ---------------------------------------------------------------------------
+# the 2-bit format
+# ---------------------------------------------------------------------------
+
+def _check_packed2(packed, scales, N, K, G, device, what):
+    _dev(packed, "packed", U8, None, device)
+    _dev(scales, "scales", F16, None, device)
+    if (N < 1 or K < 1 or K % 4 or packed.numel() * 4 != N * K
+            or scales.numel() != N * _groups(K, G)):
+        raise TQError("%s: shapes do not match N=%d K=%d G=%d" % (what, N, K, G))
+
+
+def quantize_pack2(w: torch.Tensor, G: int, status=None):
+    """2-bit format: w [N,K] bf16 -> (packed2 uint8 [N, K/4], scales fp16 [N, K/G])."""
+    _dev(w, "w", BF16, 2)
+    N, K = w.shape
+    if _groups(K, G) == 0 or K % 4:
+        raise TQError("quantize_pack2: K=%d does not fit G=%d" % (K, G))
+    packed = torch.empty((N, K // 4), dtype=torch.uint8, device=w.device)
+    scales = torch.empty((N, K // G), dtype=torch.float16, device=w.device)
+    _rc(lib().tq_quantize_pack2(w.data_ptr(), N, K, G, packed.data_ptr(), scales.data_ptr(),
+                                _st(status, w.device), _stream()), "tq_quantize_pack2")
+    return packed, scales
+
+
+def quantize_pack2_batched(ws, G: int, status=None):
+    """2-bit format, same-shaped bf16 matrices -> list of (packed2, scales),
+    one launch per 64."""
+    N, K = _same_shape(ws, "w")
+    if not ws:
+        return []
+    if _groups(K, G) == 0 or K % 4:
+        raise TQError("quantize_pack2_batched: K=%d does not fit G=%d" % (K, G))
+    dev = ws[0].device
+    pk = [torch.empty((N, K // 4), dtype=torch.uint8, device=dev) for _ in ws]
+    sc = [torch.empty((N, K // G), dtype=torch.float16, device=dev) for _ in ws]
+    _rc(lib().tq_quantize_pack2_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(pk), _ptrs(sc),
+                                        _st(status, dev), _stream()), "tq_quantize_pack2_batched")
+    return list(zip(pk, sc))
+
+
+def unpack2(packed: torch.Tensor, N: int, K: int, G: int, status=None):
+    """2-bit packed [N, K/4] -> codes int8 [N,K]."""
+    _dev(packed, "packed", U8)
+    if N < 1 or K < 1 or packed.numel() * 4 != N * K:
+        raise TQError("packed has %d bytes, expected %d" % (packed.numel(), N * K // 4))
+    codes = torch.empty((N, K), dtype=torch.int8, device=packed.device)
+    _rc(lib().tq_unpack2(packed.data_ptr(), N, K, G, codes.data_ptr(),
+                         _st(status, packed.device), _stream()), "tq_unpack2")
+    return codes
+
+
+def gemv2(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int,
+          status=None, out=None):
+    """2-bit format, M = 1: x [1,K] bf16 -> y fp32 [1,N]."""
+    _dev(x, "x", BF16, 2)
+    dev = x.device
+    if tuple(x.shape) != (1, K):
+        raise TQError("gemv2: x must be [1,%d]" % K)
+    _check_packed2(packed, scales, N, K, G, dev, "gemv2")
+    y = _out(out, "y", (1, N), torch.float32, F32, dev)
+    _rc(lib().tq_gemv2(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K, G, y.data_ptr(),
+                       _st(status, dev), _stream()), "tq_gemv2")
+    return y
+
+
+def gemv2_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """2-bit format, M = 1, same-shaped problems: list of y fp32 [1,N], one launch per 128."""
+    n = len(xs)
+    if len(packeds) != n or len(scales_list) != n:
+        raise TQError("xs, packeds and scales differ in length")
+    if n == 0:
+        return []
+    _dev(xs[0], "x", BF16, 2)
+    dev = xs[0].device
+    for x, pk, sc in zip(xs, packeds, scales_list):
+        _dev(x, "x", BF16, 2, dev)
+        if tuple(x.shape) != (1, K):
+            raise TQError("gemv2_batched: every x must be [1,%d]" % K)
+        _check_packed2(pk, sc, N, K, G, dev, "gemv2_batched")
+    outs = _outs(outs, "outs", [(1, N)] * n, torch.float32, F32, dev)
+    _rc(lib().tq_gemv2_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
+                               N, K, G, _st(status, dev), _stream()), "tq_gemv2_batched")
+    return outs
+
+
+def gemv2_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
+    """2-bit format, M = 1, problems of mixed shapes in one launch:
+    list of y fp32 [1, Ns[i]]."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == n):
+        raise TQError("xs, packeds, scales, Ns and Ks differ in length")
+    if n == 0:
+        return []
+    _dev(xs[0], "x", BF16, 2)
+    dev = xs[0].device
+    for x, pk, sc, N, K in zip(xs, packeds, scales_list, Ns, Ks):
+        _dev(x, "x", BF16, 2, dev)
+        if tuple(x.shape) != (1, K):
+            raise TQError("gemv2_grouped: x must be [1,%d]" % K)
+        _check_packed2(pk, sc, N, K, G, dev, "gemv2_grouped")
+    outs = _outs(outs, "outs", [(1, int(N)) for N in Ns], torch.float32, F32, dev)
+    _rc(lib().tq_gemv2_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
+                               _i64s(Ns), _i64s(Ks), G, _st(status, dev), _stream()),
+        "tq_gemv2_grouped")
+    return outs
+
+
+# ---------------------------------------------------------------------------
+# W4A16
+# ---------------------------------------------------------------------------
+
+def _w4_check(x, packed, scales, biases, N, K, G, device=None):
+    _dev(x, "x", BF16, 2, device)
+    dev = x.device
+    _dev(packed, "packed", W4, None, dev)
+    _dev(scales, "scales", BF16, None, dev)
+    _dev(biases, "biases", BF16, None, dev)
+    if (tuple(x.shape) != (1, K) or N < 1 or K < 1 or packed.numel() * 8 != N * K
+            or _groups(K, G) == 0 or scales.numel() != N * (K // G)
+            or biases.numel() != scales.numel()):
+        raise TQError("w4a16: shapes do not match N=%d K=%d G=%d" % (N, K, G))
+    return dev
+
+
+def w4a16_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+               biases: torch.Tensor, N: int, K: int, G: int, out=None):
+    """W4A16, M = 1: x [1,K] bf16, packed int32/uint32 [N, K/8], scales and
+    biases bf16 [N, K/G] -> y bf16 [1,N]."""
+    dev = _w4_check(x, packed, scales, biases, N, K, G)
+    y = _out(out, "y", (1, N), torch.bfloat16, BF16, dev)
+    _rc(lib().tq_w4a16_gemv(x.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                            biases.data_ptr(), N, K, G, y.data_ptr(), _stream()),
+        "tq_w4a16_gemv")
+    return y
+
+
+def w4a16_gemv_batched(xs, packeds, scales_list, biases_list, N: int, K: int, G: int,
+                       outs=None):
+    """Same-shaped W4A16 problems -> list of y bf16 [1,N], one launch per 128."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(biases_list) == n):
+        raise TQError("xs, packeds, scales and biases differ in length")
+    if n == 0:
+        return []
+    dev = None
+    for x, pk, sc, bi in zip(xs, packeds, scales_list, biases_list):
+        dev = _w4_check(x, pk, sc, bi, N, K, G, dev)
+    outs = _outs(outs, "outs", [(1, N)] * n, torch.bfloat16, BF16, dev)
+    _rc(lib().tq_w4a16_gemv_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
+                                    _ptrs(biases_list), _ptrs(outs), N, K, G, _stream()),
+        "tq_w4a16_gemv_batched")
+    return outs
+
+
+def w4a16_gemv_grouped(xs, packeds, scales_list, biases_list, Ns, Ks, G: int, outs=None):
+    """W4A16 problems of mixed shapes in one launch -> list of y bf16 [1, Ns[i]]."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(biases_list) == len(Ns) == len(Ks) == n):
+        raise TQError("xs, packeds, scales, biases, Ns and Ks differ in length")
+    if n == 0:
+        return []
+    dev = None
+    for x, pk, sc, bi, N, K in zip(xs, packeds, scales_list, biases_list, Ns, Ks):
+        dev = _w4_check(x, pk, sc, bi, N, K, G, dev)
+    outs = _outs(outs, "outs", [(1, int(N)) for N in Ns], torch.bfloat16, BF16, dev)
+    _rc(lib().tq_w4a16_gemv_grouped(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
+                                    _ptrs(biases_list), _ptrs(outs), _i64s(Ns), _i64s(Ks), G,
+                                    _stream()), "tq_w4a16_gemv_grouped")
+    return outs

@@ -48,9 +48,15 @@ const char *tq_status_string(int status) {
   }
 }
 
+int64_t tq_packed_row_bytes(int64_t K, int G) {
+  if (K < 1 || G < 1 || K % G != 0) return 0;
+  return (K / G) * (int64_t)((G + 4) / 5);
+}
+
 int64_t tq_packed_bytes(int64_t N, int64_t K, int G) {
-  if (N < 1 || K < 1 || G < 1 || K % G != 0) return 0;
-  return N * (K / G) * (int64_t)((G + 4) / 5);
+  const int64_t rb = tq_packed_row_bytes(K, G);
+  if (N < 1 || rb == 0 || N > INT64_MAX / rb) return 0;
+  return N * rb;
 }
 
 int tq_quantize_pack(const uint16_t *w, int64_t N, int64_t K, int G, uint8_t *packed,

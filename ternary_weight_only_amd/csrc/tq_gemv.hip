@@ -20,7 +20,10 @@
 //     ds_read_b128 per byte, no decode arithmetic.  The table is replicated
 //     16 times, copy j in bank group j, and lane l reads copy l % 16; the
 //     address (byte * 256 + copy * 16) is one v_perm_b32.  Entries 243..255
-//     are NaN, so an invalid byte makes its output NaN, which is flagged.
+//     are NaN, so an invalid byte makes its outputs NaN.  Inf activations or
+//     fp32 overflow can give NaN too, so a NaN output only marks its weight
+//     row: the row's bytes are scanned when it is stored, and only a byte
+//     >= 243 sets the invalid-byte status.
 //   * Byte slots past the group's ceil(G/5) bytes (and code positions past G)
 //     meet zero activations, so the padding trits and the neighbouring
 //     group's bytes contribute nothing.
@@ -74,6 +77,15 @@ __device__ __forceinline__ uint4 lut_entry(uint32_t e) {
     h[i] = d == 0u ? 0xBF80u : (d == 2u ? 0x3F80u : 0u);  // code -1, 0, +1 in bf16
   }
   return make_uint4(h[0] | (h[1] << 16), h[2] | (h[3] << 16), h[4], 0u);
+}
+
+// 1 if one of the `len` bytes at p is >= 243 (an invalid base-3 byte); the
+// rare path of a NaN output.
+__device__ __attribute__((noinline)) uint32_t row_has_invalid_byte(const uint8_t *p,
+                                                                  uint32_t len) {
+  for (uint32_t i = 0; i < len; ++i)
+    if (p[i] >= 243u) return 1u;
+  return 0u;
 }
 
 // Buffer resource over [p, p + bytes): the hardware range check returns 0 for
@@ -377,7 +389,9 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
           for (int e = 0; e < 4; ++e) {
             const int m = 4 * q + e;
             if (m < M && r < w.nrows) {
-              flags |= (v[e] != v[e]);
+              if (v[e] != v[e] && !flags)
+                flags = row_has_invalid_byte(
+                    args.packed[w.pi] + (int64_t)(w.row0 + r) * rowbytes, rowbytes);
               y[(int64_t)m * ldy + w.row0 + r] = v[e];
             }
           }

@@ -17,8 +17,10 @@
 //   * A byte is decoded by one LDS lookup: a 256-entry table maps it to three
 //     bf16 pairs of codes (c0,c1)(c2,c3)(c4,0); v_dot2_f32_bf16 multiplies
 //     them with the activation pairs into fp32.  Entries 243..255 hold NaN,
-//     so an invalid byte turns the chunk sum into NaN, which is checked once
-//     per chunk.  The table is replicated 16 times, copy j living in LDS bank
+//     so an invalid byte turns its row's sum into NaN.  A NaN row sum can
+//     also come from Inf activations or fp32 overflow, so it only marks the
+//     row: after the main loop the lanes that stored NaN rows scan those
+//     rows' bytes, and only a byte >= 243 sets the invalid-byte status.  The table is replicated 16 times, copy j living in LDS bank
 //     group j, and lane l reads copy l%16: the 16 lanes served together hit
 //     16 different bank groups whatever the byte values are.
 //   * The lookup address (byte * 256 + copy * 16) is built by one v_perm_b32
@@ -85,6 +87,25 @@ __device__ __forceinline__ uint4 lut_entry(uint32_t e) {
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
                                            0x00020000);
+}
+
+// 1 if bytes [base, base + len) of the buffer hold a value >= 243 (an
+// invalid base-3 byte).  Used only on the rare path of a NaN output; reads
+// whole dwords and ignores the bytes outside the range.
+__device__ __attribute__((noinline)) uint32_t range_has_invalid_byte(__amdgpu_buffer_rsrc_t r,
+                                                                    uint32_t base,
+                                                                    uint32_t len) {
+  uint32_t hit = 0;
+  const uint32_t end = base + len;
+  for (uint32_t o = base & ~3u; o < end; o += 4u) {
+    const uint32_t w = __builtin_amdgcn_raw_buffer_load_b32(r, o, 0, 0);
+#pragma unroll
+    for (uint32_t i = 0; i < 4u; ++i) {
+      const uint32_t a = o + i;
+      if (a >= base && a < end && ((w >> (8u * i)) & 0xFFu) >= 243u) hit = 1u;
+    }
+  }
+  return hit;
 }
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
@@ -295,7 +316,8 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   const uint32_t copyoff = (uint32_t)(tid % kCopies) * 16u;
 
   lds_bytes_c *lut_bytes = (lds_bytes_c *)(lut);
-  uint32_t bad = 0;
+  // bit (round % 32) of nanmask: this lane stored a NaN row in that round
+  uint32_t nanmask = 0;
   int buf = 0;
   const int l16 = tid & 15;  // lane within its 16-lane DPP row
   const bool hi8 = (l16 & 8) != 0, hi4 = (l16 & 4) != 0;
@@ -366,7 +388,7 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
       if (Lp >= 64) s += __shfl_xor(s, 32);
       const int n = (g0 + k) * R + rr;
       if (c < 16 && (l16 & 3) == 0 && g0 + k < b_end && n < N) {
-        bad |= (s != s);
+        nanmask |= (uint32_t)(s != s) << (((g0 - b_begin) >> 2) & 31);
         yp[n] = s;
       }
     } else {
@@ -380,7 +402,7 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
         if (g0 + kk < b_end && n < N) {
           float sum = 0.f;
           for (int j = 0; j < nseg; ++j) sum += ss[(kk * R + r) * nseg + j];
-          bad |= (sum != sum);
+          nanmask |= (uint32_t)(sum != sum) << (((g0 - b_begin) >> 2) & 31);
           yp[n] = sum;
         }
       }
@@ -394,7 +416,20 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   // the start-up loads in another order.
   round(b_begin);
   for (int g0 = b_begin + kRing; g0 < b_end; g0 += kRing) round(g0);
-  if (bad && d_status) atomicOr(d_status, kDevInvalidByte);
+  if (nanmask && d_status) {
+    // Rare path: scan the rows this lane stored in rounds whose mask bit is
+    // set (rounds 32 apart share a bit, so some rows may be scanned for
+    // nothing) for a byte >= 243.
+    const int k = WAVE_ROWS ? (l16 >> 2) : (tid & 3);
+    const int r = WAVE_ROWS ? rr : (tid >> 2);
+    uint32_t hit = 0;
+    for (int g0 = b_begin; g0 < b_end && !hit; g0 += kRing) {
+      const int n = (g0 + k) * R + r;
+      if (((nanmask >> (((g0 - b_begin) >> 2) & 31)) & 1u) && g0 + k < b_end && n < N)
+        hit = range_has_invalid_byte(rp, (uint32_t)n * rowbytes, rowbytes);
+    }
+    if (hit) atomicOr(d_status, kDevInvalidByte);
+  }
 }
 
 // Blocks of W waves whose threads tile whole rows: Lp = 16*ceil(K/1024)

@@ -116,3 +116,48 @@ def w4a16_problem(seed: int, N: int, K: int, G: int):
     b = f32_to_bf16_bits((-sign * mag * 7.5 + 0.001 * normal_f64(seed + 1, N * nG).reshape(N, nG))
                          .astype(np.float32))
     return packed, s, b
+
+
+def stack_shapes(layers: int = 24):
+    """(N, K) of the FFN stack's matrices, layer by layer: gate, up, down."""
+    return [(N, K) for _ in range(layers) for _, N, K in ffn_shapes()]
+
+
+def stack_weights(layers: int = 24, threads: int = 8):
+    """The FFN stack's bf16 weights in stack_shapes() order (matrix i is
+    ffn_weight(i // 3, i % 3)), generated on `threads` host threads."""
+    from concurrent.futures import ThreadPoolExecutor
+    with ThreadPoolExecutor(max(1, threads)) as ex:
+        return list(ex.map(lambda i: ffn_weight(i // 3, i % 3), range(3 * layers)))
+
+
+def stack_decode_activation(i: int, K: int) -> np.ndarray:
+    """The M = 1 activations of stack matrix i (seed 5000 + i)."""
+    return activation(5000 + i, 1, K)
+
+
+def prefill_activation(M: int, K: int) -> np.ndarray:
+    """Prefill activations x[M,K] shared by every stack matrix of width K:
+    seeds 30 (K = 1024) and 31 (K = 3584) at M = 512, 32 and 33 at M = 2048,
+    and 34 + K for other M."""
+    seeds = {(512, 1024): 30, (512, 3584): 31, (2048, 1024): 32, (2048, 3584): 33}
+    return activation(seeds.get((M, K), 34 + K), M, K)
+
+
+def dense8b_shapes():
+    """(name, N, K) of the 8B-class dense FFN matrices."""
+    return [("up", 14336, 4096), ("down", 4096, 14336)]
+
+
+def dense8b_weight(N: int, K: int) -> np.ndarray:
+    """W[N,K] ~ N(0, 0.02): seed 40 for W[14336,4096], 41 for W[4096,14336]."""
+    return normal_bf16(40 if N > K else 41, (N, K), W_SIGMA)
+
+
+def dense8b_activation(M: int, N: int, K: int) -> np.ndarray:
+    """x[M,K] for the 8B-class matrix W[N,K]: seeds 50..52 (W[14336,4096]) or
+    53..55 (W[4096,14336]) for M = 1, 4, 16; 56 + M otherwise."""
+    idx = {1: 0, 4: 1, 16: 2}
+    if M in idx:
+        return activation((50 if N > K else 53) + idx[M], M, K)
+    return activation(56 + M, M, K)

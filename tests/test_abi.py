@@ -49,6 +49,38 @@ def test_packed_bytes_helper():
     assert lib.tq_packed_bytes(3584, 1024, 128) == 3584 * 8 * 26
     assert lib.tq_packed_bytes(1, 100, 64) == 0
     assert lib.tq_packed_bytes(0, 128, 64) == 0
+    assert lib.tq_packed_bytes(1 << 62, 4096, 128) == 0   # overflows int64
+    assert lib.tq_packed_row_bytes(1024, 128) == 8 * 26
+    assert lib.tq_packed_row_bytes(320, 64) == 65
+    assert lib.tq_packed_row_bytes(70, 7) == 10 * 2       # any G >= 1
+    assert lib.tq_packed_row_bytes(100, 64) == 0
+    assert lib.tq_packed_row_bytes(128, 0) == 0
+
+
+def test_binding_rejects_host_tensors_before_the_library():
+    """Every binding entry point refuses host (CPU) tensors with TQError;
+    nothing is passed to the library."""
+    import torch
+    import ternary_weight_only_amd as tq
+    w = torch.zeros(4, 64, dtype=torch.bfloat16)
+    x = torch.zeros(1, 64, dtype=torch.bfloat16)
+    p = torch.zeros(4, 13, dtype=torch.uint8)
+    s = torch.zeros(4, 1, dtype=torch.float16)
+    calls = [lambda: tq.quantize_pack(w, 64), lambda: tq.fake_quantize(w, 64),
+             lambda: tq.quantize_pack_batched([w], 64), lambda: tq.unpack(p, 4, 64, 64),
+             lambda: tq.unpack_batched([p], 4, 64, 64), lambda: tq.dequantize(p, s, 4, 64, 64),
+             lambda: tq.dequantize_batched([p], [s], 4, 64, 64),
+             lambda: tq.gemv(x, p, s, 4, 64, 64), lambda: tq.gemm(x, p, s, 4, 64, 64),
+             lambda: tq.gemv_batched([x], [p], [s], 4, 64, 64),
+             lambda: tq.gemm_batched([x], [p], [s], 4, 64, 64),
+             lambda: tq.gemv_grouped([x], [p], [s], [4], [64], 64),
+             lambda: tq.quantize_pack2(w, 64), lambda: tq.unpack2(p, 4, 52, 64),
+             lambda: tq.gemv2(x, p, s, 4, 64, 64),
+             lambda: tq.w4a16_gemv(x, torch.zeros(4, 8, dtype=torch.int32), w[:, :1], w[:, :1],
+                                   4, 64, 64)]
+    for c in calls:
+        with pytest.raises(tq.TQError):
+            c()
 
 
 FAKE = 0x100000  # never dereferenced: every call below fails validation first

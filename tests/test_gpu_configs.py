@@ -1,16 +1,26 @@
-"""GPU parity at the workloads' full sizes, in the launch configuration the
-benchmark uses (the library picks its launch shape from the call alone).
+"""GPU parity at the workloads' full sizes, in the launch configurations the
+benchmark times, with every output compared against the CPU oracle:
+packed bytes and scales bit for bit, matmul outputs within
+|y - y_ref| <= 1e-3 * sum_k |x_k w_hat_k| (y_ref in fp64).
 
-Outputs too large for the oracle to recompute whole are checked on sampled
-rows, which the oracle computes one by one from the same inputs.
+Workloads (seeds in ternary_weight_only_amd.inputs):
+  - one Qwen-like FFN block and the 72-matrix stack (24 layers of gate and up
+    W[3584,1024] and down W[1024,3584]), G = 64 and 128, decode at M = 1;
+  - the prefill GEMM on the stack's shapes at M = 512 and 2048, G = 128;
+  - the 8B-class FFN matrices W[14336,4096] and W[4096,14336], G = 128,
+    decode at M = 1, 4 and 16.
+The only outputs not all compared are those of the M = 2048 stack launch:
+there three problems of each shape are compared whole, and every other
+problem on the first and last row of every 256-row tile plus random rows.
 """
+import functools
+
 import numpy as np
 import pytest
 
 import oracle
 from ternary_weight_only_amd import inputs
-from tests.gpu_helpers import (assert_within_bound, dev_bf16, dev_f16bits, dev_u8, gpu_matmul,
-                               host_u16, say)
+from tests.gpu_helpers import (assert_within_bound, dev_bf16, gpu_matmul, host_u16, say)
 
 import torch
 import ternary_weight_only_amd as tq
@@ -18,133 +28,209 @@ import ternary_weight_only_amd as tq
 pytestmark = pytest.mark.gpu
 
 
-def _sample_rows(N, k, seed):
-    rng = np.random.default_rng(seed)
-    rows = set(rng.choice(N, size=min(k, N), replace=False).tolist()) | {0, N - 1}
-    return np.array(sorted(rows))
+@functools.lru_cache(maxsize=1)
+def _stack():
+    say("generating the 72 stack matrices")
+    return inputs.stack_weights()
 
 
-def _quantize_dev(w_bits, G):
+@functools.lru_cache(maxsize=2)
+def _stack_ref(G):
+    """The oracle's packed bytes and scales of every stack matrix."""
+    out = []
+    for w in _stack():
+        p, s, st = oracle.quantize_pack(w, G)
+        assert st == 0
+        out.append((p, s))
+    return out
+
+
+def _groups():
+    """Indices of the stack matrices per shape, in stack order."""
+    g = {}
+    for i, NK in enumerate(inputs.stack_shapes()):
+        g.setdefault(NK, []).append(i)
+    return g
+
+
+def _quantize_stack_batched(G):
+    """The benchmark's quantize launch: one tq_quantize_pack_batched call per
+    shape (48 and 24 matrices)."""
+    ws = [dev_bf16(w) for w in _stack()]
     st = tq.new_status()
-    packed, scales = tq.quantize_pack(dev_bf16(w_bits), G, status=st)
-    return packed, scales, st
-
-
-def _check_rows_exact(w_bits, packed_d, scales_d, st_d, G, rows, what):
-    N, K = w_bits.shape
-    p_ref, s_ref, st_ref = oracle.quantize_pack(w_bits[rows], G)
-    p = packed_d[torch.from_numpy(rows).cuda()].cpu().numpy()
-    s = host_u16(scales_d[torch.from_numpy(rows).cuda()])
-    assert np.array_equal(p, p_ref), what + ": packed"
-    assert np.array_equal(s, s_ref), what + ": scales"
-    assert int(st_d.item()) == 0 and st_ref == 0
-
-
-def _check_gemv_rows(kind, x_bits, packed_d, scales_d, w_rows_packed, w_rows_scales, N, K, G, rows,
-                     what):
-    st = tq.new_status()
-    fn = tq.gemv if kind == "gemv" else tq.gemm
-    y = fn(dev_bf16(x_bits), packed_d, scales_d, N, K, G, status=st).cpu().numpy()
-    assert int(st.item()) == 0
-    y_ref, bound, _ = oracle.matmul(x_bits, w_rows_packed, w_rows_scales, len(rows), K, G)
-    assert_within_bound(y[:, rows], y_ref, bound, what)
-    assert np.isfinite(y).all()
+    out = [None] * len(ws)
+    for (N, K), idx in _groups().items():
+        res = tq.quantize_pack_batched([ws[i] for i in idx], G, status=st)
+        for i, r in zip(idx, res):
+            out[i] = r
+    torch.cuda.synchronize()
+    return out, int(st.item())
 
 
 @pytest.mark.parametrize("G", [64, 128])
 def test_ffn_block_decode(G):
-    """One Qwen-like FFN block (gate, up [3584,1024]; down [1024,3584]), M=1:
-    every output checked."""
+    """One FFN block (gate, up [3584,1024]; down [1024,3584]) quantized by
+    single calls and decoded at M = 1: every byte, scale and output."""
     for p_idx, (name, N, K) in enumerate(inputs.ffn_shapes()):
-        w = inputs.ffn_weight(0, p_idx)
+        w = _stack()[p_idx]
         say("FFN block %s W[%d,%d] G=%d: quantize + gemv M=1" % (name, N, K, G))
-        packed, scales, st = _quantize_dev(w, G)
-        p_ref, s_ref, st_ref = oracle.quantize_pack(w, G)
+        st = tq.new_status()
+        packed, scales = tq.quantize_pack(dev_bf16(w), G, status=st)
+        p_ref, s_ref = _stack_ref(G)[p_idx]
         assert np.array_equal(packed.cpu().numpy(), p_ref)
         assert np.array_equal(host_u16(scales), s_ref)
-        assert int(st.item()) == st_ref == 0
-        x = inputs.activation(20 + p_idx, 1, K)
+        assert int(st.item()) == 0
+        x = inputs.stack_decode_activation(p_idx, K)
         y, st2 = gpu_matmul("gemv", x, p_ref, s_ref, N, K, G)
         y_ref, bound, _ = oracle.matmul(x, p_ref, s_ref, N, K, G)
         assert st2 == 0
         assert_within_bound(y, y_ref, bound, "FFN %s G=%d" % (name, G))
 
 
-def test_ffn_stack_72_matrices():
-    """24 layers x {gate, up, down}: quantize + pack all 72, GEMV through all
-    72 at M=1, for G=64 and G=128; sampled rows checked per matrix."""
-    for layer in range(24):
-        for p_idx, (name, N, K) in enumerate(inputs.ffn_shapes()):
-            w = inputs.ffn_weight(layer, p_idx)
-            x = inputs.activation(5000 + 3 * layer + p_idx, 1, K)
-            rows = _sample_rows(N, 48, 1000 + 3 * layer + p_idx)
-            for G in (64, 128):
-                what = "stack layer %d %s G=%d" % (layer, name, G)
-                if layer % 8 == 0:
-                    say(what)
-                packed, scales, st = _quantize_dev(w, G)
-                _check_rows_exact(w, packed, scales, st, G, rows, what)
-                p_ref, s_ref, _ = oracle.quantize_pack(w[rows], G)
-                _check_gemv_rows("gemv", x, packed, scales, p_ref, s_ref, N, K, G, rows, what)
-
-
-@pytest.mark.parametrize("M", [512, 2048])
-def test_prefill_gemm_ffn(M):
-    """Prefill GEMM on the FFN shapes, G=128; sampled activation rows x all N."""
-    G = 128
-    for p_idx, (name, N, K) in enumerate(inputs.ffn_shapes()):
-        w = inputs.ffn_weight(0, p_idx)
-        x = inputs.activation(30 + p_idx + (3 if M == 2048 else 0), M, K)
-        say("prefill gemm M=%d %s W[%d,%d]" % (M, name, N, K))
-        packed, scales, st = _quantize_dev(w, G)
-        yst = tq.new_status()
-        y = tq.gemm(dev_bf16(x), packed, scales, N, K, G, status=yst).cpu().numpy()
-        assert int(yst.item()) == 0 and np.isfinite(y).all()
-        mrows = _sample_rows(M, 24, 77 + M)
-        p_ref, s_ref, _ = oracle.quantize_pack(w, G)
-        y_ref, bound, _ = oracle.matmul(x[mrows], p_ref, s_ref, N, K, G)
-        assert_within_bound(y[mrows], y_ref, bound, "gemm M=%d %s" % (M, name))
-
-
-@pytest.mark.parametrize("shape", [(14336, 4096), (4096, 14336)])
-def test_8b_class_ffn_batched_gemv(shape):
-    """8B-class dense FFN matrices at G=128; batched GEMV at M = 1, 4, 16."""
-    N, K = shape
-    G = 128
-    w = inputs.normal_bf16(40 if N > K else 41, (N, K), 0.02)
-    say("8B-class W[%d,%d]: quantize" % (N, K))
-    packed, scales, st = _quantize_dev(w, G)
-    rows = _sample_rows(N, 96, N)
-    _check_rows_exact(w, packed, scales, st, G, rows, "8B W[%d,%d]" % (N, K))
-    p_ref, s_ref, _ = oracle.quantize_pack(w[rows], G)
-    for i, M in enumerate((1, 4, 16)):
-        say("8B-class W[%d,%d]: gemv M=%d" % (N, K, M))
-        x = inputs.activation((50 if N > K else 53) + i, M, K)
-        _check_gemv_rows("gemv", x, packed, scales, p_ref, s_ref, N, K, G, rows,
-                         "8B W[%d,%d] M=%d" % (N, K, M))
+@pytest.mark.parametrize("G", [64, 128])
+def test_ffn_stack_quantize_every_byte(G):
+    """All 72 stack matrices packed by the benchmark's two batched launches:
+    every packed byte and every scale bit-exact."""
+    say("stack quantize (batched launches) G=%d" % G)
+    out, st = _quantize_stack_batched(G)
+    assert st == 0
+    for i, ((p, s), (p_ref, s_ref)) in enumerate(zip(out, _stack_ref(G))):
+        assert np.array_equal(p.cpu().numpy(), p_ref), "matrix %d: packed bytes" % i
+        assert np.array_equal(host_u16(s), s_ref), "matrix %d: scales" % i
 
 
 @pytest.mark.parametrize("G", [64, 128])
-def test_ffn_stack_batched_decode(G):
-    """The 72-matrix stack decoded with two batched calls (48 gate/up matrices
-    with K=1024, 24 down matrices with K=3584); sampled rows of every matrix
-    checked against the oracle."""
-    shapes = inputs.ffn_shapes()
-    for group in ((0, 1), (2,)):
-        _, N, K = shapes[group[0]]
-        mats = [(l, p) for l in range(24) for p in group]
-        ws = [inputs.ffn_weight(l, p) for l, p in mats]
-        xs = [inputs.activation(5000 + 3 * l + p, 1, K) for l, p in mats]
-        say("batched stack decode K=%d G=%d count=%d" % (K, G, len(mats)))
-        qs = [_quantize_dev(w, G) for w in ws]
-        st = tq.new_status()
-        ys = tq.gemv_batched([dev_bf16(x) for x in xs], [q[0] for q in qs], [q[1] for q in qs],
-                             N, K, G, status=st)
+def test_ffn_stack_grouped_decode_every_output(G):
+    """The benchmark's decode pass: one tq_gemv_grouped call over all 72
+    matrices (48 x W[3584,1024] and 24 x W[1024,3584]) on the packed bytes
+    the batched quantize launches wrote; every output within the bound."""
+    out, st = _quantize_stack_batched(G)
+    assert st == 0
+    shapes = inputs.stack_shapes()
+    xs = [inputs.stack_decode_activation(i, K) for i, (N, K) in enumerate(shapes)]
+    say("stack grouped gemv G=%d" % G)
+    yst = tq.new_status()
+    ys = tq.gemv_grouped([dev_bf16(x) for x in xs], [p for p, _ in out], [s for _, s in out],
+                         [N for N, _ in shapes], [K for _, K in shapes], G, status=yst)
+    torch.cuda.synchronize()
+    assert int(yst.item()) == 0
+    for i, ((N, K), (p_ref, s_ref)) in enumerate(zip(shapes, _stack_ref(G))):
+        y_ref, bound, _ = oracle.matmul(xs[i], p_ref, s_ref, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "grouped stack matrix %d G=%d"
+                            % (i, G))
+
+
+@pytest.mark.parametrize("G", [64, 128])
+def test_ffn_stack_batched_decode_every_output(G):
+    """The stack decoded with two batched calls (48 gate/up matrices with
+    K = 1024, 24 down matrices with K = 3584); every output compared."""
+    out, st = _quantize_stack_batched(G)
+    assert st == 0
+    shapes = inputs.stack_shapes()
+    for (N, K), idx in _groups().items():
+        xs = [inputs.stack_decode_activation(i, K) for i in idx]
+        say("batched stack decode K=%d G=%d count=%d" % (K, G, len(idx)))
+        yst = tq.new_status()
+        ys = tq.gemv_batched([dev_bf16(x) for x in xs], [out[i][0] for i in idx],
+                             [out[i][1] for i in idx], N, K, G, status=yst)
         torch.cuda.synchronize()
-        assert int(st.item()) == 0
-        for i, (l, p) in enumerate(mats):
-            rows = _sample_rows(N, 24, 7000 + i)
-            p_ref, s_ref, _ = oracle.quantize_pack(ws[i][rows], G)
-            y_ref, bound, _ = oracle.matmul(xs[i], p_ref, s_ref, len(rows), K, G)
-            assert_within_bound(ys[i].cpu().numpy()[:, rows], y_ref, bound,
-                                "batched stack layer %d proj %d" % (l, p))
+        assert int(yst.item()) == 0
+        for j, i in enumerate(idx):
+            p_ref, s_ref = _stack_ref(G)[i]
+            y_ref, bound, _ = oracle.matmul(xs[j], p_ref, s_ref, N, K, G)
+            assert_within_bound(ys[j].cpu().numpy(), y_ref, bound,
+                                "batched stack matrix %d G=%d" % (i, G))
+    assert len(shapes) == 72
+
+
+@pytest.mark.parametrize("M", [512, 2048])
+def test_prefill_gemm_single_every_output(M):
+    """Single tq_gemm calls on one gate and one down matrix, G = 128: every
+    output compared."""
+    G = 128
+    for p_idx in (0, 2):
+        _, N, K = inputs.ffn_shapes()[p_idx]
+        x = inputs.prefill_activation(M, K)
+        p_ref, s_ref = _stack_ref(G)[p_idx]
+        say("prefill gemm (single call) M=%d W[%d,%d]" % (M, N, K))
+        y, st = gpu_matmul("gemm", x, p_ref, s_ref, N, K, G)
+        assert st == 0
+        y_ref, bound, _ = oracle.matmul(x, p_ref, s_ref, N, K, G)
+        assert_within_bound(y, y_ref, bound, "gemm M=%d W[%d,%d]" % (M, N, K))
+
+
+def _stack_gemm(M, G):
+    """The benchmark's prefill launch: one tq_gemm_batched call per shape
+    (48 problems of K = 1024 sharing one x, 24 of K = 3584 sharing another),
+    on the packed bytes the batched quantize launches wrote."""
+    out, st = _quantize_stack_batched(G)
+    assert st == 0
+    xs = {K: inputs.prefill_activation(M, K) for K in (1024, 3584)}
+    ys = [None] * len(out)
+    yst = tq.new_status()
+    for (N, K), idx in _groups().items():
+        say("stack prefill gemm M=%d W[%d,%d] x %d" % (M, N, K, len(idx)))
+        xd = dev_bf16(xs[K])
+        res = tq.gemm_batched([xd] * len(idx), [out[i][0] for i in idx], [out[i][1] for i in idx],
+                              N, K, G, status=yst)
+        for i, y in zip(idx, res):
+            ys[i] = y
+    torch.cuda.synchronize()
+    assert int(yst.item()) == 0
+    return xs, ys
+
+
+def test_prefill_gemm_stack_m512_every_output():
+    """M = 512: every output of all 72 problems of the benchmark's two
+    batched launches."""
+    G, M = 128, 512
+    xs, ys = _stack_gemm(M, G)
+    for i, (N, K) in enumerate(inputs.stack_shapes()):
+        p_ref, s_ref = _stack_ref(G)[i]
+        y_ref, bound, _ = oracle.matmul(xs[K], p_ref, s_ref, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "stack gemm M=512 matrix %d" % i)
+
+
+def test_prefill_gemm_stack_m2048():
+    """M = 2048, the same two batched launches: problems 0, 1, 46 (gate/up)
+    and 2, 35, 71 (down) compared whole; on every other problem the first
+    and last row of every 256-row tile and 8 random rows."""
+    G, M = 128, 2048
+    xs, ys = _stack_gemm(M, G)
+    rng = np.random.default_rng(2048)
+    tile_rows = sorted({r for t in range(0, M, 256) for r in (t, min(t + 255, M - 1))})
+    for i, (N, K) in enumerate(inputs.stack_shapes()):
+        p_ref, s_ref = _stack_ref(G)[i]
+        y = ys[i].cpu().numpy()
+        if i in (0, 1, 46, 2, 35, 71):
+            rows = np.arange(M)
+        else:
+            rows = np.unique(np.concatenate([tile_rows, rng.integers(0, M, 8)]))
+        y_ref, bound, _ = oracle.matmul(xs[K][rows], p_ref, s_ref, N, K, G)
+        assert_within_bound(y[rows], y_ref, bound, "stack gemm M=2048 matrix %d" % i)
+        assert np.isfinite(y).all()
+
+
+@pytest.mark.parametrize("shape", [(14336, 4096), (4096, 14336)])
+def test_8b_class_ffn_every_output(shape):
+    """8B-class dense FFN matrix at G = 128: every packed byte and scale, and
+    every output of the decode at M = 1, 4 and 16."""
+    N, K = shape
+    G = 128
+    w = inputs.dense8b_weight(N, K)
+    say("8B-class W[%d,%d]: quantize" % (N, K))
+    st = tq.new_status()
+    packed, scales = tq.quantize_pack(dev_bf16(w), G, status=st)
+    p_ref, s_ref, st_ref = oracle.quantize_pack(w, G)
+    assert int(st.item()) == st_ref == 0
+    assert np.array_equal(packed.cpu().numpy(), p_ref)
+    assert np.array_equal(host_u16(scales), s_ref)
+    for M in (1, 4, 16):
+        say("8B-class W[%d,%d]: gemv M=%d" % (N, K, M))
+        x = inputs.dense8b_activation(M, N, K)
+        yst = tq.new_status()
+        y = tq.gemv(dev_bf16(x), packed, scales, N, K, G, status=yst)
+        torch.cuda.synchronize()
+        assert int(yst.item()) == 0
+        y_ref, bound, _ = oracle.matmul(x, p_ref, s_ref, N, K, G)
+        assert_within_bound(y.cpu().numpy(), y_ref, bound, "8B W[%d,%d] M=%d" % (N, K, M))

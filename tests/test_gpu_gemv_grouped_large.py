@@ -4,8 +4,8 @@ in one tq_gemv_grouped call, against the CPU oracle: |y - y_ref| <=
 (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation").
 
 The packed bytes are random valid bytes (padding trits included, which the
-matmul ignores) with random fp16 scales; outputs are checked on sampled
-rows, which the oracle computes from the same bytes."""
+matmul ignores) with random fp16 scales; every output is checked against the oracle on the
+same bytes."""
 import numpy as np
 import pytest
 
@@ -43,9 +43,9 @@ def _check_rows(y, x, p, s, K, G, rows, what):
 
 
 @pytest.mark.parametrize("G", [64, 128])
-def test_ffn_stack_shapes_sampled_rows(G):
+def test_ffn_stack_shapes_every_output(G):
     """48 x W[3584,1024] and 24 x W[1024,3584] in one grouped call (12288 row
-    tiles), each with its own activations."""
+    tiles), each with its own activations: every output of every problem."""
     rng = np.random.default_rng(800 + G)
     shapes = [(3584, 1024)] * 48 + [(1024, 3584)] * 24
     problems = [_problem(rng, N, K, G) for N, K in shapes]
@@ -54,14 +54,13 @@ def test_ffn_stack_shapes_sampled_rows(G):
     ys, st = _grouped(problems, xs, G)
     assert st == 0
     for i, ((N, K), (p, s)) in enumerate(zip(shapes, problems)):
-        rows = np.unique(np.concatenate([[0, 15, 16, N - 1], rng.integers(0, N, 4)]))
-        _check_rows(ys[i], xs[i], p, s, K, G, rows, "problem %d W[%d,%d]" % (i, N, K))
+        _check_rows(ys[i], xs[i], p, s, K, G, np.arange(N), "problem %d W[%d,%d]" % (i, N, K))
 
 
 @pytest.mark.parametrize("G", [64, 128])
 def test_ragged_rows_mixed_k_invalid_bytes(G):
     """100 problems with N not a multiple of 16 and K from 1024 to 4160, every
-    row of three of them checked, invalid bytes at the first and the very
+    output of every problem checked, invalid bytes at the first and the very
     last byte of two problems flagged."""
     rng = np.random.default_rng(820 + G)
     Ks = [1024, 2048, 2560, 4096, 1088, 4160]
@@ -72,14 +71,10 @@ def test_ragged_rows_mixed_k_invalid_bytes(G):
     say("grouped gemv: 100 ragged problems G=%d" % G)
     ys, st = _grouped(problems, xs, G)
     assert st == 0
-    for i in (0, 1, 57):
+    for i in range(100):
         N, K = shapes[i]
         _check_rows(ys[i], xs[i], problems[i][0], problems[i][1], K, G, np.arange(N),
                     "problem %d all rows" % i)
-    for i in range(3, 100, 11):
-        N, K = shapes[i]
-        rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 5)]))
-        _check_rows(ys[i], xs[i], problems[i][0], problems[i][1], K, G, rows, "problem %d" % i)
     for i, pos in ((5, (0, 0)), (99, (-1, -1))):   # the first and the very last byte
         bad = [(p.copy(), s) for p, s in problems]
         bad[i][0][pos] = 250 if i == 5 else 255
@@ -101,7 +96,7 @@ def test_one_hot_activations_exact():
     say("grouped gemv: one-hot")
     ys, st = _grouped(problems, xs, G)
     assert st == 0
-    for i in (0, 7, 19):
+    for i in range(20):
         N, K = shapes[i]
         y_ref, _, _ = oracle.matmul(xs[i], problems[i][0], problems[i][1], N, K, G)
         assert np.array_equal(ys[i], y_ref.reshape(-1).astype(np.float32)), i
@@ -136,10 +131,10 @@ def test_wide_range_activations():
     say("grouped gemv: wide-range activations")
     ys, st = _grouped(problems, xs, G)
     assert st == 0
-    for i in (0, 1, 31):
+    for i in range(32):
         N, K = shapes[i]
-        rows = np.unique(np.concatenate([[0, N - 1], rng.integers(0, N, 6)]))
-        _check_rows(ys[i], xs[i], problems[i][0], problems[i][1], K, G, rows, "problem %d" % i)
+        _check_rows(ys[i], xs[i], problems[i][0], problems[i][1], K, G, np.arange(N),
+                    "problem %d" % i)
 
 
 def test_repeatable():

@@ -298,8 +298,8 @@ def test_gemv_grouped_mixed_shapes(G):
     """tq_gemv_grouped over mixed shapes -- two kernel configurations, one
     shape the M = 1 kernel does not take (K = 8320: 130 chunks), ragged N --
     and more problems than one launch holds for the commonest configuration:
-    bit-identical to one tq_gemv per problem, within the oracle's bound on
-    sampled problems; an invalid byte in one problem is flagged."""
+    bit-identical to one tq_gemv per problem, every output within the
+    oracle's bound; an invalid byte in one problem is flagged."""
     import torch
     import ternary_weight_only_amd as tq
     from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
@@ -322,10 +322,9 @@ def test_gemv_grouped_mixed_shapes(G):
     for i, (n, k) in enumerate(shapes):
         y1 = tq.gemv(xd[i], pdv[i], sdv[i], n, k, G)
         assert torch.equal(ys[i], y1), "grouped item %d (N=%d K=%d) differs" % (i, n, k)
-        if i < 10 or i == len(shapes) - 1:
-            p, s, _ = refs[i]
-            y_ref, bound, _ = oracle.matmul(xs[i], p, s, n, k, G)
-            assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "grouped item %d" % i)
+        p, s, _ = refs[i]
+        y_ref, bound, _ = oracle.matmul(xs[i], p, s, n, k, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "grouped item %d" % i)
     bad = refs[1][0].reshape(-1).copy()
     bad[bad.size // 3] = 247
     pdv[1] = dev_u8(bad.reshape(refs[1][0].shape))
@@ -362,11 +361,10 @@ def test_gemm_wide_tiles_ragged_unaligned_and_invalid_bytes():
     ys = tq.gemm_batched(xd, pdv, sdv, N, K, G, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    rows = np.array(list(range(8)) + list(range(248, 264)) + list(range(M - 8, M)))
     for i in range(count):
         p, s, _ = refs[i]
-        y_ref, bound, _ = oracle.matmul(xs[i][rows], p, s, N, K, G)
-        assert_within_bound(ys[i].cpu().numpy()[rows], y_ref, bound, "wide item %d" % i)
+        y_ref, bound, _ = oracle.matmul(xs[i], p, s, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "wide item %d" % i)
     bad = refs[5][0].reshape(-1).copy()
     bad[-1] = 249
     pdv[5].copy_(torch.from_numpy(bad))
@@ -380,7 +378,7 @@ def test_gemm_wide_tiles_ragged_unaligned_and_invalid_bytes():
                                            (300, 96, 320, 64, 70)])
 def test_gemm_batched_matches_single_calls_and_oracle(M, N, K, G, count):
     """tq_gemm_batched: bit-identical to one tq_gemm per problem (count=70
-    takes two launches), and within the bound of the oracle on sampled rows."""
+    takes two launches), and every output within the bound of the oracle."""
     import torch
     import ternary_weight_only_amd as tq
     from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
@@ -395,12 +393,9 @@ def test_gemm_batched_matches_single_calls_and_oracle(M, N, K, G, count):
     ys = tq.gemm_batched(xd, pdv, sdv, N, K, G, status=st)
     torch.cuda.synchronize()
     assert int(st.item()) == 0
-    rng = np.random.default_rng(M + count)
     for i in range(count):
         y1 = tq.gemm(xd[i], pdv[i], sdv[i], N, K, G)
         assert torch.equal(ys[i], y1), "batched item %d differs from the single call" % i
-        if i < 3 or i == count - 1:
-            rows = np.sort(rng.choice(M, size=min(M, 16), replace=False))
-            p, s, _ = refs[i]
-            y_ref, bound, _ = oracle.matmul(xs[i][rows], p, s, N, K, G)
-            assert_within_bound(ys[i].cpu().numpy()[rows], y_ref, bound, "batched item %d" % i)
+        p, s, _ = refs[i]
+        y_ref, bound, _ = oracle.matmul(xs[i], p, s, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "batched item %d" % i)
