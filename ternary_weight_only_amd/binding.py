@@ -27,6 +27,8 @@ SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_qua
            "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
            "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
            "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+# Every symbol include/tq_probe.h declares (measurement probes).
+PROBE_SYMBOLS = ("tq_probe_mfma_bf16", "tq_probe_read_stream")
 
 _lib = None
 
@@ -98,6 +100,11 @@ def lib() -> ctypes.CDLL:
             f.restype = i32
         l.tq_gemv_grouped.argtypes = [i32, p, p, p, p, p, p, i32, p, p]
         l.tq_gemv_grouped.restype = i32
+        # measurement probes (include/tq_probe.h)
+        l.tq_probe_read_stream.argtypes = [p, i64, i32, p, p]
+        l.tq_probe_read_stream.restype = i32
+        l.tq_probe_mfma_bf16.argtypes = [i64, i32, p, p]
+        l.tq_probe_mfma_bf16.restype = i32
         _lib = l
     return _lib
 

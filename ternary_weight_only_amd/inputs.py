@@ -54,14 +54,27 @@ def normal_f64(seed: int, n: int, start: int = 0) -> np.ndarray:
     return np.where((idx & np.uint64(1)) == 0, rad * np.cos(ang), rad * np.sin(ang))
 
 
-def normal_bf16(seed: int, shape, sigma: float = 1.0, chunk: int = 1 << 22) -> np.ndarray:
-    """bf16 bit patterns (uint16 array of `shape`) of N(0, sigma^2) samples."""
+def normal_bf16(seed: int, shape, sigma: float = 1.0, chunk: int = 1 << 22,
+                threads: int = 8) -> np.ndarray:
+    """bf16 bit patterns (uint16 array of `shape`) of N(0, sigma^2) samples.
+    Element i depends only on (seed, i), so the chunks are drawn on up to
+    `threads` host threads with the same result."""
     n = int(np.prod(shape))
     out = np.empty(n, np.uint16)
-    for s in range(0, n, chunk):
+
+    def fill(s):
         e = min(n, s + chunk)
         v = (normal_f64(seed, e - s, start=s) * sigma).astype(np.float32)
         out[s:e] = f32_to_bf16_bits(v)
+
+    starts = list(range(0, n, chunk))
+    if len(starts) > 1 and threads > 1:
+        from concurrent.futures import ThreadPoolExecutor
+        with ThreadPoolExecutor(min(threads, len(starts))) as ex:
+            list(ex.map(fill, starts))
+    else:
+        for s in starts:
+            fill(s)
     return out.reshape(shape)
 
 

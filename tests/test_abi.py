@@ -12,6 +12,7 @@ import pytest
 
 ROOT = os.path.dirname(os.path.dirname(os.path.abspath(__file__)))
 HEADER = os.path.join(ROOT, "include", "tq.h")
+PROBE_HEADER = os.path.join(ROOT, "include", "tq_probe.h")
 
 
 def _lib():
@@ -22,8 +23,8 @@ def _lib():
     return tq.lib()
 
 
-def declared_functions():
-    text = open(HEADER).read()
+def declared_functions(header=HEADER):
+    text = open(header).read()
     text = re.sub(r"/\*.*?\*/", "", text, flags=re.S)
     return sorted(set(re.findall(r"\b(tq_[a-z0-9_]+)\s*\(", text)))
 
@@ -40,6 +41,29 @@ def test_library_exports_every_declared_symbol():
         assert hasattr(lib, name), name
     import ternary_weight_only_amd.binding as b
     assert sorted(b.SYMBOLS) == declared_functions()
+
+
+def test_library_exports_every_probe_symbol():
+    lib = _lib()
+    import ternary_weight_only_amd.binding as b
+    assert sorted(b.PROBE_SYMBOLS) == declared_functions(PROBE_HEADER)
+    for name in b.PROBE_SYMBOLS:
+        assert hasattr(lib, name), name
+
+
+def test_probe_argument_errors():
+    lib = _lib()
+    assert lib.tq_probe_read_stream(None, 1024, 4, FAKE, None) == -1
+    assert lib.tq_probe_read_stream(FAKE, 1024, 4, None, None) == -1
+    assert lib.tq_probe_read_stream(FAKE + 8, 1024, 4, FAKE, None) == -4
+    assert lib.tq_probe_read_stream(FAKE, 1000, 4, FAKE, None) == -2   # not 16-byte chunks
+    assert lib.tq_probe_read_stream(FAKE, 0, 4, FAKE, None) == -2
+    assert lib.tq_probe_read_stream(FAKE, 1024, 0, FAKE, None) == -2
+    assert lib.tq_probe_read_stream(FAKE, 1024, 65536, FAKE, None) == -2
+    assert lib.tq_probe_mfma_bf16(10, 4, None, None) == -1
+    assert lib.tq_probe_mfma_bf16(0, 4, FAKE, None) == -2
+    assert lib.tq_probe_mfma_bf16(10, 0, FAKE, None) == -2
+    assert lib.tq_probe_mfma_bf16((1 << 24) + 1, 4, FAKE, None) == -2
 
 
 def test_packed_bytes_helper():

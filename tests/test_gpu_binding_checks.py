@@ -47,7 +47,7 @@ def test_bad_status_words_rejected():
 def test_bad_matmul_outputs_rejected():
     w, x, packed, scales = _inputs()
     say("binding checks: matmul outputs")
-    sentinel = 12345.0
+    sentinel = 3.0   # exact in every dtype used below
     bad = [torch.full((2, N - 1), sentinel, device="cuda"),                   # short
            torch.full((2, N), sentinel, dtype=torch.bfloat16, device="cuda"),  # dtype
            torch.full((2, N), sentinel),                                      # host
