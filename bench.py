@@ -1,56 +1,50 @@
 """Benchmark of the ternary hot path on one MI355X.
 
-    python bench.py [--gpus 1] [--steps K] [--warmup W] [--G 128] [--prefill-m 512]
+    python bench.py [--gpus 1] [--steps K] [--warmup W] [--G 128] [--rows all]
+    python bench.py --trace-summary <rocprofv3 kernel_stats.csv> [<kernel_trace.csv>]
 
-Workload: the 24-layer Qwen-like FFN stack (hidden 1024, intermediate 3584:
-gate and up W[3584,1024], down W[1024,3584]; 72 matrices, 264,241,152 bf16
-weights ~ N(0, 0.02)), G = 128.  One step is one pass of every step of the
-hot path over that stack, in this order:
+Workload of the step (`value`, `roofline`): the 24-layer Qwen-like FFN stack
+(hidden 1024, intermediate 3584: gate and up W[3584,1024], down
+W[1024,3584]; 72 matrices, 264,241,152 bf16 weights ~ N(0, 0.02)), G = 128.
+One step is one pass of every step of the hot path over that stack:
   decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
       one launch for the 48 K=1024 and the 24 K=3584 matrices together)
   prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
-      two launches, one per shape; each matrix has its own activations and output)
+      two launches, one per shape; each matrix has its own output)
   quantize + pack all 72 bf16 matrices                 (tq_quantize_pack_batched:
       two launches, one per shape)
   unpack + validate all 72 packed matrices             (tq_unpack_batched: two)
 The packed weights live in a ring of eight slots (480 MB, more than the
 256 MB memory-side cache); step t reads slot t%8 and packs into slot
 (t+2)%8, so the weights a GEMV reads were written six steps (several GB of
-traffic) earlier and come from HBM, not from the caches.
-Every row is direct launches (pointer arrays built once per ring slot).  HIP
-events between the rows time each row on the stream the kernels run on, so
-a row's time includes its launches' dispatch.
+traffic) earlier and come from HBM.  Every row is direct launches (pointer
+arrays built once per ring slot); HIP events recorded between the rows on
+the stream the kernels run on time each row, dispatch included.
 
-Outside the step, the decode to bf16 of every matrix of a slot (two
-tq_dequantize_batched calls, one per shape) runs over all eight slots back to
-back between two HIP events (median of three such chains, per pass); each
-chain writes 4.2 GB, so the 256 MB memory-side cache holds at most 6% of the
-writes back.  The row counts packed + scale bytes read and bf16 bytes
-written.
+The GEMV kernel alone (`roofline`): after the steps, the decode pass runs
+over all eight slots back to back (eight launches, each launch's dispatch
+overlapping the previous kernel) between two HIP events; the average launch
+is the median of three such chains / 8.
 
-Also outside the step, the QAT forward (tq_fake_quantize_batched: bf16
-weights to their bf16 ternarized values, two launches a pass) runs eight passes
-back to back between two HIP events (median of three chains); its row counts
-2 bytes read and 2 written per weight.
-
-Also outside the step, two other weight formats run the decode GEMV through
-the same 72 shapes, each over eight ring-slot copies back to back between two
-HIP events (median of three chains): the 2-bit ternary format (the same
-scales and codes, four codes a byte; tq_gemv2_grouped, one launch a pass)
-and W4A16 (seeded stored 4-bit affine codes with bf16 scales and biases;
-tq_w4a16_gemv_grouped, one launch a pass).  Their rows count code plus
-scale (and bias) bytes.
-
-The roofline entry times the GEMV kernel itself: after the timed steps, the
-decode pass runs over all eight slots back to back (8 launches, so each
-launch's dispatch overlaps the previous kernel) between two HIP events, and
-the average launch is the elapsed time / 8; every slot is read once per
-chain, after 7 others (405 MB), so the weights again come from HBM.
+Rows outside the step (each selectable with --rows; every one times chains
+of launches between HIP events on the same stream, median of three):
+  gemv_g64     the decode pass of the stack at G = 64 (its own 8-slot ring)
+  gemm_m2048   the prefill GEMM of the stack at M = 2048 (each shape's
+               launch timed on its own)
+  dense8b      8B-class FFN matrices W[14336,4096] and W[4096,14336], G = 128,
+               decode at M = 1, 4, 16 over a ring of copies (>= 1 GiB)
+  dequant      decode to bf16 of every matrix of a slot (two launches per slot)
+  gemv2        the decode pass over the 2-bit format (one grouped launch)
+  w4a16        the decode pass over seeded W4A16 parameters (one grouped launch)
+  qat          the QAT forward of the stack (two launches a pass)
+  ceilings     plain HBM read streams over the decode pass's bytes (eight
+               57.8 MB buffers) and over 1 GiB, and a bf16 MFMA-only loop
+  cpu          the CPU oracle on bounded samples of the same workloads, at
+               one thread and at the host's cores; it also checks the GPU
+               outputs captured above against its own results
 
 `value` is the decode GEMV's packed-weight bandwidth: (packed code bytes +
-fp16 scale bytes of the 72 matrices) / GEMV time per step.  The JSON line
-also carries every row's throughput, the roofline entry of the GEMV kernel
-and the CPU oracle's rate on a bounded sample of the same GEMV workload.
+fp16 scale bytes of the 72 matrices) / GEMV time per step.
 """
 from __future__ import annotations
 
@@ -68,6 +62,9 @@ if ROOT not in sys.path:
 HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
+RING = 8
+ALL_ROWS = ("step", "gemv_g64", "gemm_m2048", "dense8b", "dequant", "gemv2", "w4a16", "qat",
+            "ceilings", "cpu")
 # HBM bytes per GEMV launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this bench, each
 # scaled by the same counter on a 256 MiB copy (profiles/gemv_m1_hbm_traffic.md); valid only
 # for the kernel source they were taken on (sha256 prefix of csrc/tq_gemv_m1.hip).
@@ -81,424 +78,740 @@ def parse():
     ap.add_argument("--warmup", type=int, default=3)
     ap.add_argument("--G", type=int, default=128)
     ap.add_argument("--prefill-m", type=int, default=512)
-    ap.add_argument("--no-cpu-baseline", action="store_true")
-    ap.add_argument("--cpu-seconds", type=float, default=10.0)
+    ap.add_argument("--rows", default="all",
+                    help="comma-separated rows to run (%s), or all" % ",".join(ALL_ROWS))
+    ap.add_argument("--no-cpu-baseline", action="store_true", help="same as leaving out row cpu")
+    ap.add_argument("--cpu-seconds", type=float, default=4.0,
+                    help="minimum time of each timed oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
-                    help="after the timed steps, copy 256 MiB device to device three times "
+                    help="after the rows, copy 256 MiB device to device three times "
                          "(a kernel of known traffic for scaling hardware byte counters)")
+    ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
+                    help="print a markdown summary of a rocprofv3 kernel_stats.csv (and, if "
+                         "given, its kernel_trace.csv) and exit")
     return ap.parse_args()
 
 
-def gen_weights():
-    """The 72 bf16 weight matrices (seeded; generated in parallel processes)."""
-    from concurrent.futures import ProcessPoolExecutor
-    from ternary_weight_only_amd import inputs
-    jobs = [(l, p) for l in range(24) for p in range(3)]
-    workers = min(16, os.cpu_count() or 1)
-    with ProcessPoolExecutor(max_workers=workers) as ex:
-        return list(ex.map(_gen_one, jobs))
-
-
-def _gen_one(job):
-    from ternary_weight_only_amd import inputs
-    return inputs.ffn_weight(job[0], job[1])
-
-
-def cpu_baseline(mats, x_dec, G, seconds):
-    """The CPU oracle (unchanged) on a bounded sample of the GEMV workload:
-    whole passes of fp64 GEMV through the 72 packed matrices, on one core."""
-    import oracle
-    packed = [oracle.quantize_pack(w, G)[:2] for w in mats]
-    nbytes = sum(p.nbytes + s.nbytes for p, s in packed)
-    t0 = time.perf_counter()
-    passes = 0
-    while True:
-        for (p, s), w, x in zip(packed, mats, x_dec):
-            N, K = w.shape
-            oracle.matmul(x, p, s, N, K, G)
-        passes += 1
-        el = time.perf_counter() - t0
-        if el >= seconds:
-            break
-    return {"value": nbytes * passes / el / 1e9, "unit": "GB/s", "cores": 1, "kind": "oracle",
-            "sample": "%d full passes of M=1 fp64 GEMV through the 72-matrix FFN stack (G=%d), "
-                      "single thread, %.1f s" % (passes, G, el)}
-
-
-def gemv_traffic():
+def source_hash(name):
     import hashlib
-    path = os.path.join(ROOT, "ternary_weight_only_amd", "csrc", "tq_gemv_m1.hip")
+    path = os.path.join(ROOT, "ternary_weight_only_amd", "csrc", name)
     try:
         with open(path, "rb") as f:
-            h = hashlib.sha256(f.read()).hexdigest()[:16]
+            return hashlib.sha256(f.read()).hexdigest()[:16]
     except OSError:
         return None
-    return GEMV_TRAFFIC.get(h)
+
+
+# ---------------------------------------------------------------------------
+# rocprofv3 summaries
+# ---------------------------------------------------------------------------
+
+def trace_summary(paths):
+    """Markdown tables of a rocprofv3 run: per kernel (stats CSV) and per
+    kernel and grid (trace CSV)."""
+    import csv
+    import statistics
+    rows = list(csv.DictReader(open(paths[0])))
+    tot = sum(float(r["TotalDurationNs"]) for r in rows) or 1.0
+    print("| kernel | calls | avg us | min us | max us | share |")
+    print("|---|---|---|---|---|---|")
+    for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
+        print("| %s | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
+            r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / tot))
+    if len(paths) > 1:
+        tr = list(csv.DictReader(open(paths[1])))
+        groups = {}
+        for r in tr:
+            key = (r["Kernel_Name"][:70], r.get("Grid_Size_X", r.get("Grid_Size", "?")),
+                   r.get("Grid_Size_Y", ""), r.get("Workgroup_Size_X", r.get("Workgroup_Size", "")))
+            groups.setdefault(key, []).append(
+                (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
+        print()
+        print("| kernel | grid x | grid y | block | calls | median us | min us | max us |")
+        print("|---|---|---|---|---|---|---|---|")
+        for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
+            print("| %s | %s | %s | %s | %d | %.2f | %.2f | %.2f |" % (
+                key[0], key[1], key[2], key[3], len(d), statistics.median(d), min(d), max(d)))
+
+
+# ---------------------------------------------------------------------------
+# the GPU rows
+# ---------------------------------------------------------------------------
+
+class Bench:
+    def __init__(self, args):
+        import numpy as np
+        import torch
+
+        import ternary_weight_only_amd as tq
+        from ternary_weight_only_amd import inputs
+        from ternary_weight_only_amd.binding import lib
+
+        self.np, self.torch, self.tq, self.inputs = np, torch, tq, inputs
+        self.args = args
+        self.G = args.G
+        self.dev = torch.device("cuda:0")
+        torch.cuda.set_device(self.dev)
+        self.L = lib()
+        self.stream = torch.cuda.Stream()
+        self.sp = self.stream.cuda_stream
+        self.status = tq.new_status(self.dev)
+        self.stp = self.status.data_ptr()
+        self.mats = inputs.stack_weights(threads=16)
+        self.shapes = inputs.stack_shapes()
+        self.groups = {}
+        for i, NK in enumerate(self.shapes):
+            self.groups.setdefault(NK, []).append(i)
+        self.w_dev = [self.bf16(w) for w in self.mats]
+        self.x_dec_host = [inputs.stack_decode_activation(i, K)
+                           for i, (N, K) in enumerate(self.shapes)]
+        self.x_dec = [self.bf16(x) for x in self.x_dec_host]
+        self.i64s = ctypes.c_int64 * len(self.shapes)
+        self.g_ns = self.i64s(*[N for N, K in self.shapes])
+        self.g_ks = self.i64s(*[K for N, K in self.shapes])
+        self.weights = sum(N * K for N, K in self.shapes)
+        self.captured = {}  # GPU results the cpu row checks against the oracle
+        self.rows = {}
+
+    # helpers
+    def bf16(self, a):
+        np, torch = self.np, self.torch
+        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(self.dev).view(
+            torch.bfloat16)
+
+    @staticmethod
+    def ptrs(ts):
+        return (ctypes.c_void_p * len(ts))(*[t.data_ptr() for t in ts])
+
+    def ok(self, rc):
+        assert rc == 0, "library call failed: %s" % self.L.tq_status_string(rc).decode()
+
+    def check_status(self):
+        self.torch.cuda.synchronize()
+        st = int(self.status.item())
+        assert st == 0, "device status %d" % st
+
+    def chain(self, body, inner, reps=4):
+        """Median time (ms) of one body(i) call over `reps` chains of `inner`
+        calls between HIP events on the bench stream (the first chain is a
+        warm-up)."""
+        torch = self.torch
+        res = []
+        with torch.cuda.stream(self.stream):
+            for _ in range(reps):
+                e0 = torch.cuda.Event(enable_timing=True)
+                e1 = torch.cuda.Event(enable_timing=True)
+                e0.record(self.stream)
+                for i in range(inner):
+                    body(i)
+                e1.record(self.stream)
+                res.append((e0, e1))
+        self.check_status()
+        t = sorted(a.elapsed_time(b) for a, b in res[1:])
+        return t[len(t) // 2] / inner
+
+    def quantize_ring(self, G, slots=RING):
+        """`slots` copies of the stack packed at G (one batched launch per shape)."""
+        torch, tq = self.torch, self.tq
+        P = [[torch.empty(tq.packed_bytes(N, K, G), dtype=torch.uint8, device=self.dev)
+              for N, K in self.shapes] for _ in range(slots)]
+        S = [[torch.empty(N * (K // G), dtype=torch.float16, device=self.dev)
+              for N, K in self.shapes] for _ in range(slots)]
+        for slot in range(slots):
+            for (N, K), idx in self.groups.items():
+                self.ok(self.L.tq_quantize_pack_batched(
+                    len(idx), self.ptrs([self.w_dev[i] for i in idx]), N, K, G,
+                    self.ptrs([P[slot][i] for i in idx]), self.ptrs([S[slot][i] for i in idx]),
+                    self.stp, self.sp))
+        self.check_status()
+        return P, S
+
+    def packed_bytes(self, G):
+        return sum(self.tq.packed_bytes(N, K, G) + 2 * N * (K // G) for N, K in self.shapes)
+
+    # ---- the step ----
+    def row_step(self):
+        args, torch, tq, L = self.args, self.torch, self.tq, self.L
+        G, MP = self.G, args.prefill_m
+        P, S = self.quantize_ring(G)
+        self.captured["step_packed"] = [p.cpu().numpy() for p in P[0]]
+        self.captured["step_scales"] = [s.cpu().view(torch.int16).numpy() for s in S[0]]
+        y_dec = [torch.empty(1, N, dtype=torch.float32, device=self.dev) for N, K in self.shapes]
+        codes = [torch.empty(N, K, dtype=torch.int8, device=self.dev) for N, K in self.shapes]
+        x_pre = {K: self.bf16(self.inputs.prefill_activation(MP, K))
+                 for K in sorted({k for _, k in self.shapes})}
+        y_pre = [torch.empty(MP, N, dtype=torch.float32, device=self.dev) for N, K in self.shapes]
+        ptrs = self.ptrs
+        grouped = {slot: (ptrs(self.x_dec), ptrs(P[slot]), ptrs(S[slot]), ptrs(y_dec))
+                   for slot in range(RING)}
+        gcalls = {slot: [(N, K, len(idx), ptrs([x_pre[K]] * len(idx)),
+                          ptrs([P[slot][i] for i in idx]), ptrs([S[slot][i] for i in idx]),
+                          ptrs([y_pre[i] for i in idx]))
+                         for (N, K), idx in self.groups.items()] for slot in range(RING)}
+        qcalls = {slot: [(N, K, len(idx), ptrs([self.w_dev[i] for i in idx]),
+                          ptrs([P[slot][i] for i in idx]), ptrs([S[slot][i] for i in idx]),
+                          ptrs([codes[i] for i in idx]))
+                         for (N, K), idx in self.groups.items()] for slot in range(RING)}
+        stp, sp = self.stp, self.sp
+
+        def run_gemv(slot):
+            ax, ap, asc, ay = grouped[slot]
+            self.ok(L.tq_gemv_grouped(len(self.shapes), ax, ap, asc, ay, self.g_ns, self.g_ks,
+                                      G, stp, sp))
+
+        def run_gemm(slot):
+            for N, K, n, ax, ap, asc, ay in gcalls[slot]:
+                self.ok(L.tq_gemm_batched(n, ax, ap, asc, ay, MP, N, K, G, stp, sp))
+
+        def run_quant(slot):
+            for N, K, n, aw, ap, asc, _ in qcalls[slot]:
+                self.ok(L.tq_quantize_pack_batched(n, aw, N, K, G, ap, asc, stp, sp))
+
+        def run_unpack(slot):
+            for N, K, n, _, ap, _, ac in qcalls[slot]:
+                self.ok(L.tq_unpack_batched(n, ap, N, K, G, ac, stp, sp))
+
+        run = {"gemv": run_gemv, "gemm": run_gemm, "quant": run_quant, "unpack": run_unpack}
+        order = ("gemv", "gemm", "quant", "unpack")
+
+        def step(t, evs=None):
+            rd, wr = t % RING, (t + 2) % RING
+            slots = {"gemv": rd, "gemm": rd, "quant": wr, "unpack": wr}
+            with torch.cuda.stream(self.stream):
+                if evs is not None:
+                    evs[0].record(self.stream)
+                for j, name in enumerate(order):
+                    run[name](slots[name])
+                    if evs is not None:
+                        evs[j + 1].record(self.stream)
+
+        for t in range(args.warmup):
+            step(t)
+        torch.cuda.synchronize()
+        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+               for _ in range(args.steps)]
+        t0 = time.perf_counter()
+        for t in range(args.steps):
+            step(args.warmup + t, evs[t])
+        torch.cuda.synchronize()
+        self.wall = time.perf_counter() - t0
+        self.check_status()
+        # outputs of the last step for the oracle check (every slot holds the same bytes)
+        self.captured["step_y_dec"] = [y.cpu().numpy() for y in y_dec]
+        self.captured["step_y_pre"] = {i: y_pre[i].cpu().numpy() for i in (0, 2)}
+        self.captured["step_codes"] = {i: codes[i].cpu().numpy() for i in (0, 71)}
+        # the GEMV kernel alone: the decode pass over all slots back to back
+        launch_ms = self.chain(run_gemv, RING)
+
+        per = {name: 0.0 for name in order}
+        total = 0.0
+        for t in range(args.steps):
+            for j, name in enumerate(order):
+                per[name] += evs[t][j].elapsed_time(evs[t][j + 1])
+            total += evs[t][0].elapsed_time(evs[t][-1])
+        per = {k: v / args.steps for k, v in per.items()}
+        self.ms_per_step = total / args.steps
+        pb = self.packed_bytes(G)
+        gemm_flops = sum(2.0 * MP * N * K for N, K in self.shapes)
+        gemv_gbs = pb / (per["gemv"] * 1e-3) / 1e9
+        gemm_tf = gemm_flops / (per["gemm"] * 1e-3) / 1e12
+        quant_bytes = self.weights * 2 + pb
+        unpack_bytes = pb + self.weights
+        self.value = gemv_gbs
+        self.rows["decode_gemv"] = {
+            "config": "72-matrix FFN stack, G=%d, M=1, one grouped launch" % G,
+            "ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
+            "kernel_us": launch_ms * 1e3,
+            "kernel_GB/s": pb / (launch_ms * 1e-3) / 1e9,
+            "kernel_frac_hbm": pb / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "launches": 1, "bytes_per_step": pb}
+        self.rows["prefill_gemm"] = {
+            "config": "72-matrix FFN stack, G=%d, M=%d, two batched launches" % (G, MP),
+            "ms": per["gemm"], "TFLOP/s": gemm_tf, "frac_mfma": gemm_tf / MFMA_BF16_PEAK_TFLOPS,
+            "M": MP, "flop_per_step": gemm_flops}
+        self.rows["quantize_pack"] = {
+            "ms": per["quant"], "GB/s": quant_bytes / (per["quant"] * 1e-3) / 1e9,
+            "bytes_per_step": quant_bytes}
+        self.rows["unpack"] = {
+            "ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
+            "bytes_per_step": unpack_bytes}
+        achieved = pb / (launch_ms * 1e-3) / 1e9
+        h = source_hash("tq_gemv_m1.hip")
+        self.roofline = {
+            "kernel": "gemv_m1_kernel (tq_gemv_grouped)", "bound": "hbm",
+            "achieved": round(achieved, 2), "peak": HBM_PEAK_GBS, "unit": "GB/s",
+            "frac": round(achieved / HBM_PEAK_GBS, 4),
+            "traffic": GEMV_TRAFFIC.get(h),
+            "algorithmic_bytes_per_launch": pb,
+            "avg_launch_us": round(launch_ms * 1e3, 3),
+            "timing": "median of 3 chains of the decode pass over all %d slots "
+                      "(%d back-to-back launches) between HIP events" % (RING, RING)}
+        self.P128, self.S128 = P, S
+        del y_pre, codes
+
+    # ---- the stack decode at G = 64 ----
+    def row_gemv_g64(self):
+        torch, L = self.torch, self.L
+        G = 64
+        P, S = self.quantize_ring(G)
+        self.captured["g64_packed"] = [p.cpu().numpy() for p in P[0]]
+        y = [torch.empty(1, N, dtype=torch.float32, device=self.dev) for N, K in self.shapes]
+        calls = {slot: (self.ptrs(self.x_dec), self.ptrs(P[slot]), self.ptrs(S[slot]),
+                        self.ptrs(y)) for slot in range(RING)}
+
+        def run(slot):
+            ax, ap, asc, ay = calls[slot]
+            self.ok(L.tq_gemv_grouped(len(self.shapes), ax, ap, asc, ay, self.g_ns, self.g_ks,
+                                      G, self.stp, self.sp))
+
+        ms = self.chain(run, RING)
+        self.captured["g64_y"] = [t.cpu().numpy() for t in y]
+        self.captured["g64_scales"] = [s.cpu().view(torch.int16).numpy() for s in S[0]]
+        pb = self.packed_bytes(G)
+        gbs = pb / (ms * 1e-3) / 1e9
+        self.rows["decode_gemv_g64"] = {
+            "config": "72-matrix FFN stack, G=64, M=1, one grouped launch per pass",
+            "kernel_us": ms * 1e3, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+            "bytes_per_pass": pb, "in_step": False,
+            "timing": "median of 3 chains over %d ring slots" % RING}
+        del P, S
+
+    # ---- the stack GEMM at M = 2048 ----
+    def row_gemm_m2048(self):
+        torch, L = self.torch, self.L
+        G, M = self.G, 2048
+        if not hasattr(self, "P128"):
+            self.P128, self.S128 = self.quantize_ring(G, slots=1)
+        P, S = self.P128[0], self.S128[0]
+        x = {K: self.bf16(self.inputs.prefill_activation(M, K)) for K in (1024, 3584)}
+        y = [torch.empty(M, N, dtype=torch.float32, device=self.dev) for N, K in self.shapes]
+        calls = {(N, K): (len(idx), self.ptrs([x[K]] * len(idx)), self.ptrs([P[i] for i in idx]),
+                          self.ptrs([S[i] for i in idx]), self.ptrs([y[i] for i in idx]))
+                 for (N, K), idx in self.groups.items()}
+        out = {}
+        total_ms = 0.0
+        for (N, K), (n, ax, ap, asc, ay) in calls.items():
+            def run(_):
+                self.ok(L.tq_gemm_batched(n, ax, ap, asc, ay, M, N, K, G, self.stp, self.sp))
+            ms = self.chain(run, 2)
+            flops = 2.0 * M * N * K * n
+            tf = flops / (ms * 1e-3) / 1e12
+            out["%dx W[%d,%d]" % (n, N, K)] = {"ms": ms, "TFLOP/s": tf,
+                                               "frac_mfma": tf / MFMA_BF16_PEAK_TFLOPS}
+            total_ms += ms
+        flops = sum(2.0 * M * N * K for N, K in self.shapes)
+        tf = flops / (total_ms * 1e-3) / 1e12
+        self.captured["m2048_y"] = {i: y[i][:64].cpu().numpy() for i in (0, 2)}
+        self.rows["prefill_gemm_m2048"] = {
+            "config": "72-matrix FFN stack, G=%d, M=2048, two batched launches" % G,
+            "ms": total_ms, "TFLOP/s": tf, "frac_mfma": tf / MFMA_BF16_PEAK_TFLOPS,
+            "launches": out, "in_step": False,
+            "timing": "each launch: median of 3 chains of 2 launches"}
+        del y
+
+    # ---- the 8B-class FFN matrices ----
+    def row_dense8b(self):
+        torch, tq, L, inputs = self.torch, self.tq, self.L, self.inputs
+        G = 128
+        res = {}
+        for name, N, K in inputs.dense8b_shapes():
+            w = inputs.dense8b_weight(N, K)
+            wd = self.bf16(w)
+            packed, scales = tq.quantize_pack(wd, G, status=self.status)
+            self.check_status()
+            del wd
+            self.captured["d8_packed_%d" % N] = packed.cpu().numpy()
+            self.captured["d8_scales_%d" % N] = scales.cpu().view(torch.int16).numpy()
+            nbytes = packed.numel() + 2 * scales.numel()
+            copies = max(2, -(-(1 << 30) // nbytes))
+            ring = [(packed.clone(), scales.clone()) for _ in range(copies)]
+            for M in (1, 4, 16):
+                xh = inputs.dense8b_activation(M, N, K)
+                x = self.bf16(xh)
+                y = torch.empty(M, N, dtype=torch.float32, device=self.dev)
+
+                def run(i):
+                    p, s = ring[i]
+                    self.ok(L.tq_gemv(x.data_ptr(), p.data_ptr(), s.data_ptr(), M, N, K, G,
+                                      y.data_ptr(), self.stp, self.sp))
+
+                ms = self.chain(run, copies)
+                self.captured["d8_y_%d_%d" % (N, M)] = y.cpu().numpy()
+                gbs = nbytes / (ms * 1e-3) / 1e9
+                res["W[%d,%d] M=%d" % (N, K, M)] = {
+                    "kernel_us": ms * 1e3, "GB/s": gbs, "frac_hbm": gbs / HBM_PEAK_GBS,
+                    "TFLOP/s": 2.0 * M * N * K / (ms * 1e-3) / 1e12}
+            del ring
+        self.rows["dense8b_gemv"] = {
+            "config": "W[14336,4096] and W[4096,14336], G=128, tq_gemv at M=1,4,16",
+            "cases": res, "bytes_per_launch": nbytes, "in_step": False,
+            "timing": "median of 3 chains over a ring of copies (>= 1 GiB)"}
+
+    # ---- decode to bf16 ----
+    def row_dequant(self):
+        torch, L = self.torch, self.L
+        G = self.G
+        if not hasattr(self, "P128"):
+            self.P128, self.S128 = self.quantize_ring(G)
+        P, S = self.P128, self.S128
+        w_hat = [torch.empty(N, K, dtype=torch.bfloat16, device=self.dev) for N, K in self.shapes]
+        calls = {slot: [(N, K, len(idx), self.ptrs([P[slot][i] for i in idx]),
+                         self.ptrs([S[slot][i] for i in idx]), self.ptrs([w_hat[i] for i in idx]))
+                        for (N, K), idx in self.groups.items()] for slot in range(len(P))}
+
+        def run(slot):
+            for N, K, n, ap, asc, aw in calls[slot % len(P)]:
+                self.ok(L.tq_dequantize_batched(n, ap, asc, aw, N, K, G, self.stp, self.sp))
+
+        ms = self.chain(run, RING)
+        self.captured["dequant_w_hat"] = {i: w_hat[i].cpu().view(torch.int16).numpy()
+                                          for i in (0, 71)}
+        b = self.packed_bytes(G) + 2 * self.weights
+        self.rows["decode_bf16"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                                    "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "bytes_per_pass": b, "launches": len(self.groups),
+                                    "in_step": False}
+        del w_hat
+
+    # ---- 2-bit format ----
+    def row_gemv2(self):
+        torch, L = self.torch, self.L
+        G = self.G
+        P2 = {}
+        for (N, K), idx in self.groups.items():
+            out2 = [(torch.empty(N, K // 4, dtype=torch.uint8, device=self.dev),
+                     torch.empty(N, K // G, dtype=torch.float16, device=self.dev)) for _ in idx]
+            self.ok(L.tq_quantize_pack2_batched(len(idx), self.ptrs([self.w_dev[i] for i in idx]),
+                                                N, K, G, self.ptrs([p for p, _ in out2]),
+                                                self.ptrs([s for _, s in out2]), self.stp,
+                                                self.sp))
+            P2.update(zip(idx, out2))
+        self.check_status()
+        self.captured["gemv2_packed"] = {i: P2[i][0].cpu().numpy() for i in (0, 71)}
+        nm = range(len(self.shapes))
+        slots = [{i: (P2[i][0].clone(), P2[i][1].clone()) for i in nm} for _ in range(RING)]
+        y2 = [torch.empty(1, N, dtype=torch.float32, device=self.dev) for N, K in self.shapes]
+        calls = [(self.ptrs(self.x_dec), self.ptrs([sl[i][0] for i in nm]),
+                  self.ptrs([sl[i][1] for i in nm]), self.ptrs(y2)) for sl in slots]
+
+        def run(slot):
+            ax, ap, asc, ay = calls[slot]
+            self.ok(L.tq_gemv2_grouped(len(self.shapes), ax, ap, asc, ay, self.g_ns, self.g_ks,
+                                       G, self.stp, self.sp))
+
+        ms = self.chain(run, RING)
+        self.captured["gemv2_y"] = {i: y2[i].cpu().numpy() for i in (0, 71)}
+        b = sum(N * K // 4 + 2 * N * (K // G) for N, K in self.shapes)
+        self.rows["decode_gemv_2bit"] = {
+            "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "Tweights/s": self.weights / (ms * 1e-3) / 1e12, "bytes_per_pass": b, "launches": 1,
+            "in_step": False}
+
+    # ---- W4A16 ----
+    def row_w4a16(self):
+        np, torch, L, inputs = self.np, self.torch, self.L, self.inputs
+        G = self.G
+        W4 = {}
+        host = {}
+        for i, (N, K) in enumerate(self.shapes):
+            pk, sc, bi = inputs.w4a16_problem(5000 + i, N, K, G)
+            if i in (0, 71):
+                host[i] = (pk, sc, bi)
+            W4[i] = tuple(torch.from_numpy(a.view(np.int32 if a.dtype == np.uint32 else np.int16))
+                          .to(self.dev) for a in (pk, sc, bi))
+        nm = range(len(self.shapes))
+        y4 = [torch.empty(1, N, dtype=torch.bfloat16, device=self.dev) for N, K in self.shapes]
+        slots = [{i: tuple(t.clone() for t in W4[i]) for i in nm} for _ in range(RING)]
+        calls = [(self.ptrs(self.x_dec), self.ptrs([sl[i][0] for i in nm]),
+                  self.ptrs([sl[i][1] for i in nm]), self.ptrs([sl[i][2] for i in nm]),
+                  self.ptrs(y4)) for sl in slots]
+
+        def run(slot):
+            ax, ap, asc, abi, ay = calls[slot]
+            self.ok(L.tq_w4a16_gemv_grouped(len(self.shapes), ax, ap, asc, abi, ay, self.g_ns,
+                                            self.g_ks, G, self.sp))
+
+        ms = self.chain(run, RING)
+        self.captured["w4a16"] = {i: host[i] + (y4[i].float().cpu().numpy(),) for i in (0, 71)}
+        b = sum(N * K // 2 + 4 * N * (K // G) for N, K in self.shapes)
+        self.rows["decode_gemv_w4a16"] = {
+            "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+            "Tweights/s": self.weights / (ms * 1e-3) / 1e12, "bytes_per_pass": b, "launches": 1,
+            "in_step": False}
+
+    # ---- QAT forward ----
+    def row_qat(self):
+        torch, L = self.torch, self.L
+        G = self.G
+        w_hat = [torch.empty(N, K, dtype=torch.bfloat16, device=self.dev) for N, K in self.shapes]
+        calls = [(N, K, len(idx), self.ptrs([self.w_dev[i] for i in idx]),
+                  self.ptrs([w_hat[i] for i in idx])) for (N, K), idx in self.groups.items()]
+
+        def run(_):
+            for N, K, n, aw, awh in calls:
+                self.ok(L.tq_fake_quantize_batched(n, aw, N, K, G, awh, None, self.stp, self.sp))
+
+        ms = self.chain(run, RING)
+        self.captured["qat_w_hat"] = {i: w_hat[i].cpu().view(torch.int16).numpy() for i in (0, 71)}
+        b = 4 * self.weights
+        self.rows["qat_forward"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                                    "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                    "bytes_per_pass": b, "launches": len(self.groups),
+                                    "in_step": False}
+        del w_hat
+
+    # ---- ceilings ----
+    def row_ceilings(self):
+        torch, L = self.torch, self.L
+        sink = torch.zeros(65535 * 512, dtype=torch.int32, device=self.dev)
+        pass_bytes = self.packed_bytes(128) // 16 * 16
+        bufs = [torch.empty(pass_bytes, dtype=torch.uint8, device=self.dev) for _ in range(RING)]
+        for b in bufs:
+            b.fill_(1)
+        big = torch.empty(1 << 30, dtype=torch.uint8, device=self.dev)
+        big.fill_(1)
+        out = {}
+        for grid in (512, 1024):
+            def run(i, grid=grid):
+                self.ok(L.tq_probe_read_stream(bufs[i].data_ptr(), pass_bytes, grid,
+                                               sink.data_ptr(), self.sp))
+            ms = self.chain(run, RING)
+            out["read_stream_57.8MB_grid%d" % grid] = {
+                "us": ms * 1e3, "GB/s": pass_bytes / (ms * 1e-3) / 1e9}
+
+            def run_big(i, grid=grid):
+                self.ok(L.tq_probe_read_stream(big.data_ptr(), big.numel(), grid,
+                                               sink.data_ptr(), self.sp))
+            ms = self.chain(run_big, 2)
+            out["read_stream_1GiB_grid%d" % grid] = {
+                "us": ms * 1e3, "GB/s": big.numel() / (ms * 1e-3) / 1e9}
+        grid, iters = 512, 4096
+        fs = sink.view(torch.float32)
+
+        def run_mfma(_):
+            self.ok(L.tq_probe_mfma_bf16(iters, grid, fs.data_ptr(), self.sp))
+        ms = self.chain(run_mfma, 2)
+        flops = grid * 8 * iters * 8 * 16384.0
+        out["mfma_bf16_16x16x32"] = {"us": ms * 1e3, "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+        best_read = max(v["GB/s"] for k, v in out.items() if k.startswith("read_stream_57"))
+        out["spec_hbm_GB/s"] = HBM_PEAK_GBS
+        out["spec_mfma_bf16_TFLOP/s"] = MFMA_BF16_PEAK_TFLOPS
+        self.ceilings = out
+        if "decode_gemv" in self.rows:
+            r = self.rows["decode_gemv"]
+            r["kernel_frac_of_read_stream"] = r["kernel_GB/s"] / best_read
+        del bufs, big, sink
+
+    # ---- the oracle on the host ----
+    def row_cpu(self):
+        self.cpu = cpu_baseline(self, self.args.cpu_seconds)
+
+
+def _timed(fn, min_s):
+    """Run fn() until min_s seconds have passed; returns (calls, seconds, last result)."""
+    t0 = time.perf_counter()
+    n, r = 0, None
+    while True:
+        r = fn()
+        n += 1
+        el = time.perf_counter() - t0
+        if el >= min_s:
+            return n, el, r
+
+
+def cpu_model():
+    try:
+        for line in open("/proc/cpuinfo"):
+            if line.startswith("model name"):
+                return line.split(":", 1)[1].strip()
+    except OSError:
+        pass
+    return "unknown"
+
+
+def cpu_baseline(b, min_s):
+    """The CPU oracle (unchanged) on bounded samples of the bench's workloads:
+    quantize + pack, the M = 1 GEMV pass and the M = 512 prefill GEMM, at one
+    thread and at the host's cores (rows split over threads).  Its results
+    are then compared with the GPU outputs the rows captured: packed bytes,
+    scales and codes bit-exact, matmul outputs within 1e-3 * sum |x w_hat|."""
+    import numpy as np
+    import oracle
+    inputs = b.inputs
+    G = b.G
+    nt = oracle.default_threads()
+    shapes, mats = b.shapes, b.mats
+    out = {"cpu_model": cpu_model(), "threads_available": nt}
+    checks = []
+
+    # quantize + pack: 8 matrices at one thread, all 72 at nt threads
+    def quant(idx, th):
+        return [oracle.quantize_pack(mats[i], G, threads=th) for i in idx]
+    n1, t1, _ = _timed(lambda: quant(range(8), 1), min_s / 2)
+    ntc, tnt, qres = _timed(lambda: quant(range(72), nt), min_s / 2)
+    qb8 = sum(mats[i].nbytes + b.tq.packed_bytes(*shapes[i], G) + 2 * shapes[i][0] *
+              (shapes[i][1] // G) for i in range(8))
+    qb72 = sum(w.nbytes + b.tq.packed_bytes(N, K, G) + 2 * N * (K // G)
+               for w, (N, K) in zip(mats, shapes))
+    out["quantize_pack"] = {"GB/s_1_thread": qb8 * n1 / t1 / 1e9,
+                            "GB/s_threads": qb72 * ntc / tnt / 1e9, "threads": nt}
+    packs = [(p, s) for p, s, _ in qres]
+
+    # GEMV pass over the 72 matrices (M = 1, fp64)
+    def gemv_pass(th):
+        return [oracle.matmul(x, p, s, N, K, G, threads=th)
+                for (p, s), x, (N, K) in zip(packs, b.x_dec_host, shapes)]
+    nb = sum(p.nbytes + s.nbytes for p, s in packs)
+    n1, t1, _ = _timed(lambda: gemv_pass(1), min_s)
+    ntc, tnt, gres = _timed(lambda: gemv_pass(nt), min_s)
+    gemv_1 = nb * n1 / t1 / 1e9
+    gemv_nt = nb * ntc / tnt / 1e9
+
+    # prefill GEMM, M = 512, on gate (matrix 0) and down (matrix 2) of layer 0
+    M = 512
+    xs = {K: inputs.prefill_activation(M, K) for K in (1024, 3584)}
+
+    def gemm(idx, th):
+        return {i: oracle.matmul(xs[shapes[i][1]], packs[i][0], packs[i][1], *shapes[i], G,
+                                 threads=th) for i in idx}
+    n1, t1, _ = _timed(lambda: gemm((0,), 1), min_s / 2)
+    ntc, tnt, mres = _timed(lambda: gemm((0, 2), nt), min_s / 2)
+    f0 = 2.0 * M * shapes[0][0] * shapes[0][1]
+    f02 = f0 + 2.0 * M * shapes[2][0] * shapes[2][1]
+    out["prefill_gemm_m512"] = {"GFLOP/s_1_thread": f0 * n1 / t1 / 1e9,
+                                "GFLOP/s_threads": f02 * ntc / tnt / 1e9, "threads": nt}
+
+    # ---- checks of the GPU outputs (untimed) ----
+    def within(y, ref, bound, what):
+        err = np.abs(np.asarray(y, np.float64) - ref)
+        ok = bool((err <= 1e-3 * bound).all() and np.isfinite(y).all())
+        checks.append({"what": what, "ok": ok})
+        assert ok, "bench check failed: " + what
+
+    def exact(a, bref, what):
+        ok = bool(np.array_equal(a, bref))
+        checks.append({"what": what, "ok": ok})
+        assert ok, "bench check failed: " + what
+
+    cap = b.captured
+    if "step_packed" in cap:
+        ok = all(np.array_equal(g.reshape(-1), p.reshape(-1))
+                 for g, (p, _) in zip(cap["step_packed"], packs))
+        ok = ok and all(np.array_equal(g.view(np.uint16).reshape(-1), s.reshape(-1))
+                        for g, (_, s) in zip(cap["step_scales"], packs))
+        exact(ok, True, "G=%d packed bytes and scales of all 72 matrices" % G)
+        ok = all(bool((np.abs(cap["step_y_dec"][i].astype(np.float64) - gres[i][0])
+                       <= 1e-3 * gres[i][1]).all()) for i in range(72))
+        exact(ok, True, "decode GEMV outputs of all 72 matrices within the bound")
+        for i in (0, 2):
+            y_ref, bound, _ = mres[i]
+            within(cap["step_y_pre"][i], y_ref, bound, "prefill GEMM M=512 matrix %d" % i)
+        for i in (0, 71):
+            codes, _ = oracle.unpack(packs[i][0], *shapes[i], G)
+            exact(cap["step_codes"][i], codes, "unpacked codes, matrix %d" % i)
+    if "g64_packed" in cap:
+        q64 = [oracle.quantize_pack(w, 64, threads=nt) for w in mats]
+        ok = all(np.array_equal(g.reshape(-1), p.reshape(-1)) and
+                 np.array_equal(gs.view(np.uint16).reshape(-1), s.reshape(-1))
+                 for g, gs, (p, s, _) in zip(cap["g64_packed"], cap["g64_scales"], q64))
+        exact(ok, True, "G=64 packed bytes and scales of all 72 matrices")
+        ok = True
+        for i, ((p, s, _), x, (N, K)) in enumerate(zip(q64, b.x_dec_host, shapes)):
+            y_ref, bound, _ = oracle.matmul(x, p, s, N, K, 64, threads=nt)
+            ok = ok and bool((np.abs(cap["g64_y"][i].astype(np.float64) - y_ref)
+                              <= 1e-3 * bound).all())
+        exact(ok, True, "G=64 decode GEMV outputs of all 72 matrices within the bound")
+    if "m2048_y" in cap:
+        for i in (0, 2):
+            N, K = shapes[i]
+            x = inputs.prefill_activation(2048, K)[:64]
+            y_ref, bound, _ = oracle.matmul(x, packs[i][0], packs[i][1], N, K, G, threads=nt)
+            within(cap["m2048_y"][i], y_ref, bound, "prefill GEMM M=2048 rows 0-63, matrix %d" % i)
+    for name, N, K in inputs.dense8b_shapes():
+        key = "d8_packed_%d" % N
+        if key not in cap:
+            continue
+        w = inputs.dense8b_weight(N, K)
+        p, s, _ = oracle.quantize_pack(w, 128, threads=nt)
+        exact(cap[key], p, "8B-class W[%d,%d] packed bytes" % (N, K))
+        exact(cap["d8_scales_%d" % N].view(np.uint16), s, "8B-class W[%d,%d] scales" % (N, K))
+        for M in (1, 4, 16):
+            x = inputs.dense8b_activation(M, N, K)
+            y_ref, bound, _ = oracle.matmul(x, p, s, N, K, 128, threads=nt)
+            within(cap["d8_y_%d_%d" % (N, M)], y_ref, bound, "8B-class W[%d,%d] M=%d" % (N, K, M))
+    if "dequant_w_hat" in cap:
+        for i in (0, 71):
+            d, _ = oracle.dequantize(packs[i][0], packs[i][1], *shapes[i], G)
+            exact(cap["dequant_w_hat"][i].view(np.uint16), d, "decode to bf16, matrix %d" % i)
+    if "gemv2_packed" in cap:
+        for i in (0, 71):
+            N, K = shapes[i]
+            p2, s2, _ = oracle.quantize_pack2(mats[i], G)
+            exact(cap["gemv2_packed"][i], p2, "2-bit packed bytes, matrix %d" % i)
+            y_ref, bound, _ = oracle.matmul2(b.x_dec_host[i], p2, s2, N, K, G, threads=nt)
+            within(cap["gemv2_y"][i], y_ref, bound, "2-bit decode GEMV, matrix %d" % i)
+    if "w4a16" in cap:
+        for i in (0, 71):
+            N, K = shapes[i]
+            pk, sc, bi, yg = cap["w4a16"][i]
+            y_ref, bd = oracle.w4a16_matmul(b.x_dec_host[i], pk, sc, bi, N, K, G, threads=nt)
+            tol = 1e-3 * bd * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref)
+            ok = bool((np.abs(yg.astype(np.float64) - y_ref) <= tol).all())
+            exact(ok, True, "W4A16 decode GEMV, matrix %d" % i)
+    if "qat_w_hat" in cap:
+        for i in (0, 71):
+            f, _, _ = oracle.fake_quantize(mats[i], G)
+            exact(cap["qat_w_hat"][i].view(np.uint16), f, "QAT forward, matrix %d" % i)
+
+    return {"value": gemv_nt, "unit": "GB/s", "cores": nt, "kind": "oracle",
+            "sample": "fp64 GEMV passes (M=1) through the 72-matrix FFN stack (G=%d) on %d "
+                      "threads, %d passes in %.1f s; the same at 1 thread: %.4f GB/s; "
+                      "quantize+pack and the M=512 GEMM in 'detail'" % (G, nt, ntc, tnt, gemv_1),
+            "single_thread_GB/s": gemv_1, "detail": out,
+            "checks": {"passed": all(c["ok"] for c in checks), "count": len(checks),
+                       "items": [c["what"] for c in checks]}}
 
 
 def main():
     args = parse()
+    if args.trace_summary:
+        trace_summary(args.trace_summary)
+        return
     if args.gpus != 1:
         print("bench.py runs on one GPU only; --gpus %d is not supported (no multi-GPU path is "
               "built)" % args.gpus, file=sys.stderr)
         sys.exit(2)
+    rows = ALL_ROWS if args.rows == "all" else tuple(r for r in args.rows.split(",") if r)
+    bad = [r for r in rows if r not in ALL_ROWS]
+    if bad:
+        print("unknown rows %s (rows: %s)" % (bad, ",".join(ALL_ROWS)), file=sys.stderr)
+        sys.exit(2)
+    if args.no_cpu_baseline:
+        rows = tuple(r for r in rows if r != "cpu")
 
-    import numpy as np
-    import torch
-
-    import ternary_weight_only_amd as tq
-    from ternary_weight_only_amd import inputs
-    from ternary_weight_only_amd.binding import lib
-
-    G, MP = args.G, args.prefill_m
-    dev = torch.device("cuda:0")
-    torch.cuda.set_device(dev)
-    L = lib()
-
-    mats = gen_weights()
-    shapes = [w.shape for w in mats]
-    x_dec_host = [inputs.activation(5000 + i, 1, K) for i, (N, K) in enumerate(shapes)]
-
-    def bf16(a):
-        return torch.from_numpy(np.ascontiguousarray(a).view(np.int16)).to(dev).view(torch.bfloat16)
-
-    w_dev = [bf16(w) for w in mats]
-    x_dec = [bf16(x) for x in x_dec_host]
-    x_pre = {K: bf16(inputs.activation(30 + K, MP, K)) for K in sorted({k for _, k in shapes})}
-    RING = 8
-    P = [[torch.empty(tq.packed_bytes(N, K, G), dtype=torch.uint8, device=dev) for N, K in shapes]
-         for _ in range(RING)]
-    S = [[torch.empty(N * (K // G), dtype=torch.float16, device=dev) for N, K in shapes]
-         for _ in range(RING)]
-    y_dec = [torch.empty(1, N, dtype=torch.float32, device=dev) for N, K in shapes]
-    codes = [torch.empty(N, K, dtype=torch.int8, device=dev) for N, K in shapes]
-    status = tq.new_status(dev)
-    stp = status.data_ptr()
-
-
-    # the decode pass: one grouped call over all 72 matrices (one launch);
-    # the prefill pass: two batched calls (gate+up of all layers share
-    # K=1024, the downs K=3584); the pointer arrays of every slot are built
-    # once
-    groups = {}
-    for i, (N, K) in enumerate(shapes):
-        groups.setdefault((N, K), []).append(i)
-    arr = ctypes.c_void_p
-
-    def ptrs(ts):
-        return (arr * len(ts))(*[t.data_ptr() for t in ts])
-
-    y_pre = [torch.empty(MP, N, dtype=torch.float32, device=dev) for N, K in shapes]
-    calls = {}  # (slot, (N, K)) -> pointer arrays of the GEMV and GEMM calls
-    for slot in range(RING):
-        for key, idx in groups.items():
-            calls[(slot, key)] = (
-                len(idx), ptrs([x_dec[i] for i in idx]), ptrs([P[slot][i] for i in idx]),
-                ptrs([S[slot][i] for i in idx]), ptrs([y_dec[i] for i in idx]),
-                ptrs([x_pre[key[1]] for i in idx]), ptrs([y_pre[i] for i in idx]))
-
-    # quantize/pack and unpack: one batched call per shape (48 and 24 matrices)
-    qcalls = {slot: [(N, K, len(idx), ptrs([w_dev[i] for i in idx]), ptrs([P[slot][i] for i in idx]),
-                      ptrs([S[slot][i] for i in idx]), ptrs([codes[i] for i in idx]))
-                     for (N, K), idx in groups.items()] for slot in range(RING)}
-
-    def run_quant(slot, stream):
-        for N, K, n, aw, ap, asc, _ in qcalls[slot]:
-            rc = L.tq_quantize_pack_batched(n, aw, N, K, G, ap, asc, stp, stream)
-            assert rc == 0, rc
-
-    def run_unpack(slot, stream):
-        for N, K, n, _, ap, _, ac in qcalls[slot]:
-            rc = L.tq_unpack_batched(n, ap, N, K, G, ac, stp, stream)
-            assert rc == 0, rc
-
-    i64s = ctypes.c_int64 * len(shapes)
-    g_ns = i64s(*[N for N, K in shapes])
-    g_ks = i64s(*[K for N, K in shapes])
-    grouped = {slot: (ptrs(x_dec), ptrs(P[slot]), ptrs(S[slot]), ptrs(y_dec))
-               for slot in range(RING)}
-
-    def run_gemv(slot, stream):
-        ax, ap, asc, ay = grouped[slot]
-        rc = L.tq_gemv_grouped(len(shapes), ax, ap, asc, ay, g_ns, g_ks, G, stp, stream)
-        assert rc == 0, rc
-
-    # the prefill pass: likewise two batched calls, each problem with its own
-    # output (the activations of a K are shared)
-    def run_gemm(slot, stream):
-        for (N, K) in groups:
-            n, _, ap, asc, _, axp, ayp = calls[(slot, (N, K))]
-            rc = L.tq_gemm_batched(n, axp, ap, asc, ayp, MP, N, K, G, stp, stream)
-            assert rc == 0, rc
-
-    # fill every ring slot, then check slot 0 against the oracle on sampled rows
-    s0 = torch.cuda.current_stream().cuda_stream
-    for slot in range(RING):
-        run_quant(slot, s0)
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0
-    import oracle
-    for i in (0, 2, 71):
-        N, K = shapes[i]
-        rows = np.array([0, 1, N // 2, N - 1])
-        p_ref, s_ref, _ = oracle.quantize_pack(mats[i][rows], G)
-        p = P[0][i].view(N, -1)[torch.from_numpy(rows).to(dev)].cpu().numpy()
-        assert np.array_equal(p, p_ref), "bench inputs: packed bytes differ from the oracle"
-
-    # all rows run on one side stream, every launch a direct one
-    stream = torch.cuda.Stream()
-    sp = stream.cuda_stream
-    run = {"gemv": run_gemv, "gemm": run_gemm, "quant": run_quant, "unpack": run_unpack}
-
-    order = ("gemv", "gemm", "quant", "unpack")
-
-    def step(t, evs=None):
-        rd, wr = t % RING, (t + 2) % RING
-        slots = {"gemv": rd, "gemm": rd, "quant": wr, "unpack": wr}
-        with torch.cuda.stream(stream):
-            if evs is not None:
-                evs[0].record(stream)
-            for j, name in enumerate(order):
-                run[name](slots[name], sp)
-                if evs is not None:
-                    evs[j + 1].record(stream)
-
-    for t in range(args.warmup):
-        step(t)
-    torch.cuda.synchronize()
-    evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
-           for _ in range(args.steps)]
-    t_start = time.perf_counter()
-    for t in range(args.steps):
-        step(args.warmup + t, evs[t])
-    torch.cuda.synchronize()
-    wall = time.perf_counter() - t_start
-    assert int(status.item()) == 0, "device status %d" % int(status.item())
-
-    # the GEMV kernel on its own: the decode pass over all slots back to back
-    chain = []
-    with torch.cuda.stream(stream):
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for slot in range(RING):
-                run_gemv(slot, sp)
-            e1.record(stream)
-            chain.append((e0, e1))
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, "device status %d" % int(status.item())
-    chain_ms = sorted(a.elapsed_time(b) for a, b in chain[1:])
-    gemv_launches = 1
-    launch_ms = chain_ms[len(chain_ms) // 2] / (RING * gemv_launches)
-
-    # decode to bf16, outside the step: every matrix of a slot into its own
-    # bf16 output, one batched call per shape (2 launches), median of 3 passes
-    w_hat = [torch.empty(N, K, dtype=torch.bfloat16, device=dev) for N, K in shapes]
-    dq_calls = {slot: [(N, K, len(idx), ptrs([P[slot][i] for i in idx]),
-                        ptrs([S[slot][i] for i in idx]), ptrs([w_hat[i] for i in idx]))
-                       for (N, K), idx in groups.items()] for slot in range(RING)}
-
-    def run_dequant(slot, stream):
-        for N, K, n, ap, asc, aw in dq_calls[slot]:
-            rc = L.tq_dequantize_batched(n, ap, asc, aw, N, K, G, stp, stream)
-            assert rc == 0, rc
-
-    dq = []
-    with torch.cuda.stream(stream):
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for slot in range(RING):
-                run_dequant(slot, sp)
-            e1.record(stream)
-            dq.append((e0, e1))
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, "device status %d" % int(status.item())
-    dq_ms = sorted(a.elapsed_time(b) for a, b in dq[1:])[1] / RING
-
-    # decode GEMV over the 2-bit format, outside the step: the same matrices
-    # packed four codes a byte (same scales and codes), one batched call per
-    # shape over each ring slot, all slots back to back
-    P2 = {}
-    for (N, K), idx in groups.items():
-        out2 = [(torch.empty(N, K // 4, dtype=torch.uint8, device=dev),
-                 torch.empty(N, K // G, dtype=torch.float16, device=dev)) for _ in idx]
-        rc = L.tq_quantize_pack2_batched(len(idx), ptrs([w_dev[i] for i in idx]), N, K, G,
-                                         ptrs([p for p, _ in out2]), ptrs([s for _, s in out2]),
-                                         stp, s0)
-        assert rc == 0, rc
-        P2.update(zip(idx, out2))
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0
-    for i in (0, 71):
-        N, K = shapes[i]
-        rows = np.array([0, N // 2, N - 1])
-        p_ref, _, _ = oracle.quantize_pack2(mats[i][rows], G)
-        p = P2[i][0][torch.from_numpy(rows).to(dev)].cpu().numpy()
-        assert np.array_equal(p, p_ref), "bench inputs: 2-bit packed bytes differ from the oracle"
-    P2s = {slot: {i: (P2[i][0].clone(), P2[i][1].clone()) for i in P2} for slot in range(RING)}
-    del P2
-    y2 = [torch.empty(1, N, dtype=torch.float32, device=dev) for N, K in shapes]
-    g2_calls = {slot: (ptrs(x_dec), ptrs([P2s[slot][i][0] for i in range(len(shapes))]),
-                       ptrs([P2s[slot][i][1] for i in range(len(shapes))]), ptrs(y2))
-                for slot in range(RING)}
-
-    def run_gemv2(slot, stream):
-        ax, ap, asc, ay = g2_calls[slot]
-        rc = L.tq_gemv2_grouped(len(shapes), ax, ap, asc, ay, g_ns, g_ks, G, stp, stream)
-        assert rc == 0, rc
-
-    g2 = []
-    with torch.cuda.stream(stream):
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for slot in range(RING):
-                run_gemv2(slot, sp)
-            e1.record(stream)
-            g2.append((e0, e1))
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, "device status %d" % int(status.item())
-    g2_ms = sorted(a.elapsed_time(b) for a, b in g2[1:])[1] / RING
-    packed2_bytes = sum(N * K // 4 + 2 * N * (K // G) for N, K in shapes)
-    del P2s, g2_calls
-
-    # W4A16 decode GEMV, outside the step: stored 4-bit affine parameters of
-    # the same 72 shapes (seeded, both scale orientations), each ring slot a
-    # copy, one batched call per shape and slot, all slots back to back
-    W4 = {}
-    for i, (N, K) in enumerate(shapes):
-        pk, sc, bi = inputs.w4a16_problem(5000 + i, N, K, G)
-        W4[i] = tuple(torch.from_numpy(a.view(np.int32 if a.dtype == np.uint32 else np.int16))
-                      .to(dev) for a in (pk, sc, bi))
-    y4 = [torch.empty(1, N, dtype=torch.bfloat16, device=dev) for N, K in shapes]
-    W4s = {slot: {i: tuple(t.clone() for t in W4[i]) for i in W4} for slot in range(RING)}
-    nm = range(len(shapes))
-    w4_calls = {slot: (ptrs(x_dec), ptrs([W4s[slot][i][0] for i in nm]),
-                       ptrs([W4s[slot][i][1] for i in nm]), ptrs([W4s[slot][i][2] for i in nm]),
-                       ptrs(y4))
-                for slot in range(RING)}
-
-    def run_w4(slot, stream):
-        ax, ap, asc, abi, ay = w4_calls[slot]
-        rc = L.tq_w4a16_gemv_grouped(len(shapes), ax, ap, asc, abi, ay, g_ns, g_ks, G, stream)
-        assert rc == 0, rc
-
-    with torch.cuda.stream(stream):
-        run_w4(0, sp)
-    torch.cuda.synchronize()
-    # sampled rows of two matrices against the oracle, to the W4A16 bar
-    for i in (0, 71):
-        N, K = shapes[i]
-        rows = np.array([0, N // 2, N - 1])
-        pk, sc, bi = (t.cpu().numpy() for t in W4[i])
-        xb = x_dec[i].cpu().view(torch.int16).numpy().view(np.uint16)
-        y_ref, bd = oracle.w4a16_matmul(xb, pk.view(np.uint32)[rows], sc.view(np.uint16)[rows],
-                                        bi.view(np.uint16)[rows], len(rows), K, G)
-        yg = y4[i].float().cpu().numpy()[0, rows].astype(np.float64)
-        tol = 1e-3 * bd[0] * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref[0])
-        assert (np.abs(yg - y_ref[0]) <= tol).all(), "W4A16 GEMV differs from the oracle"
-    w4 = []
-    with torch.cuda.stream(stream):
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for slot in range(RING):
-                run_w4(slot, sp)
-            e1.record(stream)
-            w4.append((e0, e1))
-    torch.cuda.synchronize()
-    w4_ms = sorted(a.elapsed_time(b) for a, b in w4[1:])[1] / RING
-    w4_bytes = sum(N * K // 2 + 4 * N * (K // G) for N, K in shapes)
-    del W4, W4s, w4_calls
-
-    # QAT forward (fake quantization), outside the step: every bf16 matrix to
-    # its bf16 w_hat (72 direct launches a pass), eight passes per chain
-    fq_calls = [(N, K, len(idx), ptrs([w_dev[i] for i in idx]), ptrs([w_hat[i] for i in idx]))
-                for (N, K), idx in groups.items()]
-
-    def run_fake(stream):
-        for N, K, n, aw, awh in fq_calls:
-            rc = L.tq_fake_quantize_batched(n, aw, N, K, G, awh, None, stp, stream)
-            assert rc == 0, rc
-
-    fq = []
-    with torch.cuda.stream(stream):
-        for rep in range(4):
-            e0, e1 = torch.cuda.Event(enable_timing=True), torch.cuda.Event(enable_timing=True)
-            e0.record(stream)
-            for _ in range(RING):
-                run_fake(sp)
-            e1.record(stream)
-            fq.append((e0, e1))
-    torch.cuda.synchronize()
-    assert int(status.item()) == 0, "device status %d" % int(status.item())
-    fq_ms = sorted(a.elapsed_time(b) for a, b in fq[1:])[1] / RING
-    del w_hat
-
+    b = Bench(args)
+    for r in rows:
+        t0 = time.perf_counter()
+        getattr(b, "row_" + r)()
+        print("# row %s done in %.1f s" % (r, time.perf_counter() - t0), file=sys.stderr,
+              flush=True)
     if args.calibrate_copy:
-        src = torch.empty(256 << 20, dtype=torch.uint8, device=dev)
+        torch = b.torch
+        src = torch.empty(256 << 20, dtype=torch.uint8, device=b.dev)
         dst = torch.empty_like(src)
         for _ in range(3):
             dst.copy_(src)
         torch.cuda.synchronize()
-        del src, dst
 
-    per = {name: 0.0 for name in order}
-    total_ms = 0.0
-    for t in range(args.steps):
-        for j, name in enumerate(order):
-            per[name] += evs[t][j].elapsed_time(evs[t][j + 1])
-        total_ms += evs[t][0].elapsed_time(evs[t][-1])
-    per = {k: v / args.steps for k, v in per.items()}
-    ms_per_step = total_ms / args.steps
-
-    packed_bytes = sum(P[0][i].numel() + 2 * S[0][i].numel() for i in range(len(shapes)))
-    weights = sum(N * K for N, K in shapes)
-    gemm_flops = sum(2.0 * MP * N * K for N, K in shapes)
-    gemv_gbs = packed_bytes / (per["gemv"] * 1e-3) / 1e9
-    gemm_tflops = gemm_flops / (per["gemm"] * 1e-3) / 1e12
-    quant_bytes = weights * 2 + packed_bytes
-    unpack_bytes = packed_bytes + weights
-    dequant_bytes = packed_bytes + 2 * weights
-    rows = {
-        "decode_gemv": {"ms": per["gemv"], "GB/s": gemv_gbs, "frac_hbm": gemv_gbs / HBM_PEAK_GBS,
-                    "launches": gemv_launches, "bytes_per_step": packed_bytes},
-        "prefill_gemm": {"ms": per["gemm"], "TFLOP/s": gemm_tflops,
-                    "frac_mfma": gemm_tflops / MFMA_BF16_PEAK_TFLOPS, "M": MP,
-                    "flop_per_step": gemm_flops},
-        "quantize_pack": {"ms": per["quant"],
-                                "GB/s": quant_bytes / (per["quant"] * 1e-3) / 1e9,
-                                "bytes_per_step": quant_bytes},
-        "decode_bf16": {"ms": dq_ms, "GB/s": dequant_bytes / (dq_ms * 1e-3) / 1e9,
-                        "frac_hbm": dequant_bytes / (dq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "bytes_per_pass": dequant_bytes, "launches": len(groups),
-                        "in_step": False},
-        "decode_gemv_2bit": {"ms": g2_ms, "GB/s": packed2_bytes / (g2_ms * 1e-3) / 1e9,
-                             "frac_hbm": packed2_bytes / (g2_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                             "Tweights/s": weights / (g2_ms * 1e-3) / 1e12,
-                             "bytes_per_pass": packed2_bytes, "launches": 1,
-                             "in_step": False},
-        "decode_gemv_w4a16": {"ms": w4_ms, "GB/s": w4_bytes / (w4_ms * 1e-3) / 1e9,
-                              "frac_hbm": w4_bytes / (w4_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                              "Tweights/s": weights / (w4_ms * 1e-3) / 1e12,
-                              "bytes_per_pass": w4_bytes, "launches": 1,
-                              "in_step": False},
-        "qat_forward": {"ms": fq_ms, "GB/s": 4 * weights / (fq_ms * 1e-3) / 1e9,
-                        "frac_hbm": 4 * weights / (fq_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
-                        "bytes_per_pass": 4 * weights, "launches": len(groups),
-                        "in_step": False},
-        "unpack": {"ms": per["unpack"], "GB/s": unpack_bytes / (per["unpack"] * 1e-3) / 1e9,
-                      "bytes_per_step": unpack_bytes},
-    }
     out = {
         "metric": METRIC,
-        "value": round(gemv_gbs, 2),
+        "value": round(b.value, 2) if hasattr(b, "value") else None,
         "unit": "GB/s",
         "n_gpus": 1,
         "steps": args.steps,
         "warmup": args.warmup,
-        "ms_per_step": round(ms_per_step, 4),
+        "ms_per_step": round(b.ms_per_step, 4) if hasattr(b, "ms_per_step") else None,
         "higher_is_better": True,
         "scaling": "weak",
         "vs_baseline": None,
@@ -506,24 +819,19 @@ def main():
         "data": "synthetic",
         "config": {"workload": "qwen-like FFN stack: 24 layers x {gate,up W[3584,1024], down "
                                "W[1024,3584]}, G=%d; decode GEMV M=1 + prefill GEMM M=%d + "
-                               "quantize/pack + unpack per step" % (G, MP),
-                   "G": G, "matrices": len(shapes), "weights": weights, "decode_M": 1,
-                   "prefill_M": MP, "parallelism": "single GPU"},
-        "roofline": {"kernel": "gemv_m1_kernel (tq_gemv_grouped)", "bound": "hbm",
-                     "achieved": round(packed_bytes / gemv_launches / (launch_ms * 1e-3) / 1e9, 2),
-                     "peak": HBM_PEAK_GBS, "unit": "GB/s",
-                     "frac": round(packed_bytes / gemv_launches / (launch_ms * 1e-3) / 1e9
-                                   / HBM_PEAK_GBS, 4),
-                     "traffic": gemv_traffic(),
-                     "avg_launch_us": round(launch_ms * 1e3, 3),
-                     "timing": "median of 3 chains of the decode pass over all %d slots "
-                               "(%d back-to-back launches) between HIP events"
-                               % (RING, RING * gemv_launches)},
-        "rows": rows,
-        "wall_s_timed": round(wall, 4),
+                               "quantize/pack + unpack per step" % (args.G, args.prefill_m),
+                   "G": args.G, "matrices": len(b.shapes), "weights": b.weights, "decode_M": 1,
+                   "prefill_M": args.prefill_m, "parallelism": "single GPU"},
+        "rows": b.rows,
     }
-    if not args.no_cpu_baseline:
-        out["cpu_baseline"] = cpu_baseline(mats, x_dec_host, G, args.cpu_seconds)
+    if hasattr(b, "roofline"):
+        out["roofline"] = b.roofline
+    if hasattr(b, "ceilings"):
+        out["ceilings"] = b.ceilings
+    if hasattr(b, "wall"):
+        out["wall_s_timed"] = round(b.wall, 4)
+    if hasattr(b, "cpu"):
+        out["cpu_baseline"] = b.cpu
     print(json.dumps(out), flush=True)
 
 

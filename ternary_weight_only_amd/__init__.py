@@ -52,6 +52,7 @@ from .binding import (  # noqa: F401
     lib,
     new_status,
     packed_bytes,
+    packed_row_bytes,
     quantize_pack,
     quantize_pack_batched,
     quantize_pack2,
