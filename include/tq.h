@@ -389,14 +389,37 @@ int tq_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const 
  *   y       [1,N] bf16, 2-byte aligned, overwritten
  *   y[n] = bf16_RNE( sum_k x[k] * (q[n,k] * s[n,k/G] + b[n,k/G]) ), the sum
  *   taken in fp32 as s * sum(x q) + b * sum(x) per group.
- * G is 64 or 128 (TQ_ERR_GROUP otherwise); K <= 4096 (K/64 <= 64) and
- * N < 2^28, else TQ_ERR_SHAPE.  No data errors exist in this format: every
+ * G is 64 or 128 (TQ_ERR_GROUP otherwise).  K <= 4096 (K/64 <= 64) with
+ * N < 2^28 runs a table-decode kernel; longer rows run tq_w4a16_gemm's
+ * matrix-core kernel at M = 1 (its limits apply, else TQ_ERR_SHAPE).  No data
+ * errors exist in this format: every
  * code is valid, and Inf/NaN parameters or activations propagate to y.
  * Deterministic.  Accuracy: |y - y_exact| <= 1e-3 * sum_k |x| (|q s| + |b|)
  * before the final bf16 rounding.
  */
 int tq_w4a16_gemv(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
                   const uint16_t *biases, int64_t N, int64_t K, int G, uint16_t *y,
+                  void *stream);
+
+/*
+ * W4A16 matmul for any number of activation rows, in the format of
+ * tq_w4a16_gemv (tiny-llm "Week 2 Day 3: Quantize the Model": "Group-Wise
+ * Affine Quantization", "Packed Storage Layout", "Mathematical
+ * Formulation", "Computation Flow", "GPU Dispatch"):
+ *   y[m,n] = bf16_RNE( sum_k x[m,k] * (q[n,k] * s[n,k/G] + b[n,k/G]) ),
+ *   the sum taken in fp32 as s * sum(x q) + b * sum(x) per group, on the
+ *   matrix cores (bf16 MFMA on the exact bf16 values of the codes).
+ *   x       [M,K] bf16, 16-byte aligned
+ *   packed  [N, K/8] uint32, 4-byte aligned, as tq_w4a16_gemv
+ *   scales, biases  [N, K/G] bf16, 2-byte aligned
+ *   y       [M,N] bf16, 2-byte aligned, overwritten
+ * G is 64 or 128 (TQ_ERR_GROUP otherwise); K % G == 0, M * K * 2 and
+ * N * K / 2 below 2^31 and M <= 4194240, else TQ_ERR_SHAPE.  M = 1 with K <=
+ * 4096 runs tq_w4a16_gemv's kernel.  No data errors; Inf/NaN parameters or
+ * activations propagate.  Deterministic; accuracy as tq_w4a16_gemv.
+ */
+int tq_w4a16_gemm(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                  const uint16_t *biases, int64_t M, int64_t N, int64_t K, int G, uint16_t *y,
                   void *stream);
 
 /* Batched form: `count` same-shaped problems, each as tq_w4a16_gemv on

@@ -49,6 +49,7 @@ from .binding import (  # noqa: F401
     w4a16_gemv,
     w4a16_gemv_batched,
     w4a16_gemv_grouped,
+    w4a16_gemm,
     lib,
     new_status,
     packed_bytes,

@@ -25,7 +25,7 @@ SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_qua
            "tq_quantize_pack_batched", "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack",
            "tq_unpack_batched", "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2",
            "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
-           "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
+           "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped", "tq_w4a16_gemm",
            "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 # Every symbol include/tq_probe.h declares (measurement probes).
 PROBE_SYMBOLS = ("tq_probe_mfma_bf16", "tq_probe_read_stream")
@@ -84,6 +84,8 @@ def lib() -> ctypes.CDLL:
         l.tq_w4a16_gemv_batched.restype = i32
         l.tq_w4a16_gemv_grouped.argtypes = [i32, p, p, p, p, p, p, p, i32, p]
         l.tq_w4a16_gemv_grouped.restype = i32
+        l.tq_w4a16_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
+        l.tq_w4a16_gemm.restype = i32
         l.tq_unpack_batched.argtypes = [i32, p, i64, i64, i32, p, p, p]
         l.tq_unpack_batched.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
@@ -562,17 +564,30 @@ def gemv2_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=No
 # W4A16
 # ---------------------------------------------------------------------------
 
-def _w4_check(x, packed, scales, biases, N, K, G, device=None):
+def _w4_check(x, packed, scales, biases, N, K, G, device=None, any_m=False):
     _dev(x, "x", BF16, 2, device)
     dev = x.device
     _dev(packed, "packed", W4, None, dev)
     _dev(scales, "scales", BF16, None, dev)
     _dev(biases, "biases", BF16, None, dev)
-    if (tuple(x.shape) != (1, K) or N < 1 or K < 1 or packed.numel() * 8 != N * K
-            or _groups(K, G) == 0 or scales.numel() != N * (K // G)
-            or biases.numel() != scales.numel()):
+    if ((x.shape[1] != K or (not any_m and x.shape[0] != 1)) or N < 1 or K < 1
+            or packed.numel() * 8 != N * K or _groups(K, G) == 0
+            or scales.numel() != N * (K // G) or biases.numel() != scales.numel()):
         raise TQError("w4a16: shapes do not match N=%d K=%d G=%d" % (N, K, G))
     return dev
+
+
+def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
+               biases: torch.Tensor, N: int, K: int, G: int, out=None):
+    """W4A16, any M: x [M,K] bf16, packed int32/uint32 [N, K/8], scales and
+    biases bf16 [N, K/G] -> y bf16 [M,N]."""
+    dev = _w4_check(x, packed, scales, biases, N, K, G, any_m=True)
+    M = x.shape[0]
+    y = _out(out, "y", (M, N), torch.bfloat16, BF16, dev)
+    _rc(lib().tq_w4a16_gemm(x.data_ptr(), packed.data_ptr(), scales.data_ptr(),
+                            biases.data_ptr(), M, N, K, G, y.data_ptr(), _stream()),
+        "tq_w4a16_gemm")
+    return y
 
 
 def w4a16_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,

@@ -280,7 +280,8 @@ int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *
   if (!xs || !packeds || !scales || !biases || !ys) return TQ_ERR_NULL;
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
-  if (!tq::w4a16_gemv_supported(N, K, G)) return TQ_ERR_SHAPE;
+  const bool table = tq::w4a16_gemv_supported(N, K, G);
+  if (!table && !tq::w4a16_mfma_supported(1, N, K, G)) return TQ_ERR_SHAPE;
   for (int i = 0; i < count; ++i) {
     if (!xs[i] || !packeds[i] || !scales[i] || !biases[i] || !ys[i]) return TQ_ERR_NULL;
     if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
@@ -288,8 +289,16 @@ int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *
       return TQ_ERR_ALIGN;
   }
   (void)hipGetLastError();
-  tq::launch_w4a16_gemv_batched(count, xs, packeds, scales, biases, ys, N, K, G,
-                                (hipStream_t)stream);
+  if (table) {
+    tq::launch_w4a16_gemv_batched(count, xs, packeds, scales, biases, ys, N, K, G,
+                                  (hipStream_t)stream);
+  } else {
+    // rows longer than the table kernel takes (K > 4096): the matrix-core
+    // kernel, one launch per problem
+    for (int i = 0; i < count; ++i)
+      tq::launch_w4a16_mfma(xs[i], packeds[i], scales[i], biases[i], 1, N, K, G, ys[i],
+                            (hipStream_t)stream);
+  }
   return finish_launch();
 }
 
@@ -303,15 +312,52 @@ int tq_w4a16_gemv_grouped(int count, const uint16_t *const *xs, const uint32_t *
   for (int i = 0; i < count; ++i) {
     const int rc = check_nkg(Ns[i], Ks[i], G);
     if (rc) return rc;
-    if (!tq::w4a16_gemv_supported(Ns[i], Ks[i], G)) return TQ_ERR_SHAPE;
+    if (!tq::w4a16_gemv_supported(Ns[i], Ks[i], G) &&
+        !tq::w4a16_mfma_supported(1, Ns[i], Ks[i], G))
+      return TQ_ERR_SHAPE;
     if (!xs[i] || !packeds[i] || !scales[i] || !biases[i] || !ys[i]) return TQ_ERR_NULL;
     if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
         !aligned(biases[i], 2) || !aligned(ys[i], 2))
       return TQ_ERR_ALIGN;
   }
   (void)hipGetLastError();
-  tq::launch_w4a16_gemv_grouped(count, xs, packeds, scales, biases, ys, Ns, Ks, G,
-                                (hipStream_t)stream);
+  // the shapes the table kernel takes share launches; longer rows run alone
+  // on the matrix-core kernel
+  std::vector<const uint16_t *> gx, gs, gb;
+  std::vector<const uint32_t *> gp;
+  std::vector<uint16_t *> gy;
+  std::vector<int64_t> gn, gk;
+  for (int i = 0; i < count; ++i) {
+    if (tq::w4a16_gemv_supported(Ns[i], Ks[i], G)) {
+      gx.push_back(xs[i]); gp.push_back(packeds[i]); gs.push_back(scales[i]);
+      gb.push_back(biases[i]); gy.push_back(ys[i]); gn.push_back(Ns[i]); gk.push_back(Ks[i]);
+    } else {
+      tq::launch_w4a16_mfma(xs[i], packeds[i], scales[i], biases[i], 1, Ns[i], Ks[i], G, ys[i],
+                            (hipStream_t)stream);
+    }
+  }
+  if (!gx.empty())
+    tq::launch_w4a16_gemv_grouped((int)gx.size(), gx.data(), gp.data(), gs.data(), gb.data(),
+                                  gy.data(), gn.data(), gk.data(), G, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_w4a16_gemm(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                  const uint16_t *biases, int64_t M, int64_t N, int64_t K, int G, uint16_t *y,
+                  void *stream) {
+  if (!x || !packed || !scales || !biases || !y) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (M < 1 || !tq::w4a16_mfma_supported(M, N, K, G)) return TQ_ERR_SHAPE;
+  if (!aligned(x, 16) || !aligned(packed, 4) || !aligned(scales, 2) || !aligned(biases, 2) ||
+      !aligned(y, 2))
+    return TQ_ERR_ALIGN;
+  (void)hipGetLastError();
+  if (M == 1 && tq::w4a16_gemv_supported(N, K, G) && aligned(packed, 16))
+    tq::launch_w4a16_gemv_batched(1, &x, &packed, &scales, &biases, &y, N, K, G,
+                                  (hipStream_t)stream);
+  else
+    tq::launch_w4a16_mfma(x, packed, scales, biases, M, N, K, G, y, (hipStream_t)stream);
   return finish_launch();
 }
 

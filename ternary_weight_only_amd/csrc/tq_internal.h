@@ -55,6 +55,13 @@ void launch_w4a16_gemv_grouped(int count, const uint16_t *const *xs,
                                const uint16_t *const *biases, uint16_t *const *ys,
                                const int64_t *Ns, const int64_t *Ks, int G, hipStream_t stream);
 
+// W4A16 on the matrix cores, any M (tq_w4a16_gemm.hip): also the W4A16 GEMV's
+// path for the shapes w4a16_gemv_supported() rejects.
+bool w4a16_mfma_supported(int64_t M, int64_t N, int64_t K, int G);
+void launch_w4a16_mfma(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
+                       const uint16_t *biases, int64_t M, int64_t N, int64_t K, int G,
+                       uint16_t *y, hipStream_t stream);
+
 void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
                            int8_t *const *codes, int32_t *d_status, hipStream_t stream);
 

@@ -317,7 +317,7 @@ def test_w4a16_argument_errors():
     g = lib.tq_w4a16_gemv
     assert g(None, FAKE, FAKE, FAKE, 4, 128, 128, FAKE, None) == -1
     assert g(FAKE, FAKE, FAKE, None, 4, 128, 128, FAKE, None) == -1
-    assert g(FAKE, FAKE, FAKE, FAKE, 4, 8192, 128, FAKE, None) == -2   # K/64 > 64
+    assert g(FAKE, FAKE, FAKE, FAKE, 1 << 20, 8192, 128, FAKE, None) == -2  # codes >= 2^31 B
     assert g(FAKE, FAKE, FAKE, FAKE, 4, 200, 100, FAKE, None) == -3
     assert g(FAKE + 8, FAKE, FAKE, FAKE, 4, 128, 128, FAKE, None) == -4
     assert g(FAKE, FAKE + 4, FAKE, FAKE, 4, 128, 128, FAKE, None) == -4
@@ -337,10 +337,28 @@ def test_w4a16_argument_errors():
     assert gr(0, None, None, None, None, None, None, None, 128, None) == 0
     assert gr(-1, good, good, good, good, good, ns, ks, 128, None) == -2
     assert gr(2, good, good, good, good, good, ns, None, 128, None) == -1
-    assert gr(2, good, good, good, good, good, ns, i64s(128, 8192), 128, None) == -2
+    assert gr(2, good, good, good, good, good, i64s(4, 1 << 20), i64s(128, 8192), 128,
+              None) == -2
     assert gr(2, good, good, good, good, good, ns, ks, 100, None) == -3
     assert gr(2, good, arr(FAKE, FAKE + 8), good, good, good, ns, ks, 128, None) == -4
     assert gr(2, good, good, good, arr(FAKE, None), good, ns, ks, 128, None) == -1
+
+
+def test_w4a16_gemm_argument_errors():
+    lib = _lib()
+    f = lib.tq_w4a16_gemm
+    assert f(None, FAKE, FAKE, FAKE, 2, 4, 128, 128, FAKE, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 128, None, None) == -1
+    assert f(FAKE, FAKE, FAKE, FAKE, 0, 4, 128, 128, FAKE, None) == -2     # M < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 0, 128, 128, FAKE, None) == -2     # N < 1
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 4, 192, 128, FAKE, None) == -2     # K % G
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 32, FAKE, None) == -3      # G
+    assert f(FAKE, FAKE, FAKE, FAKE, 1 << 17, 4, 8192, 128, FAKE, None) == -2  # x >= 2^31 B
+    assert f(FAKE, FAKE, FAKE, FAKE, 5000000, 4, 128, 128, FAKE, None) == -2  # grid rows
+    assert f(FAKE + 8, FAKE, FAKE, FAKE, 2, 4, 128, 128, FAKE, None) == -4
+    assert f(FAKE, FAKE + 2, FAKE, FAKE, 2, 4, 128, 128, FAKE, None) == -4
+    assert f(FAKE, FAKE, FAKE + 1, FAKE, 2, 4, 128, 128, FAKE, None) == -4
+    assert f(FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 128, FAKE + 1, None) == -4
 
 
 def test_product_path_does_not_import_oracle():
