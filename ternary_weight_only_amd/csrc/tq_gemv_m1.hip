@@ -109,7 +109,6 @@ __device__ __attribute__((noinline)) uint32_t range_has_invalid_byte(__amdgpu_bu
 }
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
-constexpr uint32_t kFar = 0x40000000u;  // buffer ranges here stay below this
 constexpr int kRing = 4;  // row batches in flight per lane
 constexpr int kMaxBatch = 128;  // problems per launch (6.5 KB of kernel arguments)
 
@@ -130,9 +129,10 @@ struct GemvShapes {
 
 // The work of a launch is the row batches of its problems (nb per problem);
 // a batch is one row per row slot (R = 64W / Lp rows).  Block (s, p) of the
-// 2-D grid takes segment s of problem p: q or q+1 consecutive batches
-// starting at s*q + min(s, rem), so its activations are loaded once and no
-// block divides.  Problems of one launch may differ in N and K, as long as
+// 2-D grid takes segment s of problem p: batches s, s + S, s + 2S, ... (q or
+// q+1 of them), so its activations are loaded once and no block divides,
+// and at any moment the blocks of a problem read one contiguous stretch of
+// it rather than S stretches far apart.  Problems of one launch may differ in N and K, as long as
 // they share the block size and the template configuration.  Threads t = 0..64W-1 map to (row slot rr = t/Lp, chunk
 // c = t % Lp); lanes with c >= L idle.  Each lane keeps the packed bytes of
 // its next D batches in flight in a register ring; the loop body loads
@@ -177,8 +177,10 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   const uint32_t rowbytes = (uint32_t)L * kChunk;
   const uint32_t total = (uint32_t)N * rowbytes;  // < 2^30, checked by the launcher
   const int gidx = G == 64 ? c : (c >> 1);
-  const int b_begin = seg * q + (seg < rem ? seg : rem);
-  const int b_end = b_begin + q + (seg < rem ? 1 : 0);
+  const int S = shp.S[pi];
+  // the segment's batches by local index i in [0, b_end): global batch seg + i*S
+  const int b_begin = 0;
+  const int b_end = q + (seg < rem ? 1 : 0);
 
   // activations x[0, K); reads past the end give zeros (the last lane's
   // window reaches 16 bytes beyond x)
@@ -198,13 +200,15 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
     xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
   }
 
-  // lane's byte address of batch b is a0 + b * bstep; idle lanes get
-  // an offset past any range so their loads read zeros.  Rows past N lie
-  // past the end of the buffers and read zeros too (they are never stored).
-  const uint32_t a0 = lane_on ? (uint32_t)rr * rowbytes + (uint32_t)c * kChunk : kOutOfRange;
-  const uint32_t bstep = (uint32_t)R * rowbytes;
-  const uint32_t s0 = lane_on ? 2u * ((uint32_t)rr * (uint32_t)nG + (uint32_t)gidx) : kOutOfRange;
-  const uint32_t sstep = 2u * (uint32_t)R * (uint32_t)nG;
+  // lane's byte address of local batch b is a0 + b * bstep (its first row is
+  // seg*R + rr, S*R rows further per batch); idle lanes get an offset past
+  // any range so their loads read zeros.  Rows past N lie past the end of
+  // the buffers and read zeros too (they are never stored).
+  const uint32_t row0 = (uint32_t)(seg * R + rr);
+  const uint32_t a0 = lane_on ? row0 * rowbytes + (uint32_t)c * kChunk : kOutOfRange;
+  const uint32_t bstep = (uint32_t)(S * R) * rowbytes;
+  const uint32_t s0 = lane_on ? 2u * (row0 * (uint32_t)nG + (uint32_t)gidx) : kOutOfRange;
+  const uint32_t sstep = 2u * (uint32_t)(S * R) * (uint32_t)nG;
   const uint32_t pbytes = (total + 3u) & ~3u, sbytes = (uint32_t)N * (uint32_t)nG * 2u;
   const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[pi], pbytes);
   // scales are read as the aligned dwords holding them (a 16-bit load's
@@ -213,15 +217,18 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   // whole dwords, which never reaches past a page the buffer touches
   const uintptr_t sp = (uintptr_t)args.scales[pi];
   const uint32_t shead = (uint32_t)(sp & 3u);
-  const __amdgpu_buffer_rsrc_t rs =
-      make_rsrc((const void *)(sp - shead), (sbytes + shead + 3u) & ~3u);
+  const uint32_t sbytes_al = (sbytes + shead + 3u) & ~3u;
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc((const void *)(sp - shead), sbytes_al);
+  const uint8_t *const pk8 = args.packed[pi];
+  const uint8_t *const sc8 = (const uint8_t *)(sp - shead);
   float *__restrict__ yp = args.y[pi];
 
   // With AL (both batch steps multiples of 4 bytes) a lane's byte offset
   // within its dword and the half holding its scale are the same for every
-  // batch, and a batch's load offsets are the lane's base plus a uniform
-  // step, or plus kFar past the segment (bases and ranges stay below kFar,
-  // so the sums stay past the range without wrapping).
+  // batch, so a batch's loads take the lane's fixed offsets into buffer
+  // resources that start b * bstep and b * sstep bytes in (scalar
+  // arithmetic; a batch past the segment gets an empty range and reads
+  // zeros).
   const uint32_t o_lane = a0 & 3u, sh_lane = ((shead + s0) & 2u) << 3;
   const uint32_t a0al = lane_on ? (a0 & ~3u) : kOutOfRange;
   const uint32_t s0al = lane_on ? ((shead + s0) & ~3u) : kOutOfRange;
@@ -230,9 +237,13 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   auto issue = [&](int slot, int b) {  // batches at or past b_end read zeros
     const bool on = b < b_end;
     if (AL) {
-      const uint32_t pb = on ? (uint32_t)b * bstep : kFar, sb = on ? (uint32_t)b * sstep : kFar;
-      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, a0al + pb, 0, 0);
-      rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rs, s0al + sb, 0, 0);
+      const int bu = __builtin_amdgcn_readfirstlane(b);  // uniform: keeps this scalar
+      const bool onu = bu < b_end;
+      const uint32_t pb = (uint32_t)bu * bstep, sb = (uint32_t)bu * sstep;
+      const __amdgpu_buffer_rsrc_t rpb = make_rsrc(pk8 + pb, onu ? pbytes - pb : 0u);
+      const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sc8 + sb, onu ? sbytes_al - sb : 0u);
+      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rpb, a0al, 0, 0);
+      rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rsb, s0al, 0, 0);
     } else {
       const uint32_t a = a0 + (uint32_t)b * bstep;
       ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, on ? (a & ~3u) : kOutOfRange, 0, 0);
@@ -320,6 +331,9 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   uint32_t nanmask = 0;
   int buf = 0;
   const int l16 = tid & 15;  // lane within its 16-lane DPP row
+  // ds_bpermute byte addresses of the lanes 16 and 32 apart (rows of 32 and
+  // 64 lanes add their DPP rows' sums), computed once
+  const int bp16 = ((tid & 63) ^ 16) << 2, bp32 = ((tid & 63) ^ 32) << 2;
   const bool hi8 = (l16 & 8) != 0, hi4 = (l16 & 4) != 0;
   auto round = [&](int g0) {
     float v[kRing];
@@ -384,9 +398,9 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
     const int k = l16 >> 2;                 // this lane's batch
     if (WAVE_ROWS) {
       // a row is Lp = 16, 32 or 64 lanes of one wave: add its DPP rows
-      if (Lp >= 32) s += __shfl_xor(s, 16);
-      if (Lp >= 64) s += __shfl_xor(s, 32);
-      const int n = (g0 + k) * R + rr;
+      if (Lp >= 32) s += __int_as_float(__builtin_amdgcn_ds_bpermute(bp16, __float_as_int(s)));
+      if (Lp >= 64) s += __int_as_float(__builtin_amdgcn_ds_bpermute(bp32, __float_as_int(s)));
+      const int n = (seg + (g0 + k) * S) * R + rr;
       if (c < 16 && (l16 & 3) == 0 && g0 + k < b_end && n < N) {
         nanmask |= (uint32_t)(s != s) << (((g0 - b_begin) >> 2) & 31);
         yp[n] = s;
@@ -398,7 +412,7 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
       __syncthreads();
       if (tid < kRing * R) {
         const int kk = tid & 3, r = tid >> 2;
-        const int n = (g0 + kk) * R + r;
+        const int n = (seg + (g0 + kk) * S) * R + r;
         if (g0 + kk < b_end && n < N) {
           float sum = 0.f;
           for (int j = 0; j < nseg; ++j) sum += ss[(kk * R + r) * nseg + j];
@@ -424,7 +438,7 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
     const int r = WAVE_ROWS ? rr : (tid >> 2);
     uint32_t hit = 0;
     for (int g0 = b_begin; g0 < b_end && !hit; g0 += kRing) {
-      const int n = (g0 + k) * R + r;
+      const int n = (seg + (g0 + k) * S) * R + r;
       if (((nanmask >> (((g0 - b_begin) >> 2) & 31)) & 1u) && g0 + k < b_end && n < N)
         hit = range_has_invalid_byte(rp, (uint32_t)n * rowbytes, rowbytes);
     }
@@ -578,7 +592,7 @@ void launch_m1(const M1Config &c, int count, const uint16_t *const *xs,
 }
 
 bool m1_supported(int64_t M, int64_t N, int64_t K) {
-  // packed bytes below 1 GiB: offsets plus kFar never wrap
+  // packed bytes below 1 GiB: 32-bit offsets never wrap
   return M == 1 && m1_waves(K) > 0 && N * (K / 64) * 13 < (int64_t(1) << 30);
 }
 
