@@ -32,6 +32,7 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
 #include <type_traits>
 #include <vector>
 
@@ -335,10 +336,17 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   // 64 lanes add their DPP rows' sums), computed once
   const int bp16 = ((tid & 63) ^ 16) << 2, bp32 = ((tid & 63) ^ 32) << 2;
   const bool hi8 = (l16 & 8) != 0, hi4 = (l16 & 4) != 0;
-  auto round = [&](int g0) {
+  // NLIVE: the round's first NLIVE batches lie in the segment; the others
+  // (only in a segment's last round) are neither loaded nor computed
+  auto round = [&](int g0, auto NLIVE) {
+    constexpr int nlive = decltype(NLIVE)::value;
     float v[kRing];
 #pragma unroll
     for (int d = 0; d < kRing; ++d) {
+      if (d >= nlive) {  // resolved at compile time
+        v[d] = 0.f;
+        continue;
+      }
       const int b = g0 + d;
       // realign the lane's 13 bytes to byte 0
       const uint32_t o = AL ? o_lane : ((a0 + (uint32_t)b * bstep) & 3u);
@@ -427,9 +435,15 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   // flight in the same order as on its back edge.  Every segment holds at
   // least one batch (the launcher makes at most nb segments), so the peeled
   // round runs unconditionally: no path reaches the loop around it, with
-  // the start-up loads in another order.
-  round(b_begin);
-  for (int g0 = b_begin + kRing; g0 < b_end; g0 += kRing) round(g0);
+  // the start-up loads in another order.  A last round with fewer than
+  // kRing batches skips the work of the missing ones.
+  const std::integral_constant<int, kRing> full{};
+  round(b_begin, full);
+  int g0 = b_begin + kRing;
+  for (; g0 + kRing < b_end; g0 += kRing) round(g0, full);
+  if (g0 < b_end) {
+    if (b_end - g0 <= 2) round(g0, std::integral_constant<int, 2>{}); else round(g0, full);
+  }
   if (nanmask && d_status) {
     // Rare path: scan the rows this lane stored in rounds whose mask bit is
     // set (rounds 32 apart share a bit, so some rows may be scanned for
@@ -569,18 +583,31 @@ void launch_m1(const M1Config &c, int count, const uint16_t *const *xs,
   // sizes (weights, i.e. packed bytes)
   double total = 0.0;
   for (int i = 0; i < count; ++i) total += (double)Ns[i] * (double)Ks[i];
+  int segs[kMaxBatch], most[kMaxBatch], order[kMaxBatch];
   for (int i = 0; i < count; ++i) {
-    args.x[i] = xs[i]; args.packed[i] = packeds[i]; args.scales[i] = scales[i]; args.y[i] = ys[i];
     const int L = (int)(Ks[i] / 64), Lp = 16 * ((L + 15) / 16), R = c.threads / Lp;
     const int64_t nb = (Ns[i] + R - 1) / R;
     int64_t share = (int64_t)(512.0 * ((double)Ns[i] * (double)Ks[i]) / total);
     if (share < 1) share = 1;
-    const int S = m1_segments(share, nb);
-    shp.N[i] = (int)Ns[i];
-    shp.K[i] = (int)Ks[i];
-    shp.S[i] = S;
-    shp.q[i] = (int)(nb / S);
-    shp.rem[i] = (int)(nb % S);
+    segs[i] = m1_segments(share, nb);
+    most[i] = (int)((nb + segs[i] - 1) / segs[i]);  // batches of the longest segment
+    order[i] = i;
+  }
+  // Problems with the longest segments first: blocks are dispatched in
+  // order, one to each CU before any CU gets a second, so the heaviest
+  // blocks share their CUs with lighter ones.
+  std::stable_sort(order, order + count, [&](int a, int b) { return most[a] > most[b]; });
+  for (int j = 0; j < count; ++j) {
+    const int i = order[j];
+    args.x[j] = xs[i]; args.packed[j] = packeds[i]; args.scales[j] = scales[i]; args.y[j] = ys[i];
+    const int L = (int)(Ks[i] / 64), Lp = 16 * ((L + 15) / 16), R = c.threads / Lp;
+    const int64_t nb = (Ns[i] + R - 1) / R;
+    const int S = segs[i];
+    shp.N[j] = (int)Ns[i];
+    shp.K[j] = (int)Ks[i];
+    shp.S[j] = S;
+    shp.q[j] = (int)(nb / S);
+    shp.rem[j] = (int)(nb % S);
     if (S > smax) smax = S;
     if (!c.direct && m1_stage_bytes((int)Ks[i]) > lds) lds = m1_stage_bytes((int)Ks[i]);
   }
