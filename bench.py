@@ -89,6 +89,11 @@ def parse():
     ap.add_argument("--trace-summary", nargs="+", metavar="CSV",
                     help="print a markdown summary of a rocprofv3 kernel_stats.csv (and, if "
                          "given, its kernel_trace.csv) and exit")
+    ap.add_argument("--pmc-summary", nargs="+", metavar="CSV",
+                    help="print a markdown summary of rocprofv3 counter_collection.csv files "
+                         "(per kernel and grid: dispatches, mean of each counter) and exit")
+    ap.add_argument("--kernels", metavar="REGEX",
+                    help="with --pmc-summary: only kernels whose name matches")
     return ap.parse_args()
 
 
@@ -133,6 +138,77 @@ def trace_summary(paths):
         for key, d in sorted(groups.items(), key=lambda kv: -sum(kv[1])):
             print("| %s | %s | %s | %s | %d | %.2f | %.2f | %.2f |" % (
                 key[0], key[1], key[2], key[3], len(d), statistics.median(d), min(d), max(d)))
+
+
+def pmc_summary(paths, pattern=None):
+    """Markdown tables of rocprofv3 counter runs: per kernel and grid, the mean
+    of each counter over the dispatches (counters are summed over the chip;
+    GRBM_GUI_ACTIVE over the 8 XCDs), and the figures derived from them:
+    MFMA busy = SQ_VALU_MFMA_BUSY_CYCLES / (1024 SIMDs x GRBM_GUI_ACTIVE / 8),
+    bf16 MFMA flop = 512 x SQ_INSTS_VALU_MFMA_MOPS_BF16, and HBM bytes =
+    1024 x FETCH_SIZE or WRITE_SIZE (KiB), before any scaling."""
+    import csv
+    import statistics
+    # dispatches are grouped by kernel, grid and block, and, where the run has
+    # an instruction counter (exact for a given launch shape), by its value,
+    # which tells apart launches of one kernel on different problems
+    per_disp = {}  # (path, dispatch) -> (kernel, grid, block), {counter: value}, ns
+    for path in paths:
+        for r in csv.DictReader(open(path)):
+            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
+            short = name.split("(")[0].strip()
+            short = short[len("void "):] if short.startswith("void ") else short
+            disp = (path, r["Dispatch_Id"])
+            if disp not in per_disp:
+                per_disp[disp] = ((short[-70:], r["Grid_Size"], r["Workgroup_Size"]), {},
+                                  int(r["End_Timestamp"]) - int(r["Start_Timestamp"]))
+            per_disp[disp][1][r["Counter_Name"]] = float(r["Counter_Value"])
+    data = {}   # key -> counter -> dispatch -> value
+    durs = {}   # key -> dispatch -> ns
+    for disp, (k3, ctr, ns) in per_disp.items():
+        insts = sorted(c for c in ctr if c.startswith("SQ_INSTS_"))
+        key = k3 + ((insts[0], ctr[insts[0]]) if insts else ("", 0.0),)
+        for c, v in ctr.items():
+            data.setdefault(key, {}).setdefault(c, {})[disp] = v
+        durs.setdefault(key, {})[disp] = ns
+    import re
+    for key in sorted(data, key=lambda k: -sum(durs[k].values())):
+        if pattern and not re.search(pattern, key[0]):
+            continue
+        ctr = data[key]
+        n = max(len(v) for v in ctr.values())
+        tag = ", %s = %.0f" % key[3] if key[3][0] else ""
+        print("### %s (grid %s, block %s%s): %d dispatches, median %.2f us under counters" % (
+            key[0], key[1], key[2], tag, n, statistics.median(durs[key].values()) / 1e3))
+        print()
+        print("| counter | mean per dispatch | min | max |")
+        print("|---|---|---|---|")
+        mean = {}
+        for c in sorted(ctr):
+            v = list(ctr[c].values())
+            mean[c] = statistics.fmean(v)
+            print("| %s | %.6g | %.6g | %.6g |" % (c, mean[c], min(v), max(v)))
+        derived = []
+        if "GRBM_GUI_ACTIVE" in mean:
+            derived.append(("active cycles per XCD (GRBM_GUI_ACTIVE / 8)",
+                            "%.0f" % (mean["GRBM_GUI_ACTIVE"] / 8)))
+            if mean.get("SQ_VALU_MFMA_BUSY_CYCLES"):
+                derived.append(("MFMA busy (of 1024 SIMDs x active cycles)", "%.3f" % (
+                    mean["SQ_VALU_MFMA_BUSY_CYCLES"] / (1024 * mean["GRBM_GUI_ACTIVE"] / 8))))
+            if "SQ_INSTS_VALU" in mean:
+                derived.append(("VALU instructions per CU per active cycle", "%.3f" % (
+                    mean["SQ_INSTS_VALU"] / (256 * mean["GRBM_GUI_ACTIVE"] / 8))))
+        if mean.get("SQ_INSTS_VALU_MFMA_MOPS_BF16"):
+            derived.append(("bf16 MFMA flop (512 x MOPS)",
+                            "%.6g" % (512 * mean["SQ_INSTS_VALU_MFMA_MOPS_BF16"])))
+        for c in ("FETCH_SIZE", "WRITE_SIZE"):
+            if c in mean:
+                derived.append(("%s bytes (1024 x KiB, unscaled)" % c, "%.0f" % (1024 * mean[c])))
+        if derived:
+            print()
+            for name, val in derived:
+                print("- %s: %s" % (name, val))
+        print()
 
 
 # ---------------------------------------------------------------------------
@@ -777,6 +853,9 @@ def main():
     args = parse()
     if args.trace_summary:
         trace_summary(args.trace_summary)
+        return
+    if args.pmc_summary:
+        pmc_summary(args.pmc_summary, args.kernels)
         return
     if args.gpus != 1:
         print("bench.py runs on one GPU only; --gpus %d is not supported (no multi-GPU path is "
