@@ -68,7 +68,7 @@ ALL_ROWS = ("step", "gemv_g64", "gemm_m2048", "dense8b", "dequant", "gemv2", "w4
 # HBM bytes per GEMV launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this bench, each
 # scaled by the same counter on a 256 MiB copy (profiles/gemv_m1_hbm_traffic.md); valid only
 # for the kernel source they were taken on (sha256 prefix of csrc/tq_gemv_m1.hip).
-GEMV_TRAFFIC = {"1cfc50b97901eb3f": 60691548}
+GEMV_TRAFFIC = {"8b2bbb06ced5cad3": 61144785}
 
 
 def parse():
@@ -111,6 +111,12 @@ def source_hash(name):
 # rocprofv3 summaries
 # ---------------------------------------------------------------------------
 
+def short_kernel_name(name):
+    """A kernel's name without namespaces' noise, argument list or 'void'."""
+    name = name.replace("(anonymous namespace)::", "").split("(")[0].strip()
+    return name[len("void "):] if name.startswith("void ") else name
+
+
 def trace_summary(paths):
     """Markdown tables of a rocprofv3 run: per kernel (stats CSV) and per
     kernel and grid (trace CSV)."""
@@ -122,13 +128,14 @@ def trace_summary(paths):
     print("|---|---|---|---|---|---|")
     for r in sorted(rows, key=lambda r: -float(r["TotalDurationNs"])):
         print("| %s | %s | %.2f | %.2f | %.2f | %.1f%% |" % (
-            r["Name"][:90], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
+            short_kernel_name(r["Name"])[:90], r["Calls"], float(r["AverageNs"]) / 1e3, float(r["MinNs"]) / 1e3,
             float(r["MaxNs"]) / 1e3, 100.0 * float(r["TotalDurationNs"]) / tot))
     if len(paths) > 1:
         tr = list(csv.DictReader(open(paths[1])))
         groups = {}
         for r in tr:
-            key = (r["Kernel_Name"][:70], r.get("Grid_Size_X", r.get("Grid_Size", "?")),
+            key = (short_kernel_name(r["Kernel_Name"])[:70],
+                   r.get("Grid_Size_X", r.get("Grid_Size", "?")),
                    r.get("Grid_Size_Y", ""), r.get("Workgroup_Size_X", r.get("Workgroup_Size", "")))
             groups.setdefault(key, []).append(
                 (int(r["End_Timestamp"]) - int(r["Start_Timestamp"])) / 1e3)
@@ -155,9 +162,7 @@ def pmc_summary(paths, pattern=None):
     per_disp = {}  # (path, dispatch) -> (kernel, grid, block), {counter: value}, ns
     for path in paths:
         for r in csv.DictReader(open(path)):
-            name = r["Kernel_Name"].replace("(anonymous namespace)::", "")
-            short = name.split("(")[0].strip()
-            short = short[len("void "):] if short.startswith("void ") else short
+            short = short_kernel_name(r["Kernel_Name"])
             disp = (path, r["Dispatch_Id"])
             if disp not in per_disp:
                 per_disp[disp] = ((short[-70:], r["Grid_Size"], r["Workgroup_Size"]), {},
