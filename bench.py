@@ -675,6 +675,31 @@ class Bench:
         ms = self.chain(run_mfma, 2)
         flops = grid * 8 * iters * 8 * 16384.0
         out["mfma_bf16_16x16x32"] = {"us": ms * 1e3, "TFLOP/s": flops / (ms * 1e-3) / 1e12}
+        # LDS table reads and VALU issue, per CU and core cycle (the probe reports
+        # the core clock of its own loop)
+        clocks = torch.zeros(2, dtype=torch.int64, device=self.dev)
+        sk = sink.data_ptr()
+
+        def per_cycle(count, ms):
+            c = clocks.cpu().tolist()
+            ghz = c[0] / (c[1] * 10.0) if c[1] > 0 else float("nan")
+            return ghz, count / (ms * 1e-3) / 256 / (ghz * 1e9)
+        lds_iters = 4096
+
+        def run_lds(_):
+            self.ok(L.tq_probe_lds_table(lds_iters, grid, sk, clocks.data_ptr(), self.sp))
+        ms = self.chain(run_lds, 2)
+        lds_bytes = grid * 512 * lds_iters * 128.0
+        ghz, bpc = per_cycle(lds_bytes, ms)
+        out["lds_table_ds_read_b128"] = {"us": ms * 1e3, "GB/s": lds_bytes / (ms * 1e-3) / 1e9,
+                                         "core_GHz": ghz, "bytes_per_CU_per_cycle": bpc}
+        valu_iters = 2048
+        for kind, name in ((0, "valu_v_dot2_f32_bf16"), (1, "valu_v_perm_b32")):
+            def run_valu(_, kind=kind):
+                self.ok(L.tq_probe_valu(kind, valu_iters, grid, sk, clocks.data_ptr(), self.sp))
+            ms = self.chain(run_valu, 2)
+            ghz, ipc = per_cycle(grid * 8 * valu_iters * 128.0, ms)
+            out[name] = {"us": ms * 1e3, "core_GHz": ghz, "wave_instr_per_CU_per_cycle": ipc}
         best_read = max(v["GB/s"] for k, v in out.items() if k.startswith("read_stream_57"))
         out["spec_hbm_GB/s"] = HBM_PEAK_GBS
         out["spec_mfma_bf16_TFLOP/s"] = MFMA_BF16_PEAK_TFLOPS

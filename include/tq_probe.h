@@ -42,6 +42,35 @@ int tq_probe_read_stream(const void *buf, int64_t bytes, int grid, uint32_t *sin
  */
 int tq_probe_mfma_bf16(int64_t iters, int grid, float *sink, void *stream);
 
+/*
+ * LDS table reads in the layout of the decode kernels' code tables: each of
+ * `grid` blocks of 512 threads fills a 64 KB table (entry e of copy j at
+ * byte e * 256 + j * 16), then every thread performs `iters` iterations of
+ * eight 16-byte reads (ds_read_b128) from copy (thread % 16), at eight
+ * entries drawn once per thread: grid * 512 * iters * 128 bytes read.
+ * `sink` (grid * 512 uint32) is written only if the XOR of what was read
+ * equals a value the table cannot give.  If `clocks` (two uint64, may be
+ * NULL) is given, block 0's first thread stores the core-clock cycles and the
+ * 10 ns ticks its loop took, so the caller can turn the rate into bytes per
+ * cycle per CU.
+ *   iters  1 .. 2^24;  grid 1 .. 65535
+ * TQ_ERR_NULL or TQ_ERR_SHAPE otherwise.
+ */
+int tq_probe_lds_table(int iters, int grid, uint32_t *sink, unsigned long long *clocks,
+                       void *stream);
+
+/*
+ * VALU issue rate: every wave of `grid` blocks of 512 threads runs `iters`
+ * iterations of 16 steps of eight independent chains of one instruction,
+ * kind 0 v_dot2_f32_bf16 or kind 1 v_perm_b32 (the decode GEMV's per-byte
+ * instructions): grid * 8 * iters * 128 wave instructions.  `sink` and
+ * `clocks` as for tq_probe_lds_table.
+ *   kind 0 or 1;  iters 1 .. 2^24;  grid 1 .. 65535
+ * TQ_ERR_NULL or TQ_ERR_SHAPE otherwise.
+ */
+int tq_probe_valu(int kind, int iters, int grid, uint32_t *sink, unsigned long long *clocks,
+                  void *stream);
+
 #ifdef __cplusplus
 }
 #endif

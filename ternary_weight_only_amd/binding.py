@@ -28,7 +28,8 @@ SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_qua
            "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped", "tq_w4a16_gemm",
            "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 # Every symbol include/tq_probe.h declares (measurement probes).
-PROBE_SYMBOLS = ("tq_probe_mfma_bf16", "tq_probe_read_stream")
+PROBE_SYMBOLS = ("tq_probe_lds_table", "tq_probe_mfma_bf16", "tq_probe_read_stream",
+                 "tq_probe_valu")
 
 _lib = None
 
@@ -107,6 +108,10 @@ def lib() -> ctypes.CDLL:
         l.tq_probe_read_stream.restype = i32
         l.tq_probe_mfma_bf16.argtypes = [i64, i32, p, p]
         l.tq_probe_mfma_bf16.restype = i32
+        l.tq_probe_lds_table.argtypes = [i32, i32, p, p, p]
+        l.tq_probe_lds_table.restype = i32
+        l.tq_probe_valu.argtypes = [i32, i32, i32, p, p, p]
+        l.tq_probe_valu.restype = i32
         _lib = l
     return _lib
 

@@ -17,7 +17,26 @@ constexpr uint32_t kNever = 0x9E3779B9u;  // the sink is written only for this X
 
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef __bf16 bf16x2 __attribute__((ext_vector_type(2)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef __attribute__((address_space(3))) const volatile u32x4 lds_u32x4_cv;
+typedef __attribute__((address_space(3))) const unsigned char lds_bytes_c;
+
+// Core clock cycles (s_memtime) and 10 ns ticks (s_memrealtime) between two
+// points of block 0's first thread, for the caller's clock estimate.
+struct ClockMark {
+  unsigned long long c, r;
+};
+__device__ __forceinline__ ClockMark clock_mark() {
+  return ClockMark{__builtin_amdgcn_s_memtime(), __builtin_amdgcn_s_memrealtime()};
+}
+__device__ __forceinline__ void clock_store(const ClockMark &a, const ClockMark &b,
+                                            unsigned long long *clocks) {
+  if (clocks && blockIdx.x == 0 && threadIdx.x == 0) {
+    clocks[0] = b.c - a.c;
+    clocks[1] = b.r - a.r;
+  }
+}
 
 // Chunk c (16 bytes) of the buffer is read by thread c % T of the grid's T
 // threads, in round c / T; eight rounds' loads are issued before any is
@@ -72,6 +91,77 @@ __global__ __launch_bounds__(kThreads) void mfma_bf16_kernel(int64_t iters,
   }
 }
 
+// A 64 KB LDS table in the decode kernels' layout (entry e of copy j at
+// e * 256 + j * 16); every thread reads eight entries per iteration, one
+// 16-byte ds_read_b128 each, from copy lane % 16 at entries drawn once per
+// thread.  The reads are volatile, so each iteration performs all eight.
+__global__ __launch_bounds__(kThreads) void lds_table_kernel(int iters, uint32_t *__restrict__ sink,
+                                                             unsigned long long *clocks) {
+  __shared__ u32x4 table[4096];
+  for (int i = threadIdx.x; i < 4096; i += kThreads)
+    table[i] = u32x4{(uint32_t)i, (uint32_t)i * 3u, (uint32_t)i * 5u, (uint32_t)i * 7u};
+  __syncthreads();
+  const uint32_t copy = (threadIdx.x & 15u) * 16u;
+  uint32_t st = threadIdx.x * 2654435761u + blockIdx.x * 40503u;
+  uint32_t addr[8];
+#pragma unroll
+  for (int u = 0; u < 8; ++u) {
+    st = st * 1664525u + 1013904223u;
+    addr[u] = ((st >> 24) << 8) | copy;
+  }
+  lds_bytes_c *base = (lds_bytes_c *)table;
+  uint32_t acc = 0;
+  const ClockMark t0 = clock_mark();
+  for (int it = 0; it < iters; ++it) {
+    u32x4 e[8];
+#pragma unroll
+    for (int u = 0; u < 8; ++u) e[u] = *(lds_u32x4_cv *)(base + addr[u]);
+#pragma unroll
+    for (int u = 0; u < 8; ++u) acc ^= e[u].x;
+    // the other dwords stay live until here, so no read waits on another
+#pragma unroll
+    for (int u = 0; u < 8; ++u) asm volatile("" ::"v"(e[u].y), "v"(e[u].z), "v"(e[u].w));
+  }
+  const ClockMark t1 = clock_mark();
+  clock_store(t0, t1, clocks);
+  if (acc == kNever) sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = acc;
+}
+
+// Eight independent chains of one VALU instruction kind, 16 steps per
+// iteration: kind 0 v_dot2_f32_bf16 (fp32 accumulate), kind 1 v_perm_b32.
+template <int KIND>
+__global__ __launch_bounds__(kThreads) void valu_kernel(int iters, uint32_t *__restrict__ sink,
+                                                        unsigned long long *clocks) {
+  uint32_t a[8];
+  float f[8];
+  const uint32_t b = threadIdx.x * 0x9E3779B9u;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) {
+    a[i] = threadIdx.x + (uint32_t)i;
+    f[i] = (float)i;
+  }
+  const ClockMark t0 = clock_mark();
+  for (int it = 0; it < iters; ++it) {
+#pragma unroll
+    for (int u = 0; u < 16; ++u) {
+#pragma unroll
+      for (int i = 0; i < 8; ++i) {
+        if (KIND == 0)
+          f[i] = __builtin_amdgcn_fdot2_f32_bf16(__builtin_bit_cast(bf16x2, a[i]),
+                                                 __builtin_bit_cast(bf16x2, b), f[i], false);
+        else
+          a[i] = __builtin_amdgcn_perm(a[i], b, 0x05040100u + (uint32_t)u);
+      }
+    }
+  }
+  const ClockMark t1 = clock_mark();
+  clock_store(t0, t1, clocks);
+  uint32_t x = 0;
+#pragma unroll
+  for (int i = 0; i < 8; ++i) x ^= a[i] ^ __float_as_uint(f[i]);
+  if (x == kNever) sink[(int64_t)blockIdx.x * kThreads + threadIdx.x] = x;
+}
+
 }  // namespace
 
 extern "C" {
@@ -84,6 +174,31 @@ int tq_probe_read_stream(const void *buf, int64_t bytes, int grid, uint32_t *sin
   (void)hipGetLastError();
   hipLaunchKernelGGL(read_stream_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
                      (hipStream_t)stream, static_cast<const u32x4 *>(buf), bytes / 16, sink);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_probe_lds_table(int iters, int grid, uint32_t *sink, unsigned long long *clocks,
+                       void *stream) {
+  if (!sink) return TQ_ERR_NULL;
+  if (iters < 1 || iters > (1 << 24) || grid < 1 || grid > 65535) return TQ_ERR_SHAPE;
+  (void)hipGetLastError();
+  hipLaunchKernelGGL(lds_table_kernel, dim3((unsigned)grid), dim3(kThreads), 0,
+                     (hipStream_t)stream, iters, sink, clocks);
+  return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
+}
+
+int tq_probe_valu(int kind, int iters, int grid, uint32_t *sink, unsigned long long *clocks,
+                  void *stream) {
+  if (!sink) return TQ_ERR_NULL;
+  if (kind < 0 || kind > 1 || iters < 1 || iters > (1 << 24) || grid < 1 || grid > 65535)
+    return TQ_ERR_SHAPE;
+  (void)hipGetLastError();
+  if (kind == 0)
+    hipLaunchKernelGGL(valu_kernel<0>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, iters, sink, clocks);
+  else
+    hipLaunchKernelGGL(valu_kernel<1>, dim3((unsigned)grid), dim3(kThreads), 0,
+                       (hipStream_t)stream, iters, sink, clocks);
   return hipGetLastError() == hipSuccess ? TQ_OK : TQ_ERR_LAUNCH;
 }
 

@@ -64,6 +64,14 @@ def test_probe_argument_errors():
     assert lib.tq_probe_mfma_bf16(0, 4, FAKE, None) == -2
     assert lib.tq_probe_mfma_bf16(10, 0, FAKE, None) == -2
     assert lib.tq_probe_mfma_bf16((1 << 24) + 1, 4, FAKE, None) == -2
+    assert lib.tq_probe_lds_table(10, 4, None, None, None) == -1
+    assert lib.tq_probe_lds_table(0, 4, FAKE, None, None) == -2
+    assert lib.tq_probe_lds_table(10, 65536, FAKE, None, None) == -2
+    assert lib.tq_probe_valu(0, 10, 4, None, None, None) == -1
+    assert lib.tq_probe_valu(2, 10, 4, FAKE, None, None) == -2
+    assert lib.tq_probe_valu(-1, 10, 4, FAKE, None, None) == -2
+    assert lib.tq_probe_valu(1, 0, 4, FAKE, None, None) == -2
+    assert lib.tq_probe_valu(1, 10, 0, FAKE, None, None) == -2
 
 
 def test_packed_bytes_helper():
