@@ -35,10 +35,12 @@ of launches between HIP events on the same stream, median of three):
                decode at M = 1, 4, 16 over a ring of copies (>= 1 GiB)
   dequant      decode to bf16 of every matrix of a slot (two launches per slot)
   gemv2        the decode pass over the 2-bit format (one grouped launch)
-  w4a16        the decode pass over seeded W4A16 parameters (one grouped launch)
+  w4a16        the decode pass over seeded W4A16 parameters (one grouped launch), and
+               the W4A16 prefill matmul at --prefill-m rows (one launch per shape)
   qat          the QAT forward of the stack (two launches a pass)
   ceilings     plain HBM read streams over the decode pass's bytes (eight
-               57.8 MB buffers) and over 1 GiB, and a bf16 MFMA-only loop
+               57.8 MB buffers) and over 1 GiB, a bf16 MFMA-only loop, LDS
+               table reads and VALU issue of v_dot2_f32_bf16 and v_perm_b32
   cpu          the CPU oracle on bounded samples of the same workloads, at
                one thread and at the host's cores; it also checks the GPU
                outputs captured above against its own results
@@ -620,6 +622,32 @@ class Bench:
             "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "Tweights/s": self.weights / (ms * 1e-3) / 1e12, "bytes_per_pass": b, "launches": 1,
             "in_step": False}
+        # the W4A16 prefill matmul on the matrix cores: one tq_w4a16_gemm launch per matrix
+        MP = self.args.prefill_m
+        xs = {K: self.bf16(self.inputs.prefill_activation(MP, K))
+              for K in sorted({k for _, k in self.shapes})}
+        yp = [torch.empty(MP, N, dtype=torch.bfloat16, device=self.dev) for N, K in self.shapes]
+        sl = slots[0]
+
+        gcalls = [(N, K, len(idx), self.ptrs([xs[K]] * len(idx)), self.ptrs([sl[i][0] for i in idx]),
+                   self.ptrs([sl[i][1] for i in idx]), self.ptrs([sl[i][2] for i in idx]),
+                   self.ptrs([yp[i] for i in idx])) for (N, K), idx in self.groups.items()]
+
+        def run_gemm(_):
+            for N, K, n, ax, ap, asc, abi, ay in gcalls:
+                self.ok(L.tq_w4a16_gemm_batched(n, ax, ap, asc, abi, MP, N, K, G, ay, self.sp))
+
+        ms = self.chain(run_gemm, 2)
+        flops = sum(2.0 * MP * N * K for N, K in self.shapes)
+        self.captured["w4a16_gemm"] = {i: host[i] + (yp[i][:8].float().cpu().numpy(),)
+                                       for i in (0, 71)}
+        self.rows["prefill_gemm_w4a16"] = {
+            "config": "72-matrix FFN stack, W4A16 G=%d, M=%d, one tq_w4a16_gemm_batched launch "
+                      "per shape" % (G, MP),
+            "ms": ms, "TFLOP/s": flops / (ms * 1e-3) / 1e12,
+            "frac_mfma": flops / (ms * 1e-3) / 1e12 / MFMA_BF16_PEAK_TFLOPS, "launches": 2,
+            "in_step": False, "timing": "median of 3 chains of 2 passes"}
+        del yp, xs
 
     # ---- QAT forward ----
     def row_qat(self):
@@ -865,6 +893,15 @@ def cpu_baseline(b, min_s):
             tol = 1e-3 * bd * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref)
             ok = bool((np.abs(yg.astype(np.float64) - y_ref) <= tol).all())
             exact(ok, True, "W4A16 decode GEMV, matrix %d" % i)
+    if "w4a16_gemm" in cap:
+        for i in (0, 71):
+            N, K = shapes[i]
+            pk, sc, bi, yg = cap["w4a16_gemm"][i]
+            xp = b.inputs.prefill_activation(b.args.prefill_m, K)[:8]
+            y_ref, bd = oracle.w4a16_matmul(xp, pk, sc, bi, N, K, G, threads=nt)
+            tol = 1e-3 * bd * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref)
+            ok = bool((np.abs(yg.astype(np.float64) - y_ref) <= tol).all())
+            exact(ok, True, "W4A16 prefill GEMM M=%d rows 0-7, matrix %d" % (b.args.prefill_m, i))
     if "qat_w_hat" in cap:
         for i in (0, 71):
             f, _, _ = oracle.fake_quantize(mats[i], G)

@@ -422,6 +422,19 @@ int tq_w4a16_gemm(const uint16_t *x, const uint32_t *packed, const uint16_t *sca
                   const uint16_t *biases, int64_t M, int64_t N, int64_t K, int G, uint16_t *y,
                   void *stream);
 
+/* Batched form: `count` same-shaped problems, each as tq_w4a16_gemm on
+ * xs[i], packeds[i], scales[i], biases[i], ys[i] (HOST arrays of DEVICE
+ * pointers, read during the call only), one launch per 64 problems (the
+ * problems share the launch's grid, so a stack of matrices fills the GPU
+ * where one matrix would not).  M = 1 with K <= 4096 runs
+ * tq_w4a16_gemv_batched's kernel (packed then 16-byte aligned).  count == 0
+ * does nothing; count < 0 is TQ_ERR_SHAPE; a NULL or misaligned pointer in
+ * any entry rejects the whole call with nothing enqueued. */
+int tq_w4a16_gemm_batched(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
+                          const uint16_t *const *scales, const uint16_t *const *biases,
+                          int64_t M, int64_t N, int64_t K, int G, uint16_t *const *ys,
+                          void *stream);
+
 /* Batched form: `count` same-shaped problems, each as tq_w4a16_gemv on
  * xs[i], packeds[i], scales[i], biases[i], ys[i] (HOST arrays of DEVICE
  * pointers, read during the call only), one launch per 128.  Errors as

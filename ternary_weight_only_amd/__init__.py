@@ -50,6 +50,7 @@ from .binding import (  # noqa: F401
     w4a16_gemv_batched,
     w4a16_gemv_grouped,
     w4a16_gemm,
+    w4a16_gemm_batched,
     lib,
     new_status,
     packed_bytes,

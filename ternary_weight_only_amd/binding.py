@@ -25,8 +25,8 @@ SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_qua
            "tq_quantize_pack_batched", "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack",
            "tq_unpack_batched", "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2",
            "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
-           "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped", "tq_w4a16_gemm",
-           "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
+           "tq_w4a16_gemm", "tq_w4a16_gemm_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 # Every symbol include/tq_probe.h declares (measurement probes).
 PROBE_SYMBOLS = ("tq_probe_lds_table", "tq_probe_mfma_bf16", "tq_probe_read_stream",
                  "tq_probe_valu")
@@ -87,6 +87,8 @@ def lib() -> ctypes.CDLL:
         l.tq_w4a16_gemv_grouped.restype = i32
         l.tq_w4a16_gemm.argtypes = [p, p, p, p, i64, i64, i64, i32, p, p]
         l.tq_w4a16_gemm.restype = i32
+        l.tq_w4a16_gemm_batched.argtypes = [i32, p, p, p, p, i64, i64, i64, i32, p, p]
+        l.tq_w4a16_gemm_batched.restype = i32
         l.tq_unpack_batched.argtypes = [i32, p, i64, i64, i32, p, p, p]
         l.tq_unpack_batched.restype = i32
         l.tq_unpack.argtypes = [p, i64, i64, i32, p, p, p]
@@ -593,6 +595,28 @@ def w4a16_gemm(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,
                             biases.data_ptr(), M, N, K, G, y.data_ptr(), _stream()),
         "tq_w4a16_gemm")
     return y
+
+
+def w4a16_gemm_batched(xs, packeds, scales_list, biases_list, N: int, K: int, G: int,
+                       outs=None):
+    """Same-shaped W4A16 matmuls (every x [M,K] with the same M) -> list of
+    y bf16 [M,N], one launch per 64."""
+    n = len(xs)
+    if not (len(packeds) == len(scales_list) == len(biases_list) == n):
+        raise TQError("xs, packeds, scales and biases differ in length")
+    if n == 0:
+        return []
+    dev = None
+    for x, pk, sc, bi in zip(xs, packeds, scales_list, biases_list):
+        dev = _w4_check(x, pk, sc, bi, N, K, G, dev, any_m=True)
+    M = xs[0].shape[0]
+    if any(x.shape[0] != M for x in xs):
+        raise TQError("w4a16_gemm_batched: every x needs the same number of rows")
+    outs = _outs(outs, "outs", [(M, N)] * n, torch.bfloat16, BF16, dev)
+    _rc(lib().tq_w4a16_gemm_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list),
+                                    _ptrs(biases_list), M, N, K, G, _ptrs(outs), _stream()),
+        "tq_w4a16_gemm_batched")
+    return outs
 
 
 def w4a16_gemv(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor,

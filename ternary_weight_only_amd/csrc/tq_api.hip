@@ -294,10 +294,9 @@ int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *
                                   (hipStream_t)stream);
   } else {
     // rows longer than the table kernel takes (K > 4096): the matrix-core
-    // kernel, one launch per problem
-    for (int i = 0; i < count; ++i)
-      tq::launch_w4a16_mfma(xs[i], packeds[i], scales[i], biases[i], 1, N, K, G, ys[i],
-                            (hipStream_t)stream);
+    // kernel, one launch per 64 problems
+    tq::launch_w4a16_mfma_batched(count, xs, packeds, scales, biases, 1, N, K, G, ys,
+                                  (hipStream_t)stream);
   }
   return finish_launch();
 }
@@ -358,6 +357,33 @@ int tq_w4a16_gemm(const uint16_t *x, const uint32_t *packed, const uint16_t *sca
                                   (hipStream_t)stream);
   else
     tq::launch_w4a16_mfma(x, packed, scales, biases, M, N, K, G, y, (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_w4a16_gemm_batched(int count, const uint16_t *const *xs, const uint32_t *const *packeds,
+                          const uint16_t *const *scales, const uint16_t *const *biases,
+                          int64_t M, int64_t N, int64_t K, int G, uint16_t *const *ys,
+                          void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !biases || !ys) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (M < 1 || !tq::w4a16_mfma_supported(M, N, K, G)) return TQ_ERR_SHAPE;
+  const bool table = M == 1 && tq::w4a16_gemv_supported(N, K, G);
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !biases[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], table ? 16 : 4) || !aligned(scales[i], 2) ||
+        !aligned(biases[i], 2) || !aligned(ys[i], 2))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  if (table)
+    tq::launch_w4a16_gemv_batched(count, xs, packeds, scales, biases, ys, N, K, G,
+                                  (hipStream_t)stream);
+  else
+    tq::launch_w4a16_mfma_batched(count, xs, packeds, scales, biases, M, N, K, G, ys,
+                                  (hipStream_t)stream);
   return finish_launch();
 }
 

@@ -61,6 +61,10 @@ bool w4a16_mfma_supported(int64_t M, int64_t N, int64_t K, int G);
 void launch_w4a16_mfma(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
                        const uint16_t *biases, int64_t M, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream);
+void launch_w4a16_mfma_batched(int count, const uint16_t *const *xs,
+                               const uint32_t *const *packeds, const uint16_t *const *scales,
+                               const uint16_t *const *biases, int64_t M, int64_t N, int64_t K,
+                               int G, uint16_t *const *ys, hipStream_t stream);
 
 void launch_unpack_batched(int count, const uint8_t *const *packeds, int64_t N, int64_t K, int G,
                            int8_t *const *codes, int32_t *d_status, hipStream_t stream);

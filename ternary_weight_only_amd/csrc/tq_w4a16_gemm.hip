@@ -11,7 +11,8 @@
 // here BM = 16 rows per block for M <= 16, 64 above).
 //
 // Block: 4 waves; wave w computes a BM x 32 tile of y (columns n0 + 32w ..
-// n0 + 32w + 31) with v_mfma_f32_16x16x32_bf16.  Per 32-wide k step, lane
+// n0 + 32w + 31) with v_mfma_f32_16x16x32_bf16.  A launch takes up to 64
+// same-shaped problems, one per grid z index.  Per 32-wide k step, lane
 // (j, q) of a wave:
 //   * loads the uint32 of eight codes of W row n0 + 32w + 16t + j at k + 8q
 //     (t = 0, 1) and turns each code into its exact bf16 value (the B
@@ -38,6 +39,17 @@ constexpr int kThreads = 256;  // 4 waves
 constexpr int kTN = 2;         // 16-column MFMA tiles per wave
 constexpr int kBN = 4 * 16 * kTN;  // columns per block: 128
 constexpr uint32_t kOutOfRange = 0x80000000u;
+constexpr int kMaxBatch = 64;  // problems per launch (2.5 KB of kernel arguments)
+
+// Up to kMaxBatch same-shaped problems per launch, passed by value; the
+// grid's z index is the problem.
+struct W4Batch {
+  const uint16_t *x[kMaxBatch];
+  const uint32_t *packed[kMaxBatch];
+  const uint16_t *scales[kMaxBatch];
+  const uint16_t *biases[kMaxBatch];
+  uint16_t *y[kMaxBatch];
+};
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
   return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
@@ -69,10 +81,14 @@ __device__ __forceinline__ bf16x8 codes_to_bf16(uint32_t w) {
 }
 
 template <int G, int TM>
-__global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
-    const uint16_t *__restrict__ x, const uint32_t *__restrict__ packed,
-    const uint16_t *__restrict__ scales, const uint16_t *__restrict__ biases, int M, int N, int K,
-    uint16_t *__restrict__ y) {
+__global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(const W4Batch args, int M, int N,
+                                                              int K) {
+  const int pi = (int)blockIdx.z;
+  const uint16_t *__restrict__ x = args.x[pi];
+  const uint32_t *__restrict__ packed = args.packed[pi];
+  const uint16_t *__restrict__ scales = args.scales[pi];
+  const uint16_t *__restrict__ biases = args.biases[pi];
+  uint16_t *__restrict__ y = args.y[pi];
   constexpr int BM = 16 * TM;
   constexpr int KS = G / 32;  // k steps per group
   const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
@@ -178,21 +194,20 @@ __global__ __launch_bounds__(kThreads) void w4a16_mfma_kernel(
 }
 
 template <int G, int TM>
-void launch_tm(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
-               const uint16_t *biases, int64_t M, int64_t N, int64_t K, uint16_t *y,
+void launch_tm(const W4Batch &args, int count, int64_t M, int64_t N, int64_t K,
                hipStream_t stream) {
-  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + 16 * TM - 1) / (16 * TM)));
-  hipLaunchKernelGGL((w4a16_mfma_kernel<G, TM>), grid, dim3(kThreads), 0, stream, x, packed,
-                     scales, biases, (int)M, (int)N, (int)K, y);
+  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + 16 * TM - 1) / (16 * TM)),
+                  (unsigned)count);
+  hipLaunchKernelGGL((w4a16_mfma_kernel<G, TM>), grid, dim3(kThreads), 0, stream, args, (int)M,
+                     (int)N, (int)K);
 }
 
 template <int G>
-void launch_g(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
-              const uint16_t *biases, int64_t M, int64_t N, int64_t K, uint16_t *y,
+void launch_g(const W4Batch &args, int count, int64_t M, int64_t N, int64_t K,
               hipStream_t stream) {
-  if (M <= 16) launch_tm<G, 1>(x, packed, scales, biases, M, N, K, y, stream);
-  else if (M <= 32) launch_tm<G, 2>(x, packed, scales, biases, M, N, K, y, stream);
-  else launch_tm<G, 4>(x, packed, scales, biases, M, N, K, y, stream);
+  if (M <= 16) launch_tm<G, 1>(args, count, M, N, K, stream);
+  else if (M <= 32) launch_tm<G, 2>(args, count, M, N, K, stream);
+  else launch_tm<G, 4>(args, count, M, N, K, stream);
 }
 
 }  // namespace
@@ -204,11 +219,26 @@ bool w4a16_mfma_supported(int64_t M, int64_t N, int64_t K, int G) {
          (N + kBN) < (int64_t(1) << 30) && M <= int64_t(65535) * 64;  // grid.y <= 65535
 }
 
+void launch_w4a16_mfma_batched(int count, const uint16_t *const *xs,
+                               const uint32_t *const *packeds, const uint16_t *const *scales,
+                               const uint16_t *const *biases, int64_t M, int64_t N, int64_t K,
+                               int G, uint16_t *const *ys, hipStream_t stream) {
+  for (int i0 = 0; i0 < count; i0 += kMaxBatch) {
+    const int n = count - i0 < kMaxBatch ? count - i0 : kMaxBatch;
+    W4Batch args = {};
+    for (int i = 0; i < n; ++i) {
+      args.x[i] = xs[i0 + i]; args.packed[i] = packeds[i0 + i]; args.scales[i] = scales[i0 + i];
+      args.biases[i] = biases[i0 + i]; args.y[i] = ys[i0 + i];
+    }
+    if (G == 64) launch_g<64>(args, n, M, N, K, stream);
+    else launch_g<128>(args, n, M, N, K, stream);
+  }
+}
+
 void launch_w4a16_mfma(const uint16_t *x, const uint32_t *packed, const uint16_t *scales,
                        const uint16_t *biases, int64_t M, int64_t N, int64_t K, int G,
                        uint16_t *y, hipStream_t stream) {
-  if (G == 64) launch_g<64>(x, packed, scales, biases, M, N, K, y, stream);
-  else launch_g<128>(x, packed, scales, biases, M, N, K, y, stream);
+  launch_w4a16_mfma_batched(1, &x, &packed, &scales, &biases, M, N, K, G, &y, stream);
 }
 
 }  // namespace tq

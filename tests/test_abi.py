@@ -369,6 +369,24 @@ def test_w4a16_gemm_argument_errors():
     assert f(FAKE, FAKE, FAKE, FAKE, 2, 4, 128, 128, FAKE + 1, None) == -4
 
 
+def test_w4a16_gemm_batched_argument_errors():
+    lib = _lib()
+    f = lib.tq_w4a16_gemm_batched
+    P = ctypes.c_void_p
+    one = (P * 1)(FAKE)
+    null = (P * 1)(None)
+    odd = (P * 1)(FAKE + 1)
+    assert f(0, None, None, None, None, 2, 4, 128, 128, None, None) == 0   # nothing to do
+    assert f(-1, one, one, one, one, 2, 4, 128, 128, one, None) == -2
+    assert f(1, None, one, one, one, 2, 4, 128, 128, one, None) == -1
+    assert f(1, one, one, one, one, 2, 4, 128, 128, null, None) == -1
+    assert f(1, one, one, one, one, 0, 4, 128, 128, one, None) == -2       # M < 1
+    assert f(1, one, one, one, one, 2, 4, 192, 128, one, None) == -2       # K % G
+    assert f(1, one, one, one, one, 2, 4, 128, 32, one, None) == -3        # G
+    assert f(1, one, one, one, one, 2, 4, 128, 128, odd, None) == -4       # y alignment
+    assert f(1, odd, one, one, one, 2, 4, 128, 128, one, None) == -4       # x alignment
+
+
 def test_product_path_does_not_import_oracle():
     pkg = os.path.join(ROOT, "ternary_weight_only_amd")
     for dirpath, _, files in os.walk(pkg):

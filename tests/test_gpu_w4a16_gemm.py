@@ -140,3 +140,26 @@ def test_w4a16_gemm_nonfinite_parameter_stays_in_its_row():
     y_ref, bound = oracle.w4a16_matmul(x, packed, s2, b2, N, K, G)
     tol = 1e-3 * bound * (1 + 2.0 ** -8) + 2.0 ** -8 * np.abs(y_ref)
     assert (np.abs(y[:, keep] - y_ref[:, keep]) <= tol[:, keep]).all()
+
+
+@pytest.mark.parametrize("M,N,K,G,count", [(5, 300, 640, 64, 3), (40, 1024, 3584, 128, 2),
+                                           (512, 1024, 3584, 128, 3), (1, 200, 8192, 128, 2),
+                                           (1, 256, 1024, 128, 3)])
+def test_w4a16_gemm_batched(M, N, K, G, count):
+    """Batched launches (the problems on the grid's z axis, or the table GEMV
+    at M = 1 with K <= 4096): every output bit-identical to single calls and
+    within the bar."""
+    import torch
+    import ternary_weight_only_amd as tq
+    probs = [random_problem(600 + 7 * i + M, N, K, G) for i in range(count)]
+    xs = [inputs.activation(650 + 7 * i + K, M, K) for i in range(count)]
+    say("w4a16 gemm batched M=%d W[%d,%d] G=%d x%d" % (M, N, K, G, count))
+    ys = tq.w4a16_gemm_batched([dev_bf16(x) for x in xs], [dev_u32(p) for p, _, _ in probs],
+                               [dev_bf16(s) for _, s, _ in probs],
+                               [dev_bf16(b) for _, _, b in probs], N, K, G)
+    torch.cuda.synchronize()
+    for i, ((packed, s, b), x, y) in enumerate(zip(probs, xs, ys)):
+        yb = host_u16(y)
+        assert np.array_equal(yb, _gemm(x, packed, s, b, N, K, G)), "problem %d" % i
+        y_ref, bound = oracle.w4a16_matmul(x, packed, s, b, N, K, G)
+        _check(yb, y_ref, bound, "batched problem %d" % i)
