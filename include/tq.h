@@ -353,9 +353,10 @@ int tq_unpack2(const uint8_t *packed2, int64_t N, int64_t K, int G, int8_t *code
  * (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation").
  *   x [1,K] bf16 16-byte aligned; packed2 [N, K/4] 16-byte aligned; scales
  *   [N, K/G] fp16 2-byte aligned; y [N] fp32 4-byte aligned, overwritten
- * K <= 4096 (K/64 <= 64) and N < 2^28, else TQ_ERR_SHAPE.  A field of 3 sets
- * TQ_DEV_INVALID_BYTE and counts as code 0.  Deterministic; accuracy as
- * tq_gemv.
+ * K <= 4096 (K/64 <= 64) with N < 2^28 runs a table-decode kernel; longer
+ * rows run tq_gemm2's matrix-core kernel at M = 1 (its limits apply, else
+ * TQ_ERR_SHAPE).  A field of 3 sets TQ_DEV_INVALID_BYTE and counts as code
+ * 0.  Deterministic; accuracy as tq_gemv.
  */
 int tq_gemv2(const uint16_t *x, const uint8_t *packed2, const uint16_t *scales, int64_t N,
              int64_t K, int G, float *y, int32_t *d_status, void *stream);
@@ -376,6 +377,33 @@ int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const 
 int tq_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packed2s,
                      const uint16_t *const *scales, float *const *ys, const int64_t *Ns,
                      const int64_t *Ks, int G, int32_t *d_status, void *stream);
+
+/*
+ * Matmul over the 2-bit format for any number of activation rows and any row
+ * length, on the matrix cores (bf16 MFMA on the exact codes; fp32 group
+ * partials scaled by the fp16 scale):
+ *   y[m,n] = sum_g s[n,g] * sum_{j<G} x[m, gG+j] * c[n, gG+j]
+ * (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation";
+ * format as tq_gemv2).
+ *   x [M,K] bf16 16-byte aligned; packed2 [N, K/4] 2-byte aligned (16-byte
+ *   for M = 1 with K <= 4096, which runs tq_gemv2's kernel); scales [N, K/G]
+ *   fp16 2-byte aligned; y [M,N] fp32 4-byte aligned, overwritten
+ * G is 64 or 128 (TQ_ERR_GROUP otherwise); K % G == 0, M * K * 2, N * K / 4
+ * and N * K/G * 2 below 2^31, M <= 4194240, else TQ_ERR_SHAPE.  A field of 3
+ * sets TQ_DEV_INVALID_BYTE and counts as code 0.  Deterministic; accuracy as
+ * tq_gemv.
+ */
+int tq_gemm2(const uint16_t *x, const uint8_t *packed2, const uint16_t *scales, int64_t M,
+             int64_t N, int64_t K, int G, float *y, int32_t *d_status, void *stream);
+
+/* Batched form: `count` same-shaped problems, each as tq_gemm2 on xs[i],
+ * packed2s[i], scales[i], ys[i] (HOST arrays of DEVICE pointers, read during
+ * the call only), one launch per 64 problems.  count == 0 does nothing;
+ * count < 0 is TQ_ERR_SHAPE; a NULL or misaligned pointer in any entry
+ * rejects the whole call with nothing enqueued. */
+int tq_gemm2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packed2s,
+                     const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                     int64_t K, int G, int32_t *d_status, void *stream);
 
 /*
  * W4A16: group-wise affine 4-bit weights, bf16 activations and output

@@ -12,6 +12,7 @@ package only marshals torch tensors to that ABI:
     w_hat          = dequantize(packed, scales, N, K, G)  # bf16 c * s
     packed2, scales = quantize_pack2(w_bf16, G)     # 2-bit format, four codes a byte
     y              = gemv2(x_bf16, packed2, scales, N, K, G)  # its M = 1 GEMV
+    y              = gemm2(x_bf16, packed2, scales, N, K, G)  # any M, any K
     w_hats         = dequantize_batched(packeds, scales, N, K, G)  # many same-shaped
     y              = gemv(x_bf16, packed, scales, N, K, G)   # M <= 16
     ys             = gemv_batched(xs, packeds, scales, N, K, G)  # many same-shaped
@@ -43,6 +44,8 @@ from .binding import (  # noqa: F401
     gemv,
     gemv_batched,
     gemv_grouped,
+    gemm2,
+    gemm2_batched,
     gemv2,
     gemv2_batched,
     gemv2_grouped,

@@ -25,7 +25,7 @@ SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_qua
            "tq_quantize_pack_batched", "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack",
            "tq_unpack_batched", "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2",
            "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
-           "tq_gemv2_grouped", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
+           "tq_gemv2_grouped", "tq_gemm2", "tq_gemm2_batched", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
            "tq_w4a16_gemm", "tq_w4a16_gemm_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
 # Every symbol include/tq_probe.h declares (measurement probes).
 PROBE_SYMBOLS = ("tq_probe_lds_table", "tq_probe_mfma_bf16", "tq_probe_read_stream",
@@ -79,6 +79,10 @@ def lib() -> ctypes.CDLL:
         l.tq_gemv2_batched.restype = i32
         l.tq_gemv2_grouped.argtypes = [i32, p, p, p, p, p, p, i32, p, p]
         l.tq_gemv2_grouped.restype = i32
+        l.tq_gemm2.argtypes = [p, p, p, i64, i64, i64, i32, p, p, p]
+        l.tq_gemm2.restype = i32
+        l.tq_gemm2_batched.argtypes = [i32, p, p, p, p, i64, i64, i64, i32, p, p]
+        l.tq_gemm2_batched.restype = i32
         l.tq_w4a16_gemv.argtypes = [p, p, p, p, i64, i64, i32, p, p]
         l.tq_w4a16_gemv.restype = i32
         l.tq_w4a16_gemv_batched.argtypes = [i32, p, p, p, p, p, i64, i64, i32, p]
@@ -523,6 +527,43 @@ def gemv2(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, N: int, K
     _rc(lib().tq_gemv2(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), N, K, G, y.data_ptr(),
                        _st(status, dev), _stream()), "tq_gemv2")
     return y
+
+
+def gemm2(x: torch.Tensor, packed: torch.Tensor, scales: torch.Tensor, N: int, K: int, G: int,
+          status=None, out=None):
+    """2-bit format, any M: x [M,K] bf16 -> y fp32 [M,N]."""
+    _dev(x, "x", BF16, 2)
+    dev = x.device
+    if x.shape[1] != K:
+        raise TQError("gemm2: x must be [M,%d]" % K)
+    M = x.shape[0]
+    _check_packed2(packed, scales, N, K, G, dev, "gemm2")
+    y = _out(out, "y", (M, N), torch.float32, F32, dev)
+    _rc(lib().tq_gemm2(x.data_ptr(), packed.data_ptr(), scales.data_ptr(), M, N, K, G,
+                       y.data_ptr(), _st(status, dev), _stream()), "tq_gemm2")
+    return y
+
+
+def gemm2_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):
+    """2-bit format, same-shaped problems (every x [M,K] with the same M):
+    list of y fp32 [M,N], one launch per 64."""
+    n = len(xs)
+    if len(packeds) != n or len(scales_list) != n:
+        raise TQError("xs, packeds and scales differ in length")
+    if n == 0:
+        return []
+    _dev(xs[0], "x", BF16, 2)
+    dev = xs[0].device
+    M = xs[0].shape[0]
+    for x, pk, sc in zip(xs, packeds, scales_list):
+        _dev(x, "x", BF16, 2, dev)
+        if tuple(x.shape) != (M, K):
+            raise TQError("gemm2_batched: every x must be [%d,%d]" % (M, K))
+        _check_packed2(pk, sc, N, K, G, dev, "gemm2_batched")
+    outs = _outs(outs, "outs", [(M, N)] * n, torch.float32, F32, dev)
+    _rc(lib().tq_gemm2_batched(n, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(outs),
+                               M, N, K, G, _st(status, dev), _stream()), "tq_gemm2_batched")
+    return outs
 
 
 def gemv2_batched(xs, packeds, scales_list, N: int, K: int, G: int, status=None, outs=None):

@@ -231,7 +231,8 @@ int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const 
   if (!xs || !packeds || !scales || !ys) return TQ_ERR_NULL;
   const int rc = check_nkg(N, K, G);
   if (rc) return rc;
-  if (!tq::gemv2_supported(N, K, G)) return TQ_ERR_SHAPE;
+  const bool table = tq::gemv2_supported(N, K, G);
+  if (!table && !tq::matmul2_supported(1, N, K, G)) return TQ_ERR_SHAPE;
   if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
   for (int i = 0; i < count; ++i) {
     if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
@@ -240,8 +241,12 @@ int tq_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const 
       return TQ_ERR_ALIGN;
   }
   (void)hipGetLastError();
-  tq::launch_gemv2_batched(count, xs, packeds, scales, ys, N, K, G, d_status,
-                           (hipStream_t)stream);
+  if (table)
+    tq::launch_gemv2_batched(count, xs, packeds, scales, ys, N, K, G, d_status,
+                             (hipStream_t)stream);
+  else  // rows longer than the table kernel takes: the matrix-core kernel
+    tq::launch_matmul2_batched(count, xs, packeds, scales, ys, 1, N, K, G, d_status,
+                               (hipStream_t)stream);
   return finish_launch();
 }
 
@@ -255,21 +260,70 @@ int tq_gemv2_grouped(int count, const uint16_t *const *xs, const uint8_t *const 
   for (int i = 0; i < count; ++i) {
     const int rc = check_nkg(Ns[i], Ks[i], G);
     if (rc) return rc;
-    if (!tq::gemv2_supported(Ns[i], Ks[i], G)) return TQ_ERR_SHAPE;
+    if (!tq::gemv2_supported(Ns[i], Ks[i], G) && !tq::matmul2_supported(1, Ns[i], Ks[i], G))
+      return TQ_ERR_SHAPE;
     if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
     if (!aligned(xs[i], 16) || !aligned(packeds[i], 16) || !aligned(scales[i], 2) ||
         !aligned(ys[i], 4))
       return TQ_ERR_ALIGN;
   }
   (void)hipGetLastError();
-  tq::launch_gemv2_grouped(count, xs, packeds, scales, ys, Ns, Ks, G, d_status,
-                           (hipStream_t)stream);
+  // the shapes the table kernel takes share launches; longer rows run alone
+  // on the matrix-core kernel
+  std::vector<const uint16_t *> gx, gs;
+  std::vector<const uint8_t *> gp;
+  std::vector<float *> gy;
+  std::vector<int64_t> gn, gk;
+  for (int i = 0; i < count; ++i) {
+    if (tq::gemv2_supported(Ns[i], Ks[i], G)) {
+      gx.push_back(xs[i]); gp.push_back(packeds[i]); gs.push_back(scales[i]);
+      gy.push_back(ys[i]); gn.push_back(Ns[i]); gk.push_back(Ks[i]);
+    } else {
+      tq::launch_matmul2_batched(1, &xs[i], &packeds[i], &scales[i], &ys[i], 1, Ns[i], Ks[i], G,
+                                 d_status, (hipStream_t)stream);
+    }
+  }
+  if (!gx.empty())
+    tq::launch_gemv2_grouped((int)gx.size(), gx.data(), gp.data(), gs.data(), gy.data(),
+                             gn.data(), gk.data(), G, d_status, (hipStream_t)stream);
   return finish_launch();
 }
 
 int tq_gemv2(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t N,
              int64_t K, int G, float *y, int32_t *d_status, void *stream) {
   return tq_gemv2_batched(1, &x, &packed, &scales, &y, N, K, G, d_status, stream);
+}
+
+int tq_gemm2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                     const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                     int64_t K, int G, int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !ys) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (M < 1 || !tq::matmul2_supported(M, N, K, G)) return TQ_ERR_SHAPE;
+  const bool table = M == 1 && tq::gemv2_supported(N, K, G);
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
+    if (!aligned(xs[i], 16) || !aligned(packeds[i], table ? 16 : 2) || !aligned(scales[i], 2) ||
+        !aligned(ys[i], 4))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  if (table)
+    tq::launch_gemv2_batched(count, xs, packeds, scales, ys, N, K, G, d_status,
+                             (hipStream_t)stream);
+  else
+    tq::launch_matmul2_batched(count, xs, packeds, scales, ys, M, N, K, G, d_status,
+                               (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_gemm2(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
+             int64_t N, int64_t K, int G, float *y, int32_t *d_status, void *stream) {
+  return tq_gemm2_batched(1, &x, &packed, &scales, &y, M, N, K, G, d_status, stream);
 }
 
 int tq_w4a16_gemv_batched(int count, const uint16_t *const *xs, const uint32_t *const *packeds,

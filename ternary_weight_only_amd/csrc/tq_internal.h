@@ -37,6 +37,11 @@ void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64
 void launch_unpack2(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
                     int32_t *d_status, hipStream_t stream);
 bool gemv2_supported(int64_t N, int64_t K, int G);
+// 2-bit matmul on the matrix cores, any M and K (tq_twobit_mm.hip)
+bool matmul2_supported(int64_t M, int64_t N, int64_t K, int G);
+void launch_matmul2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                            const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                            int64_t K, int G, int32_t *d_status, hipStream_t stream);
 void launch_gemv2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                           const uint16_t *const *scales, float *const *ys, int64_t N, int64_t K,
                           int G, int32_t *d_status, hipStream_t stream);

@@ -1,0 +1,227 @@
+// tq_twobit_mm.hip -- matmul over the 2-bit ternary format for any number of
+// activation rows and any row length, on the matrix cores (gfx950):
+//   y[m,n] = sum_g s[n,g] * sum_{j<G} x[m, gG+j] * c[n, gG+j]
+// (tiny-llm "Week 2 Day 3: Quantize the Model", "Mathematical Formulation":
+// the group scale multiplies the group's inner sum, fp32 accumulation).
+// Format (Avenue README, size note: 2-bit packing; "Autoregressive Language
+// Model on the 6502 Processor": ternary parameters four a byte): field
+// f = c + 1 in two bits, the first weight lowest, G/4 bytes a group, fp16
+// group scales; f = 3 is invalid, counts as code 0 and sets the status bit.
+//
+// Block: 4 waves; wave w computes a BM x 32 tile of y (columns n0 + 32w ..
+// n0 + 32w + 31) with v_mfma_f32_16x16x32_bf16 (BM = 16, 32 or 64 rows by
+// M).  Per 32-wide k step, lane (j, q) of a wave:
+//   * loads the two bytes of codes k + 8q .. k + 8q + 7 of W row
+//     n0 + 32w + 16t + j (t = 0, 1) and looks each byte up in an LDS table
+//     of its four codes as bf16 (exact), giving the B fragment;
+//   * loads eight activations x[m][k + 8q ..] of row m0 + 16a + j (the A
+//     fragment; rows past M read as zero);
+//   * tests the two bytes for a field of 3 with one bitwise expression.
+// At a group's end the fp32 partial tile is scaled by the group's fp16 scale
+// and added to the accumulator.  A launch takes up to 64 same-shaped
+// problems, one per grid z index.
+#include <hip/hip_fp16.h>
+#include <hip/hip_runtime.h>
+#include <stdint.h>
+
+#include "tq_internal.h"
+
+namespace tq {
+namespace {
+
+typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
+typedef float f32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
+typedef __attribute__((address_space(3))) const u32x2 lds_u32x2_c;
+typedef __attribute__((address_space(3))) const unsigned char lds_bytes_c;
+
+constexpr int kThreads = 256;      // 4 waves
+constexpr int kTN = 2;             // 16-column MFMA tiles per wave
+constexpr int kBN = 4 * 16 * kTN;  // columns per block: 128
+constexpr int kCopies = 16;        // table copies; lane l reads copy l % 16
+constexpr int kMaxBatch = 64;      // problems per launch
+constexpr uint32_t kOutOfRange = 0x80000000u;
+
+struct Mm2Batch {
+  const uint16_t *x[kMaxBatch];
+  const uint8_t *packed[kMaxBatch];
+  const uint16_t *scales[kMaxBatch];
+  float *y[kMaxBatch];
+};
+
+__device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
+  return __builtin_amdgcn_make_buffer_rsrc(const_cast<void *>(p), (short)0, (int)bytes,
+                                           0x00020000);
+}
+
+// bf16 bits of field f's code c = f - 1 (f = 3, invalid: 0)
+__device__ __forceinline__ uint32_t code_bf16(uint32_t f) {
+  return f == 0u ? 0xBF80u : (f == 2u ? 0x3F80u : 0u);
+}
+
+template <int G, int TM>
+__global__ __launch_bounds__(kThreads) void matmul2_mfma_kernel(const Mm2Batch args, int M, int N,
+                                                                int K, int32_t *d_status) {
+  constexpr int BM = 16 * TM;
+  constexpr int KS = G / 32;  // k steps per group
+  // table: entry of byte b, copy c at byte (b * kCopies + c) * 8: codes of
+  // fields 0, 1 in the low dword, 2, 3 in the high dword
+  __shared__ __align__(16) u32x2 lut[256 * kCopies];
+  for (int i = threadIdx.x; i < 256 * kCopies; i += kThreads) {
+    const uint32_t b = (uint32_t)i / kCopies;
+    lut[i] = u32x2{code_bf16(b & 3u) | (code_bf16((b >> 2) & 3u) << 16),
+                   code_bf16((b >> 4) & 3u) | (code_bf16((b >> 6) & 3u) << 16)};
+  }
+  __syncthreads();
+
+  const int pi = (int)blockIdx.z;
+  const int lane = threadIdx.x & 63, wv = threadIdx.x >> 6;
+  const int j = lane & 15, q = lane >> 4;
+  const int n0 = blockIdx.x * kBN + wv * 16 * kTN;
+  const int m0 = blockIdx.y * BM;
+  const int nG = K / G;
+  const uint32_t rb = (uint32_t)K / 4u;  // packed bytes a row
+  const uint32_t copyoff = (uint32_t)(lane & (kCopies - 1)) * 8u;
+  lds_bytes_c *lut_b = (lds_bytes_c *)lut;
+
+  // rows past M or N lie past the buffers' ranges and read as zero
+  const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[pi], (uint32_t)M * (uint32_t)K * 2u);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[pi], (uint32_t)N * rb);
+  const __amdgpu_buffer_rsrc_t rs = make_rsrc(args.scales[pi], (uint32_t)N * (uint32_t)nG * 2u);
+
+  uint32_t xoff[TM], poff[kTN], soff[kTN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a) {
+    const int m = m0 + 16 * a + j;
+    xoff[a] = m < M ? ((uint32_t)m * (uint32_t)K + 8u * (uint32_t)q) * 2u : kOutOfRange;
+  }
+#pragma unroll
+  for (int t = 0; t < kTN; ++t) {
+    const int n = n0 + 16 * t + j;
+    poff[t] = n < N ? (uint32_t)n * rb + 2u * (uint32_t)q : kOutOfRange;
+    soff[t] = n < N ? (uint32_t)n * (uint32_t)nG * 2u : kOutOfRange;
+  }
+
+  f32x4 acc[TM][kTN];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int t = 0; t < kTN; ++t) acc[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+  uint32_t bad = 0;
+
+  for (int g = 0; g < nG; ++g) {
+    uint32_t wd[KS][kTN];
+    u32x4 xa[KS][TM];
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      const uint32_t kk = (uint32_t)(g * G + 32 * s);
+#pragma unroll
+      for (int t = 0; t < kTN; ++t)
+        wd[s][t] = __builtin_amdgcn_raw_buffer_load_b16(
+            rp, poff[t] == kOutOfRange ? kOutOfRange : poff[t] + kk / 4u, 0, 0);
+#pragma unroll
+      for (int a = 0; a < TM; ++a)
+        xa[s][a] = __builtin_amdgcn_raw_buffer_load_b128(
+            rx, xoff[a] == kOutOfRange ? kOutOfRange : xoff[a] + kk * 2u, 0, 0);
+    }
+    float sc[kTN];
+#pragma unroll
+    for (int t = 0; t < kTN; ++t) {
+      const uint32_t o = soff[t] == kOutOfRange ? kOutOfRange : soff[t] + 2u * (uint32_t)g;
+      sc[t] = __half2float(
+          __ushort_as_half((unsigned short)__builtin_amdgcn_raw_buffer_load_b16(rs, o, 0, 0)));
+    }
+    f32x4 part[TM][kTN];
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int t = 0; t < kTN; ++t) part[a][t] = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+    for (int s = 0; s < KS; ++s) {
+      bf16x8 bq[kTN];
+#pragma unroll
+      for (int t = 0; t < kTN; ++t) {
+        const uint32_t w = wd[s][t] & 0xFFFFu;
+        bad |= w & (w >> 1) & 0x5555u;  // a field of 3
+        const u32x2 e0 = *(lds_u32x2_c *)(lut_b + (((w & 0xFFu) * kCopies) * 8u + copyoff));
+        const u32x2 e1 = *(lds_u32x2_c *)(lut_b + (((w >> 8) * kCopies) * 8u + copyoff));
+        bq[t] = __builtin_bit_cast(bf16x8, u32x4{e0.x, e0.y, e1.x, e1.y});
+      }
+#pragma unroll
+      for (int a = 0; a < TM; ++a) {
+        const bf16x8 av = __builtin_bit_cast(bf16x8, xa[s][a]);
+#pragma unroll
+        for (int t = 0; t < kTN; ++t)
+          part[a][t] = __builtin_amdgcn_mfma_f32_16x16x32_bf16(av, bq[t], part[a][t], 0, 0, 0);
+      }
+    }
+#pragma unroll
+    for (int a = 0; a < TM; ++a)
+#pragma unroll
+      for (int t = 0; t < kTN; ++t)
+#pragma unroll
+        for (int r = 0; r < 4; ++r) acc[a][t][r] = fmaf(sc[t], part[a][t][r], acc[a][t][r]);
+  }
+
+  // lane (j, q) holds rows 4q .. 4q+3 of column j of each 16 x 16 tile
+  float *__restrict__ y = args.y[pi];
+#pragma unroll
+  for (int a = 0; a < TM; ++a)
+#pragma unroll
+    for (int t = 0; t < kTN; ++t) {
+      const int n = n0 + 16 * t + j;
+      if (n >= N) continue;
+#pragma unroll
+      for (int r = 0; r < 4; ++r) {
+        const int m = m0 + 16 * a + 4 * q + r;
+        if (m < M) y[(int64_t)m * N + n] = acc[a][t][r];
+      }
+    }
+  if (d_status && __builtin_amdgcn_ballot_w64(bad != 0) != 0 && lane == 0)
+    atomicOr(d_status, kDevInvalidByte);
+}
+
+template <int G, int TM>
+void launch_tm(const Mm2Batch &args, int count, int64_t M, int64_t N, int64_t K,
+               int32_t *d_status, hipStream_t stream) {
+  const dim3 grid((unsigned)((N + kBN - 1) / kBN), (unsigned)((M + 16 * TM - 1) / (16 * TM)),
+                  (unsigned)count);
+  hipLaunchKernelGGL((matmul2_mfma_kernel<G, TM>), grid, dim3(kThreads), 0, stream, args,
+                     (int)M, (int)N, (int)K, d_status);
+}
+
+template <int G>
+void launch_g(const Mm2Batch &args, int count, int64_t M, int64_t N, int64_t K,
+              int32_t *d_status, hipStream_t stream) {
+  if (M <= 16) launch_tm<G, 1>(args, count, M, N, K, d_status, stream);
+  else if (M <= 32) launch_tm<G, 2>(args, count, M, N, K, d_status, stream);
+  else launch_tm<G, 4>(args, count, M, N, K, d_status, stream);
+}
+
+}  // namespace
+
+bool matmul2_supported(int64_t M, int64_t N, int64_t K, int G) {
+  // 32-bit buffer offsets: x is M*K*2 bytes, the codes N*K/4, scales N*(K/G)*2
+  return (G == 64 || G == 128) && M >= 1 && N >= 1 && K >= G && K % G == 0 &&
+         M * K * 2 < (int64_t(1) << 31) && N * (K / 4) < (int64_t(1) << 31) &&
+         N * (K / G) * 2 < (int64_t(1) << 31) && (N + kBN) < (int64_t(1) << 30) &&
+         M <= int64_t(65535) * 64;  // grid.y <= 65535
+}
+
+void launch_matmul2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                            const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                            int64_t K, int G, int32_t *d_status, hipStream_t stream) {
+  for (int i0 = 0; i0 < count; i0 += kMaxBatch) {
+    const int n = count - i0 < kMaxBatch ? count - i0 : kMaxBatch;
+    Mm2Batch args = {};
+    for (int i = 0; i < n; ++i) {
+      args.x[i] = xs[i0 + i]; args.packed[i] = packeds[i0 + i]; args.scales[i] = scales[i0 + i];
+      args.y[i] = ys[i0 + i];
+    }
+    if (G == 64) launch_g<64>(args, n, M, N, K, d_status, stream);
+    else launch_g<128>(args, n, M, N, K, d_status, stream);
+  }
+}
+
+}  // namespace tq

@@ -284,7 +284,7 @@ def test_two_bit_argument_errors():
     assert u(FAKE + 2, 4, 128, 64, FAKE, None, None) == -4
     assert u(FAKE, 4, 128, 64, FAKE + 8, None, None) == -4
     assert g(None, FAKE, FAKE, 4, 128, 64, FAKE, None, None) == -1
-    assert g(FAKE, FAKE, FAKE, 4, 8192, 64, FAKE, None, None) == -2   # K/64 > 64
+    assert g(FAKE, FAKE, FAKE, 1 << 20, 8192, 64, FAKE, None, None) == -2   # N*K/4 >= 2^31
     assert g(FAKE, FAKE, FAKE, 4, 128, 96, FAKE, None, None) == -3
     assert g(FAKE, FAKE + 4, FAKE, 4, 128, 64, FAKE, None, None) == -4
     assert g(FAKE + 8, FAKE, FAKE, 4, 128, 64, FAKE, None, None) == -4
@@ -312,7 +312,7 @@ def test_two_bit_argument_errors():
     assert gr(0, None, None, None, None, None, None, 64, None, None) == 0
     assert gr(-1, good, good, good, good, ns, ks, 64, None, None) == -2
     assert gr(2, good, good, good, good, None, ks, 64, None, None) == -1
-    assert gr(2, good, good, good, good, ns, i64s(128, 8192), 64, None, None) == -2
+    assert gr(2, good, good, good, good, i64s(4, 1 << 20), i64s(128, 8192), 64, None, None) == -2
     assert gr(2, good, good, good, good, ns, i64s(128, 200), 64, None, None) == -2
     assert gr(2, good, good, good, good, ns, ks, 96, None, None) == -3
     assert gr(2, good, arr(FAKE, FAKE + 8), good, good, ns, ks, 64, None, None) == -4
@@ -385,6 +385,30 @@ def test_w4a16_gemm_batched_argument_errors():
     assert f(1, one, one, one, one, 2, 4, 128, 32, one, None) == -3        # G
     assert f(1, one, one, one, one, 2, 4, 128, 128, odd, None) == -4       # y alignment
     assert f(1, odd, one, one, one, 2, 4, 128, 128, one, None) == -4       # x alignment
+
+
+def test_gemm2_argument_errors():
+    lib = _lib()
+    f = lib.tq_gemm2
+    assert f(None, FAKE, FAKE, 2, 4, 128, 128, FAKE, None, None) == -1
+    assert f(FAKE, FAKE, FAKE, 2, 4, 128, 128, None, None, None) == -1
+    assert f(FAKE, FAKE, FAKE, 0, 4, 128, 128, FAKE, None, None) == -2     # M < 1
+    assert f(FAKE, FAKE, FAKE, 2, 0, 128, 128, FAKE, None, None) == -2     # N < 1
+    assert f(FAKE, FAKE, FAKE, 2, 4, 192, 128, FAKE, None, None) == -2     # K % G
+    assert f(FAKE, FAKE, FAKE, 2, 4, 128, 32, FAKE, None, None) == -3      # G
+    assert f(FAKE, FAKE, FAKE, 1 << 17, 4, 8192, 128, FAKE, None, None) == -2  # x >= 2^31 B
+    assert f(FAKE + 8, FAKE, FAKE, 2, 4, 128, 128, FAKE, None, None) == -4
+    assert f(FAKE, FAKE + 1, FAKE, 2, 4, 128, 128, FAKE, None, None) == -4
+    assert f(FAKE, FAKE, FAKE + 1, 2, 4, 128, 128, FAKE, None, None) == -4
+    assert f(FAKE, FAKE, FAKE, 2, 4, 128, 128, FAKE + 2, None, None) == -4
+    assert f(FAKE, FAKE, FAKE, 2, 4, 128, 128, FAKE, FAKE + 2, None) == -4  # status
+    g = lib.tq_gemm2_batched
+    P = ctypes.c_void_p
+    one = (P * 1)(FAKE)
+    assert g(0, None, None, None, None, 2, 4, 128, 128, None, None) == 0
+    assert g(-1, one, one, one, one, 2, 4, 128, 128, None, None) == -2
+    assert g(1, None, one, one, one, 2, 4, 128, 128, None, None) == -1
+    assert g(1, one, one, one, (P * 1)(None), 2, 4, 128, 128, None, None) == -1
 
 
 def test_product_path_does_not_import_oracle():
