@@ -67,6 +67,8 @@ def _load():
         lib.oracle_dequantize.restype = ctypes.c_int
         lib.oracle_fake_quantize.argtypes = [p, i64, i64, i64, p, p, p]
         lib.oracle_fake_quantize.restype = ctypes.c_int
+        lib.oracle_fake_quantize_f32.argtypes = [p, i64, i64, i64, p, p, p]
+        lib.oracle_fake_quantize_f32.restype = ctypes.c_int
         lib.oracle_quantize_pack2.argtypes = [p, i64, i64, i64, p, p, p]
         lib.oracle_quantize_pack2.restype = ctypes.c_int
         lib.oracle_unpack2.argtypes = [p, i64, i64, i64, p, p]
@@ -191,6 +193,27 @@ def fake_quantize(w_bits: np.ndarray, G: int):
     if rc:
         raise OracleError("oracle_fake_quantize rc=%d" % rc)
     return out, sc, int(st[0])
+
+
+def fake_quantize_f32(w: np.ndarray, G: int):
+    """QAT forward from fp32 latent weights: w_hat = c * s in fp32 (exact).
+
+    w: float32 [N,K] (or its uint32 bits).  Returns (w_hat float32 [N,K],
+    scales uint16 [N,K/G] fp16 bits, status bits int)."""
+    wb = np.ascontiguousarray(w).view(np.uint32) if np.asarray(w).dtype == np.float32 \
+        else np.ascontiguousarray(w, dtype=np.uint32)
+    if wb.ndim != 2:
+        raise OracleError("w must be 2-D")
+    N, K = wb.shape
+    if G < 1 or K % G:
+        raise OracleError("K % G != 0")
+    out = np.empty((N, K), np.uint32)
+    sc = np.empty((N, K // G), np.uint16)
+    st = np.zeros(1, np.int32)
+    rc = _load().oracle_fake_quantize_f32(_ptr(wb), N, K, G, _ptr(out), _ptr(sc), _ptr(st))
+    if rc:
+        raise OracleError("oracle_fake_quantize_f32 rc=%d" % rc)
+    return out.view(np.float32), sc, int(st[0])
 
 
 def quantize_pack2(w_bits: np.ndarray, G: int):

@@ -222,6 +222,26 @@ static void bf16_mag_parts(uint16_t u, uint64_t *sig, int *e)
  *              (k << 10) + Q (a carry to 2048 moves into the exponent).
  * Returns the status bits of the group (0 or OR_SCALE_OVERFLOW).
  */
+static int scale_bits_of_sum(const big_t *A, int64_t G, int sh, uint16_t *out_bits)
+{
+    if (big_is_zero(A)) { *out_bits = 0; return 0; }
+
+    uint64_t bits;
+    if (big_cmp_g_pow2(A, (uint64_t)G, sh + 10) < 0) {
+        bits = big_rne_div(A, (uint64_t)G, sh);            /* 0 .. 1024 */
+    } else {
+        int k = 0;
+        /* smallest k with V < 2^(11+k); past k = 29 the result overflows */
+        while (k < 40 && big_cmp_g_pow2(A, (uint64_t)G, sh + 11 + k) >= 0) ++k;
+        if (k >= 30) { *out_bits = 0x7C00; return OR_SCALE_OVERFLOW; }
+        uint64_t Q = big_rne_div(A, (uint64_t)G, sh + k);  /* 1024 .. 2048 */
+        bits = ((uint64_t)k << 10) + Q;
+    }
+    if (bits >= 0x7C00) { *out_bits = 0x7C00; return OR_SCALE_OVERFLOW; }
+    *out_bits = (uint16_t)bits;
+    return 0;
+}
+
 static int group_scale_bits(const uint16_t *w, int64_t G, uint16_t *out_bits)
 {
     big_t A;
@@ -231,22 +251,8 @@ static int group_scale_bits(const uint16_t *w, int64_t G, uint16_t *out_bits)
         bf16_mag_parts((uint16_t)(w[j] & 0x7FFF), &sig, &e);
         big_add_shifted(&A, sig, e);
     }
-    if (big_is_zero(&A)) { *out_bits = 0; return 0; }
-
-    uint64_t bits;
-    if (big_cmp_g_pow2(&A, (uint64_t)G, 109 + 10) < 0) {
-        bits = big_rne_div(&A, (uint64_t)G, 109);          /* 0 .. 1024 */
-    } else {
-        int k = 0;
-        /* smallest k with V < 2^(11+k); past k = 29 the result overflows */
-        while (k < 40 && big_cmp_g_pow2(&A, (uint64_t)G, 109 + 11 + k) >= 0) ++k;
-        if (k >= 30) { *out_bits = 0x7C00; return OR_SCALE_OVERFLOW; }
-        uint64_t Q = big_rne_div(&A, (uint64_t)G, 109 + k);  /* 1024 .. 2048 */
-        bits = ((uint64_t)k << 10) + Q;
-    }
-    if (bits >= 0x7C00) { *out_bits = 0x7C00; return OR_SCALE_OVERFLOW; }
-    *out_bits = (uint16_t)bits;
-    return 0;
+    /* A counts units of 2^-133; V = A / (G * 2^109) in units of 2^-24 */
+    return scale_bits_of_sum(&A, G, 109, out_bits);
 }
 
 /* ------------------------------------------------------------------------ */
@@ -478,6 +484,84 @@ int oracle_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int64_t G, uin
         }
     }
     free(code);
+    if (status) *status |= st;
+    return OR_OK;
+}
+
+/*
+ * The same forward from fp32 latent weights (Avenue README, introduction:
+ * BitNet-style training keeps latent full-precision weights).  Reading
+ * taken here: the scale is the exact mean of the fp32 magnitudes rounded
+ * once to fp16, the codes compare the fp32 weights with s/2 exactly (ties
+ * to 0), and the output is c * s in fp32, which is exact (no rounding).
+ * Flags as above; a flagged group gives w_hat = +0.
+ *
+ * fp32 magnitude bits u (sign cleared, finite) as sig * 2^(e - 149):
+ *   normal    (E = u>>23 in 1..254): value = (2^23 + m) * 2^(E - 150)
+ *   subnormal (E = 0):               value = m * 2^-149
+ * The exact sum of G magnitudes is below G * 2^277 units, so the 512-bit
+ * integer holds it for any G below 2^234.
+ */
+static void f32_mag_parts(uint32_t u, uint64_t *sig, int *e)
+{
+    int E = (int)((u >> 23) & 0xFF);
+    uint64_t m = u & 0x7FFFFFu;
+    if (E == 0) { *sig = m; *e = 0; }
+    else        { *sig = (1ull << 23) + m; *e = E - 1; }
+}
+
+static double f32_to_double(uint32_t b)
+{
+    uint64_t sig; int e;
+    f32_mag_parts(b & 0x7FFFFFFFu, &sig, &e);
+    double v = ldexp((double)sig, e - 149);
+    return (b & 0x80000000u) ? -v : v;
+}
+
+int oracle_fake_quantize_f32(const uint32_t *w, int64_t N, int64_t K, int64_t G,
+                             uint32_t *w_hat, uint16_t *scales, int32_t *status)
+{
+    if (!w || !w_hat) return OR_ERR_NULL;
+    int rc = check_shape(N, K, G);
+    if (rc) return rc;
+    const int64_t nG = K / G;
+    int32_t st = 0;
+    for (int64_t n = 0; n < N; ++n) {
+        for (int64_t g = 0; g < nG; ++g) {
+            const uint32_t *wg = w + n * K + g * G;
+            uint16_t sbits = 0;
+            int gst = 0;
+            for (int64_t j = 0; j < G; ++j)
+                if (((wg[j] >> 23) & 0xFF) == 0xFF) gst |= OR_NONFINITE;
+            if (gst) {
+                sbits = 0x7E00;
+            } else {
+                big_t A;
+                big_zero(&A);
+                for (int64_t j = 0; j < G; ++j) {
+                    uint64_t sig; int e;
+                    f32_mag_parts(wg[j] & 0x7FFFFFFFu, &sig, &e);
+                    big_add_shifted(&A, sig, e);
+                }
+                /* A counts units of 2^-149; V = A / (G * 2^125) in units of 2^-24 */
+                gst = scale_bits_of_sum(&A, G, 125, &sbits);
+            }
+            const double s = gst ? 0.0 : f16_to_double(sbits);
+            for (int64_t j = 0; j < G; ++j) {
+                float out = 0.0f;
+                if (!gst) {
+                    double v = f32_to_double(wg[j]);
+                    double c = v > 0.5 * s ? 1.0 : (v < -0.5 * s ? -1.0 : 0.0);
+                    out = (float)(c * s);  /* exact: s is an fp16 value */
+                }
+                uint32_t ob;
+                memcpy(&ob, &out, sizeof ob);
+                w_hat[n * K + g * G + j] = ob;
+            }
+            if (scales) scales[n * nG + g] = sbits;
+            st |= gst;
+        }
+    }
     if (status) *status |= st;
     return OR_OK;
 }

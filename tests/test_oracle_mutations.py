@@ -14,6 +14,7 @@ import tempfile
 import pytest
 
 import oracle
+from tests import test_oracle_fake_quantize_f32 as fq32
 from tests import test_oracle_format as fmt
 from tests import test_oracle_matmul as mm
 from tests import test_oracle_scale as sc
@@ -51,6 +52,14 @@ MUTATIONS = {
     "w4_bound_without_bias": ("bacc += fabs(a) * (fabs(q * s) + fabs(b));",
                               "bacc += fabs(a) * fabs(q * s);"),
     "w4_activation_off_by_one_word": ("x[m * K + g * G + 8 * p + i]", "x[m * K + g * G + 8 * (p ^ 1) + i]"),
+    "f32_sum_in_bf16_units": ("gst = scale_bits_of_sum(&A, G, 125, &sbits);",
+                              "gst = scale_bits_of_sum(&A, G, 109, &sbits);"),
+    "f32_mantissa_cut_to_bf16": ("    uint64_t m = u & 0x7FFFFFu;",
+                                 "    uint64_t m = u & 0x7F0000u;"),
+    "f32_code_tie_to_one": ("double c = v > 0.5 * s ? 1.0 : (v < -0.5 * s ? -1.0 : 0.0);",
+                            "double c = v >= 0.5 * s ? 1.0 : (v <= -0.5 * s ? -1.0 : 0.0);"),
+    "f32_flagged_group_keeps_codes": ("                if (!gst) {\n                    double v = f32_to_double(wg[j]);",
+                                      "                if (1) {\n                    double v = f32_to_double(wg[j]);"),
 }
 
 PINS = [
@@ -73,11 +82,17 @@ PINS = [
     lambda: w4.test_orientation_example(GOLDEN),
     lambda: w4.test_matmul_vs_factored_form(17, 1024, 128, 2),
     w4.test_nonnegative_terms_bound_equals_y,
+    lambda: fq32.test_normal_groups_match_exact_definition(64),
+    lambda: fq32.test_wide_exponents_match_exact_definition(64),
+    fq32.test_scale_uses_the_fp32_values,
+    fq32.test_code_ties_at_fp32_resolution,
+    fq32.test_flags_and_underflow,
 ]
 
 
 FUNCTIONS = ("oracle_packed_row_bytes", "oracle_quantize_pack", "oracle_unpack", "oracle_matmul",
-             "oracle_dequantize", "oracle_fake_quantize", "oracle_quantize_pack2",
+             "oracle_dequantize", "oracle_fake_quantize", "oracle_fake_quantize_f32",
+             "oracle_quantize_pack2",
              "oracle_unpack2", "oracle_matmul2", "oracle_w4_unpack", "oracle_w4a16_dequantize",
              "oracle_w4a16_matmul", "oracle_quantize_pack_mt", "oracle_matmul_mt",
              "oracle_matmul2_mt", "oracle_w4a16_matmul_mt")
