@@ -37,7 +37,8 @@ of launches between HIP events on the same stream, median of three):
   gemv2        the decode pass over the 2-bit format (one grouped launch)
   w4a16        the decode pass over seeded W4A16 parameters (one grouped launch), and
                the W4A16 prefill matmul at --prefill-m rows (one launch per shape)
-  qat          the QAT forward of the stack (two launches a pass)
+  qat          the QAT forward of the stack from bf16 and from fp32 latent
+               weights (two launches a pass each)
   ceilings     plain HBM read streams over the decode pass's bytes (eight
                57.8 MB buffers) and over 1 GiB, a bf16 MFMA-only loop, LDS
                table reads and VALU issue of v_dot2_f32_bf16 and v_perm_b32
@@ -669,6 +670,25 @@ class Bench:
                                     "bytes_per_pass": b, "launches": len(self.groups),
                                     "in_step": False}
         del w_hat
+        # the same forward from fp32 latent weights (the bf16 weights widened)
+        w32 = [w.float() for w in self.w_dev]
+        h32 = [torch.empty_like(w) for w in w32]
+        calls32 = [(N, K, len(idx), self.ptrs([w32[i] for i in idx]),
+                    self.ptrs([h32[i] for i in idx])) for (N, K), idx in self.groups.items()]
+
+        def run32(_):
+            for N, K, n, aw, awh in calls32:
+                self.ok(L.tq_fake_quantize_f32_batched(n, aw, N, K, G, awh, None, self.stp,
+                                                       self.sp))
+
+        ms = self.chain(run32, 4)
+        self.captured["qat32_w_hat"] = {i: h32[i].cpu().numpy() for i in (0, 71)}
+        b = 8 * self.weights
+        self.rows["qat_forward_f32"] = {"ms": ms, "GB/s": b / (ms * 1e-3) / 1e9,
+                                        "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
+                                        "bytes_per_pass": b, "launches": len(self.groups),
+                                        "in_step": False}
+        del w32, h32
 
     # ---- ceilings ----
     def row_ceilings(self):
@@ -906,6 +926,12 @@ def cpu_baseline(b, min_s):
         for i in (0, 71):
             f, _, _ = oracle.fake_quantize(mats[i], G)
             exact(cap["qat_w_hat"][i].view(np.uint16), f, "QAT forward, matrix %d" % i)
+    if "qat32_w_hat" in cap:
+        for i in (0, 71):
+            w32 = inputs.bf16_bits_to_f32(mats[i]).astype(np.float32)
+            f, _, _ = oracle.fake_quantize_f32(w32, G)
+            exact(cap["qat32_w_hat"][i].view(np.uint32), f.view(np.uint32),
+                  "QAT forward from fp32, matrix %d" % i)
 
     return {"value": gemv_nt, "unit": "GB/s", "cores": nt, "kind": "oracle",
             "sample": "fp64 GEMV passes (M=1) through the 72-matrix FFN stack (G=%d) on %d "

@@ -155,6 +155,33 @@ int tq_fake_quantize_batched(int count, const uint16_t *const *ws, int64_t N, in
                              int32_t *d_status, void *stream);
 
 /*
+ * QAT forward from fp32 latent weights (Avenue README, introduction: BitNet-
+ * style training keeps full-precision latent weights and ternarizes them in
+ * the forward pass; scale and code rule of the precisit "pack-unpack-run"
+ * README applied to the fp32 values):
+ *   w_hat[n,k] = c[n,k] * s[n,k/G]   in fp32, exact (s is an fp16 value)
+ * s = RNE_fp16(exact mean of |w| over the group), c = sign(w) if |w| > s/2
+ * else 0.  Code 0 gives +0; code -1 with s = +0 gives -0.
+ *   w        [N,K] fp32, 16-byte aligned
+ *   w_hat    [N,K] fp32, 16-byte aligned, overwritten (may not alias w)
+ *   scales   [N, K/G] fp16, 2-byte aligned, or NULL (not written)
+ * A group with an Inf/NaN weight (TQ_DEV_NONFINITE, scale 0x7E00) or a mean
+ * that rounds to >= 65520 (TQ_DEV_SCALE_OVERFLOW, scale 0x7C00) gets
+ * w_hat = +0.  Bit-exact and deterministic.
+ */
+int tq_fake_quantize_f32(const float *w, int64_t N, int64_t K, int G, float *w_hat,
+                         uint16_t *scales, int32_t *d_status, void *stream);
+
+/* Batched form: `count` same-shaped matrices, each as tq_fake_quantize_f32
+ * on ws[i], w_hats[i], scales ? scales[i] : NULL (HOST arrays of DEVICE
+ * pointers, read during the call only), one launch per 64.  Errors as
+ * tq_fake_quantize_f32; a NULL or misaligned pointer in any entry rejects the
+ * whole call with nothing enqueued. */
+int tq_fake_quantize_f32_batched(int count, const float *const *ws, int64_t N, int64_t K, int G,
+                                 float *const *w_hats, uint16_t *const *scales,
+                                 int32_t *d_status, void *stream);
+
+/*
  * Decode packed bytes to codes and validate them.
  * Source: precisit "pack-unpack-run" README, codec.py description
  * (decoding; values 243..255 invalid; zero-trit padding).

@@ -6,6 +6,7 @@ package only marshals torch tensors to that ABI:
 
     packed, scales = quantize_pack(w_bf16, G)      # scale, codes, base-3 bytes
     w_hat          = fake_quantize(w_bf16, G)      # QAT forward, bf16 c * s
+    w_hat          = fake_quantize_f32(w_f32, G)   # the same from fp32 latent weights
     w_hat          = FakeQuantize.apply(w, G)      # same, straight-through gradient
     codes          = unpack(packed, N, K, G)       # codes + validation
     (the *_batched forms take lists of same-shaped matrices, one launch per 64)
@@ -39,6 +40,8 @@ from .binding import (  # noqa: F401
     dequantize_batched,
     fake_quantize,
     fake_quantize_batched,
+    fake_quantize_f32,
+    fake_quantize_f32_batched,
     gemm,
     gemm_batched,
     gemv,

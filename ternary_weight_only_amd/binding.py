@@ -22,7 +22,8 @@ DEV_BAD_PADDING = 8
 
 # Every symbol include/tq.h declares.
 SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_quantize_pack",
-           "tq_quantize_pack_batched", "tq_fake_quantize", "tq_fake_quantize_batched", "tq_unpack",
+           "tq_quantize_pack_batched", "tq_fake_quantize", "tq_fake_quantize_batched",
+           "tq_fake_quantize_f32", "tq_fake_quantize_f32_batched", "tq_unpack",
            "tq_unpack_batched", "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2",
            "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
            "tq_gemv2_grouped", "tq_gemm2", "tq_gemm2_batched", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
@@ -64,6 +65,10 @@ def lib() -> ctypes.CDLL:
         l.tq_quantize_pack.restype = i32
         l.tq_fake_quantize.argtypes = [p, i64, i64, i32, p, p, p, p]
         l.tq_fake_quantize.restype = i32
+        l.tq_fake_quantize_f32.argtypes = [p, i64, i64, i32, p, p, p, p]
+        l.tq_fake_quantize_f32.restype = i32
+        l.tq_fake_quantize_f32_batched.argtypes = [i32, p, i64, i64, i32, p, p, p, p]
+        l.tq_fake_quantize_f32_batched.restype = i32
         for f in (l.tq_quantize_pack_batched, l.tq_fake_quantize_batched):
             f.argtypes = [i32, p, i64, i64, i32, p, p, p, p]
             f.restype = i32
@@ -270,6 +275,44 @@ def fake_quantize(w: torch.Tensor, G: int, status=None, out=None, scales_out=Non
     return w_hat
 
 
+def fake_quantize_f32(w: torch.Tensor, G: int, status=None, out=None, scales_out=None):
+    """QAT forward from fp32 latent weights: w [N,K] fp32 -> w_hat fp32 [N,K]
+    = c * s (exact).  scales_out as for fake_quantize."""
+    _dev(w, "w", F32, 2)
+    N, K = w.shape
+    w_hat = _out(out, "w_hat", (N, K), torch.float32, F32, w.device)
+    if w_hat.data_ptr() == w.data_ptr():
+        raise TQError("fake_quantize_f32: w_hat may not alias w")
+    sp = 0
+    if scales_out is not None:
+        if _groups(K, G) == 0:
+            raise TQError("fake_quantize_f32: K=%d is not a multiple of G=%d" % (K, G))
+        sp = _out(scales_out, "scales_out", (N, _groups(K, G)), torch.float16, F16,
+                  w.device).data_ptr()
+    _rc(lib().tq_fake_quantize_f32(w.data_ptr(), N, K, G, w_hat.data_ptr(), sp,
+                                   _st(status, w.device), _stream()), "tq_fake_quantize_f32")
+    return w_hat
+
+
+def fake_quantize_f32_batched(ws, G: int, status=None, outs=None):
+    """Same-shaped fp32 latent matrices -> list of w_hat fp32, one launch per 64."""
+    if not ws:
+        return []
+    for w in ws:
+        _dev(w, "w", F32, 2, ws[0].device)
+    shapes = {tuple(w.shape) for w in ws}
+    if len(shapes) > 1:
+        raise TQError("fake_quantize_f32_batched: matrices of different shapes %s"
+                      % sorted(shapes))
+    N, K = shapes.pop()
+    dev = ws[0].device
+    outs = _outs(outs, "outs", [(N, K)] * len(ws), torch.float32, F32, dev)
+    _rc(lib().tq_fake_quantize_f32_batched(len(ws), _ptrs(ws), N, K, G, _ptrs(outs), None,
+                                           _st(status, dev), _stream()),
+        "tq_fake_quantize_f32_batched")
+    return outs
+
+
 def _same_shape(ws, name):
     for w in ws:
         _dev(w, name, BF16, 2, ws[0].device)
@@ -368,13 +411,14 @@ def dequantize_batched(packeds, scales_list, N: int, K: int, G: int, status=None
 
 
 class FakeQuantize(torch.autograd.Function):
-    """w_hat = fake_quantize(w, G) in the forward pass; the backward pass is
-    straight-through: the gradient of w_hat is returned as the gradient of w
-    unchanged (no kernel runs)."""
+    """w_hat = fake_quantize(w, G) (bf16 latent weights) or
+    fake_quantize_f32(w, G) (fp32 latent weights) in the forward pass; the
+    backward pass is straight-through: the gradient of w_hat is returned as
+    the gradient of w unchanged (no kernel runs)."""
 
     @staticmethod
     def forward(ctx, w, G):
-        return fake_quantize(w, G)
+        return fake_quantize_f32(w, G) if w.dtype == torch.float32 else fake_quantize(w, G)
 
     @staticmethod
     def backward(ctx, grad):

@@ -82,6 +82,34 @@ int tq_fake_quantize(const uint16_t *w, int64_t N, int64_t K, int G, uint16_t *w
   return finish_launch();
 }
 
+int tq_fake_quantize_f32_batched(int count, const float *const *ws, int64_t N, int64_t K, int G,
+                                 float *const *w_hats, uint16_t *const *scales,
+                                 int32_t *d_status, void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!ws || !w_hats) return TQ_ERR_NULL;
+  const int rc = check_nkg(N, K, G);
+  if (rc) return rc;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!ws[i] || !w_hats[i]) return TQ_ERR_NULL;
+    if (!aligned(ws[i], 16) || !aligned(w_hats[i], 16)) return TQ_ERR_ALIGN;
+    if (scales && !aligned(scales[i], 2)) return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_fake_quantize_f32_batched(count, ws, N, K, G, w_hats, scales, d_status,
+                                       (hipStream_t)stream);
+  return finish_launch();
+}
+
+int tq_fake_quantize_f32(const float *w, int64_t N, int64_t K, int G, float *w_hat,
+                         uint16_t *scales, int32_t *d_status, void *stream) {
+  if (!w || !w_hat) return TQ_ERR_NULL;
+  uint16_t *const sc[1] = {scales};
+  return tq_fake_quantize_f32_batched(1, &w, N, K, G, &w_hat, scales ? sc : nullptr, d_status,
+                                      stream);
+}
+
 int tq_quantize_pack_batched(int count, const uint16_t *const *ws, int64_t N, int64_t K, int G,
                              uint8_t *const *packeds, uint16_t *const *scales,
                              int32_t *d_status, void *stream) {

@@ -37,6 +37,10 @@ void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64
 void launch_unpack2(const uint8_t *packed, int64_t N, int64_t K, int G, int8_t *codes,
                     int32_t *d_status, hipStream_t stream);
 bool gemv2_supported(int64_t N, int64_t K, int G);
+// QAT forward from fp32 latent weights (tq_fake32.hip)
+void launch_fake_quantize_f32_batched(int count, const float *const *ws, int64_t N, int64_t K,
+                                      int G, float *const *w_hats, uint16_t *const *scales,
+                                      int32_t *d_status, hipStream_t stream);
 // 2-bit matmul on the matrix cores, any M and K (tq_twobit_mm.hip)
 bool matmul2_supported(int64_t M, int64_t N, int64_t K, int G);
 void launch_matmul2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,

@@ -411,6 +411,26 @@ def test_gemm2_argument_errors():
     assert g(1, one, one, one, (P * 1)(None), 2, 4, 128, 128, None, None) == -1
 
 
+def test_fake_quantize_f32_argument_errors():
+    lib = _lib()
+    f = lib.tq_fake_quantize_f32
+    assert f(None, 4, 128, 64, FAKE, None, None, None) == -1
+    assert f(FAKE, 4, 128, 64, None, None, None, None) == -1
+    assert f(FAKE, 0, 128, 64, FAKE, None, None, None) == -2
+    assert f(FAKE, 4, 100, 64, FAKE, None, None, None) == -2
+    assert f(FAKE, 4, 128, 32, FAKE, None, None, None) == -3
+    assert f(FAKE + 8, 4, 128, 64, FAKE, None, None, None) == -4
+    assert f(FAKE, 4, 128, 64, FAKE + 8, None, None, None) == -4
+    assert f(FAKE, 4, 128, 64, FAKE, FAKE + 1, None, None) == -4
+    assert f(FAKE, 4, 128, 64, FAKE, None, FAKE + 2, None) == -4
+    g = lib.tq_fake_quantize_f32_batched
+    P = ctypes.c_void_p
+    one = (P * 1)(FAKE)
+    assert g(0, None, 4, 128, 64, None, None, None, None) == 0
+    assert g(-1, one, 4, 128, 64, one, None, None, None) == -2
+    assert g(1, one, 4, 128, 64, (P * 1)(None), None, None, None) == -1
+
+
 def test_product_path_does_not_import_oracle():
     pkg = os.path.join(ROOT, "ternary_weight_only_amd")
     for dirpath, _, files in os.walk(pkg):
