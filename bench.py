@@ -9,8 +9,8 @@ W[1024,3584]; 72 matrices, 264,241,152 bf16 weights ~ N(0, 0.02)), G = 128.
 One step is one pass of every step of the hot path over that stack:
   decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
       one launch for the 48 K=1024 and the 24 K=3584 matrices together)
-  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_batched:
-      two launches, one per shape; each matrix has its own output)
+  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_grouped:
+      one persistent launch over both shapes; each matrix has its own output)
   quantize + pack all 72 bf16 matrices                 (tq_quantize_pack_batched:
       two launches, one per shape)
   unpack + validate all 72 packed matrices             (tq_unpack_batched: two)
@@ -29,8 +29,8 @@ is the median of three such chains / 8.
 Rows outside the step (each selectable with --rows; every one times chains
 of launches between HIP events on the same stream, median of three):
   gemv_g64     the decode pass of the stack at G = 64 (its own 8-slot ring)
-  gemm_m2048   the prefill GEMM of the stack at M = 2048 (each shape's
-               launch timed on its own)
+  gemm_m2048   the prefill GEMM of the stack at M = 2048 (the grouped
+               launch; each shape's batched launch also timed on its own)
   dense8b      8B-class FFN matrices W[14336,4096] and W[4096,14336], G = 128,
                decode at M = 1, 4, 16 over a ring of copies (>= 1 GiB)
   dequant      decode to bf16 of every matrix of a slot (two launches per slot)
@@ -329,10 +329,8 @@ class Bench:
         ptrs = self.ptrs
         grouped = {slot: (ptrs(self.x_dec), ptrs(P[slot]), ptrs(S[slot]), ptrs(y_dec))
                    for slot in range(RING)}
-        gcalls = {slot: [(N, K, len(idx), ptrs([x_pre[K]] * len(idx)),
-                          ptrs([P[slot][i] for i in idx]), ptrs([S[slot][i] for i in idx]),
-                          ptrs([y_pre[i] for i in idx]))
-                         for (N, K), idx in self.groups.items()] for slot in range(RING)}
+        gcalls = {slot: (ptrs([x_pre[K] for N, K in self.shapes]), ptrs(P[slot]), ptrs(S[slot]),
+                         ptrs(y_pre)) for slot in range(RING)}
         qcalls = {slot: [(N, K, len(idx), ptrs([self.w_dev[i] for i in idx]),
                           ptrs([P[slot][i] for i in idx]), ptrs([S[slot][i] for i in idx]),
                           ptrs([codes[i] for i in idx]))
@@ -345,8 +343,9 @@ class Bench:
                                       G, stp, sp))
 
         def run_gemm(slot):
-            for N, K, n, ax, ap, asc, ay in gcalls[slot]:
-                self.ok(L.tq_gemm_batched(n, ax, ap, asc, ay, MP, N, K, G, stp, sp))
+            ax, ap, asc, ay = gcalls[slot]
+            self.ok(L.tq_gemm_grouped(len(self.shapes), ax, ap, asc, ay, MP, self.g_ns,
+                                      self.g_ks, G, stp, sp))
 
         def run_quant(slot):
             for N, K, n, aw, ap, asc, _ in qcalls[slot]:
@@ -411,7 +410,7 @@ class Bench:
             "kernel_frac_hbm": pb / (launch_ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "launches": 1, "bytes_per_step": pb}
         self.rows["prefill_gemm"] = {
-            "config": "72-matrix FFN stack, G=%d, M=%d, two batched launches" % (G, MP),
+            "config": "72-matrix FFN stack, G=%d, M=%d, one grouped launch" % (G, MP),
             "ms": per["gemm"], "TFLOP/s": gemm_tf, "frac_mfma": gemm_tf / MFMA_BF16_PEAK_TFLOPS,
             "M": MP, "flop_per_step": gemm_flops}
         self.rows["quantize_pack"] = {
@@ -474,7 +473,7 @@ class Bench:
                           self.ptrs([S[i] for i in idx]), self.ptrs([y[i] for i in idx]))
                  for (N, K), idx in self.groups.items()}
         out = {}
-        total_ms = 0.0
+        batched_ms = 0.0
         for (N, K), (n, ax, ap, asc, ay) in calls.items():
             def run(_):
                 self.ok(L.tq_gemm_batched(n, ax, ap, asc, ay, M, N, K, G, self.stp, self.sp))
@@ -483,15 +482,23 @@ class Bench:
             tf = flops / (ms * 1e-3) / 1e12
             out["%dx W[%d,%d]" % (n, N, K)] = {"ms": ms, "TFLOP/s": tf,
                                                "frac_mfma": tf / MFMA_BF16_PEAK_TFLOPS}
-            total_ms += ms
+            batched_ms += ms
+        g = (self.ptrs([x[K] for N, K in self.shapes]), self.ptrs(P), self.ptrs(S), self.ptrs(y))
+
+        def run_grouped(_):
+            self.ok(L.tq_gemm_grouped(len(self.shapes), *g, M, self.g_ns, self.g_ks, G,
+                                      self.stp, self.sp))
+        total_ms = self.chain(run_grouped, 2)
         flops = sum(2.0 * M * N * K for N, K in self.shapes)
         tf = flops / (total_ms * 1e-3) / 1e12
         self.captured["m2048_y"] = {i: y[i][:64].cpu().numpy() for i in (0, 2)}
         self.rows["prefill_gemm_m2048"] = {
-            "config": "72-matrix FFN stack, G=%d, M=2048, two batched launches" % G,
+            "config": "72-matrix FFN stack, G=%d, M=2048, one grouped launch" % G,
             "ms": total_ms, "TFLOP/s": tf, "frac_mfma": tf / MFMA_BF16_PEAK_TFLOPS,
-            "launches": out, "in_step": False,
-            "timing": "each launch: median of 3 chains of 2 launches"}
+            "batched_per_shape": out,
+            "batched_TFLOP/s": flops / (batched_ms * 1e-3) / 1e12, "in_step": False,
+            "timing": "median of 3 chains of 2 launches (the grouped launch, and each "
+                      "shape's batched launch)"}
         del y
 
     # ---- the 8B-class FFN matrices ----

@@ -343,6 +343,30 @@ int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *
                     int32_t *d_status, void *stream);
 
 /*
+ * Grouped prefill matmul: `count` independent problems that share M but may
+ * differ in N and K, each as tq_gemm(xs[i], packeds[i], scales[i], M, Ns[i],
+ * Ks[i], G, ys[i]) -- e.g. every projection of a decoder's FFN stack over one
+ * prompt batch (gate/up [N=I, K=H] and down [N=H, K=I]).  Where the 256 x 128
+ * tile kernel takes every shape (G = 128, M >= 256) all problems share one
+ * persistent launch per 128 problems, longest K first, so that no shape's
+ * tail leaves the chip idle between launches; otherwise the problems run as
+ * one tq_gemm_batched call per distinct shape.  Same tiny-llm passages as
+ * tq_gemm.
+ *   xs, packeds, scales, ys   HOST arrays of `count` DEVICE pointers with the
+ *                             layouts and alignments of tq_gemm (problem i
+ *                             has shape Ns[i] x Ks[i]); read during the call
+ *   Ns, Ks                    HOST arrays of `count` sizes
+ *   count >= 0                (0 enqueues nothing)
+ * Accuracy as tq_gemm; the outputs must not overlap each other or any input.
+ * Errors and device status as tq_gemm; any invalid entry rejects the whole
+ * call with nothing enqueued.
+ */
+int tq_gemm_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys, int64_t M,
+                    const int64_t *Ns, const int64_t *Ks, int G,
+                    int32_t *d_status, void *stream);
+
+/*
  * The 2-bit ternary format: codes in two bits each, four a byte.
  * Source: Avenue README (size note: model sizes counted for 2-bit packing)
  * and "Autoregressive Language Model on the 6502 Processor" (ternary

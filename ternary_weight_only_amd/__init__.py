@@ -20,6 +20,7 @@ package only marshals torch tensors to that ABI:
     ys             = gemv_grouped(xs, packeds, scales, Ns, Ks, G)  # M = 1, mixed shapes
     y              = gemm(x_bf16, packed, scales, N, K, G)   # any M
     ys             = gemm_batched(xs, packeds, scales, N, K, G)  # many same-shaped
+    ys             = gemm_grouped(xs, packeds, scales, Ns, Ks, G)  # one M, mixed shapes
 
 `ternary_weight_only_amd.package` writes and reads the per-tensor package
 (codes + fp16 scales + sha256 hashes) and decodes it to bf16 on the device.
@@ -44,6 +45,7 @@ from .binding import (  # noqa: F401
     fake_quantize_f32_batched,
     gemm,
     gemm_batched,
+    gemm_grouped,
     gemv,
     gemv_batched,
     gemv_grouped,

@@ -27,7 +27,7 @@ SYMBOLS = ("tq_status_string", "tq_packed_row_bytes", "tq_packed_bytes", "tq_qua
            "tq_unpack_batched", "tq_dequantize", "tq_dequantize_batched", "tq_quantize_pack2",
            "tq_quantize_pack2_batched", "tq_unpack2", "tq_gemv2", "tq_gemv2_batched",
            "tq_gemv2_grouped", "tq_gemm2", "tq_gemm2_batched", "tq_w4a16_gemv", "tq_w4a16_gemv_batched", "tq_w4a16_gemv_grouped",
-           "tq_w4a16_gemm", "tq_w4a16_gemm_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched")
+           "tq_w4a16_gemm", "tq_w4a16_gemm_batched", "tq_gemv", "tq_gemv_batched", "tq_gemv_grouped", "tq_gemm", "tq_gemm_batched", "tq_gemm_grouped")
 # Every symbol include/tq_probe.h declares (measurement probes).
 PROBE_SYMBOLS = ("tq_probe_lds_table", "tq_probe_mfma_bf16", "tq_probe_read_stream",
                  "tq_probe_valu")
@@ -114,6 +114,8 @@ def lib() -> ctypes.CDLL:
             f.restype = i32
         l.tq_gemv_grouped.argtypes = [i32, p, p, p, p, p, p, i32, p, p]
         l.tq_gemv_grouped.restype = i32
+        l.tq_gemm_grouped.argtypes = [i32, p, p, p, p, i64, p, p, i32, p, p]
+        l.tq_gemm_grouped.restype = i32
         # measurement probes (include/tq_probe.h)
         l.tq_probe_read_stream.argtypes = [p, i64, i32, p, p]
         l.tq_probe_read_stream.restype = i32
@@ -504,6 +506,30 @@ def gemv_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=Non
     _rc(lib().tq_gemv_grouped(count, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(ys),
                               _i64s(Ns), _i64s(Ks), G, _st(status, dev), _stream()),
         "tq_gemv_grouped")
+    return ys
+
+
+def gemm_grouped(xs, packeds, scales_list, Ns, Ks, G: int, status=None, outs=None):
+    """[x_i] ([M,K_i] bf16, one M), [packed_i], [scales_i] of shapes (N_i, K_i) -> [y_i]
+    ([M,N_i] fp32): prefill matmuls of mixed shapes, one persistent launch where possible."""
+    count = len(xs)
+    if not (len(packeds) == len(scales_list) == len(Ns) == len(Ks) == count):
+        raise TQError("tq_gemm_grouped: lists of different lengths")
+    if count == 0:
+        return []
+    _dev(xs[0], "x", BF16, 2)
+    dev = xs[0].device
+    M = int(xs[0].shape[0])
+    for i in range(count):
+        N, K = int(Ns[i]), int(Ks[i])
+        _dev(xs[i], "x", BF16, 2, dev)
+        if tuple(xs[i].shape) != (M, K):
+            raise TQError("tq_gemm_grouped: x %d must be [%d,%d]" % (i, M, K))
+        _check_packed(packeds[i], scales_list[i], N, K, G, dev, "tq_gemm_grouped")
+    ys = _outs(outs, "outs", [(M, int(N)) for N in Ns], torch.float32, F32, dev)
+    _rc(lib().tq_gemm_grouped(count, _ptrs(xs), _ptrs(packeds), _ptrs(scales_list), _ptrs(ys),
+                              M, _i64s(Ns), _i64s(Ks), G, _st(status, dev), _stream()),
+        "tq_gemm_grouped")
     return ys
 
 

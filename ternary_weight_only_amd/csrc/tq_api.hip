@@ -586,4 +586,27 @@ int tq_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *const *
   return finish_launch();
 }
 
+int tq_gemm_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                    const uint16_t *const *scales, float *const *ys, int64_t M,
+                    const int64_t *Ns, const int64_t *Ks, int G, int32_t *d_status,
+                    void *stream) {
+  if (count < 0) return TQ_ERR_SHAPE;
+  if (count == 0) return TQ_OK;
+  if (!xs || !packeds || !scales || !ys || !Ns || !Ks) return TQ_ERR_NULL;
+  if (!aligned(d_status, 4)) return TQ_ERR_ALIGN;
+  for (int i = 0; i < count; ++i) {
+    if (!xs[i] || !packeds[i] || !scales[i] || !ys[i]) return TQ_ERR_NULL;
+    const int rc = check_nkg(Ns[i], Ks[i], G);
+    if (rc) return rc;
+    if (M < 1 || M > (int64_t(1) << 40) / Ks[i]) return TQ_ERR_SHAPE;
+    if (Ks[i] > (int64_t(1) << 22)) return TQ_ERR_SHAPE;
+    if (!aligned(xs[i], 16) || !aligned(scales[i], 2) || !aligned(ys[i], 4))
+      return TQ_ERR_ALIGN;
+  }
+  (void)hipGetLastError();
+  tq::launch_gemm_grouped(count, xs, packeds, scales, ys, M, Ns, Ks, G, d_status,
+                          (hipStream_t)stream);
+  return finish_launch();
+}
+
 }  // extern "C"

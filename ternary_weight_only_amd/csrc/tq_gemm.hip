@@ -35,6 +35,8 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <vector>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -411,7 +413,7 @@ constexpr int64_t kChunkRows = int64_t(1) << 18;  // per launch: <= 2^22 blocks
 void launch_gemm(const uint16_t *x, const uint8_t *packed, const uint16_t *scales, int64_t M,
                  int64_t N, int64_t K, int G, float *y, int32_t *d_status, hipStream_t stream) {
   if (gemm_wide_supported(1, M, N, K, G)) {
-    launch_gemm_wide(1, &x, &packed, &scales, &y, M, N, K, N, d_status, stream);
+    launch_gemm_wide(1, &x, &packed, &scales, &y, M, N, K, d_status, stream);
     return;
   }
   const int64_t rowbytes = (K / G) * bytes_per_group(G);
@@ -433,7 +435,7 @@ void launch_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *co
                          const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                          int64_t K, int G, int32_t *d_status, hipStream_t stream) {
   if (gemm_wide_supported(count, M, N, K, G)) {
-    launch_gemm_wide(count, xs, packeds, scales, ys, M, N, K, N, d_status, stream);
+    launch_gemm_wide(count, xs, packeds, scales, ys, M, N, K, d_status, stream);
     return;
   }
   // Same-shaped problems share a launch, kGemmMaxBatch at a time, while the
@@ -454,6 +456,34 @@ void launch_gemm_batched(int count, const uint16_t *const *xs, const uint8_t *co
       a.y[i] = ys[base + i];
     }
     launch_chunk(a, n, M, N, K, G, N, d_status, stream);
+  }
+}
+
+// Problems of mixed shapes (shared M): one persistent launch for all of them
+// when the 256 x 128 kernel takes every shape, else one batched launch per
+// distinct (N, K), in order of first appearance.
+void launch_gemm_grouped(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                         const uint16_t *const *scales, float *const *ys, int64_t M,
+                         const int64_t *Ns, const int64_t *Ks, int G, int32_t *d_status,
+                         hipStream_t stream) {
+  if (gemm_wide_grouped_supported(count, M, Ns, Ks, G)) {
+    launch_gemm_wide_grouped(count, xs, packeds, scales, ys, M, Ns, Ks, d_status, stream);
+    return;
+  }
+  std::vector<char> done(count, 0);
+  std::vector<const uint16_t *> gx, gs;
+  std::vector<const uint8_t *> gp;
+  std::vector<float *> gy;
+  for (int i = 0; i < count; ++i) {
+    if (done[i]) continue;
+    gx.clear(); gs.clear(); gp.clear(); gy.clear();
+    for (int j = i; j < count; ++j) {
+      if (done[j] || Ns[j] != Ns[i] || Ks[j] != Ks[i]) continue;
+      done[j] = 1;
+      gx.push_back(xs[j]); gp.push_back(packeds[j]); gs.push_back(scales[j]); gy.push_back(ys[j]);
+    }
+    launch_gemm_batched((int)gx.size(), gx.data(), gp.data(), gs.data(), gy.data(), M, Ns[i],
+                        Ks[i], G, d_status, stream);
   }
 }
 

@@ -30,6 +30,10 @@
 #include <hip/hip_runtime.h>
 #include <stdint.h>
 
+#include <algorithm>
+#include <vector>
+#include <climits>
+
 #include "tq_internal.h"
 
 namespace tq {
@@ -66,11 +70,22 @@ constexpr uint32_t kOutOfRange = 0x80000000u;
 constexpr uint32_t kBadFlag = 0xFF00u;  // in the high dword of entries 243..255
 constexpr int TM = 4, TN = 4;           // 16 x 16 tiles per wave: 64 x 64
 
-struct GemmBatch {
-  const uint16_t *x[kGemmMaxBatch];
-  const uint8_t *packed[kGemmMaxBatch];
-  const uint16_t *scales[kGemmMaxBatch];
-  float *y[kGemmMaxBatch];
+// Problems of one launch (M is shared): their pointers, ordered by shape,
+// and up to kWideMaxShapes shapes (N, K).  The problems of shape g are
+// first[g], first[g] + 1, ...; their tiles start at tile t0[g] of the launch
+// (t0 of an absent shape: INT_MAX) and follow one another problem by
+// problem.  The tile -> problem lookup is a fixed number of comparisons: a
+// loop there would put branches in every stage.
+constexpr int kWideMaxBatch = 128;
+constexpr int kWideMaxShapes = 4;
+struct WideBatch {
+  const uint16_t *x[kWideMaxBatch];
+  const uint8_t *packed[kWideMaxBatch];
+  const uint16_t *scales[kWideMaxBatch];
+  float *y[kWideMaxBatch];
+  int n[kWideMaxShapes], k[kWideMaxShapes], tpp[kWideMaxShapes], first[kWideMaxShapes];
+  int t0[kWideMaxShapes];
+  int total;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
@@ -130,26 +145,32 @@ struct Int {
 };
 
 // A tile of one problem: rows [m0, m0 + mrows) of x, rows [n0, n0 + nrows)
-// of W.  Tile j of a block is tile blockIdx.x + j * gridDim.x of the launch
-// (problem-major); past the launch's tiles it is empty (no rows: every load
-// of it reads zeros).
+// of W, and the problem's N and K.  Tile j of a block is tile blockIdx.x +
+// j * gridDim.x of the launch (problem-major); past the launch's tiles it is
+// empty (no rows: every load of it reads zeros; K = one group).
 struct Tile {
-  int pi, m0, n0, mrows, nrows;
+  int pi, m0, n0, mrows, nrows, N, K;
 };
 
-__device__ __forceinline__ Tile block_tile(int j, int M, int N, int tilesM, int tpp, int total) {
+__device__ __forceinline__ Tile block_tile(const WideBatch &a, int j, int M, int tilesM) {
   const int t = (int)blockIdx.x + j * (int)gridDim.x;
   Tile r;
-  if (t >= total) {
-    r.pi = 0; r.m0 = 0; r.n0 = 0; r.mrows = 0; r.nrows = 0;
+  if (t >= a.total) {
+    r.pi = 0; r.m0 = 0; r.n0 = 0; r.mrows = 0; r.nrows = 0; r.N = 0; r.K = G;
     return r;
   }
-  r.pi = t / tpp;
-  const int tt = t - r.pi * tpp;
+  static_assert(kWideMaxShapes == 4, "the shape lookup below compares against t0[1..3]");
+  const int g = (int)(t >= a.t0[1]) + (int)(t >= a.t0[2]) + (int)(t >= a.t0[3]);
+  const int tg = t - a.t0[g], tpp = a.tpp[g];
+  const int q = tg / tpp;
+  r.pi = a.first[g] + q;
+  r.N = a.n[g];
+  r.K = a.k[g];
+  const int tt = tg - q * tpp;
   r.m0 = (tt % tilesM) * BM;
   r.n0 = (tt / tilesM) * BN;
   r.mrows = min(BM, M - r.m0);
-  r.nrows = min(BN, N - r.n0);
+  r.nrows = min(BN, r.N - r.n0);
   return r;
 }
 
@@ -160,19 +181,24 @@ __device__ __forceinline__ Tile block_tile(int j, int M, int N, int tilesM, int 
 // stage count wraps, so a tile's first stages are loaded while the previous
 // tile computes, and the table is built once per block.
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
-void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, int total,
-                      int32_t *__restrict__ d_status) {
+// `args` is the first kernel argument only to lay the table out at the start of
+// the argument segment, where the body reads it.
+void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_status) {
+  (void)args;
   __shared__ __align__(16) unsigned char smem_raw[SMEM];
   lds_bytes *smem = (lds_bytes *)smem_raw;
 
   const int tid = threadIdx.x, lane = tid & (kWave - 1), wv = tid / kWave;
   const int wm = wv >> 1, wn = wv & 1;
-  const int tilesM = (M + BM - 1) / BM, tilesN = (N + BN - 1) / BN;
-  const int tpp = tilesM * tilesN;
-  const int nG = K / G, nS = K / KS;
-  const uint32_t rowbytes = (uint32_t)nG * B;
+  const int tilesM = (M + BM - 1) / BM;
+  // The problem table is read through the kernel-argument segment pointer:
+  // indexing the by-value struct with a computed shape index makes the
+  // compiler copy it to scratch memory.
+  const WideBatch &args_ = *reinterpret_cast<const WideBatch *>(
+      (const void *)__builtin_amdgcn_kernarg_segment_ptr());
+  const int total = args_.total;
   const int ntiles = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
-  auto tile = [&](int j) { return block_tile(j, M, N, tilesM, tpp, total); };
+  auto tile = [&](int j) { return block_tile(args_, j, M, tilesM); };
 
   // ---- decode table: two threads per entry, eight copies each, the copy
   // index rotated by the entry to spread the banks ----
@@ -195,14 +221,19 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
   // of a raw buffer address that is range-checked. ----
   // The row of op i is r0 + 64 i, with the same swizzled chunk for every i.
   const uint32_t xr0 = (uint32_t)tid >> 3;
-  const uint32_t xbase = (xr0 * (uint32_t)K + (((uint32_t)tid & 7u) ^ ((xr0 >> 1) & 7u)) * 8u) * 2u;
+  const uint32_t xchunk = (((uint32_t)tid & 7u) ^ ((xr0 >> 1) & 7u)) * 8u;
   int jx = 0, sx = 0, ux = 0;  // tile, its stage, ring slot of the next request
   int xrows = 0;               // rows of the stream's tile
+  uint32_t xK = 0, xbase = 0;  // its K, and this thread's offset in its first stage
+  int xnS = 1;                 // its stages
   __amdgpu_buffer_rsrc_t rx;
   auto set_x = [&](int j) {
     const Tile T = tile(j);
-    rx = make_rsrc(args.x[T.pi] + (int64_t)T.m0 * K, (uint32_t)T.mrows * (uint32_t)K * 2u);
+    rx = make_rsrc(args_.x[T.pi] + (int64_t)T.m0 * T.K, (uint32_t)T.mrows * (uint32_t)T.K * 2u);
     xrows = T.mrows;
+    xK = (uint32_t)T.K;
+    xnS = T.K / KS;
+    xbase = (xr0 * xK + xchunk) * 2u;
   };
   set_x(0);
   auto dma_x = [&]() {
@@ -211,13 +242,13 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
     for (int i = 0; i < 4; ++i) {
       lds_bytes *dst = smem + slot + 16u * (512u * i + 64u * wvs);
       const uint32_t off = (int)(xr0 + 64u * i) < xrows
-                               ? xbase + (uint32_t)i * (64u * 2u) * (uint32_t)K + (uint32_t)sx * (KS * 2)
+                               ? xbase + (uint32_t)i * (64u * 2u) * xK + (uint32_t)sx * (KS * 2)
                                : kOutOfRange;
       __builtin_amdgcn_raw_ptr_buffer_load_lds(rx, (__attribute__((address_space(3))) void *)dst,
                                                16, off, 0, 0, 0);
     }
     ux = ux == XRING - 1 ? 0 : ux + 1;
-    if (++sx == nS) {
+    if (++sx == xnS) {
       sx = 0;
       set_x(++jx);
     }
@@ -227,10 +258,12 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
   const int sn0 = wn * 64 + (lane & 15);  // column of op tn: sn0 + 16 tn
   int js = 0, gs = 0;  // tile, its group
   int srows = 0;       // rows of the stream's tile
+  int snG = 1;         // its groups per row
   __amdgpu_buffer_rsrc_t rs;
   auto set_s = [&](int j) {
     const Tile T = tile(j);
-    rs = make_rsrc(args.scales[T.pi] + (int64_t)T.n0 * nG, (uint32_t)T.nrows * (uint32_t)nG * 2u);
+    snG = T.K / G;
+    rs = make_rsrc(args_.scales[T.pi] + (int64_t)T.n0 * snG, (uint32_t)T.nrows * (uint32_t)snG * 2u);
     srows = T.nrows;
   };
   set_s(0);
@@ -239,10 +272,10 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
 #pragma unroll
     for (int tn = 0; tn < TN; ++tn) {
       const int n = sn0 + 16 * tn;
-      const uint32_t off = n < srows ? 2u * ((uint32_t)n * (uint32_t)nG + (uint32_t)gs) : kOutOfRange;
+      const uint32_t off = n < srows ? 2u * ((uint32_t)n * (uint32_t)snG + (uint32_t)gs) : kOutOfRange;
       dst[tn] = __builtin_amdgcn_raw_buffer_load_b16(rs, off, 0, 0);
     }
-    if (++gs == nG) {
+    if (++gs == snG) {
       gs = 0;
       set_s(++js);
     }
@@ -255,10 +288,13 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
   int jp = 0, sp = 0;  // tile, its stage
   __amdgpu_buffer_rsrc_t rp;
   uint32_t prow;
+  int pnS = 1;  // stages of the stream's tile
   auto set_p = [&](int j) {
     const Tile T = tile(j);
+    const uint32_t rowbytes = (uint32_t)(T.K / G) * B;
+    pnS = T.K / KS;
     const uintptr_t pabs =
-        reinterpret_cast<uintptr_t>(args.packed[T.pi]) + (uint64_t)T.n0 * rowbytes;
+        reinterpret_cast<uintptr_t>(args_.packed[T.pi]) + (uint64_t)T.n0 * rowbytes;
     const uint32_t pbase = (uint32_t)(pabs & 3u);  // packed has any alignment
     // The range is a whole number of dwords, so a dword load is either fully
     // in range or fully past it (then it reads 0).
@@ -303,7 +339,8 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
   auto store_tile = [&](int j) {
     const Tile T = tile(j);
     const int mb = wm * 64 + 4 * (lane >> 4), nb = wn * 64 + (lane & 15);
-    float *__restrict__ yl = args.y[T.pi] + (int64_t)(T.m0 + mb) * ldy + (T.n0 + nb);
+    const int64_t ldy = T.N;
+    float *__restrict__ yl = args_.y[T.pi] + (int64_t)(T.m0 + mb) * ldy + (T.n0 + nb);
     if (T.mrows == BM && T.nrows == BN) {
 #pragma unroll
       for (int a = 0; a < TM; ++a)
@@ -344,7 +381,7 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rp, a & ~3u, 0, 0);
       dst[0] = v.x;
       dst[1] = v.y;
-      if (++sp == nS) {
+      if (++sp == pnS) {
         sp = 0;
         set_p(++jp);
       }
@@ -382,6 +419,7 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
     int uc = 0;  // ring slot of the stage being computed
     int sc = 0;  // its stage within its tile
     int jc = 0;  // its tile
+    int cnS = tile(0).K / KS;  // its tile's stages
     // a stage is stage ST (= its index & 1) of its group; it reads code slot
     // ST and the activation slot uc
     auto stage = [&](auto stc) {
@@ -456,12 +494,13 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
         __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
       }
       uc = uc == XRING - 1 ? 0 : uc + 1;
-      if (ST == SPG - 1 && sc == nS - 1) {
+      if (ST == SPG - 1 && sc == cnS - 1) {
         // last stage of a tile: store it, then a full wait (the stores count
         // in vmcnt too) before the barrier
         store_tile(jc);
         ++jc;
         sc = 0;
+        cnS = tile(jc).K / KS;
         asm volatile("s_waitcnt vmcnt(0) lgkmcnt(0)\n\ts_barrier" ::: "memory");
         return;
       }
@@ -477,7 +516,8 @@ void gemm_wide_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy, in
         asm volatile("s_waitcnt vmcnt(5) lgkmcnt(0)\n\ts_barrier" ::: "memory");
     };
 
-    const int nstages = ntiles * nS;  // a multiple of SPG
+    int nstages = 0;  // a multiple of SPG
+    for (int j = 0; j < ntiles; ++j) nstages += tile(j).K / KS;
     for (int u = 0; u < nstages; u += SPG) {
       stage(Int<0>{});
       stage(Int<1>{});
@@ -501,17 +541,30 @@ bool gemm_wide_supported(int count, int64_t M, int64_t N, int64_t K, int G_) {
   // slab of x); and enough tiles to give at least 3/4 of the 256 CUs one
   // block each -- smaller grids run faster as 128 x 128 tiles, two per CU
   const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  return G_ == G && M >= BM && K % G == 0 && tiles * kGemmMaxBatch < (int64_t(1) << 31) &&
+  return G_ == G && M >= BM && K % G == 0 && tiles * kWideMaxBatch < (int64_t(1) << 30) &&
          (int64_t)BM * K * 2 < (int64_t(1) << 31) && tiles * count >= 192;
 }
 
-void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
-                      const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
-                      int64_t K, int64_t ldy, int32_t *d_status, hipStream_t stream) {
-  // one persistent block per CU
+bool gemm_wide_grouped_supported(int count, int64_t M, const int64_t *Ns, const int64_t *Ks,
+                                 int G_) {
+  int64_t tiles = 0;
+  for (int i = 0; i < count; ++i) {
+    if (!gemm_wide_supported(1 << 20, M, Ns[i], Ks[i], G_)) return false;
+    tiles += ((M + BM - 1) / BM) * ((Ns[i] + BN - 1) / BN);
+  }
+  return tiles >= 192 && tiles < (int64_t(1) << 30);
+}
+
+// Launches of up to kWideMaxBatch problems and kWideMaxShapes shapes, one
+// persistent block per CU.  Shapes are placed longest K first, so that the
+// blocks' round-robin share of the tiles ends with the short ones.
+void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,
+                              const uint8_t *const *packeds, const uint16_t *const *scales,
+                              float *const *ys, int64_t M, const int64_t *Ns, const int64_t *Ks,
+                              int32_t *d_status, hipStream_t stream) {
   static int cus[64] = {};
   int dev = 0;
-  hipGetDevice(&dev);
+  (void)hipGetDevice(&dev);
   if (dev < 0 || dev >= 64) dev = 0;
   if (cus[dev] <= 0) {
     int n = 0;
@@ -519,21 +572,55 @@ void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const
       n = 256;
     cus[dev] = n;
   }
-  const int64_t tiles = ((M + BM - 1) / BM) * ((N + BN - 1) / BN);
-  for (int base = 0; base < count; base += kGemmMaxBatch) {
-    const int n = count - base < kGemmMaxBatch ? count - base : kGemmMaxBatch;
-    GemmBatch a;
-    for (int i = 0; i < n; ++i) {
-      a.x[i] = xs[base + i];
-      a.packed[i] = packeds[base + i];
-      a.scales[i] = scales[base + i];
-      a.y[i] = ys[base + i];
+  // problems by shape: K descending, then N descending, then in order
+  std::vector<int> order(count);
+  for (int i = 0; i < count; ++i) order[i] = i;
+  std::stable_sort(order.begin(), order.end(), [&](int a, int b) {
+    return Ks[a] != Ks[b] ? Ks[a] > Ks[b] : Ns[a] > Ns[b];
+  });
+  const int64_t tilesM = (M + BM - 1) / BM;
+  WideBatch a;
+  int n = 0, shapes = 0;
+  auto flush = [&]() {
+    if (n == 0) return;
+    for (int g = shapes; g < kWideMaxShapes; ++g) {
+      a.n[g] = 0; a.k[g] = G; a.tpp[g] = 1; a.first[g] = n; a.t0[g] = INT_MAX;
     }
-    const int total = (int)(tiles * n);
-    const int grid = total < cus[dev] ? total : cus[dev];
+    const int grid = a.total < cus[dev] ? a.total : cus[dev];
     hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a, (int)M,
-                       (int)N, (int)K, ldy, total, d_status);
+                       d_status);
+    n = 0;
+    shapes = 0;
+  };
+  for (int i = 0; i < count; ++i) {
+    const int p = order[i];
+    const bool new_shape = shapes == 0 || Ns[p] != a.n[shapes - 1] || Ks[p] != a.k[shapes - 1];
+    if (n == kWideMaxBatch || (new_shape && shapes == kWideMaxShapes)) flush();
+    if (shapes == 0 || Ns[p] != a.n[shapes - 1] || Ks[p] != a.k[shapes - 1]) {
+      const int g = shapes++;
+      a.n[g] = (int)Ns[p];
+      a.k[g] = (int)Ks[p];
+      a.tpp[g] = (int)(tilesM * ((Ns[p] + BN - 1) / BN));
+      a.first[g] = n;
+      a.t0[g] = g == 0 ? 0 : a.total;
+      if (g == 0) a.total = 0;
+    }
+    a.x[n] = xs[p];
+    a.packed[n] = packeds[p];
+    a.scales[n] = scales[p];
+    a.y[n] = ys[p];
+    ++n;
+    a.total += a.tpp[shapes - 1];
   }
+  flush();
+}
+
+void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                      const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                      int64_t K, int32_t *d_status, hipStream_t stream) {
+  std::vector<int64_t> Ns(count, N), Ks(count, K);
+  launch_gemm_wide_grouped(count, xs, packeds, scales, ys, M, Ns.data(), Ks.data(), d_status,
+                           stream);
 }
 
 }  // namespace tq

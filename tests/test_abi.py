@@ -106,6 +106,7 @@ def test_binding_rejects_host_tensors_before_the_library():
              lambda: tq.gemv_batched([x], [p], [s], 4, 64, 64),
              lambda: tq.gemm_batched([x], [p], [s], 4, 64, 64),
              lambda: tq.gemv_grouped([x], [p], [s], [4], [64], 64),
+             lambda: tq.gemm_grouped([x], [p], [s], [4], [64], 64),
              lambda: tq.quantize_pack2(w, 64), lambda: tq.unpack2(p, 4, 52, 64),
              lambda: tq.gemv2(x, p, s, 4, 64, 64),
              lambda: tq.w4a16_gemv(x, torch.zeros(4, 8, dtype=torch.int32), w[:, :1], w[:, :1],
@@ -155,6 +156,29 @@ def test_batched_argument_errors(fn):
     assert f(2, good, good, good, good, 0, 8, 128, 64, None, None) == -2
     assert f(2, good, good, good, good, 1, 8, 96, 32, None, None) == -3
     assert f(2, bad_al, good, good, good, 1, 8, 128, 64, None, None) == -4
+
+
+def test_gemm_grouped_argument_errors():
+    lib = _lib()
+    f = lib.tq_gemm_grouped
+    arr = ctypes.c_void_p * 2
+    i64 = ctypes.c_int64 * 2
+    good = arr(FAKE, FAKE + 4096)
+    bad_al = arr(FAKE, FAKE + 4)
+    nul = arr(FAKE, None)
+    ns, ks = i64(8, 16), i64(128, 256)
+    assert f(0, None, None, None, None, 1, None, None, 64, None, None) == 0   # nothing to do
+    assert f(-1, good, good, good, good, 1, ns, ks, 64, None, None) == -2
+    assert f(2, good, good, good, good, 1, ns, None, 64, None, None) == -1
+    assert f(2, good, nul, good, good, 1, ns, ks, 64, None, None) == -1
+    assert f(2, good, good, good, good, 0, ns, ks, 64, None, None) == -2     # M < 1
+    assert f(2, good, good, good, good, 1, ns, i64(128, 100), 64, None, None) == -2  # K % G
+    assert f(2, good, good, good, good, 1, i64(8, 0), ks, 64, None, None) == -2      # N < 1
+    assert f(2, good, good, good, good, 1, ns, i64(128, (1 << 22) + 64), 64, None, None) == -2
+    assert f(2, good, good, good, good, 1, ns, i64(96, 96), 32, None, None) == -3    # G
+    assert f(2, bad_al, good, good, good, 1, ns, ks, 64, None, None) == -4   # x alignment
+    assert f(2, good, good, good, arr(FAKE, FAKE + 2), 1, ns, ks, 64, None, None) == -4  # y
+    assert f(2, good, good, good, good, 1, ns, ks, 64, FAKE + 2, None) == -4  # status
 
 
 def test_grouped_argument_errors():

@@ -6,7 +6,8 @@ packed bytes and scales bit for bit, matmul outputs within
 Workloads (seeds in ternary_weight_only_amd.inputs):
   - one Qwen-like FFN block and the 72-matrix stack (24 layers of gate and up
     W[3584,1024] and down W[1024,3584]), G = 64 and 128, decode at M = 1;
-  - the prefill GEMM on the stack's shapes at M = 512 and 2048, G = 128;
+  - the prefill GEMM on the stack's shapes at M = 512 and 2048, G = 128
+    (the grouped launch over all 72 problems, and per-shape batched launches);
   - the 8B-class FFN matrices W[14336,4096] and W[4096,14336], G = 128,
     decode at M = 1, 4 and 16.
 The only outputs not all compared are those of the M = 2048 stack launch:
@@ -159,15 +160,25 @@ def test_prefill_gemm_single_every_output(M):
         assert_within_bound(y, y_ref, bound, "gemm M=%d W[%d,%d]" % (M, N, K))
 
 
-def _stack_gemm(M, G):
-    """The benchmark's prefill launch: one tq_gemm_batched call per shape
-    (48 problems of K = 1024 sharing one x, 24 of K = 3584 sharing another),
-    on the packed bytes the batched quantize launches wrote."""
+def _stack_gemm(M, G, launch="grouped"):
+    """The benchmark's prefill launch: one tq_gemm_grouped call over all 72
+    problems (48 of K = 1024 sharing one x, 24 of K = 3584 sharing another),
+    on the packed bytes the batched quantize launches wrote; or
+    (launch="batched") one tq_gemm_batched call per shape."""
     out, st = _quantize_stack_batched(G)
     assert st == 0
     xs = {K: inputs.prefill_activation(M, K) for K in (1024, 3584)}
     ys = [None] * len(out)
     yst = tq.new_status()
+    if launch == "grouped":
+        shapes = inputs.stack_shapes()
+        say("stack prefill gemm M=%d grouped x %d" % (M, len(shapes)))
+        xd = {K: dev_bf16(x) for K, x in xs.items()}
+        ys = tq.gemm_grouped([xd[K] for _, K in shapes], [p for p, _ in out], [s for _, s in out],
+                             [N for N, _ in shapes], [K for _, K in shapes], G, status=yst)
+        torch.cuda.synchronize()
+        assert int(yst.item()) == 0
+        return xs, ys
     for (N, K), idx in _groups().items():
         say("stack prefill gemm M=%d W[%d,%d] x %d" % (M, N, K, len(idx)))
         xd = dev_bf16(xs[K])
@@ -180,11 +191,12 @@ def _stack_gemm(M, G):
     return xs, ys
 
 
-def test_prefill_gemm_stack_m512_every_output():
-    """M = 512: every output of all 72 problems of the benchmark's two
-    batched launches."""
+@pytest.mark.parametrize("launch", ["grouped", "batched"])
+def test_prefill_gemm_stack_m512_every_output(launch):
+    """M = 512: every output of all 72 problems of the benchmark's grouped
+    launch, and of the two batched launches (one per shape)."""
     G, M = 128, 512
-    xs, ys = _stack_gemm(M, G)
+    xs, ys = _stack_gemm(M, G, launch)
     for i, (N, K) in enumerate(inputs.stack_shapes()):
         p_ref, s_ref = _stack_ref(G)[i]
         y_ref, bound, _ = oracle.matmul(xs[K], p_ref, s_ref, N, K, G)
@@ -192,7 +204,7 @@ def test_prefill_gemm_stack_m512_every_output():
 
 
 def test_prefill_gemm_stack_m2048():
-    """M = 2048, the same two batched launches: problems 0, 1, 46 (gate/up)
+    """M = 2048, the same grouped launch: problems 0, 1, 46 (gate/up)
     and 2, 35, 71 (down) compared whole; on every other problem the first
     and last row of every 256-row tile and 8 random rows."""
     G, M = 128, 2048
