@@ -426,10 +426,6 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
       constexpr int ST = decltype(stc)::value;
       constexpr int P = ST, Q = 1 - ST;
       constexpr int ST1 = (ST + 1) % SPG;  // place of the next stage in its group
-      // table lookups for the next stage: its bytes were requested two stages
-      // ago (past the last stage they decode junk into the free code slot)
-      uint32_t lo[4], hi[4];
-      lookup(ring[Q], rofs[Q], lo, hi);
       const uint32_t xs = (uint32_t)uc * XSLOT;
       // operands of one 32-wide step: 4 activation and 4 code fragments
       auto read_ops = [&](int ks, bf16x8 (&av)[TM], bf16x8 (&bv)[TN]) {
@@ -451,11 +447,16 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
       };
       bf16x8 av0[TM], bv0[TN], av1[TM], bv1[TN];
       read_ops(0, av0, bv0);
+      // table lookups for the next stage, after this stage's first operand
+      // reads so that the first MFMAs wait for those only: its bytes were
+      // requested two stages ago (past the last stage they decode junk into
+      // the free code slot)
+      uint32_t lo[4], hi[4];
+      lookup(ring[Q], rofs[Q], lo, hi);
       if (ST == 0) load_scales(sc_next);
       dma_x();
       load_packed(ring[Q], rofs[Q]);
-      // the next stage's codes are assembled and written before the MFMAs,
-      // so that the table entries are not live across them
+      // the next stage's codes, assembled and written between the first MFMAs
       emit(Int<ST1>{}, lo, hi, kCsOff + (uint32_t)Q * CSLOT);
       mfmas(0, av0, bv0);
       read_ops(1, av1, bv1);
@@ -473,20 +474,23 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
 #pragma unroll
         for (int b = 0; b < TN; ++b) sc_cur[b] = sc_next[b];
       }
-      // Instruction order for the scheduler: the table and operand reads and
-      // the loads first, then each MFMA followed by vector-ALU work, so that
-      // the decode and the scaling run in the MFMA shadow.
+      // Instruction order for the scheduler: the operand and table reads and
+      // the loads first, then each MFMA followed by vector-ALU work -- the
+      // code assembly after the first seven, the scaling after the rest -- so
+      // that the decode and the scaling run in the MFMA shadow.
       constexpr int kValu = ST == SPG - 1 ? 3 : 1;
-      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU: table addresses
-      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: table, step 0
+      __builtin_amdgcn_sched_group_barrier(0x002, 10, 0);  // VALU: addresses
+      __builtin_amdgcn_sched_group_barrier(0x100, 12, 0);  // DS reads: step 0, then table
       __builtin_amdgcn_sched_group_barrier(0x020, 10, 0);  // VMEM reads
-      __builtin_amdgcn_sched_group_barrier(0x002, 14, 0);  // VALU: code assembly
-      __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);   // DS writes
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
         __builtin_amdgcn_sched_group_barrier(0x008, 1, 0);      // MFMA
-        __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
+        if (i < 7)
+          __builtin_amdgcn_sched_group_barrier(0x002, 2, 0);  // VALU: code assembly
+        else
+          __builtin_amdgcn_sched_group_barrier(0x002, kValu, 0);  // VALU
         if (i == 3) __builtin_amdgcn_sched_group_barrier(0x100, 8, 0);  // DS reads: step 1
+        if (i == 7) __builtin_amdgcn_sched_group_barrier(0x200, 2, 0);  // DS writes
       }
 #pragma unroll
       for (int i = 0; i < 16; ++i) {
