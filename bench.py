@@ -6,20 +6,25 @@
 Workload of the step (`value`, `roofline`): the 24-layer Qwen-like FFN stack
 (hidden 1024, intermediate 3584: gate and up W[3584,1024], down
 W[1024,3584]; 72 matrices, 264,241,152 bf16 weights ~ N(0, 0.02)), G = 128.
-One step is one pass of every step of the hot path over that stack:
-  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
-      one launch for the 48 K=1024 and the 24 K=3584 matrices together)
-  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_grouped:
-      one persistent launch over both shapes; each matrix has its own output)
+One step is one pass of every step of the hot path over that stack, in the
+path's own order (pack the weights, validate them, prefill, decode):
   quantize + pack all 72 bf16 matrices                 (tq_quantize_pack_batched:
       two launches, one per shape)
   unpack + validate all 72 packed matrices             (tq_unpack_batched: two)
+  prefill GEMM, M = 512 tokens, through all 72 matrices (tq_gemm_grouped:
+      one persistent launch over both shapes; each matrix has its own output)
+  decode GEMV, M = 1, through all 72 matrices          (tq_gemv_grouped:
+      one launch for the 48 K=1024 and the 24 K=3584 matrices together)
 The packed weights live in a ring of eight slots (480 MB, more than the
-256 MB memory-side cache); step t reads slot t%8 and packs into slot
-(t+2)%8, so the weights a GEMV reads were written six steps (several GB of
-traffic) earlier and come from HBM.  Every row is direct launches (pointer
-arrays built once per ring slot); HIP events recorded between the rows on
-the stream the kernels run on time each row, dispatch included.
+256 MB memory-side cache).  Step t packs into slot (t+2)%8 and unpacks it,
+runs the GEMM on slot (t+4)%8 and the GEMV on slot t%8: the bytes the GEMV
+reads were packed and unpacked two steps (several GB of traffic) earlier and
+come from HBM, and no row reads bytes the row before it read.  Every row is
+direct launches (pointer arrays built once per ring slot); HIP events
+recorded between the rows on the stream the kernels run on time each row,
+dispatch included.  The events are created with hipEventDisableSystemFence
+(--torch-events: torch's events, whose recording writes back and invalidates
+the caches), so an interval holds its kernels and not the fences.
 
 The GEMV kernel alone (`roofline`): after the steps, the decode pass runs
 over all eight slots back to back (eight launches, each launch's dispatch
@@ -84,6 +89,9 @@ def parse():
     ap.add_argument("--rows", default="all",
                     help="comma-separated rows to run (%s), or all" % ",".join(ALL_ROWS))
     ap.add_argument("--no-cpu-baseline", action="store_true", help="same as leaving out row cpu")
+    ap.add_argument("--torch-events", action="store_true",
+                    help="time with torch.cuda.Event (system-scope fences) instead of HIP "
+                         "events created with hipEventDisableSystemFence")
     ap.add_argument("--cpu-seconds", type=float, default=4.0,
                     help="minimum time of each timed oracle sample")
     ap.add_argument("--calibrate-copy", action="store_true",
@@ -223,6 +231,44 @@ def pmc_summary(paths, pattern=None):
 # the GPU rows
 # ---------------------------------------------------------------------------
 
+class HipEvent:
+    """A HIP timing event created with hipEventDisableSystemFence: recording it
+    does not write back and invalidate the caches, so the interval between two
+    such events holds the kernels between them and not the fences' cost (HIP
+    documents the flag for events used only to measure time).  Read only
+    after a device synchronisation."""
+    DISABLE_SYSTEM_FENCE = 0x20000000
+    _hip = None
+
+    def __init__(self):
+        if HipEvent._hip is None:
+            # the HIP runtime the process already has (torch's), by its soname
+            h = ctypes.CDLL("libamdhip64.so.7")
+            vp = ctypes.c_void_p
+            h.hipEventCreateWithFlags.argtypes = [ctypes.POINTER(vp), ctypes.c_uint]
+            h.hipEventRecord.argtypes = [vp, vp]
+            h.hipEventElapsedTime.argtypes = [ctypes.POINTER(ctypes.c_float), vp, vp]
+            h.hipEventDestroy.argtypes = [vp]
+            HipEvent._hip = h
+        self.ev = ctypes.c_void_p()
+        rc = self._hip.hipEventCreateWithFlags(ctypes.byref(self.ev), self.DISABLE_SYSTEM_FENCE)
+        assert rc == 0, "hipEventCreateWithFlags failed (%d)" % rc
+
+    def record(self, stream):
+        rc = self._hip.hipEventRecord(self.ev, stream.cuda_stream)
+        assert rc == 0, "hipEventRecord failed (%d)" % rc
+
+    def elapsed_time(self, end):
+        ms = ctypes.c_float()
+        rc = self._hip.hipEventElapsedTime(ctypes.byref(ms), self.ev, end.ev)
+        assert rc == 0, "hipEventElapsedTime failed (%d)" % rc
+        return ms.value
+
+    def __del__(self):
+        if self.ev and HipEvent._hip is not None:
+            HipEvent._hip.hipEventDestroy(self.ev)
+
+
 class Bench:
     def __init__(self, args):
         import numpy as np
@@ -276,6 +322,12 @@ class Bench:
         st = int(self.status.item())
         assert st == 0, "device status %d" % st
 
+    def event(self):
+        """A timing event (HipEvent, or torch's with --torch-events)."""
+        if self.args.torch_events:
+            return self.torch.cuda.Event(enable_timing=True)
+        return HipEvent()
+
     def chain(self, body, inner, reps=4):
         """Median time (ms) of one body(i) call over `reps` chains of `inner`
         calls between HIP events on the bench stream (the first chain is a
@@ -284,8 +336,8 @@ class Bench:
         res = []
         with torch.cuda.stream(self.stream):
             for _ in range(reps):
-                e0 = torch.cuda.Event(enable_timing=True)
-                e1 = torch.cuda.Event(enable_timing=True)
+                e0 = self.event()
+                e1 = self.event()
                 e0.record(self.stream)
                 for i in range(inner):
                     body(i)
@@ -356,11 +408,11 @@ class Bench:
                 self.ok(L.tq_unpack_batched(n, ap, N, K, G, ac, stp, sp))
 
         run = {"gemv": run_gemv, "gemm": run_gemm, "quant": run_quant, "unpack": run_unpack}
-        order = ("gemv", "gemm", "quant", "unpack")
+        order = ("quant", "unpack", "gemm", "gemv")
 
         def step(t, evs=None):
-            rd, wr = t % RING, (t + 2) % RING
-            slots = {"gemv": rd, "gemm": rd, "quant": wr, "unpack": wr}
+            wr = (t + 2) % RING
+            slots = {"quant": wr, "unpack": wr, "gemm": (t + 4) % RING, "gemv": t % RING}
             with torch.cuda.stream(self.stream):
                 if evs is not None:
                     evs[0].record(self.stream)
@@ -372,7 +424,7 @@ class Bench:
         for t in range(args.warmup):
             step(t)
         torch.cuda.synchronize()
-        evs = [[torch.cuda.Event(enable_timing=True) for _ in range(len(order) + 1)]
+        evs = [[self.event() for _ in range(len(order) + 1)]
                for _ in range(args.steps)]
         t0 = time.perf_counter()
         for t in range(args.steps):
