@@ -29,10 +29,12 @@
 //     group's bytes contribute nothing.
 //   * A group's partial tile is scaled by its fp16 scale in fp32 and added
 //     to the accumulator.
-// Work: a block of 8 waves takes "chunks" of TB consecutive 16-row tiles
-// (over the problems of the launch), with the K groups of each tile split
-// into S contiguous parts (TB * S = 8): wave (a, p) computes part p of tile
-// a of each chunk.  Every wave runs the same number of group iterations per
+// Work: a wave's tile is R consecutive 16-row MFMA tiles (R = 1, 2 or 4):
+// the activation fragments of a group are built once and feed the MFMAs of
+// all R, so the activations are read once per 16R weight rows.  A block of
+// 8 waves takes "chunks" of TB consecutive tiles (over the problems of the
+// launch), with the K groups of each tile split into S contiguous parts
+// (TB * S = 8): wave (a, p) computes part p of tile a of each chunk.  Every wave runs the same number of group iterations per
 // chunk (ceil(nG / S); past its part a wave reads zeros), so the block
 // reaches each chunk's end together; the S partial tiles are then added
 // through LDS in a fixed order (deterministic results) and stored.  Within a
@@ -114,7 +116,7 @@ struct Geo {
   static constexpr int XW = G == 128 ? 4 : 2;   // dwords per activation load
 };
 
-template <int G, int BR>
+template <int G, int BR, int R>
 __global__ __launch_bounds__(kThreads) __attribute__((amdgpu_waves_per_eu(2, 2)))
 void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, int nchunks,
                  int64_t ldy, int32_t *__restrict__ d_status) {
@@ -131,7 +133,8 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
   const int ngw = (nG + S - 1) >> lgS;                // group iterations per chunk
   const int g_begin = part * ngw;                     // the wave's first group (may be >= nG)
   const uint32_t rowbytes = (uint32_t)nG * B;
-  const int tpp = (N + 15) >> 4;                      // tiles per problem
+  constexpr int TR = 16 * R;                          // rows of a wave's tile: R MFMA tiles
+  const int tpp = (N + TR - 1) / TR;                  // tiles per problem
   const int ntiles = tpp * count;
   const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
   const int mychunks = nchunks > bid ? (nchunks - bid + grid - 1) / grid : 0;
@@ -170,8 +173,9 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
                  : kOutOfRange;
   }
 
-  // Tile of the wave in chunk k of the block; past the block's chunks or
-  // the launch's tiles it has no rows (every load of it reads zeros).
+  // Tile of the wave in chunk k of the block: TR = 16 R weight rows, R MFMA
+  // tiles that share the activations; past the block's chunks or the
+  // launch's tiles it has no rows (every load of it reads zeros).
   struct Tile {
     int pi, row0, nrows;
   };
@@ -179,14 +183,14 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
     const int t = (bid + k * grid) * TB + slot;
     if (k >= mychunks || t >= ntiles) return Tile{0, 0, 0};
     const int pi = t / tpp;
-    const int row0 = (t - pi * tpp) << 4;
-    return Tile{pi, row0, min(16, N - row0)};
+    const int row0 = (t - pi * tpp) * TR;
+    return Tile{pi, row0, min(TR, N - row0)};
   };
 
   struct PkStage {
-    uint32_t pk[PD];
-    uint32_t sc;
-    uint32_t ofs;
+    uint32_t pk[R][PD];
+    uint32_t sc[R];
+    uint32_t ofs[R];
   };
   struct XStage {
     uint32_t xd[XL * XW];
@@ -226,15 +230,19 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
   // read 0: scale 0 and zero activations add nothing)
   auto issue_pk = [&](const PkCursor &c, int gi, bool live, PkStage &st) {
     const int g = g_begin + gi;
-    const bool on = live && j < c.nrows && g < nG;
-    const uint32_t a = c.pbase + (uint32_t)j * rowbytes + (uint32_t)(g * B + T * q);
-    const uint32_t a4 = on ? (a & ~3u) : kOutOfRange;
-    st.ofs = a & 3u;
 #pragma unroll
-    for (int d = 0; d < PD; ++d)
-      st.pk[d] = __builtin_amdgcn_raw_buffer_load_b32(c.rp, a4 + 4u * d, 0, 0);
-    st.sc = __builtin_amdgcn_raw_buffer_load_b16(
-        c.rs, on ? 2u * ((uint32_t)j * (uint32_t)nG + (uint32_t)g) : kOutOfRange, 0, 0);
+    for (int r = 0; r < R; ++r) {
+      const int row = 16 * r + j;  // the lane's row within the tile
+      const bool on = live && row < c.nrows && g < nG;
+      const uint32_t a = c.pbase + (uint32_t)row * rowbytes + (uint32_t)(g * B + T * q);
+      const uint32_t a4 = on ? (a & ~3u) : kOutOfRange;
+      st.ofs[r] = a & 3u;
+#pragma unroll
+      for (int d = 0; d < PD; ++d)
+        st.pk[r][d] = __builtin_amdgcn_raw_buffer_load_b32(c.rp, a4 + 4u * d, 0, 0);
+      st.sc[r] = __builtin_amdgcn_raw_buffer_load_b16(
+          c.rs, on ? 2u * ((uint32_t)row * (uint32_t)nG + (uint32_t)g) : kOutOfRange, 0, 0);
+    }
   };
   // activations of group iteration gi of the cursor's tile (zeros past the
   // tiles, past nG and past the burst)
@@ -255,9 +263,12 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
     }
   };
 
-  f32x4 acc = f32x4{0.f, 0.f, 0.f, 0.f};
+  f32x4 acc[R];
+#pragma unroll
+  for (int r = 0; r < R; ++r) acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
 
-  // the T MFMAs of one group iteration and the scaled accumulation
+  // the R x T MFMAs of one group iteration (the A fragments built once for
+  // the R MFMA tiles) and the scaled accumulation
   auto compute = [&](const PkStage &sp, const XStage &sx) {
     // A fragments: byte t of the lane's run takes activations 5t .. 5t+4
     u32x4 A[T];
@@ -272,56 +283,64 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
           ((e + 4) & 1) ? (sx.xd[(e + 3) / 2] >> 16) : (sx.xd[(e + 4) / 2] & 0xFFFFu);
       A[t] = u32x4{pair(e), pair(e + 2), last, 0u};
     }
-    uint32_t w[2];
-    w[0] = (__builtin_amdgcn_alignbyte(sp.pk[1], sp.pk[0], sp.ofs) & wmask[0]) | wfill[0];
-    w[1] = PD == 3 ? (__builtin_amdgcn_alignbyte(sp.pk[PD - 1], sp.pk[1], sp.ofs) & wmask[1]) |
-                         wfill[1]
-                   : 0u;
-    u32x4 b[T];
 #pragma unroll
-    for (int t = 0; t < T; ++t) {
-      // address = byte * 256 + copy * 16: byte (t % 4) of w[t / 4] into byte 1
-      const uint32_t sel = 0x0C0C0004u | ((uint32_t)(t & 3) << 8);
-      const uint32_t addr = __builtin_amdgcn_perm(copyoff, w[t >> 2], sel);
-      b[t] = *(lds_u32x4_c *)(lut_bytes + addr);
+    for (int r = 0; r < R; ++r) {
+      uint32_t w[2];
+      w[0] = (__builtin_amdgcn_alignbyte(sp.pk[r][1], sp.pk[r][0], sp.ofs[r]) & wmask[0]) |
+             wfill[0];
+      w[1] = PD == 3 ? (__builtin_amdgcn_alignbyte(sp.pk[r][PD - 1], sp.pk[r][1], sp.ofs[r]) &
+                        wmask[1]) | wfill[1]
+                     : 0u;
+      u32x4 b[T];
+#pragma unroll
+      for (int t = 0; t < T; ++t) {
+        // address = byte * 256 + copy * 16: byte (t % 4) of w[t / 4] into byte 1
+        const uint32_t sel = 0x0C0C0004u | ((uint32_t)(t & 3) << 8);
+        const uint32_t addr = __builtin_amdgcn_perm(copyoff, w[t >> 2], sel);
+        b[t] = *(lds_u32x4_c *)(lut_bytes + addr);
+      }
+      f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
+#pragma unroll
+      for (int t = 0; t < T; ++t)
+        part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[t]),
+                                                        __builtin_bit_cast(bf16x8, b[t]), part, 0,
+                                                        0, 0);
+      const float sc = __half2float(__ushort_as_half((unsigned short)sp.sc[r]));
+#pragma unroll
+      for (int e = 0; e < 4; ++e) acc[r][e] = fmaf(sc, part[e], acc[r][e]);
+      __builtin_amdgcn_sched_group_barrier(0x100, T, 0);  // table reads
+      __builtin_amdgcn_sched_group_barrier(0x008, T, 0);  // MFMAs
     }
-    f32x4 part = f32x4{0.f, 0.f, 0.f, 0.f};
-#pragma unroll
-    for (int t = 0; t < T; ++t)
-      part = __builtin_amdgcn_mfma_f32_16x16x32_bf16(__builtin_bit_cast(bf16x8, A[t]),
-                                                      __builtin_bit_cast(bf16x8, b[t]), part, 0,
-                                                      0, 0);
-    const float sc = __half2float(__ushort_as_half((unsigned short)sp.sc));
-#pragma unroll
-    for (int r = 0; r < 4; ++r) acc[r] = fmaf(sc, part[r], acc[r]);
-    __builtin_amdgcn_sched_group_barrier(0x100, T, 0);  // table reads
-    __builtin_amdgcn_sched_group_barrier(0x008, T, 0);  // MFMAs
   };
 
   uint32_t flags = 0;
   // end of chunk k: park the partial tiles, add the S parts of each tile in
   // order and store
   auto finish_chunk = [&](int k) {
-    red[wv][lane] = acc;
-    acc = f32x4{0.f, 0.f, 0.f, 0.f};
-    __syncthreads();
-    if (part == 0) {
-      const Tile w = tile_of(k);
-      f32x4 v = red[wv][lane];
-      for (int p = 1; p < S; ++p) v += red[wv + p][lane];
-      float *__restrict__ y = args.y[w.pi];
+    const Tile w = tile_of(k);
 #pragma unroll
-      for (int e = 0; e < 4; ++e) {
-        const int m = 4 * q + e;
-        if (m < M && j < w.nrows) {
-          if (v[e] != v[e] && !flags)
-            flags = row_has_invalid_byte(args.packed[w.pi] + (int64_t)(w.row0 + j) * rowbytes,
-                                         rowbytes);
-          y[(int64_t)m * ldy + w.row0 + j] = v[e];
+    for (int r = 0; r < R; ++r) {
+      red[wv][lane] = acc[r];
+      acc[r] = f32x4{0.f, 0.f, 0.f, 0.f};
+      __syncthreads();
+      if (part == 0) {
+        f32x4 v = red[wv][lane];
+        for (int p = 1; p < S; ++p) v += red[wv + p][lane];
+        float *__restrict__ y = args.y[w.pi];
+        const int row = 16 * r + j;
+#pragma unroll
+        for (int e = 0; e < 4; ++e) {
+          const int m = 4 * q + e;
+          if (m < M && row < w.nrows) {
+            if (v[e] != v[e] && !flags)
+              flags = row_has_invalid_byte(
+                  args.packed[w.pi] + (int64_t)(w.row0 + row) * rowbytes, rowbytes);
+            y[(int64_t)m * ldy + w.row0 + row] = v[e];
+          }
         }
       }
+      __syncthreads();  // red[] is reused by the next MFMA tile and chunk
     }
-    __syncthreads();  // red[] is reused at the next chunk's end
   };
 
   // Chunk by chunk (every wave of the block has the same chunks and group
@@ -364,9 +383,9 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
 // whose chunks still fill three quarters of the resident blocks (two per
 // CU), so each wave streams the longest runs of groups; every part keeps at
 // least one group.
-int choose_lgS(int count, int64_t N, int64_t K, int G) {
+int choose_lgS(int count, int64_t N, int64_t K, int G, int R) {
   const int64_t nG = K / G;
-  const int64_t tiles = count * ((N + 15) / 16);
+  const int64_t tiles = count * ((N + 16 * R - 1) / (16 * R));
   int lg = 0;
   for (; lg < 3; ++lg) {
     const int64_t tb = kWaves >> lg;
@@ -376,24 +395,44 @@ int choose_lgS(int count, int64_t N, int64_t K, int G) {
   return lg;
 }
 
-template <int G>
-void launch(const GemvBatch &args, int count, int64_t M, int64_t N, int64_t K, int64_t ldy,
-            int32_t *d_status, hipStream_t stream) {
-  const int lgS = choose_lgS(count, N, K, G);
-  const int64_t tiles = count * ((N + 15) / 16);
+template <int G, int BR, int R>
+void launch_with(const GemvBatch &args, int count, int64_t M, int64_t N, int64_t K, int64_t ldy,
+                 int lgS, int32_t *d_status, hipStream_t stream) {
+  const int64_t tiles = count * ((N + 16 * R - 1) / (16 * R));
   const int64_t tb = kWaves >> lgS;
   const int nchunks = (int)((tiles + tb - 1) / tb);
   const int grid = nchunks < kMaxBlocks ? nchunks : kMaxBlocks;
+  hipLaunchKernelGGL((gemv_kernel<G, BR, R>), dim3(grid), dim3(kThreads), 0, stream, args, count,
+                     (int)M, (int)N, (int)K, lgS, nchunks, ldy, d_status);
+}
+
+// R MFMA tiles a wave (the activation fragments are built once for them):
+// up to 4 from M = 8 rows, 2 from 3, else 1, and no more than leave 192
+// chunks (three quarters of the CUs a block) at the largest K split; bursts
+// of BR groups, BR * R <= 16.
+template <int G>
+void launch(const GemvBatch &args, int count, int64_t M, int64_t N, int64_t K, int64_t ldy,
+            int32_t *d_status, hipStream_t stream) {
+  int R = M >= 8 ? 4 : (M >= 3 ? 2 : 1);
+  for (; R > 1; R /= 2) {
+    const int lg = choose_lgS(count, N, K, G, R);
+    const int64_t tiles = count * ((N + 16 * R - 1) / (16 * R));
+    if ((tiles + (kWaves >> lg) - 1) / (kWaves >> lg) >= 192) break;
+  }
+  const int lgS = choose_lgS(count, N, K, G, R);
   const int64_t ngw = ((K / G) + (1 << lgS) - 1) >> lgS;  // group iterations per chunk
-  if (ngw <= 4)
-    hipLaunchKernelGGL((gemv_kernel<G, 4>), dim3(grid), dim3(kThreads), 0, stream, args, count,
-                       (int)M, (int)N, (int)K, lgS, nchunks, ldy, d_status);
+  if (R == 4)
+    launch_with<G, 4, 4>(args, count, M, N, K, ldy, lgS, d_status, stream);
+  else if (R == 2 && ngw <= 4)
+    launch_with<G, 4, 2>(args, count, M, N, K, ldy, lgS, d_status, stream);
+  else if (R == 2)
+    launch_with<G, 8, 2>(args, count, M, N, K, ldy, lgS, d_status, stream);
+  else if (ngw <= 4)
+    launch_with<G, 4, 1>(args, count, M, N, K, ldy, lgS, d_status, stream);
   else if (ngw <= 8)
-    hipLaunchKernelGGL((gemv_kernel<G, 8>), dim3(grid), dim3(kThreads), 0, stream, args, count,
-                       (int)M, (int)N, (int)K, lgS, nchunks, ldy, d_status);
+    launch_with<G, 8, 1>(args, count, M, N, K, ldy, lgS, d_status, stream);
   else
-    hipLaunchKernelGGL((gemv_kernel<G, 16>), dim3(grid), dim3(kThreads), 0, stream, args, count,
-                       (int)M, (int)N, (int)K, lgS, nchunks, ldy, d_status);
+    launch_with<G, 16, 1>(args, count, M, N, K, ldy, lgS, d_status, stream);
 }
 
 constexpr int64_t kChunkRows = int64_t(1) << 24;  // weight rows per launch
