@@ -176,9 +176,7 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
   constexpr int LPG = G / 8;               // lanes per group
   constexpr int GPC = 512 / G;             // groups per chunk
   constexpr int B = bytes_per_group(G);    // bytes per group
-  constexpr int CB = GPC * B;              // bytes per chunk (104)
   constexpr int LOG2G = (G == 64) ? 6 : 7;
-  __shared__ __align__(16) uint8_t digits_s[kWavesPerBlock][512];
 
   const int lane = threadIdx.x & (kWave - 1);
   const int wv = threadIdx.x / kWave;
@@ -384,29 +382,28 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
       continue;
     }
 
-    __syncthreads();  // previous iteration's readers are done with digits_s
-    *reinterpret_cast<uint64_t *>(&digits_s[wv][lane * 8]) = dig;
-    __syncthreads();
-
-    // five digits per byte, base 3, first weight least significant
+    // Five digits a byte, base 3, first weight least significant.  Byte b of
+    // the group holds digits 5b .. 5b+4; the lane with 8 sub <= 5b < 8 sub + 8
+    // writes it (one or two bytes a lane, every byte once), from its own 8
+    // digits and the next lane's 8 (2-bit fields, one DPP shift within the
+    // group's lanes; past the group's last lane the padding digits are 1,
+    // code 0).
+    uint32_t mine = 0;
 #pragma unroll
-    for (int pass = 0; pass < 2; ++pass) {
-      const int j = lane + pass * kWave;
-      if (j < CB) {
-        const int q = j / B, b = j % B;
-        const int64_t gq = chunk * GPC + q;
-        if (chunk < nchunks && gq < total_groups) {
-          uint32_t byte = 0, p3 = 1;
-#pragma unroll
-          for (int i = 0; i < 5; ++i) {
-            const int pos = 5 * b + i;
-            const uint32_t d = pos < G ? digits_s[wv][q * G + pos] : 1u;
-            byte += d * p3;
-            p3 *= 3;
-          }
-          packed[gq * B + b] = (uint8_t)byte;
-        }
-      }
+    for (int i = 0; i < 8; ++i) mine |= (uint32_t)((dig >> (8 * i)) & 3u) << (2 * i);
+    const uint32_t from_next =
+        (uint32_t)__builtin_amdgcn_update_dpp((int)0x5555, (int)mine, 0x101, 0xF, 0xF, false);
+    const uint32_t win = mine | ((sub == LPG - 1 ? 0x5555u : from_next) << 16);
+    const int b0 = (8 * sub + 4) / 5;  // the lane's first byte
+    const int p0 = 5 * b0 - 8 * sub;   // its first digit in the window: 0..4
+    auto byte_at = [&](int p) {
+      const uint32_t x = win >> (2 * p);
+      return (x & 3u) + 3u * ((x >> 2) & 3u) + 9u * ((x >> 4) & 3u) + 27u * ((x >> 6) & 3u) +
+             81u * ((x >> 8) & 3u);
+    };
+    if (active) {
+      packed[gi * B + b0] = (uint8_t)byte_at(p0);
+      if (p0 <= 2) packed[gi * B + b0 + 1] = (uint8_t)byte_at(p0 + 5);
     }
     if (active && sub == 0) {
       scales[gi] = (uint16_t)sbits;
