@@ -144,15 +144,17 @@ __device__ __forceinline__ uint64_t shfl_xor_u64(uint64_t v, int mask) {
 
 // ---------------------------------------------------------------------------
 // quantize + pack.
-// A wave handles a chunk of 512 consecutive weights (= 512/G whole groups,
+// A wave handles a chunk of 2048 consecutive weights (= 2048/G whole groups,
 // since the flat group index n*(K/G) + g addresses w at (n*(K/G) + g) * G).
-// Each lane loads 8 bf16 with one 128-bit load; G/8 lanes share a group and
-// combine their exponent maxima, fixed-point sums and flags with xor
-// shuffles.  Digits go through LDS to be regrouped five per byte.
+// Each lane loads 32 bf16 with four 128-bit loads; G/32 lanes (4 or 2) share
+// a group and combine their sums, maxima and flags with DPP moves and xor
+// shuffles.  Magnitudes and codes are worked two weights a dword with packed
+// 16-bit integer operations; digits d = c + 1 are held one a byte.
 //
-// FAKE: the QAT forward instead.  Each lane writes its own 8 weights'
-// w_hat = bf16(c * s) where it read them (no LDS, no barrier), and the
-// scales are written only if `scales` is not null.
+// MODE kPack3: bytes of five base-3 digits, each formed by the lane whose
+// digits it starts in (a dot product of four digit bytes with 1, 3, 9, 27
+// plus 81 times the fifth).  kPack2: four 2-bit fields a byte.  The QAT
+// forward (w_hat = bf16(c * s)) is fake_quantize_kernel below.
 // ---------------------------------------------------------------------------
 // Problems of one launch (blockIdx.y picks one), all of one shape.
 struct QuantBatch {
@@ -162,8 +164,15 @@ struct QuantBatch {
   uint16_t *w_hat[kQuantMaxBatch];
 };
 
-// MODE: kPack3 (base-3 bytes), kFake (QAT forward), kPack2 (2-bit fields).
-constexpr int kPack3 = 0, kFake = 1, kPack2 = 2;
+constexpr int kWPL = 32;             // weights per lane
+constexpr int kChunk = kWave * kWPL;  // weights per wave and chunk
+
+typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+__device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
+__device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
+
+// MODE: kPack3 (base-3 bytes), kPack2 (2-bit fields).
+constexpr int kPack3 = 0, kPack2 = 2;
 
 template <int G, int MODE>
 __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch args,
@@ -172,10 +181,254 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
   const uint16_t *__restrict__ w = args.w[blockIdx.y];
   uint8_t *__restrict__ packed = args.packed[blockIdx.y];
   uint16_t *__restrict__ scales = args.scales[blockIdx.y];
+  constexpr int LPG = G / kWPL;            // lanes per group: 4 or 2
+  constexpr int GPC = kChunk / G;          // groups per chunk
+  constexpr int B = bytes_per_group(G);    // bytes per group
+  constexpr int LOG2G = (G == 64) ? 6 : 7;
+
+  const int lane = threadIdx.x & (kWave - 1);
+  const int wv = threadIdx.x / kWave;
+  const int sub = lane % LPG;
+  const int qg = lane / LPG;
+  const int64_t nchunks = (total_groups + GPC - 1) / GPC;
+
+  for (int64_t base = (int64_t)blockIdx.x * kWavesPerBlock; base < nchunks;
+       base += (int64_t)gridDim.x * kWavesPerBlock) {
+    const int64_t chunk = base + wv;
+    const int64_t gi = chunk * GPC + qg;
+    const bool active = chunk < nchunks && gi < total_groups;
+
+    uint32_t raw[16];
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (active) v = reinterpret_cast<const uint4 *>(w + gi * G + sub * kWPL)[i];
+      raw[4 * i] = v.x; raw[4 * i + 1] = v.y; raw[4 * i + 2] = v.z; raw[4 * i + 3] = v.w;
+    }
+    // magnitudes, two a dword (sign bits cleared)
+    uint32_t m2[16];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) m2[i] = raw[i] & 0x7FFF7FFFu;
+
+    // Fast path.  The sum of |w| in fp32: each lane adds its 32 magnitudes in
+    // a fixed tree (depth 5), then an xor butterfly over the group's LPG lanes
+    // (fp32 addition commutes, so every lane ends with the same sum S_hat).
+    // Along any path there are at most 5 + log2(LPG) <= 7 rounded additions
+    // of non-negative terms, so |S_hat - S| <= 7 * 2^-24 * S, plus at most
+    // G * 2^-126 should subnormals be flushed.  With E = 2^-19 S_hat + 2^-118
+    // the exact sum lies in [S_hat - E, S_hat + E] even after the rounding of
+    // those two operations; when both ends, divided by G, round to the same
+    // fp16 value, so does the exact mean (rounding is monotonic).  Otherwise
+    // the group takes the exact path below.
+    float f[32];
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      f[2 * i] = __uint_as_float(m2[i] << 16);
+      f[2 * i + 1] = __uint_as_float(m2[i] & 0xFFFF0000u);
+    }
+#pragma unroll
+    for (int st = 1; st < 32; st <<= 1)
+#pragma unroll
+      for (int i = 0; i < 32; i += 2 * st) f[i] += f[i + st];
+    float acc = f[0];
+    u16x2 mx = as_u16x2(m2[0]);
+#pragma unroll
+    for (int i = 1; i < 16; ++i) mx = __builtin_elementwise_max(mx, as_u16x2(m2[i]));
+    uint32_t maxmag = mx.x > mx.y ? mx.x : mx.y;
+    auto step = [&](auto k) {
+      acc += __uint_as_float(dpp_partner<decltype(k)::value>(__float_as_uint(acc)));
+      const uint32_t o = dpp_partner<decltype(k)::value>(maxmag);
+      maxmag = o > maxmag ? o : maxmag;
+    };
+    step(std::integral_constant<int, 0>{});
+    if constexpr (LPG == 4) step(std::integral_constant<int, 1>{});
+    uint32_t sbits = 0;
+    int flags = 0;
+    bool slow = false;
+    if (maxmag >= 0x7F80u) {  // an Inf or NaN weight
+      sbits = 0x7E00;
+      flags = kDevNonfinite;
+    } else {
+      const float E = fmaf(acc, 0x1p-19f, 0x1p-118f);
+      constexpr float kInvG = 1.0f / G;
+      const uint32_t qlo = __half_as_ushort(__float2half_rn(fmaxf(acc - E, 0.f) * kInvG));
+      const uint32_t qhi = __half_as_ushort(__float2half_rn((acc + E) * kInvG));
+      if (qlo == qhi) {
+        sbits = qlo;
+        if (sbits >= 0x7C00u) {
+          sbits = 0x7C00;
+          flags = kDevScaleOverflow;
+        }
+      } else {
+        slow = true;
+      }
+    }
+
+    // Exact path, taken by the whole wave when one of its groups needs it
+    // (its shuffles need every lane): a fixed-point sum anchored at the
+    // group's largest exponent (that of its largest magnitude), and the
+    // 320-bit sum when that window is not enough.
+    if (__any(slow)) {
+      const uint32_t sbits_fast = sbits;
+      const int flags_fast = flags;
+      const uint32_t Emax = maxmag >> 7;  // group maximum, after the butterfly
+      const int emax = Emax ? (int)Emax - 1 : 0;
+      const bool nonfinite = Emax == 0xFFu;
+
+      // fixed-point sum anchored at emax
+      uint64_t T = 0;
+      uint32_t inexact = 0;
+#pragma unroll
+      for (int i = 0; i < 32; ++i) {
+        const uint32_t u = (i & 1) ? (m2[i >> 1] >> 16) : (m2[i >> 1] & 0xFFFFu);
+        const uint32_t E = u >> 7;
+        const uint64_t sig = E ? 128u + (u & 0x7Fu) : (u & 0x7Fu);
+        const int e = E ? (int)E - 1 : 0;
+        const int sh = e - emax + kWin;
+        if (sh >= 0) {
+          T += sig << sh;
+        } else if (sh > -8) {
+          T += sig >> (-sh);
+          inexact |= (sig & ((1ull << (-sh)) - 1)) != 0;
+        } else {
+          inexact |= sig != 0;
+        }
+      }
+#pragma unroll
+      for (int m = 1; m < LPG; m <<= 1) {
+        T += shfl_xor_u64(T, m);
+        inexact |= shfl_xor_u32(inexact, m);
+      }
+
+      // one rounding of the mean to fp16; the true sum lies in [T, T + G) units
+      // of 2^(emax - 181) and the mean in units of 2^-24 is that times
+      // 2^(emax - 157 - log2 G)
+      sbits = 0;
+      flags = 0;
+      bool need_exact = false;
+      if (nonfinite) {
+        sbits = 0x7E00;
+        flags = kDevNonfinite;
+      } else {
+        const int sh = emax - 157 - LOG2G;
+        bool ovf;
+        sbits = f16_bits_of_fixed(T, sh, &ovf);
+        if (inexact) {
+          bool ovf2;
+          const uint32_t hi = f16_bits_of_fixed(T + (uint64_t)G, sh, &ovf2);
+          need_exact = hi != sbits;
+        }
+        if (ovf && !need_exact) flags = kDevScaleOverflow;
+      }
+      if (need_exact && active && sub == 0) {
+        bool ovf;
+        sbits = f16_scale_exact(w + gi * G, G, LOG2G, &ovf);
+        flags = ovf ? kDevScaleOverflow : 0;
+      }
+      const int leader = qg * LPG;
+      sbits = (uint32_t)__shfl((int)sbits, leader, kWave);
+      flags = __shfl(flags, leader, kWave);
+      if (!slow) {
+        sbits = sbits_fast;
+        flags = flags_fast;
+      }
+    }
+
+    // Codes: |w| > s/2, decided on bit patterns.  For a bf16 magnitude m
+    // (fp32 bits m << 16) and the fp32 bits H of s/2, (m << 16) > H exactly
+    // when m > H >> 16, so two weights are compared at once as 16-bit halves
+    // (a saturating subtraction is non-zero exactly when m > H >> 16).  The
+    // digit is 1 + t - 2 t sign with t = [m > H >> 16]; flagged groups keep
+    // every digit at 1 (code 0).
+    const uint32_t half_bits =
+        __float_as_uint(__half2float(__ushort_as_half((unsigned short)sbits)) * 0.5f);
+    const u16x2 hb = as_u16x2((half_bits >> 16) * 0x00010001u);
+    const u16x2 one = as_u16x2(0x00010001u);
+    uint32_t d2[16];  // digits 2i, 2i+1 in the low bytes of the halves
+#pragma unroll
+    for (int i = 0; i < 16; ++i) {
+      const u16x2 t = __builtin_elementwise_min(
+          __builtin_elementwise_sub_sat(as_u16x2(m2[i]), hb), one);
+      const u16x2 sg = as_u16x2((raw[i] >> 15) & 0x00010001u);
+      const u16x2 ts = t & sg;
+      d2[i] = flags ? 0x00010001u : as_u32(one + t - (ts + ts));
+    }
+    uint32_t db[9];  // digits as bytes: db[j] holds digits 4j .. 4j+3
+#pragma unroll
+    for (int j = 0; j < 8; ++j) db[j] = __builtin_amdgcn_perm(d2[2 * j + 1], d2[2 * j], 0x06040200u);
+
+    if constexpr (MODE == kPack2) {
+      // four 2-bit fields d = c + 1 a byte, first weight lowest: this lane's
+      // 32 weights are 8 bytes of the group's G/4, stored as four halves
+      // (the buffer is 2-byte aligned)
+      uint32_t by[8];
+#pragma unroll
+      for (int j = 0; j < 8; ++j) by[j] = __builtin_amdgcn_udot4(db[j], 0x40100401u, 0u, false);
+      if (active) {
+        uint16_t *dst = reinterpret_cast<uint16_t *>(packed + gi * (G / 4) + sub * 8);
+#pragma unroll
+        for (int h = 0; h < 4; ++h) dst[h] = (uint16_t)(by[2 * h] | (by[2 * h + 1] << 8));
+        if (sub == 0) {
+          scales[gi] = (uint16_t)sbits;
+          if (flags && d_status) atomicOr(d_status, flags);
+        }
+      }
+      continue;
+    }
+    // Five digits a byte, base 3, first weight least significant.  Byte b of
+    // the group holds digits 5b .. 5b+4 and is written by the lane with
+    // 32 sub <= 5b < 32 sub + 32 (6 or 7 bytes a lane, every byte once).  Its
+    // last byte reaches up to 4 digits into the next lane's, fetched by one
+    // DPP shift within the group's lanes; past the group's last lane they are
+    // padding digits 1 (code 0).  The lane's window is first shifted by p0
+    // digits so that its own bytes start at window digit 0.
+    const uint32_t next =
+        (uint32_t)__builtin_amdgcn_update_dpp((int)0x01010101, (int)db[0], 0x101, 0xF, 0xF, false);
+    db[8] = sub == LPG - 1 ? 0x01010101u : next;
+    const int b0 = (kWPL * sub + 4) / 5;           // the lane's first byte
+    const uint32_t p0 = (uint32_t)(5 * b0 - kWPL * sub);  // its first digit: 0..4
+    const int nb = (kWPL * sub + kWPL - 1) / 5 - b0 + 1;  // its bytes: 6 or 7
+    // (alignbyte shifts by 0..3 bytes; a shift of 4 is the next dword)
+    uint32_t wd[9];
+#pragma unroll
+    for (int j = 0; j < 8; ++j)
+      wd[j] = p0 == 4u ? db[j + 1] : __builtin_amdgcn_alignbyte(db[j + 1], db[j], p0);
+    wd[8] = p0 == 4u ? 0x01010101u : __builtin_amdgcn_alignbyte(0x01010101u, db[8], p0);
+    if (active) {
+#pragma unroll
+      for (int k = 0; k < 7; ++k) {
+        const int q0 = 5 * k;  // window digit of the byte's first digit
+        const uint32_t four = (q0 & 3) ? __builtin_amdgcn_alignbyte(wd[(q0 >> 2) + 1], wd[q0 >> 2],
+                                                                    (uint32_t)(q0 & 3))
+                                       : wd[q0 >> 2];
+        const uint32_t fifth = (wd[(q0 + 4) >> 2] >> (8 * ((q0 + 4) & 3))) & 0xFFu;
+        const uint32_t byte = __builtin_amdgcn_udot4(four, 0x1B090301u, 81u * fifth, false);
+        if (k < nb) packed[gi * B + b0 + k] = (uint8_t)byte;
+      }
+      if (sub == 0) {
+        scales[gi] = (uint16_t)sbits;
+        if (flags && d_status) atomicOr(d_status, flags);
+      }
+    }
+  }
+}
+
+// The QAT forward on 8 weights a lane (G/8 lanes a group, one 16-byte load
+// and one 16-byte store each, so a wave's loads and stores are contiguous):
+// the same scale computation as quantize_pack_kernel (an fp32 sum over an
+// in-order chain of 8 and a butterfly over the group's lanes, the exact path
+// when the interval test fails), then w_hat = bf16(c * s) written where the
+// weights were read.  Its writes are as large as its reads, and 16-byte lanes
+// 64 bytes apart (32 weights a lane) made it 12% slower.
+template <int G>
+__global__ __launch_bounds__(kBlock) void fake_quantize_kernel(const QuantBatch args,
+                                                               int64_t total_groups,
+                                                               int32_t *__restrict__ d_status) {
+  const uint16_t *__restrict__ w = args.w[blockIdx.y];
+  uint16_t *__restrict__ scales = args.scales[blockIdx.y];
   uint16_t *__restrict__ w_hat = args.w_hat[blockIdx.y];
   constexpr int LPG = G / 8;               // lanes per group
   constexpr int GPC = 512 / G;             // groups per chunk
-  constexpr int B = bytes_per_group(G);    // bytes per group
   constexpr int LOG2G = (G == 64) ? 6 : 7;
 
   const int lane = threadIdx.x & (kWave - 1);
@@ -343,22 +596,7 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
       dig |= (uint64_t)d << (8 * i);
     }
 
-    if constexpr (MODE == kPack2) {
-      // four 2-bit fields d = c + 1 a byte, first weight lowest: this lane's
-      // 8 weights are 2 bytes of the group's G/4
-      uint32_t v = 0;
-#pragma unroll
-      for (int i = 0; i < 8; ++i) v |= (uint32_t)((dig >> (8 * i)) & 3u) << (2 * i);
-      if (active) {
-        *reinterpret_cast<uint16_t *>(packed + gi * (G / 4) + sub * 2) = (uint16_t)v;
-        if (sub == 0) {
-          scales[gi] = (uint16_t)sbits;
-          if (flags && d_status) atomicOr(d_status, flags);
-        }
-      }
-      continue;
-    }
-    if constexpr (MODE == kFake) {
+    {
       // w_hat of the 8 weights: a pair takes bytes 2d, 2d+1 of {hi, lo}
       // per digit d (0..1 is -s, 2..3 +0, 4..5 +s); a flagged group is +0
       const uint32_t sb = flags ? 0u : bf16_of_f16(sbits);
@@ -379,38 +617,11 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
           if (flags && d_status) atomicOr(d_status, flags);
         }
       }
-      continue;
     }
 
-    // Five digits a byte, base 3, first weight least significant.  Byte b of
-    // the group holds digits 5b .. 5b+4; the lane with 8 sub <= 5b < 8 sub + 8
-    // writes it (one or two bytes a lane, every byte once), from its own 8
-    // digits and the next lane's 8 (2-bit fields, one DPP shift within the
-    // group's lanes; past the group's last lane the padding digits are 1,
-    // code 0).
-    uint32_t mine = 0;
-#pragma unroll
-    for (int i = 0; i < 8; ++i) mine |= (uint32_t)((dig >> (8 * i)) & 3u) << (2 * i);
-    const uint32_t from_next =
-        (uint32_t)__builtin_amdgcn_update_dpp((int)0x5555, (int)mine, 0x101, 0xF, 0xF, false);
-    const uint32_t win = mine | ((sub == LPG - 1 ? 0x5555u : from_next) << 16);
-    const int b0 = (8 * sub + 4) / 5;  // the lane's first byte
-    const int p0 = 5 * b0 - 8 * sub;   // its first digit in the window: 0..4
-    auto byte_at = [&](int p) {
-      const uint32_t x = win >> (2 * p);
-      return (x & 3u) + 3u * ((x >> 2) & 3u) + 9u * ((x >> 4) & 3u) + 27u * ((x >> 6) & 3u) +
-             81u * ((x >> 8) & 3u);
-    };
-    if (active) {
-      packed[gi * B + b0] = (uint8_t)byte_at(p0);
-      if (p0 <= 2) packed[gi * B + b0 + 1] = (uint8_t)byte_at(p0 + 5);
-    }
-    if (active && sub == 0) {
-      scales[gi] = (uint16_t)sbits;
-      if (flags && d_status) atomicOr(d_status, flags);
-    }
   }
 }
+
 
 // ---------------------------------------------------------------------------
 // unpack: one thread per 16 consecutive codes of a group (G % 16 == 0), one
@@ -511,8 +722,10 @@ void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64
                           uint16_t *const *w_hats, int32_t *d_status, hipStream_t stream,
                           bool two_bit) {
   const int64_t total_groups = N * (K / G);
-  const int64_t nchunks = (total_groups * G + 511) / 512;
   const bool fake = w_hats != nullptr;
+  // chunks of 2048 weights a wave (packing) or 512 (the QAT forward)
+  const int64_t per = fake ? 512 : kChunk;
+  const int64_t nchunks = (total_groups * G + per - 1) / per;
   for (int c0 = 0; c0 < count; c0 += kQuantMaxBatch) {
     const int n = count - c0 < kQuantMaxBatch ? count - c0 : kQuantMaxBatch;
     QuantBatch a{};
@@ -523,22 +736,21 @@ void launch_quant_batched(int count, const uint16_t *const *ws, int64_t N, int64
       a.w_hat[i] = fake ? w_hats[c0 + i] : nullptr;
     }
     const dim3 grid(grid_for(nchunks, kWavesPerBlock, kMaxBlocks / n), n);
-    const int mode = fake ? kFake : (two_bit ? kPack2 : kPack3);
     if (G == 64) {
-      if (mode == kFake)
-        hipLaunchKernelGGL((quantize_pack_kernel<64, kFake>), grid, dim3(kBlock), 0, stream, a,
+      if (fake)
+        hipLaunchKernelGGL((fake_quantize_kernel<64>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
-      else if (mode == kPack2)
+      else if (two_bit)
         hipLaunchKernelGGL((quantize_pack_kernel<64, kPack2>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
       else
         hipLaunchKernelGGL((quantize_pack_kernel<64, kPack3>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
     } else {
-      if (mode == kFake)
-        hipLaunchKernelGGL((quantize_pack_kernel<128, kFake>), grid, dim3(kBlock), 0, stream, a,
+      if (fake)
+        hipLaunchKernelGGL((fake_quantize_kernel<128>), grid, dim3(kBlock), 0, stream, a,
                            total_groups, d_status);
-      else if (mode == kPack2)
+      else if (two_bit)
         hipLaunchKernelGGL((quantize_pack_kernel<128, kPack2>), grid, dim3(kBlock), 0, stream,
                            a, total_groups, d_status);
       else
