@@ -192,19 +192,30 @@ __global__ __launch_bounds__(kBlock) void quantize_pack_kernel(const QuantBatch 
   const int qg = lane / LPG;
   const int64_t nchunks = (total_groups + GPC - 1) / GPC;
 
-  for (int64_t base = (int64_t)blockIdx.x * kWavesPerBlock; base < nchunks;
-       base += (int64_t)gridDim.x * kWavesPerBlock) {
+  // the next chunk's weights are loaded before this chunk's work
+  const int64_t bstep = (int64_t)gridDim.x * kWavesPerBlock;
+  uint32_t nraw[16];
+  auto load_chunk = [&](int64_t base) {
+    const int64_t chunk = base + wv;
+    const int64_t gi = chunk * GPC + qg;
+    const bool on = chunk < nchunks && gi < total_groups;
+#pragma unroll
+    for (int i = 0; i < 4; ++i) {
+      uint4 v = make_uint4(0u, 0u, 0u, 0u);
+      if (on) v = reinterpret_cast<const uint4 *>(w + gi * G + sub * kWPL)[i];
+      nraw[4 * i] = v.x; nraw[4 * i + 1] = v.y; nraw[4 * i + 2] = v.z; nraw[4 * i + 3] = v.w;
+    }
+  };
+  load_chunk((int64_t)blockIdx.x * kWavesPerBlock);
+  for (int64_t base = (int64_t)blockIdx.x * kWavesPerBlock; base < nchunks; base += bstep) {
     const int64_t chunk = base + wv;
     const int64_t gi = chunk * GPC + qg;
     const bool active = chunk < nchunks && gi < total_groups;
 
     uint32_t raw[16];
 #pragma unroll
-    for (int i = 0; i < 4; ++i) {
-      uint4 v = make_uint4(0u, 0u, 0u, 0u);
-      if (active) v = reinterpret_cast<const uint4 *>(w + gi * G + sub * kWPL)[i];
-      raw[4 * i] = v.x; raw[4 * i + 1] = v.y; raw[4 * i + 2] = v.z; raw[4 * i + 3] = v.w;
-    }
+    for (int i = 0; i < 16; ++i) raw[i] = nraw[i];
+    if (base + bstep < nchunks) load_chunk(base + bstep);
     // magnitudes, two a dword (sign bits cleared)
     uint32_t m2[16];
 #pragma unroll
