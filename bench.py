@@ -39,7 +39,8 @@ of launches between HIP events on the same stream, median of three):
   dense8b      8B-class FFN matrices W[14336,4096] and W[4096,14336], G = 128,
                decode at M = 1, 4, 16 over a ring of copies (>= 1 GiB)
   dequant      decode to bf16 of every matrix of a slot (two launches per slot)
-  gemv2        the decode pass over the 2-bit format (one grouped launch)
+  gemv2        the decode pass over the 2-bit format (one grouped launch), and the
+               2-bit prefill matmul at --prefill-m rows (one launch per shape)
   w4a16        the decode pass over seeded W4A16 parameters (one grouped launch), and
                the W4A16 prefill matmul at --prefill-m rows (one launch per shape)
   qat          the QAT forward of the stack from bf16 and from fp32 latent
@@ -650,6 +651,28 @@ class Bench:
             "ms": ms, "GB/s": b / (ms * 1e-3) / 1e9, "frac_hbm": b / (ms * 1e-3) / 1e9 / HBM_PEAK_GBS,
             "Tweights/s": self.weights / (ms * 1e-3) / 1e12, "bytes_per_pass": b, "launches": 1,
             "in_step": False}
+        # the 2-bit prefill matmul on the matrix cores: one tq_gemm2_batched launch per shape
+        MP = self.args.prefill_m
+        xs = {K: self.bf16(self.inputs.prefill_activation(MP, K))
+              for K in sorted({k for _, k in self.shapes})}
+        yp = [torch.empty(MP, N, dtype=torch.float32, device=self.dev) for N, K in self.shapes]
+        pcalls = [(N, K, len(idx), self.ptrs([xs[K]] * len(idx)),
+                   self.ptrs([slots[0][i][0] for i in idx]), self.ptrs([slots[0][i][1] for i in idx]),
+                   self.ptrs([yp[i] for i in idx])) for (N, K), idx in self.groups.items()]
+
+        def run_mm(_):
+            for N, K, n, ax, ap, asc, ay in pcalls:
+                self.ok(L.tq_gemm2_batched(n, ax, ap, asc, ay, MP, N, K, G, self.stp, self.sp))
+
+        ms2 = self.chain(run_mm, 2)
+        self.captured["gemm2_y"] = {i: yp[i][:8].cpu().numpy() for i in (0, 71)}
+        flops = sum(2.0 * MP * N * K for N, K in self.shapes)
+        tf = flops / (ms2 * 1e-3) / 1e12
+        self.rows["prefill_gemm_2bit"] = {
+            "config": "72-matrix FFN stack, 2-bit G=%d, M=%d, one tq_gemm2_batched launch per shape"
+                      % (G, MP),
+            "ms": ms2, "TFLOP/s": tf, "frac_mfma": tf / MFMA_BF16_PEAK_TFLOPS, "launches": 2,
+            "in_step": False, "timing": "median of 3 chains of 2 passes"}
 
     # ---- W4A16 ----
     def row_w4a16(self):
@@ -964,6 +987,11 @@ def cpu_baseline(b, min_s):
             exact(cap["gemv2_packed"][i], p2, "2-bit packed bytes, matrix %d" % i)
             y_ref, bound, _ = oracle.matmul2(b.x_dec_host[i], p2, s2, N, K, G, threads=nt)
             within(cap["gemv2_y"][i], y_ref, bound, "2-bit decode GEMV, matrix %d" % i)
+            if "gemm2_y" in cap:
+                xp = b.inputs.prefill_activation(b.args.prefill_m, K)[:8]
+                y_ref, bound, _ = oracle.matmul2(xp, p2, s2, N, K, G, threads=nt)
+                within(cap["gemm2_y"][i], y_ref, bound,
+                       "2-bit prefill GEMM M=%d rows 0-7, matrix %d" % (b.args.prefill_m, i))
     if "w4a16" in cap:
         for i in (0, 71):
             N, K = shapes[i]
