@@ -111,6 +111,9 @@ __device__ __attribute__((noinline)) uint32_t range_has_invalid_byte(__amdgpu_bu
 
 constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range: loads give 0
 constexpr int kRing = 4;  // row batches in flight per lane
+// Cache policy of the loads of packed weights and their group parameters:
+// nontemporal (gfx950's nt bit), since every byte is read once.
+constexpr int kStreamed = 2;
 constexpr int kMaxBatch = 128;  // problems per launch (6.5 KB of kernel arguments)
 
 // Up to kMaxBatch same-shaped problems per launch, passed by value.
@@ -243,13 +246,14 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
       const uint32_t pb = (uint32_t)bu * bstep, sb = (uint32_t)bu * sstep;
       const __amdgpu_buffer_rsrc_t rpb = make_rsrc(pk8 + pb, onu ? pbytes - pb : 0u);
       const __amdgpu_buffer_rsrc_t rsb = make_rsrc(sc8 + sb, onu ? sbytes_al - sb : 0u);
-      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rpb, a0al, 0, 0);
-      rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rsb, s0al, 0, 0);
+      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rpb, a0al, 0, kStreamed);
+      rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(rsb, s0al, 0, kStreamed);
     } else {
       const uint32_t a = a0 + (uint32_t)b * bstep;
-      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, on ? (a & ~3u) : kOutOfRange, 0, 0);
+      ring[slot] = __builtin_amdgcn_raw_buffer_load_b128(rp, on ? (a & ~3u) : kOutOfRange, 0,
+                                                         kStreamed);
       rsc[slot] = __builtin_amdgcn_raw_buffer_load_b32(
-          rs, on ? ((shead + s0 + (uint32_t)b * sstep) & ~3u) : kOutOfRange, 0, 0);
+          rs, on ? ((shead + s0 + (uint32_t)b * sstep) & ~3u) : kOutOfRange, 0, kStreamed);
     }
   };
 #pragma unroll

@@ -168,6 +168,20 @@ constexpr int kWPL = 32;             // weights per lane
 constexpr int kChunk = kWave * kWPL;  // weights per wave and chunk
 
 typedef unsigned short u16x2 __attribute__((ext_vector_type(2)));
+typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
+
+// Nontemporal loads and stores, for data used once where each instruction
+// covers whole cache lines (a wave's 16-byte accesses contiguous).  The
+// quantize kernel's weight loads stay cached: each of its four loads reads a
+// quarter of the same lines, and nontemporal loads there fetched them again.
+__device__ __forceinline__ uint4 load_streamed(const void *p) {
+  const u32x4 v = __builtin_nontemporal_load(reinterpret_cast<const u32x4 *>(p));
+  return make_uint4(v.x, v.y, v.z, v.w);
+}
+__device__ __forceinline__ void store_streamed(void *p, uint32_t a, uint32_t b, uint32_t c,
+                                               uint32_t d) {
+  __builtin_nontemporal_store(u32x4{a, b, c, d}, reinterpret_cast<u32x4 *>(p));
+}
 __device__ __forceinline__ u16x2 as_u16x2(uint32_t v) { return __builtin_bit_cast(u16x2, v); }
 __device__ __forceinline__ uint32_t as_u32(u16x2 v) { return __builtin_bit_cast(uint32_t, v); }
 
@@ -456,7 +470,7 @@ __global__ __launch_bounds__(kBlock) void fake_quantize_kernel(const QuantBatch 
 
     uint32_t raw[4] = {0, 0, 0, 0};
     if (active) {
-      const uint4 v = *reinterpret_cast<const uint4 *>(w + gi * G + sub * 8);
+      const uint4 v = load_streamed(w + gi * G + sub * 8);
       raw[0] = v.x; raw[1] = v.y; raw[2] = v.z; raw[3] = v.w;
     }
     uint32_t h[8];
@@ -621,8 +635,7 @@ __global__ __launch_bounds__(kBlock) void fake_quantize_kernel(const QuantBatch 
         out[k] = __builtin_amdgcn_perm(hi, lo, pair * 0x0202u + 0x01000100u);
       }
       if (active) {
-        *reinterpret_cast<uint4 *>(w_hat + gi * G + sub * 8) =
-            make_uint4(out[0], out[1], out[2], out[3]);
+        store_streamed(w_hat + gi * G + sub * 8, out[0], out[1], out[2], out[3]);
         if (sub == 0) {
           if (scales) scales[gi] = (uint16_t)sbits;
           if (flags && d_status) atomicOr(d_status, flags);
@@ -708,7 +721,7 @@ __global__ __launch_bounds__(kBlock) void unpack_kernel(const UnpackBatch args, 
       }
       int8_t *dst = codes + gi * G + p0;
       if (a16) {
-        *reinterpret_cast<uint4 *>(dst) = make_uint4(out[0], out[1], out[2], out[3]);
+        store_streamed(dst, out[0], out[1], out[2], out[3]);
       } else {  // codes only 8-byte aligned (the ABI's minimum)
         reinterpret_cast<uint2 *>(dst)[0] = make_uint2(out[0], out[1]);
         reinterpret_cast<uint2 *>(dst)[1] = make_uint2(out[2], out[3]);

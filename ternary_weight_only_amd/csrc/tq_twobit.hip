@@ -33,6 +33,9 @@ constexpr int kRing = 4;                  // row steps in flight per lane
 constexpr int kFlush = 16;                // rounds of results held in LDS per wave
 constexpr int kResCap = kFlush * kRing * 4;  // floats a wave (at most 4 rows a step)
 constexpr uint32_t kOOR = 0x80000000u;   // a buffer offset past any range: loads give 0
+// Cache policy of the loads of packed weights and their group parameters:
+// nontemporal (gfx950's nt bit), since every byte is read once.
+constexpr int kStreamed = 2;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x2 __attribute__((ext_vector_type(2)));
@@ -140,9 +143,9 @@ __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) 
     const uint32_t row = (uint32_t)(r < N ? r : N - 1);
     ring[d] = __builtin_bit_cast(
         u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, lane_on ? row * rb + 16u * lr : kOOR, 0,
-                                                     0));
+                                                     kStreamed));
     const uint32_t so = 2u * (row * (uint32_t)nG + (uint32_t)(lr / CPG)) + shead;
-    rsc[d] = __builtin_amdgcn_raw_buffer_load_b32(rs_, lane_on ? (so & ~3u) : kOOR, 0, 0);
+    rsc[d] = __builtin_amdgcn_raw_buffer_load_b32(rs_, lane_on ? (so & ~3u) : kOOR, 0, kStreamed);
   };
 #pragma unroll
   for (int d = 0; d < kRing; ++d) issue(d, d);
@@ -256,7 +259,9 @@ __global__ __launch_bounds__(kBlock) void unpack2_kernel(const uint32_t *__restr
       y = (y | (y << 6)) & 0x03030303u;                     // one field a byte
       out[k] = __builtin_amdgcn_perm(0u, 0x000100FFu, y);   // -1, 0, +1; 3 -> 0
     }
-    *reinterpret_cast<uint4 *>(codes + 16 * t) = make_uint4(out[0], out[1], out[2], out[3]);
+    // nontemporal: the codes are written once and not read back here
+    __builtin_nontemporal_store(u32x4{out[0], out[1], out[2], out[3]},
+                                reinterpret_cast<u32x4 *>(codes + 16 * t));
   }
   if (flags && d_status) atomicOr(d_status, flags);
 }
