@@ -367,7 +367,8 @@ void gemm_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
   // no load may still be writing this block's LDS when it exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane>>4) + r ----
+  // ---- epilogue: lane holds column (lane & 15), rows 4*(lane>>4) + r; y is
+  // written with nontemporal stores (never read back here) ----
   const int mb = wm * 64 + 4 * (lane >> 4), nb = wn * 64 + (lane & 15);
   float *__restrict__ yl = args.y[pi] + (int64_t)(m0 + mb) * ldy + (n0 + nb);
   if (mrows == BM && nrows == BN) {
@@ -377,7 +378,7 @@ void gemm_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
       for (int r = 0; r < 4; ++r) {
         float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
 #pragma unroll
-        for (int b = 0; b < TN; ++b) yr[16 * b] = acc[a][b][r];
+        for (int b = 0; b < TN; ++b) __builtin_nontemporal_store(acc[a][b][r], yr + 16 * b);
       }
   } else {
 #pragma unroll
@@ -388,7 +389,7 @@ void gemm_kernel(const GemmBatch args, int M, int N, int K, int64_t ldy,
         float *__restrict__ yr = yl + (int64_t)(16 * a + r) * ldy;
 #pragma unroll
         for (int b = 0; b < TN; ++b)
-          if (nb + 16 * b < nrows) yr[16 * b] = acc[a][b][r];
+          if (nb + 16 * b < nrows) __builtin_nontemporal_store(acc[a][b][r], yr + 16 * b);
       }
   }
   if ((flags & kBadFlag) && drow_on && d_status) atomicOr(d_status, kDevInvalidByte);

@@ -242,7 +242,8 @@ __global__ __launch_bounds__(kThreads) void matmul2_mfma_kernel(const Mm2Batch a
   if (g + 1 < nG) group(Int<1>{}, g + 1);
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
 
-  // lane (j, q) holds rows 4q .. 4q+3 of column j of each 16 x 16 tile
+  // lane (j, q) holds rows 4q .. 4q+3 of column j of each 16 x 16 tile; y is
+  // written with nontemporal stores (never read back here)
   float *__restrict__ y = args.y[pi];
 #pragma unroll
   for (int a = 0; a < TM; ++a)
@@ -253,7 +254,7 @@ __global__ __launch_bounds__(kThreads) void matmul2_mfma_kernel(const Mm2Batch a
 #pragma unroll
       for (int r = 0; r < 4; ++r) {
         const int m = m0 + 16 * a + 4 * q + r;
-        if (m < M) y[(int64_t)m * N + n] = acc[a][t][r];
+        if (m < M) __builtin_nontemporal_store(acc[a][t][r], y + (int64_t)m * N + n);
       }
     }
   if (d_status && __builtin_amdgcn_ballot_w64(bad != 0) != 0 && lane == 0)
