@@ -77,7 +77,7 @@ ALL_ROWS = ("step", "gemv_g64", "gemm_m2048", "dense8b", "dequant", "gemv2", "w4
 # HBM bytes per GEMV launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this bench, each
 # scaled by the same counter on a 256 MiB copy (profiles/gemv_m1_hbm_traffic.md); valid only
 # for the kernel source they were taken on (sha256 prefix of csrc/tq_gemv_m1.hip).
-GEMV_TRAFFIC = {"8b2bbb06ced5cad3": 61144785}
+GEMV_TRAFFIC = {"26d5db229a6fc019": 61281585}
 
 
 def parse():
