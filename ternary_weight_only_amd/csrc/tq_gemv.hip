@@ -40,8 +40,9 @@
 // through LDS in a fixed order (deterministic results) and stored.  Within a
 // chunk a wave issues the packed bytes and scales of up to BR groups at
 // once, and the activations two groups ahead (see the main loop for why the
-// two streams are issued in that order).  The blocks are persistent (at most
-// two per CU, all resident at once) and take chunks b, b + grid, ...
+// two streams are issued in that order).  The blocks are persistent (one per
+// CU: the kernel takes up to 256 registers a lane at two waves a SIMD, so all
+// are resident at once) and take chunks b, b + grid, ...
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -60,7 +61,7 @@ constexpr uint32_t kOutOfRange = 0x80000000u;  // a buffer offset past any range
 constexpr int kMaxBatch = 64;      // problems per batched launch
 constexpr int kXLead = 2;          // group iterations of activations in flight per wave
 constexpr int kXBuf = 4;           // activation buffers (> kXLead)
-constexpr int kMaxBlocks = 512;    // two 8-wave blocks per CU
+constexpr int kMaxBlocks = 256;    // one 8-wave block per CU (two waves a SIMD)
 
 typedef __bf16 bf16x8 __attribute__((ext_vector_type(8)));
 typedef float f32x4 __attribute__((ext_vector_type(4)));
@@ -380,7 +381,7 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
 }
 
 // Chunk shape: the K split S (TB = 8 / S tiles a chunk).  The smallest S
-// whose chunks still fill three quarters of the resident blocks (two per
+// whose chunks still fill three quarters of the resident blocks (one per
 // CU), so each wave streams the longest runs of groups; every part keeps at
 // least one group.
 int choose_lgS(int count, int64_t N, int64_t K, int G, int R) {
