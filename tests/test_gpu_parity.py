@@ -192,6 +192,30 @@ def test_gemv_batched_matches_oracle(N, K, G, count):
     assert int(st.item()) & 4
 
 
+@pytest.mark.parametrize("M,count", [(2, 1), (5, 2)])
+def test_skinny_matmul_blocks_with_several_chunks(M, count):
+    """The skinny matmul (2 <= M <= 16) on tall matrices: 2500 tiles of 16 or
+    32 rows leave more chunks than the 256 persistent blocks, so blocks walk
+    two chunks; every output is checked, over one and two problems."""
+    import torch
+    import ternary_weight_only_amd as tq
+    from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
+    N, K, G = 40000, 512, 128
+    ws = [inputs.normal_bf16(500 + i, (N, K), 0.02) for i in range(count)]
+    refs = [oracle.quantize_pack(w, G) for w in ws]
+    xs = [inputs.activation(510 + i, M, K) for i in range(count)]
+    say("skinny matmul M=%d N=%d K=%d count=%d" % (M, N, K, count))
+    st = tq.new_status()
+    ys = tq.gemv_batched([dev_bf16(x) for x in xs], [dev_u8(p) for p, _, _ in refs],
+                         [dev_f16bits(s) for _, s, _ in refs], N, K, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == 0
+    for i in range(count):
+        p, s, _ = refs[i]
+        y_ref, bound, _ = oracle.matmul(xs[i], p, s, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "skinny M=%d problem %d" % (M, i))
+
+
 @pytest.mark.parametrize("G", [64, 128])
 @pytest.mark.parametrize("offset", [0, 1, 2, 3])
 def test_gemm_ragged_unaligned_packed_and_invalid_bytes(G, offset):
