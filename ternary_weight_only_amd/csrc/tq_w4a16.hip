@@ -10,10 +10,12 @@
 // b[n,g] sum_j x_j) over the group's j, accumulated in fp32 and rounded
 // once to bf16 ("Computation Flow").
 //
-// The GEMV: lane lr of a row owns weights 64 lr .. 64 lr + 63 (32 bytes,
-// inside one group for G = 64 or 128), read as two aligned 16-byte loads;
-// its 64 activations stay in registers as bf16 pairs and their fp32 sum
-// serves the bias term of every row it visits.  A byte (two codes) is one
+// The GEMV: lane lr of a row (Lp lanes) owns two pieces of 32 weights,
+// weights 32 lr .. 32 lr + 31 and 32 (lr + Lp) .. 32 (lr + Lp) + 31 (16 bytes
+// each, each inside one group for G = 64 or 128), so each of a wave's two
+// 16-byte loads per row covers contiguous bytes; its 64 activations stay in
+// registers as bf16 pairs and each piece's fp32 sum serves the bias term of
+// every row it visits.  A byte (two codes) is one
 // 4-byte lookup in a 256-entry LDS table of bf16 code pairs (64 copies,
 // lane l reads copy l, so no two lanes share a bank) and one
 // v_dot2_f32_bf16; the products x * q are exact in fp32.
@@ -33,6 +35,11 @@ constexpr int kDepth = 2;                    // row steps in flight per lane (32
 constexpr int kFlush = 16;                   // rounds of results held in LDS per wave
 constexpr int kResCap = kFlush * kRing * 4;  // floats a wave (at most 4 rows a step)
 constexpr uint32_t kOOR = 0x80000000u;       // a buffer offset past any range: loads give 0
+// Cache policy of the code loads: nontemporal (gfx950's nt bit); each byte
+// is read once and each load instruction of a wave covers whole lines.  The
+// scale and bias loads keep the default policy: a row's two pieces read
+// their parameters from the same line with two instructions.
+constexpr int kStreamed = 2;
 
 typedef __bf16 bf16x2_t __attribute__((ext_vector_type(2)));
 typedef uint32_t u32x4 __attribute__((ext_vector_type(4)));
@@ -81,7 +88,6 @@ struct W4Batch {
 template <int G>
 __global__ __launch_bounds__(kBlock) __attribute__((amdgpu_waves_per_eu(4, 4))) void
 w4a16_gemv_kernel(const W4Batch args) {
-  constexpr int CPG = G / 64;  // lanes a group
   __shared__ __align__(16) uint32_t lut[256 * kCopies];
   __shared__ float res[kWaves][kResCap];
   const int p = blockIdx.y;
@@ -104,23 +110,30 @@ w4a16_gemv_kernel(const W4Batch args) {
   const int Lp = L <= 16 ? 16 : (L <= 32 ? 32 : 64);  // lanes a row
   const int R = 64 / Lp;                              // rows a wave step
   const int lr = lane & (Lp - 1), rs = lane / Lp;
-  const bool lane_on = lr < L;
+  // The lane's two 32-code pieces of a row: A = bytes [16 lr, 16 lr + 16), B
+  // = bytes [16 (lr + Lp), ...), so each load instruction of a wave covers
+  // whole lines of the row (and can use the nontemporal policy).  A piece
+  // lies in one group; pieces past the row's K/2 bytes read zeros.
+  const uint32_t rbytes = (uint32_t)K / 2u;
+  const bool onA = 16u * (uint32_t)lr < rbytes, onB = 16u * (uint32_t)(lr + Lp) < rbytes;
+  const uint32_t gA = 32u * (uint32_t)lr / (uint32_t)G, gB = 32u * (uint32_t)(lr + Lp) / (uint32_t)G;
 
   // this lane's 64 activations as bf16 pairs, and their sum
   uint32_t xa[32];
-  float xsum = 0.f;
+  float xsumA = 0.f, xsumB = 0.f;
   {
     const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[p], (uint32_t)K * 2u);
 #pragma unroll
     for (int i = 0; i < 8; ++i) {
       const u32x4 v = __builtin_bit_cast(
-          u32x4, __builtin_amdgcn_raw_buffer_load_b128(rx, lane_on ? 128u * lr + 16u * i : kOOR,
-                                                       0, 0));
+          u32x4, __builtin_amdgcn_raw_buffer_load_b128(
+                     rx, i < 4 ? (onA ? 64u * lr + 16u * i : kOOR)
+                               : (onB ? 64u * (uint32_t)(lr + Lp) + 16u * (i - 4) : kOOR),
+                     0, 0));
       xa[4 * i] = v[0]; xa[4 * i + 1] = v[1]; xa[4 * i + 2] = v[2]; xa[4 * i + 3] = v[3];
     }
   }
-  const uint32_t rb = (uint32_t)K / 2u;  // bytes a row
-  const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[p], (uint32_t)N * rb);
+  const __amdgpu_buffer_rsrc_t rp = make_rsrc(args.packed[p], (uint32_t)N * rbytes);
   // scales and biases: bf16, read as the dword holding the lane's one
   const uintptr_t sp = (uintptr_t)args.scales[p], bp = (uintptr_t)args.biases[p];
   const uint32_t shead = (uint32_t)(sp & 3u), bhead = (uint32_t)(bp & 3u);
@@ -142,32 +155,41 @@ w4a16_gemv_kernel(const W4Batch args) {
   const int nsteps = first < N ? (N - first + RS - 1) / RS : 0;
   const int nround = (nsteps + kRing - 1) / kRing;
   u32x4 ring_a[kDepth], ring_b[kDepth];
-  uint32_t rsw[kDepth], rbw[kDepth];
-  auto param_off = [&](uint32_t row, uint32_t head) {
-    return 2u * (row * (uint32_t)nG + (uint32_t)(lr / CPG)) + head;
+  uint32_t rswA[kDepth], rbwA[kDepth], rswB[kDepth], rbwB[kDepth];
+  auto param_off = [&](uint32_t row, uint32_t g, uint32_t head) {
+    return 2u * (row * (uint32_t)nG + g) + head;
   };
-  // a lane with no chunk reads past every range (offsets stay below 2^31, so
+  // a piece past the row reads past every range (offsets stay below 2^31, so
   // setting bit 31 is enough): an OR, where a select was turned into a
   // branch around each load, and a load under a branch makes the next wait
   // a full drain
-  const uint32_t off_mask = lane_on ? 0u : kOOR;
+  const uint32_t maskA = onA ? 0u : kOOR, maskB = onB ? 0u : kOOR;
   auto issue = [&](int d, int step) {
     const int r = first + rs + step * RS;
     const uint32_t row = (uint32_t)(r < N ? r : N - 1);
-    const uint32_t o = (row * rb + 32u * lr) | off_mask;
-    ring_a[d] = __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, o, 0, 0));
-    ring_b[d] =
-        __builtin_bit_cast(u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, o + 16u, 0, 0));
-    rsw[d] = __builtin_amdgcn_raw_buffer_load_b32(
-        rsc_, (param_off(row, shead) & ~3u) | off_mask, 0, 0);
-    rbw[d] = __builtin_amdgcn_raw_buffer_load_b32(
-        rbi_, (param_off(row, bhead) & ~3u) | off_mask, 0, 0);
+    const uint32_t o = row * rbytes + 16u * (uint32_t)lr;
+    ring_a[d] = __builtin_bit_cast(
+        u32x4, __builtin_amdgcn_raw_buffer_load_b128(rp, o | maskA, 0, kStreamed));
+    ring_b[d] = __builtin_bit_cast(
+        u32x4,
+        __builtin_amdgcn_raw_buffer_load_b128(rp, (o + 16u * (uint32_t)Lp) | maskB, 0, kStreamed));
+    rswA[d] = __builtin_amdgcn_raw_buffer_load_b32(
+        rsc_, (param_off(row, gA, shead) & ~3u) | maskA, 0, 0);
+    rbwA[d] = __builtin_amdgcn_raw_buffer_load_b32(
+        rbi_, (param_off(row, gA, bhead) & ~3u) | maskA, 0, 0);
+    rswB[d] = __builtin_amdgcn_raw_buffer_load_b32(
+        rsc_, (param_off(row, gB, shead) & ~3u) | maskB, 0, 0);
+    rbwB[d] = __builtin_amdgcn_raw_buffer_load_b32(
+        rbi_, (param_off(row, gB, bhead) & ~3u) | maskB, 0, 0);
   };
 #pragma unroll
   for (int d = 0; d < kDepth; ++d) issue(d, d);
   // the activations' sum once the ring's first loads are out
 #pragma unroll
-  for (int j = 0; j < 32; ++j) xsum = dot2(xa[j], 0x3F803F80u, xsum);  // x0 + x1 per pair
+  for (int j = 0; j < 16; ++j) {  // x0 + x1 per pair, for each piece
+    xsumA = dot2(xa[j], 0x3F803F80u, xsumA);
+    xsumB = dot2(xa[16 + j], 0x3F803F80u, xsumB);
+  }
   const int l16 = lane & 15;
   const bool hi8 = (l16 & 8) != 0, hi4 = (l16 & 4) != 0;
   // Results go to LDS and out to y every kFlush rounds: a global store
@@ -194,8 +216,14 @@ w4a16_gemv_kernel(const W4Batch args) {
       const int r = first + rs + (s0 + d) * RS;
       const uint32_t row = (uint32_t)(r < N ? r : N - 1);
       const int sl = d % kDepth;
-      const float sc = bf16_to_f32((rsw[sl] >> ((param_off(row, shead) & 2u) << 3)) & 0xFFFFu);
-      const float bi = bf16_to_f32((rbw[sl] >> ((param_off(row, bhead) & 2u) << 3)) & 0xFFFFu);
+      const float scA =
+          bf16_to_f32((rswA[sl] >> ((param_off(row, gA, shead) & 2u) << 3)) & 0xFFFFu);
+      const float biA =
+          bf16_to_f32((rbwA[sl] >> ((param_off(row, gA, bhead) & 2u) << 3)) & 0xFFFFu);
+      const float scB =
+          bf16_to_f32((rswB[sl] >> ((param_off(row, gB, shead) & 2u) << 3)) & 0xFFFFu);
+      const float biB =
+          bf16_to_f32((rbwB[sl] >> ((param_off(row, gB, bhead) & 2u) << 3)) & 0xFFFFu);
       // the table addresses of the slot's 32 bytes (byte * 256 + copy offset),
       // pinned before the refill: computed after it they would keep the
       // slot's old words live beside the new load, and the register copies
@@ -209,20 +237,20 @@ w4a16_gemv_kernel(const W4Batch args) {
 #pragma unroll
       for (int q = 0; q < 32; ++q) asm volatile("" : "+v"(addr[q]));
       issue(sl, s0 + d + kDepth);  // refill the slot with the step kDepth ahead
-      float acc = 0.f;
-      // two halves of 16 bytes, each looked up in full before its products
+      float acc[2] = {0.f, 0.f};
+      // the two pieces of 16 bytes, each looked up in full before its products
 #pragma unroll
       for (int h = 0; h < 2; ++h) {
         uint32_t e[16];
 #pragma unroll
         for (int q = 0; q < 16; ++q) e[q] = *(lds_u32_c *)(lut_b + addr[16 * h + q]);
 #pragma unroll
-        for (int q = 0; q < 16; ++q) acc = dot2(e[q], xa[16 * h + q], acc);
+        for (int q = 0; q < 16; ++q) acc[h] = dot2(e[q], xa[16 * h + q], acc[h]);
         // the products now: sunk to the round's end they would hold every
         // step's lookups at once
-        asm volatile("" : "+v"(acc));
+        asm volatile("" : "+v"(acc[h]));
       }
-      v[d] = sc * acc + bi * xsum;
+      v[d] = scA * acc[0] + biA * xsumA + (scB * acc[1] + biB * xsumB);
     }
     // Sum each step's chunk values over the 16 lanes of a DPP row, four steps
     // at once: exchange across lane bit 3 (row_ror:8), then across bit 2
