@@ -75,7 +75,11 @@ constexpr int TM = 4, TN = 4;           // 16 x 16 tiles per wave: 64 x 64
 // first[g], first[g] + 1, ...; their tiles start at tile t0[g] of the launch
 // (t0 of an absent shape: INT_MAX) and follow one another problem by
 // problem.  The tile -> problem lookup is a fixed number of comparisons: a
-// loop there would put branches in every stage.
+// loop there would put branches in every stage.  Tile walk: block b takes
+// tiles b, b + grid, ... (skip = 0).  With skip > 0 the `heavy` first blocks,
+// which draw one more tile of the longest shape (lead + 1 against lead), let
+// the others take the first `skip` rounds of the remaining tiles alone, so
+// that the blocks' shares of stages come out closer to equal.
 constexpr int kWideMaxBatch = 128;
 constexpr int kWideMaxShapes = 4;
 struct WideBatch {
@@ -86,6 +90,7 @@ struct WideBatch {
   int n[kWideMaxShapes], k[kWideMaxShapes], tpp[kWideMaxShapes], first[kWideMaxShapes];
   int t0[kWideMaxShapes];
   int total;
+  int heavy, lead, skip;
 };
 
 __device__ __forceinline__ __amdgpu_buffer_rsrc_t make_rsrc(const void *p, uint32_t bytes) {
@@ -152,8 +157,31 @@ struct Tile {
   int pi, m0, n0, mrows, nrows, N, K;
 };
 
+// Tile index of the j-th tile of this block (see WideBatch).
+__device__ __forceinline__ int walk_tile(const WideBatch &a, int j) {
+  const int b = (int)blockIdx.x, grid = (int)gridDim.x;
+  if (a.skip == 0) return b + j * grid;
+  const bool heavy = b < a.heavy;
+  const int jl = a.lead + (heavy ? 1 : 0);  // this block's tiles of the longest shape
+  if (j < jl) return b + j * grid;
+  const int light = grid - a.heavy;
+  const int v = j - jl + (heavy ? a.skip : 0);  // round among the remaining tiles
+  return v < a.skip ? a.t0[1] + v * light + (b - a.heavy)
+                    : a.t0[1] + a.skip * light + (v - a.skip) * grid + b;
+}
+
+// Tiles of this block.
+__device__ __forceinline__ int walk_count(const WideBatch &a) {
+  const int b = (int)blockIdx.x, grid = (int)gridDim.x;
+  if (a.skip == 0) return (a.total - b + grid - 1) / grid;
+  const bool heavy = b < a.heavy;
+  const int rest0 = a.t0[1] + a.skip * (grid - a.heavy);  // first tile of the shared rounds
+  const int left = a.total - rest0 - b;
+  return a.lead + (heavy ? 1 : a.skip) + (left > 0 ? (left + grid - 1) / grid : 0);
+}
+
 __device__ __forceinline__ Tile block_tile(const WideBatch &a, int j, int M, int tilesM) {
-  const int t = (int)blockIdx.x + j * (int)gridDim.x;
+  const int t = walk_tile(a, j);
   Tile r;
   if (t >= a.total) {
     r.pi = 0; r.m0 = 0; r.n0 = 0; r.mrows = 0; r.nrows = 0; r.N = 0; r.K = G;
@@ -196,8 +224,7 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
   // compiler copy it to scratch memory.
   const WideBatch &args_ = *reinterpret_cast<const WideBatch *>(
       (const void *)__builtin_amdgcn_kernarg_segment_ptr());
-  const int total = args_.total;
-  const int ntiles = (total - (int)blockIdx.x + (int)gridDim.x - 1) / (int)gridDim.x;
+  const int ntiles = walk_count(args_);
   auto tile = [&](int j) { return block_tile(args_, j, M, tilesM); };
 
   // ---- decode table: two threads per entry, eight copies each, the copy
@@ -560,6 +587,46 @@ bool gemm_wide_grouped_supported(int count, int64_t M, const int64_t *Ns, const 
   return tiles >= 192 && tiles < (int64_t(1) << 30);
 }
 
+// The tile walk of a launch (WideBatch): when the tiles of the longest shape
+// do not split evenly over the blocks, the number of rounds of the remaining
+// tiles that the blocks with one more long tile skip, chosen to minimise the
+// largest block's stages (each tile counted by its K), 0 if none helps.
+static void plan_walk(WideBatch &a, int grid) {
+  a.heavy = 0; a.lead = 0; a.skip = 0;
+  if (a.t0[1] == INT_MAX || grid <= 0) return;  // one shape
+  const int L = a.t0[1], heavy = L % grid;
+  if (heavy == 0) return;
+  const int light = grid - heavy, cap = (a.total - L) / light;
+  auto cost_of = [&](int t) {
+    const int g = (int)(t >= a.t0[1]) + (int)(t >= a.t0[2]) + (int)(t >= a.t0[3]);
+    return (int64_t)a.k[g];
+  };
+  int64_t best = -1;
+  int best_d = 0;
+  for (int d = 0; d <= cap && d <= 16; ++d) {
+    std::vector<int64_t> load(grid, 0);
+    for (int b = 0; b < grid; ++b) {
+      const bool hv = b < heavy;
+      const int jl = L / grid + (hv ? 1 : 0);
+      for (int j = 0;; ++j) {
+        int t;
+        if (d == 0 || j < jl) {
+          t = b + j * grid;
+        } else {
+          const int v = j - jl + (hv ? d : 0);
+          t = v < d ? L + v * light + (b - heavy) : L + d * light + (v - d) * grid + b;
+        }
+        if (t >= a.total) break;
+        load[b] += cost_of(t);
+      }
+    }
+    int64_t mx = 0;
+    for (int b = 0; b < grid; ++b) mx = load[b] > mx ? load[b] : mx;
+    if (best < 0 || mx < best) { best = mx; best_d = d; }
+  }
+  if (best_d > 0) { a.heavy = heavy; a.lead = L / grid; a.skip = best_d; }
+}
+
 // Launches of up to kWideMaxBatch problems and kWideMaxShapes shapes, one
 // persistent block per CU.  Shapes are placed longest K first, so that the
 // blocks' round-robin share of the tiles ends with the short ones.
@@ -592,6 +659,7 @@ void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,
       a.n[g] = 0; a.k[g] = G; a.tpp[g] = 1; a.first[g] = n; a.t0[g] = INT_MAX;
     }
     const int grid = a.total < cus[dev] ? a.total : cus[dev];
+    plan_walk(a, grid);
     hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a, (int)M,
                        d_status);
     n = 0;
