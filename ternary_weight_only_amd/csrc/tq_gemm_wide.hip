@@ -591,6 +591,9 @@ bool gemm_wide_grouped_supported(int count, int64_t M, const int64_t *Ns, const 
 // do not split evenly over the blocks, the number of rounds of the remaining
 // tiles that the blocks with one more long tile skip, chosen to minimise the
 // largest block's stages (each tile counted by its K), 0 if none helps.
+// Tiles are ordered by K, longest first, so within each class of blocks
+// (one more long tile, or not) the first block draws the most and the
+// costliest tiles: the walk is simulated for blocks 0 and `heavy` only.
 static void plan_walk(WideBatch &a, int grid) {
   a.heavy = 0; a.lead = 0; a.skip = 0;
   if (a.t0[1] == INT_MAX || grid <= 0) return;  // one shape
@@ -601,27 +604,28 @@ static void plan_walk(WideBatch &a, int grid) {
     const int g = (int)(t >= a.t0[1]) + (int)(t >= a.t0[2]) + (int)(t >= a.t0[3]);
     return (int64_t)a.k[g];
   };
+  auto load_of = [&](int b, int d) {
+    const bool hv = b < heavy;
+    const int jl = L / grid + (hv ? 1 : 0);
+    int64_t sum = 0;
+    for (int j = 0;; ++j) {
+      int t;
+      if (d == 0 || j < jl) {
+        t = b + j * grid;
+      } else {
+        const int v = j - jl + (hv ? d : 0);
+        t = v < d ? L + v * light + (b - heavy) : L + d * light + (v - d) * grid + b;
+      }
+      if (t >= a.total) break;
+      sum += cost_of(t);
+    }
+    return sum;
+  };
   int64_t best = -1;
   int best_d = 0;
   for (int d = 0; d <= cap && d <= 16; ++d) {
-    std::vector<int64_t> load(grid, 0);
-    for (int b = 0; b < grid; ++b) {
-      const bool hv = b < heavy;
-      const int jl = L / grid + (hv ? 1 : 0);
-      for (int j = 0;; ++j) {
-        int t;
-        if (d == 0 || j < jl) {
-          t = b + j * grid;
-        } else {
-          const int v = j - jl + (hv ? d : 0);
-          t = v < d ? L + v * light + (b - heavy) : L + d * light + (v - d) * grid + b;
-        }
-        if (t >= a.total) break;
-        load[b] += cost_of(t);
-      }
-    }
-    int64_t mx = 0;
-    for (int b = 0; b < grid; ++b) mx = load[b] > mx ? load[b] : mx;
+    const int64_t l0 = load_of(0, d), l1 = load_of(heavy, d);
+    const int64_t mx = l0 > l1 ? l0 : l1;
     if (best < 0 || mx < best) { best = mx; best_d = d; }
   }
   if (best_d > 0) { a.heavy = heavy; a.lead = L / grid; a.skip = best_d; }
