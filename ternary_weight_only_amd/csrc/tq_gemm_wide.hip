@@ -26,6 +26,9 @@
 //   - one barrier, after a wait that leaves the younger loads in flight.
 // Codes enter the MFMA as the bf16 value 2c (exact, low byte zero: a pair of
 // codes is one v_perm of table bytes), as in gemm_kernel.
+// The kernel also takes the 2-bit format (four codes a byte, field c + 1,
+// first code lowest: Avenue README, size note on 2-bit packing); only the
+// table, the bytes a group and the way a run's codes are stitched differ.
 #include <hip/hip_fp16.h>
 #include <hip/hip_runtime.h>
 #include <stdint.h>
@@ -51,7 +54,12 @@ typedef __attribute__((address_space(3))) const bf16x8 lds_bf16x8_c;
 
 constexpr int kWave = 64;
 constexpr int G = 128;                  // this kernel's group size
-constexpr int B = 26;                   // bytes per group
+// Weight formats: base-3 bytes (five codes a byte, 26 bytes a group) and
+// 2-bit fields (four codes a byte, field c + 1, 32 bytes a group).
+constexpr int kFmtBase3 = 0, kFmt2Bit = 1;
+template <int FMT> struct Fmt;
+template <> struct Fmt<kFmtBase3> { static constexpr int B = 26, CPB = 5; };
+template <> struct Fmt<kFmt2Bit> { static constexpr int B = 32, CPB = 4; };
 constexpr int BM = 256;                 // activation rows per block
 constexpr int BN = 128;                 // weight rows per block
 constexpr int NT = 512;                 // threads per block (8 waves)
@@ -67,7 +75,7 @@ constexpr uint32_t kCsOff = XRING * XSLOT;
 constexpr uint32_t kLutOff = kCsOff + 2 * CSLOT;
 constexpr int SMEM = kLutOff + LUTB;    // 160 KiB: the whole LDS of a CU
 constexpr uint32_t kOutOfRange = 0x80000000u;
-constexpr uint32_t kBadFlag = 0xFF00u;  // in the high dword of entries 243..255
+constexpr uint32_t kBadFlag = 0xFF00u;  // in the high dword of invalid bytes' entries
 constexpr int TM = 4, TN = 4;           // 16 x 16 tiles per wave: 64 x 64
 
 // Problems of one launch (M is shared): their pointers, ordered by shape,
@@ -119,6 +127,20 @@ __device__ __forceinline__ u32x2 code_entry(uint32_t e) {
   return u32x2{h[0] | (h[1] << 8) | (h[2] << 16) | (h[3] << 24), h[4]};
 }
 
+// Table entry for a byte of 2-bit fields (field i = c_i + 1, first code
+// lowest): high bytes of 2*c_i, i = 0..3, in the low dword; the flag in the
+// high dword when a field is 3 (invalid; its code counts as 0).
+__device__ __forceinline__ u32x2 code_entry2(uint32_t e) {
+  uint32_t lo = 0u, bad = 0u;
+#pragma unroll
+  for (int i = 0; i < 4; ++i) {
+    const uint32_t f = (e >> (2 * i)) & 3u;
+    lo |= (f == 0u ? 0xC0u : (f == 2u ? 0x40u : 0u)) << (8 * i);
+    bad |= f == 3u ? kBadFlag : 0u;
+  }
+  return u32x2{lo, bad};
+}
+
 // A run of 16 codes starts at digit D0 of its first byte; lo/hi are the table
 // entries of the run's four bytes.  Output dword w is the bf16 pair
 // (2c_{2w}, 2c_{2w+1}) of the run.
@@ -141,6 +163,15 @@ __device__ __forceinline__ void stitch(const uint32_t (&lo)[4], const uint32_t (
       s0 = hi[j1]; s1 = lo[j2]; b1 = 4; b2 = 0;
     }
     out[w] = __builtin_amdgcn_perm(s0, s1, 0x000C000Cu | ((uint32_t)b1 << 8) | ((uint32_t)b2 << 24));
+  }
+}
+
+// The same for a run of 16 2-bit codes: four whole bytes, four codes each.
+__device__ __forceinline__ void stitch2(const uint32_t (&lo)[4], uint32_t (&out)[8]) {
+#pragma unroll
+  for (int w = 0; w < 8; ++w) {
+    const uint32_t b1 = 2u * (uint32_t)(w & 1), b2 = b1 + 1u;
+    out[w] = __builtin_amdgcn_perm(lo[w >> 1], lo[w >> 1], 0x000C000Cu | (b1 << 8) | (b2 << 24));
   }
 }
 
@@ -207,11 +238,14 @@ __device__ __forceinline__ Tile block_tile(const WideBatch &a, int j, int M, int
 // bytes three, scales one group) runs on across tile boundaries: each of the
 // three load streams keeps its own tile and moves to the next tile when its
 // stage count wraps, so a tile's first stages are loaded while the previous
-// tile computes, and the table is built once per block.
+// tile computes, and the table is built once per block.  FMT: the weight
+// format (kFmtBase3 or kFmt2Bit).
+template <int FMT>
 __global__ __launch_bounds__(NT) __attribute__((amdgpu_waves_per_eu(2, 2)))
 // `args` is the first kernel argument only to lay the table out at the start of
 // the argument segment, where the body reads it.
 void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_status) {
+  constexpr int B = Fmt<FMT>::B, CPB = Fmt<FMT>::CPB;
   (void)args;
   __shared__ __align__(16) unsigned char smem_raw[SMEM];
   lds_bytes *smem = (lds_bytes *)smem_raw;
@@ -231,7 +265,7 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
   // index rotated by the entry to spread the banks ----
   {
     const uint32_t e = (uint32_t)tid & 255u, half = (uint32_t)tid >> 8;
-    const u32x2 v = code_entry(e);
+    const u32x2 v = FMT == kFmtBase3 ? code_entry(e) : code_entry2(e);
 #pragma unroll
     for (int k = 0; k < kCopies / 2; ++k) {
       const uint32_t j = (8u * half + (uint32_t)k + e) & (kCopies - 1);
@@ -404,7 +438,7 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
     // first byte
     auto load_packed = [&](uint32_t (&dst)[2], uint32_t &ofs) {
       const uint32_t a = prow + (uint32_t)((sp >> 1) * B) +
-                         ((sp & 1) ? (uint32_t)((KS + 16 * DQ) / 5) : (uint32_t)(16 * DQ / 5));
+                         ((sp & 1) ? (uint32_t)((KS + 16 * DQ) / CPB) : (uint32_t)(16 * DQ / CPB));
       ofs = a & 3u;
       const u32x2 v = __builtin_amdgcn_raw_buffer_load_b64(rp, a & ~3u, 0, 0);
       dst[0] = v.x;
@@ -419,7 +453,10 @@ void gemm_wide_kernel(const WideBatch args, int M, int32_t *__restrict__ d_statu
       constexpr int ST = decltype(stc)::value;
       flags |= (hi[0] | hi[1]) | (hi[2] | hi[3]);
       uint32_t out[8];
-      stitch<(ST * KS + 16 * DQ) % 5>(lo, hi, out);
+      if constexpr (FMT == kFmtBase3)
+        stitch<(ST * KS + 16 * DQ) % 5>(lo, hi, out);
+      else
+        stitch2(lo, out);
 #pragma unroll
       for (int i = 0; i < 2; ++i)
         *(lds_u32x4 *)(smem + cs + swz((uint32_t)dr, (uint32_t)(2 * DQ + i))) =
@@ -634,10 +671,11 @@ static void plan_walk(WideBatch &a, int grid) {
 // Launches of up to kWideMaxBatch problems and kWideMaxShapes shapes, one
 // persistent block per CU.  Shapes are placed longest K first, so that the
 // blocks' round-robin share of the tiles ends with the short ones.
-void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,
-                              const uint8_t *const *packeds, const uint16_t *const *scales,
-                              float *const *ys, int64_t M, const int64_t *Ns, const int64_t *Ks,
-                              int32_t *d_status, hipStream_t stream) {
+static void launch_wide_fmt(int fmt, int count, const uint16_t *const *xs,
+                            const uint8_t *const *packeds, const uint16_t *const *scales,
+                            float *const *ys, int64_t M, const int64_t *Ns, const int64_t *Ks,
+                            int32_t *d_status, hipStream_t stream) {
+  auto kernel = fmt == kFmtBase3 ? gemm_wide_kernel<kFmtBase3> : gemm_wide_kernel<kFmt2Bit>;
   static int cus[64] = {};
   int dev = 0;
   (void)hipGetDevice(&dev);
@@ -664,8 +702,7 @@ void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,
     }
     const int grid = a.total < cus[dev] ? a.total : cus[dev];
     plan_walk(a, grid);
-    hipLaunchKernelGGL(gemm_wide_kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a, (int)M,
-                       d_status);
+    hipLaunchKernelGGL(kernel, dim3((unsigned)grid), dim3(NT), 0, stream, a, (int)M, d_status);
     n = 0;
     shapes = 0;
   };
@@ -692,12 +729,27 @@ void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,
   flush();
 }
 
+void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,
+                              const uint8_t *const *packeds, const uint16_t *const *scales,
+                              float *const *ys, int64_t M, const int64_t *Ns, const int64_t *Ks,
+                              int32_t *d_status, hipStream_t stream) {
+  launch_wide_fmt(kFmtBase3, count, xs, packeds, scales, ys, M, Ns, Ks, d_status, stream);
+}
+
 void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                       const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                       int64_t K, int32_t *d_status, hipStream_t stream) {
   std::vector<int64_t> Ns(count, N), Ks(count, K);
-  launch_gemm_wide_grouped(count, xs, packeds, scales, ys, M, Ns.data(), Ks.data(), d_status,
-                           stream);
+  launch_wide_fmt(kFmtBase3, count, xs, packeds, scales, ys, M, Ns.data(), Ks.data(), d_status,
+                  stream);
+}
+
+void launch_gemm2_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                       const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                       int64_t K, int32_t *d_status, hipStream_t stream) {
+  std::vector<int64_t> Ns(count, N), Ks(count, K);
+  launch_wide_fmt(kFmt2Bit, count, xs, packeds, scales, ys, M, Ns.data(), Ks.data(), d_status,
+                  stream);
 }
 
 }  // namespace tq

@@ -136,6 +136,12 @@ void launch_gemm_wide(int count, const uint16_t *const *xs, const uint8_t *const
                       const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                       int64_t K, int32_t *d_status, hipStream_t stream);
 
+// The same kernel over the 2-bit format (four codes a byte, G/4 bytes a
+// group): count same-shaped problems, under gemm_wide_supported's conditions.
+void launch_gemm2_wide(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
+                       const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
+                       int64_t K, int32_t *d_status, hipStream_t stream);
+
 // Problems of different N and K (shared M) in one persistent launch (per 128).
 bool gemm_wide_grouped_supported(int count, int64_t M, const int64_t *Ns, const int64_t *Ks, int G);
 void launch_gemm_wide_grouped(int count, const uint16_t *const *xs,

@@ -291,6 +291,13 @@ bool matmul2_supported(int64_t M, int64_t N, int64_t K, int G) {
 void launch_matmul2_batched(int count, const uint16_t *const *xs, const uint8_t *const *packeds,
                             const uint16_t *const *scales, float *const *ys, int64_t M, int64_t N,
                             int64_t K, int G, int32_t *d_status, hipStream_t stream) {
+  // large launches (G = 128, M >= 256, enough 256 x 128 tiles to fill the
+  // CUs) go to the persistent kernel of the base-3 matmul, which takes this
+  // format too
+  if (gemm_wide_supported(count, M, N, K, G)) {
+    launch_gemm2_wide(count, xs, packeds, scales, ys, M, N, K, d_status, stream);
+    return;
+  }
   for (int i0 = 0; i0 < count; i0 += kMaxBatch) {
     const int n = count - i0 < kMaxBatch ? count - i0 : kMaxBatch;
     Mm2Batch args = {};

@@ -97,6 +97,35 @@ def test_gemm2_invalid_field(M, K):
     assert_within_bound(y, y_ref, bound, "gemm2 with invalid fields")
 
 
+@pytest.mark.parametrize("bad", [False, True])
+def test_gemm2_persistent_launch_every_output(bad):
+    """Launches with enough 256 x 128 tiles (12 problems W[1000,1024] at
+    M = 260: 192 tiles, ragged in M and N) run on the persistent matrix-core
+    kernel shared with the base-3 format; every output of every problem is
+    checked, and with `bad` one problem holds fields of 3 (INVALID_BYTE, the
+    field counting as code 0)."""
+    import torch
+    import ternary_weight_only_amd as tq
+    M, N, K, G, count = 260, 1000, 1024, 128, 12
+    probs = [_packed(760 + i, N, K, G) for i in range(count)]
+    if bad:
+        p0 = probs[5][0].copy()
+        p0[3, 7] = 0xFF
+        p0[N - 1, K // 4 - 1] |= 0xC0
+        probs[5] = (p0, probs[5][1])
+    xs = [inputs.activation(770 + i, M, K) for i in range(count)]
+    say("gemm2 persistent M=%d W[%d,%d] x%d bad=%d" % (M, N, K, count, bad))
+    st = tq.new_status()
+    ys = tq.gemm2_batched([dev_bf16(x) for x in xs], [dev_u8(p) for p, _ in probs],
+                          [dev_f16bits(s) for _, s in probs], N, K, G, status=st)
+    torch.cuda.synchronize()
+    assert int(st.item()) == (4 if bad else 0)
+    for i, ((p, s), x, y) in enumerate(zip(probs, xs, ys)):
+        y_ref, bound, st_ref = oracle.matmul2(x, p, s, N, K, G, threads=16)
+        assert st_ref == (4 if bad and i == 5 else 0)
+        assert_within_bound(y.cpu().numpy(), y_ref, bound, "gemm2 persistent problem %d" % i)
+
+
 @pytest.mark.parametrize("M,N,K,G,count", [(4, 300, 640, 64, 3), (64, 1024, 3584, 128, 2),
                                            (1, 200, 8192, 128, 3), (1, 256, 1024, 128, 2)])
 def test_gemm2_batched_equals_single(M, N, K, G, count):
