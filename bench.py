@@ -72,12 +72,14 @@ HBM_PEAK_GBS = 8000.0          # MI355X HBM3E, 8 TB/s
 MFMA_BF16_PEAK_TFLOPS = 2500.0  # MI355X dense bf16 MFMA
 METRIC = "ternary GEMV packed-weight GB/s (% HBM peak); prefill GEMM TFLOP/s (% MFMA)"
 RING = 8
+# bytes one 8B-class matrix launch reads: packed bytes + fp16 scales at G = 128
+D8_LAUNCH_BYTES = 12845056
 ALL_ROWS = ("step", "gemv_g64", "gemm_m2048", "dense8b", "dequant", "gemv2", "w4a16", "qat",
             "ceilings", "cpu")
 # HBM bytes per GEMV launch from rocprofv3 FETCH_SIZE and WRITE_SIZE runs of this bench, each
 # scaled by the same counter on a 256 MiB copy (profiles/gemv_m1_hbm_traffic.md); valid only
 # for the kernel source they were taken on (sha256 prefix of csrc/tq_gemv_m1.hip).
-GEMV_TRAFFIC = {"26d5db229a6fc019": 61281585}
+GEMV_TRAFFIC = {"88cc61fdaeb49a3a": 61250201}
 
 
 def parse():
@@ -797,6 +799,18 @@ class Bench:
             ms = self.chain(run_big, 2)
             out["read_stream_1GiB_grid%d" % grid] = {
                 "us": ms * 1e3, "GB/s": big.numel() / (ms * 1e-3) / 1e9}
+
+            # one 8B-class matrix's bytes (packed + scales) per launch, each
+            # launch on the next stretch of the 1 GiB buffer
+            nbytes8 = D8_LAUNCH_BYTES // 16 * 16
+            stretches = big.numel() // nbytes8
+
+            def run_d8(i, grid=grid):
+                self.ok(L.tq_probe_read_stream(big.data_ptr() + i * nbytes8, nbytes8, grid,
+                                               sink.data_ptr(), self.sp))
+            ms = self.chain(run_d8, stretches)
+            out["read_stream_12.8MB_grid%d" % grid] = {
+                "us": ms * 1e3, "GB/s": nbytes8 / (ms * 1e-3) / 1e9}
         grid, iters = 512, 4096
         fs = sink.view(torch.float32)
 
@@ -837,6 +851,10 @@ class Bench:
         if "decode_gemv" in self.rows:
             r = self.rows["decode_gemv"]
             r["kernel_frac_of_read_stream"] = r["kernel_GB/s"] / best_read
+        best_d8 = max(v["GB/s"] for k, v in out.items() if k.startswith("read_stream_12.8"))
+        if "dense8b_gemv" in self.rows:
+            for case in self.rows["dense8b_gemv"]["cases"].values():
+                case["frac_of_read_stream"] = case["GB/s"] / best_d8
         del bufs, big, sink
 
     # ---- the oracle on the host ----

@@ -145,16 +145,13 @@ struct GemvShapes {
 //
 // Start-up order: the activations are requested first, then the first D
 // batches of packed bytes; the table is built while both are in flight.
-// Then the activations reach registers in one of two ways:
-//   * staged (XDIRECT false): the block loads x once (XL 16-byte pieces per
-//     thread at most) into LDS, padded by 16 bytes after every 128, and each
-//     lane reads its 144-byte window from there: lanes 16 apart in chunk
-//     index land in different bank groups, and the caches see one copy of x
-//     per block instead of one per row of a batch;
-//   * direct (XDIRECT true, long rows whose staged copy would not leave room
-//     for two blocks per CU): each lane loads its window itself; a batch
-//     then has few rows, so little is loaded twice.
-template <int G, bool WAVE_ROWS, int XL, bool XDIRECT, bool AL>
+// Then the block stages x once (XL 16-byte pieces per thread at most) in
+// LDS, padded by 16 bytes after every 128, and each lane reads its 144-byte
+// window from there: lanes 16 apart in chunk index land in different bank
+// groups, and the caches see one copy of x per block instead of one per row
+// of a batch.  Rows too long for two blocks' LDS per CU (K >= 6848) run one
+// block per CU.
+template <int G, bool WAVE_ROWS, int XL, bool AL>
 __global__ __launch_bounds__(kWave * kMaxWaves) __attribute__((amdgpu_waves_per_eu(4, 4)))
 void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restrict__ d_status) {
   __shared__ uint4 lut[kLutEntries * kCopies];
@@ -190,18 +187,12 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   // window reaches 16 bytes beyond x)
   const __amdgpu_buffer_rsrc_t rx = make_rsrc(args.x[pi], (uint32_t)K * 2u);
   const int nxc = (K >> 3) + 1;  // staged 16-byte pieces: x plus one of zeros
-  constexpr int kXLoads = XDIRECT ? 9 : XL;
-  u32x4 xv[kXLoads];
+  u32x4 xv[XL];
 #pragma unroll
-  for (int i = 0; i < kXLoads; ++i) {
-    uint32_t off;
-    if (XDIRECT) {
-      off = lane_on ? 128u * (uint32_t)c + 16u * (uint32_t)i : kOutOfRange;
-    } else {
-      const int j = tid + i * nthreads;
-      off = j < nxc ? 16u * (uint32_t)j : kOutOfRange;
-    }
-    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, off, 0, 0);
+  for (int i = 0; i < XL; ++i) {
+    const int j = tid + i * nthreads;
+    xv[i] = __builtin_amdgcn_raw_buffer_load_b128(rx, j < nxc ? 16u * (uint32_t)j : kOutOfRange,
+                                                  0, 0);
   }
 
   // lane's byte address of local batch b is a0 + b * bstep (its first row is
@@ -275,13 +266,11 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
       }
     }
   }
-  if constexpr (!XDIRECT) {
-    // piece j goes to slot j + j/8
+  // piece j goes to slot j + j/8
 #pragma unroll
-    for (int i = 0; i < XL; ++i) {
-      const int j = tid + i * nthreads;
-      if (j < nxc) xstage[j + (j >> 3)] = xv[i];
-    }
+  for (int i = 0; i < XL; ++i) {
+    const int j = tid + i * nthreads;
+    if (j < nxc) xstage[j + (j >> 3)] = xv[i];
   }
   __syncthreads();
 
@@ -294,12 +283,8 @@ void gemv_m1_kernel(const GemvBatch args, const GemvShapes shp, int32_t *__restr
   {
     u32x4 xr[9];
 #pragma unroll
-    for (int i = 0; i < 9; ++i) {
-      if constexpr (XDIRECT)
-        xr[i] = xv[i];
-      else
-        xr[i] = lane_on ? xstage[9 * c + i + (i >> 3)] : u32x4{0u, 0u, 0u, 0u};
-    }
+    for (int i = 0; i < 9; ++i)
+      xr[i] = lane_on ? xstage[9 * c + i + (i >> 3)] : u32x4{0u, 0u, 0u, 0u};
     const int h = (G == 128) ? (c & 1) : 0;
     uint32_t Dw[36];
 #pragma unroll
@@ -487,18 +472,23 @@ int m1_stage_bytes(int K) {
   return 16 * (nxc + (nxc - 1) / 8 + 1);
 }
 bool m1_staged(int K) { return kStaticLds + m1_stage_bytes(K) <= 80 * 1024; }
+// Longer rows stage x too, with one block per CU (the whole 160 KB): a block
+// then reads x once from the caches instead of each lane its own window.
+bool m1_staged_one(int K) { return kStaticLds + m1_stage_bytes(K) <= 160 * 1024; }
+constexpr int kXlOne = 5;  // staged pieces per thread when one block holds a CU (K <= 16384)
 
 // Segments of a problem with nb row batches whose share of a launch is
-// `share` blocks out of 512 (at most two blocks per CU -- two fit the 64 KB
-// table -- so every block is resident from the start).  A block runs whole
-// rounds of kRing batches (a round's batches past its segment are computed
-// on zeros), so a CU's work is about ceil(blocks / 256) blocks times the
-// rounds of the longest segment, the launch counting 512 / share problems
-// like this one.  Among the segment counts up to the share that give each
+// `share` blocks out of `slots` (512: two blocks per CU -- two fit the 64 KB
+// table; 256 when a block's staged activations take a CU's LDS -- so every
+// block is resident from the start).  A block runs whole rounds of kRing
+// batches (a round's batches past its segment are computed on zeros), so a
+// CU's work is about ceil(blocks / per-CU) blocks times the rounds of the
+// longest segment, the launch counting slots / share problems like this
+// one.  Among the segment counts up to the share that give each
 // segment a batch, take the one with the least work on the busiest CU, then
 // the least work in all, then the most blocks (more loads in flight).
-int m1_segments(int64_t share, int64_t nb) {
-  const int64_t count = share >= 512 ? 1 : 512 / share;
+int m1_segments(int64_t share, int64_t nb, int64_t slots) {
+  const int64_t count = share >= slots ? 1 : slots / share;
   int64_t smax = share < nb ? share : nb;
   int best = 1;
   int64_t best_cu = -1, best_all = -1;
@@ -507,7 +497,7 @@ int m1_segments(int64_t share, int64_t nb) {
     const int64_t rounds_long = (q + (rem ? 1 : 0) + kRing - 1) / kRing;
     const int64_t rounds_short = (q + kRing - 1) / kRing;
     const int64_t blocks = (int64_t)count * S;
-    const int64_t cu = ((blocks + 255) / 256) * rounds_long;
+    const int64_t cu = ((blocks + slots - 1) / slots) * rounds_long;
     const int64_t all = (int64_t)count * (rem * rounds_long + (S - rem) * rounds_short);
     if (best_cu < 0 || cu < best_cu || (cu == best_cu && all <= best_all)) {
       best = (int)S;
@@ -523,11 +513,11 @@ int m1_segments(int64_t share, int64_t nb) {
 struct M1Config {
   int threads;
   bool wave_rows;  // rows of 16, 32 or 64 lanes, inside one wave
-  bool direct;     // activations loaded per lane (rows too long to stage)
-  int xl;          // staged pieces per thread: 1, 2 or 3
+  bool one_per_cu; // staged activations too large for two blocks per CU
+  int xl;          // staged pieces per thread: 1, 2, 3 or kXlOne
   bool aligned;    // both batch steps in whole dwords
   bool operator==(const M1Config &o) const {
-    return threads == o.threads && wave_rows == o.wave_rows && direct == o.direct &&
+    return threads == o.threads && wave_rows == o.wave_rows && one_per_cu == o.one_per_cu &&
            xl == o.xl && aligned == o.aligned;
   }
 };
@@ -538,41 +528,54 @@ M1Config m1_config(int64_t K, int G) {
   c.threads = 64 * m1_waves(K);
   const int R = c.threads / Lp;
   c.wave_rows = Lp == 16 || Lp == 32 || Lp == 64;
-  c.direct = !m1_staged((int)K);
   const int xl = ((int)(K >> 3) + 1 + c.threads - 1) / c.threads;
-  c.xl = c.direct ? 1 : (xl <= 1 ? 1 : (xl <= 2 ? 2 : 3));
+  // rows of K >= 6848 (two blocks' LDS per CU exceeded) take 112 to 256
+  // lanes, which span waves, and at most kXlOne pieces a thread
+  c.one_per_cu = !m1_staged((int)K);
+  c.xl = c.one_per_cu ? kXlOne : (xl <= 1 ? 1 : (xl <= 2 ? 2 : 3));
   const int64_t bstep = (int64_t)R * L * kChunk, sstep = 2 * (int64_t)R * (K / G);
   c.aligned = bstep % 4 == 0 && sstep % 4 == 0;
   return c;
 }
 
-template <int G, bool WR, int XL, bool XD, bool AL>
+template <int G, bool WR, int XL, bool AL>
 void launch_m1_k(const GemvBatch &args, const GemvShapes &shp, dim3 grid, int threads, int lds,
                  int32_t *d_status, hipStream_t stream) {
-  hipLaunchKernelGGL((gemv_m1_kernel<G, WR, XL, XD, AL>), grid, dim3(threads), lds, stream, args,
+  if (kStaticLds + lds > 64 * 1024) {
+    // a block above 64 KB of LDS (one per CU): allow the dynamic part
+    static const hipError_t set = hipFuncSetAttribute(
+        reinterpret_cast<const void *>(&gemv_m1_kernel<G, WR, XL, AL>),
+        hipFuncAttributeMaxDynamicSharedMemorySize, 160 * 1024 - kStaticLds);
+    (void)set;
+  }
+  hipLaunchKernelGGL((gemv_m1_kernel<G, WR, XL, AL>), grid, dim3(threads), lds, stream, args,
                      shp, d_status);
 }
 
-template <int G, bool WR, int XL, bool XD>
+template <int G, bool WR, int XL>
 void launch_m1_al(const M1Config &c, const GemvBatch &args, const GemvShapes &shp, dim3 grid,
                   int lds, int32_t *d_status, hipStream_t stream) {
   if (c.aligned)
-    launch_m1_k<G, WR, XL, XD, true>(args, shp, grid, c.threads, lds, d_status, stream);
+    launch_m1_k<G, WR, XL, true>(args, shp, grid, c.threads, lds, d_status, stream);
   else
-    launch_m1_k<G, WR, XL, XD, false>(args, shp, grid, c.threads, lds, d_status, stream);
+    launch_m1_k<G, WR, XL, false>(args, shp, grid, c.threads, lds, d_status, stream);
 }
 
 template <int G, bool WR>
 void launch_m1_wr(const M1Config &c, const GemvBatch &args, const GemvShapes &shp, dim3 grid,
                   int lds, int32_t *d_status, hipStream_t stream) {
-  if (c.direct)
-    launch_m1_al<G, WR, 1, true>(c, args, shp, grid, lds, d_status, stream);
-  else if (c.xl == 1)
-    launch_m1_al<G, WR, 1, false>(c, args, shp, grid, lds, d_status, stream);
+  if constexpr (!WR) {
+    if (c.one_per_cu) {  // only rows that span waves are this long
+      launch_m1_al<G, WR, kXlOne>(c, args, shp, grid, lds, d_status, stream);
+      return;
+    }
+  }
+  if (c.xl == 1)
+    launch_m1_al<G, WR, 1>(c, args, shp, grid, lds, d_status, stream);
   else if (c.xl == 2)
-    launch_m1_al<G, WR, 2, false>(c, args, shp, grid, lds, d_status, stream);
+    launch_m1_al<G, WR, 2>(c, args, shp, grid, lds, d_status, stream);
   else
-    launch_m1_al<G, WR, 3, false>(c, args, shp, grid, lds, d_status, stream);
+    launch_m1_al<G, WR, 3>(c, args, shp, grid, lds, d_status, stream);
 }
 
 // One launch over up to kMaxBatch problems that share configuration c.
@@ -583,17 +586,18 @@ void launch_m1(const M1Config &c, int count, const uint16_t *const *xs,
   GemvBatch args = {};
   GemvShapes shp = {};
   int smax = 1, lds = 0;
-  // the 512 blocks of a launch are shared out in proportion to the problems'
-  // sizes (weights, i.e. packed bytes)
+  // the blocks of a launch (512, or 256 at one per CU) are shared out in
+  // proportion to the problems' sizes (weights, i.e. packed bytes)
+  const int slots = c.one_per_cu ? 256 : 512;
   double total = 0.0;
   for (int i = 0; i < count; ++i) total += (double)Ns[i] * (double)Ks[i];
   int segs[kMaxBatch], most[kMaxBatch], order[kMaxBatch];
   for (int i = 0; i < count; ++i) {
     const int L = (int)(Ks[i] / 64), Lp = 16 * ((L + 15) / 16), R = c.threads / Lp;
     const int64_t nb = (Ns[i] + R - 1) / R;
-    int64_t share = (int64_t)(512.0 * ((double)Ns[i] * (double)Ks[i]) / total);
+    int64_t share = (int64_t)((double)slots * ((double)Ns[i] * (double)Ks[i]) / total);
     if (share < 1) share = 1;
-    segs[i] = m1_segments(share, nb);
+    segs[i] = m1_segments(share, nb, slots);
     most[i] = (int)((nb + segs[i] - 1) / segs[i]);  // batches of the longest segment
     order[i] = i;
   }
@@ -613,7 +617,7 @@ void launch_m1(const M1Config &c, int count, const uint16_t *const *xs,
     shp.q[j] = (int)(nb / S);
     shp.rem[j] = (int)(nb % S);
     if (S > smax) smax = S;
-    if (!c.direct && m1_stage_bytes((int)Ks[i]) > lds) lds = m1_stage_bytes((int)Ks[i]);
+    if (m1_stage_bytes((int)Ks[i]) > lds) lds = m1_stage_bytes((int)Ks[i]);
   }
   const dim3 grid(smax, count);
   if (c.wave_rows)
@@ -623,8 +627,12 @@ void launch_m1(const M1Config &c, int count, const uint16_t *const *xs,
 }
 
 bool m1_supported(int64_t M, int64_t N, int64_t K) {
-  // packed bytes below 1 GiB: 32-bit offsets never wrap
-  return M == 1 && m1_waves(K) > 0 && N * (K / 64) * 13 < (int64_t(1) << 30);
+  // packed bytes below 1 GiB: 32-bit offsets never wrap; the staged
+  // activations fit a configuration (always so for the K that m1_waves takes)
+  if (M != 1 || m1_waves(K) <= 0 || N * (K / 64) * 13 >= (int64_t(1) << 30)) return false;
+  const M1Config c = m1_config(K, 128);
+  const int xl = ((int)(K >> 3) + 1 + c.threads - 1) / c.threads;
+  return c.one_per_cu ? (!c.wave_rows && m1_staged_one((int)K) && xl <= kXlOne) : xl <= 3;
 }
 
 }  // namespace

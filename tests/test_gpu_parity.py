@@ -285,8 +285,8 @@ def test_gemv_ragged_buffer_ends_and_invalid_bytes(G, N):
 
 # Row lengths K that take every block shape of the one-row kernel: 16-, 32-
 # and 64-lane rows summed inside a wave, 48-lane rows that cross waves, and
-# 80- to 256-lane rows summed through LDS; activations staged through LDS or
-# loaded per lane; batch steps in whole dwords or not (K = 9280 and 13376
+# 80- to 256-lane rows summed through LDS; activations staged with two
+# blocks per CU or, from K = 6848, one; batch steps in whole dwords or not (K = 9280 and 13376
 # give odd byte offsets from one batch to the next).
 @pytest.mark.parametrize("K,G", [(1088, 64), (2048, 128), (2560, 64), (3072, 128), (4160, 64),
                                  (6144, 128), (7168, 64), (8192, 128), (9280, 64), (13376, 64),
