@@ -10,9 +10,6 @@ Workloads (seeds in ternary_weight_only_amd.inputs):
     (the grouped launch over all 72 problems, and per-shape batched launches);
   - the 8B-class FFN matrices W[14336,4096] and W[4096,14336], G = 128,
     decode at M = 1, 4 and 16.
-The only outputs not all compared are those of the M = 2048 stack launch:
-there three problems of each shape are compared whole, and every other
-problem on the first and last row of every 256-row tile plus random rows.
 """
 import functools
 
@@ -203,24 +200,19 @@ def test_prefill_gemm_stack_m512_every_output(launch):
         assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "stack gemm M=512 matrix %d" % i)
 
 
-def test_prefill_gemm_stack_m2048():
-    """M = 2048, the same grouped launch: problems 0, 1, 46 (gate/up)
-    and 2, 35, 71 (down) compared whole; on every other problem the first
-    and last row of every 256-row tile and 8 random rows."""
+@pytest.mark.parametrize("part", range(4))
+def test_prefill_gemm_stack_m2048_every_output(part):
+    """M = 2048, the same grouped launch over all 72 problems: every output
+    of the problems i with i % 4 == part (the oracle's cost split over four
+    cases)."""
     G, M = 128, 2048
     xs, ys = _stack_gemm(M, G)
-    rng = np.random.default_rng(2048)
-    tile_rows = sorted({r for t in range(0, M, 256) for r in (t, min(t + 255, M - 1))})
     for i, (N, K) in enumerate(inputs.stack_shapes()):
+        if i % 4 != part:
+            continue
         p_ref, s_ref = _stack_ref(G)[i]
-        y = ys[i].cpu().numpy()
-        if i in (0, 1, 46, 2, 35, 71):
-            rows = np.arange(M)
-        else:
-            rows = np.unique(np.concatenate([tile_rows, rng.integers(0, M, 8)]))
-        y_ref, bound, _ = oracle.matmul(xs[K][rows], p_ref, s_ref, N, K, G)
-        assert_within_bound(y[rows], y_ref, bound, "stack gemm M=2048 matrix %d" % i)
-        assert np.isfinite(y).all()
+        y_ref, bound, _ = oracle.matmul(xs[K], p_ref, s_ref, N, K, G)
+        assert_within_bound(ys[i].cpu().numpy(), y_ref, bound, "stack gemm M=2048 matrix %d" % i)
 
 
 @pytest.mark.parametrize("shape", [(14336, 4096), (4096, 14336)])

@@ -52,19 +52,15 @@ def test_w4a16_gemm_parity(M, N, K, G):
     _check(y, y_ref, bound, "M=%d W[%d,%d] G=%d" % (M, N, K, G))
 
 
-def test_w4a16_gemm_prefill_m2048_sampled_rows():
-    """M = 2048 on the FFN's gate shape: the first and last row of every
-    64-row tile and 16 random rows, every column."""
+def test_w4a16_gemm_prefill_m2048_every_output():
+    """M = 2048 on the FFN's gate shape: every output."""
     M, N, K, G = 2048, 3584, 1024, 128
     packed, s, b = inputs.w4a16_problem(520, N, K, G)
     x = inputs.activation(521, M, K)
     say("w4a16 gemm M=2048")
     y = _gemm(x, packed, s, b, N, K, G)
-    rng = np.random.default_rng(522)
-    rows = np.unique(np.concatenate([[t for t0 in range(0, M, 64) for t in (t0, t0 + 63)],
-                                     rng.integers(0, M, 16)]))
-    y_ref, bound = oracle.w4a16_matmul(x[rows], packed, s, b, N, K, G)
-    _check(y[rows], y_ref, bound, "M=2048 sampled rows")
+    y_ref, bound = oracle.w4a16_matmul(x, packed, s, b, N, K, G)
+    _check(y, y_ref, bound, "M=2048")
 
 
 @pytest.mark.parametrize("N,K", [(4096, 14336), (37, 8192)])
