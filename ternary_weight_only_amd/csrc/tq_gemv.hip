@@ -140,16 +140,6 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
   const int bid = (int)blockIdx.x, grid = (int)gridDim.x;
   const int mychunks = nchunks > bid ? (nchunks - bid + grid - 1) / grid : 0;
 
-  // ---- decode table: each thread writes 8 of the 4096 (entry, copy) slots,
-  // the copy index rotated by the entry so a wave's writes spread the banks ----
-  {
-    const int ent = tid % kLutEntries;
-    const uint4 e = lut_entry((uint32_t)ent);
-    const int first = (tid / kLutEntries) * (kCopies / 2);
-#pragma unroll
-    for (int k = 0; k < kCopies / 2; ++k) lut[ent * kCopies + ((first + k + ent) & (kCopies - 1))] = e;
-  }
-  __syncthreads();
 
   const int j = lane & 15, q = lane >> 4;
   const uint32_t copyoff = (uint32_t)j * 16u;  // byte 0 of a perm source: the lane's table copy
@@ -353,27 +343,68 @@ void gemv_kernel(const GemvBatch args, int count, int M, int N, int K, int lgS, 
   // load issued behind a fresh HBM load would wait for it: issuing the
   // burst's HBM loads together leaves one HBM latency per burst and only the
   // activations' cache latency between its iterations.
-  for (int k = 0; k < mychunks; ++k) {
+  //
+  // The first burst of the block's first chunk is requested before the
+  // decode table is built (the loads fill registers only), so the table
+  // build runs under their latency.
+  auto issue_burst = [&](const PkCursor &pc, const XCursor &xc, int b0, int nb, XStage (&xs)[kXBuf],
+                         PkStage (&st)[BR]) {
+#pragma unroll
+    for (int d = 0; d < kXLead; ++d) issue_x(xc, b0 + d, d < nb, xs[d]);
+#pragma unroll
+    for (int i = 0; i < BR; ++i) issue_pk(pc, b0 + i, i < nb, st[i]);
+  };
+  auto compute_burst = [&](const XCursor &xc, int b0, int nb, XStage (&xs)[kXBuf],
+                           PkStage (&st)[BR]) {
+#pragma unroll
+    for (int i = 0; i < BR; ++i) {
+      compute(st[i], xs[i % kXBuf]);
+      if (i + kXLead < BR)
+        issue_x(xc, b0 + i + kXLead, i + kXLead < nb, xs[(i + kXLead) % kXBuf]);
+    }
+  };
+  // the bursts of chunk k from group iteration b_first on, then its end
+  auto chunk_from = [&](int k, const PkCursor &pc, const XCursor &xc, int b_first) {
+    for (int b0 = b_first; b0 < ngw; b0 += BR) {
+      const int nb = min(BR, ngw - b0);
+      XStage xs[kXBuf];
+      PkStage st[BR];
+      issue_burst(pc, xc, b0, nb, xs, st);
+      compute_burst(xc, b0, nb, xs, st);
+    }
+    finish_chunk(k);
+  };
+  if (mychunks == 0) return;  // the grid is at most the chunk count: not taken
+  {
+    PkCursor pc;
+    XCursor xc;
+    pc.k = 0; set_pk(pc);
+    xc.k = 0; set_x(xc);
+    {
+      const int nb = min(BR, ngw);
+      XStage xs[kXBuf];
+      PkStage st[BR];
+      issue_burst(pc, xc, 0, nb, xs, st);
+      // decode table: each thread writes 8 of the 4096 (entry, copy) slots,
+      // the copy index rotated by the entry so a wave's writes spread the banks
+      {
+        const int ent = tid % kLutEntries;
+        const uint4 e = lut_entry((uint32_t)ent);
+        const int first = (tid / kLutEntries) * (kCopies / 2);
+#pragma unroll
+        for (int k = 0; k < kCopies / 2; ++k) lut[ent * kCopies + ((first + k + ent) & (kCopies - 1))] = e;
+      }
+      __syncthreads();
+      compute_burst(xc, 0, nb, xs, st);
+    }
+    chunk_from(0, pc, xc, BR);
+  }
+  for (int k = 1; k < mychunks; ++k) {
     PkCursor pc;
     XCursor xc;
     pc.k = k; set_pk(pc);
     xc.k = k; set_x(xc);
-    for (int b0 = 0; b0 < ngw; b0 += BR) {
-      const int nb = min(BR, ngw - b0);
-      XStage xs[kXBuf];
-#pragma unroll
-      for (int d = 0; d < kXLead; ++d) issue_x(xc, b0 + d, d < nb, xs[d]);
-      PkStage st[BR];
-#pragma unroll
-      for (int i = 0; i < BR; ++i) issue_pk(pc, b0 + i, i < nb, st[i]);
-#pragma unroll
-      for (int i = 0; i < BR; ++i) {
-        compute(st[i], xs[i % kXBuf]);
-        if (i + kXLead < BR)
-          issue_x(xc, b0 + i + kXLead, i + kXLead < nb, xs[(i + kXLead) % kXBuf]);
-      }
-    }
-    finish_chunk(k);
+    chunk_from(k, pc, xc, 0);
   }
   // no load may still be writing this wave's registers when it exits
   asm volatile("s_waitcnt vmcnt(0)" ::: "memory");
