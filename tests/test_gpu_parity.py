@@ -289,8 +289,8 @@ def test_gemv_ragged_buffer_ends_and_invalid_bytes(G, N):
 # blocks per CU or, from K = 6848, one; batch steps in whole dwords or not (K = 9280 and 13376
 # give odd byte offsets from one batch to the next).
 @pytest.mark.parametrize("K,G", [(1088, 64), (2048, 128), (2560, 64), (3072, 128), (4160, 64),
-                                 (6144, 128), (7168, 64), (8192, 128), (9280, 64), (13376, 64),
-                                 (16384, 128)])
+                                 (6144, 128), (6784, 64), (6848, 64), (7168, 64), (8192, 128),
+                                 (9280, 64), (13376, 64), (16384, 128)])
 def test_gemv_row_shapes(K, G):
     """tq_gemv at M = 1 over K values covering each row shape, N = 37 (a
     ragged last batch of rows); an invalid byte in the middle of the buffer
@@ -319,8 +319,9 @@ def test_gemv_row_shapes(K, G):
 
 @pytest.mark.parametrize("G", [64, 128])
 def test_gemv_grouped_mixed_shapes(G):
-    """tq_gemv_grouped over mixed shapes -- two kernel configurations, one
-    shape the M = 1 kernel does not take (K = 8320: 130 chunks), ragged N --
+    """tq_gemv_grouped over mixed shapes -- several kernel configurations
+    (among them rows long enough to run one block per CU), one shape the
+    M = 1 kernel does not take (K = 8320: 130 chunks), ragged N --
     and more problems than one launch holds for the commonest configuration:
     bit-identical to one tq_gemv per problem, every output within the
     oracle's bound; an invalid byte in one problem is flagged."""
@@ -329,6 +330,9 @@ def test_gemv_grouped_mixed_shapes(G):
     from tests.gpu_helpers import dev_bf16, dev_f16bits, dev_u8
     base = [(96, 1024), (40, 3584), (37, 640), (5, 8320), (64, 2048)]
     shapes = [base[i % len(base)] if i < 10 else (32 + i % 7, 1024) for i in range(140)]
+    # rows of 6784 (two blocks a CU) and 6848 and 14336 (one block a CU, x
+    # staged): three more configurations in the same call
+    shapes += [(23, 6784), (19, 6848), (11, 14336)]
     shapes = [(n, k) for n, k in shapes if k % G == 0]
     ws = [inputs.normal_bf16(900 + i, (n, k), 0.02) for i, (n, k) in enumerate(shapes)]
     xs = [inputs.activation(1000 + i, 1, k) for i, (n, k) in enumerate(shapes)]
